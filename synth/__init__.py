@@ -1,0 +1,168 @@
+"""Seeded synthetic workloads for the Lightning Attention mixer.
+
+This module only draws inputs: it holds none of the mixer's arithmetic, and both the GPU path
+(through the tests and the benchmark) and the fp64 oracle receive the identical tensors it
+returns.  Values are drawn in float32 from a seeded ``torch.Generator`` and rounded once to the
+storage dtype, so the bits that reach the GPU are the bits the oracle widens.
+
+The named workloads mirror the shapes of the layers the pages benchmark (Qwen3-shaped RNN
+layers with 128-wide heads, batch 1, long context; "Hybrid Linear Attention Done Right",
+Table 6 and Section 6.6).  Real activations need trained weights and datasets that are not
+available here; after the prologue's RMSNorm and RoPE the q/k statistics have the realistic
+scale, and only v and the gate logits are idealised as N(0, 1).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+
+def qwen_lambdas(H: int) -> list[float]:
+    """Per-head decays 1 - 2^-(5 + 8h/H), h = 0..H-1, used by the Qwen3-shaped workloads."""
+    return [1.0 - 2.0 ** (-(5.0 + 8.0 * h / H)) for h in range(H)]
+
+
+@dataclasses.dataclass(frozen=True)
+class PrefillSpec:
+    name: str
+    B: int
+    T: int
+    H: int
+    d: int
+    dtype: torch.dtype
+    lambdas: tuple
+    rope_base: float
+    norm_w: str  # "ones" or "uniform" (U(0.5, 1.5) per head and channel)
+    state: str  # "zeros" or "randn" (0.01 * N(0, 1))
+    chunk: int  # 0 = library default
+    seed: int
+    eps: float = 1e-6
+    pos0: int = 0
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeSpec:
+    name: str
+    B: int
+    H: int
+    d: int
+    dtype: torch.dtype
+    lambdas: tuple
+    rope_base: float
+    max_pos: int
+    seed: int
+    eps: float = 1e-6
+
+
+TINY = PrefillSpec("tiny prefill B=1 H=2 T=256 d=64 fp32", 1, 256, 2, 64, torch.float32,
+                   (0.9, 0.99), 1e4, "ones", "zeros", 64, 1000)
+QWEN17_32K = PrefillSpec("Qwen3-1.7B-shaped RNN layer prefill B=1 H=16 T=32768 d=128 bf16", 1,
+                         32768, 16, 128, torch.bfloat16, tuple(qwen_lambdas(16)), 1e6, "uniform",
+                         "zeros", 0, 1001)
+QWEN17_512K = dataclasses.replace(
+    QWEN17_32K, name="Qwen3-1.7B-shaped RNN layer prefill B=1 H=16 T=524288 d=128 bf16",
+    T=524288, seed=1002)
+DECODE_B64 = DecodeSpec("batched decode step B=64 H=16 d=128 bf16, fp32 state", 64, 16, 128,
+                        torch.bfloat16, tuple(qwen_lambdas(16)), 1e6, 524288, 1003)
+QWEN8_128K = PrefillSpec("Qwen3-8B-shaped RNN layer prefill B=4 H=32 T=131072 d=128 bf16", 4,
+                         131072, 32, 128, torch.bfloat16, tuple(qwen_lambdas(32)), 1e6, "uniform",
+                         "randn", 0, 1004)
+
+WORKLOADS = {
+    "tiny": TINY,
+    "qwen17_32k": QWEN17_32K,
+    "qwen17_512k": QWEN17_512K,
+    "decode_b64": DECODE_B64,
+    "qwen8_128k": QWEN8_128K,
+}
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def _randn(shape, gen, device, dtype, scale=1.0):
+    x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    if scale != 1.0:
+        x.mul_(scale)
+    return x.to(dtype)
+
+
+def make_prefill(spec: PrefillSpec, device="cpu", T: int | None = None) -> dict:
+    """Draw one prefill batch.  ``T`` overrides the sequence length (same distributions)."""
+    T = spec.T if T is None else T
+    B, H, d = spec.B, spec.H, spec.d
+    gen = _gen(spec.seed, device)
+    shape = (B, T, H, d)
+    q = _randn(shape, gen, device, spec.dtype)
+    k = _randn(shape, gen, device, spec.dtype)
+    v = _randn(shape, gen, device, spec.dtype)
+    g = _randn(shape, gen, device, spec.dtype)
+    if spec.norm_w == "ones":
+        qw = torch.ones((H, d), device=device, dtype=torch.float32)
+        kw = torch.ones((H, d), device=device, dtype=torch.float32)
+    else:
+        qw = 0.5 + torch.rand((H, d), generator=gen, device=device, dtype=torch.float32)
+        kw = 0.5 + torch.rand((H, d), generator=gen, device=device, dtype=torch.float32)
+    state = None
+    if spec.state == "randn":
+        state = _randn((B, H, d, d), gen, device, torch.float32, 0.01)
+    return dict(q=q, k=k, v=v, g=g, qw=qw, kw=kw, ow=None, lambdas=list(spec.lambdas),
+                rope_base=spec.rope_base, eps=spec.eps, pos0=spec.pos0, state_in=state,
+                B=B, T=T, H=H, d=d, dtype=spec.dtype, chunk=spec.chunk)
+
+
+def make_decode(spec: DecodeSpec, device="cpu", B: int | None = None) -> dict:
+    B = spec.B if B is None else B
+    H, d = spec.H, spec.d
+    gen = _gen(spec.seed, device)
+    q = _randn((B, H, d), gen, device, spec.dtype)
+    k = _randn((B, H, d), gen, device, spec.dtype)
+    v = _randn((B, H, d), gen, device, spec.dtype)
+    g = _randn((B, H, d), gen, device, spec.dtype)
+    qw = 0.5 + torch.rand((H, d), generator=gen, device=device, dtype=torch.float32)
+    kw = 0.5 + torch.rand((H, d), generator=gen, device=device, dtype=torch.float32)
+    state = _randn((B, H, d, d), gen, device, torch.float32, 0.01)
+    positions = torch.randint(0, spec.max_pos, (B,), generator=gen, device=device,
+                              dtype=torch.int64)
+    return dict(q=q, k=k, v=v, g=g, qw=qw, kw=kw, ow=None, lambdas=list(spec.lambdas),
+                rope_base=spec.rope_base, eps=spec.eps, positions=positions, state_in=state,
+                B=B, H=H, d=d, dtype=spec.dtype)
+
+
+def make_custom_prefill(B, T, H, d, dtype=torch.bfloat16, seed=0, lambdas=None, rope_base=1e6,
+                        norm_w="uniform", state="zeros", pos0=0, eps=1e-6, device="cpu",
+                        v_scale=1.0) -> dict:
+    """Arbitrary-shape prefill batch with the same distributions as the named workloads."""
+    if lambdas is None:
+        lambdas = qwen_lambdas(H)
+    spec = PrefillSpec("custom", B, T, H, d, dtype, tuple(lambdas), rope_base, norm_w, state, 0,
+                       seed, eps, pos0)
+    out = make_prefill(spec, device)
+    if v_scale != 1.0:
+        out["v"] = (out["v"].float() * v_scale).to(dtype)
+    return out
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    """The raw storage of a CPU tensor as numpy: bf16 -> uint16 bits, fp32 -> float32."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.numpy()
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def rel_l2(x: np.ndarray, ref: np.ndarray) -> float:
+    """||x - ref||_2 / ||ref||_2 over the whole array (float64)."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = math.sqrt(float(np.sum(ref * ref)))
+    num = math.sqrt(float(np.sum((x - ref) ** 2)))
+    return num / den if den > 0 else num
