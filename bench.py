@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark of the Lightning Attention mixer library on one MI355X.
+
+One step is one ``lightning_prefill`` call over the 512K-token Qwen3-1.7B-shaped RNN layer
+(B = 1, H = 16, T = 524288, d = 128, bf16 activations, fp32 state): the segment pre-pass, the
+segment scan and the main chunk-loop kernel, i.e. every prefill step of the mixer (prologue,
+decayed intra-chunk scores, inter-chunk term, state update, gated output norm).  Inputs are
+drawn on the device from a seeded generator and are resident in HBM before timing starts.
+
+Printed (one JSON line): prefill tokens/s/layer (``value``), the main kernel's roofline
+(algorithmic HBM bytes per launch / its average duration, timed with HIP events recorded by the
+library around that kernel on the launch stream), its MFMA rate, the batched decode step
+(B = 64, H = 16, d = 128) in microseconds with its HBM roofline, and the fp64 CPU oracle timed on
+a bounded sample of the same prefill workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as ct
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+METRIC = "prefill tokens/s/layer at T=512K (MFMA %) ; decode step µs at B=64 (HBM %)"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen17_512k",
+                    choices=["qwen17_512k", "qwen17_32k", "qwen8_128k"])
+    ap.add_argument("--segments", type=int, default=0, help="0 = library default")
+    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--decode-buffers", type=int, default=8,
+                    help="rotating state buffers (64 MiB each) so the step cannot run from MALL")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime PyTorch already loaded (one runtime)."""
+
+    def __init__(self):
+        self.hip = ct.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ct.POINTER(ct.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ct.POINTER(ct.c_float), ct.c_void_p, ct.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ct.c_void_p]
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = ct.c_void_p()
+            if self.hip.hipEventCreate(ct.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            evs.append(e.value)
+        return evs
+
+    def elapsed_ms(self, a, b):
+        ms = ct.c_float()
+        if self.hip.hipEventElapsedTime(ct.byref(ms), ct.c_void_p(a), ct.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(ct.c_void_p(e))
+
+
+def bench_prefill(args, torch, lt, synth):
+    spec = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    inp = synth.make_prefill(spec, device=dev)
+    B, T, H, d = inp["B"], inp["T"], inp["H"], inp["d"]
+    chunk, P = lt.lightning_prefill_plan(B, T, H, d, spec.dtype, 0, args.segments)
+    y = torch.empty_like(inp["q"])
+    s_out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    ws_bytes = lt.lightning_prefill_workspace_size(B, T, H, d, spec.dtype, 0, args.segments)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    call_args = (inp["q"], inp["k"], inp["v"], inp["g"], inp["qw"], inp["kw"], inp["lambdas"],
+                 inp["rope_base"])
+    kw = dict(rms_eps=inp["eps"], pos0=inp["pos0"], state_in=inp["state_in"], state_out=s_out,
+              y=y, segments=args.segments, workspace=ws)
+    for _ in range(args.warmup):
+        lt.lightning_prefill(*call_args, **kw)
+    torch.cuda.synchronize()
+
+    hev = HipEvents()
+    ev = hev.create(2 * args.steps)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        lt.lightning_prefill(*call_args, **kw, main_kernel_events=(ev[2 * i], ev[2 * i + 1]))
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    main_ms = sum(hev.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for i in range(args.steps)) / args.steps
+    hev.destroy(ev)
+
+    ms_per_step = total_ms / args.steps
+    tokens = B * T
+    act_bytes = 2 if spec.dtype == torch.bfloat16 else 4
+    units = B * H * T  # token-heads per launch
+    per_unit = 5 * d * act_bytes  # read q, k, v, g and write y
+    state_bytes = B * H * P * 2 * d * d * 4  # each segment reads its entry state, writes its end
+    alg_bytes = units * per_unit + state_bytes
+    achieved = alg_bytes / (main_ms * 1e-3) / 1e9
+    useful_flops = units * (4 * d * d + 2 * chunk * d)
+    tflops = useful_flops / (main_ms * 1e-3) / 1e12
+    pre_bytes = B * H * (P - 1) * (T // P) * 2 * d * act_bytes if P > 1 else 0
+    return dict(
+        spec=spec, inp=inp, chunk=chunk, P=P, ms_per_step=ms_per_step, main_ms=main_ms,
+        value=tokens / (ms_per_step * 1e-3),
+        roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                  "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                  "kernel": "chunk_kernel<ModeBF16,128,false> (main chunk loop)",
+                  "alg_bytes_per_launch": alg_bytes, "bytes_per_token_head": per_unit,
+                  "launch_ms": round(main_ms, 4)},
+        mfma={"useful_flops_per_launch": useful_flops, "achieved_tflops": round(tflops, 1),
+              "peak_tflops": BF16_PEAK_TFLOPS, "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+              "flops_per_token_head": 4 * d * d + 2 * chunk * d},
+        whole_call={"ms": round(ms_per_step, 4), "prepass_alg_bytes": pre_bytes,
+                    "alg_bytes": alg_bytes + pre_bytes,
+                    "hbm_frac": round((alg_bytes + pre_bytes) / (ms_per_step * 1e-3) / 1e9
+                                      / HBM_PEAK_GBS, 4)},
+    )
+
+
+def bench_decode(args, torch, lt, synth):
+    spec = synth.DECODE_B64
+    dev = torch.device("cuda:0")
+    inp = synth.make_decode(spec, device=dev)
+    B, H, d = inp["B"], inp["H"], inp["d"]
+    states = [inp["state_in"].clone() for _ in range(args.decode_buffers)]
+    y = torch.empty_like(inp["q"])
+    a = (inp["q"], inp["k"], inp["v"], inp["g"], inp["qw"], inp["kw"], inp["lambdas"],
+         inp["rope_base"], inp["positions"])
+    for i in range(3):
+        lt.lightning_decode_step(*a, states[i % len(states)], y=y, rms_eps=inp["eps"])
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.decode_steps):
+        lt.lightning_decode_step(*a, states[i % len(states)], y=y, rms_eps=inp["eps"])
+    stop.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(stop) * 1e3 / args.decode_steps
+    act_bytes = 2
+    per_bh = 2 * d * d * 4 + 5 * d * act_bytes
+    alg = B * H * per_bh + B * 8
+    gbs = alg / (us * 1e-6) / 1e9
+    return {"workload": spec.name, "us_per_step": round(us, 3),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "decode_kernel<ModeBF16,128>", "alg_bytes_per_launch": alg,
+                         "bytes_per_bh": per_bh},
+            "state_buffers": len(states)}
+
+
+def cpu_baseline(args, torch, synth, pre):
+    import numpy as np
+
+    import oracle
+
+    inp = pre["inp"]
+    Ts = min(args.cpu_sample_tokens, inp["T"])
+    B, H = inp["B"], inp["H"]
+    host = {n: synth.host_bits(inp[n][:, :Ts]) for n in ("q", "k", "v", "g")}
+    s0 = None if inp["state_in"] is None else inp["state_in"].cpu().numpy()
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    out = oracle.prefill(host["q"], host["k"], host["v"], host["g"], inp["qw"].cpu().numpy(),
+                         inp["kw"].cpu().numpy(), inp["lambdas"], inp["rope_base"],
+                         eps=inp["eps"], pos0=inp["pos0"], state_in=s0, want_o=False,
+                         want_state=False, nthreads=cores)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(out["y"]).all()
+    return {"value": round(B * Ts / dt, 1), "unit": "tokens/s/layer", "cores": out["threads"],
+            "kind": "oracle",
+            "sample": f"first {Ts} tokens of the {pre['spec'].name} workload, all {B * H} "
+                      f"(b, h) slices, fp64 token-by-token recurrence, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this mixer build runs on a single MI355X and has "
+              f"no multi-GPU path (asked for --gpus {args.gpus}, WORLD_SIZE={world}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import long_context_hybrid_amd.lightning as lt
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    print(f"[bench] prefill {args.workload}: warmup {args.warmup}, steps {args.steps}",
+          file=sys.stderr, flush=True)
+    pre = bench_prefill(args, torch, lt, synth)
+    dec = None
+    if not args.no_decode:
+        print(f"[bench] decode B=64: steps {args.decode_steps}", file=sys.stderr, flush=True)
+        dec = bench_decode(args, torch, lt, synth)
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(args, torch, synth, pre)
+    spec = pre["spec"]
+    line = {
+        "metric": METRIC,
+        "value": round(pre["value"], 1),
+        "unit": "tokens/s/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if spec.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "B": spec.B, "T": spec.T, "H": spec.H, "d": spec.d,
+                   "chunk": pre["chunk"], "segments": pre["P"], "state": "fp32"},
+        "roofline": pre["roofline"],
+        "mfma": pre["mfma"],
+        "whole_call": pre["whole_call"],
+        "decode": dec,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,134 @@
+/*
+ * lightning.h -- C ABI of the MI355X (gfx950) Lightning Attention mixer library.
+ *
+ * The mixer is the RNN layer of HypeNet ("Hybrid Linear Attention Done Right: Efficient
+ * Distillation and Effective Architectures for Extremely Long Contexts", arXiv 2601.22156,
+ * Appendix A, Eq. 18 and Eq. 19; Section 5.2, Eq. 12 and Eq. 14).  Per batch row b, head h and
+ * token t, given the projections q_t = x W_q, k_t = x W_k, v_t = x W_v and gate logits
+ * g_t = x W_z (one d-vector each):
+ *
+ *   q^  = RMSNorm(q_t) * w_q[h]        k^ = RMSNorm(k_t) * w_k[h]       (Eq. 12 / Eq. 18)
+ *   q~  = RoPE_p(q^)                   k~ = RoPE_p(k^) / sqrt(d)         (Eq. 18), p = pos0 + t
+ *   S_t = lambda_h S_{t-1} + k~^T v_t                                    (Eq. 18, update rule)
+ *   o_t = q~ S_t                                                         (Eq. 18, query rule)
+ *   y_t = RMSNorm(o_t) * w_o[h] * sigmoid(g_t)                           (Eq. 14 / Eq. 18)
+ *
+ * RMSNorm(x) = x / sqrt(mean(x^2) + eps) over the d entries of one head.  RoPE rotates the
+ * half-split pairs (x_i, x_{i+d/2}) by the angle p * base^(-2i/d), i < d/2.  The state S is a
+ * d x d fp32 matrix indexed [key dim][value dim].  The W_o projection is outside this library.
+ *
+ * Conventions shared by every call:
+ *   - Device pointers are plain device addresses (hipMalloc or a PyTorch CUDA tensor); they are
+ *     borrowed for the duration of the work enqueued on `stream` and never freed or retained.
+ *     `lambda` (and `out` of lightning_hypenet_gamma) are HOST pointers read before the call
+ *     returns.  The library allocates no device memory: prefill takes a caller-owned workspace.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only enqueues work and
+ *     never synchronises the device.  The calls keep no state between calls and are re-entrant;
+ *     calls that share a workspace or output buffers must be ordered by the caller.
+ *   - Layouts are dense and row-major: activations [B][T][H][d] (prefill) or [B][H][d] (decode),
+ *     state [B][H][d][d], norm weights [H][d] (or one shared [d] when norm_w_head_stride == 0).
+ *   - Argument errors are detected on the host before anything is launched; the call then
+ *     returns an error status and touches no memory.  Nothing throws across this ABI.
+ *   - Supported: d = 64 or 128, 1 <= H <= LT_MAX_HEADS, every device pointer 16-byte aligned.
+ */
+#ifndef LIGHTNING_H
+#define LIGHTNING_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LT_OK = 0,
+    LT_ERR_INVALID_ARG = 1, /* null/misaligned pointer, non-positive size, lambda outside [0,1],
+                               rope_base <= 0, eps < 0 or not finite */
+    LT_ERR_UNSUPPORTED = 2, /* a valid request this build does not implement (d, dtype, H, chunk) */
+    LT_ERR_WORKSPACE = 3,   /* workspace pointer missing or smaller than the size query says */
+    LT_ERR_HIP = 4          /* the HIP runtime reported an error while enqueuing */
+} lt_status;
+
+typedef enum {
+    LT_F32 = 0, /* activations and outputs stored as IEEE fp32 */
+    LT_BF16 = 1 /* activations and outputs stored as bfloat16 */
+} lt_dtype;
+
+#define LT_MAX_HEADS 256
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* lightning_status_string(int status);
+
+/* Eq. 19 of the paper (Appendix A, "Forget Gate"): gamma_h = exp(-2^(-8h/H)) for h = 1..H,
+ * written to out[h-1] (host memory, H doubles).  LT_ERR_INVALID_ARG if H < 1 or out is NULL. */
+lt_status lightning_hypenet_gamma(int H, double* out);
+
+/* Fill the fp32 recurrent state [B][H][d][d] with zeros (init == NULL) or with a copy of `init`
+ * (same shape, device memory; may not overlap `state` unless equal to it). */
+lt_status lightning_state_init(float* state, int B, int H, int d, const float* init, void* stream);
+
+/* Chunk length and number of sequence segments lightning_prefill will use for this shape when
+ * called with the same `chunk` and `segments` requests (0 = automatic).  Returns
+ * LT_ERR_UNSUPPORTED for a request the build does not implement. */
+lt_status lightning_prefill_plan(int B, int T, int H, int d, int dtype, int chunk, int segments,
+                                 int* chunk_out, int* segments_out);
+
+/* Device workspace (bytes) lightning_prefill needs for this shape and request. */
+size_t lightning_prefill_workspace_size(int B, int T, int H, int d, int dtype, int chunk,
+                                        int segments);
+
+/*
+ * Chunkwise-parallel prefill of T tokens for every (b, h).
+ *   q, k, v, gate : device [B][T][H][d] of `dtype`; gate holds the logits x W_z.
+ *   q_norm_w, k_norm_w : device fp32 QK-RMSNorm weights (Eq. 12); o_norm_w : output-norm weight
+ *                  (Eq. 14) or NULL for ones.  All three use `norm_w_head_stride` (d or 0).
+ *   lambda       : HOST fp64 [H], the per-head decay (gamma_h of Eq. 18/19), each in [0, 1].
+ *   rope_base    : RoPE base (theta), > 0.   rms_eps : RMSNorm epsilon, >= 0.
+ *   pos0         : absolute position of token 0 (positions are 0-based, p = pos0 + t).
+ *   state_in     : device fp32 [B][H][d][d] state before token 0, or NULL for zeros.
+ *   state_out    : device fp32 [B][H][d][d] state after token T-1, or NULL.  May equal
+ *                  state_in (in-place update); any other overlap is undefined.
+ *   y            : device [B][T][H][d] of `dtype`, the gated, normalised output.
+ *   o_raw        : device fp32 [B][T][H][d] receiving o_t before the output norm, or NULL.
+ *   chunk        : chunk length (0 = automatic); segments : sequence segments per (b, h)
+ *                  processed in parallel (0 = automatic).
+ *   workspace    : device scratch of at least lightning_prefill_workspace_size(...) bytes
+ *                  (may be NULL when that size is 0).
+ *   main_kernel_events : NULL, or two hipEvent_t handles (created by the caller) that are
+ *                  recorded on `stream` immediately before and after the main chunk-loop kernel,
+ *                  so a caller can time that kernel alone (the segment pre-pass and scan run
+ *                  before the first event).
+ * Composition: prefill(T1) then prefill(T2, pos0 + T1, state_in = state_out) equals
+ * prefill(T1 + T2) up to rounding.
+ */
+lt_status lightning_prefill(const void* q, const void* k, const void* v, const void* gate,
+                            const float* q_norm_w, const float* k_norm_w, const float* o_norm_w,
+                            int norm_w_head_stride, const double* lambda, double rope_base,
+                            double rms_eps, int64_t pos0, const float* state_in, float* state_out,
+                            void* y, float* o_raw, int B, int T, int H, int d, int dtype,
+                            int chunk, int segments, void* workspace, size_t workspace_bytes,
+                            void* const* main_kernel_events, void* stream);
+
+/*
+ * One recurrent decode step: one new token per batch row, every head.
+ *   q, k, v, gate : device [B][H][d] of `dtype`.
+ *   positions    : device int64 [B], the absolute (0-based) position of each row's token.
+ *   state_in     : device fp32 [B][H][d][d]; state_out : same shape, may equal state_in.
+ *   y            : device [B][H][d] of `dtype`; o_raw : device fp32 [B][H][d] or NULL.
+ * Other arguments as for lightning_prefill.  prefill(T) followed by a decode step at position
+ * pos0 + T equals token T of prefill(T + 1), and its state.
+ */
+lt_status lightning_decode_step(const void* q, const void* k, const void* v, const void* gate,
+                                const float* q_norm_w, const float* k_norm_w,
+                                const float* o_norm_w, int norm_w_head_stride,
+                                const double* lambda, double rope_base, double rms_eps,
+                                const int64_t* positions, const float* state_in,
+                                float* state_out, void* y, float* o_raw, int B, int H, int d,
+                                int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIGHTNING_H */

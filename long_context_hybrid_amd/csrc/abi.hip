@@ -1,0 +1,209 @@
+// C ABI of the Lightning Attention mixer (declared in include/lightning.h).
+//
+// Every entry point validates its arguments on the host before anything is enqueued and maps
+// HIP launch errors to LT_ERR_HIP.  Per-call constants that need fp64 (log2 of the decay, the
+// rotary frequencies, lambda^L for the segment scan) are computed here on the host and passed
+// to the kernels by value.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "lt_internal.h"
+
+namespace {
+
+constexpr double kPi = 3.14159265358979323846;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
+bool ok_opt(const void* p) { return p == nullptr || aligned16(p); }
+
+lt_status check_common(int H, int d, int dtype, const float* qw, const float* kw,
+                       const float* ow, int w_stride, const double* lambda, double rope_base,
+                       double eps) {
+    if (dtype != LT_F32 && dtype != LT_BF16) return LT_ERR_INVALID_ARG;
+    if (H <= 0 || d <= 0) return LT_ERR_INVALID_ARG;
+    if (!ok_ptr(qw) || !ok_ptr(kw) || !ok_opt(ow) || lambda == nullptr) return LT_ERR_INVALID_ARG;
+    if (w_stride != 0 && w_stride != d) return LT_ERR_INVALID_ARG;
+    if (!(rope_base > 0.0) || !isfinite(rope_base)) return LT_ERR_INVALID_ARG;
+    if (!(eps >= 0.0) || !isfinite(eps)) return LT_ERR_INVALID_ARG;
+    for (int h = 0; h < H; ++h)
+        if (!(lambda[h] >= 0.0 && lambda[h] <= 1.0)) return LT_ERR_INVALID_ARG;  // also NaN
+    if (d != 64 && d != 128) return LT_ERR_UNSUPPORTED;
+    if (H > LT_MAX_HEADS) return LT_ERR_UNSUPPORTED;
+    return LT_OK;
+}
+
+// Rotary frequencies base^(-2i/d) expressed in revolutions per position.
+void fill_inv_freq_rev(double* out, int d, double base) {
+    for (int i = 0; i < 64; ++i) out[i] = (i < d / 2) ? pow(base, -2.0 * i / d) / (2.0 * kPi) : 0.0;
+}
+
+float log2_lambda(double lam) {
+    return lam == 0.0 ? -INFINITY : (float)log2(lam);
+}
+
+// Chunk length and segment split.  Segments exist to give every CU a workgroup when B*H is
+// small; each segment gets at least kMinChunksPerSegment chunks.
+lt_status plan(int B, int T, int H, int d, int dtype, int chunk, int segments, int* chunk_out,
+               int* seg_out, int* seg_len_out) {
+    if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || segments < 0 || chunk < 0) return LT_ERR_INVALID_ARG;
+    if (dtype != LT_F32 && dtype != LT_BF16) return LT_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return LT_ERR_UNSUPPORTED;
+    if (chunk != 0 && chunk != lt::kChunk) return LT_ERR_UNSUPPORTED;
+    const int C = lt::kChunk;
+    const long long n_chunks = ((long long)T + C - 1) / C;
+    long long P = segments;
+    if (P == 0) {
+        const long long bh = (long long)B * H;
+        P = (lt::kNumCUs + bh - 1) / bh;
+        const long long cap = n_chunks / lt::kMinChunksPerSegment;
+        if (P > cap) P = cap;
+        if (P < 1) P = 1;
+    }
+    if (P > n_chunks) P = n_chunks;
+    const long long chunks_per_seg = (n_chunks + P - 1) / P;
+    P = (n_chunks + chunks_per_seg - 1) / chunks_per_seg;  // every segment non-empty
+    if ((long long)B * H * P > 0x7fffffffLL) return LT_ERR_UNSUPPORTED;
+    if (chunk_out) *chunk_out = C;
+    if (seg_out) *seg_out = (int)P;
+    if (seg_len_out) *seg_len_out = (int)(chunks_per_seg * C);
+    return LT_OK;
+}
+
+size_t workspace_bytes_for(int B, int H, int d, int P) {
+    return P > 1 ? (size_t)B * H * P * d * d * sizeof(float) : 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lightning_status_string(int status) {
+    switch (status) {
+        case LT_OK: return "LT_OK";
+        case LT_ERR_INVALID_ARG: return "LT_ERR_INVALID_ARG: invalid argument";
+        case LT_ERR_UNSUPPORTED: return "LT_ERR_UNSUPPORTED: shape or option not supported";
+        case LT_ERR_WORKSPACE: return "LT_ERR_WORKSPACE: workspace missing or too small";
+        case LT_ERR_HIP: return "LT_ERR_HIP: HIP runtime error while enqueuing";
+        default: return "unknown lightning status";
+    }
+}
+
+lt_status lightning_hypenet_gamma(int H, double* out) {
+    if (H < 1 || out == nullptr) return LT_ERR_INVALID_ARG;
+    for (int h = 1; h <= H; ++h) out[h - 1] = exp(-pow(2.0, -8.0 * h / H));
+    return LT_OK;
+}
+
+lt_status lightning_state_init(float* state, int B, int H, int d, const float* init, void* stream) {
+    if (!ok_ptr(state) || !ok_opt(init) || B <= 0 || H <= 0 || d <= 0) return LT_ERR_INVALID_ARG;
+    const size_t n = (size_t)B * H * d * d;
+    if (lt::launch_state_init(state, init, n, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return LT_ERR_HIP;
+    return LT_OK;
+}
+
+lt_status lightning_prefill_plan(int B, int T, int H, int d, int dtype, int chunk, int segments,
+                                 int* chunk_out, int* segments_out) {
+    return plan(B, T, H, d, dtype, chunk, segments, chunk_out, segments_out, nullptr);
+}
+
+size_t lightning_prefill_workspace_size(int B, int T, int H, int d, int dtype, int chunk,
+                                        int segments) {
+    int C = 0, P = 0, L = 0;
+    if (plan(B, T, H, d, dtype, chunk, segments, &C, &P, &L) != LT_OK) return 0;
+    return workspace_bytes_for(B, H, d, P);
+}
+
+lt_status lightning_prefill(const void* q, const void* k, const void* v, const void* gate,
+                            const float* q_norm_w, const float* k_norm_w, const float* o_norm_w,
+                            int norm_w_head_stride, const double* lambda, double rope_base,
+                            double rms_eps, int64_t pos0, const float* state_in, float* state_out,
+                            void* y, float* o_raw, int B, int T, int H, int d, int dtype,
+                            int chunk, int segments, void* workspace, size_t workspace_bytes,
+                            void* const* main_kernel_events, void* stream) {
+    if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(gate) || !ok_ptr(y))
+        return LT_ERR_INVALID_ARG;
+    if (!ok_opt(state_in) || !ok_opt(state_out) || !ok_opt(o_raw)) return LT_ERR_INVALID_ARG;
+    if (B <= 0 || T <= 0) return LT_ERR_INVALID_ARG;
+    if (pos0 < 0 || pos0 > ((int64_t)1 << 52) - T) return LT_ERR_INVALID_ARG;
+    lt_status st = check_common(H, d, dtype, q_norm_w, k_norm_w, o_norm_w, norm_w_head_stride,
+                                lambda, rope_base, rms_eps);
+    if (st != LT_OK) return st;
+    if ((double)B * T * H * d > 9.0e15) return LT_ERR_UNSUPPORTED;
+    int C = 0, P = 0, L = 0;
+    st = plan(B, T, H, d, dtype, chunk, segments, &C, &P, &L);
+    if (st != LT_OK) return st;
+    const size_t need = workspace_bytes_for(B, H, d, P);
+    if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need))
+        return LT_ERR_WORKSPACE;
+
+    lt::ChunkParams cp;
+    memset(&cp, 0, sizeof cp);
+    cp.q = q; cp.k = k; cp.v = v; cp.g = gate;
+    cp.qw = q_norm_w; cp.kw = k_norm_w; cp.ow = o_norm_w;
+    cp.state_in = state_in; cp.state_out = state_out;
+    cp.y = y; cp.o_raw = o_raw;
+    cp.ws = static_cast<float*>(workspace);
+    cp.pos0 = pos0;
+    cp.B = B; cp.T = T; cp.H = H; cp.P = P; cp.L = L;
+    cp.w_stride = norm_w_head_stride;
+    cp.eps = (float)rms_eps;
+    for (int h = 0; h < H; ++h) cp.log2_lambda[h] = log2_lambda(lambda[h]);
+    fill_inv_freq_rev(cp.inv_freq_rev, d, rope_base);
+
+    lt::ScanParams sp;
+    memset(&sp, 0, sizeof sp);
+    sp.state_in = state_in;
+    sp.ws = cp.ws;
+    sp.BH = B * H; sp.H = H; sp.P = P; sp.dd = d * d;
+    for (int h = 0; h < H; ++h) sp.lambda_pow_L[h] = (float)pow(lambda[h], (double)L);
+
+    if (main_kernel_events && (!main_kernel_events[0] || !main_kernel_events[1]))
+        return LT_ERR_INVALID_ARG;
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    if (main_kernel_events) {
+        ev[0] = static_cast<hipEvent_t>(main_kernel_events[0]);
+        ev[1] = static_cast<hipEvent_t>(main_kernel_events[1]);
+    }
+    if (lt::launch_prefill(cp, sp, d, dtype, ev, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return LT_ERR_HIP;
+    return LT_OK;
+}
+
+lt_status lightning_decode_step(const void* q, const void* k, const void* v, const void* gate,
+                                const float* q_norm_w, const float* k_norm_w,
+                                const float* o_norm_w, int norm_w_head_stride,
+                                const double* lambda, double rope_base, double rms_eps,
+                                const int64_t* positions, const float* state_in,
+                                float* state_out, void* y, float* o_raw, int B, int H, int d,
+                                int dtype, void* stream) {
+    if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(gate) || !ok_ptr(y))
+        return LT_ERR_INVALID_ARG;
+    if (!ok_ptr(positions) || !ok_ptr(state_in) || !ok_ptr(state_out) || !ok_opt(o_raw))
+        return LT_ERR_INVALID_ARG;
+    if (B <= 0) return LT_ERR_INVALID_ARG;
+    lt_status st = check_common(H, d, dtype, q_norm_w, k_norm_w, o_norm_w, norm_w_head_stride,
+                                lambda, rope_base, rms_eps);
+    if (st != LT_OK) return st;
+    if ((long long)B * H > 0x7fffffffLL) return LT_ERR_UNSUPPORTED;
+
+    lt::DecodeParams dp;
+    memset(&dp, 0, sizeof dp);
+    dp.q = q; dp.k = k; dp.v = v; dp.g = gate;
+    dp.qw = q_norm_w; dp.kw = k_norm_w; dp.ow = o_norm_w;
+    dp.positions = positions;
+    dp.state_in = state_in; dp.state_out = state_out;
+    dp.y = y; dp.o_raw = o_raw;
+    dp.B = B; dp.H = H; dp.w_stride = norm_w_head_stride;
+    dp.eps = (float)rms_eps;
+    for (int h = 0; h < H; ++h) dp.lambda[h] = (float)lambda[h];
+    fill_inv_freq_rev(dp.inv_freq_rev, d, rope_base);
+
+    if (lt::launch_decode(dp, d, dtype, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return LT_ERR_HIP;
+    return LT_OK;
+}
+
+}  // extern "C"

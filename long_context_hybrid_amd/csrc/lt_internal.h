@@ -1,0 +1,73 @@
+// Internal interface between the C-ABI layer (abi.hip) and the kernel launchers.
+// Everything here has already been validated by the ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lightning.h"
+
+namespace lt {
+
+constexpr int kChunk = 64;        // tokens per chunk of the prefill chunk loop
+constexpr int kNumCUs = 256;      // compute units of an MI355X; sizes the automatic segment split
+constexpr int kMinChunksPerSegment = 4;
+
+// Kernel parameters of the prefill chunk loop (passed by value in the kernel argument segment).
+struct ChunkParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const float* qw;
+    const float* kw;
+    const float* ow;        // may be null (ones)
+    const float* state_in;  // may be null (zeros); only read when P == 1
+    float* state_out;       // may be null
+    void* y;
+    float* o_raw;           // may be null
+    float* ws;              // [B][H][P][d][d] fp32 when P > 1
+    int64_t pos0;
+    int B, T, H;
+    int P;      // segments per (b, h)
+    int L;      // tokens per segment (multiple of the chunk), the last segment may be shorter
+    int w_stride;
+    float eps;
+    float log2_lambda[LT_MAX_HEADS];  // log2(lambda_h), -inf for lambda_h = 0
+    double inv_freq_rev[64];          // base^(-2i/d) / (2 pi): rotation in revolutions per position
+};
+
+// Segment-boundary scan: ws[b][h][p] <- S_in(p) from the per-segment end states.
+struct ScanParams {
+    const float* state_in;  // may be null (zeros)
+    float* ws;
+    int BH, H, P, dd;
+    float lambda_pow_L[LT_MAX_HEADS];  // lambda_h^L
+};
+
+struct DecodeParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const float* qw;
+    const float* kw;
+    const float* ow;
+    const int64_t* positions;
+    const float* state_in;
+    float* state_out;
+    void* y;
+    float* o_raw;
+    int B, H, w_stride;
+    float eps;
+    float lambda[LT_MAX_HEADS];
+    double inv_freq_rev[64];
+};
+
+// events[0] / events[1] (may be null) are recorded just before / after the main chunk kernel.
+hipError_t launch_prefill(const ChunkParams& cp, const ScanParams& sp, int d, int dtype,
+                          const hipEvent_t events[2], hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& dp, int d, int dtype, hipStream_t stream);
+hipError_t launch_state_init(float* state, const float* init, size_t n, hipStream_t stream);
+
+}  // namespace lt

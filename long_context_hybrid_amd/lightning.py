@@ -1,0 +1,219 @@
+"""Python binding of ``liblightning.so``, the gfx950 Lightning Attention mixer library.
+
+Argument marshalling only: every step of the mixer runs in the library's HIP kernels.  PyTorch
+provides device memory (outputs and the workspace are allocated here with ``torch.empty`` when
+the caller does not pass them) and the stream (the current stream unless one is given).  The
+functions carry the names of the C entry points declared in ``include/lightning.h``; see that
+header for the mathematics, layouts and error behaviour.  A missing library raises at import.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblightning.so")
+
+LT_OK, LT_ERR_INVALID_ARG, LT_ERR_UNSUPPORTED, LT_ERR_WORKSPACE, LT_ERR_HIP = range(5)
+LT_F32, LT_BF16 = 0, 1
+LT_MAX_HEADS = 256
+
+EXPORTS = (
+    "lightning_status_string",
+    "lightning_hypenet_gamma",
+    "lightning_state_init",
+    "lightning_prefill_plan",
+    "lightning_prefill_workspace_size",
+    "lightning_prefill",
+    "lightning_decode_step",
+)
+
+
+class LightningError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {lib.lightning_status_string(status).decode()}")
+
+
+def _load() -> ct.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m long_context_hybrid_amd.build` first")
+    h = ct.CDLL(LIB_PATH)
+    vp, i32, i64, f64, sz = ct.c_void_p, ct.c_int, ct.c_int64, ct.c_double, ct.c_size_t
+    h.lightning_status_string.argtypes = [i32]
+    h.lightning_status_string.restype = ct.c_char_p
+    h.lightning_hypenet_gamma.argtypes = [i32, vp]
+    h.lightning_hypenet_gamma.restype = i32
+    h.lightning_state_init.argtypes = [vp, i32, i32, i32, vp, vp]
+    h.lightning_state_init.restype = i32
+    h.lightning_prefill_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp]
+    h.lightning_prefill_plan.restype = i32
+    h.lightning_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    h.lightning_prefill_workspace_size.restype = sz
+    h.lightning_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, f64, f64, i64, vp, vp,
+                                    vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp, vp]
+    h.lightning_prefill.restype = i32
+    h.lightning_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, f64, f64, vp, vp,
+                                        vp, vp, vp, i32, i32, i32, i32, vp]
+    h.lightning_decode_step.restype = i32
+    return h
+
+
+lib = _load()
+
+
+def _check(status: int, where: str):
+    if status != LT_OK:
+        raise LightningError(status, where)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return LT_BF16
+    if dt == torch.float32:
+        return LT_F32
+    raise TypeError(f"activations must be bfloat16 or float32, got {dt}")
+
+
+def _dev(t, name, dtype=None, shape=None, device=None):
+    """Device pointer of a tensor, after checking it is a contiguous GPU tensor of the expected
+    dtype/shape (a host pointer handed to a kernel would fault the GPU)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return ct.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ct.c_void_p(stream.cuda_stream)
+
+
+def _norm_weights(qw, kw, ow, H, d, device):
+    shape = tuple(qw.shape)
+    if shape == (d,):
+        stride = 0
+    elif shape == (H, d):
+        stride = d
+    else:
+        raise ValueError(f"norm weights must be [d] or [H, d], got {shape}")
+    ptrs = [_dev(qw, "q_norm_w", torch.float32, shape, device),
+            _dev(kw, "k_norm_w", torch.float32, shape, device),
+            _dev(ow, "o_norm_w", torch.float32, shape, device)]
+    return ptrs, stride
+
+
+def _lambda_array(lambdas, H):
+    lam = [float(x) for x in lambdas]
+    if len(lam) != H:
+        raise ValueError(f"need one lambda per head ({H}), got {len(lam)}")
+    return (ct.c_double * H)(*lam)
+
+
+def lightning_status_string(status: int) -> str:
+    return lib.lightning_status_string(int(status)).decode()
+
+
+def lightning_hypenet_gamma(H: int) -> list:
+    out = (ct.c_double * max(int(H), 1))()
+    _check(lib.lightning_hypenet_gamma(int(H), out), "lightning_hypenet_gamma")
+    return list(out)[:H]
+
+
+def lightning_state_init(state: torch.Tensor, init: torch.Tensor | None = None, stream=None):
+    B, H, d, d2 = state.shape
+    if d != d2:
+        raise ValueError("state must be [B, H, d, d]")
+    dev = state.device
+    sp = _dev(state, "state", torch.float32, None, dev)
+    ip = _dev(init, "init", torch.float32, state.shape, dev)
+    _check(lib.lightning_state_init(sp, B, H, d, ip, _stream(stream, dev)), "lightning_state_init")
+    return state
+
+
+def lightning_prefill_plan(B, T, H, d, dtype=torch.bfloat16, chunk=0, segments=0):
+    c, p = ct.c_int(0), ct.c_int(0)
+    _check(lib.lightning_prefill_plan(B, T, H, d, _dtype_code(dtype), chunk, segments,
+                                      ct.byref(c), ct.byref(p)), "lightning_prefill_plan")
+    return c.value, p.value
+
+
+def lightning_prefill_workspace_size(B, T, H, d, dtype=torch.bfloat16, chunk=0, segments=0) -> int:
+    return int(lib.lightning_prefill_workspace_size(B, T, H, d, _dtype_code(dtype), chunk,
+                                                    segments))
+
+
+def lightning_prefill(q, k, v, gate, q_norm_w, k_norm_w, lambdas, rope_base, rms_eps=1e-6,
+                      pos0=0, state_in=None, state_out=None, y=None, o_raw=None, o_norm_w=None,
+                      chunk=0, segments=0, workspace=None, main_kernel_events=None, stream=None):
+    """Prefill ``[B, T, H, d]`` activations; returns ``y`` (allocated if not given).  Pass a
+    ``state_out`` tensor ([B, H, d, d] fp32) to receive the final state and an ``o_raw`` tensor
+    ([B, T, H, d] fp32) to receive o before the output norm.  ``main_kernel_events`` is None or
+    a pair of raw hipEvent_t handles (integers) recorded around the main chunk kernel."""
+    B, T, H, d = q.shape
+    dev = q.device
+    dt = _dtype_code(q.dtype)
+    act = dict(dtype=q.dtype, shape=q.shape, device=dev)
+    ptrs = [_dev(t, n, **act) for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"))]
+    (qwp, kwp, owp), stride = _norm_weights(q_norm_w, k_norm_w, o_norm_w, H, d, dev)
+    if y is None:
+        y = torch.empty_like(q)
+    yp = _dev(y, "y", **act)
+    sshape = (B, H, d, d)
+    sip = _dev(state_in, "state_in", torch.float32, sshape, dev)
+    sop = _dev(state_out, "state_out", torch.float32, sshape, dev)
+    orp = _dev(o_raw, "o_raw", torch.float32, q.shape, dev)
+    need = lightning_prefill_workspace_size(B, T, H, d, q.dtype, chunk, segments)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsp = _dev(workspace, "workspace", None, None, dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    evp = None
+    if main_kernel_events is not None:
+        evp = (ct.c_void_p * 2)(*(ct.c_void_p(int(e)) for e in main_kernel_events))
+    st = lib.lightning_prefill(*ptrs, qwp, kwp, owp, stride, _lambda_array(lambdas, H),
+                               float(rope_base), float(rms_eps), int(pos0), sip, sop, yp, orp,
+                               B, T, H, d, dt, int(chunk), int(segments), wsp, wbytes, evp,
+                               _stream(stream, dev))
+    _check(st, "lightning_prefill")
+    return y
+
+
+def lightning_decode_step(q, k, v, gate, q_norm_w, k_norm_w, lambdas, rope_base, positions,
+                          state_in, state_out=None, rms_eps=1e-6, y=None, o_raw=None,
+                          o_norm_w=None, stream=None):
+    """One decode step on ``[B, H, d]`` activations.  ``state_out`` defaults to ``state_in``
+    (in-place update).  Returns ``y``."""
+    B, H, d = q.shape
+    dev = q.device
+    dt = _dtype_code(q.dtype)
+    act = dict(dtype=q.dtype, shape=q.shape, device=dev)
+    ptrs = [_dev(t, n, **act) for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"))]
+    (qwp, kwp, owp), stride = _norm_weights(q_norm_w, k_norm_w, o_norm_w, H, d, dev)
+    if y is None:
+        y = torch.empty_like(q)
+    if state_out is None:
+        state_out = state_in
+    sshape = (B, H, d, d)
+    st = lib.lightning_decode_step(*ptrs, qwp, kwp, owp, stride, _lambda_array(lambdas, H),
+                                   float(rope_base), float(rms_eps),
+                                   _dev(positions, "positions", torch.int64, (B,), dev),
+                                   _dev(state_in, "state_in", torch.float32, sshape, dev),
+                                   _dev(state_out, "state_out", torch.float32, sshape, dev),
+                                   _dev(y, "y", **act), _dev(o_raw, "o_raw", torch.float32, q.shape, dev),
+                                   B, H, d, dt, _stream(stream, dev))
+    _check(st, "lightning_decode_step")
+    return y

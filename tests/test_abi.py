@@ -1,0 +1,199 @@
+"""The C-ABI library on the host: it loads, exports what include/lightning.h declares, and its
+host-only logic (the Eq. 19 helper, the plan, argument validation) behaves.  No GPU needed.
+
+The validation cases pass fake (but 16-byte aligned) device addresses together with exactly one
+invalid argument, so a call that wrongly passed validation would try to launch.  They therefore
+run only where no GPU is visible; the same cases run on the GPU with real buffers in
+tests/test_gpu_errors.py.
+"""
+import ctypes as ct
+import math
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lightning.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "hypenet_gamma_h32.txt")
+
+lt = pytest.importorskip("long_context_hybrid_amd.lightning")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(lightning_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(lt.EXPORTS)
+
+
+@pytest.mark.parametrize("name", declared_functions())
+def test_library_exports(name):
+    assert hasattr(lt.lib, name), f"liblightning.so does not export {name}"
+
+
+def test_status_strings():
+    for code in range(5):
+        s = lt.lightning_status_string(code)
+        assert s.startswith("LT_")
+    assert "unknown" in lt.lightning_status_string(99)
+
+
+def _golden_gamma():
+    vals = []
+    for line in open(GOLDEN):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            vals.append(float(line))
+    return vals
+
+
+def test_hypenet_gamma_matches_printed_values():
+    printed = _golden_gamma()
+    assert len(printed) == 32
+    got = lt.lightning_hypenet_gamma(32)
+    for h, (g, ref) in enumerate(zip(got, printed), start=1):
+        assert abs(g - ref) <= 1e-7, f"gamma_{h}: {g} vs printed {ref}"
+
+
+def test_hypenet_gamma_time_scales():
+    # tau_h = 1 / -ln(gamma_h) = 2^(8h/H); the slowest head has tau = 256 tokens, and its
+    # decay over 4096 tokens is e^-16 ~ 1.13e-7.
+    for H in (16, 32):
+        g = lt.lightning_hypenet_gamma(H)
+        for h, gh in enumerate(g, start=1):
+            assert 0.0 < gh < 1.0
+            assert math.isclose(1.0 / -math.log(gh), 2.0 ** (8.0 * h / H), rel_tol=1e-12)
+        assert math.isclose(g[-1], math.exp(-1.0 / 256.0), rel_tol=1e-15)
+        assert math.isclose(g[-1] ** 4096, 1.13e-7, rel_tol=1e-2)
+    with pytest.raises(lt.LightningError):
+        lt.lightning_hypenet_gamma(0)
+
+
+@pytest.mark.parametrize("B,T,H,d,expect_p", [
+    (1, 524288, 16, 128, 16),   # 512K-token layer: one segment per CU
+    (1, 32768, 16, 128, 16),
+    (4, 131072, 32, 128, 2),
+    (64, 4096, 16, 128, 1),      # B*H already fills the CUs
+    (1, 256, 2, 64, 1),          # too short to split (4 chunks)
+    (1, 300, 1, 128, 1),
+    (1, 4096, 1, 128, 16),       # 64 chunks, 4 per segment
+])
+def test_plan_and_workspace(B, T, H, d, expect_p):
+    c, p = lt.lightning_prefill_plan(B, T, H, d)
+    assert c == 64 and p == expect_p
+    ws = lt.lightning_prefill_workspace_size(B, T, H, d)
+    assert ws == (B * H * p * d * d * 4 if p > 1 else 0)
+
+
+def test_plan_explicit_segments_and_chunk():
+    assert lt.lightning_prefill_plan(1, 1000, 2, 128, segments=3) == (64, 3)
+    # more segments than chunks collapses to one chunk per segment
+    assert lt.lightning_prefill_plan(1, 100, 2, 128, segments=50) == (64, 2)
+    with pytest.raises(lt.LightningError) as e:
+        lt.lightning_prefill_plan(1, 1000, 2, 128, chunk=48)
+    assert e.value.status == lt.LT_ERR_UNSUPPORTED
+    with pytest.raises(lt.LightningError) as e:
+        lt.lightning_prefill_plan(1, 1000, 2, 96)
+    assert e.value.status == lt.LT_ERR_UNSUPPORTED
+    assert lt.lightning_prefill_workspace_size(1, 1000, 2, 96) == 0
+
+
+# ---- argument validation with fake device addresses (only where no GPU is visible) ---------
+
+no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                            reason="fake-address validation cases run only without a GPU")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced by a correctly rejected call
+
+
+def _prefill_args(**over):
+    H = over.pop("H", 2)
+    lam = over.pop("lam", [0.9] * H)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, qw=FAKE, kw=FAKE, ow=None, stride=128,
+             lam=(ct.c_double * len(lam))(*lam), base=1e6, eps=1e-6, pos0=0, sin=None, sout=None,
+             y=FAKE, oraw=None, B=1, T=256, H=H, d=128, dt=lt.LT_BF16, chunk=0, seg=0, ws=None,
+             wsb=0, ev=None, stream=None)
+    a.update(over)
+    return a
+
+
+def _call_prefill(a):
+    return lt.lib.lightning_prefill(a["q"], a["k"], a["v"], a["g"], a["qw"], a["kw"], a["ow"],
+                                    a["stride"], a["lam"], a["base"], a["eps"], a["pos0"],
+                                    a["sin"], a["sout"], a["y"], a["oraw"], a["B"], a["T"],
+                                    a["H"], a["d"], a["dt"], a["chunk"], a["seg"], a["ws"],
+                                    a["wsb"], a["ev"], a["stream"])
+
+
+PREFILL_BAD = [
+    ("null_q", dict(q=None), lt.LT_ERR_INVALID_ARG),
+    ("misaligned_k", dict(k=FAKE + 2), lt.LT_ERR_INVALID_ARG),
+    ("null_gate", dict(g=None), lt.LT_ERR_INVALID_ARG),
+    ("null_y", dict(y=None), lt.LT_ERR_INVALID_ARG),
+    ("null_qnorm", dict(qw=None), lt.LT_ERR_INVALID_ARG),
+    ("misaligned_state_in", dict(sin=FAKE + 4), lt.LT_ERR_INVALID_ARG),
+    ("zero_B", dict(B=0), lt.LT_ERR_INVALID_ARG),
+    ("zero_T", dict(T=0), lt.LT_ERR_INVALID_ARG),
+    ("neg_H", dict(H=-1, lam=[0.9]), lt.LT_ERR_INVALID_ARG),
+    ("d_96", dict(d=96, stride=96), lt.LT_ERR_UNSUPPORTED),
+    ("too_many_heads", dict(H=257), lt.LT_ERR_UNSUPPORTED),
+    ("bad_dtype", dict(dt=7), lt.LT_ERR_INVALID_ARG),
+    ("bad_stride", dict(stride=5), lt.LT_ERR_INVALID_ARG),
+    ("lambda_above_one", dict(lam=[0.9, 1.0000001]), lt.LT_ERR_INVALID_ARG),
+    ("lambda_negative", dict(lam=[-0.1, 0.5]), lt.LT_ERR_INVALID_ARG),
+    ("lambda_nan", dict(lam=[float("nan"), 0.5]), lt.LT_ERR_INVALID_ARG),
+    ("rope_base_zero", dict(base=0.0), lt.LT_ERR_INVALID_ARG),
+    ("rope_base_inf", dict(base=float("inf")), lt.LT_ERR_INVALID_ARG),
+    ("eps_negative", dict(eps=-1e-6), lt.LT_ERR_INVALID_ARG),
+    ("pos0_negative", dict(pos0=-1), lt.LT_ERR_INVALID_ARG),
+    ("chunk_unsupported", dict(chunk=32), lt.LT_ERR_UNSUPPORTED),
+    ("workspace_missing", dict(T=524288, H=16, lam=[0.9] * 16), lt.LT_ERR_WORKSPACE),
+    ("workspace_small", dict(T=524288, H=16, lam=[0.9] * 16, ws=FAKE, wsb=1024), lt.LT_ERR_WORKSPACE),
+    ("workspace_misaligned", dict(T=524288, H=16, lam=[0.9] * 16, ws=FAKE + 8, wsb=1 << 30),
+     lt.LT_ERR_WORKSPACE),
+    ("events_null_entries", dict(ev=(ct.c_void_p * 2)(None, None)), lt.LT_ERR_INVALID_ARG),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,over,status", PREFILL_BAD, ids=[c[0] for c in PREFILL_BAD])
+def test_prefill_rejects(name, over, status):
+    assert _call_prefill(_prefill_args(**over)) == status
+
+
+DECODE_BAD = [
+    ("null_positions", dict(pos=None), lt.LT_ERR_INVALID_ARG),
+    ("null_state_in", dict(sin=None), lt.LT_ERR_INVALID_ARG),
+    ("null_state_out", dict(sout=None), lt.LT_ERR_INVALID_ARG),
+    ("misaligned_v", dict(v=FAKE + 2), lt.LT_ERR_INVALID_ARG),
+    ("zero_B", dict(B=0), lt.LT_ERR_INVALID_ARG),
+    ("d_32", dict(d=32, stride=32), lt.LT_ERR_UNSUPPORTED),
+    ("lambda_above_one", dict(lam=[2.0, 0.5]), lt.LT_ERR_INVALID_ARG),
+    ("eps_nan", dict(eps=float("nan")), lt.LT_ERR_INVALID_ARG),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,over,status", DECODE_BAD, ids=[c[0] for c in DECODE_BAD])
+def test_decode_rejects(name, over, status):
+    lam = over.pop("lam", [0.9, 0.99])
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, qw=FAKE, kw=FAKE, ow=None, stride=128,
+             lam=(ct.c_double * 2)(*lam), base=1e6, eps=1e-6, pos=FAKE, sin=FAKE, sout=FAKE,
+             y=FAKE, oraw=None, B=4, H=2, d=128, dt=lt.LT_BF16, stream=None)
+    a.update(over)
+    st = lt.lib.lightning_decode_step(a["q"], a["k"], a["v"], a["g"], a["qw"], a["kw"], a["ow"],
+                                      a["stride"], a["lam"], a["base"], a["eps"], a["pos"],
+                                      a["sin"], a["sout"], a["y"], a["oraw"], a["B"], a["H"],
+                                      a["d"], a["dt"], a["stream"])
+    assert st == status
+
+
+@no_gpu
+def test_state_init_rejects():
+    assert lt.lib.lightning_state_init(None, 1, 1, 64, None, None) == lt.LT_ERR_INVALID_ARG
+    assert lt.lib.lightning_state_init(FAKE + 4, 1, 1, 64, None, None) == lt.LT_ERR_INVALID_ARG
+    assert lt.lib.lightning_state_init(FAKE, 0, 1, 64, None, None) == lt.LT_ERR_INVALID_ARG
