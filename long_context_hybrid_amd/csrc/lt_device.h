@@ -32,8 +32,12 @@ __device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
 __device__ __forceinline__ uint16_t to_bf16_bits(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// Two RNE conversions in one v_cvt_pk_bf16_f32; a lands in the low half.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return (uint32_t)to_bf16_bits(a) | ((uint32_t)to_bf16_bits(b) << 16);
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -58,6 +62,28 @@ __device__ __forceinline__ void rope_cos_sin(int64_t pos, double f_rev, float& c
     sincosf(ang, &s, &c);
 }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// Hardware reciprocal and reciprocal square root (1 ulp).
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float fast_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }
+
+__device__ __forceinline__ float sigmoidf_(float x) { return fast_rcp(1.0f + __expf(-x)); }
+
+// Lane permutations inside 16-lane rows (DPP): quad_perm [1,0,3,2] and [2,3,0,1], mirror
+// within 8 lanes, mirror within 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL,
+                                                              0xf, 0xf, true));
+}
+// Sum over aligned groups of N = 2, 4, 8 or 16 consecutive lanes; every lane gets the sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(N == 2 || N == 4 || N == 8 || N == 16, "group of 2..16 lanes");
+    x += dpp_mov<0xb1>(x);                       // lane ^ 1
+    if constexpr (N >= 4) x += dpp_mov<0x4e>(x);  // lane ^ 2
+    if constexpr (N >= 8) x += dpp_mov<0x141>(x); // 8-lane mirror: joins the two quads
+    if constexpr (N >= 16) x += dpp_mov<0x140>(x); // 16-lane mirror: joins the two halves
+    return x;
+}
 
 }  // namespace lt

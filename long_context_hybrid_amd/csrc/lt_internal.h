@@ -9,9 +9,9 @@
 
 namespace lt {
 
-constexpr int kChunk = 64;        // tokens per chunk of the prefill chunk loop
+constexpr int kChunk = 32;        // tokens per chunk of the prefill chunk loop
 constexpr int kNumCUs = 256;      // compute units of an MI355X; sizes the automatic segment split
-constexpr int kMinChunksPerSegment = 4;
+constexpr int kMinChunksPerSegment = 8;
 
 // Kernel parameters of the prefill chunk loop (passed by value in the kernel argument segment).
 struct ChunkParams {

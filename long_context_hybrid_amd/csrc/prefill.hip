@@ -1,109 +1,189 @@
 // Chunkwise-parallel prefill of the Lightning Attention mixer on gfx950.
 //
 // Math ("Hybrid Linear Attention Done Right", Appendix A, Eq. 18 with the decay of Eq. 19): for
-// one (b, h), with q~, k~ the normalised, rotated query/key (key scaled by 1/sqrt(d)) and the
-// state S after token t0-1, a chunk of n tokens t0..t0+n-1 gives
+// one (b, h), with q~, k~ the normalised, rotated query/key (key scaled by 1/sqrt(d)) and S the
+// state after token t0-1, a chunk of n tokens t0..t0+n-1 gives
 //     o_i = lambda^(i+1) q~_i S  +  sum_{j<=i} lambda^(i-j) (q~_i . k~_j) v_j
 //     S  <- lambda^n S  +  sum_j lambda^(n-1-j) k~_j^T v_j
 // which is the recurrence S_t = lambda S_{t-1} + k~_t^T v_t, o_t = q~_t S_t regrouped by chunk.
 //
-// Work decomposition (one workgroup per (b, h, segment)):
-//   * A sequence is split into P segments of L tokens.  A state-only pass computes each segment's
-//     end state from zero, a scan turns those into each segment's entry state, and the main pass
-//     runs every segment's chunk loop in parallel from its entry state.  This keeps all CUs busy
-//     when B*H is much smaller than the CU count (B = 1, H = 16 at 512K tokens).
-//   * The workgroup has d/32 wavefronts; wavefront w owns value columns [32w, 32w+32): its slice
-//     of the fp32 state S (d x 32) lives in MFMA accumulator registers for the whole chunk loop,
-//     and it produces the same output columns.  The state never round-trips through LDS: the
-//     query-state product reads its B operand straight from those registers, with the key index
-//     permuted to match the accumulator layout (the A operand is read with the same permutation).
-//   * Per chunk: a fused prologue (RMSNorm + RoPE + key scale + per-row decay, hi/lo bf16 split of
-//     the decayed keys) writes the operand tiles to LDS; MFMA computes the decayed causal scores
-//     (Q K^T (.) D), the inter-chunk term (Q S), the intra-chunk term (P V) and the state update
-//     (K'^T V, as hi + lo products so the fp32 state stays fp32-accurate); a row-wise epilogue
-//     applies the output RMSNorm and the sigmoid gate and stores y.
-//   * The next chunk's q/k/v are prefetched into registers while the current chunk computes.
+// Work decomposition
+//   * One workgroup per (b, h, sequence segment).  A sequence is split into P segments; a
+//     state-only pass computes each segment's end state from zero, a scan turns those into each
+//     segment's entry state, and the main pass runs every segment from its entry state.  This
+//     fills the 256 CUs when B*H is small (B = 1, H = 16 at 512K tokens).
+//   * A workgroup has 2 * d/32 wavefronts in two roles (warp specialisation):
+//       - d/32 "math" wavefronts.  Wavefront w owns value columns [32w, 32w+32): its d x 32 slice
+//         of the fp32 state lives in MFMA accumulators for the whole segment.  Per chunk it
+//         computes the transposed decayed scores P^T = (K~ Q~^T) (.) D^T, the inter-chunk term
+//         diag(lambda^(i+1)) Q~ S, the intra-chunk term P V (its A operand is the score
+//         accumulator itself, re-typed to bf16), and the state update K'^T V with K' = hi + lo
+//         bf16 parts of the decayed keys so the fp32 state stays fp32-accurate.
+//       - d/32 "io" wavefronts.  They stream q/k/v/g from HBM with a two-chunk register
+//         prefetch, run the prologue (RMSNorm, RoPE, key scale, per-row decay, hi/lo split) into
+//         LDS, and run the epilogue (output RMSNorm, sigmoid gate, bf16 store of y).
+//     On every SIMD one math and one io wavefront are resident, so VALU work, memory traffic and
+//     MFMA work of consecutive chunks overlap.
+//   * Chunks of 32 tokens; operand tiles and the output stage are double-buffered in LDS, so a
+//     step needs one workgroup barrier: in step s the io waves write chunk s and read back the
+//     output of chunk s-2 while the math waves process chunk s-1.
+//   * The state never round-trips through LDS: the query-state product takes its B operand from
+//     the accumulator registers, with the key index permuted to match the accumulator layout.
+//   * RoPE: the io waves build a per-chunk table of cos/sin(p0 f_i) (one fp64-reduced sincos per
+//     frequency, p0 = the chunk's first position) and each thread rotates it by loop-invariant
+//     cos/sin(j f_i) of its rows j, so the per-element cost is one complex multiply.
 //
-// MFMA layouts used (v_mfma_f32_32x32x16_bf16 and v_mfma_f32_32x32x2_f32 on gfx950):
+// MFMA layouts (v_mfma_f32_32x32x16_bf16 and v_mfma_f32_32x32x2_f32 on gfx950):
 //   A[m][k]: lane l holds m = l % 32 and k = 8 (l / 32) + e (bf16, e < 8) or k = l / 32 (fp32);
 //   B[k][n]: lane l holds n = l % 32 and the same k;
 //   C[m][n]: lane l, register r holds n = l % 32, m = 8 (r / 4) + 4 (l / 32) + r % 4.
-#include <type_traits>
-
 #include "lt_device.h"
 #include "lt_internal.h"
 
 namespace lt {
 namespace {
 
-constexpr int C = kChunk;
+constexpr int C = kChunk;  // 32 tokens per chunk
+static_assert(C == 32, "the tiling below assumes one 32-row block per chunk");
+// Chunks of q/k/v in flight per workgroup (register sets of the io wavefronts).  The main pass
+// is limited by its 256-VGPR budget at two wavefronts per SIMD.
+#ifndef LT_PREFETCH_MAIN
+#define LT_PREFETCH_MAIN 3
+#endif
+#ifndef LT_PREFETCH_STATE
+#define LT_PREFETCH_STATE 6
+#endif
+constexpr int kPrefetchMain = LT_PREFETCH_MAIN;
+constexpr int kPrefetchStateOnly = LT_PREFETCH_STATE;
 
-template <class M, int D>
-struct Smem {
+// Row index inside a 32x32 accumulator tile for lane half lh and register r.
+__device__ __forceinline__ int acc_row(int r, int lh) { return 8 * (r >> 2) + 4 * lh + (r & 3); }
+
+// Placement of the contraction index inside an LDS tile row.
+//   kpos: bits 2 and 3 exchanged.  A product whose k order follows the accumulator layout
+//         (k = 16 st + 8 (e / 4) + 4 lh + e % 4 for operand element e) then reads one contiguous,
+//         aligned 16-byte block per lane, like the products in natural k order.  Every operand of
+//         a contraction uses the same placement, so the sums are unchanged.
+//   tsw:  transposed tiles ([feature][token]) XOR their 8-token blocks with bits 4-5 of the row,
+//         which spreads the prologue's 2-token column writes over the LDS banks while keeping
+//         every 8-token block contiguous.
+template <class M>
+struct Layout {
+    static __device__ __forceinline__ int kpos(int k) {
+        return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+    }
+    static __device__ __forceinline__ int tsw(int row) { return 8 * ((row >> 4) & 3); }
+};
+template <>
+struct Layout<ModeF32> {  // fp32 tiles keep the natural placement
+    static __device__ __forceinline__ int kpos(int k) { return k; }
+    static __device__ __forceinline__ int tsw(int) { return 0; }
+};
+
+template <class M, int D, bool kStateOnly>
+struct Cfg {
     using E = typename M::E;
+    static constexpr int NW = D / 32;                 // math wavefronts = io wavefronts
+    static constexpr int NT = 128 * NW;               // threads per workgroup
+    static constexpr int HALF = D / 2;
     static constexpr int kPad = (sizeof(E) == 2) ? 8 : 4;  // 16 bytes of padding per row
-    static constexpr int QS = D + kPad;                    // row stride of the q~/k~ tiles
-    static constexpr int TS = C + kPad;                    // row stride of transposed tiles and P
-    static constexpr int OS = D + 4;                       // row stride of the fp32 output stage
-    union {
-        struct {
-            E q[C * QS];  // q~ [token][key dim]
-            E k[C * QS];  // k~ [token][key dim]
-        } qk;
-        float o[C * OS];  // o [token][value dim], written after q~/k~ are consumed
-    } u;
-    E khT[D * TS];                       // decayed keys (hi part) [key dim][token]
-    E klT[M::kSplit ? D * TS : 1];       // decayed keys (lo part) [key dim][token]
-    E vT[D * TS];                        // v [value dim][token]
-    E p[C * TS];                         // decayed causal scores [token i][token j]
+    static constexpr int QS = D + kPad;               // row stride of q~/k~ tiles [token][dim]
+    static constexpr int TS = C + kPad;               // row stride of transposed tiles [dim][token]
+    static constexpr int OS = D + 8;                  // row stride of the fp32 output stage
+    // Double buffering needs ~2x the tile space; fp32 tiles at d = 128 only fit single-buffered.
+    static constexpr bool kOverlap = (sizeof(E) == 2) || (D == 64);
+    static constexpr int NBUF = kOverlap ? 2 : 1;
+};
+
+template <class M, int D, bool kStateOnly>
+struct Tiles {
+    using G = Cfg<M, D, kStateOnly>;
+    using E = typename G::E;
+    E q[kStateOnly ? 1 : C * G::QS];   // q~ [token][key dim]
+    E k[kStateOnly ? 1 : C * G::QS];   // k~ [token][key dim]
+    E khT[D * G::TS];                  // decayed keys, hi part, [key dim][token]
+    E klT[M::kSplit ? D * G::TS : 1];  // decayed keys, lo part
+    E vT[D * G::TS];                   // v [value dim][token]
+};
+
+template <class M, int D, bool kStateOnly>
+struct Smem {
+    using G = Cfg<M, D, kStateOnly>;
+    Tiles<M, D, kStateOnly> buf[G::NBUF];
+    float o[kStateOnly ? 1 : G::NBUF * C * G::OS];  // o before the output norm [token][value dim]
+    float2 rope[2][64];                             // cos/sin(p0 f_i) of the next two chunks
     float wo[D];
 };
 
+// ---- activation access ------------------------------------------------------------------------
+
 template <class M>
-struct Act;  // how one group of 4 consecutive activations is loaded and widened
+struct Act;
 template <>
 struct Act<ModeBF16> {
-    using V = uint2;
-    static __device__ __forceinline__ void widen(V x, float* o) {
+    using V4 = uint2;  // 4 consecutive activations
+    static __device__ __forceinline__ void widen(V4 x, float* o) {
         o[0] = bf16_lo(x.x); o[1] = bf16_hi(x.x); o[2] = bf16_lo(x.y); o[3] = bf16_hi(x.y);
     }
-    static __device__ __forceinline__ V zero() { return make_uint2(0u, 0u); }
+    static __device__ __forceinline__ V4 zero() { return make_uint2(0u, 0u); }
 };
 template <>
 struct Act<ModeF32> {
-    using V = float4;
-    static __device__ __forceinline__ void widen(V x, float* o) {
+    using V4 = float4;
+    static __device__ __forceinline__ void widen(V4 x, float* o) {
         o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w;
     }
-    static __device__ __forceinline__ V zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+    static __device__ __forceinline__ V4 zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
 };
 
-// Store 4 values to a 4-element-aligned LDS location.
+// Element u (0..3) of two consecutive tokens' 4-element groups, as one 2-token pair of a
+// transposed tile row, without widening: bf16 pairs are assembled with a byte permute.
+__device__ __forceinline__ void st_pair(__bf16* dst, uint2 row0, uint2 row1, int u) {
+    const uint32_t a = (u < 2) ? row0.x : row0.y, b = (u < 2) ? row1.x : row1.y;
+    const uint32_t sel = (u & 1) ? 0x07060302u : 0x05040100u;  // low or high bf16 of each word
+    *reinterpret_cast<uint32_t*>(dst) = __builtin_amdgcn_perm(b, a, sel);
+}
+__device__ __forceinline__ void st_pair(float* dst, float4 row0, float4 row1, int u) {
+    const float a = u == 0 ? row0.x : u == 1 ? row0.y : u == 2 ? row0.z : row0.w;
+    const float b = u == 0 ? row1.x : u == 1 ? row1.y : u == 2 ? row1.z : row1.w;
+    *reinterpret_cast<float2*>(dst) = make_float2(a, b);
+}
+
+// LDS stores of 4 (row-major tiles) or 2 (transposed tiles) consecutive elements.
 __device__ __forceinline__ void st4(__bf16* dst, float a, float b, float c, float d) {
     *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
 }
 __device__ __forceinline__ void st4(float* dst, float a, float b, float c, float d) {
     *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
 }
+__device__ __forceinline__ void st2(__bf16* dst, float a, float b) {
+    *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(a, b);
+}
+__device__ __forceinline__ void st2(float* dst, float a, float b) {
+    *reinterpret_cast<float2*>(dst) = make_float2(a, b);
+}
 
-// acc += A[rowA, k0:k0+KB] . B[rowB, k0:k0+KB]^T over a whole row of K elements, natural k map.
+// ---- MFMA contractions ------------------------------------------------------------------------
+
+// acc += A[row a, 0:K] . B[row b, 0:K] with both operands read from LDS rows (natural k order).
+// swa / swb: the XOR applied to 8-element blocks of each row (transposed tiles), else 0.
 template <int K>
 __device__ __forceinline__ void contract_rows(f32x16& acc, const __bf16* a, const __bf16* b,
-                                              int lh) {
+                                              int lh, int swa = 0, int swb = 0) {
 #pragma unroll
     for (int k0 = 0; k0 < K; k0 += 16) {
-        bf16x8 av = *reinterpret_cast<const bf16x8*>(a + k0 + 8 * lh);
-        bf16x8 bv = *reinterpret_cast<const bf16x8*>(b + k0 + 8 * lh);
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(a + ((k0 + 8 * lh) ^ swa));
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(b + ((k0 + 8 * lh) ^ swb));
         acc = mfma_bf16(av, bv, acc);
     }
 }
 template <int K>
 __device__ __forceinline__ void contract_rows(f32x16& acc, const float* a, const float* b,
-                                              int lh) {
+                                              int lh, int swa = 0, int swb = 0) {
 #pragma unroll
     for (int k0 = 0; k0 < K; k0 += 8) {
-        float4 av = *reinterpret_cast<const float4*>(a + k0 + 4 * lh);
-        float4 bv = *reinterpret_cast<const float4*>(b + k0 + 4 * lh);
+        const float4 av = *reinterpret_cast<const float4*>(a + ((k0 + 4 * lh) ^ swa));
+        const float4 bv = *reinterpret_cast<const float4*>(b + ((k0 + 4 * lh) ^ swb));
         acc = mfma_f32(av.x, bv.x, acc);
         acc = mfma_f32(av.y, bv.y, acc);
         acc = mfma_f32(av.z, bv.z, acc);
@@ -111,57 +191,51 @@ __device__ __forceinline__ void contract_rows(f32x16& acc, const float* a, const
     }
 }
 
-// acc += Q~[row, 32c:32c+32] . S[32c:32c+32, cols] with the B operand taken from the state
-// accumulator tile `s` (same layout as C[m][n] above: key index m, value column n).
-__device__ __forceinline__ void contract_state(f32x16& acc, const __bf16* qrow, const f32x16& s,
-                                               int lh) {
+// The 16 registers of an accumulator tile X (rows m = acc_row(r), column n = lane % 32) used as
+// the k-operand of a product: register r pairs with k = acc_row(r, lh) of the tile, so the
+// LDS-side operand is needed at k = 16 st + 8 (e / 4) + 4 lh + e % 4 (bf16; with the kpos
+// placement that is the block at 16 st + 8 lh) or 8 g + 4 lh + e (fp32).
+// acc += X-side . row, where `row` is the LDS row of the other operand and sw its block XOR.
+__device__ __forceinline__ void contract_acc(f32x16& acc, const f32x16& x, const __bf16* row,
+                                             int lh, bool x_is_a, int sw = 0) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-        // operand element e pairs with key 16 st + 8 (e / 4) + 4 lh + e % 4 of this tile
-        uint2 lo = *reinterpret_cast<const uint2*>(qrow + 16 * st + 4 * lh);
-        uint2 hi = *reinterpret_cast<const uint2*>(qrow + 16 * st + 8 + 4 * lh);
-        uint4 packed = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        bf16x8 av = __builtin_bit_cast(bf16x8, packed);
-        bf16x8 bv;
+        const bf16x8 lv = *reinterpret_cast<const bf16x8*>(row + ((16 * st + 8 * lh) ^ sw));
+        bf16x8 xv;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) bv[e] = to_bf16(s[8 * st + e]);
-        acc = mfma_bf16(av, bv, acc);
+        for (int e = 0; e < 8; ++e) xv[e] = to_bf16(x[8 * st + e]);
+        acc = x_is_a ? mfma_bf16(xv, lv, acc) : mfma_bf16(lv, xv, acc);
     }
 }
-__device__ __forceinline__ void contract_state(f32x16& acc, const float* qrow, const f32x16& s,
-                                               int lh) {
+__device__ __forceinline__ void contract_acc(f32x16& acc, const f32x16& x, const float* row,
+                                             int lh, bool x_is_a, int sw = 0) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        float4 av = *reinterpret_cast<const float4*>(qrow + 8 * g + 4 * lh);
-        acc = mfma_f32(av.x, s[4 * g + 0], acc);
-        acc = mfma_f32(av.y, s[4 * g + 1], acc);
-        acc = mfma_f32(av.z, s[4 * g + 2], acc);
-        acc = mfma_f32(av.w, s[4 * g + 3], acc);
+        const float4 lv = *reinterpret_cast<const float4*>(row + ((8 * g + 4 * lh) ^ sw));
+        const float l4[4] = {lv.x, lv.y, lv.z, lv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            acc = x_is_a ? mfma_f32(x[4 * g + e], l4[e], acc) : mfma_f32(l4[e], x[4 * g + e], acc);
     }
 }
 
-// Row index inside a 32x32 accumulator tile for lane half lh and register r.
-__device__ __forceinline__ int acc_row(int r, int lh) { return 8 * (r >> 2) + 4 * lh + (r & 3); }
-
-template <class M, int D, bool kStateOnly>
-__global__ void __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(1, 1)))
-chunk_kernel(const ChunkParams p) {
-    using E = typename M::E;
+template <class M, int D, bool kStateOnly, int PF>
+__global__ void __launch_bounds__(128 * (D / 32)) chunk_kernel(const ChunkParams p) {
+    using G = Cfg<M, D, kStateOnly>;
+    using E = typename G::E;
     using In = typename M::In;
     using A = Act<M>;
-    using SM = Smem<M, D>;
-    constexpr int NW = D / 32;  // wavefronts; wavefront w owns value columns [32w, 32w + 32)
-    constexpr int NT = 64 * NW;
-    constexpr int FG = D / 8;   // prologue: threads per row group (4 features per half each)
-    constexpr int HALF = D / 2;
-    constexpr int QS = SM::QS, TS = SM::TS, OS = SM::OS;
-    static_assert(NT / FG * 4 == C, "prologue covers the chunk with 4 rows per thread");
+    using V4 = typename A::V4;
+    constexpr int NW = G::NW, HALF = G::HALF, QS = G::QS, TS = G::TS, OS = G::OS;
+    constexpr int NBUF = G::NBUF;
+    constexpr bool kOverlap = G::kOverlap;
 
-    __shared__ SM sm;
+    __shared__ Smem<M, D, kStateOnly> sm;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     const int lm = lane & 31, lh = lane >> 5;
+    const bool is_math = wave < NW;
 
     const int nseg = kStateOnly ? p.P - 1 : p.P;
     const int seg = blockIdx.x % nseg;
@@ -169,332 +243,438 @@ chunk_kernel(const ChunkParams p) {
     const int b = bh / p.H, h = bh - b * p.H;
     const int t_begin = seg * p.L;
     const int t_end = min(p.T, t_begin + p.L);
+    const int n_chunks = (t_end - t_begin + C - 1) / C;
+    // pipeline steps: chunk s is written in step s, computed in step s+1 and stored in step s+2;
+    // rounded up to a multiple of PF so the io loop can rotate PF register sets without branches
+    const int n_steps = (n_chunks + 2 + PF - 1) / PF * PF;
     const float l2l = p.log2_lambda[h];
     const size_t dd = (size_t)D * D;
+    const size_t row_stride = (size_t)p.H * D;  // elements between consecutive tokens
+    const size_t head_base = ((size_t)b * p.T * p.H + h) * D;
 
-    // ---- prologue mapping: rows 4 rg + s (s < 4), features 4 fg + u and HALF + 4 fg + u ----
-    const int fg = tid % FG, rg = tid / FG;
-    float wq[8], wk[8];
-    double frev[4];
-    {
-        const float* pq = p.qw + (size_t)h * p.w_stride;
-        const float* pk = p.kw + (size_t)h * p.w_stride;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            wq[u] = pq[4 * fg + u];
-            wq[4 + u] = pq[HALF + 4 * fg + u];
-            wk[u] = pk[4 * fg + u];
-            wk[4 + u] = pk[HALF + 4 * fg + u];
-            frev[u] = p.inv_freq_rev[4 * fg + u];
+    // ---- io-role constants ----
+    constexpr int FG = D / 8;                 // prologue: threads per row group
+    const int it = threadIdx.x - 64 * NW;     // io thread index (negative in math waves)
+    const int fg = it % FG, rg = it / FG;     // rows 2 rg + s, features 4 fg + u and HALF + 4 fg + u
+    constexpr int EPT = 16, TPR = D / EPT;    // epilogue: 16 outputs per thread, TPR per row
+    const int er = it / TPR, ec = it % TPR;
+
+    // Per-chunk RoPE base table cos/sin(p0 f_i): HALF / NW frequencies per io wave, one per lane.
+    // (The frequency is read once: a dynamically indexed kernel-argument read is a vector memory
+    // load, and waiting for it inside the loop would also wait for the prefetches.)
+    constexpr int FPW = HALF / NW;  // frequencies per io wave
+    const int table_i = (wave - NW) * FPW + lane;
+    const bool table_lane = wave >= NW && lane < FPW;
+    const double table_frev = table_lane ? p.inv_freq_rev[table_i] : 0.0;
+    auto fill_rope_table = [&](int chunk, int slot) {
+        if (table_lane) {
+            float cs, sn;
+            rope_cos_sin(p.pos0 + t_begin + (int64_t)chunk * C, table_frev, cs, sn);
+            sm.rope[slot][table_i] = make_float2(cs, sn);
         }
-    }
+    };
+
     if (!kStateOnly)
-        for (int i = tid; i < D; i += NT) sm.wo[i] = p.ow ? p.ow[(size_t)h * p.w_stride + i] : 1.0f;
+        for (int i = threadIdx.x; i < D; i += G::NT) sm.wo[i] = p.ow ? p.ow[(size_t)h * p.w_stride + i] : 1.0f;
+    fill_rope_table(0, 0);
+    __syncthreads();
 
-    // ---- state slice in accumulator registers: S[c] = rows [32c, 32c+32), cols [32 wave, +32) ----
-    f32x16 S[NW];
-    {
-        const float* src = nullptr;
-        if (!kStateOnly)
-            src = (p.P > 1) ? p.ws + ((size_t)bh * p.P + seg) * dd
-                            : (p.state_in ? p.state_in + (size_t)bh * dd : nullptr);
-#pragma unroll
-        for (int c = 0; c < NW; ++c)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                S[c][r] = src ? src[(size_t)(32 * c + acc_row(r, lh)) * D + 32 * wave + lm] : 0.0f;
-    }
-
-    // ---- loop-invariant decay factors for this lane's accumulator elements ----
-    float mask_diag[16], mask_off[16], rs0[16], rs1[16];
-    if (!kStateOnly) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int m = acc_row(r, lh);
-            mask_diag[r] = (m >= lm) ? pow_lambda(l2l, m - lm) : 0.0f;  // D_ij, same 32-block
-            mask_off[r] = pow_lambda(l2l, 32 + m - lm);                  // D_ij, block below
-            rs0[r] = pow_lambda(l2l, m + 1);                             // lambda^(i+1), i < 32
-            rs1[r] = pow_lambda(l2l, 33 + m);                            // lambda^(i+1), i >= 32
-        }
-    }
-
-    // ---- register prefetch of one chunk's q/k/v ----
-    typename A::V rq[4][2], rk[4][2], rv[4][2];
-    const In* gq = static_cast<const In*>(p.q);
-    const In* gk = static_cast<const In*>(p.k);
-    const In* gv = static_cast<const In*>(p.v);
-    auto row_offset = [&](int t) { return ((size_t)((size_t)b * p.T + t) * p.H + h) * D; };
-    auto load_chunk = [&](int t0) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int t = t0 + 4 * rg + s;
-            if (t < t_end) {
-                const size_t o = row_offset(t) + 4 * fg;
-                if (!kStateOnly) {
-                    rq[s][0] = *reinterpret_cast<const typename A::V*>(gq + o);
-                    rq[s][1] = *reinterpret_cast<const typename A::V*>(gq + o + HALF);
-                }
-                rk[s][0] = *reinterpret_cast<const typename A::V*>(gk + o);
-                rk[s][1] = *reinterpret_cast<const typename A::V*>(gk + o + HALF);
-                rv[s][0] = *reinterpret_cast<const typename A::V*>(gv + o);
-                rv[s][1] = *reinterpret_cast<const typename A::V*>(gv + o + HALF);
-            } else {
-                rq[s][0] = rq[s][1] = rk[s][0] = rk[s][1] = rv[s][0] = rv[s][1] = A::zero();
-            }
-        }
-    };
-
-    // ---- prologue: registers -> normalised, rotated, decayed operand tiles in LDS ----
-    const float kscale = 1.0f / sqrtf((float)D);
-    auto prologue = [&](int t0, int n) {
-        float kd[8][4], vv[8][4];  // [feature][row] for the transposed stores
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int j = 4 * rg + s;
-            const bool valid = j < n;
-            float qa[8], ka[8], va[8];
-            if (!kStateOnly) {
-                A::widen(rq[s][0], qa);
-                A::widen(rq[s][1], qa + 4);
-            }
-            A::widen(rk[s][0], ka);
-            A::widen(rk[s][1], ka + 4);
-            A::widen(rv[s][0], va);
-            A::widen(rv[s][1], va + 4);
-            float ssq = 0.0f, ssk = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if (!kStateOnly) ssq += qa[i] * qa[i];
-                ssk += ka[i] * ka[i];
-            }
-#pragma unroll
-            for (int off = FG / 2; off >= 1; off >>= 1) {
-                if (!kStateOnly) ssq += __shfl_xor(ssq, off);
-                ssk += __shfl_xor(ssk, off);
-            }
-            const float rinv_q = rsqrtf(ssq * (1.0f / D) + p.eps);
-            const float rinv_k = rsqrtf(ssk * (1.0f / D) + p.eps) * kscale;
-            const int64_t pos = p.pos0 + t0 + j;
-            const float kdec = valid ? pow_lambda(l2l, n - 1 - j) : 0.0f;
-            float qt[8], kt[8];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                float cs, sn;
-                rope_cos_sin(pos, frev[u], cs, sn);
-                if (!kStateOnly) {
-                    const float x1 = qa[u] * rinv_q * wq[u], x2 = qa[4 + u] * rinv_q * wq[4 + u];
-                    qt[u] = x1 * cs - x2 * sn;
-                    qt[4 + u] = x2 * cs + x1 * sn;
-                }
-                const float y1 = ka[u] * rinv_k * wk[u], y2 = ka[4 + u] * rinv_k * wk[4 + u];
-                kt[u] = y1 * cs - y2 * sn;
-                kt[4 + u] = y2 * cs + y1 * sn;
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if (!valid) {
-                    qt[i] = 0.0f;
-                    kt[i] = 0.0f;
-                    va[i] = 0.0f;
-                }
-                kd[i][s] = kt[i] * kdec;
-                vv[i][s] = va[i];
-            }
-            if (!kStateOnly) {
-                E* qdst = sm.u.qk.q + j * QS;
-                E* kdst = sm.u.qk.k + j * QS;
-                st4(qdst + 4 * fg, qt[0], qt[1], qt[2], qt[3]);
-                st4(qdst + HALF + 4 * fg, qt[4], qt[5], qt[6], qt[7]);
-                st4(kdst + 4 * fg, kt[0], kt[1], kt[2], kt[3]);
-                st4(kdst + HALF + 4 * fg, kt[4], kt[5], kt[6], kt[7]);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int f = (i < 4) ? 4 * fg + i : HALF + 4 * fg + (i - 4);
-            if constexpr (M::kSplit) {
-                float hi[4], lo[4];
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    hi[s] = (float)to_bf16(kd[i][s]);
-                    lo[s] = kd[i][s] - hi[s];
-                }
-                st4(sm.khT + f * TS + 4 * rg, hi[0], hi[1], hi[2], hi[3]);
-                st4(sm.klT + f * TS + 4 * rg, lo[0], lo[1], lo[2], lo[3]);
-            } else {
-                st4(sm.khT + f * TS + 4 * rg, kd[i][0], kd[i][1], kd[i][2], kd[i][3]);
-            }
-            st4(sm.vT + f * TS + 4 * rg, vv[i][0], vv[i][1], vv[i][2], vv[i][3]);
-        }
-    };
-
-    // ---- epilogue mapping: row er, value columns [32 ec, 32 ec + 32) ----
-    const int er = tid / NW, ec = tid % NW;
-    constexpr int GV = (sizeof(In) == 2) ? 4 : 8;  // 16-byte vectors per 32 activations
-    uint4 rg_gate[GV];
-    const In* gg = static_cast<const In*>(p.g);
-
-    const int n_chunks = (t_end - t_begin + C - 1) / C;
-    load_chunk(t_begin);
-    for (int ci = 0; ci < n_chunks; ++ci) {
-        const int t0 = t_begin + ci * C;
-        const int n = min(C, t_end - t0);
-        prologue(t0, n);
-        __syncthreads();
-        if (!kStateOnly) {
-            if (er < n) {
-                const uint4* src = reinterpret_cast<const uint4*>(gg + row_offset(t0 + er) + 32 * ec);
-#pragma unroll
-                for (int i = 0; i < GV; ++i) rg_gate[i] = src[i];
-            } else {
-#pragma unroll
-                for (int i = 0; i < GV; ++i) rg_gate[i] = make_uint4(0u, 0u, 0u, 0u);
-            }
-        }
-        if (ci + 1 < n_chunks) load_chunk(t0 + C);
-
-        if (!kStateOnly) {
-            // (1) decayed causal scores P = (Q~ K~^T) (.) D for the 3 non-empty 32x32 tiles
-            for (int ti = wave; ti < 3; ti += NW) {
-                const int ta = (ti == 0) ? 0 : 1, tb = (ti == 2) ? 1 : 0;
-                f32x16 acc = {};
-                contract_rows<D>(acc, sm.u.qk.q + (32 * ta + lm) * QS, sm.u.qk.k + (32 * tb + lm) * QS, lh);
-                if (ta == tb) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[r] *= mask_diag[r];
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[r] *= mask_off[r];
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    sm.p[(32 * ta + acc_row(r, lh)) * TS + 32 * tb + lm] = (E)acc[r];
-            }
-        }
-
-        f32x16 O[2];
-        if (!kStateOnly) {
-            // (2) inter-chunk term: O = diag(lambda^(i+1)) Q~ S_prev, B operand from registers
-#pragma unroll
-            for (int a = 0; a < 2; ++a) {
-                O[a] = f32x16{};
-                const E* qrow = sm.u.qk.q + (32 * a + lm) * QS;
-#pragma unroll
-                for (int c = 0; c < NW; ++c) contract_state(O[a], qrow + 32 * c, S[c], lh);
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                O[0][r] *= rs0[r];
-                O[1][r] *= rs1[r];
-            }
-        }
-        __syncthreads();  // P complete
-
-        const E* vrow = sm.vT + (32 * wave + lm) * TS;
-        if (!kStateOnly) {
-            // (3) intra-chunk term: O += P V (causal: block row 0 only needs token block 0)
-            contract_rows<32>(O[0], sm.p + lm * TS, vrow, lh);
-            contract_rows<64>(O[1], sm.p + (32 + lm) * TS, vrow, lh);
-        }
-
-        // (4) state update: S <- lambda^n S + K'^T V  (K' carries lambda^(n-1-j) per token j)
+    if (is_math) {
+        // ============================ math wavefronts ============================
+        const int w = wave;
+        f32x16 S[NW];  // S[c]: key rows [32c, 32c+32), value columns [32w, 32w+32)
         {
-            const float carry = pow_lambda(l2l, n);
+            const float* src = nullptr;
+            if (!kStateOnly)
+                src = (p.P > 1) ? p.ws + ((size_t)bh * p.P + seg) * dd
+                                : (p.state_in ? p.state_in + (size_t)bh * dd : nullptr);
 #pragma unroll
             for (int c = 0; c < NW; ++c)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) S[c][r] *= carry;
+                for (int r = 0; r < 16; ++r)
+                    S[c][r] = src ? src[(size_t)(32 * c + acc_row(r, lh)) * D + 32 * w + lm] : 0.0f;
+        }
+        // decay factors of this lane's accumulator elements
+        float mask[16], rsc[16];
 #pragma unroll
-            for (int c = 0; c < NW; ++c) {
-                contract_rows<C>(S[c], sm.khT + (32 * c + lm) * TS, vrow, lh);
-                if constexpr (M::kSplit) contract_rows<C>(S[c], sm.klT + (32 * c + lm) * TS, vrow, lh);
+        for (int r = 0; r < 16; ++r) {
+            const int m = acc_row(r, lh);
+            mask[r] = (lm >= m) ? pow_lambda(l2l, lm - m) : 0.0f;  // P^T[j = m][i = lm]
+            rsc[r] = pow_lambda(l2l, m + 1);                       // lambda^(i+1), i = m
+        }
+        const float lam_full = pow_lambda(l2l, C);
+
+        using L = Layout<M>;
+        const int vsw = L::tsw(32 * w + lm);
+        auto compute = [&](int chunk, const Tiles<M, D, kStateOnly>& t, float* o_stage) {
+            const int n = min(C, t_end - (t_begin + chunk * C));
+            const float carry = (n == C) ? lam_full : pow_lambda(l2l, n);
+            const E* vrow = t.vT + (32 * w + lm) * TS;
+            if constexpr (M::kSplit) {
+                // bf16 operands.  With the kpos placement the 16-byte block at 16 s + 8 lh of a
+                // q~ row is both the B operand of the scores (natural k) and the A operand of the
+                // query-state product (k in accumulator order), so one read feeds both and the
+                // two accumulation chains interleave.
+                f32x16 pt = {}, o = {};
+                if (!kStateOnly) {
+                    const E* qrow = t.q + lm * QS;
+                    const E* krow = t.k + lm * QS;
+#pragma unroll
+                    for (int s8 = 0; s8 < D / 16; ++s8) {
+                        const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qrow + 16 * s8 + 8 * lh);
+                        const bf16x8 kv = *reinterpret_cast<const bf16x8*>(krow + 16 * s8 + 8 * lh);
+                        bf16x8 sv;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) sv[e] = to_bf16(S[s8 / 2][8 * (s8 % 2) + e]);
+                        pt = mfma_bf16(kv, qv, pt);  // P^T[j][i] += k~_j . q~_i
+                        o = mfma_bf16(qv, sv, o);    // O[i][v]   += q~_i . S[:, v]
+                    }
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        pt[r] *= mask[r];
+                        o[r] *= rsc[r];
+                    }
+                }
+                // P V and the state update read the same V blocks
+                bf16x8 vb[2];
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+                    vb[st] = *reinterpret_cast<const bf16x8*>(vrow + ((16 * st + 8 * lh) ^ vsw));
+                if (!kStateOnly) {
+#pragma unroll
+                    for (int st = 0; st < 2; ++st) {
+                        bf16x8 pv;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) pv[e] = to_bf16(pt[8 * st + e]);
+                        o = mfma_bf16(pv, vb[st], o);  // O[i][v] += P[i][:] V[:, v]
+                    }
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o_stage[acc_row(r, lh) * OS + 32 * w + lm] = o[r];
+                }
+                // state update S <- lambda^n S + K'^T V, the NW accumulators interleaved
+#pragma unroll
+                for (int c = 0; c < NW; ++c)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) S[c][r] *= carry;
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    bf16x8 ah[NW], al[NW];
+#pragma unroll
+                    for (int c = 0; c < NW; ++c) {
+                        const int off = (32 * c + lm) * TS + ((16 * st + 8 * lh) ^ L::tsw(32 * c + lm));
+                        ah[c] = *reinterpret_cast<const bf16x8*>(t.khT + off);
+                        al[c] = *reinterpret_cast<const bf16x8*>(t.klT + off);
+                    }
+#pragma unroll
+                    for (int c = 0; c < NW; ++c) S[c] = mfma_bf16(ah[c], vb[st], S[c]);
+#pragma unroll
+                    for (int c = 0; c < NW; ++c) S[c] = mfma_bf16(al[c], vb[st], S[c]);
+                }
+            } else {
+                // fp32 operands (v_mfma_f32_32x32x2_f32)
+                if (!kStateOnly) {
+                    // P^T[j][i] = (k~_j . q~_i) lambda^(i-j) for j <= i
+                    f32x16 pt = {};
+                    contract_rows<D>(pt, t.k + lm * QS, t.q + lm * QS, lh);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) pt[r] *= mask[r];
+                    // inter-chunk term diag(lambda^(i+1)) Q~ S, B operand from the state registers
+                    f32x16 o = {};
+#pragma unroll
+                    for (int c = 0; c < NW; ++c) contract_acc(o, S[c], t.q + lm * QS + 32 * c, lh, false);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[r] *= rsc[r];
+                    // intra-chunk term P V, A operand from the score registers
+                    contract_acc(o, pt, vrow, lh, true, vsw);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o_stage[acc_row(r, lh) * OS + 32 * w + lm] = o[r];
+                }
+#pragma unroll
+                for (int c = 0; c < NW; ++c)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) S[c][r] *= carry;
+#pragma unroll
+                for (int c = 0; c < NW; ++c)
+                    contract_rows<C>(S[c], t.khT + (32 * c + lm) * TS, vrow, lh, L::tsw(32 * c + lm), vsw);
+            }
+        };
+
+        if constexpr (kOverlap) {
+            // step s: math processes chunk s-1 (steps 1 .. n_chunks); io runs ahead/behind
+            for (int s = 0; s < n_steps; ++s) {
+                if (s >= 1 && s <= n_chunks)
+                    compute(s - 1, sm.buf[(s - 1) & 1], kStateOnly ? nullptr : sm.o + ((s - 1) & 1) * C * OS);
+                __syncthreads();
+            }
+        } else {
+            for (int s = 0; s < n_chunks; ++s) {
+                __syncthreads();  // chunk s in LDS
+                compute(s, sm.buf[0], kStateOnly ? nullptr : sm.o);
+                __syncthreads();  // tiles consumed, output staged
             }
         }
 
-        if (!kStateOnly) {
-            __syncthreads();  // q~/k~ tiles consumed; their space becomes the output stage
+        float* dst = nullptr;
+        if (kStateOnly)
+            dst = p.ws + ((size_t)bh * p.P + seg) * dd;
+        else if (seg == p.P - 1 && p.state_out)
+            dst = p.state_out + (size_t)bh * dd;
+        if (dst) {
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
+            for (int c = 0; c < NW; ++c)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    sm.u.o[(32 * a + acc_row(r, lh)) * OS + 32 * wave + lm] = O[a][r];
-            __syncthreads();
+                    dst[(size_t)(32 * c + acc_row(r, lh)) * D + 32 * w + lm] = S[c][r];
+        }
+    } else {
+        // ============================= io wavefronts =============================
+        const In* gq = static_cast<const In*>(p.q) + head_base;
+        const In* gk = static_cast<const In*>(p.k) + head_base;
+        const In* gv = static_cast<const In*>(p.v) + head_base;
+        const In* gg = static_cast<const In*>(p.g) + head_base;
+        In* gy = static_cast<In*>(p.y) + head_base;
 
-            // (5) epilogue: y = RMSNorm(o) * w_o * sigmoid(g), one row per NW threads
-            float o[32];
-            const float* orow = sm.u.o + er * OS + 32 * ec;
+        float wq[8], wk[8];
+        {
+            const float* pq = p.qw + (size_t)h * p.w_stride;
+            const float* pk = p.kw + (size_t)h * p.w_stride;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                wq[u] = pq[4 * fg + u];
+                wq[4 + u] = pq[HALF + 4 * fg + u];
+                wk[u] = pk[4 * fg + u];
+                wk[4 + u] = pk[HALF + 4 * fg + u];
+            }
+        }
+        // cos/sin(j f_i) for this thread's two rows j = 2 rg + s and four frequencies
+        float2 rot[2][4];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float cs, sn;
+                rope_cos_sin(2 * rg + s, p.inv_freq_rev[4 * fg + u], cs, sn);
+                rot[s][u] = make_float2(cs, sn);
+            }
+        const float kscale = 1.0f / sqrtf((float)D);
+
+        struct Regs {
+            V4 q[2][2], k[2][2], v[2][2];  // [row s][half]
+        };
+        // Loads are unconditional (rows past the segment end re-read its last row and are zeroed
+        // by the prologue), which keeps the memory-wait bookkeeping exact across iterations.
+        // Row addresses: a uniform per-chunk base plus a 32-bit per-lane offset.
+        const uint32_t rs32 = (uint32_t)row_stride;
+        auto chunk_start = [&](int chunk) { return t_begin + min(chunk, n_chunks - 1) * C; };
+        auto load = [&](int chunk, Regs& r) {
+            const int cs = chunk_start(chunk);
+            const size_t cb = (size_t)cs * row_stride;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const uint32_t o = (uint32_t)min(2 * rg + s, t_end - 1 - cs) * rs32 + 4 * fg;
+                if (!kStateOnly) {
+                    r.q[s][0] = *reinterpret_cast<const V4*>(gq + cb + o);
+                    r.q[s][1] = *reinterpret_cast<const V4*>(gq + cb + o + HALF);
+                }
+                r.k[s][0] = *reinterpret_cast<const V4*>(gk + cb + o);
+                r.k[s][1] = *reinterpret_cast<const V4*>(gk + cb + o + HALF);
+                r.v[s][0] = *reinterpret_cast<const V4*>(gv + cb + o);
+                r.v[s][1] = *reinterpret_cast<const V4*>(gv + cb + o + HALF);
+            }
+        };
+
+        // prologue of one chunk: registers -> normalised, rotated, decayed tiles in LDS
+        auto prologue = [&](int chunk, const Regs& r, Tiles<M, D, kStateOnly>& t) {
+            const int n = min(C, t_end - (t_begin + chunk * C));
+            const float2* base = sm.rope[chunk & 1];
+            float2 b4[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) b4[u] = base[4 * fg + u];
+            float kd[2][8];  // decayed keys [row][feature slot]
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int j = 2 * rg + s;
+                const bool valid = j < n;
+                float qa[8], ka[8];
+                if (!kStateOnly) {
+                    A::widen(r.q[s][0], qa);
+                    A::widen(r.q[s][1], qa + 4);
+                }
+                A::widen(r.k[s][0], ka);
+                A::widen(r.k[s][1], ka + 4);
+                float ssq = 0.0f, ssk = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    if (!kStateOnly) ssq = fmaf(qa[i], qa[i], ssq);
+                    ssk = fmaf(ka[i], ka[i], ssk);
+                }
+                if (!kStateOnly) ssq = group_sum<FG>(ssq);
+                ssk = group_sum<FG>(ssk);
+                // Rows past the segment end hold a copy of its last row; a zero scale makes their
+                // q~, k~ and decayed keys zero, so they add nothing to scores, outputs or state.
+                const float rq = valid ? fast_rsqrt(ssq * (1.0f / D) + p.eps) : 0.0f;
+                const float rk = valid ? fast_rsqrt(ssk * (1.0f / D) + p.eps) * kscale : 0.0f;
+                const float kdec = valid ? pow_lambda(l2l, n - 1 - j) : 0.0f;
+                float qt[8], kt[8];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    // angle (p0 + j) f = p0 f + j f
+                    const float cs = b4[u].x * rot[s][u].x - b4[u].y * rot[s][u].y;
+                    const float sn = b4[u].y * rot[s][u].x + b4[u].x * rot[s][u].y;
+                    if (!kStateOnly) {
+                        const float x1 = qa[u] * wq[u] * rq, x2 = qa[4 + u] * wq[4 + u] * rq;
+                        qt[u] = x1 * cs - x2 * sn;
+                        qt[4 + u] = x2 * cs + x1 * sn;
+                    }
+                    const float y1 = ka[u] * wk[u] * rk, y2 = ka[4 + u] * wk[4 + u] * rk;
+                    kt[u] = y1 * cs - y2 * sn;
+                    kt[4 + u] = y2 * cs + y1 * sn;
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) kd[s][i] = kt[i] * kdec;
+                if (!kStateOnly) {
+                    const int c0 = Layout<M>::kpos(4 * fg);
+                    E* qdst = t.q + j * QS;
+                    E* kdst = t.k + j * QS;
+                    st4(qdst + c0, qt[0], qt[1], qt[2], qt[3]);
+                    st4(qdst + HALF + c0, qt[4], qt[5], qt[6], qt[7]);
+                    st4(kdst + c0, kt[0], kt[1], kt[2], kt[3]);
+                    st4(kdst + HALF + c0, kt[4], kt[5], kt[6], kt[7]);
+                }
+            }
+            const int jp = Layout<M>::kpos(2 * rg);  // the two tokens stay adjacent
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                float4 x = *reinterpret_cast<const float4*>(orow + 4 * i);
+                const int f = (i < 4) ? 4 * fg + i : HALF + 4 * fg + (i - 4);
+                const int col = f * TS + (jp ^ Layout<M>::tsw(f));
+                if constexpr (M::kSplit) {
+                    // hi = bf16(k'), lo = bf16(k' - hi), two tokens per instruction
+                    const uint32_t hi = pack_bf16x2(kd[0][i], kd[1][i]);
+                    const float lo0 = kd[0][i] - bf16_lo(hi), lo1 = kd[1][i] - bf16_hi(hi);
+                    *reinterpret_cast<uint32_t*>(t.khT + col) = hi;
+                    *reinterpret_cast<uint32_t*>(t.klT + col) = pack_bf16x2(lo0, lo1);
+                } else {
+                    st2(t.khT + col, kd[0][i], kd[1][i]);
+                }
+                st_pair(t.vT + col, r.v[0][i / 4], r.v[1][i / 4], i % 4);
+            }
+        };
+
+        // epilogue of one chunk: y = RMSNorm(o) * w_o * sigmoid(g)
+        constexpr int GV = EPT * sizeof(In) / 16;  // 16-byte vectors of gate logits per thread
+        auto load_gate = [&](int chunk, uint4* gr) {
+            const int cs = chunk_start(chunk);
+            const uint32_t o = (uint32_t)min(er, t_end - 1 - cs) * rs32 + EPT * ec;
+            const uint4* src = reinterpret_cast<const uint4*>(gg + (size_t)cs * row_stride + o);
+#pragma unroll
+            for (int i = 0; i < GV; ++i) gr[i] = src[i];
+        };
+        auto epilogue = [&](int chunk, const float* o_stage, const uint4* gr) {
+            const int t = t_begin + chunk * C + er;
+            float o[EPT];
+            const float* orow = o_stage + er * OS + EPT * ec;
+#pragma unroll
+            for (int i = 0; i < EPT / 4; ++i) {
+                const float4 x = *reinterpret_cast<const float4*>(orow + 4 * i);
                 o[4 * i] = x.x; o[4 * i + 1] = x.y; o[4 * i + 2] = x.z; o[4 * i + 3] = x.w;
             }
             float ss = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 32; ++i) ss += o[i] * o[i];
+            for (int i = 0; i < EPT; ++i) ss = fmaf(o[i], o[i], ss);
+            ss = group_sum<TPR>(ss);
+            const float rinv = fast_rsqrt(ss * (1.0f / D) + p.eps);
+            if (t >= t_end) return;
+            float gl[EPT];
+            if constexpr (sizeof(In) == 2) {
 #pragma unroll
-            for (int off = NW / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-            const float rinv = rsqrtf(ss * (1.0f / D) + p.eps);
-            if (er < n) {
-                float gl[32];
-                if constexpr (sizeof(In) == 2) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const uint4 x = rg_gate[i];
-                        gl[8 * i + 0] = bf16_lo(x.x); gl[8 * i + 1] = bf16_hi(x.x);
-                        gl[8 * i + 2] = bf16_lo(x.y); gl[8 * i + 3] = bf16_hi(x.y);
-                        gl[8 * i + 4] = bf16_lo(x.z); gl[8 * i + 5] = bf16_hi(x.z);
-                        gl[8 * i + 6] = bf16_lo(x.w); gl[8 * i + 7] = bf16_hi(x.w);
-                    }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const uint4 x = rg_gate[i];
-                        gl[4 * i + 0] = __uint_as_float(x.x); gl[4 * i + 1] = __uint_as_float(x.y);
-                        gl[4 * i + 2] = __uint_as_float(x.z); gl[4 * i + 3] = __uint_as_float(x.w);
-                    }
+                for (int i = 0; i < GV; ++i) {
+                    const uint4 x = gr[i];
+                    gl[8 * i + 0] = bf16_lo(x.x); gl[8 * i + 1] = bf16_hi(x.x);
+                    gl[8 * i + 2] = bf16_lo(x.y); gl[8 * i + 3] = bf16_hi(x.y);
+                    gl[8 * i + 4] = bf16_lo(x.z); gl[8 * i + 5] = bf16_hi(x.z);
+                    gl[8 * i + 6] = bf16_lo(x.w); gl[8 * i + 7] = bf16_hi(x.w);
                 }
-                float yv[32];
+            } else {
 #pragma unroll
-                for (int i = 0; i < 32; ++i)
-                    yv[i] = o[i] * rinv * sm.wo[32 * ec + i] * sigmoidf_(gl[i]);
-                const size_t off = row_offset(t0 + er) + 32 * ec;
-                if constexpr (sizeof(In) == 2) {
-                    uint4* dst = reinterpret_cast<uint4*>(static_cast<In*>(p.y) + off);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        dst[i] = make_uint4(pack_bf16x2(yv[8 * i], yv[8 * i + 1]),
-                                            pack_bf16x2(yv[8 * i + 2], yv[8 * i + 3]),
-                                            pack_bf16x2(yv[8 * i + 4], yv[8 * i + 5]),
-                                            pack_bf16x2(yv[8 * i + 6], yv[8 * i + 7]));
-                } else {
-                    float4* dst = reinterpret_cast<float4*>(static_cast<In*>(p.y) + off);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        dst[i] = make_float4(yv[4 * i], yv[4 * i + 1], yv[4 * i + 2], yv[4 * i + 3]);
-                }
-                if (p.o_raw) {
-                    float4* dst = reinterpret_cast<float4*>(p.o_raw + off);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        dst[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+                for (int i = 0; i < GV; ++i) {
+                    const uint4 x = gr[i];
+                    gl[4 * i + 0] = __uint_as_float(x.x); gl[4 * i + 1] = __uint_as_float(x.y);
+                    gl[4 * i + 2] = __uint_as_float(x.z); gl[4 * i + 3] = __uint_as_float(x.w);
                 }
             }
-        }
-        __syncthreads();  // LDS tiles free for the next chunk's prologue
-    }
+            float yv[EPT];
+            if (p.ow) {
+#pragma unroll
+                for (int i = 0; i < EPT; ++i) yv[i] = o[i] * (rinv * sm.wo[EPT * ec + i]) * sigmoidf_(gl[i]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < EPT; ++i) yv[i] = o[i] * rinv * sigmoidf_(gl[i]);
+            }
+            const size_t off = (size_t)(t - er) * row_stride + ((uint32_t)er * rs32 + EPT * ec);
+            if constexpr (sizeof(In) == 2) {
+                uint4* dst = reinterpret_cast<uint4*>(gy + off);
+#pragma unroll
+                for (int i = 0; i < GV; ++i)
+                    dst[i] = make_uint4(pack_bf16x2(yv[8 * i], yv[8 * i + 1]),
+                                        pack_bf16x2(yv[8 * i + 2], yv[8 * i + 3]),
+                                        pack_bf16x2(yv[8 * i + 4], yv[8 * i + 5]),
+                                        pack_bf16x2(yv[8 * i + 6], yv[8 * i + 7]));
+            } else {
+                float4* dst = reinterpret_cast<float4*>(gy + off);
+#pragma unroll
+                for (int i = 0; i < GV; ++i)
+                    dst[i] = make_float4(yv[4 * i], yv[4 * i + 1], yv[4 * i + 2], yv[4 * i + 3]);
+            }
+            if (p.o_raw) {
+                float4* dst = reinterpret_cast<float4*>(p.o_raw + head_base + off);
+#pragma unroll
+                for (int i = 0; i < EPT / 4; ++i)
+                    dst[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+            }
+        };
 
-    // ---- write the state slice: segment end state (state-only pass) or the final state ----
-    float* dst = nullptr;
-    if (kStateOnly)
-        dst = p.ws + ((size_t)bh * p.P + seg) * dd;
-    else if (seg == p.P - 1 && p.state_out)
-        dst = p.state_out + (size_t)bh * dd;
-    if (dst) {
+        if constexpr (kOverlap) {
+            // PF register sets hold the q/k/v (and gate logits) of the next PF chunks, so each load
+            // is issued PF steps before its use; the step loop is unrolled by PF so the sets stay
+            // static registers.
+            Regs rs[PF];
+            uint4 gs[PF][GV];
 #pragma unroll
-        for (int c = 0; c < NW; ++c)
+            for (int i = 0; i < PF; ++i) {
+                load(i, rs[i]);
+                if (!kStateOnly) load_gate(i, gs[i]);
+            }
+            auto step = [&](int s, Regs& cur, uint4* gep) {
+                if (s < n_chunks) prologue(s, cur, sm.buf[s & 1]);
+                load(s + PF, cur);
+                if (s + 1 < n_chunks) fill_rope_table(s + 1, (s + 1) & 1);
+                if (!kStateOnly && s >= 2) {
+                    epilogue(s - 2, sm.o + (s & 1) * C * OS, gep);
+                    load_gate(s - 2 + PF, gep);
+                }
+                __syncthreads();
+            };
+            // (the first round is peeled so the loop header sees the same in-flight loads from
+            // both of its predecessors and waits only for the chunk it consumes)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                dst[(size_t)(32 * c + acc_row(r, lh)) * D + 32 * wave + lm] = S[c][r];
+            for (int i = 0; i < PF; ++i) step(i, rs[i], gs[(i + PF - 2) % PF]);
+            for (int s0 = PF; s0 < n_steps; s0 += PF) {
+#pragma unroll
+                for (int i = 0; i < PF; ++i) step(s0 + i, rs[i], gs[(i + PF - 2) % PF]);
+            }
+        } else {
+            Regs ra;
+            uint4 ga[GV];
+            for (int s = 0; s < n_chunks; ++s) {
+                load(s, ra);
+                if (!kStateOnly) load_gate(s, ga);
+                prologue(s, ra, sm.buf[0]);
+                if (s + 1 < n_chunks) fill_rope_table(s + 1, (s + 1) & 1);
+                __syncthreads();  // chunk s in LDS
+                __syncthreads();  // math done with chunk s
+                if (!kStateOnly) epilogue(s, sm.o, ga);
+            }
+        }
     }
 }
 
@@ -520,15 +700,16 @@ template <class M, int D>
 hipError_t launch_typed(const ChunkParams& cp, const ScanParams& sp, const hipEvent_t ev[2],
                         hipStream_t stream) {
     const int BH = cp.B * cp.H;
+    constexpr int NT = 128 * (D / 32);
     if (cp.P > 1) {
-        chunk_kernel<M, D, true><<<dim3(BH * (cp.P - 1)), dim3(2 * D), 0, stream>>>(cp);
+        chunk_kernel<M, D, true, kPrefetchStateOnly><<<dim3(BH * (cp.P - 1)), dim3(NT), 0, stream>>>(cp);
         const size_t n = (size_t)BH * D * D;
         segment_scan_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(sp);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (ev[0] && (err = hipEventRecord(ev[0], stream)) != hipSuccess) return err;
-    chunk_kernel<M, D, false><<<dim3(BH * cp.P), dim3(2 * D), 0, stream>>>(cp);
+    chunk_kernel<M, D, false, kPrefetchMain><<<dim3(BH * cp.P), dim3(NT), 0, stream>>>(cp);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev[1] && (err = hipEventRecord(ev[1], stream)) != hipSuccess) return err;
     return hipSuccess;

@@ -78,21 +78,22 @@ def test_hypenet_gamma_time_scales():
     (1, 32768, 16, 128, 16),
     (4, 131072, 32, 128, 2),
     (64, 4096, 16, 128, 1),      # B*H already fills the CUs
-    (1, 256, 2, 64, 1),          # too short to split (4 chunks)
+    (1, 256, 2, 64, 1),          # too short to split (8 chunks)
     (1, 300, 1, 128, 1),
-    (1, 4096, 1, 128, 16),       # 64 chunks, 4 per segment
+    (1, 4096, 1, 128, 16),       # 128 chunks, 8 per segment
+    (2, 100000, 2, 64, 64),      # 3125 chunks over 64 segments
 ])
 def test_plan_and_workspace(B, T, H, d, expect_p):
     c, p = lt.lightning_prefill_plan(B, T, H, d)
-    assert c == 64 and p == expect_p
+    assert c == 32 and p == expect_p
     ws = lt.lightning_prefill_workspace_size(B, T, H, d)
     assert ws == (B * H * p * d * d * 4 if p > 1 else 0)
 
 
 def test_plan_explicit_segments_and_chunk():
-    assert lt.lightning_prefill_plan(1, 1000, 2, 128, segments=3) == (64, 3)
+    assert lt.lightning_prefill_plan(1, 1000, 2, 128, segments=3) == (32, 3)
     # more segments than chunks collapses to one chunk per segment
-    assert lt.lightning_prefill_plan(1, 100, 2, 128, segments=50) == (64, 2)
+    assert lt.lightning_prefill_plan(1, 100, 2, 128, segments=50) == (32, 4)
     with pytest.raises(lt.LightningError) as e:
         lt.lightning_prefill_plan(1, 1000, 2, 128, chunk=48)
     assert e.value.status == lt.LT_ERR_UNSUPPORTED
@@ -150,7 +151,7 @@ PREFILL_BAD = [
     ("rope_base_inf", dict(base=float("inf")), lt.LT_ERR_INVALID_ARG),
     ("eps_negative", dict(eps=-1e-6), lt.LT_ERR_INVALID_ARG),
     ("pos0_negative", dict(pos0=-1), lt.LT_ERR_INVALID_ARG),
-    ("chunk_unsupported", dict(chunk=32), lt.LT_ERR_UNSUPPORTED),
+    ("chunk_unsupported", dict(chunk=48), lt.LT_ERR_UNSUPPORTED),
     ("workspace_missing", dict(T=524288, H=16, lam=[0.9] * 16), lt.LT_ERR_WORKSPACE),
     ("workspace_small", dict(T=524288, H=16, lam=[0.9] * 16, ws=FAKE, wsb=1024), lt.LT_ERR_WORKSPACE),
     ("workspace_misaligned", dict(T=524288, H=16, lam=[0.9] * 16, ws=FAKE + 8, wsb=1 << 30),
