@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--decode-buffers", type=int, default=8,
                     help="rotating state buffers (64 MiB each) so the step cannot run from MALL")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=524288)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     return ap.parse_args()

@@ -111,7 +111,8 @@ struct Smem {
     using G = Cfg<M, D, kStateOnly>;
     Tiles<M, D, kStateOnly> buf[G::NBUF];
     float o[kStateOnly ? 1 : G::NBUF * C * G::OS];  // o before the output norm [token][value dim]
-    float2 rope[2][64];                             // cos/sin(p0 f_i) of the next two chunks
+    float2 rope[2][65];                             // cos/sin(p0 f_i) of the next two chunks
+                                                    // (entry 64: write sink of idle lanes)
     float wo[D];
 };
 
@@ -263,15 +264,15 @@ __global__ void __launch_bounds__(128 * (D / 32)) chunk_kernel(const ChunkParams
     // (The frequency is read once: a dynamically indexed kernel-argument read is a vector memory
     // load, and waiting for it inside the loop would also wait for the prefetches.)
     constexpr int FPW = HALF / NW;  // frequencies per io wave
-    const int table_i = (wave - NW) * FPW + lane;
+    // Every lane computes (no divergent branch in the loop); lanes without a frequency write to
+    // the sink entry.
     const bool table_lane = wave >= NW && lane < FPW;
-    const double table_frev = table_lane ? p.inv_freq_rev[table_i] : 0.0;
+    const int table_i = table_lane ? (wave - NW) * FPW + lane : 64;
+    const double table_frev = p.inv_freq_rev[table_lane ? table_i : 0];
     auto fill_rope_table = [&](int chunk, int slot) {
-        if (table_lane) {
-            float cs, sn;
-            rope_cos_sin(p.pos0 + t_begin + (int64_t)chunk * C, table_frev, cs, sn);
-            sm.rope[slot][table_i] = make_float2(cs, sn);
-        }
+        float cs, sn;
+        rope_cos_sin(p.pos0 + t_begin + (int64_t)chunk * C, table_frev, cs, sn);
+        sm.rope[slot][table_i] = make_float2(cs, sn);
     };
 
     if (!kStateOnly)
@@ -569,7 +570,7 @@ __global__ void __launch_bounds__(128 * (D / 32)) chunk_kernel(const ChunkParams
 #pragma unroll
             for (int i = 0; i < GV; ++i) gr[i] = src[i];
         };
-        auto epilogue = [&](int chunk, const float* o_stage, const uint4* gr) {
+        auto epilogue = [&](int chunk, const float* o_stage, const uint4* gr, bool full) {
             const int t = t_begin + chunk * C + er;
             float o[EPT];
             const float* orow = o_stage + er * OS + EPT * ec;
@@ -583,7 +584,7 @@ __global__ void __launch_bounds__(128 * (D / 32)) chunk_kernel(const ChunkParams
             for (int i = 0; i < EPT; ++i) ss = fmaf(o[i], o[i], ss);
             ss = group_sum<TPR>(ss);
             const float rinv = fast_rsqrt(ss * (1.0f / D) + p.eps);
-            if (t >= t_end) return;
+            if (!full && t >= t_end) return;
             float gl[EPT];
             if constexpr (sizeof(In) == 2) {
 #pragma unroll
@@ -602,14 +603,9 @@ __global__ void __launch_bounds__(128 * (D / 32)) chunk_kernel(const ChunkParams
                     gl[4 * i + 2] = __uint_as_float(x.z); gl[4 * i + 3] = __uint_as_float(x.w);
                 }
             }
-            float yv[EPT];
-            if (p.ow) {
+            float yv[EPT];  // (w_o holds ones when the output norm has no weight)
 #pragma unroll
-                for (int i = 0; i < EPT; ++i) yv[i] = o[i] * (rinv * sm.wo[EPT * ec + i]) * sigmoidf_(gl[i]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < EPT; ++i) yv[i] = o[i] * rinv * sigmoidf_(gl[i]);
-            }
+            for (int i = 0; i < EPT; ++i) yv[i] = o[i] * (rinv * sm.wo[EPT * ec + i]) * sigmoidf_(gl[i]);
             const size_t off = (size_t)(t - er) * row_stride + ((uint32_t)er * rs32 + EPT * ec);
             if constexpr (sizeof(In) == 2) {
                 uint4* dst = reinterpret_cast<uint4*>(gy + off);
@@ -644,23 +640,32 @@ __global__ void __launch_bounds__(128 * (D / 32)) chunk_kernel(const ChunkParams
                 load(i, rs[i]);
                 if (!kStateOnly) load_gate(i, gs[i]);
             }
-            auto step = [&](int s, Regs& cur, uint4* gep) {
-                if (s < n_chunks) prologue(s, cur, sm.buf[s & 1]);
+            // `steady`: 2 <= s and s + 1 < n_chunks, so every part of the step runs and the chunk
+            // being stored is full; the step then has no branches and the scheduler can interleave
+            // the prologue of chunk s with the epilogue of chunk s-2.
+            auto step = [&](int s, Regs& cur, uint4* gep, bool steady) {
+                if (steady || s < n_chunks) prologue(s, cur, sm.buf[s & 1]);
                 load(s + PF, cur);
-                if (s + 1 < n_chunks) fill_rope_table(s + 1, (s + 1) & 1);
-                if (!kStateOnly && s >= 2) {
-                    epilogue(s - 2, sm.o + (s & 1) * C * OS, gep);
+                if (steady || s + 1 < n_chunks) fill_rope_table(s + 1, (s + 1) & 1);
+                if (!kStateOnly && (steady || s >= 2)) {
+                    epilogue(s - 2, sm.o + (s & 1) * C * OS, gep, steady);
                     load_gate(s - 2 + PF, gep);
                 }
                 __syncthreads();
             };
-            // (the first round is peeled so the loop header sees the same in-flight loads from
-            // both of its predecessors and waits only for the chunk it consumes)
+            // The first round is peeled (the loop header then sees the same in-flight loads from
+            // both of its predecessors and waits only for the chunk it consumes), steady rounds
+            // follow, and the remaining rounds handle the pipeline drain.
 #pragma unroll
-            for (int i = 0; i < PF; ++i) step(i, rs[i], gs[(i + PF - 2) % PF]);
-            for (int s0 = PF; s0 < n_steps; s0 += PF) {
+            for (int i = 0; i < PF; ++i) step(i, rs[i], gs[(i + PF - 2) % PF], false);
+            int s0 = PF;
+            for (; s0 + PF < n_chunks; s0 += PF) {
 #pragma unroll
-                for (int i = 0; i < PF; ++i) step(s0 + i, rs[i], gs[(i + PF - 2) % PF]);
+                for (int i = 0; i < PF; ++i) step(s0 + i, rs[i], gs[(i + PF - 2) % PF], true);
+            }
+            for (; s0 < n_steps; s0 += PF) {
+#pragma unroll
+                for (int i = 0; i < PF; ++i) step(s0 + i, rs[i], gs[(i + PF - 2) % PF], false);
             }
         } else {
             Regs ra;
@@ -672,7 +677,7 @@ __global__ void __launch_bounds__(128 * (D / 32)) chunk_kernel(const ChunkParams
                 if (s + 1 < n_chunks) fill_rope_table(s + 1, (s + 1) & 1);
                 __syncthreads();  // chunk s in LDS
                 __syncthreads();  // math done with chunk s
-                if (!kStateOnly) epilogue(s, sm.o, ga);
+                if (!kStateOnly) epilogue(s, sm.o, ga, false);
             }
         }
     }
