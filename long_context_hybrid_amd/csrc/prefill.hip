@@ -96,14 +96,14 @@ struct Cfg {
 };
 
 template <class M, int D, bool kStateOnly>
-struct Tiles {
+struct alignas(16) Tiles {
     using G = Cfg<M, D, kStateOnly>;
     using E = typename G::E;
-    E q[kStateOnly ? 1 : C * G::QS];   // q~ [token][key dim]
-    E k[kStateOnly ? 1 : C * G::QS];   // k~ [token][key dim]
-    E khT[D * G::TS];                  // decayed keys, hi part, [key dim][token]
-    E klT[M::kSplit ? D * G::TS : 1];  // decayed keys, lo part
-    E vT[D * G::TS];                   // v [value dim][token]
+    alignas(16) E q[kStateOnly ? 1 : C * G::QS];   // q~ [token][key dim]
+    alignas(16) E k[kStateOnly ? 1 : C * G::QS];   // k~ [token][key dim]
+    alignas(16) E khT[D * G::TS];                  // decayed keys, hi part, [key dim][token]
+    alignas(16) E klT[M::kSplit ? D * G::TS : 1];  // decayed keys, lo part
+    alignas(16) E vT[D * G::TS];                   // v [value dim][token]
 };
 
 template <class M, int D, bool kStateOnly>
