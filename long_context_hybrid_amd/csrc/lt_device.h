@@ -47,9 +47,10 @@ __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-// lambda^n from log2(lambda), with lambda^0 = 1 also for lambda = 0 (log2 = -inf).
+// lambda^n from log2(lambda), with lambda^0 = 1 also for lambda = 0 (log2 = -inf).  The bare
+// hardware exp2 is used: a decay factor below 2^-126 contributes nothing at fp32 precision.
 __device__ __forceinline__ float pow_lambda(float log2_lambda, int n) {
-    return n == 0 ? 1.0f : exp2f((float)n * log2_lambda);
+    return n == 0 ? 1.0f : __builtin_amdgcn_exp2f((float)n * log2_lambda);
 }
 
 // cos and sin of the rotary angle pos * f, where f_rev = f / (2 pi) is given in revolutions per

@@ -233,7 +233,7 @@ __global__ void __launch_bounds__(128 * (D / 32)) chunk_kernel(const ChunkParams
 
     __shared__ Smem<M, D, kStateOnly> sm;
 
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int lm = lane & 31, lh = lane >> 5;
     const bool is_math = wave < NW;
@@ -260,16 +260,16 @@ __global__ void __launch_bounds__(128 * (D / 32)) chunk_kernel(const ChunkParams
     constexpr int EPT = 16, TPR = D / EPT;    // epilogue: 16 outputs per thread, TPR per row
     const int er = it / TPR, ec = it % TPR;
 
-    // Per-chunk RoPE base table cos/sin(p0 f_i): HALF / NW frequencies per io wave, one per lane.
-    // (The frequency is read once: a dynamically indexed kernel-argument read is a vector memory
-    // load, and waiting for it inside the loop would also wait for the prefetches.)
-    constexpr int FPW = HALF / NW;  // frequencies per io wave
-    // Every lane computes (no divergent branch in the loop); lanes without a frequency write to
+    // Per-chunk RoPE base table cos/sin(p0 f_i), one frequency per lane.  A single io wavefront
+    // fills it, the io wavefronts taking turns chunk by chunk (the angle is reduced in fp64 and
+    // a full wavefront costs the same for 1 lane as for 64).  The frequency is read once: a
+    // dynamically indexed kernel-argument read is a vector memory load, and waiting for it
+    // inside the loop would also wait for the prefetches.  Lanes without a frequency write to
     // the sink entry.
-    const bool table_lane = wave >= NW && lane < FPW;
-    const int table_i = table_lane ? (wave - NW) * FPW + lane : 64;
-    const double table_frev = p.inv_freq_rev[table_lane ? table_i : 0];
+    const int table_i = lane < HALF ? lane : 64;
+    const double table_frev = p.inv_freq_rev[min(lane, HALF - 1)];
     auto fill_rope_table = [&](int chunk, int slot) {
+        if (wave - NW != chunk % NW) return;  // wave-uniform (there are NW io wavefronts)
         float cs, sn;
         rope_cos_sin(p.pos0 + t_begin + (int64_t)chunk * C, table_frev, cs, sn);
         sm.rope[slot][table_i] = make_float2(cs, sn);
@@ -515,7 +515,7 @@ __global__ void __launch_bounds__(128 * (D / 32)) chunk_kernel(const ChunkParams
                 // q~, k~ and decayed keys zero, so they add nothing to scores, outputs or state.
                 const float rq = valid ? fast_rsqrt(ssq * (1.0f / D) + p.eps) : 0.0f;
                 const float rk = valid ? fast_rsqrt(ssk * (1.0f / D) + p.eps) * kscale : 0.0f;
-                const float kdec = valid ? pow_lambda(l2l, n - 1 - j) : 0.0f;
+                const float kds = valid ? rk * pow_lambda(l2l, n - 1 - j) : 0.0f;  // decayed-key scale
                 float qt[8], kt[8];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
@@ -527,12 +527,16 @@ __global__ void __launch_bounds__(128 * (D / 32)) chunk_kernel(const ChunkParams
                         qt[u] = x1 * cs - x2 * sn;
                         qt[4 + u] = x2 * cs + x1 * sn;
                     }
-                    const float y1 = ka[u] * wk[u] * rk, y2 = ka[4 + u] * wk[4 + u] * rk;
-                    kt[u] = y1 * cs - y2 * sn;
-                    kt[4 + u] = y2 * cs + y1 * sn;
+                    // rotate the weighted key, then apply the per-token scales
+                    const float y1 = ka[u] * wk[u], y2 = ka[4 + u] * wk[4 + u];
+                    const float r1 = y1 * cs - y2 * sn, r2 = y2 * cs + y1 * sn;
+                    if (!kStateOnly) {
+                        kt[u] = r1 * rk;
+                        kt[4 + u] = r2 * rk;
+                    }
+                    kd[s][u] = r1 * kds;
+                    kd[s][4 + u] = r2 * kds;
                 }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) kd[s][i] = kt[i] * kdec;
                 if (!kStateOnly) {
                     const int c0 = Layout<M>::kpos(4 * fg);
                     E* qdst = t.q + j * QS;
