@@ -45,7 +45,21 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=524288)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the timed runs, copy this many MiB device to device three times "
+                         "(a plain copy of known size that calibrates HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration(torch, mib):
+    """Three device-to-device copies of `mib` MiB: each reads and writes exactly mib MiB."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 class HipEvents:
@@ -219,6 +233,9 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(args, torch, synth, pre)
+    if args.copy_mib > 0:
+        print(f"[bench] calibration copy of {args.copy_mib} MiB", file=sys.stderr, flush=True)
+        copy_calibration(torch, args.copy_mib)
     spec = pre["spec"]
     line = {
         "metric": METRIC,

@@ -44,18 +44,20 @@ float log2_lambda(double lam) {
 }
 
 // Chunk length and segment split.  Segments exist to give every CU a workgroup when B*H is
-// small; each segment gets at least kMinChunksPerSegment chunks.
+// small; each segment gets at least kMinChunksPerSegment chunks.  The state-only pass over
+// segments 0 .. P-2 may split each of them further into `sub` equal sub-segments so that it
+// fills kStateOnlyBlocksPerCU workgroups per CU.
 lt_status plan(int B, int T, int H, int d, int dtype, int chunk, int segments, int* chunk_out,
-               int* seg_out, int* seg_len_out) {
+               int* seg_out, int* seg_len_out, int* sub_out = nullptr) {
     if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || segments < 0 || chunk < 0) return LT_ERR_INVALID_ARG;
     if (dtype != LT_F32 && dtype != LT_BF16) return LT_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return LT_ERR_UNSUPPORTED;
     if (chunk != 0 && chunk != lt::kChunk) return LT_ERR_UNSUPPORTED;
     const int C = lt::kChunk;
     const long long n_chunks = ((long long)T + C - 1) / C;
+    const long long bh = (long long)B * H;
     long long P = segments;
     if (P == 0) {
-        const long long bh = (long long)B * H;
         P = (lt::kNumCUs + bh - 1) / bh;
         const long long cap = n_chunks / lt::kMinChunksPerSegment;
         if (P > cap) P = cap;
@@ -64,15 +66,26 @@ lt_status plan(int B, int T, int H, int d, int dtype, int chunk, int segments, i
     if (P > n_chunks) P = n_chunks;
     const long long chunks_per_seg = (n_chunks + P - 1) / P;
     P = (n_chunks + chunks_per_seg - 1) / chunks_per_seg;  // every segment non-empty
-    if ((long long)B * H * P > 0x7fffffffLL) return LT_ERR_UNSUPPORTED;
+    long long sub = 1;
+    if (P > 1) {
+        const long long want = (long long)lt::kStateOnlyBlocksPerCU * lt::kNumCUs;
+        sub = (want + bh * (P - 1) - 1) / (bh * (P - 1));
+        while (sub > 1 && (chunks_per_seg % sub != 0 ||
+                           chunks_per_seg / sub < lt::kMinChunksPerSegment))
+            --sub;
+    }
+    if (bh * ((P - 1) * sub + 1) > 0x7fffffffLL) return LT_ERR_UNSUPPORTED;
     if (chunk_out) *chunk_out = C;
     if (seg_out) *seg_out = (int)P;
     if (seg_len_out) *seg_len_out = (int)(chunks_per_seg * C);
+    if (sub_out) *sub_out = (int)sub;
     return LT_OK;
 }
 
-size_t workspace_bytes_for(int B, int H, int d, int P) {
-    return P > 1 ? (size_t)B * H * P * d * d * sizeof(float) : 0;
+// State slots per (b, h) in the workspace: one per state-only sub-segment, plus the entry state
+// of the last segment.
+size_t workspace_bytes_for(int B, int H, int d, int P, int sub) {
+    return P > 1 ? (size_t)B * H * ((size_t)(P - 1) * sub + 1) * d * d * sizeof(float) : 0;
 }
 
 }  // namespace
@@ -112,8 +125,9 @@ lt_status lightning_prefill_plan(int B, int T, int H, int d, int dtype, int chun
 size_t lightning_prefill_workspace_size(int B, int T, int H, int d, int dtype, int chunk,
                                         int segments) {
     int C = 0, P = 0, L = 0;
-    if (plan(B, T, H, d, dtype, chunk, segments, &C, &P, &L) != LT_OK) return 0;
-    return workspace_bytes_for(B, H, d, P);
+    int sub = 1;
+    if (plan(B, T, H, d, dtype, chunk, segments, &C, &P, &L, &sub) != LT_OK) return 0;
+    return workspace_bytes_for(B, H, d, P, sub);
 }
 
 lt_status lightning_prefill(const void* q, const void* k, const void* v, const void* gate,
@@ -132,10 +146,10 @@ lt_status lightning_prefill(const void* q, const void* k, const void* v, const v
                                 lambda, rope_base, rms_eps);
     if (st != LT_OK) return st;
     if ((double)B * T * H * d > 9.0e15) return LT_ERR_UNSUPPORTED;
-    int C = 0, P = 0, L = 0;
-    st = plan(B, T, H, d, dtype, chunk, segments, &C, &P, &L);
+    int C = 0, P = 0, L = 0, sub = 1;
+    st = plan(B, T, H, d, dtype, chunk, segments, &C, &P, &L, &sub);
     if (st != LT_OK) return st;
-    const size_t need = workspace_bytes_for(B, H, d, P);
+    const size_t need = workspace_bytes_for(B, H, d, P, sub);
     if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need))
         return LT_ERR_WORKSPACE;
 
@@ -148,6 +162,7 @@ lt_status lightning_prefill(const void* q, const void* k, const void* v, const v
     cp.ws = static_cast<float*>(workspace);
     cp.pos0 = pos0;
     cp.B = B; cp.T = T; cp.H = H; cp.P = P; cp.L = L;
+    cp.SM = sub; cp.SL = L / sub; cp.SP = (P - 1) * sub + 1;
     cp.w_stride = norm_w_head_stride;
     cp.eps = (float)rms_eps;
     for (int h = 0; h < H; ++h) cp.log2_lambda[h] = log2_lambda(lambda[h]);
@@ -157,8 +172,8 @@ lt_status lightning_prefill(const void* q, const void* k, const void* v, const v
     memset(&sp, 0, sizeof sp);
     sp.state_in = state_in;
     sp.ws = cp.ws;
-    sp.BH = B * H; sp.H = H; sp.P = P; sp.dd = d * d;
-    for (int h = 0; h < H; ++h) sp.lambda_pow_L[h] = (float)pow(lambda[h], (double)L);
+    sp.BH = B * H; sp.H = H; sp.P = cp.SP; sp.dd = d * d;
+    for (int h = 0; h < H; ++h) sp.lambda_pow_L[h] = (float)pow(lambda[h], (double)cp.SL);
 
     if (main_kernel_events && (!main_kernel_events[0] || !main_kernel_events[1]))
         return LT_ERR_INVALID_ARG;

@@ -12,6 +12,7 @@ namespace lt {
 constexpr int kChunk = 32;        // tokens per chunk of the prefill chunk loop
 constexpr int kNumCUs = 256;      // compute units of an MI355X; sizes the automatic segment split
 constexpr int kMinChunksPerSegment = 8;
+constexpr int kStateOnlyBlocksPerCU = 2;  // workgroups per CU that the state-only pass is sized for
 
 // Kernel parameters of the prefill chunk loop (passed by value in the kernel argument segment).
 struct ChunkParams {
@@ -26,11 +27,15 @@ struct ChunkParams {
     float* state_out;       // may be null
     void* y;
     float* o_raw;           // may be null
-    float* ws;              // [B][H][P][d][d] fp32 when P > 1
+    float* ws;              // [B][H][SP][d][d] fp32 when P > 1
     int64_t pos0;
     int B, T, H;
-    int P;      // segments per (b, h)
+    int P;      // segments per (b, h) of the main pass
     int L;      // tokens per segment (multiple of the chunk), the last segment may be shorter
+    // The state-only pass splits segments 0 .. P-2 into SM sub-segments of SL = L / SM tokens;
+    // the workspace holds SP = (P - 1) SM + 1 states per (b, h), and the main pass of segment p
+    // reads its entry state from slot p SM.
+    int SP, SL, SM;
     int w_stride;
     float eps;
     float log2_lambda[LT_MAX_HEADS];  // log2(lambda_h), -inf for lambda_h = 0
@@ -41,8 +46,8 @@ struct ChunkParams {
 struct ScanParams {
     const float* state_in;  // may be null (zeros)
     float* ws;
-    int BH, H, P, dd;
-    float lambda_pow_L[LT_MAX_HEADS];  // lambda_h^L
+    int BH, H, P, dd;                  // P = slots per (b, h) (sub-segments + 1)
+    float lambda_pow_L[LT_MAX_HEADS];  // lambda_h^L, L = sub-segment length
 };
 
 struct DecodeParams {

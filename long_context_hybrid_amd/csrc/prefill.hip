@@ -51,7 +51,7 @@ static_assert(C == 32, "the tiling below assumes one 32-row block per chunk");
 #define LT_PREFETCH_MAIN 3
 #endif
 #ifndef LT_PREFETCH_STATE
-#define LT_PREFETCH_STATE 6
+#define LT_PREFETCH_STATE 2
 #endif
 constexpr int kPrefetchMain = LT_PREFETCH_MAIN;
 constexpr int kPrefetchStateOnly = LT_PREFETCH_STATE;
@@ -220,8 +220,12 @@ __device__ __forceinline__ void contract_acc(f32x16& acc, const f32x16& x, const
     }
 }
 
+// The state-only pass is register-limited so that kStateOnlyBlocksPerCU of its workgroups share
+// a CU (their barriers are independent, so one hides the other's stalls).
 template <class M, int D, bool kStateOnly, int PF>
-__global__ void __launch_bounds__(128 * (D / 32)) chunk_kernel(const ChunkParams p) {
+__global__ void __launch_bounds__(128 * (D / 32))
+__attribute__((amdgpu_waves_per_eu(kStateOnly ? kStateOnlyBlocksPerCU * D / 64 : 1)))
+chunk_kernel(const ChunkParams p) {
     using G = Cfg<M, D, kStateOnly>;
     using E = typename G::E;
     using In = typename M::In;
@@ -238,12 +242,14 @@ __global__ void __launch_bounds__(128 * (D / 32)) chunk_kernel(const ChunkParams
     const int lm = lane & 31, lh = lane >> 5;
     const bool is_math = wave < NW;
 
-    const int nseg = kStateOnly ? p.P - 1 : p.P;
+    // the state-only pass runs over the sub-segments of segments 0 .. P-2
+    const int nseg = kStateOnly ? p.SP - 1 : p.P;
+    const int seg_len = kStateOnly ? p.SL : p.L;
     const int seg = blockIdx.x % nseg;
     const int bh = blockIdx.x / nseg;
     const int b = bh / p.H, h = bh - b * p.H;
-    const int t_begin = seg * p.L;
-    const int t_end = min(p.T, t_begin + p.L);
+    const int t_begin = seg * seg_len;
+    const int t_end = min(p.T, t_begin + seg_len);
     const int n_chunks = (t_end - t_begin + C - 1) / C;
     // pipeline steps: chunk s is written in step s, computed in step s+1 and stored in step s+2;
     // rounded up to a multiple of PF so the io loop can rotate PF register sets without branches
@@ -287,7 +293,7 @@ __global__ void __launch_bounds__(128 * (D / 32)) chunk_kernel(const ChunkParams
         {
             const float* src = nullptr;
             if (!kStateOnly)
-                src = (p.P > 1) ? p.ws + ((size_t)bh * p.P + seg) * dd
+                src = (p.P > 1) ? p.ws + ((size_t)bh * p.SP + (size_t)seg * p.SM) * dd
                                 : (p.state_in ? p.state_in + (size_t)bh * dd : nullptr);
 #pragma unroll
             for (int c = 0; c < NW; ++c)
@@ -417,7 +423,7 @@ __global__ void __launch_bounds__(128 * (D / 32)) chunk_kernel(const ChunkParams
 
         float* dst = nullptr;
         if (kStateOnly)
-            dst = p.ws + ((size_t)bh * p.P + seg) * dd;
+            dst = p.ws + ((size_t)bh * p.SP + seg) * dd;
         else if (seg == p.P - 1 && p.state_out)
             dst = p.state_out + (size_t)bh * dd;
         if (dst) {
@@ -711,7 +717,7 @@ hipError_t launch_typed(const ChunkParams& cp, const ScanParams& sp, const hipEv
     const int BH = cp.B * cp.H;
     constexpr int NT = 128 * (D / 32);
     if (cp.P > 1) {
-        chunk_kernel<M, D, true, kPrefetchStateOnly><<<dim3(BH * (cp.P - 1)), dim3(NT), 0, stream>>>(cp);
+        chunk_kernel<M, D, true, kPrefetchStateOnly><<<dim3(BH * (cp.SP - 1)), dim3(NT), 0, stream>>>(cp);
         const size_t n = (size_t)BH * D * D;
         segment_scan_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(sp);
     }

@@ -73,21 +73,24 @@ def test_hypenet_gamma_time_scales():
         lt.lightning_hypenet_gamma(0)
 
 
-@pytest.mark.parametrize("B,T,H,d,expect_p", [
-    (1, 524288, 16, 128, 16),   # 512K-token layer: one segment per CU
-    (1, 32768, 16, 128, 16),
-    (4, 131072, 32, 128, 2),
-    (64, 4096, 16, 128, 1),      # B*H already fills the CUs
-    (1, 256, 2, 64, 1),          # too short to split (8 chunks)
-    (1, 300, 1, 128, 1),
-    (1, 4096, 1, 128, 16),       # 128 chunks, 8 per segment
-    (2, 100000, 2, 64, 64),      # 3125 chunks over 64 segments
+@pytest.mark.parametrize("B,T,H,d,expect_p,expect_sub", [
+    (1, 524288, 16, 128, 16, 2),   # 512K-token layer: one segment per CU, state-only pass 2 per CU
+    (1, 32768, 16, 128, 16, 2),
+    (4, 131072, 32, 128, 2, 4),
+    (64, 4096, 16, 128, 1, 1),      # B*H already fills the CUs
+    (1, 256, 2, 64, 1, 1),          # too short to split (8 chunks)
+    (1, 300, 1, 128, 1, 1),
+    (1, 4096, 1, 128, 16, 1),       # 128 chunks, 8 per segment: no further split
+    (2, 100000, 2, 64, 64, 1),      # 3125 chunks over 64 segments of 49 (not divisible)
 ])
-def test_plan_and_workspace(B, T, H, d, expect_p):
+def test_plan_and_workspace(B, T, H, d, expect_p, expect_sub):
     c, p = lt.lightning_prefill_plan(B, T, H, d)
     assert c == 32 and p == expect_p
     ws = lt.lightning_prefill_workspace_size(B, T, H, d)
-    assert ws == (B * H * p * d * d * 4 if p > 1 else 0)
+    # one fp32 d x d state per state-only sub-segment of segments 0 .. P-2, plus the entry state
+    # of the last segment
+    slots = (p - 1) * expect_sub + 1
+    assert ws == (B * H * slots * d * d * 4 if p > 1 else 0)
 
 
 def test_plan_explicit_segments_and_chunk():

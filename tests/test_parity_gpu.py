@@ -36,6 +36,10 @@ SMALL = [
     ("fp32_d128_ragged", 1, 777, 2, 128, torch.float32, (0.5, 0.999), "randn", (0, 4)),
     ("bf16_d128_long", 1, 4096 + 17, 2, 128, torch.bfloat16, None, "randn", (0, 7, 65)),
     ("fp32_d64_ragged", 3, 130, 2, 64, torch.float32, (0.0, 1.0), "randn", (0, 3)),
+    # segments whose state-only pass is split further (3 and 5 sub-segments per segment)
+    ("bf16_d128_subsegments", 1, 8192 + 5, 2, 128, torch.bfloat16, None, "randn", (2, 4)),
+    # 3 and 2 sub-segments per segment, fp32 activations
+    ("fp32_d64_subsegments", 2, 2048 + 40, 1, 64, torch.float32, (0.9999,), "randn", (2, 3)),
 ]
 
 
