@@ -96,7 +96,7 @@ def bench_prefill(args, torch, lt, synth):
     dev = torch.device("cuda:0")
     inp = synth.make_prefill(spec, device=dev)
     B, T, H, d = inp["B"], inp["T"], inp["H"], inp["d"]
-    chunk, P = lt.lightning_prefill_plan(B, T, H, d, spec.dtype, 0, args.segments)
+    chunk, P, seg_len = lt.lightning_prefill_plan(B, T, H, d, spec.dtype, 0, args.segments)
     y = torch.empty_like(inp["q"])
     s_out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
     ws_bytes = lt.lightning_prefill_workspace_size(B, T, H, d, spec.dtype, 0, args.segments)
@@ -132,7 +132,7 @@ def bench_prefill(args, torch, lt, synth):
     achieved = alg_bytes / (main_ms * 1e-3) / 1e9
     useful_flops = units * (4 * d * d + 2 * chunk * d)
     tflops = useful_flops / (main_ms * 1e-3) / 1e12
-    pre_bytes = B * H * (P - 1) * (T // P) * 2 * d * act_bytes if P > 1 else 0
+    pre_bytes = B * H * (P - 1) * seg_len * 2 * d * act_bytes if P > 1 else 0  # k, v of segments 0 .. P-2
     return dict(
         spec=spec, inp=inp, chunk=chunk, P=P, ms_per_step=ms_per_step, main_ms=main_ms,
         value=tokens / (ms_per_step * 1e-3),

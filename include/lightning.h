@@ -69,10 +69,11 @@ lt_status lightning_hypenet_gamma(int H, double* out);
 lt_status lightning_state_init(float* state, int B, int H, int d, const float* init, void* stream);
 
 /* Chunk length and number of sequence segments lightning_prefill will use for this shape when
- * called with the same `chunk` and `segments` requests (0 = automatic).  Returns
- * LT_ERR_UNSUPPORTED for a request the build does not implement. */
+ * called with the same `chunk` and `segments` requests (0 = automatic), and the number of tokens
+ * in each segment but the last (which holds the rest of the sequence, never more).  Any output
+ * pointer may be NULL.  Returns LT_ERR_UNSUPPORTED for a request the build does not implement. */
 lt_status lightning_prefill_plan(int B, int T, int H, int d, int dtype, int chunk, int segments,
-                                 int* chunk_out, int* segments_out);
+                                 int* chunk_out, int* segments_out, int* segment_len_out);
 
 /* Device workspace (bytes) lightning_prefill needs for this shape and request. */
 size_t lightning_prefill_workspace_size(int B, int T, int H, int d, int dtype, int chunk,

@@ -45,10 +45,14 @@ float log2_lambda(double lam) {
 
 // Chunk length and segment split.  Segments exist to give every CU a workgroup when B*H is
 // small; each segment gets at least kMinChunksPerSegment chunks.  The state-only pass over
-// segments 0 .. P-2 may split each of them further into `sub` equal sub-segments so that it
-// fills kStateOnlyBlocksPerCU workgroups per CU.
-lt_status plan(int B, int T, int H, int d, int dtype, int chunk, int segments, int* chunk_out,
-               int* seg_out, int* seg_len_out, int* sub_out = nullptr) {
+// segments 0 .. P-2 may cut each of them further into `sub` sub-segments (of sub_len chunks,
+// the last one per segment shorter) so that it fills kStateOnlyBlocksPerCU workgroups per CU.
+struct Plan {
+    int C, P, L;       // chunk, segments, tokens per segment (segments 0 .. P-2)
+    int sub, sub_len;  // state-only sub-segments per segment, tokens per sub-segment
+};
+
+lt_status plan(int B, int T, int H, int d, int dtype, int chunk, int segments, Plan* out) {
     if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || segments < 0 || chunk < 0) return LT_ERR_INVALID_ARG;
     if (dtype != LT_F32 && dtype != LT_BF16) return LT_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return LT_ERR_UNSUPPORTED;
@@ -64,21 +68,45 @@ lt_status plan(int B, int T, int H, int d, int dtype, int chunk, int segments, i
         if (P < 1) P = 1;
     }
     if (P > n_chunks) P = n_chunks;
-    const long long chunks_per_seg = (n_chunks + P - 1) / P;
-    P = (n_chunks + chunks_per_seg - 1) / chunks_per_seg;  // every segment non-empty
-    long long sub = 1;
+    long long cps = (n_chunks + P - 1) / P;
+    if (P > 1 && dtype == LT_BF16) {
+        // In bf16 mode the last segment may also carry the low parts of the decayed keys for the
+        // final state, which costs it about 100 / kLastSegmentPercent times the others' time per
+        // chunk.  Pick the segment length that minimises the slowest segment's time.
+        const long long pct = lt::kLastSegmentPercent;
+        const long long hi = (n_chunks * 100 + (P - 1) * 100 + pct - 1) / ((P - 1) * 100 + pct);
+        long long best = cps, best_t = -1;
+        for (long long c = cps; c <= hi; ++c) {
+            const long long last = n_chunks - (P - 1) * c;
+            if (last < 1) break;
+            const long long t = (c * pct > last * 100) ? c * pct : last * 100;
+            if (best_t < 0 || t < best_t) { best = c; best_t = t; }
+        }
+        cps = best;
+    }
+    P = (n_chunks + cps - 1) / cps;  // every segment non-empty
+    long long sub = 1, sub_chunks = cps;
     if (P > 1) {
-        const long long want = (long long)lt::kStateOnlyBlocksPerCU * lt::kNumCUs;
-        sub = (want + bh * (P - 1) - 1) / (bh * (P - 1));
-        while (sub > 1 && (chunks_per_seg % sub != 0 ||
-                           chunks_per_seg / sub < lt::kMinChunksPerSegment))
-            --sub;
+        // Among splits that keep kMinChunksPerSegment chunks per sub-segment and leave the last
+        // one non-empty, take the one with the fewest chunks per workgroup slot, counting
+        // kStateOnlyBlocksPerCU slots per CU (fewer sub-segments on a tie).
+        const long long slots = (long long)lt::kStateOnlyBlocksPerCU * lt::kNumCUs;
+        const long long most = (slots + bh * (P - 1) - 1) / (bh * (P - 1));
+        long long best_cost = -1;
+        for (long long s = 1; s <= most; ++s) {
+            const long long sc = (cps + s - 1) / s;
+            if (s > 1 && (sc < lt::kMinChunksPerSegment || cps - (s - 1) * sc < 1)) continue;
+            const long long rounds = (bh * (P - 1) * s + slots - 1) / slots;
+            const long long cost = rounds * sc;
+            if (best_cost < 0 || cost < best_cost) { best_cost = cost; sub = s; sub_chunks = sc; }
+        }
     }
     if (bh * ((P - 1) * sub + 1) > 0x7fffffffLL) return LT_ERR_UNSUPPORTED;
-    if (chunk_out) *chunk_out = C;
-    if (seg_out) *seg_out = (int)P;
-    if (seg_len_out) *seg_len_out = (int)(chunks_per_seg * C);
-    if (sub_out) *sub_out = (int)sub;
+    out->C = C;
+    out->P = (int)P;
+    out->L = (int)(cps * C);
+    out->sub = (int)sub;
+    out->sub_len = (int)(sub_chunks * C);
     return LT_OK;
 }
 
@@ -118,16 +146,21 @@ lt_status lightning_state_init(float* state, int B, int H, int d, const float* i
 }
 
 lt_status lightning_prefill_plan(int B, int T, int H, int d, int dtype, int chunk, int segments,
-                                 int* chunk_out, int* segments_out) {
-    return plan(B, T, H, d, dtype, chunk, segments, chunk_out, segments_out, nullptr);
+                                 int* chunk_out, int* segments_out, int* segment_len_out) {
+    Plan pl;
+    const lt_status st = plan(B, T, H, d, dtype, chunk, segments, &pl);
+    if (st != LT_OK) return st;
+    if (chunk_out) *chunk_out = pl.C;
+    if (segments_out) *segments_out = pl.P;
+    if (segment_len_out) *segment_len_out = pl.P > 1 ? pl.L : T;
+    return LT_OK;
 }
 
 size_t lightning_prefill_workspace_size(int B, int T, int H, int d, int dtype, int chunk,
                                         int segments) {
-    int C = 0, P = 0, L = 0;
-    int sub = 1;
-    if (plan(B, T, H, d, dtype, chunk, segments, &C, &P, &L, &sub) != LT_OK) return 0;
-    return workspace_bytes_for(B, H, d, P, sub);
+    Plan pl;
+    if (plan(B, T, H, d, dtype, chunk, segments, &pl) != LT_OK) return 0;
+    return workspace_bytes_for(B, H, d, pl.P, pl.sub);
 }
 
 lt_status lightning_prefill(const void* q, const void* k, const void* v, const void* gate,
@@ -146,10 +179,11 @@ lt_status lightning_prefill(const void* q, const void* k, const void* v, const v
                                 lambda, rope_base, rms_eps);
     if (st != LT_OK) return st;
     if ((double)B * T * H * d > 9.0e15) return LT_ERR_UNSUPPORTED;
-    int C = 0, P = 0, L = 0, sub = 1;
-    st = plan(B, T, H, d, dtype, chunk, segments, &C, &P, &L, &sub);
+    Plan pl;
+    st = plan(B, T, H, d, dtype, chunk, segments, &pl);
     if (st != LT_OK) return st;
-    const size_t need = workspace_bytes_for(B, H, d, P, sub);
+    const int P = pl.P;
+    const size_t need = workspace_bytes_for(B, H, d, P, pl.sub);
     if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need))
         return LT_ERR_WORKSPACE;
 
@@ -161,8 +195,8 @@ lt_status lightning_prefill(const void* q, const void* k, const void* v, const v
     cp.y = y; cp.o_raw = o_raw;
     cp.ws = static_cast<float*>(workspace);
     cp.pos0 = pos0;
-    cp.B = B; cp.T = T; cp.H = H; cp.P = P; cp.L = L;
-    cp.SM = sub; cp.SL = L / sub; cp.SP = (P - 1) * sub + 1;
+    cp.B = B; cp.T = T; cp.H = H; cp.P = P; cp.L = pl.L;
+    cp.SM = pl.sub; cp.SL = pl.sub_len; cp.SP = (P - 1) * pl.sub + 1;
     cp.w_stride = norm_w_head_stride;
     cp.eps = (float)rms_eps;
     for (int h = 0; h < H; ++h) cp.log2_lambda[h] = log2_lambda(lambda[h]);
@@ -172,8 +206,13 @@ lt_status lightning_prefill(const void* q, const void* k, const void* v, const v
     memset(&sp, 0, sizeof sp);
     sp.state_in = state_in;
     sp.ws = cp.ws;
-    sp.BH = B * H; sp.H = H; sp.P = cp.SP; sp.dd = d * d;
-    for (int h = 0; h < H; ++h) sp.lambda_pow_L[h] = (float)pow(lambda[h], (double)cp.SL);
+    sp.BH = B * H; sp.H = H; sp.P = cp.SP; sp.sub = pl.sub; sp.dd = d * d;
+    // sub-segments 0 .. sub-2 of a segment have sub_len tokens, the last one the rest of L
+    const int rest = pl.L - (pl.sub - 1) * pl.sub_len;
+    for (int h = 0; h < H; ++h) {
+        sp.lambda_pow_sub[h] = (float)pow(lambda[h], (double)pl.sub_len);
+        sp.lambda_pow_rest[h] = (float)pow(lambda[h], (double)rest);
+    }
 
     if (main_kernel_events && (!main_kernel_events[0] || !main_kernel_events[1]))
         return LT_ERR_INVALID_ARG;

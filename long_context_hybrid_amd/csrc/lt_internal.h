@@ -13,6 +13,7 @@ constexpr int kChunk = 32;        // tokens per chunk of the prefill chunk loop
 constexpr int kNumCUs = 256;      // compute units of an MI355X; sizes the automatic segment split
 constexpr int kMinChunksPerSegment = 8;
 constexpr int kStateOnlyBlocksPerCU = 2;  // workgroups per CU that the state-only pass is sized for
+constexpr int kLastSegmentPercent = 92;   // bf16: last segment length relative to the others
 
 // Kernel parameters of the prefill chunk loop (passed by value in the kernel argument segment).
 struct ChunkParams {
@@ -32,9 +33,9 @@ struct ChunkParams {
     int B, T, H;
     int P;      // segments per (b, h) of the main pass
     int L;      // tokens per segment (multiple of the chunk), the last segment may be shorter
-    // The state-only pass splits segments 0 .. P-2 into SM sub-segments of SL = L / SM tokens;
-    // the workspace holds SP = (P - 1) SM + 1 states per (b, h), and the main pass of segment p
-    // reads its entry state from slot p SM.
+    // The state-only pass splits segments 0 .. P-2 into SM sub-segments: SM - 1 of SL tokens and
+    // a last one with the rest of the segment.  The workspace holds SP = (P - 1) SM + 1 states
+    // per (b, h), and the main pass of segment p reads its entry state from slot p SM.
     int SP, SL, SM;
     int w_stride;
     float eps;
@@ -46,8 +47,9 @@ struct ChunkParams {
 struct ScanParams {
     const float* state_in;  // may be null (zeros)
     float* ws;
-    int BH, H, P, dd;                  // P = slots per (b, h) (sub-segments + 1)
-    float lambda_pow_L[LT_MAX_HEADS];  // lambda_h^L, L = sub-segment length
+    int BH, H, P, sub, dd;                // P = slots per (b, h) (sub-segments + 1)
+    float lambda_pow_sub[LT_MAX_HEADS];   // lambda_h^len of sub-segments 0 .. sub-2 of a segment
+    float lambda_pow_rest[LT_MAX_HEADS];  // lambda_h^len of the last sub-segment of a segment
 };
 
 struct DecodeParams {

@@ -110,10 +110,13 @@ template <class M, int D, bool kStateOnly>
 struct Smem {
     using G = Cfg<M, D, kStateOnly>;
     Tiles<M, D, kStateOnly> buf[G::NBUF];
-    float o[kStateOnly ? 1 : G::NBUF * C * G::OS];  // o before the output norm [token][value dim]
-    float2 rope[2][65];                             // cos/sin(p0 f_i) of the next two chunks
-                                                    // (entry 64: write sink of idle lanes)
-    float wo[D];
+    alignas(16) float o[kStateOnly ? 1 : G::NBUF * C * G::OS];  // o before the output norm [token][value dim]
+    alignas(16) float2 rope[2][65];  // cos/sin(p0 f_i) of the next two chunks
+                                     // (entry 64: write sink of idle lanes)
+    // decay factors of the math wavefronts' accumulator elements, per lane: [0, 4) the causal
+    // decay of the transposed score tile, [4, 8) lambda^(i+1) of the output rows
+    alignas(16) float4 dec[kStateOnly ? 1 : 64 * 8];
+    alignas(16) float wo[D];
 };
 
 // ---- activation access ------------------------------------------------------------------------
@@ -220,12 +223,10 @@ __device__ __forceinline__ void contract_acc(f32x16& acc, const f32x16& x, const
     }
 }
 
-// The state-only pass is register-limited so that kStateOnlyBlocksPerCU of its workgroups share
-// a CU (their barriers are independent, so one hides the other's stalls).
-template <class M, int D, bool kStateOnly, int PF>
-__global__ void __launch_bounds__(128 * (D / 32))
-__attribute__((amdgpu_waves_per_eu(kStateOnly ? kStateOnlyBlocksPerCU * D / 64 : 1)))
-chunk_kernel(const ChunkParams p) {
+// One workgroup's pass over its segment.  kPrecise: the state update uses the hi + lo parts of
+// the decayed keys (bf16 mode; fp32 mode is always exact to fp32).
+template <class M, int D, bool kStateOnly, int PF, bool kPrecise>
+__device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kStateOnly>& sm) {
     using G = Cfg<M, D, kStateOnly>;
     using E = typename G::E;
     using In = typename M::In;
@@ -235,7 +236,6 @@ chunk_kernel(const ChunkParams p) {
     constexpr int NBUF = G::NBUF;
     constexpr bool kOverlap = G::kOverlap;
 
-    __shared__ Smem<M, D, kStateOnly> sm;
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -244,17 +244,24 @@ chunk_kernel(const ChunkParams p) {
 
     // the state-only pass runs over the sub-segments of segments 0 .. P-2
     const int nseg = kStateOnly ? p.SP - 1 : p.P;
-    const int seg_len = kStateOnly ? p.SL : p.L;
     const int seg = blockIdx.x % nseg;
     const int bh = blockIdx.x / nseg;
     const int b = bh / p.H, h = bh - b * p.H;
-    const int t_begin = seg * seg_len;
-    const int t_end = min(p.T, t_begin + seg_len);
+    int t_begin, t_end;
+    if (kStateOnly) {  // sub-segment seg % SM of segment seg / SM
+        const int s0 = seg / p.SM, s1 = seg - s0 * p.SM;
+        t_begin = s0 * p.L + s1 * p.SL;
+        t_end = min((s0 + 1) * p.L, t_begin + p.SL);
+    } else {
+        t_begin = seg * p.L;
+        t_end = min(p.T, t_begin + p.L);
+    }
     const int n_chunks = (t_end - t_begin + C - 1) / C;
     // pipeline steps: chunk s is written in step s, computed in step s+1 and stored in step s+2;
     // rounded up to a multiple of PF so the io loop can rotate PF register sets without branches
     const int n_steps = (n_chunks + 2 + PF - 1) / PF * PF;
     const float l2l = p.log2_lambda[h];
+    constexpr bool precise = kPrecise;
     const size_t dd = (size_t)D * D;
     const size_t row_stride = (size_t)p.H * D;  // elements between consecutive tokens
     const size_t head_base = ((size_t)b * p.T * p.H + h) * D;
@@ -284,6 +291,24 @@ chunk_kernel(const ChunkParams p) {
     if (!kStateOnly)
         for (int i = threadIdx.x; i < D; i += G::NT) sm.wo[i] = p.ow ? p.ow[(size_t)h * p.w_stride + i] : 1.0f;
     fill_rope_table(0, 0);
+    if (!kStateOnly && wave == 0) {
+        // Per lane of a math wavefront: accumulator register r sits at row m = acc_row(r) and
+        // column lm.  Score tile (transposed, P^T[j = m][i = lm]): lambda^(i-j) for j <= i, else
+        // 0.  Output tile (row i = m): lambda^(i+1).
+        float4* dl = sm.dec + 8 * lane;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float mk[4], rs[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = acc_row(4 * g + e, lh);
+                mk[e] = (lm >= m) ? pow_lambda(l2l, lm - m) : 0.0f;
+                rs[e] = pow_lambda(l2l, m + 1);
+            }
+            dl[g] = make_float4(mk[0], mk[1], mk[2], mk[3]);
+            dl[4 + g] = make_float4(rs[0], rs[1], rs[2], rs[3]);
+        }
+    }
     __syncthreads();
 
     if (is_math) {
@@ -301,14 +326,8 @@ chunk_kernel(const ChunkParams p) {
                 for (int r = 0; r < 16; ++r)
                     S[c][r] = src ? src[(size_t)(32 * c + acc_row(r, lh)) * D + 32 * w + lm] : 0.0f;
         }
-        // decay factors of this lane's accumulator elements
-        float mask[16], rsc[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int m = acc_row(r, lh);
-            mask[r] = (lm >= m) ? pow_lambda(l2l, lm - m) : 0.0f;  // P^T[j = m][i = lm]
-            rsc[r] = pow_lambda(l2l, m + 1);                       // lambda^(i+1), i = m
-        }
+        // this lane's decay factors, kept in LDS rather than in 32 registers for the whole loop
+        const float* dec = reinterpret_cast<const float*>(sm.dec + 8 * lane);
         const float lam_full = pow_lambda(l2l, C);
 
         using L = Layout<M>;
@@ -338,8 +357,8 @@ chunk_kernel(const ChunkParams p) {
                     }
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        pt[r] *= mask[r];
-                        o[r] *= rsc[r];
+                        pt[r] *= dec[r];
+                        o[r] *= dec[16 + r];
                     }
                 }
                 // P V and the state update read the same V blocks
@@ -370,12 +389,14 @@ chunk_kernel(const ChunkParams p) {
                     for (int c = 0; c < NW; ++c) {
                         const int off = (32 * c + lm) * TS + ((16 * st + 8 * lh) ^ L::tsw(32 * c + lm));
                         ah[c] = *reinterpret_cast<const bf16x8*>(t.khT + off);
-                        al[c] = *reinterpret_cast<const bf16x8*>(t.klT + off);
+                        if (precise) al[c] = *reinterpret_cast<const bf16x8*>(t.klT + off);
                     }
 #pragma unroll
                     for (int c = 0; c < NW; ++c) S[c] = mfma_bf16(ah[c], vb[st], S[c]);
+                    if (precise) {
 #pragma unroll
-                    for (int c = 0; c < NW; ++c) S[c] = mfma_bf16(al[c], vb[st], S[c]);
+                        for (int c = 0; c < NW; ++c) S[c] = mfma_bf16(al[c], vb[st], S[c]);
+                    }
                 }
             } else {
                 // fp32 operands (v_mfma_f32_32x32x2_f32)
@@ -384,13 +405,13 @@ chunk_kernel(const ChunkParams p) {
                     f32x16 pt = {};
                     contract_rows<D>(pt, t.k + lm * QS, t.q + lm * QS, lh);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) pt[r] *= mask[r];
+                    for (int r = 0; r < 16; ++r) pt[r] *= dec[r];
                     // inter-chunk term diag(lambda^(i+1)) Q~ S, B operand from the state registers
                     f32x16 o = {};
 #pragma unroll
                     for (int c = 0; c < NW; ++c) contract_acc(o, S[c], t.q + lm * QS + 32 * c, lh, false);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) o[r] *= rsc[r];
+                    for (int r = 0; r < 16; ++r) o[r] *= dec[16 + r];
                     // intra-chunk term P V, A operand from the score registers
                     contract_acc(o, pt, vrow, lh, true, vsw);
 #pragma unroll
@@ -554,20 +575,31 @@ chunk_kernel(const ChunkParams p) {
                 }
             }
             const int jp = Layout<M>::kpos(2 * rg);  // the two tokens stay adjacent
+            auto tcol = [&](int i) {
+                const int f = (i < 4) ? 4 * fg + i : HALF + 4 * fg + (i - 4);
+                return f * TS + (jp ^ Layout<M>::tsw(f));
+            };
+            uint32_t hi[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const int f = (i < 4) ? 4 * fg + i : HALF + 4 * fg + (i - 4);
-                const int col = f * TS + (jp ^ Layout<M>::tsw(f));
+                const int col = tcol(i);
                 if constexpr (M::kSplit) {
-                    // hi = bf16(k'), lo = bf16(k' - hi), two tokens per instruction
-                    const uint32_t hi = pack_bf16x2(kd[0][i], kd[1][i]);
-                    const float lo0 = kd[0][i] - bf16_lo(hi), lo1 = kd[1][i] - bf16_hi(hi);
-                    *reinterpret_cast<uint32_t*>(t.khT + col) = hi;
-                    *reinterpret_cast<uint32_t*>(t.klT + col) = pack_bf16x2(lo0, lo1);
+                    hi[i] = pack_bf16x2(kd[0][i], kd[1][i]);  // two tokens per instruction
+                    *reinterpret_cast<uint32_t*>(t.khT + col) = hi[i];
                 } else {
                     st2(t.khT + col, kd[0][i], kd[1][i]);
                 }
                 st_pair(t.vT + col, r.v[0][i / 4], r.v[1][i / 4], i % 4);
+            }
+            if constexpr (M::kSplit) {
+                if (precise) {
+                    // lo = bf16(k' - hi): hi + lo carries k' to about 16 significant bits
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float lo0 = kd[0][i] - bf16_lo(hi[i]), lo1 = kd[1][i] - bf16_hi(hi[i]);
+                        *reinterpret_cast<uint32_t*>(t.klT + tcol(i)) = pack_bf16x2(lo0, lo1);
+                    }
+                }
             }
         };
 
@@ -693,21 +725,46 @@ chunk_kernel(const ChunkParams p) {
     }
 }
 
-// ws[b][h][s] holds each segment's end state from zero (s < P-1).  Replace it, in place, by the
-// state entering segment s:  S_in(0) = state_in,  S_in(s+1) = lambda^L S_in(s) + dS(s).
+// bf16 mode updates the state with hi + lo parts of the decayed keys (fp32-accurate) where the
+// state leaves the kernel: in the state-only pass, whose sums become segment entry states, and in
+// the last segment when the final state is requested.  Inside the other segments the state only
+// feeds outputs (bf16, normalised), and the hi part alone is used.  The choice is per workgroup
+// and made once, so each pass is branch-free inside its loop.
+// The state-only pass is register-limited so that kStateOnlyBlocksPerCU of its workgroups share
+// a CU (their barriers are independent, so one hides the other's stalls).
+template <class M, int D, bool kStateOnly, int PF>
+__global__ void __launch_bounds__(128 * (D / 32))
+__attribute__((amdgpu_waves_per_eu(kStateOnly ? kStateOnlyBlocksPerCU * D / 64 : 1)))
+chunk_kernel(const ChunkParams p) {
+    __shared__ Smem<M, D, kStateOnly> sm;
+    if constexpr (kStateOnly || !M::kSplit) {
+        chunk_pass<M, D, kStateOnly, PF, true>(p, sm);
+    } else {
+        const int seg = blockIdx.x % p.P;
+        if (seg == p.P - 1 && p.state_out != nullptr)
+            chunk_pass<M, D, kStateOnly, PF, true>(p, sm);
+        else
+            chunk_pass<M, D, kStateOnly, PF, false>(p, sm);
+    }
+}
+
+// ws[b][h][j] holds each state-only sub-segment's end state from zero (j < P-1).  Replace it, in
+// place, by the state entering sub-segment j:  S_in(0) = state_in,
+// S_in(j+1) = lambda^len(j) S_in(j) + dS(j), where len(j) is the sub-segment's length.
 __global__ void __launch_bounds__(256) segment_scan_kernel(const ScanParams p) {
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (size_t)p.BH * p.dd) return;
     const int bh = (int)(idx / p.dd);
     const int e = (int)(idx - (size_t)bh * p.dd);
     const int h = bh % p.H;
-    const float lamL = p.lambda_pow_L[h];
+    const float lam_sub = p.lambda_pow_sub[h], lam_rest = p.lambda_pow_rest[h];
     float s = p.state_in ? p.state_in[idx] : 0.0f;
     float* w = p.ws + (size_t)bh * p.P * p.dd + e;
-    for (int i = 0; i < p.P; ++i) {
+    for (int i = 0, k = 0; i < p.P; ++i) {  // k = i % sub
         const float ds = (i < p.P - 1) ? w[(size_t)i * p.dd] : 0.0f;
         w[(size_t)i * p.dd] = s;
-        s = fmaf(lamL, s, ds);
+        s = fmaf(k == p.sub - 1 ? lam_rest : lam_sub, s, ds);
+        k = (k == p.sub - 1) ? 0 : k + 1;
     }
 }
 

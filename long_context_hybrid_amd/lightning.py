@@ -49,7 +49,7 @@ def _load() -> ct.CDLL:
     h.lightning_hypenet_gamma.restype = i32
     h.lightning_state_init.argtypes = [vp, i32, i32, i32, vp, vp]
     h.lightning_state_init.restype = i32
-    h.lightning_prefill_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp]
+    h.lightning_prefill_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp]
     h.lightning_prefill_plan.restype = i32
     h.lightning_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     h.lightning_prefill_workspace_size.restype = sz
@@ -145,10 +145,12 @@ def lightning_state_init(state: torch.Tensor, init: torch.Tensor | None = None, 
 
 
 def lightning_prefill_plan(B, T, H, d, dtype=torch.bfloat16, chunk=0, segments=0):
-    c, p = ct.c_int(0), ct.c_int(0)
+    """(chunk, segments, tokens per segment but the last) that lightning_prefill will use."""
+    c, p, n = ct.c_int(0), ct.c_int(0), ct.c_int(0)
     _check(lib.lightning_prefill_plan(B, T, H, d, _dtype_code(dtype), chunk, segments,
-                                      ct.byref(c), ct.byref(p)), "lightning_prefill_plan")
-    return c.value, p.value
+                                      ct.byref(c), ct.byref(p), ct.byref(n)),
+           "lightning_prefill_plan")
+    return c.value, p.value, n.value
 
 
 def lightning_prefill_workspace_size(B, T, H, d, dtype=torch.bfloat16, chunk=0, segments=0) -> int:

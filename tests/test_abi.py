@@ -81,11 +81,17 @@ def test_hypenet_gamma_time_scales():
     (1, 256, 2, 64, 1, 1),          # too short to split (8 chunks)
     (1, 300, 1, 128, 1, 1),
     (1, 4096, 1, 128, 16, 1),       # 128 chunks, 8 per segment: no further split
-    (2, 100000, 2, 64, 64, 1),      # 3125 chunks over 64 segments of 49 (not divisible)
+    (2, 100000, 2, 64, 64, 2),      # 3125 chunks over 64 segments of 49 (sub-segments 25 + 24)
 ])
 def test_plan_and_workspace(B, T, H, d, expect_p, expect_sub):
-    c, p = lt.lightning_prefill_plan(B, T, H, d)
+    c, p, seg_len = lt.lightning_prefill_plan(B, T, H, d)
     assert c == 32 and p == expect_p
+    # every segment but the last has seg_len tokens (a whole number of chunks); the last is
+    # non-empty and no longer; one segment is the whole sequence
+    if p > 1:
+        assert seg_len % 32 == 0 and 0 < T - (p - 1) * seg_len <= seg_len
+    else:
+        assert seg_len == T
     ws = lt.lightning_prefill_workspace_size(B, T, H, d)
     # one fp32 d x d state per state-only sub-segment of segments 0 .. P-2, plus the entry state
     # of the last segment
@@ -94,9 +100,9 @@ def test_plan_and_workspace(B, T, H, d, expect_p, expect_sub):
 
 
 def test_plan_explicit_segments_and_chunk():
-    assert lt.lightning_prefill_plan(1, 1000, 2, 128, segments=3) == (32, 3)
+    assert lt.lightning_prefill_plan(1, 1000, 2, 128, segments=3)[:2] == (32, 3)
     # more segments than chunks collapses to one chunk per segment
-    assert lt.lightning_prefill_plan(1, 100, 2, 128, segments=50) == (32, 4)
+    assert lt.lightning_prefill_plan(1, 100, 2, 128, segments=50)[:2] == (32, 4)
     with pytest.raises(lt.LightningError) as e:
         lt.lightning_prefill_plan(1, 1000, 2, 128, chunk=48)
     assert e.value.status == lt.LT_ERR_UNSUPPORTED
