@@ -512,8 +512,13 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
         };
 
         // prologue of one chunk: registers -> normalised, rotated, decayed tiles in LDS
-        auto prologue = [&](int chunk, const Regs& r, Tiles<M, D, kStateOnly>& t) {
-            const int n = min(C, t_end - (t_begin + chunk * C));
+        // decay of this thread's two rows in a full chunk, lambda^(C-1-j)
+        float kdec_full[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) kdec_full[s] = pow_lambda(l2l, C - 1 - (2 * rg + s));
+        // full: the chunk is known to hold C tokens (every row valid, no per-row test)
+        auto prologue = [&](int chunk, const Regs& r, Tiles<M, D, kStateOnly>& t, bool full) {
+            const int n = full ? C : min(C, t_end - (t_begin + chunk * C));
             const float2* base = sm.rope[chunk & 1];
             float2 b4[4];
 #pragma unroll
@@ -522,7 +527,7 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 const int j = 2 * rg + s;
-                const bool valid = j < n;
+                const bool valid = full || j < n;
                 float qa[8], ka[8];
                 if (!kStateOnly) {
                     A::widen(r.q[s][0], qa);
@@ -540,9 +545,13 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
                 ssk = group_sum<FG>(ssk);
                 // Rows past the segment end hold a copy of its last row; a zero scale makes their
                 // q~, k~ and decayed keys zero, so they add nothing to scores, outputs or state.
-                const float rq = valid ? fast_rsqrt(ssq * (1.0f / D) + p.eps) : 0.0f;
-                const float rk = valid ? fast_rsqrt(ssk * (1.0f / D) + p.eps) * kscale : 0.0f;
-                const float kds = valid ? rk * pow_lambda(l2l, n - 1 - j) : 0.0f;  // decayed-key scale
+                // (computed unconditionally, then selected: no divergent branch in the step)
+                const float rq0 = fast_rsqrt(ssq * (1.0f / D) + p.eps);
+                const float rk0 = fast_rsqrt(ssk * (1.0f / D) + p.eps) * kscale;
+                const float kdec = full ? kdec_full[s] : pow_lambda(l2l, n - 1 - j);
+                const float rq = valid ? rq0 : 0.0f;
+                const float rk = valid ? rk0 : 0.0f;
+                const float kds = rk * kdec;  // decayed-key scale
                 float qt[8], kt[8];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
@@ -686,7 +695,7 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
             // being stored is full; the step then has no branches and the scheduler can interleave
             // the prologue of chunk s with the epilogue of chunk s-2.
             auto step = [&](int s, Regs& cur, uint4* gep, bool steady) {
-                if (steady || s < n_chunks) prologue(s, cur, sm.buf[s & 1]);
+                if (steady || s < n_chunks) prologue(s, cur, sm.buf[s & 1], steady);
                 load(s + PF, cur);
                 if (steady || s + 1 < n_chunks) fill_rope_table(s + 1, (s + 1) & 1);
                 if (!kStateOnly && (steady || s >= 2)) {
@@ -715,7 +724,7 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
             for (int s = 0; s < n_chunks; ++s) {
                 load(s, ra);
                 if (!kStateOnly) load_gate(s, ga);
-                prologue(s, ra, sm.buf[0]);
+                prologue(s, ra, sm.buf[0], false);
                 if (s + 1 < n_chunks) fill_rope_table(s + 1, (s + 1) & 1);
                 __syncthreads();  // chunk s in LDS
                 __syncthreads();  // math done with chunk s
