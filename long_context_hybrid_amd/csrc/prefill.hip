@@ -55,6 +55,7 @@ static_assert(C == 32, "the tiling below assumes one 32-row block per chunk");
 #endif
 constexpr int kPrefetchMain = LT_PREFETCH_MAIN;
 constexpr int kPrefetchStateOnly = LT_PREFETCH_STATE;
+constexpr int kRopeAnchor = 64;  // chunks between exact recomputations of the RoPE base table
 
 // Row index inside a 32x32 accumulator tile for lane half lh and register r.
 __device__ __forceinline__ int acc_row(int r, int lh) { return 8 * (r >> 2) + 4 * lh + (r & 3); }
@@ -273,19 +274,28 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
     constexpr int EPT = 16, TPR = D / EPT;    // epilogue: 16 outputs per thread, TPR per row
     const int er = it / TPR, ec = it % TPR;
 
-    // Per-chunk RoPE base table cos/sin(p0 f_i), one frequency per lane.  A single io wavefront
-    // fills it, the io wavefronts taking turns chunk by chunk (the angle is reduced in fp64 and
-    // a full wavefront costs the same for 1 lane as for 64).  The frequency is read once: a
-    // dynamically indexed kernel-argument read is a vector memory load, and waiting for it
-    // inside the loop would also wait for the prefetches.  Lanes without a frequency write to
-    // the sink entry.
+    // Per-chunk RoPE base table cos/sin(p0 f_i), one frequency per lane, filled by a single io
+    // wavefront (the io wavefronts take turns chunk by chunk).  Most chunks advance the previous
+    // chunk's entry by the rotation C f_i (a complex product, about 1 ulp of drift per chunk);
+    // every kRopeAnchor-th chunk recomputes it from the position with the angle reduced in fp64,
+    // which bounds the drift to a few 1e-6.  The frequency is read once: a dynamically indexed
+    // kernel-argument read is a vector memory load, and waiting for it inside the loop would
+    // also wait for the prefetches.  Lanes without a frequency use the sink entry.
     const int table_i = lane < HALF ? lane : 64;
     const double table_frev = p.inv_freq_rev[min(lane, HALF - 1)];
+    float2 table_step;  // cos/sin(C f_i)
+    rope_cos_sin(C, table_frev, table_step.x, table_step.y);
     auto fill_rope_table = [&](int chunk, int slot) {
         if (wave - NW != chunk % NW) return;  // wave-uniform (there are NW io wavefronts)
-        float cs, sn;
-        rope_cos_sin(p.pos0 + t_begin + (int64_t)chunk * C, table_frev, cs, sn);
-        sm.rope[slot][table_i] = make_float2(cs, sn);
+        float2 e;
+        if (chunk % kRopeAnchor == 0) {
+            rope_cos_sin(p.pos0 + t_begin + (int64_t)chunk * C, table_frev, e.x, e.y);
+        } else {
+            const float2 a = sm.rope[slot ^ 1][table_i];  // the previous chunk's entry
+            e.x = a.x * table_step.x - a.y * table_step.y;
+            e.y = a.y * table_step.x + a.x * table_step.y;
+        }
+        sm.rope[slot][table_i] = e;
     };
 
     if (!kStateOnly)
