@@ -271,8 +271,10 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
     constexpr int FG = D / 8;                 // prologue: threads per row group
     const int it = threadIdx.x - 64 * NW;     // io thread index (negative in math waves)
     const int fg = it % FG, rg = it / FG;     // rows 2 rg + s, features 4 fg + u and HALF + 4 fg + u
-    constexpr int EPT = 16, TPR = D / EPT;    // epilogue: 16 outputs per thread, TPR per row
-    const int er = it / TPR, ec = it % TPR;
+    // ---- output epilogue (math wavefronts, thread index threadIdx.x < 64 NW) ----
+    constexpr int EPT = 16, TPR = D / EPT;    // 16 outputs per thread, TPR threads per row
+    const int er = threadIdx.x / TPR, ec = threadIdx.x % TPR;
+    static_assert(64 * NW / TPR == C, "the math wavefronts cover the chunk's rows");
 
     // Per-chunk RoPE base table cos/sin(p0 f_i), one frequency per lane, filled by a single io
     // wavefront (the io wavefronts take turns chunk by chunk).  Most chunks advance the previous
@@ -320,6 +322,82 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
         }
     }
     __syncthreads();
+
+    // Row addresses: a uniform per-chunk base plus a 32-bit per-lane offset.  Loads are
+    // unconditional (rows past the segment end re-read its last row), which keeps the
+    // memory-wait bookkeeping exact across iterations.
+    const uint32_t rs32 = (uint32_t)row_stride;
+    auto chunk_start = [&](int chunk) { return t_begin + min(chunk, n_chunks - 1) * C; };
+    const In* gg = static_cast<const In*>(p.g) + head_base;
+    In* gy = static_cast<In*>(p.y) + head_base;
+    // epilogue of one chunk: y = RMSNorm(o) * w_o * sigmoid(g)
+    constexpr int GV = EPT * sizeof(In) / 16;  // 16-byte vectors of gate logits per thread
+    auto load_gate = [&](int chunk, uint4* gr) {
+        const int cs = chunk_start(chunk);
+        const uint32_t o = (uint32_t)min(er, t_end - 1 - cs) * rs32 + EPT * ec;
+        const uint4* src = reinterpret_cast<const uint4*>(gg + (size_t)cs * row_stride + o);
+#pragma unroll
+        for (int i = 0; i < GV; ++i) gr[i] = src[i];
+    };
+    auto epilogue = [&](int chunk, const float* o_stage, const uint4* gr, bool full) {
+        const int t = t_begin + chunk * C + er;
+        float o[EPT];
+        const float* orow = o_stage + er * OS + EPT * ec;
+#pragma unroll
+        for (int i = 0; i < EPT / 4; ++i) {
+            const float4 x = *reinterpret_cast<const float4*>(orow + 4 * i);
+            o[4 * i] = x.x; o[4 * i + 1] = x.y; o[4 * i + 2] = x.z; o[4 * i + 3] = x.w;
+        }
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) ss = fmaf(o[i], o[i], ss);
+        ss = group_sum<TPR>(ss);
+        const float rinv = fast_rsqrt(ss * (1.0f / D) + p.eps);
+        if (!full && t >= t_end) return;
+        float gl[EPT];
+        if constexpr (sizeof(In) == 2) {
+#pragma unroll
+            for (int i = 0; i < GV; ++i) {
+                const uint4 x = gr[i];
+                gl[8 * i + 0] = bf16_lo(x.x); gl[8 * i + 1] = bf16_hi(x.x);
+                gl[8 * i + 2] = bf16_lo(x.y); gl[8 * i + 3] = bf16_hi(x.y);
+                gl[8 * i + 4] = bf16_lo(x.z); gl[8 * i + 5] = bf16_hi(x.z);
+                gl[8 * i + 6] = bf16_lo(x.w); gl[8 * i + 7] = bf16_hi(x.w);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < GV; ++i) {
+                const uint4 x = gr[i];
+                gl[4 * i + 0] = __uint_as_float(x.x); gl[4 * i + 1] = __uint_as_float(x.y);
+                gl[4 * i + 2] = __uint_as_float(x.z); gl[4 * i + 3] = __uint_as_float(x.w);
+            }
+        }
+        float yv[EPT];  // (w_o holds ones when the output norm has no weight)
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) yv[i] = o[i] * (rinv * sm.wo[EPT * ec + i]) * sigmoidf_(gl[i]);
+        const size_t off = (size_t)(t - er) * row_stride + ((uint32_t)er * rs32 + EPT * ec);
+        if constexpr (sizeof(In) == 2) {
+            uint4* dst = reinterpret_cast<uint4*>(gy + off);
+#pragma unroll
+            for (int i = 0; i < GV; ++i)
+                dst[i] = make_uint4(pack_bf16x2(yv[8 * i], yv[8 * i + 1]),
+                                    pack_bf16x2(yv[8 * i + 2], yv[8 * i + 3]),
+                                    pack_bf16x2(yv[8 * i + 4], yv[8 * i + 5]),
+                                    pack_bf16x2(yv[8 * i + 6], yv[8 * i + 7]));
+        } else {
+            float4* dst = reinterpret_cast<float4*>(gy + off);
+#pragma unroll
+            for (int i = 0; i < GV; ++i)
+                dst[i] = make_float4(yv[4 * i], yv[4 * i + 1], yv[4 * i + 2], yv[4 * i + 3]);
+        }
+        if (p.o_raw) {
+            float4* dst = reinterpret_cast<float4*>(p.o_raw + head_base + off);
+#pragma unroll
+            for (int i = 0; i < EPT / 4; ++i)
+                dst[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+        }
+    };
+
 
     if (is_math) {
         // ============================ math wavefronts ============================
@@ -438,17 +516,31 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
         };
 
         if constexpr (kOverlap) {
-            // step s: math processes chunk s-1 (steps 1 .. n_chunks); io runs ahead/behind
+            // Step s: the io wavefronts stage chunk s, the math wavefronts write the outputs of
+            // chunk s-2 (staged in step s-1) and then process chunk s-1.  The gate logits of a
+            // chunk are loaded one step before its outputs.
+            uint4 gcur[GV];
+            if (!kStateOnly) load_gate(0, gcur);
             for (int s = 0; s < n_steps; ++s) {
+                if (!kStateOnly && s >= 2 && s - 2 < n_chunks) {
+                    epilogue(s - 2, sm.o + (s & 1) * C * OS, gcur, s - 1 < n_chunks);
+                    load_gate(s - 1, gcur);
+                }
                 if (s >= 1 && s <= n_chunks)
                     compute(s - 1, sm.buf[(s - 1) & 1], kStateOnly ? nullptr : sm.o + ((s - 1) & 1) * C * OS);
                 __syncthreads();
             }
         } else {
+            uint4 gcur[GV];
+            if (!kStateOnly) load_gate(0, gcur);
             for (int s = 0; s < n_chunks; ++s) {
                 __syncthreads();  // chunk s in LDS
                 compute(s, sm.buf[0], kStateOnly ? nullptr : sm.o);
                 __syncthreads();  // tiles consumed, output staged
+                if (!kStateOnly) {
+                    epilogue(s, sm.o, gcur, s + 1 < n_chunks);
+                    load_gate(s + 1, gcur);
+                }
             }
         }
 
@@ -469,8 +561,6 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
         const In* gq = static_cast<const In*>(p.q) + head_base;
         const In* gk = static_cast<const In*>(p.k) + head_base;
         const In* gv = static_cast<const In*>(p.v) + head_base;
-        const In* gg = static_cast<const In*>(p.g) + head_base;
-        In* gy = static_cast<In*>(p.y) + head_base;
 
         float wq[8], wk[8];
         {
@@ -499,11 +589,7 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
         struct Regs {
             V4 q[2][2], k[2][2], v[2][2];  // [row s][half]
         };
-        // Loads are unconditional (rows past the segment end re-read its last row and are zeroed
-        // by the prologue), which keeps the memory-wait bookkeeping exact across iterations.
-        // Row addresses: a uniform per-chunk base plus a 32-bit per-lane offset.
-        const uint32_t rs32 = (uint32_t)row_stride;
-        auto chunk_start = [&](int chunk) { return t_begin + min(chunk, n_chunks - 1) * C; };
+        // (rows past the segment end re-read its last row; the prologue zeroes them)
         auto load = [&](int chunk, Regs& r) {
             const int cs = chunk_start(chunk);
             const size_t cb = (size_t)cs * row_stride;
@@ -622,123 +708,43 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
             }
         };
 
-        // epilogue of one chunk: y = RMSNorm(o) * w_o * sigmoid(g)
-        constexpr int GV = EPT * sizeof(In) / 16;  // 16-byte vectors of gate logits per thread
-        auto load_gate = [&](int chunk, uint4* gr) {
-            const int cs = chunk_start(chunk);
-            const uint32_t o = (uint32_t)min(er, t_end - 1 - cs) * rs32 + EPT * ec;
-            const uint4* src = reinterpret_cast<const uint4*>(gg + (size_t)cs * row_stride + o);
-#pragma unroll
-            for (int i = 0; i < GV; ++i) gr[i] = src[i];
-        };
-        auto epilogue = [&](int chunk, const float* o_stage, const uint4* gr, bool full) {
-            const int t = t_begin + chunk * C + er;
-            float o[EPT];
-            const float* orow = o_stage + er * OS + EPT * ec;
-#pragma unroll
-            for (int i = 0; i < EPT / 4; ++i) {
-                const float4 x = *reinterpret_cast<const float4*>(orow + 4 * i);
-                o[4 * i] = x.x; o[4 * i + 1] = x.y; o[4 * i + 2] = x.z; o[4 * i + 3] = x.w;
-            }
-            float ss = 0.0f;
-#pragma unroll
-            for (int i = 0; i < EPT; ++i) ss = fmaf(o[i], o[i], ss);
-            ss = group_sum<TPR>(ss);
-            const float rinv = fast_rsqrt(ss * (1.0f / D) + p.eps);
-            if (!full && t >= t_end) return;
-            float gl[EPT];
-            if constexpr (sizeof(In) == 2) {
-#pragma unroll
-                for (int i = 0; i < GV; ++i) {
-                    const uint4 x = gr[i];
-                    gl[8 * i + 0] = bf16_lo(x.x); gl[8 * i + 1] = bf16_hi(x.x);
-                    gl[8 * i + 2] = bf16_lo(x.y); gl[8 * i + 3] = bf16_hi(x.y);
-                    gl[8 * i + 4] = bf16_lo(x.z); gl[8 * i + 5] = bf16_hi(x.z);
-                    gl[8 * i + 6] = bf16_lo(x.w); gl[8 * i + 7] = bf16_hi(x.w);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < GV; ++i) {
-                    const uint4 x = gr[i];
-                    gl[4 * i + 0] = __uint_as_float(x.x); gl[4 * i + 1] = __uint_as_float(x.y);
-                    gl[4 * i + 2] = __uint_as_float(x.z); gl[4 * i + 3] = __uint_as_float(x.w);
-                }
-            }
-            float yv[EPT];  // (w_o holds ones when the output norm has no weight)
-#pragma unroll
-            for (int i = 0; i < EPT; ++i) yv[i] = o[i] * (rinv * sm.wo[EPT * ec + i]) * sigmoidf_(gl[i]);
-            const size_t off = (size_t)(t - er) * row_stride + ((uint32_t)er * rs32 + EPT * ec);
-            if constexpr (sizeof(In) == 2) {
-                uint4* dst = reinterpret_cast<uint4*>(gy + off);
-#pragma unroll
-                for (int i = 0; i < GV; ++i)
-                    dst[i] = make_uint4(pack_bf16x2(yv[8 * i], yv[8 * i + 1]),
-                                        pack_bf16x2(yv[8 * i + 2], yv[8 * i + 3]),
-                                        pack_bf16x2(yv[8 * i + 4], yv[8 * i + 5]),
-                                        pack_bf16x2(yv[8 * i + 6], yv[8 * i + 7]));
-            } else {
-                float4* dst = reinterpret_cast<float4*>(gy + off);
-#pragma unroll
-                for (int i = 0; i < GV; ++i)
-                    dst[i] = make_float4(yv[4 * i], yv[4 * i + 1], yv[4 * i + 2], yv[4 * i + 3]);
-            }
-            if (p.o_raw) {
-                float4* dst = reinterpret_cast<float4*>(p.o_raw + head_base + off);
-#pragma unroll
-                for (int i = 0; i < EPT / 4; ++i)
-                    dst[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
-            }
-        };
-
         if constexpr (kOverlap) {
             // PF register sets hold the q/k/v (and gate logits) of the next PF chunks, so each load
             // is issued PF steps before its use; the step loop is unrolled by PF so the sets stay
             // static registers.
             Regs rs[PF];
-            uint4 gs[PF][GV];
 #pragma unroll
-            for (int i = 0; i < PF; ++i) {
-                load(i, rs[i]);
-                if (!kStateOnly) load_gate(i, gs[i]);
-            }
-            // `steady`: 2 <= s and s + 1 < n_chunks, so every part of the step runs and the chunk
-            // being stored is full; the step then has no branches and the scheduler can interleave
-            // the prologue of chunk s with the epilogue of chunk s-2.
-            auto step = [&](int s, Regs& cur, uint4* gep, bool steady) {
+            for (int i = 0; i < PF; ++i) load(i, rs[i]);
+            // `steady`: s + 1 < n_chunks, so the chunk staged is full and the next one exists; the
+            // step then has no branches.
+            auto step = [&](int s, Regs& cur, bool steady) {
                 if (steady || s < n_chunks) prologue(s, cur, sm.buf[s & 1], steady);
                 load(s + PF, cur);
                 if (steady || s + 1 < n_chunks) fill_rope_table(s + 1, (s + 1) & 1);
-                if (!kStateOnly && (steady || s >= 2)) {
-                    epilogue(s - 2, sm.o + (s & 1) * C * OS, gep, steady);
-                    load_gate(s - 2 + PF, gep);
-                }
                 __syncthreads();
             };
             // The first round is peeled (the loop header then sees the same in-flight loads from
             // both of its predecessors and waits only for the chunk it consumes), steady rounds
             // follow, and the remaining rounds handle the pipeline drain.
 #pragma unroll
-            for (int i = 0; i < PF; ++i) step(i, rs[i], gs[(i + PF - 2) % PF], false);
+            for (int i = 0; i < PF; ++i) step(i, rs[i], false);
             int s0 = PF;
             for (; s0 + PF < n_chunks; s0 += PF) {
 #pragma unroll
-                for (int i = 0; i < PF; ++i) step(s0 + i, rs[i], gs[(i + PF - 2) % PF], true);
+                for (int i = 0; i < PF; ++i) step(s0 + i, rs[i], true);
             }
             for (; s0 < n_steps; s0 += PF) {
 #pragma unroll
-                for (int i = 0; i < PF; ++i) step(s0 + i, rs[i], gs[(i + PF - 2) % PF], false);
+                for (int i = 0; i < PF; ++i) step(s0 + i, rs[i], false);
             }
         } else {
             Regs ra;
-            uint4 ga[GV];
             for (int s = 0; s < n_chunks; ++s) {
                 load(s, ra);
-                if (!kStateOnly) load_gate(s, ga);
                 prologue(s, ra, sm.buf[0], false);
                 if (s + 1 < n_chunks) fill_rope_table(s + 1, (s + 1) & 1);
                 __syncthreads();  // chunk s in LDS
                 __syncthreads();  // math done with chunk s
-                if (!kStateOnly) epilogue(s, sm.o, ga, false);
             }
         }
     }
