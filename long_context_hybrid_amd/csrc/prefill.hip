@@ -60,6 +60,22 @@ constexpr int kRopeAnchor = 64;  // chunks between exact recomputations of the R
 // Row index inside a 32x32 accumulator tile for lane half lh and register r.
 __device__ __forceinline__ int acc_row(int r, int lh) { return 8 * (r >> 2) + 4 * lh + (r & 3); }
 
+// The chunk loop keeps the state lazily decayed: state = alpha * S with alpha = lambda^X, where
+// X counts the tokens since the last renormalisation, so most chunks skip the d x d rescale and
+// instead divide their decayed keys by alpha.  Every renorm_period chunks (counted from the
+// segment start) S absorbs alpha and alpha returns to 1; the period keeps alpha >= 2^-20, so S
+// stays within 2^20 of the state's own magnitude.  lambda = 0 renormalises every chunk and
+// lambda = 1 never needs to.
+__device__ __forceinline__ int renorm_period(float log2_lambda) {
+    const float r = 20.0f / ((float)C * -log2_lambda);
+    return r >= 1048576.0f ? 1048576 : max(1, (int)r);
+}
+// X after chunk `chunk` (0-based within the segment) holding n tokens
+__device__ __forceinline__ int lazy_exponent(int chunk, int period, int n) {
+    const int cr = chunk % period;
+    return cr == 0 ? 0 : C * (cr - 1) + n;
+}
+
 // Placement of the contraction index inside an LDS tile row.
 //   kpos: bits 2 and 3 exchanged.  A product whose k order follows the accumulator layout
 //         (k = 16 st + 8 (e / 4) + 4 lh + e % 4 for operand element e) then reads one contiguous,
@@ -417,12 +433,17 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
         // this lane's decay factors, kept in LDS rather than in 32 registers for the whole loop
         const float* dec = reinterpret_cast<const float*>(sm.dec + 8 * lane);
         const float lam_full = pow_lambda(l2l, C);
+        const int period = renorm_period(l2l);
+        float alpha = 1.0f;  // state = alpha * S
 
         using L = Layout<M>;
         const int vsw = L::tsw(32 * w + lm);
         auto compute = [&](int chunk, const Tiles<M, D, kStateOnly>& t, float* o_stage) {
             const int n = min(C, t_end - (t_begin + chunk * C));
-            const float carry = (n == C) ? lam_full : pow_lambda(l2l, n);
+            const bool renorm = chunk % period == 0;
+            // renormalising chunks fold alpha and this chunk's decay into S
+            const float carry = alpha * ((n == C) ? lam_full : pow_lambda(l2l, n));
+            const float alpha_next = pow_lambda(l2l, lazy_exponent(chunk, period, n));
             const E* vrow = t.vT + (32 * w + lm) * TS;
             if constexpr (M::kSplit) {
                 // bf16 operands.  With the kpos placement the 16-byte block at 16 s + 8 lh of a
@@ -446,7 +467,7 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         pt[r] *= dec[r];
-                        o[r] *= dec[16 + r];
+                        o[r] *= dec[16 + r] * alpha;
                     }
                 }
                 // P V and the state update read the same V blocks
@@ -465,11 +486,14 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
 #pragma unroll
                     for (int r = 0; r < 16; ++r) o_stage[acc_row(r, lh) * OS + 32 * w + lm] = o[r];
                 }
-                // state update S <- lambda^n S + K'^T V, the NW accumulators interleaved
+                // state update S <- carry S + K'^T V (K' already divided by the new alpha), the NW
+                // accumulators interleaved
+                if (renorm) {
 #pragma unroll
-                for (int c = 0; c < NW; ++c)
+                    for (int c = 0; c < NW; ++c)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) S[c][r] *= carry;
+                        for (int r = 0; r < 16; ++r) S[c][r] *= carry;
+                }
 #pragma unroll
                 for (int st = 0; st < 2; ++st) {
                     bf16x8 ah[NW], al[NW];
@@ -499,20 +523,23 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
 #pragma unroll
                     for (int c = 0; c < NW; ++c) contract_acc(o, S[c], t.q + lm * QS + 32 * c, lh, false);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) o[r] *= dec[16 + r];
+                    for (int r = 0; r < 16; ++r) o[r] *= dec[16 + r] * alpha;
                     // intra-chunk term P V, A operand from the score registers
                     contract_acc(o, pt, vrow, lh, true, vsw);
 #pragma unroll
                     for (int r = 0; r < 16; ++r) o_stage[acc_row(r, lh) * OS + 32 * w + lm] = o[r];
                 }
+                if (renorm) {
 #pragma unroll
-                for (int c = 0; c < NW; ++c)
+                    for (int c = 0; c < NW; ++c)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) S[c][r] *= carry;
+                        for (int r = 0; r < 16; ++r) S[c][r] *= carry;
+                }
 #pragma unroll
                 for (int c = 0; c < NW; ++c)
                     contract_rows<C>(S[c], t.khT + (32 * c + lm) * TS, vrow, lh, L::tsw(32 * c + lm), vsw);
             }
+            alpha = alpha_next;
         };
 
         if constexpr (kOverlap) {
@@ -554,7 +581,7 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
             for (int c = 0; c < NW; ++c)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    dst[(size_t)(32 * c + acc_row(r, lh)) * D + 32 * w + lm] = S[c][r];
+                    dst[(size_t)(32 * c + acc_row(r, lh)) * D + 32 * w + lm] = alpha * S[c][r];
         }
     } else {
         // ============================= io wavefronts =============================
@@ -612,9 +639,11 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
         float kdec_full[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) kdec_full[s] = pow_lambda(l2l, C - 1 - (2 * rg + s));
+        const int period = renorm_period(l2l);  // the math wavefronts' lazy state scale
         // full: the chunk is known to hold C tokens (every row valid, no per-row test)
         auto prologue = [&](int chunk, const Regs& r, Tiles<M, D, kStateOnly>& t, bool full) {
             const int n = full ? C : min(C, t_end - (t_begin + chunk * C));
+            const float inv_alpha = pow_lambda(l2l, -lazy_exponent(chunk, period, C));  // full chunks
             const float2* base = sm.rope[chunk & 1];
             float2 b4[4];
 #pragma unroll
@@ -644,7 +673,9 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
                 // (computed unconditionally, then selected: no divergent branch in the step)
                 const float rq0 = fast_rsqrt(ssq * (1.0f / D) + p.eps);
                 const float rk0 = fast_rsqrt(ssk * (1.0f / D) + p.eps) * kscale;
-                const float kdec = full ? kdec_full[s] : pow_lambda(l2l, n - 1 - j);
+                // lambda^(n-1-j) / alpha, alpha = lambda^X the state's scale after this chunk
+                const float kdec = full ? kdec_full[s] * inv_alpha
+                                        : pow_lambda(l2l, n - 1 - j - lazy_exponent(chunk, period, n));
                 const float rq = valid ? rq0 : 0.0f;
                 const float rk = valid ? rk0 : 0.0f;
                 const float kds = rk * kdec;  // decayed-key scale
