@@ -27,6 +27,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic_qwen17_512k.md")
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 METRIC = "prefill tokens/s/layer at T=512K (MFMA %) ; decode step µs at B=64 (HBM %)"
 
@@ -60,6 +61,41 @@ def copy_calibration(torch, mib):
         dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
+
+
+def source_fingerprint():
+    """sha256 over the library's kernel and ABI sources (the code the byte counters measured)."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "long_context_hybrid_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "lightning.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    record, scaled by what the same counters read for a plain copy of known size; None when no
+    record exists for this workload or the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_RECORD) as fh:
+            lines = [l for l in fh if l.startswith("traffic-record: ")]
+    except OSError:
+        return None
+    if not lines:
+        return None
+    rec = json.loads(lines[-1][len("traffic-record: "):])
+    if rec.get("source_sha256") != source_fingerprint():
+        return None
+    k = rec["kernels"].get(kernel)
+    if k is None or k.get("workload") != workload:
+        return None
+    return int(round((k["fetch_kib"] * rec["fetch_scale"] + k["write_kib"] * rec["write_scale"]) * 1024))
 
 
 class HipEvents:
@@ -137,7 +173,8 @@ def bench_prefill(args, torch, lt, synth):
         spec=spec, inp=inp, chunk=chunk, P=P, ms_per_step=ms_per_step, main_ms=main_ms,
         value=tokens / (ms_per_step * 1e-3),
         roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                  "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                  "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                  "traffic": measured_traffic("main", spec.name),
                   "kernel": "chunk_kernel<ModeBF16,128,false> (main chunk loop)",
                   "alg_bytes_per_launch": alg_bytes, "bytes_per_token_head": per_unit,
                   "launch_ms": round(main_ms, 4)},
@@ -176,7 +213,8 @@ def bench_decode(args, torch, lt, synth):
     gbs = alg / (us * 1e-6) / 1e9
     return {"workload": spec.name, "us_per_step": round(us, 3),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("decode", spec.name),
                          "kernel": "decode_kernel<ModeBF16,128>", "alg_bytes_per_launch": alg,
                          "bytes_per_bh": per_bh},
             "state_buffers": len(states)}
