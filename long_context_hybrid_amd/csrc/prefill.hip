@@ -782,9 +782,10 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
 }
 
 // bf16 mode updates the state with hi + lo parts of the decayed keys (fp32-accurate) where the
-// state leaves the kernel: in the state-only pass, whose sums become segment entry states, and in
-// the last segment when the final state is requested.  Inside the other segments the state only
-// feeds outputs (bf16, normalised), and the hi part alone is used.  The choice is per workgroup
+// result reaches the final state unattenuated: in the last segment, and in state-only
+// sub-segments near the end, when the final state is requested.  Elsewhere the state only feeds
+// outputs (bf16, normalised) or reaches the final state strongly decayed, and the hi part alone
+// is used.  The choice is per workgroup
 // and made once, so each pass is branch-free inside its loop.
 // The state-only pass is register-limited so that kStateOnlyBlocksPerCU of its workgroups share
 // a CU (their barriers are independent, so one hides the other's stalls).
@@ -793,15 +794,27 @@ __global__ void __launch_bounds__(128 * (D / 32))
 __attribute__((amdgpu_waves_per_eu(kStateOnly ? kStateOnlyBlocksPerCU * D / 64 : 1)))
 chunk_kernel(const ChunkParams p) {
     __shared__ Smem<M, D, kStateOnly> sm;
-    if constexpr (kStateOnly || !M::kSplit) {
-        chunk_pass<M, D, kStateOnly, PF, true>(p, sm);
-    } else {
-        const int seg = blockIdx.x % p.P;
-        if (seg == p.P - 1 && p.state_out != nullptr)
-            chunk_pass<M, D, kStateOnly, PF, true>(p, sm);
-        else
-            chunk_pass<M, D, kStateOnly, PF, false>(p, sm);
+    bool precise = true;
+    if constexpr (M::kSplit) {
+        if constexpr (kStateOnly) {
+            // A sub-segment's sum reaches the final state attenuated by lambda^(T - its end).
+            // Below 2^-8 the hi-only sum's rounding (about 2^-9 relative) lands under 2^-17 of the
+            // final state, so the low parts are needed only for sub-segments closer to the end
+            // than that, and only when the final state is requested; entry states feeding the
+            // outputs alone do not need them.
+            const int nseg = p.SP - 1;
+            const int seg = blockIdx.x % nseg, h = (blockIdx.x / nseg) % p.H;
+            const int s0 = seg / p.SM, s1 = seg - s0 * p.SM;
+            const int t_end = min((s0 + 1) * p.L, s0 * p.L + (s1 + 1) * p.SL);
+            precise = p.state_out != nullptr && p.log2_lambda[h] * (float)(p.T - t_end) > -8.0f;
+        } else {
+            precise = blockIdx.x % p.P == p.P - 1 && p.state_out != nullptr;
+        }
     }
+    if (precise)
+        chunk_pass<M, D, kStateOnly, PF, true>(p, sm);
+    else
+        chunk_pass<M, D, kStateOnly, PF, false>(p, sm);
 }
 
 // ws[b][h][j] holds each state-only sub-segment's end state from zero (j < P-1).  Replace it, in
