@@ -118,9 +118,10 @@ struct alignas(16) Tiles {
     using E = typename G::E;
     alignas(16) E q[kStateOnly ? 1 : C * G::QS];   // q~ [token][key dim]
     alignas(16) E k[kStateOnly ? 1 : C * G::QS];   // k~ [token][key dim]
-    alignas(16) E khT[D * G::TS];                  // decayed keys, hi part, [key dim][token]
-    alignas(16) E klT[M::kSplit ? D * G::TS : 1];  // decayed keys, lo part
-    alignas(16) E vT[D * G::TS];                   // v [value dim][token]
+    // decayed keys (hi part) and v: bf16 mode [token][dim] (nat_index), fp32 mode [dim][token]
+    alignas(16) E khT[D * G::TS];
+    alignas(16) E klT[M::kSplit ? D * G::TS : 1];  // decayed keys, lo part (bf16 mode)
+    alignas(16) E vT[D * G::TS];
 };
 
 template <class M, int D, bool kStateOnly>
@@ -168,6 +169,37 @@ __device__ __forceinline__ void st_pair(float* dst, float4 row0, float4 row1, in
     const float a = u == 0 ? row0.x : u == 1 ? row0.y : u == 2 ? row0.z : row0.w;
     const float b = u == 0 ? row1.x : u == 1 ? row1.y : u == 2 ? row1.z : row1.w;
     *reinterpret_cast<float2*>(dst) = make_float2(a, b);
+}
+
+// bf16 tiles of decayed keys and values are kept in natural [token][feature] order with D-element
+// rows.  The 32-feature blocks of a row are XOR-permuted by the row's position within a 256-byte
+// bank window, so that an MFMA operand gathered across four consecutive rows with
+// ds_read_b64_tr_b16 touches 64 distinct banks.
+template <int D>
+__device__ __forceinline__ int nat_index(int row, int col) {
+    return row * D + (col ^ (32 * ((row / (128 / D)) % (D / 32))));
+}
+// An MFMA operand whose m (or n) index runs along the rows of a natural tile, with its 16 k
+// values (tokens kbase .. kbase + 15) in accumulator order: lane l receives column
+// colbase + l % 32 of row kbase + 8 (e / 4) + 4 (l / 32) + e % 4 in element e < 8, the order in
+// which a score accumulator re-typed to bf16 holds its tokens (so P V and the state update can
+// share the V operand; any common order serves the state update).  ds_read_b64_tr_b16 gives lane
+// 4a + c of each 16-lane group element c of the 4-element row segments addressed by lanes a,
+// 4 + a, 8 + a and 12 + a of that group; lane s therefore addresses row
+// kbase + 4 (group / 2) + s / 4 at column colbase + 16 (group % 2) + 4 (s % 4), and a second read
+// does the rows 8 further on.
+typedef short tr16x4 __attribute__((ext_vector_type(4)));
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const __bf16* tile, int kbase, int colbase, int lane) {
+    const int g = lane >> 4, sl = lane & 15;
+    const int row = kbase + 4 * (g >> 1) + (sl >> 2);
+    const int col = colbase + 16 * (g & 1) + 4 * (sl & 3);
+    typedef __attribute__((address_space(3))) tr16x4 lds_t;
+    const tr16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_t*)(tile + nat_index<D>(row, col)));
+    const tr16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_t*)(tile + nat_index<D>(row + 8, col)));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, ab);
 }
 
 // LDS stores of 4 (row-major tiles) or 2 (transposed tiles) consecutive elements.
@@ -473,8 +505,7 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
                 // P V and the state update read the same V blocks
                 bf16x8 vb[2];
 #pragma unroll
-                for (int st = 0; st < 2; ++st)
-                    vb[st] = *reinterpret_cast<const bf16x8*>(vrow + ((16 * st + 8 * lh) ^ vsw));
+                for (int st = 0; st < 2; ++st) vb[st] = tr_operand<D>(t.vT, 16 * st, 32 * w, lane);
                 if (!kStateOnly) {
 #pragma unroll
                     for (int st = 0; st < 2; ++st) {
@@ -499,9 +530,8 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
                     bf16x8 ah[NW], al[NW];
 #pragma unroll
                     for (int c = 0; c < NW; ++c) {
-                        const int off = (32 * c + lm) * TS + ((16 * st + 8 * lh) ^ L::tsw(32 * c + lm));
-                        ah[c] = *reinterpret_cast<const bf16x8*>(t.khT + off);
-                        if (precise) al[c] = *reinterpret_cast<const bf16x8*>(t.klT + off);
+                        ah[c] = tr_operand<D>(t.khT, 16 * st, 32 * c, lane);
+                        if (precise) al[c] = tr_operand<D>(t.klT, 16 * st, 32 * c, lane);
                     }
 #pragma unroll
                     for (int c = 0; c < NW; ++c) S[c] = mfma_bf16(ah[c], vb[st], S[c]);
@@ -710,31 +740,34 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
                     st4(kdst + HALF + c0, kt[4], kt[5], kt[6], kt[7]);
                 }
             }
-            const int jp = Layout<M>::kpos(2 * rg);  // the two tokens stay adjacent
-            auto tcol = [&](int i) {
-                const int f = (i < 4) ? 4 * fg + i : HALF + 4 * fg + (i - 4);
-                return f * TS + (jp ^ Layout<M>::tsw(f));
-            };
-            uint32_t hi[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int col = tcol(i);
-                if constexpr (M::kSplit) {
-                    hi[i] = pack_bf16x2(kd[0][i], kd[1][i]);  // two tokens per instruction
-                    *reinterpret_cast<uint32_t*>(t.khT + col) = hi[i];
-                } else {
-                    st2(t.khT + col, kd[0][i], kd[1][i]);
-                }
-                st_pair(t.vT + col, r.v[0][i / 4], r.v[1][i / 4], i % 4);
-            }
             if constexpr (M::kSplit) {
-                if (precise) {
-                    // lo = bf16(k' - hi): hi + lo carries k' to about 16 significant bits
+                // natural [token][feature] tiles: v as loaded, decayed keys as bf16 hi (+ lo)
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const float lo0 = kd[0][i] - bf16_lo(hi[i]), lo1 = kd[1][i] - bf16_hi(hi[i]);
-                        *reinterpret_cast<uint32_t*>(t.klT + tcol(i)) = pack_bf16x2(lo0, lo1);
+                for (int s = 0; s < 2; ++s) {
+                    const int j = 2 * rg + s;
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const int col = nat_index<D>(j, hf * HALF + 4 * fg);
+                        const float* x = kd[s] + 4 * hf;
+                        const uint2 hi = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+                        *reinterpret_cast<uint2*>(t.khT + col) = hi;
+                        *reinterpret_cast<uint2*>(t.vT + col) = r.v[s][hf];
+                        if (precise) {
+                            // lo = bf16(k' - hi): hi + lo carries k' to about 16 significant bits
+                            *reinterpret_cast<uint2*>(t.klT + col) =
+                                make_uint2(pack_bf16x2(x[0] - bf16_lo(hi.x), x[1] - bf16_hi(hi.x)),
+                                           pack_bf16x2(x[2] - bf16_lo(hi.y), x[3] - bf16_hi(hi.y)));
+                        }
                     }
+                }
+            } else {
+                const int jp = Layout<M>::kpos(2 * rg);  // the two tokens stay adjacent
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int f = (i < 4) ? 4 * fg + i : HALF + 4 * fg + (i - 4);
+                    const int col = f * TS + (jp ^ Layout<M>::tsw(f));
+                    st2(t.khT + col, kd[0][i], kd[1][i]);
+                    st_pair(t.vT + col, r.v[0][i / 4], r.v[1][i / 4], i % 4);
                 }
             }
         };
