@@ -100,8 +100,12 @@ struct Layout<ModeF32> {  // fp32 tiles keep the natural placement
 template <class M, int D, bool kStateOnly>
 struct Cfg {
     using E = typename M::E;
-    static constexpr int NW = D / 32;                 // math wavefronts = io wavefronts
-    static constexpr int NT = 128 * NW;               // threads per workgroup
+    static constexpr int NW = D / 32;                 // math wavefronts
+    // The bf16 main pass has two io wavefronts per SIMD (a lone wavefront issues VALU work at
+    // about half the rate two do) and they also run the output stage; elsewhere one.
+    static constexpr bool kWideIo = M::kSplit && !kStateOnly;
+    static constexpr int NIO = kWideIo ? 2 * NW : NW;  // io wavefronts
+    static constexpr int NT = 64 * (NW + NIO);        // threads per workgroup
     static constexpr int HALF = D / 2;
     static constexpr int kPad = (sizeof(E) == 2) ? 8 : 4;  // 16 bytes of padding per row
     static constexpr int QS = D + kPad;               // row stride of q~/k~ tiles [token][dim]
@@ -281,7 +285,8 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
     using In = typename M::In;
     using A = Act<M>;
     using V4 = typename A::V4;
-    constexpr int NW = G::NW, HALF = G::HALF, QS = G::QS, TS = G::TS, OS = G::OS;
+    constexpr int NW = G::NW, NIO = G::NIO, HALF = G::HALF, QS = G::QS, TS = G::TS, OS = G::OS;
+    constexpr bool kEpiIo = G::kWideIo;  // the output stage runs on the io wavefronts
     constexpr int NBUF = G::NBUF;
     constexpr bool kOverlap = G::kOverlap;
 
@@ -316,13 +321,17 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
     const size_t head_base = ((size_t)b * p.T * p.H + h) * D;
 
     // ---- io-role constants ----
+    constexpr int RPT = 2 * NW / NIO;         // rows per io thread (2, or 1 with two io per SIMD)
     constexpr int FG = D / 8;                 // prologue: threads per row group
     const int it = threadIdx.x - 64 * NW;     // io thread index (negative in math waves)
-    const int fg = it % FG, rg = it / FG;     // rows 2 rg + s, features 4 fg + u and HALF + 4 fg + u
-    // ---- output epilogue (math wavefronts, thread index threadIdx.x < 64 NW) ----
-    constexpr int EPT = 16, TPR = D / EPT;    // 16 outputs per thread, TPR threads per row
-    const int er = threadIdx.x / TPR, ec = threadIdx.x % TPR;
-    static_assert(64 * NW / TPR == C, "the math wavefronts cover the chunk's rows");
+    const int fg = it % FG, rg = it / FG;     // rows RPT rg + s, features 4 fg + u and HALF + 4 fg + u
+    static_assert(64 * NIO / FG * RPT == C, "the io wavefronts cover the chunk's rows");
+    // ---- output stage (io or math wavefronts) ----
+    constexpr int ETH = 64 * (kEpiIo ? NIO : NW);  // its threads
+    constexpr int EPT = C * D / ETH, TPR = D / EPT;  // outputs per thread, threads per row
+    const int et = kEpiIo ? it : (int)threadIdx.x;
+    const int er = et / TPR, ec = et % TPR;
+    static_assert(ETH / TPR == C && EPT % 8 == 0, "the output stage covers the chunk's rows");
 
     // Per-chunk RoPE base table cos/sin(p0 f_i), one frequency per lane, filled by a single io
     // wavefront (the io wavefronts take turns chunk by chunk).  Most chunks advance the previous
@@ -336,7 +345,7 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
     float2 table_step;  // cos/sin(C f_i)
     rope_cos_sin(C, table_frev, table_step.x, table_step.y);
     auto fill_rope_table = [&](int chunk, int slot) {
-        if (wave - NW != chunk % NW) return;  // wave-uniform (there are NW io wavefronts)
+        if (wave - NW != chunk % NIO) return;  // wave-uniform
         float2 e;
         if (chunk % kRopeAnchor == 0) {
             rope_cos_sin(p.pos0 + t_begin + (int64_t)chunk * C, table_frev, e.x, e.y);
@@ -577,9 +586,9 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
             // chunk s-2 (staged in step s-1) and then process chunk s-1.  The gate logits of a
             // chunk are loaded one step before its outputs.
             uint4 gcur[GV];
-            if (!kStateOnly) load_gate(0, gcur);
+            if (!kStateOnly && !kEpiIo) load_gate(0, gcur);
             for (int s = 0; s < n_steps; ++s) {
-                if (!kStateOnly && s >= 2 && s - 2 < n_chunks) {
+                if (!kStateOnly && !kEpiIo && s >= 2 && s - 2 < n_chunks) {
                     epilogue(s - 2, sm.o + (s & 1) * C * OS, gcur, s - 1 < n_chunks);
                     load_gate(s - 1, gcur);
                 }
@@ -631,28 +640,28 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
                 wk[4 + u] = pk[HALF + 4 * fg + u];
             }
         }
-        // cos/sin(j f_i) for this thread's two rows j = 2 rg + s and four frequencies
-        float2 rot[2][4];
+        // cos/sin(j f_i) for this thread's rows j = RPT rg + s and four frequencies
+        float2 rot[RPT][4];
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+        for (int s = 0; s < RPT; ++s)
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 float cs, sn;
-                rope_cos_sin(2 * rg + s, p.inv_freq_rev[4 * fg + u], cs, sn);
+                rope_cos_sin(RPT * rg + s, p.inv_freq_rev[4 * fg + u], cs, sn);
                 rot[s][u] = make_float2(cs, sn);
             }
         const float kscale = 1.0f / sqrtf((float)D);
 
         struct Regs {
-            V4 q[2][2], k[2][2], v[2][2];  // [row s][half]
+            V4 q[RPT][2], k[RPT][2], v[RPT][2];  // [row s][half]
         };
         // (rows past the segment end re-read its last row; the prologue zeroes them)
         auto load = [&](int chunk, Regs& r) {
             const int cs = chunk_start(chunk);
             const size_t cb = (size_t)cs * row_stride;
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const uint32_t o = (uint32_t)min(2 * rg + s, t_end - 1 - cs) * rs32 + 4 * fg;
+            for (int s = 0; s < RPT; ++s) {
+                const uint32_t o = (uint32_t)min(RPT * rg + s, t_end - 1 - cs) * rs32 + 4 * fg;
                 if (!kStateOnly) {
                     r.q[s][0] = *reinterpret_cast<const V4*>(gq + cb + o);
                     r.q[s][1] = *reinterpret_cast<const V4*>(gq + cb + o + HALF);
@@ -666,9 +675,9 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
 
         // prologue of one chunk: registers -> normalised, rotated, decayed tiles in LDS
         // decay of this thread's two rows in a full chunk, lambda^(C-1-j)
-        float kdec_full[2];
+        float kdec_full[RPT];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) kdec_full[s] = pow_lambda(l2l, C - 1 - (2 * rg + s));
+        for (int s = 0; s < RPT; ++s) kdec_full[s] = pow_lambda(l2l, C - 1 - (RPT * rg + s));
         const int period = renorm_period(l2l);  // the math wavefronts' lazy state scale
         // full: the chunk is known to hold C tokens (every row valid, no per-row test)
         auto prologue = [&](int chunk, const Regs& r, Tiles<M, D, kStateOnly>& t, bool full) {
@@ -678,10 +687,10 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
             float2 b4[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) b4[u] = base[4 * fg + u];
-            float kd[2][8];  // decayed keys [row][feature slot]
+            float kd[RPT][8];  // decayed keys [row][feature slot]
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int j = 2 * rg + s;
+            for (int s = 0; s < RPT; ++s) {
+                const int j = RPT * rg + s;
                 const bool valid = full || j < n;
                 float qa[8], ka[8];
                 if (!kStateOnly) {
@@ -743,8 +752,8 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
             if constexpr (M::kSplit) {
                 // natural [token][feature] tiles: v as loaded, decayed keys as bf16 hi (+ lo)
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const int j = 2 * rg + s;
+                for (int s = 0; s < RPT; ++s) {
+                    const int j = RPT * rg + s;
 #pragma unroll
                     for (int hf = 0; hf < 2; ++hf) {
                         const int col = nat_index<D>(j, hf * HALF + 4 * fg);
@@ -761,6 +770,7 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
                     }
                 }
             } else {
+                static_assert(RPT == 2 || kStateOnly || M::kSplit, "fp32 tiles pair two rows");
                 const int jp = Layout<M>::kpos(2 * rg);  // the two tokens stay adjacent
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
@@ -776,30 +786,39 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
             // PF register sets hold the q/k/v (and gate logits) of the next PF chunks, so each load
             // is issued PF steps before its use; the step loop is unrolled by PF so the sets stay
             // static registers.
+            static_assert(PF >= 2, "steady steps store chunk s - 2");
             Regs rs[PF];
+            uint4 gs[PF][kEpiIo ? GV : 1];  // gate logits, loaded PF steps ahead (io output stage)
 #pragma unroll
-            for (int i = 0; i < PF; ++i) load(i, rs[i]);
-            // `steady`: s + 1 < n_chunks, so the chunk staged is full and the next one exists; the
-            // step then has no branches.
-            auto step = [&](int s, Regs& cur, bool steady) {
+            for (int i = 0; i < PF; ++i) {
+                load(i, rs[i]);
+                if (kEpiIo) load_gate(i, gs[i]);
+            }
+            // `steady`: PF <= s and s + 1 < n_chunks, so the chunk staged is full, the next one
+            // exists and the chunk stored (s - 2) is full; the step then has no branches.
+            auto step = [&](int s, Regs& cur, uint4* gep, bool steady) {
                 if (steady || s < n_chunks) prologue(s, cur, sm.buf[s & 1], steady);
                 load(s + PF, cur);
                 if (steady || s + 1 < n_chunks) fill_rope_table(s + 1, (s + 1) & 1);
+                if (kEpiIo && (steady || (s >= 2 && s - 2 < n_chunks))) {
+                    epilogue(s - 2, sm.o + (s & 1) * C * OS, gep, steady || s - 1 < n_chunks);
+                    load_gate(s - 2 + PF, gep);
+                }
                 __syncthreads();
             };
             // The first round is peeled (the loop header then sees the same in-flight loads from
             // both of its predecessors and waits only for the chunk it consumes), steady rounds
             // follow, and the remaining rounds handle the pipeline drain.
 #pragma unroll
-            for (int i = 0; i < PF; ++i) step(i, rs[i], false);
+            for (int i = 0; i < PF; ++i) step(i, rs[i], gs[(i + PF - 2) % PF], false);
             int s0 = PF;
             for (; s0 + PF < n_chunks; s0 += PF) {
 #pragma unroll
-                for (int i = 0; i < PF; ++i) step(s0 + i, rs[i], true);
+                for (int i = 0; i < PF; ++i) step(s0 + i, rs[i], gs[(i + PF - 2) % PF], true);
             }
             for (; s0 < n_steps; s0 += PF) {
 #pragma unroll
-                for (int i = 0; i < PF; ++i) step(s0 + i, rs[i], false);
+                for (int i = 0; i < PF; ++i) step(s0 + i, rs[i], gs[(i + PF - 2) % PF], false);
             }
         } else {
             Regs ra;
@@ -823,7 +842,7 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
 // The state-only pass is register-limited so that kStateOnlyBlocksPerCU of its workgroups share
 // a CU (their barriers are independent, so one hides the other's stalls).
 template <class M, int D, bool kStateOnly, int PF>
-__global__ void __launch_bounds__(128 * (D / 32))
+__global__ void __launch_bounds__((Cfg<M, D, kStateOnly>::NT))
 __attribute__((amdgpu_waves_per_eu(kStateOnly ? kStateOnlyBlocksPerCU * D / 64 : 1)))
 chunk_kernel(const ChunkParams p) {
     __shared__ Smem<M, D, kStateOnly> sm;
@@ -874,8 +893,8 @@ template <class M, int D>
 hipError_t launch_typed(const ChunkParams& cp, const ScanParams& sp, const hipEvent_t ev[2],
                         hipStream_t stream) {
     const int BH = cp.B * cp.H;
-    constexpr int NT = 128 * (D / 32);
     if (cp.P > 1) {
+        constexpr int NT = Cfg<M, D, true>::NT;
         chunk_kernel<M, D, true, kPrefetchStateOnly><<<dim3(BH * (cp.SP - 1)), dim3(NT), 0, stream>>>(cp);
         const size_t n = (size_t)BH * D * D;
         segment_scan_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(sp);
@@ -883,7 +902,7 @@ hipError_t launch_typed(const ChunkParams& cp, const ScanParams& sp, const hipEv
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (ev[0] && (err = hipEventRecord(ev[0], stream)) != hipSuccess) return err;
-    chunk_kernel<M, D, false, kPrefetchMain><<<dim3(BH * cp.P), dim3(NT), 0, stream>>>(cp);
+    chunk_kernel<M, D, false, kPrefetchMain><<<dim3(BH * cp.P), dim3(Cfg<M, D, false>::NT), 0, stream>>>(cp);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev[1] && (err = hipEventRecord(ev[1], stream)) != hipSuccess) return err;
     return hipSuccess;
