@@ -48,7 +48,7 @@ static_assert(C == 32, "the tiling below assumes one 32-row block per chunk");
 // Chunks of q/k/v in flight per workgroup (register sets of the io wavefronts).  The main pass
 // is limited by its 256-VGPR budget at two wavefronts per SIMD.
 #ifndef LT_PREFETCH_MAIN
-#define LT_PREFETCH_MAIN 3
+#define LT_PREFETCH_MAIN 4
 #endif
 #ifndef LT_PREFETCH_STATE
 #define LT_PREFETCH_STATE 2
