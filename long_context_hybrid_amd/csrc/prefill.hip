@@ -869,9 +869,10 @@ chunk_kernel(const ChunkParams p) {
         chunk_pass<M, D, kStateOnly, PF, false>(p, sm);
 }
 
-// ws[b][h][j] holds each state-only sub-segment's end state from zero (j < P-1).  Replace it, in
-// place, by the state entering sub-segment j:  S_in(0) = state_in,
-// S_in(j+1) = lambda^len(j) S_in(j) + dS(j), where len(j) is the sub-segment's length.
+// ws[b][h][j] holds each state-only sub-segment's end state from zero (j < P-1).  The state
+// entering sub-segment j is S_in(0) = state_in, S_in(j+1) = lambda^len(j) S_in(j) + dS(j), where
+// len(j) is the sub-segment's length; it replaces slot j in place for the slots that start a
+// segment (j % sub == 0, including the last slot), the only ones the main pass reads.
 __global__ void __launch_bounds__(256) segment_scan_kernel(const ScanParams p) {
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (size_t)p.BH * p.dd) return;
@@ -881,11 +882,21 @@ __global__ void __launch_bounds__(256) segment_scan_kernel(const ScanParams p) {
     const float lam_sub = p.lambda_pow_sub[h], lam_rest = p.lambda_pow_rest[h];
     float s = p.state_in ? p.state_in[idx] : 0.0f;
     float* w = p.ws + (size_t)bh * p.P * p.dd + e;
-    for (int i = 0, k = 0; i < p.P; ++i) {  // k = i % sub
-        const float ds = (i < p.P - 1) ? w[(size_t)i * p.dd] : 0.0f;
-        w[(size_t)i * p.dd] = s;
-        s = fmaf(k == p.sub - 1 ? lam_rest : lam_sub, s, ds);
-        k = (k == p.sub - 1) ? 0 : k + 1;
+    // eight slots' loads in flight at a time; only the slots the main pass reads (segment
+    // starts, i % sub == 0) are written back
+    constexpr int U = 8;
+    for (int i0 = 0; i0 < p.P; i0 += U) {
+        float ds[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) ds[u] = (i0 + u < p.P - 1) ? w[(size_t)(i0 + u) * p.dd] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u;
+            if (i >= p.P) break;
+            const int k = i % p.sub;
+            if (k == 0) w[(size_t)i * p.dd] = s;
+            s = fmaf(k == p.sub - 1 ? lam_rest : lam_sub, s, ds[u]);
+        }
     }
 }
 
