@@ -38,6 +38,10 @@ SMALL = [
     ("fp32_d64_ragged", 3, 130, 2, 64, torch.float32, (0.0, 1.0), "randn", (0, 3)),
     # segments whose state-only pass is split further (3 and 5 sub-segments per segment)
     ("bf16_d128_subsegments", 1, 8192 + 5, 2, 128, torch.bfloat16, None, "randn", (2, 4)),
+    # slow heads: state-only sub-segments close enough to the end to need the low key parts
+    # (lambda^(T - end) above 2^-8), a head between, and a fast head whose lazy state scale
+    # renormalises every chunk
+    ("bf16_d128_slow_heads", 1, 8192 + 33, 3, 128, torch.bfloat16, (0.99999, 0.999, 0.5), "randn", (3, 5)),
     # 3 and 2 sub-segments per segment, fp32 activations
     ("fp32_d64_subsegments", 2, 2048 + 40, 1, 64, torch.float32, (0.9999,), "randn", (2, 3)),
 ]
