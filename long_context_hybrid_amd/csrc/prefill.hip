@@ -389,9 +389,9 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
     In* gy = static_cast<In*>(p.y) + head_base;
     // epilogue of one chunk: y = RMSNorm(o) * w_o * sigmoid(g)
     constexpr int GV = EPT * sizeof(In) / 16;  // 16-byte vectors of gate logits per thread
-    auto load_gate = [&](int chunk, uint4* gr) {
-        const int cs = chunk_start(chunk);
-        const uint32_t o = (uint32_t)min(er, t_end - 1 - cs) * rs32 + EPT * ec;
+    auto load_gate = [&](int chunk, uint4* gr, bool full = false) {
+        const int cs = full ? t_begin + chunk * C : chunk_start(chunk);
+        const uint32_t o = (uint32_t)(full ? er : min(er, t_end - 1 - cs)) * rs32 + EPT * ec;
         const uint4* src = reinterpret_cast<const uint4*>(gg + (size_t)cs * row_stride + o);
 #pragma unroll
         for (int i = 0; i < GV; ++i) gr[i] = src[i];
@@ -656,12 +656,14 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
             V4 q[RPT][2], k[RPT][2], v[RPT][2];  // [row s][half]
         };
         // (rows past the segment end re-read its last row; the prologue zeroes them)
-        auto load = [&](int chunk, Regs& r) {
-            const int cs = chunk_start(chunk);
+        // full: the chunk is known to be full and not past the end (no clamping)
+        auto load = [&](int chunk, Regs& r, bool full) {
+            const int cs = full ? t_begin + chunk * C : chunk_start(chunk);
             const size_t cb = (size_t)cs * row_stride;
 #pragma unroll
             for (int s = 0; s < RPT; ++s) {
-                const uint32_t o = (uint32_t)min(RPT * rg + s, t_end - 1 - cs) * rs32 + 4 * fg;
+                const int row = full ? RPT * rg + s : min(RPT * rg + s, t_end - 1 - cs);
+                const uint32_t o = (uint32_t)row * rs32 + 4 * fg;
                 if (!kStateOnly) {
                     r.q[s][0] = *reinterpret_cast<const V4*>(gq + cb + o);
                     r.q[s][1] = *reinterpret_cast<const V4*>(gq + cb + o + HALF);
@@ -791,18 +793,19 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
             uint4 gs[PF][kEpiIo ? GV : 1];  // gate logits, loaded PF steps ahead (io output stage)
 #pragma unroll
             for (int i = 0; i < PF; ++i) {
-                load(i, rs[i]);
+                load(i, rs[i], false);
                 if (kEpiIo) load_gate(i, gs[i]);
             }
-            // `steady`: PF <= s and s + 1 < n_chunks, so the chunk staged is full, the next one
-            // exists and the chunk stored (s - 2) is full; the step then has no branches.
+            // `steady`: PF <= s and s + PF + 1 < n_chunks, so every chunk the step touches (staged,
+            // loaded, stored) is full and none is the last; the step then has no branches and
+            // its addresses need no clamping.
             auto step = [&](int s, Regs& cur, uint4* gep, bool steady) {
                 if (steady || s < n_chunks) prologue(s, cur, sm.buf[s & 1], steady);
-                load(s + PF, cur);
+                load(s + PF, cur, steady);
                 if (steady || s + 1 < n_chunks) fill_rope_table(s + 1, (s + 1) & 1);
                 if (kEpiIo && (steady || (s >= 2 && s - 2 < n_chunks))) {
                     epilogue(s - 2, sm.o + (s & 1) * C * OS, gep, steady || s - 1 < n_chunks);
-                    load_gate(s - 2 + PF, gep);
+                    load_gate(s - 2 + PF, gep, steady);
                 }
                 __syncthreads();
             };
@@ -812,7 +815,7 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
 #pragma unroll
             for (int i = 0; i < PF; ++i) step(i, rs[i], gs[(i + PF - 2) % PF], false);
             int s0 = PF;
-            for (; s0 + PF < n_chunks; s0 += PF) {
+            for (; s0 + 2 * PF < n_chunks; s0 += PF) {
 #pragma unroll
                 for (int i = 0; i < PF; ++i) step(s0 + i, rs[i], gs[(i + PF - 2) % PF], true);
             }
@@ -823,7 +826,7 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
         } else {
             Regs ra;
             for (int s = 0; s < n_chunks; ++s) {
-                load(s, ra);
+                load(s, ra, false);
                 prologue(s, ra, sm.buf[0], false);
                 if (s + 1 < n_chunks) fill_rope_table(s + 1, (s + 1) & 1);
                 __syncthreads();  // chunk s in LDS
