@@ -11,7 +11,10 @@ Printed (one JSON line): prefill tokens/s/layer (``value``), the main kernel's r
 (algorithmic HBM bytes per launch / its average duration, timed with HIP events recorded by the
 library around that kernel on the launch stream), its MFMA rate, the batched decode step
 (B = 64, H = 16, d = 128) in microseconds with its HBM roofline, and the fp64 CPU oracle timed on
-a bounded sample of the same prefill workload on this host's cores.
+a bounded sample of the same prefill workload on this host's cores.  Under ``layer``: the whole
+RNN layer around the mixer (QKVZ projection GEMM, mixer, output projection GEMM; d_model = 2048)
+at the same 512K tokens with per-stage times and the QKVZ GEMM's MFMA roofline, its B = 64
+decode step, and the layer oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -46,6 +49,10 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=524288)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-layer", action="store_true",
+                    help="skip the whole-layer legs (projections + mixer + output projection)")
+    ap.add_argument("--layer-steps", type=int, default=5)
+    ap.add_argument("--cpu-layer-tokens", type=int, default=8192)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed runs, copy this many MiB device to device three times "
                          "(a plain copy of known size that calibrates HBM byte counters)")
@@ -63,14 +70,16 @@ def copy_calibration(torch, mib):
     del src, dst
 
 
+MIXER_SOURCES = ("abi.hip", "decode.hip", "lt_device.h", "lt_internal.h", "prefill.hip")
+
+
 def source_fingerprint():
-    """sha256 over the library's kernel and ABI sources (the code the byte counters measured)."""
-    import glob
+    """sha256 over the sources of the mixer kernels and their launch configuration (the code the
+    byte counters measured)."""
     import hashlib
 
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "long_context_hybrid_amd", "csrc", "*")))
-    files.append(os.path.join(ROOT, "include", "lightning.h"))
+    files = [os.path.join(ROOT, "long_context_hybrid_amd", "csrc", f) for f in MIXER_SOURCES]
     for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
@@ -220,6 +229,123 @@ def bench_decode(args, torch, lt, synth):
             "state_buffers": len(states)}
 
 
+def bench_layer(args, torch, lt, synth):
+    """The whole RNN layer (QKVZ GEMM, mixer, W_o GEMM) at 512K tokens, with each stage timed by
+    the HIP events the library records between the stages on the launch stream."""
+    spec = synth.LAYER_QWEN17_512K
+    dev = torch.device("cuda:0")
+    inp = synth.make_layer(spec, device=dev)
+    B, T, H, d, dm = inp["B"], inp["T"], inp["H"], inp["d"], inp["d_model"]
+    out = torch.empty_like(inp["x"])
+    s_out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(lt.lightning_layer_prefill_workspace_size(B, T, H, d, dm), dtype=torch.uint8,
+                     device=dev)
+    call = (inp["x"], inp["w_qkvz"], inp["w_o"], inp["qw"], inp["kw"], inp["lambdas"],
+            inp["rope_base"], H, d)
+    kw = dict(rms_eps=inp["eps"], state_out=s_out, out=out, workspace=ws)
+    for _ in range(args.warmup):
+        lt.lightning_layer_prefill(*call, **kw)
+    torch.cuda.synchronize()
+    hev = HipEvents()
+    n = args.layer_steps
+    ev = hev.create(4 * n)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(n):
+        lt.lightning_layer_prefill(*call, **kw, stage_events=ev[4 * i:4 * i + 4])
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / n
+    stage = [sum(hev.elapsed_ms(ev[4 * i + j], ev[4 * i + j + 1]) for i in range(n)) / n
+             for j in range(3)]
+    hev.destroy(ev)
+    rows = B * T
+    f1 = 2 * rows * (4 * H * d) * dm
+    f2 = 2 * rows * dm * (H * d)
+    t1 = f1 / (stage[0] * 1e-3) / 1e12
+    t2 = f2 / (stage[2] * 1e-3) / 1e12
+    del inp, out, ws
+    return {"workload": spec.name, "ms_per_step": round(ms, 4),
+            "value": round(rows / (ms * 1e-3), 1), "unit": "tokens/s/layer", "steps": n,
+            "stages_ms": {"qkvz_gemm": round(stage[0], 4), "mixer": round(stage[1], 4),
+                          "o_gemm": round(stage[2], 4)},
+            "roofline": {"bound": "mfma", "achieved": round(t1, 1), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(t1 / BF16_PEAK_TFLOPS, 4),
+                         "traffic": None,
+                         "kernel": "hipBLASLt bf16 GEMM x [W_q|W_k|W_v|W_z] (M=%d N=%d K=%d)"
+                                   % (rows, 4 * H * d, dm),
+                         "flops_per_launch": f1, "launch_ms": round(stage[0], 4)},
+            "o_gemm": {"achieved_tflops": round(t2, 1), "frac": round(t2 / BF16_PEAK_TFLOPS, 4),
+                       "flops_per_launch": f2},
+            "mfma_floor_ms": round((f1 + f2) / (BF16_PEAK_TFLOPS * 1e12) * 1e3, 3)}
+
+
+def bench_layer_decode(args, torch, lt, synth):
+    """One layer decode step at B = 64 over rotating sets of (state, weights), so that neither
+    the 64 MiB state nor the 40 MiB of projection weights can be served from MALL."""
+    spec = synth.LAYER_DECODE_B64
+    dev = torch.device("cuda:0")
+    inp = synth.make_layer(spec, device=dev)
+    B, H, d, dm = inp["B"], inp["H"], inp["d"], inp["d_model"]
+    nset = args.decode_buffers
+    sets = [(inp["state_in"].clone(), inp["w_qkvz"].clone(), inp["w_o"].clone())
+            for _ in range(nset)]
+    out = torch.empty_like(inp["x"])
+    ws = torch.empty(lt.lightning_layer_decode_workspace_size(B, H, d, dm), dtype=torch.uint8,
+                     device=dev)
+
+    def step(i):
+        st, w, wo = sets[i % nset]
+        lt.lightning_layer_decode_step(inp["x"], w, wo, inp["qw"], inp["kw"], inp["lambdas"],
+                                       inp["rope_base"], H, d, inp["positions"], st,
+                                       rms_eps=inp["eps"], out=out, workspace=ws)
+
+    for i in range(3):
+        step(i)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.decode_steps):
+        step(i)
+    stop.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(stop) * 1e3 / args.decode_steps
+    wbytes = (4 * H * d * dm + dm * H * d) * 2
+    io = B * dm * 2 * 2 + B * (4 * H * d + H * d) * 2 * 2  # x, out; projections and y written + read
+    alg = wbytes + B * H * 2 * d * d * 4 + io + B * 8
+    gbs = alg / (us * 1e-6) / 1e9
+    return {"workload": spec.name, "us_per_step": round(us, 3),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "alg_bytes_per_step": alg, "weight_bytes": wbytes},
+            "rotating_sets": nset}
+
+
+def cpu_baseline_layer(args, torch, synth):
+    """The layer oracle (fp64 projections through numpy, the fp64 recurrence in C threads) on the
+    first tokens of the 512K layer workload."""
+    import numpy as np
+
+    from oracle import layer as ol
+
+    spec = synth.LAYER_QWEN17_512K
+    Ts = args.cpu_layer_tokens
+    inp = synth.make_layer(spec, device="cpu", T=Ts)
+    cores = len(os.sched_getaffinity(0))
+    args_h = (synth.host_bits(inp["x"]), synth.host_bits(inp["w_qkvz"]),
+              synth.host_bits(inp["w_o"]), inp["qw"].numpy(), inp["kw"].numpy(), inp["lambdas"],
+              inp["rope_base"], inp["H"], inp["d"])
+    t0 = time.perf_counter()
+    r = ol.layer_prefill(*args_h, eps=inp["eps"], nthreads=cores)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(r["out"]).all()
+    return {"value": round(Ts / dt, 1), "unit": "tokens/s/layer", "cores": cores, "kind": "oracle",
+            "sample": f"first {Ts} tokens of the {spec.name} workload (same generator, same "
+                      f"shapes), fp64: numpy matmuls for the projections, the token-by-token "
+                      f"recurrence on {r['threads']} threads, {dt:.1f} s"}
+
+
 def cpu_baseline(args, torch, synth, pre):
     import numpy as np
 
@@ -267,10 +393,22 @@ def main():
     if not args.no_decode:
         print(f"[bench] decode B=64: steps {args.decode_steps}", file=sys.stderr, flush=True)
         dec = bench_decode(args, torch, lt, synth)
+    layer = None
+    if not args.no_layer:
+        print(f"[bench] layer prefill 512K: warmup {args.warmup}, steps {args.layer_steps}",
+              file=sys.stderr, flush=True)
+        layer = bench_layer(args, torch, lt, synth)
+        if not args.no_decode:
+            print(f"[bench] layer decode B=64: steps {args.decode_steps}", file=sys.stderr,
+                  flush=True)
+            layer["decode"] = bench_layer_decode(args, torch, lt, synth)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(args, torch, synth, pre)
+        if layer is not None:
+            print("[bench] cpu baseline of the layer (oracle)", file=sys.stderr, flush=True)
+            layer["cpu_baseline"] = cpu_baseline_layer(args, torch, synth)
     if args.copy_mib > 0:
         print(f"[bench] calibration copy of {args.copy_mib} MiB", file=sys.stderr, flush=True)
         copy_calibration(torch, args.copy_mib)
@@ -294,6 +432,7 @@ def main():
         "mfma": pre["mfma"],
         "whole_call": pre["whole_call"],
         "decode": dec,
+        "layer": layer,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -15,16 +15,26 @@
  *
  * RMSNorm(x) = x / sqrt(mean(x^2) + eps) over the d entries of one head.  RoPE rotates the
  * half-split pairs (x_i, x_{i+d/2}) by the angle p * base^(-2i/d), i < d/2.  The state S is a
- * d x d fp32 matrix indexed [key dim][value dim].  The W_o projection is outside this library.
+ * d x d fp32 matrix indexed [key dim][value dim].
+ *
+ * The layer calls (lightning_layer_*) add the projections of Eq. 18 around the mixer:
+ * [q | k | v | g]_t = x_t [W_q | W_k | W_v | W_z] for all heads at once, and the layer output
+ * out_t = [y_t^(1) | ... | y_t^(H)] W_o^T, which is the sum over heads of y_t^(h) W_o^(h)T that
+ * Appendix A describes.
  *
  * Conventions shared by every call:
  *   - Device pointers are plain device addresses (hipMalloc or a PyTorch CUDA tensor); they are
  *     borrowed for the duration of the work enqueued on `stream` and never freed or retained.
  *     `lambda` (and `out` of lightning_hypenet_gamma) are HOST pointers read before the call
- *     returns.  The library allocates no device memory: prefill takes a caller-owned workspace.
+ *     returns.  The library's own code allocates no device memory: prefill and the layer calls
+ *     take a caller-owned workspace.  The layer calls run their two GEMMs through hipBLASLt; one
+ *     hipBLASLt handle per device is created on the first layer call and kept (with whatever
+ *     memory hipBLASLt gives it) until the process ends.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only enqueues work and
- *     never synchronises the device.  The calls keep no state between calls and are re-entrant;
- *     calls that share a workspace or output buffers must be ordered by the caller.
+ *     never synchronises the device.  The mixer calls keep no state between calls; the layer
+ *     calls cache, per device and GEMM shape, the hipBLASLt descriptors and algorithm (guarded
+ *     by a lock).  All calls are re-entrant; calls that share a workspace or output buffers must
+ *     be ordered by the caller.
  *   - Layouts are dense and row-major: activations [B][T][H][d] (prefill) or [B][H][d] (decode),
  *     state [B][H][d][d], norm weights [H][d] (or one shared [d] when norm_w_head_stride == 0).
  *   - Argument errors are detected on the host before anything is launched; the call then
@@ -127,6 +137,60 @@ lt_status lightning_decode_step(const void* q, const void* k, const void* v, con
                                 const int64_t* positions, const float* state_in,
                                 float* state_out, void* y, float* o_raw, int B, int H, int d,
                                 int dtype, void* stream);
+
+/*
+ * ---- The whole RNN layer (Appendix A, Eq. 18, with the projections; Section 5.2, Eq. 14) ----
+ *
+ *   x       : device [B][T][d_model] (prefill) or [B][d_model] (decode) of `dtype`, the layer's
+ *             input (in the model, the RMS-normalised residual stream of Eq. 15).
+ *   w_qkvz  : device [4 H d][d_model] of `dtype`, row-major: row n holds the weights of
+ *             projection output n.  Rows [0, Hd) are W_q with head h at rows [h d, h d + d),
+ *             then W_k, W_v and W_z in the same order (W_q = w_qkvz[0:Hd]^T in the paper's
+ *             x W_q form).
+ *   w_o     : device [d_model][H d] of `dtype`, row-major: W_o of Eq. 18 with the heads side by
+ *             side, column h d + i for entry i of head h.
+ *   out     : device [B][T][d_model] (prefill) or [B][d_model] (decode) of `dtype`.
+ *   d_model : the model width, a positive multiple of 8.
+ * The projections accumulate in fp32 and, like the mixer output y, are stored in `dtype` before
+ * the next step reads them.  All other arguments mean what they mean for lightning_prefill /
+ * lightning_decode_step, and the same argument checks run before anything is enqueued.
+ *
+ * workspace : device memory of at least the size query's bytes, 256-byte aligned, holding
+ *   at offset 0                     the projections [B][T][4 H d] (column blocks q | k | v | g),
+ *   at round_up(B T 4 H d es, 256)  the mixer output y [B][T][H][d],
+ * (es = 2 for bf16, 4 for fp32), then the mixer's and the GEMMs' scratch.  After the call's work
+ * has run, the first two parts hold the layer's intermediate tensors (a test hook).
+ * stage_events : NULL, or four hipEvent_t handles recorded on `stream` before the QKVZ GEMM,
+ *   after it, after the mixer and after the output GEMM.
+ * Errors: as for the mixer calls; LT_ERR_UNSUPPORTED also when hipBLASLt has no algorithm for a
+ * GEMM shape, LT_ERR_HIP when hipBLASLt fails to enqueue.  d_model not a multiple of 8 is
+ * LT_ERR_INVALID_ARG.
+ */
+size_t lightning_layer_prefill_workspace_size(int B, int T, int H, int d, int d_model, int dtype,
+                                              int chunk, int segments);
+
+lt_status lightning_layer_prefill(const void* x, const void* w_qkvz, const void* w_o,
+                                  const float* q_norm_w, const float* k_norm_w,
+                                  const float* o_norm_w, int norm_w_head_stride,
+                                  const double* lambda, double rope_base, double rms_eps,
+                                  int64_t pos0, const float* state_in, float* state_out,
+                                  void* out, int B, int T, int H, int d, int d_model, int dtype,
+                                  int chunk, int segments, void* workspace,
+                                  size_t workspace_bytes, void* const* stage_events,
+                                  void* stream);
+
+/* One decode step of the layer: x [B][d_model] -> out [B][d_model], the state updated as by
+ * lightning_decode_step.  Workspace layout as above with T = 1. */
+size_t lightning_layer_decode_workspace_size(int B, int H, int d, int d_model, int dtype);
+
+lt_status lightning_layer_decode_step(const void* x, const void* w_qkvz, const void* w_o,
+                                      const float* q_norm_w, const float* k_norm_w,
+                                      const float* o_norm_w, int norm_w_head_stride,
+                                      const double* lambda, double rope_base, double rms_eps,
+                                      const int64_t* positions, const float* state_in,
+                                      float* state_out, void* out, int B, int H, int d,
+                                      int d_model, int dtype, void* workspace,
+                                      size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,4 +1,5 @@
-"""Build step of the gfx950 library: compiles csrc/*.hip into liblightning.so in this directory.
+"""Build step of the gfx950 library: compiles csrc/*.hip into liblightning.so in this directory
+(linked against hipBLASLt, which runs the layer's two projection GEMMs).
 
 Run ``python -m long_context_hybrid_amd.build`` (or call ``build()``).  The library is built for
 gfx950 only.  Packed-fp32 VALU instructions are disabled for the device code.
@@ -21,7 +22,8 @@ def sources():
 def command(out=LIB, extra=()):
     return [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I", os.path.join(ROOT, "include"), *extra, *sources(), "-o", out]
+            "-I", os.path.join(ROOT, "include"), *extra, *sources(),
+            "-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib", "-o", out]
 
 
 def build(out=LIB, extra=(), verbose=False):

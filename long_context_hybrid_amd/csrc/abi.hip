@@ -163,13 +163,18 @@ size_t lightning_prefill_workspace_size(int B, int T, int H, int d, int dtype, i
     return workspace_bytes_for(B, H, d, pl.P, pl.sub);
 }
 
-lt_status lightning_prefill(const void* q, const void* k, const void* v, const void* gate,
-                            const float* q_norm_w, const float* k_norm_w, const float* o_norm_w,
-                            int norm_w_head_stride, const double* lambda, double rope_base,
-                            double rms_eps, int64_t pos0, const float* state_in, float* state_out,
-                            void* y, float* o_raw, int B, int T, int H, int d, int dtype,
-                            int chunk, int segments, void* workspace, size_t workspace_bytes,
-                            void* const* main_kernel_events, void* stream) {
+}  // extern "C"
+
+namespace lt {
+
+lt_status prefill_strided(const void* q, const void* k, const void* v, const void* gate,
+                          int x_stride, const float* q_norm_w, const float* k_norm_w,
+                          const float* o_norm_w, int norm_w_head_stride, const double* lambda,
+                          double rope_base, double rms_eps, int64_t pos0, const float* state_in,
+                          float* state_out, void* y, float* o_raw, int B, int T, int H, int d,
+                          int dtype, int chunk, int segments, void* workspace,
+                          size_t workspace_bytes, void* const* main_kernel_events, void* stream,
+                          bool validate_only) {
     if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(gate) || !ok_ptr(y))
         return LT_ERR_INVALID_ARG;
     if (!ok_opt(state_in) || !ok_opt(state_out) || !ok_opt(o_raw)) return LT_ERR_INVALID_ARG;
@@ -178,10 +183,14 @@ lt_status lightning_prefill(const void* q, const void* k, const void* v, const v
     lt_status st = check_common(H, d, dtype, q_norm_w, k_norm_w, o_norm_w, norm_w_head_stride,
                                 lambda, rope_base, rms_eps);
     if (st != LT_OK) return st;
-    if ((double)B * T * H * d > 9.0e15) return LT_ERR_UNSUPPORTED;
+    if (x_stride < H * d || x_stride % 8 != 0) return LT_ERR_INVALID_ARG;
+    if ((double)B * T * x_stride > 9.0e15) return LT_ERR_UNSUPPORTED;
     Plan pl;
     st = plan(B, T, H, d, dtype, chunk, segments, &pl);
     if (st != LT_OK) return st;
+    if (main_kernel_events && (!main_kernel_events[0] || !main_kernel_events[1]))
+        return LT_ERR_INVALID_ARG;
+    if (validate_only) return LT_OK;
     const int P = pl.P;
     const size_t need = workspace_bytes_for(B, H, d, P, pl.sub);
     if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need))
@@ -196,6 +205,7 @@ lt_status lightning_prefill(const void* q, const void* k, const void* v, const v
     cp.ws = static_cast<float*>(workspace);
     cp.pos0 = pos0;
     cp.B = B; cp.T = T; cp.H = H; cp.P = P; cp.L = pl.L;
+    cp.x_stride = x_stride;
     cp.SM = pl.sub; cp.SL = pl.sub_len; cp.SP = (P - 1) * pl.sub + 1;
     cp.w_stride = norm_w_head_stride;
     cp.eps = (float)rms_eps;
@@ -214,8 +224,6 @@ lt_status lightning_prefill(const void* q, const void* k, const void* v, const v
         sp.lambda_pow_rest[h] = (float)pow(lambda[h], (double)rest);
     }
 
-    if (main_kernel_events && (!main_kernel_events[0] || !main_kernel_events[1]))
-        return LT_ERR_INVALID_ARG;
     hipEvent_t ev[2] = {nullptr, nullptr};
     if (main_kernel_events) {
         ev[0] = static_cast<hipEvent_t>(main_kernel_events[0]);
@@ -226,13 +234,12 @@ lt_status lightning_prefill(const void* q, const void* k, const void* v, const v
     return LT_OK;
 }
 
-lt_status lightning_decode_step(const void* q, const void* k, const void* v, const void* gate,
-                                const float* q_norm_w, const float* k_norm_w,
-                                const float* o_norm_w, int norm_w_head_stride,
-                                const double* lambda, double rope_base, double rms_eps,
-                                const int64_t* positions, const float* state_in,
-                                float* state_out, void* y, float* o_raw, int B, int H, int d,
-                                int dtype, void* stream) {
+lt_status decode_strided(const void* q, const void* k, const void* v, const void* gate,
+                         int x_stride, const float* q_norm_w, const float* k_norm_w,
+                         const float* o_norm_w, int norm_w_head_stride, const double* lambda,
+                         double rope_base, double rms_eps, const int64_t* positions,
+                         const float* state_in, float* state_out, void* y, float* o_raw, int B,
+                         int H, int d, int dtype, void* stream, bool validate_only) {
     if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(gate) || !ok_ptr(y))
         return LT_ERR_INVALID_ARG;
     if (!ok_ptr(positions) || !ok_ptr(state_in) || !ok_ptr(state_out) || !ok_opt(o_raw))
@@ -242,6 +249,8 @@ lt_status lightning_decode_step(const void* q, const void* k, const void* v, con
                                 lambda, rope_base, rms_eps);
     if (st != LT_OK) return st;
     if ((long long)B * H > 0x7fffffffLL) return LT_ERR_UNSUPPORTED;
+    if (x_stride < H * d || x_stride % 8 != 0) return LT_ERR_INVALID_ARG;
+    if (validate_only) return LT_OK;
 
     lt::DecodeParams dp;
     memset(&dp, 0, sizeof dp);
@@ -251,6 +260,7 @@ lt_status lightning_decode_step(const void* q, const void* k, const void* v, con
     dp.state_in = state_in; dp.state_out = state_out;
     dp.y = y; dp.o_raw = o_raw;
     dp.B = B; dp.H = H; dp.w_stride = norm_w_head_stride;
+    dp.x_stride = x_stride;
     dp.eps = (float)rms_eps;
     for (int h = 0; h < H; ++h) dp.lambda[h] = (float)lambda[h];
     fill_inv_freq_rev(dp.inv_freq_rev, d, rope_base);
@@ -258,6 +268,37 @@ lt_status lightning_decode_step(const void* q, const void* k, const void* v, con
     if (lt::launch_decode(dp, d, dtype, static_cast<hipStream_t>(stream)) != hipSuccess)
         return LT_ERR_HIP;
     return LT_OK;
+}
+
+}  // namespace lt
+
+extern "C" {
+
+lt_status lightning_prefill(const void* q, const void* k, const void* v, const void* gate,
+                            const float* q_norm_w, const float* k_norm_w, const float* o_norm_w,
+                            int norm_w_head_stride, const double* lambda, double rope_base,
+                            double rms_eps, int64_t pos0, const float* state_in, float* state_out,
+                            void* y, float* o_raw, int B, int T, int H, int d, int dtype,
+                            int chunk, int segments, void* workspace, size_t workspace_bytes,
+                            void* const* main_kernel_events, void* stream) {
+    if (H <= 0 || d <= 0 || (long long)H * d > 0x7fffffffLL) return LT_ERR_INVALID_ARG;
+    return lt::prefill_strided(q, k, v, gate, H * d, q_norm_w, k_norm_w, o_norm_w,
+                               norm_w_head_stride, lambda, rope_base, rms_eps, pos0, state_in,
+                               state_out, y, o_raw, B, T, H, d, dtype, chunk, segments,
+                               workspace, workspace_bytes, main_kernel_events, stream, false);
+}
+
+lt_status lightning_decode_step(const void* q, const void* k, const void* v, const void* gate,
+                                const float* q_norm_w, const float* k_norm_w,
+                                const float* o_norm_w, int norm_w_head_stride,
+                                const double* lambda, double rope_base, double rms_eps,
+                                const int64_t* positions, const float* state_in,
+                                float* state_out, void* y, float* o_raw, int B, int H, int d,
+                                int dtype, void* stream) {
+    if (H <= 0 || d <= 0 || (long long)H * d > 0x7fffffffLL) return LT_ERR_INVALID_ARG;
+    return lt::decode_strided(q, k, v, gate, H * d, q_norm_w, k_norm_w, o_norm_w,
+                              norm_w_head_stride, lambda, rope_base, rms_eps, positions, state_in,
+                              state_out, y, o_raw, B, H, d, dtype, stream, false);
 }
 
 }  // extern "C"

@@ -55,15 +55,16 @@ __global__ void __launch_bounds__(256) decode_kernel(const DecodeParams p) {
     for (int i = 0; i < RPT; ++i)
         st[i] = ld_stream(reinterpret_cast<const float4*>(s_in + (size_t)(r0 + RG * i) * D + 4 * c4));
 
-    const size_t base = (size_t)bh * D;
+    const size_t base = (size_t)bh * D;                              // y, o_raw
+    const size_t x_base = (size_t)b * p.x_stride + (size_t)h * D;    // q, k, v, g
     if (wave < 2) {
         // wavefront 0: q, wavefront 1: k.  Lane i holds the rotary pair (i, i + d/2).
         const void* src = wave == 0 ? p.q : p.k;
         const float* w = (wave == 0 ? p.qw : p.kw) + (size_t)h * p.w_stride;
         float x1 = 0.0f, x2 = 0.0f;
         if (lane < HALF) {
-            x1 = load_act<M>(src, base + lane);
-            x2 = load_act<M>(src, base + lane + HALF);
+            x1 = load_act<M>(src, x_base + lane);
+            x2 = load_act<M>(src, x_base + lane + HALF);
         }
         float ss = x1 * x1 + x2 * x2;
 #pragma unroll
@@ -81,7 +82,7 @@ __global__ void __launch_bounds__(256) decode_kernel(const DecodeParams p) {
     } else {
         const void* src = wave == 2 ? p.v : p.g;
         float* dst = wave == 2 ? sv : sg;
-        for (int i = lane; i < D; i += 64) dst[i] = load_act<M>(src, base + i);
+        for (int i = lane; i < D; i += 64) dst[i] = load_act<M>(src, x_base + i);
     }
     __syncthreads();
 

@@ -31,6 +31,7 @@ struct ChunkParams {
     float* ws;              // [B][H][SP][d][d] fp32 when P > 1
     int64_t pos0;
     int B, T, H;
+    int x_stride;  // elements between consecutive tokens of q, k, v and g (y is [B][T][H][d])
     int P;      // segments per (b, h) of the main pass
     int L;      // tokens per segment (multiple of the chunk), the last segment may be shorter
     // The state-only pass splits segments 0 .. P-2 into SM sub-segments: SM - 1 of SL tokens and
@@ -66,6 +67,7 @@ struct DecodeParams {
     void* y;
     float* o_raw;
     int B, H, w_stride;
+    int x_stride;  // elements between consecutive sequences of q, k, v and g (y is [B][H][d])
     float eps;
     float lambda[LT_MAX_HEADS];
     double inv_freq_rev[64];
@@ -76,5 +78,29 @@ hipError_t launch_prefill(const ChunkParams& cp, const ScanParams& sp, int d, in
                           const hipEvent_t events[2], hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& dp, int d, int dtype, hipStream_t stream);
 hipError_t launch_state_init(float* state, const float* init, size_t n, hipStream_t stream);
+
+// lightning_prefill / lightning_decode_step with q, k, v and g read at a token (prefill) or
+// sequence (decode) stride of x_stride elements, e.g. column blocks of one fused projection.
+// validate_only: run every argument check (but the prefill workspace's) and enqueue nothing.
+lt_status prefill_strided(const void* q, const void* k, const void* v, const void* gate,
+                          int x_stride, const float* q_norm_w, const float* k_norm_w,
+                          const float* o_norm_w, int norm_w_head_stride, const double* lambda,
+                          double rope_base, double rms_eps, int64_t pos0, const float* state_in,
+                          float* state_out, void* y, float* o_raw, int B, int T, int H, int d,
+                          int dtype, int chunk, int segments, void* workspace,
+                          size_t workspace_bytes, void* const* main_kernel_events, void* stream,
+                          bool validate_only);
+lt_status decode_strided(const void* q, const void* k, const void* v, const void* gate,
+                         int x_stride, const float* q_norm_w, const float* k_norm_w,
+                         const float* o_norm_w, int norm_w_head_stride, const double* lambda,
+                         double rope_base, double rms_eps, const int64_t* positions,
+                         const float* state_in, float* state_out, void* y, float* o_raw, int B,
+                         int H, int d, int dtype, void* stream, bool validate_only);
+
+// D[M][N] = A[M][K] W[N][K]^T, row-major, fp32 accumulation, A, W and D in `dtype`.
+// ws: at least gemm_workspace_limit() bytes of device memory, 256-byte aligned.
+size_t gemm_workspace_limit();
+lt_status gemm_xwt(const void* A, const void* W, void* D, int64_t M, int64_t N, int64_t K,
+                   int dtype, void* ws, size_t ws_bytes, hipStream_t stream);
 
 }  // namespace lt

@@ -317,8 +317,10 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
     const float l2l = p.log2_lambda[h];
     constexpr bool precise = kPrecise;
     const size_t dd = (size_t)D * D;
-    const size_t row_stride = (size_t)p.H * D;  // elements between consecutive tokens
+    const size_t row_stride = (size_t)p.H * D;  // y / o_raw: elements between consecutive tokens
     const size_t head_base = ((size_t)b * p.T * p.H + h) * D;
+    const size_t x_stride = (size_t)p.x_stride;  // q, k, v, g: elements between consecutive tokens
+    const size_t x_base = (size_t)b * p.T * x_stride + (size_t)h * D;
 
     // ---- io-role constants ----
     constexpr int RPT = 2 * NW / NIO;         // rows per io thread (2, or 1 with two io per SIMD)
@@ -383,16 +385,16 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
     // Row addresses: a uniform per-chunk base plus a 32-bit per-lane offset.  Loads are
     // unconditional (rows past the segment end re-read its last row), which keeps the
     // memory-wait bookkeeping exact across iterations.
-    const uint32_t rs32 = (uint32_t)row_stride;
+    const uint32_t rs32 = (uint32_t)row_stride, xs32 = (uint32_t)x_stride;
     auto chunk_start = [&](int chunk) { return t_begin + min(chunk, n_chunks - 1) * C; };
-    const In* gg = static_cast<const In*>(p.g) + head_base;
+    const In* gg = static_cast<const In*>(p.g) + x_base;
     In* gy = static_cast<In*>(p.y) + head_base;
     // epilogue of one chunk: y = RMSNorm(o) * w_o * sigmoid(g)
     constexpr int GV = EPT * sizeof(In) / 16;  // 16-byte vectors of gate logits per thread
     auto load_gate = [&](int chunk, uint4* gr, bool full = false) {
         const int cs = full ? t_begin + chunk * C : chunk_start(chunk);
-        const uint32_t o = (uint32_t)(full ? er : min(er, t_end - 1 - cs)) * rs32 + EPT * ec;
-        const uint4* src = reinterpret_cast<const uint4*>(gg + (size_t)cs * row_stride + o);
+        const uint32_t o = (uint32_t)(full ? er : min(er, t_end - 1 - cs)) * xs32 + EPT * ec;
+        const uint4* src = reinterpret_cast<const uint4*>(gg + (size_t)cs * x_stride + o);
 #pragma unroll
         for (int i = 0; i < GV; ++i) gr[i] = src[i];
     };
@@ -624,9 +626,9 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
         }
     } else {
         // ============================= io wavefronts =============================
-        const In* gq = static_cast<const In*>(p.q) + head_base;
-        const In* gk = static_cast<const In*>(p.k) + head_base;
-        const In* gv = static_cast<const In*>(p.v) + head_base;
+        const In* gq = static_cast<const In*>(p.q) + x_base;
+        const In* gk = static_cast<const In*>(p.k) + x_base;
+        const In* gv = static_cast<const In*>(p.v) + x_base;
 
         float wq[8], wk[8];
         {
@@ -659,11 +661,11 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
         // full: the chunk is known to be full and not past the end (no clamping)
         auto load = [&](int chunk, Regs& r, bool full) {
             const int cs = full ? t_begin + chunk * C : chunk_start(chunk);
-            const size_t cb = (size_t)cs * row_stride;
+            const size_t cb = (size_t)cs * x_stride;
 #pragma unroll
             for (int s = 0; s < RPT; ++s) {
                 const int row = full ? RPT * rg + s : min(RPT * rg + s, t_end - 1 - cs);
-                const uint32_t o = (uint32_t)row * rs32 + 4 * fg;
+                const uint32_t o = (uint32_t)row * xs32 + 4 * fg;
                 if (!kStateOnly) {
                     r.q[s][0] = *reinterpret_cast<const V4*>(gq + cb + o);
                     r.q[s][1] = *reinterpret_cast<const V4*>(gq + cb + o + HALF);

@@ -28,6 +28,10 @@ EXPORTS = (
     "lightning_prefill_workspace_size",
     "lightning_prefill",
     "lightning_decode_step",
+    "lightning_layer_prefill_workspace_size",
+    "lightning_layer_prefill",
+    "lightning_layer_decode_workspace_size",
+    "lightning_layer_decode_step",
 )
 
 
@@ -59,6 +63,17 @@ def _load() -> ct.CDLL:
     h.lightning_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, f64, f64, vp, vp,
                                         vp, vp, vp, i32, i32, i32, i32, vp]
     h.lightning_decode_step.restype = i32
+    h.lightning_layer_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
+    h.lightning_layer_prefill_workspace_size.restype = sz
+    h.lightning_layer_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, f64, f64, i64, vp, vp,
+                                          vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp,
+                                          vp]
+    h.lightning_layer_prefill.restype = i32
+    h.lightning_layer_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    h.lightning_layer_decode_workspace_size.restype = sz
+    h.lightning_layer_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, f64, f64, vp, vp,
+                                              vp, vp, i32, i32, i32, i32, i32, vp, sz, vp]
+    h.lightning_layer_decode_step.restype = i32
     return h
 
 
@@ -219,3 +234,91 @@ def lightning_decode_step(q, k, v, gate, q_norm_w, k_norm_w, lambdas, rope_base,
                                    B, H, d, dt, _stream(stream, dev))
     _check(st, "lightning_decode_step")
     return y
+
+
+# ---- the whole RNN layer ---------------------------------------------------------------------------
+
+def lightning_layer_prefill_workspace_size(B, T, H, d, d_model, dtype=torch.bfloat16, chunk=0,
+                                           segments=0) -> int:
+    return int(lib.lightning_layer_prefill_workspace_size(B, T, H, d, d_model, _dtype_code(dtype),
+                                                          chunk, segments))
+
+
+def lightning_layer_decode_workspace_size(B, H, d, d_model, dtype=torch.bfloat16) -> int:
+    return int(lib.lightning_layer_decode_workspace_size(B, H, d, d_model, _dtype_code(dtype)))
+
+
+def _layer_weights(w_qkvz, w_o, H, d, d_model, dtype, dev):
+    return (_dev(w_qkvz, "w_qkvz", dtype, (4 * H * d, d_model), dev),
+            _dev(w_o, "w_o", dtype, (d_model, H * d), dev))
+
+
+def _workspace(workspace, need, dev):
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    return workspace, _dev(workspace, "workspace", None, None, dev), \
+        workspace.numel() * workspace.element_size()
+
+
+def lightning_layer_prefill(x, w_qkvz, w_o, q_norm_w, k_norm_w, lambdas, rope_base, H, d,
+                            rms_eps=1e-6, pos0=0, state_in=None, state_out=None, out=None,
+                            o_norm_w=None, chunk=0, segments=0, workspace=None,
+                            stage_events=None, stream=None):
+    """The RNN layer on ``x`` [B, T, d_model]: x W_qkvz^T -> mixer -> W_o; returns ``out``
+    [B, T, d_model] (allocated if not given).  ``workspace`` (uint8, at least the size query's
+    bytes) receives the projections and the mixer output at the offsets the C header gives.
+    ``stage_events``: None or four raw hipEvent_t handles (integers)."""
+    B, T, d_model = x.shape
+    dev = x.device
+    dt = _dtype_code(x.dtype)
+    xp = _dev(x, "x", x.dtype, x.shape, dev)
+    wqp, wop = _layer_weights(w_qkvz, w_o, H, d, d_model, x.dtype, dev)
+    (qwp, kwp, owp), stride = _norm_weights(q_norm_w, k_norm_w, o_norm_w, H, d, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    outp = _dev(out, "out", x.dtype, x.shape, dev)
+    sshape = (B, H, d, d)
+    sip = _dev(state_in, "state_in", torch.float32, sshape, dev)
+    sop = _dev(state_out, "state_out", torch.float32, sshape, dev)
+    need = lightning_layer_prefill_workspace_size(B, T, H, d, d_model, x.dtype, chunk, segments)
+    workspace, wsp, wbytes = _workspace(workspace, need, dev)
+    evp = None
+    if stage_events is not None:
+        evp = (ct.c_void_p * 4)(*(ct.c_void_p(int(e)) for e in stage_events))
+    st = lib.lightning_layer_prefill(xp, wqp, wop, qwp, kwp, owp, stride,
+                                     _lambda_array(lambdas, H), float(rope_base), float(rms_eps),
+                                     int(pos0), sip, sop, outp, B, T, H, d, d_model, dt,
+                                     int(chunk), int(segments), wsp, wbytes, evp,
+                                     _stream(stream, dev))
+    _check(st, "lightning_layer_prefill")
+    return out
+
+
+def lightning_layer_decode_step(x, w_qkvz, w_o, q_norm_w, k_norm_w, lambdas, rope_base, H, d,
+                                positions, state_in, state_out=None, rms_eps=1e-6, out=None,
+                                o_norm_w=None, workspace=None, stream=None):
+    """One decode step of the RNN layer on ``x`` [B, d_model]; ``state_out`` defaults to
+    ``state_in`` (in place).  Returns ``out`` [B, d_model]."""
+    B, d_model = x.shape
+    dev = x.device
+    dt = _dtype_code(x.dtype)
+    xp = _dev(x, "x", x.dtype, x.shape, dev)
+    wqp, wop = _layer_weights(w_qkvz, w_o, H, d, d_model, x.dtype, dev)
+    (qwp, kwp, owp), stride = _norm_weights(q_norm_w, k_norm_w, o_norm_w, H, d, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    if state_out is None:
+        state_out = state_in
+    sshape = (B, H, d, d)
+    need = lightning_layer_decode_workspace_size(B, H, d, d_model, x.dtype)
+    workspace, wsp, wbytes = _workspace(workspace, need, dev)
+    st = lib.lightning_layer_decode_step(xp, wqp, wop, qwp, kwp, owp, stride,
+                                         _lambda_array(lambdas, H), float(rope_base),
+                                         float(rms_eps),
+                                         _dev(positions, "positions", torch.int64, (B,), dev),
+                                         _dev(state_in, "state_in", torch.float32, sshape, dev),
+                                         _dev(state_out, "state_out", torch.float32, sshape, dev),
+                                         _dev(out, "out", x.dtype, x.shape, dev), B, H, d, d_model,
+                                         dt, wsp, wbytes, _stream(stream, dev))
+    _check(st, "lightning_layer_decode_step")
+    return out

@@ -71,12 +71,50 @@ QWEN8_128K = PrefillSpec("Qwen3-8B-shaped RNN layer prefill B=4 H=32 T=131072 d=
                          131072, 32, 128, torch.bfloat16, tuple(qwen_lambdas(32)), 1e6, "uniform",
                          "randn", 0, 1004)
 
+@dataclasses.dataclass(frozen=True)
+class LayerSpec:
+    """Inputs of the whole RNN layer: x [B, T, d_model] and the projection weights.
+
+    values = "gauss": x ~ N(0, 1) (the layer input is an RMS-normalised residual stream) and
+    weights ~ N(0, 1/fan_in), so the projections have unit scale like the mixer workloads.
+    values = "ternary": x and the weights drawn from {-1, 0, 1} (weights mostly 0), so that with
+    d_model <= 256 every projection is an integer of magnitude <= 256, exactly representable in
+    bf16 and summed exactly in fp32 (a case where the projections carry no rounding at all).
+    """
+    name: str
+    B: int
+    T: int  # 1 for a decode step
+    H: int
+    d: int
+    d_model: int
+    dtype: torch.dtype
+    lambdas: tuple
+    rope_base: float
+    norm_w: str
+    state: str
+    seed: int
+    values: str = "gauss"
+    eps: float = 1e-6
+    pos0: int = 0
+    max_pos: int = 524288  # decode positions ~ U[0, max_pos)
+
+
+LAYER_QWEN17_512K = LayerSpec(
+    "Qwen3-1.7B-shaped RNN layer (projections + mixer) B=1 T=524288 H=16 d=128 d_model=2048 bf16",
+    1, 524288, 16, 128, 2048, torch.bfloat16, tuple(qwen_lambdas(16)), 1e6, "uniform", "zeros",
+    1005)
+LAYER_DECODE_B64 = LayerSpec(
+    "Qwen3-1.7B-shaped RNN layer decode step B=64 H=16 d=128 d_model=2048 bf16, fp32 state",
+    64, 1, 16, 128, 2048, torch.bfloat16, tuple(qwen_lambdas(16)), 1e6, "uniform", "randn", 1006)
+
 WORKLOADS = {
     "tiny": TINY,
     "qwen17_32k": QWEN17_32K,
     "qwen17_512k": QWEN17_512K,
     "decode_b64": DECODE_B64,
     "qwen8_128k": QWEN8_128K,
+    "layer_qwen17_512k": LAYER_QWEN17_512K,
+    "layer_decode_b64": LAYER_DECODE_B64,
 }
 
 
@@ -147,6 +185,60 @@ def make_custom_prefill(B, T, H, d, dtype=torch.bfloat16, seed=0, lambdas=None, 
     if v_scale != 1.0:
         out["v"] = (out["v"].float() * v_scale).to(dtype)
     return out
+
+
+def _ternary(shape, gen, device, p_nonzero):
+    u = torch.rand(shape, generator=gen, device=device, dtype=torch.float32)
+    s = torch.rand(shape, generator=gen, device=device, dtype=torch.float32)
+    return torch.where(u < p_nonzero, torch.where(s < 0.5, -1.0, 1.0), 0.0)
+
+
+def make_layer(spec: LayerSpec, device="cpu", T: int | None = None, B: int | None = None) -> dict:
+    """Draw one layer batch: x [B, T, d_model] (prefill) or [B, d_model] (a decode step, T = 1
+    in the spec), w_qkvz [4 H d, d_model], w_o [d_model, H d] and the mixer's parameters."""
+    T = spec.T if T is None else T
+    B = spec.B if B is None else B
+    H, d, dm = spec.H, spec.d, spec.d_model
+    gen = _gen(spec.seed, device)
+    decode = spec.T == 1
+    xshape = (B, dm) if decode else (B, T, dm)
+    if spec.values == "ternary":
+        if dm > 256 or H * d > 256:
+            raise ValueError("ternary layer inputs need d_model <= 256 and H d <= 256")
+        x = _ternary(xshape, gen, device, 0.5).to(spec.dtype)
+        w_qkvz = _ternary((4 * H * d, dm), gen, device, 0.125).to(spec.dtype)
+        w_o = _ternary((dm, H * d), gen, device, 0.125).to(spec.dtype)
+    else:
+        x = _randn(xshape, gen, device, spec.dtype)
+        w_qkvz = _randn((4 * H * d, dm), gen, device, spec.dtype, dm ** -0.5)
+        w_o = _randn((dm, H * d), gen, device, spec.dtype, (H * d) ** -0.5)
+    if spec.norm_w == "ones":
+        qw = torch.ones((H, d), device=device, dtype=torch.float32)
+        kw = torch.ones((H, d), device=device, dtype=torch.float32)
+    else:
+        qw = 0.5 + torch.rand((H, d), generator=gen, device=device, dtype=torch.float32)
+        kw = 0.5 + torch.rand((H, d), generator=gen, device=device, dtype=torch.float32)
+    state = None
+    if spec.state == "randn":
+        state = _randn((B, H, d, d), gen, device, torch.float32, 0.01)
+    out = dict(x=x, w_qkvz=w_qkvz, w_o=w_o, qw=qw, kw=kw, ow=None, lambdas=list(spec.lambdas),
+               rope_base=spec.rope_base, eps=spec.eps, pos0=spec.pos0, state_in=state, B=B, T=T,
+               H=H, d=d, d_model=dm, dtype=spec.dtype)
+    if decode:
+        out["positions"] = torch.randint(0, spec.max_pos, (B,), generator=gen, device=device,
+                                         dtype=torch.int64)
+    return out
+
+
+def make_custom_layer(B, T, H, d, d_model, dtype=torch.bfloat16, seed=0, lambdas=None,
+                      rope_base=1e6, norm_w="uniform", state="zeros", values="gauss", pos0=0,
+                      eps=1e-6, device="cpu") -> dict:
+    """Arbitrary-shape layer batch (T = 1 draws a decode step with random positions)."""
+    if lambdas is None:
+        lambdas = qwen_lambdas(H)
+    spec = LayerSpec("custom", B, T, H, d, d_model, dtype, tuple(lambdas), rope_base, norm_w,
+                     state, seed, values, eps, pos0)
+    return make_layer(spec, device)
 
 
 def host_bits(t: torch.Tensor) -> np.ndarray:

@@ -207,3 +207,95 @@ def test_state_init_rejects():
     assert lt.lib.lightning_state_init(None, 1, 1, 64, None, None) == lt.LT_ERR_INVALID_ARG
     assert lt.lib.lightning_state_init(FAKE + 4, 1, 1, 64, None, None) == lt.LT_ERR_INVALID_ARG
     assert lt.lib.lightning_state_init(FAKE, 0, 1, 64, None, None) == lt.LT_ERR_INVALID_ARG
+
+
+# ---- the whole layer -------------------------------------------------------------------------------
+
+def test_layer_workspace_sizes():
+    # 512K-token Qwen3-1.7B-shaped layer: projections and y in bf16, then the mixer's state slots,
+    # then 32 MiB of GEMM scratch, each part 256-byte aligned
+    B, T, H, d, dm = 1, 524288, 16, 128, 2048
+    mix = lt.lightning_prefill_workspace_size(B, T, H, d)
+    expect = T * 4 * H * d * 2 + T * H * d * 2 + (mix + 255) // 256 * 256 + (32 << 20)
+    assert lt.lightning_layer_prefill_workspace_size(B, T, H, d, dm) == expect
+    assert lt.lightning_layer_decode_workspace_size(64, H, d, dm) == \
+        64 * 4 * H * d * 2 + 64 * H * d * 2 + (32 << 20)
+    f32 = lt.lightning_layer_decode_workspace_size(3, 2, 64, 64, torch.float32)
+    assert f32 == (3 * 512 * 4 + 255) // 256 * 256 + (3 * 128 * 4 + 255) // 256 * 256 + (32 << 20)
+    assert lt.lightning_layer_prefill_workspace_size(B, T, H, d, 100) == 0  # d_model % 8
+    assert lt.lightning_layer_prefill_workspace_size(B, T, H, 96, dm) == 0
+    assert lt.lightning_layer_decode_workspace_size(0, H, d, dm) == 0
+
+
+def _layer_args(**over):
+    H = over.pop("H", 2)
+    lam = over.pop("lam", [0.9] * H)
+    a = dict(x=FAKE, w=FAKE, wo=FAKE, qw=FAKE, kw=FAKE, ow=None, stride=128,
+             lam=(ct.c_double * len(lam))(*lam), base=1e6, eps=1e-6, pos0=0, sin=None, sout=None,
+             out=FAKE, B=1, T=256, H=H, d=128, dm=256, dt=lt.LT_BF16, chunk=0, seg=0,
+             ws=FAKE * 16, wsb=1 << 40, ev=None, stream=None)
+    a.update(over)
+    return a
+
+
+LAYER_BAD = [
+    ("null_x", dict(x=None), lt.LT_ERR_INVALID_ARG),
+    ("misaligned_w_qkvz", dict(w=FAKE + 8), lt.LT_ERR_INVALID_ARG),
+    ("null_w_o", dict(wo=None), lt.LT_ERR_INVALID_ARG),
+    ("null_out", dict(out=None), lt.LT_ERR_INVALID_ARG),
+    ("d_model_not_multiple_of_8", dict(dm=100), lt.LT_ERR_INVALID_ARG),
+    ("zero_T", dict(T=0), lt.LT_ERR_INVALID_ARG),
+    ("bad_dtype", dict(dt=3), lt.LT_ERR_INVALID_ARG),
+    ("d_96", dict(d=96, stride=96), lt.LT_ERR_UNSUPPORTED),
+    ("workspace_missing", dict(ws=None), lt.LT_ERR_WORKSPACE),
+    ("workspace_small", dict(wsb=1 << 20), lt.LT_ERR_WORKSPACE),
+    ("workspace_not_256_aligned", dict(ws=FAKE * 16 + 16), lt.LT_ERR_WORKSPACE),
+    # mixer arguments are checked before the first GEMM is enqueued
+    ("lambda_nan", dict(lam=[float("nan"), 0.5]), lt.LT_ERR_INVALID_ARG),
+    ("null_qnorm", dict(qw=None), lt.LT_ERR_INVALID_ARG),
+    ("rope_base_zero", dict(base=0.0), lt.LT_ERR_INVALID_ARG),
+    ("misaligned_state_out", dict(sout=FAKE + 4), lt.LT_ERR_INVALID_ARG),
+    ("pos0_negative", dict(pos0=-3), lt.LT_ERR_INVALID_ARG),
+    ("events_null_entries", dict(ev=(ct.c_void_p * 4)(FAKE, None, FAKE, FAKE)),
+     lt.LT_ERR_INVALID_ARG),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,over,status", LAYER_BAD, ids=[c[0] for c in LAYER_BAD])
+def test_layer_prefill_rejects(name, over, status):
+    a = _layer_args(**over)
+    st = lt.lib.lightning_layer_prefill(a["x"], a["w"], a["wo"], a["qw"], a["kw"], a["ow"],
+                                        a["stride"], a["lam"], a["base"], a["eps"], a["pos0"],
+                                        a["sin"], a["sout"], a["out"], a["B"], a["T"], a["H"],
+                                        a["d"], a["dm"], a["dt"], a["chunk"], a["seg"], a["ws"],
+                                        a["wsb"], a["ev"], a["stream"])
+    assert st == status
+
+
+LAYER_DECODE_BAD = [
+    ("null_x", dict(x=None), lt.LT_ERR_INVALID_ARG),
+    ("d_model_not_multiple_of_8", dict(dm=12), lt.LT_ERR_INVALID_ARG),
+    ("workspace_small", dict(wsb=4096), lt.LT_ERR_WORKSPACE),
+    ("null_positions", dict(pos=None), lt.LT_ERR_INVALID_ARG),
+    ("null_state_in", dict(sin=None), lt.LT_ERR_INVALID_ARG),
+    ("lambda_above_one", dict(lam=[1.5, 0.5]), lt.LT_ERR_INVALID_ARG),
+    ("eps_negative", dict(eps=-1.0), lt.LT_ERR_INVALID_ARG),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,over,status", LAYER_DECODE_BAD,
+                         ids=[c[0] for c in LAYER_DECODE_BAD])
+def test_layer_decode_rejects(name, over, status):
+    lam = over.pop("lam", [0.9, 0.99])
+    a = dict(x=FAKE, w=FAKE, wo=FAKE, qw=FAKE, kw=FAKE, ow=None, stride=128,
+             lam=(ct.c_double * 2)(*lam), base=1e6, eps=1e-6, pos=FAKE, sin=FAKE, sout=FAKE,
+             out=FAKE, B=4, H=2, d=128, dm=256, dt=lt.LT_BF16, ws=FAKE * 16, wsb=1 << 40,
+             stream=None)
+    a.update(over)
+    st = lt.lib.lightning_layer_decode_step(a["x"], a["w"], a["wo"], a["qw"], a["kw"], a["ow"],
+                                            a["stride"], a["lam"], a["base"], a["eps"], a["pos"],
+                                            a["sin"], a["sout"], a["out"], a["B"], a["H"], a["d"],
+                                            a["dm"], a["dt"], a["ws"], a["wsb"], a["stream"])
+    assert st == status
