@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--no-layer", action="store_true",
                     help="skip the whole-layer legs (projections + mixer + output projection)")
     ap.add_argument("--layer-steps", type=int, default=5)
-    ap.add_argument("--cpu-layer-tokens", type=int, default=8192)
+    ap.add_argument("--cpu-layer-tokens", type=int, default=65536)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed runs, copy this many MiB device to device three times "
                          "(a plain copy of known size that calibrates HBM byte counters)")
@@ -71,15 +71,18 @@ def copy_calibration(torch, mib):
 
 
 MIXER_SOURCES = ("abi.hip", "decode.hip", "lt_device.h", "lt_internal.h", "prefill.hip")
+LAYER_SOURCES = ("gemm.hip", "layer.hip")
+LAYER_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic_layer_qwen17_512k.md")
 
 
-def source_fingerprint():
-    """sha256 over the sources of the mixer kernels and their launch configuration (the code the
-    byte counters measured)."""
+def source_fingerprint(sources=MIXER_SOURCES):
+    """sha256 over the sources of the measured kernels and their launch configuration (the code
+    the byte counters measured): the mixer's by default, the layer's GEMM calls with
+    LAYER_SOURCES."""
     import hashlib
 
     h = hashlib.sha256()
-    files = [os.path.join(ROOT, "long_context_hybrid_amd", "csrc", f) for f in MIXER_SOURCES]
+    files = [os.path.join(ROOT, "long_context_hybrid_amd", "csrc", f) for f in sources]
     for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
@@ -87,19 +90,19 @@ def source_fingerprint():
     return h.hexdigest()
 
 
-def measured_traffic(kernel, workload):
+def measured_traffic(kernel, workload, record=TRAFFIC_RECORD, sources=MIXER_SOURCES):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     record, scaled by what the same counters read for a plain copy of known size; None when no
     record exists for this workload or the kernel sources changed since it was taken."""
     try:
-        with open(TRAFFIC_RECORD) as fh:
+        with open(record) as fh:
             lines = [l for l in fh if l.startswith("traffic-record: ")]
     except OSError:
         return None
     if not lines:
         return None
     rec = json.loads(lines[-1][len("traffic-record: "):])
-    if rec.get("source_sha256") != source_fingerprint():
+    if rec.get("source_sha256") != source_fingerprint(sources):
         return None
     k = rec["kernels"].get(kernel)
     if k is None or k.get("workload") != workload:
@@ -272,10 +275,13 @@ def bench_layer(args, torch, lt, synth):
                           "o_gemm": round(stage[2], 4)},
             "roofline": {"bound": "mfma", "achieved": round(t1, 1), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(t1 / BF16_PEAK_TFLOPS, 4),
-                         "traffic": None,
+                         "traffic": measured_traffic("qkvz_gemm", spec.name,
+                                                     LAYER_TRAFFIC_RECORD, LAYER_SOURCES),
                          "kernel": "hipBLASLt bf16 GEMM x [W_q|W_k|W_v|W_z] (M=%d N=%d K=%d)"
                                    % (rows, 4 * H * d, dm),
-                         "flops_per_launch": f1, "launch_ms": round(stage[0], 4)},
+                         "flops_per_launch": f1, "launch_ms": round(stage[0], 4),
+                         "alg_bytes_per_launch": rows * dm * 2 + 4 * H * d * dm * 2
+                                                 + rows * 4 * H * d * 2},
             "o_gemm": {"achieved_tflops": round(t2, 1), "frac": round(t2 / BF16_PEAK_TFLOPS, 4),
                        "flops_per_launch": f2},
             "mfma_floor_ms": round((f1 + f2) / (BF16_PEAK_TFLOPS * 1e12) * 1e3, 3)}
