@@ -14,7 +14,9 @@ library around that kernel on the launch stream), its MFMA rate, the batched dec
 a bounded sample of the same prefill workload on this host's cores.  Under ``layer``: the whole
 RNN layer around the mixer (QKVZ projection GEMM, mixer, output projection GEMM; d_model = 2048)
 at the same 512K tokens with per-stage times and the QKVZ GEMM's MFMA roofline, its B = 64
-decode step, and the layer oracle timed on a bounded sample.
+decode step, and the layer oracle timed on a bounded sample.  Under ``attention``: the hybrid's
+HyPE softmax-attention layer (NoPE, s_t = log_a(t + a) logits scale, 16 query / 8 key-value
+heads) at 512K tokens with the flash kernel's MFMA roofline, and its oracle on sampled rows.
 """
 from __future__ import annotations
 
@@ -53,6 +55,10 @@ def parse():
                     help="skip the whole-layer legs (projections + mixer + output projection)")
     ap.add_argument("--layer-steps", type=int, default=5)
     ap.add_argument("--cpu-layer-tokens", type=int, default=65536)
+    ap.add_argument("--no-attn", action="store_true", help="skip the HyPE attention leg")
+    ap.add_argument("--attn-steps", type=int, default=2)
+    ap.add_argument("--attn-warmup", type=int, default=1)
+    ap.add_argument("--cpu-attn-rows", type=int, default=32)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed runs, copy this many MiB device to device three times "
                          "(a plain copy of known size that calibrates HBM byte counters)")
@@ -328,6 +334,73 @@ def bench_layer_decode(args, torch, lt, synth):
             "rotating_sets": nset}
 
 
+def bench_attn(args, torch, lt, synth):
+    """HyPE softmax attention (the hybrid's attention layers) at 512K tokens: the prologue
+    (QK-norm and the s_t log2(e)/sqrt(d) query scale) and the flash-attention kernel, the latter
+    timed with the HIP events the library records around it."""
+    spec = synth.ATTN_QWEN17_512K
+    dev = torch.device("cuda:0")
+    inp = synth.make_attn(spec, device=dev)
+    B, T, Hq, Hkv, d = inp["B"], inp["T"], inp["Hq"], inp["Hkv"], inp["d"]
+    y = torch.empty_like(inp["q"])
+    cache = torch.empty_like(inp["k"])
+    ws = torch.empty(lt.lightning_attn_prefill_workspace_size(B, T, Hq, Hkv, d, torch.bfloat16,
+                                                              True, True),
+                     dtype=torch.uint8, device=dev)
+    call = (inp["q"], inp["k"], inp["v"], inp["g"], inp["a"])
+    kw = dict(q_norm_w=inp["qw"], k_norm_w=inp["kw"], rms_eps=inp["eps"], y=y,
+              key_cache_out=cache, workspace=ws)
+    for _ in range(args.attn_warmup):
+        lt.lightning_attn_prefill(*call, **kw)
+    torch.cuda.synchronize()
+    hev = HipEvents()
+    n = args.attn_steps
+    ev = hev.create(2 * n)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(n):
+        lt.lightning_attn_prefill(*call, **kw, main_kernel_events=(ev[2 * i], ev[2 * i + 1]))
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / n
+    main_ms = sum(hev.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for i in range(n)) / n
+    hev.destroy(ev)
+    flops = 4 * d * Hq * B * T * (T + 1) // 2  # q.k and p.v over the causal triangle
+    tf = flops / (main_ms * 1e-3) / 1e12
+    del inp, y, cache, ws
+    return {"workload": spec.name, "ms_per_step": round(ms, 3),
+            "value": round(B * T / (ms * 1e-3), 1), "unit": "tokens/s/layer", "steps": n,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                         "traffic": None, "kernel": "attn_fwd_kernel<2> (flash attention)",
+                         "flops_per_launch": flops, "launch_ms": round(main_ms, 3)},
+            "prologue_ms": round(ms - main_ms, 3)}
+
+
+def cpu_baseline_attn(args, torch, synth):
+    """The attention oracle on evenly spaced query rows of the 512K workload (all heads): their
+    mean cost is the mean over all rows, so rows / time estimates the whole prefill's rate."""
+    import numpy as np
+
+    from oracle import attention as oa
+
+    spec = synth.ATTN_QWEN17_512K
+    inp = synth.make_attn(spec, device="cuda:0")
+    host = {n: synth.host_bits(inp[n].cpu()) for n in ("q", "k", "v", "g")}
+    n = args.cpu_attn_rows
+    T = inp["T"]
+    rows = (np.arange(n) * T + T // 2) // n
+    t0 = time.perf_counter()
+    r = oa.attn_prefill(host["q"], host["k"], host["v"], host["g"], inp["qw"].cpu().numpy(),
+                        inp["kw"].cpu().numpy(), None, a=inp["a"], eps=inp["eps"], rows=rows,
+                        want_k_hat=False)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(r["y"]).all()
+    return {"value": round(n / dt, 3), "unit": "tokens/s/layer", "cores": 1, "kind": "oracle",
+            "sample": f"{n} evenly spaced query rows (all {inp['Hq']} heads) of the {spec.name} "
+                      f"workload, fp64 numpy on one thread of control, {dt:.1f} s"}
+
+
 def cpu_baseline_layer(args, torch, synth):
     """The layer oracle (fp64 projections through numpy, the fp64 recurrence in C threads) on the
     first tokens of the 512K layer workload."""
@@ -408,6 +481,11 @@ def main():
             print(f"[bench] layer decode B=64: steps {args.decode_steps}", file=sys.stderr,
                   flush=True)
             layer["decode"] = bench_layer_decode(args, torch, lt, synth)
+    attn = None
+    if not args.no_attn:
+        print(f"[bench] attention prefill 512K: warmup {args.attn_warmup}, steps {args.attn_steps}",
+              file=sys.stderr, flush=True)
+        attn = bench_attn(args, torch, lt, synth)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -415,6 +493,9 @@ def main():
         if layer is not None:
             print("[bench] cpu baseline of the layer (oracle)", file=sys.stderr, flush=True)
             layer["cpu_baseline"] = cpu_baseline_layer(args, torch, synth)
+        if attn is not None:
+            print("[bench] cpu baseline of the attention (oracle)", file=sys.stderr, flush=True)
+            attn["cpu_baseline"] = cpu_baseline_attn(args, torch, synth)
     if args.copy_mib > 0:
         print(f"[bench] calibration copy of {args.copy_mib} MiB", file=sys.stderr, flush=True)
         copy_calibration(torch, args.copy_mib)
@@ -439,6 +520,7 @@ def main():
         "whole_call": pre["whole_call"],
         "decode": dec,
         "layer": layer,
+        "attention": attn,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

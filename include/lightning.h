@@ -192,6 +192,42 @@ lt_status lightning_layer_decode_step(const void* x, const void* w_qkvz, const v
                                       int d_model, int dtype, void* workspace,
                                       size_t workspace_bytes, void* stream);
 
+/*
+ * ---- HyPE softmax attention (Appendix A, Eq. 17; Section 5.1, Eq. 11; Eq. 14 gate) ----
+ *
+ * Causal attention of the hybrid's attention layers, with no position encoding (NoPE) and the
+ * logits of query t scaled by s_t = log_a(p_t + a), p_t = pos0 + t (0-based, so s = 1 at
+ * position 0):
+ *   q^ = RMSNorm(q_t) * w_q[h]   k^ = RMSNorm(k_j) * w_k[kvh]     (only when the weight is given)
+ *   o_t = sum_{j <= t} softmax_j( s_t q^_t . k^_j / sqrt(d) ) v_j
+ *   y_t = RMSNorm(o_t) * w_o[h] * sigmoid(g_t)
+ * Query head h reads key/value head h / (Hq / Hkv) (grouped-query attention; Hq a multiple of
+ * Hkv).  A prefill call attends over its own T tokens.
+ *
+ *   q, gate       : device [B][T][Hq][d] bf16;  k, v : device [B][T][Hkv][d] bf16.
+ *   q_norm_w      : device fp32 [Hq][d] (or [d] with norm_w_head_stride 0), or NULL: no norm.
+ *   k_norm_w      : device fp32 [Hkv][d] (or [d]), or NULL.   o_norm_w : [Hq][d] (or [d]) or NULL.
+ *   logit_scale_base : a > 1, or 0 for s_t = 1.
+ *   y             : device [B][T][Hq][d] bf16.  o_raw : device fp32 [B][T][Hq][d] or NULL.
+ *   key_cache_out : device [B][T][Hkv][d] bf16 receiving the keys the scores used (normalised
+ *                   when k_norm_w is given), the key cache of lightning_attn_decode_step; or NULL.
+ *   workspace     : at least lightning_attn_prefill_workspace_size(...) bytes, 256-byte aligned
+ *                   (has_key_norm = k_norm_w != NULL, has_key_cache = key_cache_out != NULL).
+ *   main_kernel_events : NULL or two hipEvent_t recorded around the attention kernel (after the
+ *                   prologue that normalises and scales q and k).
+ * Supported: d = 128, bf16 (others return LT_ERR_UNSUPPORTED).
+ */
+size_t lightning_attn_prefill_workspace_size(int B, int T, int Hq, int Hkv, int d, int dtype,
+                                             int has_key_norm, int has_key_cache);
+
+lt_status lightning_attn_prefill(const void* q, const void* k, const void* v, const void* gate,
+                                 const float* q_norm_w, const float* k_norm_w,
+                                 const float* o_norm_w, int norm_w_head_stride,
+                                 double logit_scale_base, double rms_eps, int64_t pos0, void* y,
+                                 float* o_raw, void* key_cache_out, int B, int T, int Hq, int Hkv,
+                                 int d, int dtype, void* workspace, size_t workspace_bytes,
+                                 void* const* main_kernel_events, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -73,6 +73,44 @@ __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// MFMA layouts (v_mfma_f32_32x32x16_bf16 and v_mfma_f32_32x32x2_f32 on gfx950):
+//   A[m][k]: lane l holds m = l % 32 and k = 8 (l / 32) + e (bf16, e < 8) or k = l / 32 (fp32);
+//   B[k][n]: lane l holds n = l % 32 and the same k;
+//   C[m][n]: lane l, register r holds n = l % 32, m = 8 (r / 4) + 4 (l / 32) + r % 4.
+// Row index inside a 32x32 accumulator tile for lane half lh and register r.
+__device__ __forceinline__ int acc_row(int r, int lh) { return 8 * (r >> 2) + 4 * lh + (r & 3); }
+
+// bf16 tiles (the mixer's decayed keys and values, attention values) are kept in natural
+// [token][feature] order with D-element rows.  The 32-feature blocks of a row are XOR-permuted by the row's position within a 256-byte
+// bank window, so that an MFMA operand gathered across four consecutive rows with
+// ds_read_b64_tr_b16 touches 64 distinct banks.
+template <int D>
+__device__ __forceinline__ int nat_index(int row, int col) {
+    return row * D + (col ^ (32 * ((row / (128 / D)) % (D / 32))));
+}
+// An MFMA operand whose m (or n) index runs along the rows of a natural tile, with its 16 k
+// values (tokens kbase .. kbase + 15) in accumulator order: lane l receives column
+// colbase + l % 32 of row kbase + 8 (e / 4) + 4 (l / 32) + e % 4 in element e < 8, the order in
+// which a score accumulator re-typed to bf16 holds its tokens (so P V and the state update can
+// share the V operand; any common order serves the state update).  ds_read_b64_tr_b16 gives lane
+// 4a + c of each 16-lane group element c of the 4-element row segments addressed by lanes a,
+// 4 + a, 8 + a and 12 + a of that group; lane s therefore addresses row
+// kbase + 4 (group / 2) + s / 4 at column colbase + 16 (group % 2) + 4 (s % 4), and a second read
+// does the rows 8 further on.
+typedef short tr16x4 __attribute__((ext_vector_type(4)));
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const __bf16* tile, int kbase, int colbase, int lane) {
+    const int g = lane >> 4, sl = lane & 15;
+    const int row = kbase + 4 * (g >> 1) + (sl >> 2);
+    const int col = colbase + 16 * (g & 1) + 4 * (sl & 3);
+    typedef __attribute__((address_space(3))) tr16x4 lds_t;
+    const tr16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_t*)(tile + nat_index<D>(row, col)));
+    const tr16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_t*)(tile + nat_index<D>(row + 8, col)));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, ab);
+}
+
 // lambda^n from log2(lambda), with lambda^0 = 1 also for lambda = 0 (log2 = -inf).  The bare
 // hardware exp2 is used: a decay factor below 2^-126 contributes nothing at fp32 precision.
 __device__ __forceinline__ float pow_lambda(float log2_lambda, int n) {

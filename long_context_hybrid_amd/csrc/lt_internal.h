@@ -73,11 +73,37 @@ struct DecodeParams {
     double inv_freq_rev[64];
 };
 
+// HyPE attention prefill.  qs / ks are the prologue's outputs (ks == k when the keys are used
+// as given); everything else is as passed to lightning_attn_prefill.
+constexpr int kAttnHeadDim = 128;
+struct AttnParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const float* qw;  // may be null (no query norm)
+    const float* kw;  // may be null (no key norm)
+    const float* ow;  // may be null (ones)
+    void* qs;         // [B][T][Hq][d] bf16: s_t log2(e) / sqrt(d) * normalised queries
+    void* ks;         // [B][T][Hkv][d] bf16: the keys the scores use (== k, not written, when
+                      // write_keys is 0)
+    void* y;
+    float* o_raw;     // may be null
+    int64_t pos0;
+    int B, T, Hq, Hkv, w_stride;
+    int write_keys;   // the prologue writes normalised (or copied) keys to ks
+    float eps;
+    double a, log_a;  // logits scale base and ln(a); log_a == 0: no scale
+};
+
 // events[0] / events[1] (may be null) are recorded just before / after the main chunk kernel.
 hipError_t launch_prefill(const ChunkParams& cp, const ScanParams& sp, int d, int dtype,
                           const hipEvent_t events[2], hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& dp, int d, int dtype, hipStream_t stream);
 hipError_t launch_state_init(float* state, const float* init, size_t n, hipStream_t stream);
+// events[0] / events[1] (may be null) bracket the flash-attention kernel (after the prologue).
+hipError_t launch_attn_prefill(const AttnParams& p, const hipEvent_t events[2], hipStream_t stream);
+int attn_heads_per_workgroup(int Hq, int Hkv);
 
 // lightning_prefill / lightning_decode_step with q, k, v and g read at a token (prefill) or
 // sequence (decode) stride of x_stride elements, e.g. column blocks of one fused projection.

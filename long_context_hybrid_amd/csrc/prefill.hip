@@ -57,8 +57,6 @@ constexpr int kPrefetchMain = LT_PREFETCH_MAIN;
 constexpr int kPrefetchStateOnly = LT_PREFETCH_STATE;
 constexpr int kRopeAnchor = 64;  // chunks between exact recomputations of the RoPE base table
 
-// Row index inside a 32x32 accumulator tile for lane half lh and register r.
-__device__ __forceinline__ int acc_row(int r, int lh) { return 8 * (r >> 2) + 4 * lh + (r & 3); }
 
 // The chunk loop keeps the state lazily decayed: state = alpha * S with alpha = lambda^X, where
 // X counts the tokens since the last renormalisation, so most chunks skip the d x d rescale and
@@ -173,37 +171,6 @@ __device__ __forceinline__ void st_pair(float* dst, float4 row0, float4 row1, in
     const float a = u == 0 ? row0.x : u == 1 ? row0.y : u == 2 ? row0.z : row0.w;
     const float b = u == 0 ? row1.x : u == 1 ? row1.y : u == 2 ? row1.z : row1.w;
     *reinterpret_cast<float2*>(dst) = make_float2(a, b);
-}
-
-// bf16 tiles of decayed keys and values are kept in natural [token][feature] order with D-element
-// rows.  The 32-feature blocks of a row are XOR-permuted by the row's position within a 256-byte
-// bank window, so that an MFMA operand gathered across four consecutive rows with
-// ds_read_b64_tr_b16 touches 64 distinct banks.
-template <int D>
-__device__ __forceinline__ int nat_index(int row, int col) {
-    return row * D + (col ^ (32 * ((row / (128 / D)) % (D / 32))));
-}
-// An MFMA operand whose m (or n) index runs along the rows of a natural tile, with its 16 k
-// values (tokens kbase .. kbase + 15) in accumulator order: lane l receives column
-// colbase + l % 32 of row kbase + 8 (e / 4) + 4 (l / 32) + e % 4 in element e < 8, the order in
-// which a score accumulator re-typed to bf16 holds its tokens (so P V and the state update can
-// share the V operand; any common order serves the state update).  ds_read_b64_tr_b16 gives lane
-// 4a + c of each 16-lane group element c of the 4-element row segments addressed by lanes a,
-// 4 + a, 8 + a and 12 + a of that group; lane s therefore addresses row
-// kbase + 4 (group / 2) + s / 4 at column colbase + 16 (group % 2) + 4 (s % 4), and a second read
-// does the rows 8 further on.
-typedef short tr16x4 __attribute__((ext_vector_type(4)));
-template <int D>
-__device__ __forceinline__ bf16x8 tr_operand(const __bf16* tile, int kbase, int colbase, int lane) {
-    const int g = lane >> 4, sl = lane & 15;
-    const int row = kbase + 4 * (g >> 1) + (sl >> 2);
-    const int col = colbase + 16 * (g & 1) + 4 * (sl & 3);
-    typedef __attribute__((address_space(3))) tr16x4 lds_t;
-    const tr16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_t*)(tile + nat_index<D>(row, col)));
-    const tr16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_t*)(tile + nat_index<D>(row + 8, col)));
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
-    const s16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8, ab);
 }
 
 // LDS stores of 4 (row-major tiles) or 2 (transposed tiles) consecutive elements.

@@ -32,6 +32,8 @@ EXPORTS = (
     "lightning_layer_prefill",
     "lightning_layer_decode_workspace_size",
     "lightning_layer_decode_step",
+    "lightning_attn_prefill_workspace_size",
+    "lightning_attn_prefill",
 )
 
 
@@ -74,6 +76,11 @@ def _load() -> ct.CDLL:
     h.lightning_layer_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, f64, f64, vp, vp,
                                               vp, vp, i32, i32, i32, i32, i32, vp, sz, vp]
     h.lightning_layer_decode_step.restype = i32
+    h.lightning_attn_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
+    h.lightning_attn_prefill_workspace_size.restype = sz
+    h.lightning_attn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, f64, f64, i64, vp, vp,
+                                         vp, i32, i32, i32, i32, i32, i32, vp, sz, vp, vp]
+    h.lightning_attn_prefill.restype = i32
     return h
 
 
@@ -322,3 +329,55 @@ def lightning_layer_decode_step(x, w_qkvz, w_o, q_norm_w, k_norm_w, lambdas, rop
                                          dt, wsp, wbytes, _stream(stream, dev))
     _check(st, "lightning_layer_decode_step")
     return out
+
+
+# ---- HyPE softmax attention ------------------------------------------------------------------------
+
+def lightning_attn_prefill_workspace_size(B, T, Hq, Hkv, d, dtype=torch.bfloat16,
+                                          has_key_norm=True, has_key_cache=False) -> int:
+    return int(lib.lightning_attn_prefill_workspace_size(B, T, Hq, Hkv, d, _dtype_code(dtype),
+                                                         int(bool(has_key_norm)),
+                                                         int(bool(has_key_cache))))
+
+
+def _opt_weight(w, H, d, name, dev, stride):
+    if w is None:
+        return None
+    shape = (d,) if stride == 0 else (H, d)
+    return _dev(w, name, torch.float32, shape, dev)
+
+
+def lightning_attn_prefill(q, k, v, gate, logit_scale_base, q_norm_w=None, k_norm_w=None,
+                           o_norm_w=None, rms_eps=1e-6, pos0=0, y=None, o_raw=None,
+                           key_cache_out=None, workspace=None, main_kernel_events=None,
+                           stream=None):
+    """Causal HyPE attention: q, gate [B, T, Hq, d], k, v [B, T, Hkv, d] (bf16).  Norm weights
+    are None or fp32 [d] / [heads, d] (all given ones share one layout).  Returns ``y``."""
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[2]
+    dev = q.device
+    dt = _dtype_code(q.dtype)
+    given = [w for w in (q_norm_w, k_norm_w, o_norm_w) if w is not None]
+    stride = 0 if all(w.dim() == 1 for w in given) else d
+    ptrs = [_dev(q, "q", q.dtype, (B, T, Hq, d), dev), _dev(k, "k", q.dtype, (B, T, Hkv, d), dev),
+            _dev(v, "v", q.dtype, (B, T, Hkv, d), dev),
+            _dev(gate, "gate", q.dtype, (B, T, Hq, d), dev)]
+    wq = _opt_weight(q_norm_w, Hq, d, "q_norm_w", dev, stride)
+    wk = _opt_weight(k_norm_w, Hkv, d, "k_norm_w", dev, stride)
+    wo = _opt_weight(o_norm_w, Hq, d, "o_norm_w", dev, stride)
+    if y is None:
+        y = torch.empty_like(q)
+    yp = _dev(y, "y", q.dtype, q.shape, dev)
+    orp = _dev(o_raw, "o_raw", torch.float32, q.shape, dev)
+    kcp = _dev(key_cache_out, "key_cache_out", q.dtype, k.shape, dev)
+    need = lightning_attn_prefill_workspace_size(B, T, Hq, Hkv, d, q.dtype, k_norm_w is not None,
+                                                 key_cache_out is not None)
+    workspace, wsp, wbytes = _workspace(workspace, need, dev)
+    evp = None
+    if main_kernel_events is not None:
+        evp = (ct.c_void_p * 2)(*(ct.c_void_p(int(e)) for e in main_kernel_events))
+    st = lib.lightning_attn_prefill(*ptrs, wq, wk, wo, stride, float(logit_scale_base or 0.0),
+                                    float(rms_eps), int(pos0), yp, orp, kcp, B, T, Hq, Hkv, d, dt,
+                                    wsp, wbytes, evp, _stream(stream, dev))
+    _check(st, "lightning_attn_prefill")
+    return y

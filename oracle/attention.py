@@ -59,16 +59,18 @@ def _weights(w, H, d):
 
 
 def attn_prefill(q, k, v, g, qw=None, kw=None, ow=None, a=None, eps=1e-6, pos0=0, rows=None,
-                 heads=None, batches=None):
+                 heads=None, batches=None, want_k_hat=True):
     """Causal HyPE attention over one prefill call.
 
     q, g: [B, T, Hq, d]; k, v: [B, T, Hkv, d] (bf16 bits or float32).  ``rows`` selects query
     tokens (default all), ``heads`` query heads and ``batches`` batch rows.  Returns ``y`` and
-    ``o`` of shape [nb, nrows, nheads, d] (fp64) and the normalised keys ``k_hat`` [B, T, Hkv, d].
+    ``o`` of shape [nb, nrows, nheads, d] (fp64) and, with ``want_k_hat``, the normalised keys
+    ``k_hat`` [B, T, Hkv, d].  Inputs are widened one (batch row, key/value head) at a time, and
+    queries and gates only at the requested rows.
     """
-    qf, kf, vf, gf = (widen(x) for x in (q, k, v, g))
-    B, T, Hq, d = qf.shape
-    Hkv = kf.shape[2]
+    q, k, v, g = (np.asarray(x) for x in (q, k, v, g))
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[2]
     if Hq % Hkv:
         raise ValueError("Hq must be a multiple of Hkv")
     grp = Hq // Hkv
@@ -76,28 +78,36 @@ def attn_prefill(q, k, v, g, qw=None, kw=None, ow=None, a=None, eps=1e-6, pos0=0
     heads = list(range(Hq)) if heads is None else list(heads)
     batches = list(range(B)) if batches is None else list(batches)
     qwf, kwf, owf = _weights(qw, Hq, d), _weights(kw, Hkv, d), _weights(ow, Hq, d)
-    khat = kf if kwf is None else _rmsnorm(kf, kwf[None, None], eps)
     s = logit_scale(pos0 + rows, a)
     y = np.empty((len(batches), len(rows), len(heads), d))
     o = np.empty_like(y)
+    k_hat = np.empty((B, T, Hkv, d)) if want_k_hat else None
     for bi, b in enumerate(batches):
-        for hi, h in enumerate(heads):
-            kv = h // grp
-            qh = qf[b, rows, h]
-            if qwf is not None:
-                qh = _rmsnorm(qh, qwf[h], eps)
-            K = khat[b, :, kv]
-            V = vf[b, :, kv]
-            for ri, t in enumerate(rows):
-                sc = s[ri] * (K[:t + 1] @ qh[ri]) / math.sqrt(d)
-                w = np.exp(sc - sc.max())
-                ot = (w @ V[:t + 1]) / w.sum()
-                o[bi, ri, hi] = ot
-                yo = ot / math.sqrt(float(np.mean(ot * ot)) + eps)
-                if owf is not None:
-                    yo = yo * owf[h]
-                y[bi, ri, hi] = yo * _sigmoid(gf[b, t, h])
-    return {"y": y, "o": o, "k_hat": khat}
+        qb = widen(q[b, rows])  # [nrows, Hq, d]
+        gb = widen(g[b, rows])
+        for kv in sorted({h // grp for h in heads} | (set(range(Hkv)) if want_k_hat else set())):
+            K = widen(k[b, :, kv])
+            if kwf is not None:
+                K = _rmsnorm(K, kwf[kv], eps)
+            if want_k_hat:
+                k_hat[b, :, kv] = K
+            V = widen(v[b, :, kv])
+            for hi, h in enumerate(heads):
+                if h // grp != kv:
+                    continue
+                qh = qb[:, h]
+                if qwf is not None:
+                    qh = _rmsnorm(qh, qwf[h], eps)
+                for ri, t in enumerate(rows):
+                    sc = s[ri] * (K[:t + 1] @ qh[ri]) / math.sqrt(d)
+                    w = np.exp(sc - sc.max())
+                    ot = (w @ V[:t + 1]) / w.sum()
+                    o[bi, ri, hi] = ot
+                    yo = ot / math.sqrt(float(np.mean(ot * ot)) + eps)
+                    if owf is not None:
+                        yo = yo * owf[h]
+                    y[bi, ri, hi] = yo * _sigmoid(gb[ri, h])
+    return {"y": y, "o": o, "k_hat": k_hat}
 
 
 def attn_decode_step(q, k_new, v_new, g, k_cache, v_cache, lengths, qw=None, kw=None, ow=None,

@@ -107,6 +107,32 @@ LAYER_DECODE_B64 = LayerSpec(
     "Qwen3-1.7B-shaped RNN layer decode step B=64 H=16 d=128 d_model=2048 bf16, fp32 state",
     64, 1, 16, 128, 2048, torch.bfloat16, tuple(qwen_lambdas(16)), 1e6, "uniform", "randn", 1006)
 
+@dataclasses.dataclass(frozen=True)
+class AttnSpec:
+    """Inputs of one HyPE attention layer (Eq. 17): q, gate [B, T, Hq, d], k, v [B, T, Hkv, d]
+    ~ N(0, 1) in bf16; QK-norm weights shared over heads ([d], U(0.5, 1.5)) as in Qwen3's
+    attention layers, or none; the logits scale base a of Eq. 11."""
+    name: str
+    B: int
+    T: int
+    Hq: int
+    Hkv: int
+    d: int
+    a: float
+    qk_norm: bool
+    seed: int
+    eps: float = 1e-6
+    pos0: int = 0
+
+
+ATTN_QWEN17_32K = AttnSpec(
+    "HyPE attention layer (Qwen3-1.7B shape) B=1 T=32768 Hq=16 Hkv=8 d=128 bf16, a=500",
+    1, 32768, 16, 8, 128, 500.0, True, 1007)
+ATTN_QWEN17_512K = dataclasses.replace(
+    ATTN_QWEN17_32K,
+    name="HyPE attention layer (Qwen3-1.7B shape) B=1 T=524288 Hq=16 Hkv=8 d=128 bf16, a=500",
+    T=524288, seed=1008)
+
 WORKLOADS = {
     "tiny": TINY,
     "qwen17_32k": QWEN17_32K,
@@ -115,6 +141,8 @@ WORKLOADS = {
     "qwen8_128k": QWEN8_128K,
     "layer_qwen17_512k": LAYER_QWEN17_512K,
     "layer_decode_b64": LAYER_DECODE_B64,
+    "attn_qwen17_32k": ATTN_QWEN17_32K,
+    "attn_qwen17_512k": ATTN_QWEN17_512K,
 }
 
 
@@ -239,6 +267,28 @@ def make_custom_layer(B, T, H, d, d_model, dtype=torch.bfloat16, seed=0, lambdas
     spec = LayerSpec("custom", B, T, H, d, d_model, dtype, tuple(lambdas), rope_base, norm_w,
                      state, seed, values, eps, pos0)
     return make_layer(spec, device)
+
+
+def make_attn(spec: AttnSpec, device="cpu", T: int | None = None) -> dict:
+    T = spec.T if T is None else T
+    B, Hq, Hkv, d = spec.B, spec.Hq, spec.Hkv, spec.d
+    gen = _gen(spec.seed, device)
+    q = _randn((B, T, Hq, d), gen, device, torch.bfloat16)
+    k = _randn((B, T, Hkv, d), gen, device, torch.bfloat16)
+    v = _randn((B, T, Hkv, d), gen, device, torch.bfloat16)
+    g = _randn((B, T, Hq, d), gen, device, torch.bfloat16)
+    qw = kw = None
+    if spec.qk_norm:
+        qw = 0.5 + torch.rand((d,), generator=gen, device=device, dtype=torch.float32)
+        kw = 0.5 + torch.rand((d,), generator=gen, device=device, dtype=torch.float32)
+    return dict(q=q, k=k, v=v, g=g, qw=qw, kw=kw, ow=None, a=spec.a, eps=spec.eps,
+                pos0=spec.pos0, B=B, T=T, Hq=Hq, Hkv=Hkv, d=d)
+
+
+def make_custom_attn(B, T, Hq, Hkv, d=128, a=500.0, qk_norm=True, seed=0, pos0=0, eps=1e-6,
+                     device="cpu") -> dict:
+    spec = AttnSpec("custom", B, T, Hq, Hkv, d, a, qk_norm, seed, eps, pos0)
+    return make_attn(spec, device)
 
 
 def host_bits(t: torch.Tensor) -> np.ndarray:

@@ -299,3 +299,56 @@ def test_layer_decode_rejects(name, over, status):
                                             a["sin"], a["sout"], a["out"], a["B"], a["H"], a["d"],
                                             a["dm"], a["dt"], a["ws"], a["wsb"], a["stream"])
     assert st == status
+
+
+# ---- HyPE attention ---------------------------------------------------------------------------------
+
+def test_attn_workspace_sizes():
+    B, T, Hq, Hkv, d = 1, 524288, 16, 8, 128
+    q_bytes = B * T * Hq * d * 2
+    k_bytes = B * T * Hkv * d * 2
+    assert lt.lightning_attn_prefill_workspace_size(B, T, Hq, Hkv, d, torch.bfloat16, True,
+                                                    False) == q_bytes + k_bytes
+    assert lt.lightning_attn_prefill_workspace_size(B, T, Hq, Hkv, d, torch.bfloat16, True,
+                                                    True) == q_bytes
+    assert lt.lightning_attn_prefill_workspace_size(B, T, Hq, Hkv, d, torch.bfloat16, False,
+                                                    False) == q_bytes
+    assert lt.lightning_attn_prefill_workspace_size(B, T, Hq, Hkv, 64) == 0      # d = 128 only
+    assert lt.lightning_attn_prefill_workspace_size(B, T, 6, 4, d) == 0          # Hq % Hkv
+    assert lt.lightning_attn_prefill_workspace_size(B, T, Hq, Hkv, d, torch.float32) == 0
+
+
+ATTN_BAD = [
+    ("null_q", dict(q=None), lt.LT_ERR_INVALID_ARG),
+    ("misaligned_v", dict(v=FAKE + 2), lt.LT_ERR_INVALID_ARG),
+    ("null_y", dict(y=None), lt.LT_ERR_INVALID_ARG),
+    ("misaligned_cache", dict(cache=FAKE + 8), lt.LT_ERR_INVALID_ARG),
+    ("zero_T", dict(T=0), lt.LT_ERR_INVALID_ARG),
+    ("heads_not_grouped", dict(Hq=6, Hkv=4), lt.LT_ERR_INVALID_ARG),
+    ("d_64", dict(d=64, stride=64), lt.LT_ERR_UNSUPPORTED),
+    ("fp32", dict(dt=lt.LT_F32), lt.LT_ERR_UNSUPPORTED),
+    ("bad_stride", dict(stride=7), lt.LT_ERR_INVALID_ARG),
+    ("scale_base_one", dict(a=1.0), lt.LT_ERR_INVALID_ARG),
+    ("scale_base_negative", dict(a=-500.0), lt.LT_ERR_INVALID_ARG),
+    ("scale_base_inf", dict(a=float("inf")), lt.LT_ERR_INVALID_ARG),
+    ("eps_nan", dict(eps=float("nan")), lt.LT_ERR_INVALID_ARG),
+    ("pos0_negative", dict(pos0=-1), lt.LT_ERR_INVALID_ARG),
+    ("workspace_missing", dict(ws=None), lt.LT_ERR_WORKSPACE),
+    ("workspace_small", dict(wsb=1024), lt.LT_ERR_WORKSPACE),
+    ("workspace_not_256_aligned", dict(ws=FAKE * 16 + 32), lt.LT_ERR_WORKSPACE),
+    ("events_null_entries", dict(ev=(ct.c_void_p * 2)(None, FAKE)), lt.LT_ERR_INVALID_ARG),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,over,status", ATTN_BAD, ids=[c[0] for c in ATTN_BAD])
+def test_attn_prefill_rejects(name, over, status):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, qw=FAKE, kw=FAKE, ow=None, stride=0, a=500.0,
+             eps=1e-6, pos0=0, y=FAKE, oraw=None, cache=None, B=1, T=256, Hq=4, Hkv=2, d=128,
+             dt=lt.LT_BF16, ws=FAKE * 16, wsb=1 << 40, ev=None, stream=None)
+    a.update(over)
+    st = lt.lib.lightning_attn_prefill(a["q"], a["k"], a["v"], a["g"], a["qw"], a["kw"], a["ow"],
+                                       a["stride"], a["a"], a["eps"], a["pos0"], a["y"],
+                                       a["oraw"], a["cache"], a["B"], a["T"], a["Hq"], a["Hkv"],
+                                       a["d"], a["dt"], a["ws"], a["wsb"], a["ev"], a["stream"])
+    assert st == status

@@ -1,0 +1,128 @@
+"""Parity of the HyPE attention kernels (through the C ABI) with the fp64 oracle.
+
+Small cases compare every element of y and of o (before the output norm) per (b, h) slice,
+across the three workgroup shapes (1, 2 or 4 query heads per key/value head), ragged lengths,
+T = 1, with and without QK-norm and logits scaling, and a nonzero position origin.  The full
+workloads run in the launch configuration the benchmark times and are compared on sampled query
+rows of every head (a query row depends on all earlier keys, which the oracle takes in full).
+
+Tolerances are the mixer's (relative L2 <= 2e-2 for bf16 outputs).  The scores are formed from
+bf16 queries (already scaled by s_t log2(e)/sqrt(d)) and bf16 keys, and P is rounded to bf16
+before P V, which puts o within a few 1e-3 of the exact value.  The key cache written by the
+prefill is the normalised key rounded once to bf16 from fp32: each entry must be within one
+bf16 ulp (2^-7 relative) plus fp32 rounding of the oracle's fp64 value.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as oa
+import synth
+from synth import host_bits, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def gpu_attn(inp, with_cache=True):
+    import long_context_hybrid_amd.lightning as lt
+
+    dev = torch.device("cuda")
+    q, k, v, g = (inp[n].to(dev) for n in ("q", "k", "v", "g"))
+    o_raw = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    cache = torch.empty_like(k) if with_cache else None
+    qw = None if inp["qw"] is None else inp["qw"].to(dev)
+    kw = None if inp["kw"] is None else inp["kw"].to(dev)
+    y = lt.lightning_attn_prefill(q, k, v, g, inp["a"], q_norm_w=qw, k_norm_w=kw,
+                                  rms_eps=inp["eps"], pos0=inp["pos0"], o_raw=o_raw,
+                                  key_cache_out=cache)
+    torch.cuda.synchronize()
+    return dict(y=y.float().cpu(), o=o_raw.cpu(), cache=None if cache is None else cache.float().cpu())
+
+
+def oracle_attn(inp, rows=None):
+    return oa.attn_prefill(*(host_bits(inp[n].cpu()) for n in ("q", "k", "v", "g")),
+                           None if inp["qw"] is None else inp["qw"].cpu().numpy(),
+                           None if inp["kw"] is None else inp["kw"].cpu().numpy(),
+                           None, a=inp["a"], eps=inp["eps"], pos0=inp["pos0"], rows=rows,
+                           want_k_hat=rows is None)
+
+
+def compare(gpu, ref, inp, rows=None, label=""):
+    B, Hq = inp["B"], inp["Hq"]
+    rows = slice(None) if rows is None else torch.as_tensor(rows)
+    worst = dict(y=0.0, o=0.0)
+    for b in range(B):
+        for h in range(Hq):
+            worst["y"] = max(worst["y"], rel_l2(gpu["y"][b, rows, h].numpy(), ref["y"][b, :, h]))
+            worst["o"] = max(worst["o"], rel_l2(gpu["o"][b, rows, h].numpy(), ref["o"][b, :, h]))
+    print(f"[parity] attention {label}: " + " ".join(f"{k}={v:.3e}" for k, v in worst.items()))
+    assert worst["y"] <= TOL and worst["o"] <= TOL, (label, worst)
+    return worst
+
+
+def check_cache(gpu, ref, label):
+    if gpu["cache"] is None:
+        return
+    got = gpu["cache"].numpy().astype(np.float64)
+    exact = ref["k_hat"]
+    err = np.abs(got - exact)
+    bound = 2.0 ** -7 * np.abs(exact) + 2.0 ** -20 * (np.abs(exact) + 1e-30)
+    i = int(np.argmax(err - bound))
+    assert err.flat[i] <= bound.flat[i], (label, got.flat[i], exact.flat[i])
+
+
+SMALL = [
+    # (label, B, T, Hq, Hkv, a, qk_norm, pos0)
+    ("gqa2_ragged", 1, 300, 4, 2, 500.0, True, 0),
+    ("gqa4_two_batches", 2, 1000, 8, 2, 600.0, True, 0),
+    ("mha_short_ragged", 1, 65, 2, 2, 900.0, True, 0),
+    ("gqa2_no_norm_no_scale", 1, 513, 4, 2, 0.0, False, 0),
+    ("gqa8_far_position", 1, 777, 8, 1, 500.0, True, 100000),
+    ("single_token", 3, 1, 4, 2, 500.0, True, 5),
+    ("gqa2_two_blocks_exact", 1, 128, 2, 1, 300.0, True, 0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_attn_prefill_small(case):
+    label, B, T, Hq, Hkv, a, norm, pos0 = case
+    inp = synth.make_custom_attn(B, T, Hq, Hkv, a=a, qk_norm=norm, seed=len(label) * 31 + T,
+                                 pos0=pos0)
+    ref = oracle_attn(inp)
+    gpu = gpu_attn(inp)
+    compare(gpu, ref, inp, label=label)
+    check_cache(gpu, ref, label)
+
+
+def test_attn_prefill_deterministic_and_cache_optional():
+    inp = synth.make_custom_attn(1, 700, 4, 2, seed=77)
+    a = gpu_attn(inp, with_cache=True)
+    b = gpu_attn(inp, with_cache=False)
+    assert torch.equal(a["y"], b["y"]) and torch.equal(a["o"], b["o"])
+
+
+def _sampled_rows(T, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(T, n - 4, replace=False).tolist()) | {0, 1, T // 2, T - 1}
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("spec_name,n_rows", [("attn_qwen17_32k", 96), ("attn_qwen17_512k", 20)])
+@pytest.mark.timeout(600)
+def test_attn_prefill_full_sampled_rows(spec_name, n_rows):
+    spec = synth.WORKLOADS[spec_name]
+    inp = synth.make_attn(spec, device="cuda")
+    gpu = gpu_attn(inp, with_cache=False)
+    rows = _sampled_rows(inp["T"], n_rows, seed=len(spec_name))
+    host = dict(inp, **{n: inp[n].cpu() for n in ("q", "k", "v", "g")},
+                qw=inp["qw"].cpu(), kw=inp["kw"].cpu())
+    ref = oracle_attn(host, rows=rows)
+    compare(gpu, ref, inp, rows=rows, label=f"{spec.name} rows {len(rows)}")
