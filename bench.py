@@ -59,6 +59,7 @@ def parse():
     ap.add_argument("--attn-steps", type=int, default=2)
     ap.add_argument("--attn-warmup", type=int, default=1)
     ap.add_argument("--cpu-attn-rows", type=int, default=32)
+    ap.add_argument("--attn-decode-steps", type=int, default=50)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed runs, copy this many MiB device to device three times "
                          "(a plain copy of known size that calibrates HBM byte counters)")
@@ -377,6 +378,51 @@ def bench_attn(args, torch, lt, synth):
             "prologue_ms": round(ms - main_ms, 3)}
 
 
+def bench_attn_decode(args, torch, lt, synth):
+    """One HyPE attention decode step at B = 1 with 524287 cached tokens (Qwen3-1.7B shape):
+    the step reads the whole 2 GiB key/value cache, which no cache level holds."""
+    spec = synth.ATTN_QWEN17_512K
+    dev = torch.device("cuda:0")
+    Hq, Hkv, d, cap = spec.Hq, spec.Hkv, spec.d, spec.T
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(spec.seed + 100)
+
+    def rnd(*shape):
+        return torch.randn(*shape, generator=gen, device=dev).to(torch.bfloat16)
+
+    q, kn, vn, g = rnd(1, Hq, d), rnd(1, Hkv, d), rnd(1, Hkv, d), rnd(1, Hq, d)
+    kc, vc = rnd(1, cap, Hkv, d), rnd(1, cap, Hkv, d)
+    qw = 0.5 + torch.rand(d, generator=gen, device=dev)
+    kw = 0.5 + torch.rand(d, generator=gen, device=dev)
+    n = cap - 1
+    y = torch.empty_like(q)
+    ws = torch.empty(lt.lightning_attn_decode_workspace_size(1, Hq, Hkv, d, n), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        lt.lightning_attn_decode_step(q, kn, vn, g, kc, vc, [n], spec.a, q_norm_w=qw, k_norm_w=kw,
+                                      y=y, workspace=ws)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.attn_decode_steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(stop) * 1e3 / args.attn_decode_steps
+    alg = 2 * (n + 1) * Hkv * d * 2 + (2 * Hq + 2 * Hkv + Hq) * d * 2
+    gbs = alg / (us * 1e-6) / 1e9
+    del kc, vc
+    return {"workload": "HyPE attention decode step B=1, 524287 cached tokens, Hq=16 Hkv=8 "
+                        "d=128 bf16", "us_per_step": round(us, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "alg_bytes_per_step": alg}}
+
+
 def cpu_baseline_attn(args, torch, synth):
     """The attention oracle on evenly spaced query rows of the 512K workload (all heads): their
     mean cost is the mean over all rows, so rows / time estimates the whole prefill's rate."""
@@ -486,6 +532,10 @@ def main():
         print(f"[bench] attention prefill 512K: warmup {args.attn_warmup}, steps {args.attn_steps}",
               file=sys.stderr, flush=True)
         attn = bench_attn(args, torch, lt, synth)
+        if not args.no_decode:
+            print(f"[bench] attention decode at 512K context: steps {args.attn_decode_steps}",
+                  file=sys.stderr, flush=True)
+            attn["decode"] = bench_attn_decode(args, torch, lt, synth)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

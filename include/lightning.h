@@ -228,6 +228,37 @@ lt_status lightning_attn_prefill(const void* q, const void* k, const void* v, co
                                  int d, int dtype, void* workspace, size_t workspace_bytes,
                                  void* const* main_kernel_events, void* stream);
 
+/*
+ * One HyPE attention decode step (TPOT, Fig. 1 right): one new token per batch row attends to
+ * the row's cache and itself.
+ *   q, gate       : device [B][Hq][d] bf16;  k_new, v_new : device [B][Hkv][d] bf16.
+ *   lengths       : HOST int64 [B], read before the call returns: the number of cached tokens
+ *                   of each row, which is also the new token's (0-based) position, so its
+ *                   logits scale is s = log_a(lengths[b] + a).  0 <= lengths[b] < cache_capacity.
+ *   k_cache, v_cache : device [B][cache_capacity][Hkv][d] bf16; rows 0 .. lengths[b] - 1 hold the
+ *                   earlier tokens' keys (already normalised, as lightning_attn_prefill writes
+ *                   them) and values.  The step writes the new token's key (normalised with
+ *                   k_norm_w when given) and value into row lengths[b]; no other row is written.
+ *   y             : device [B][Hq][d] bf16;  o_raw : device fp32 [B][Hq][d] or NULL.
+ *   workspace     : at least lightning_attn_decode_workspace_size(B, Hq, Hkv, d, dtype,
+ *                   max_b lengths[b]) bytes, 256-byte aligned (per-split partial results).
+ * Other arguments as for lightning_attn_prefill.  Supported: d = 128, bf16, B <= 64,
+ * Hq / Hkv in {1, 2, 4, 8}.  A step after lightning_attn_prefill(T) (cache filled through
+ * key_cache_out and the caller's values) with lengths = T equals row T of the prefill of T + 1
+ * tokens.
+ */
+size_t lightning_attn_decode_workspace_size(int B, int Hq, int Hkv, int d, int dtype,
+                                            int64_t max_length);
+
+lt_status lightning_attn_decode_step(const void* q, const void* k_new, const void* v_new,
+                                     const void* gate, const float* q_norm_w,
+                                     const float* k_norm_w, const float* o_norm_w,
+                                     int norm_w_head_stride, double logit_scale_base,
+                                     double rms_eps, const int64_t* lengths, void* k_cache,
+                                     void* v_cache, int64_t cache_capacity, void* y,
+                                     float* o_raw, int B, int Hq, int Hkv, int d, int dtype,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

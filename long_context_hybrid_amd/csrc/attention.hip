@@ -304,7 +304,285 @@ hipError_t launch_fwd(const AttnParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ---- 3. decode step ----------------------------------------------------------------------------
+// (a) attn_append_kernel writes the new token's key (normalised with key norm weights) and value
+//     into row lengths[b] of the caches;
+// (b) attn_decode_partial_kernel: one workgroup per (b, key/value head, split of
+//     kAttnDecodeChunk keys).  Each 16-lane group streams every 16th key of the split (8
+//     features per lane, 16-byte loads, four keys in flight), forms the scores with packed bf16
+//     dot products and keeps an online softmax for every query head of the group (batched over
+//     the four keys, max raised only past 2^8 headroom); the 16 streams are merged through LDS
+//     into one partial (unnormalised o, max, sum in log2 units) per head and split;
+// (c) attn_decode_combine_kernel: one workgroup per (b, h) merges the splits and applies the
+//     output norm and gate.
+
+__global__ void __launch_bounds__(256) attn_append_kernel(const AttnDecodeParams p) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // b Hkv + kvh
+    if (row >= p.B * p.Hkv) return;
+    const int b = row / p.Hkv, kvh = row - b * p.Hkv;
+    const size_t src = (size_t)row * kD;
+    const size_t dst = (((size_t)b * p.Tmax + p.lengths[b]) * p.Hkv + kvh) * kD;
+    const uint32_t k2 = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.k_new) + src)[lane];
+    float a = bf16_lo(k2), c = bf16_hi(k2);
+    if (p.kw) {
+        const float ss = wave_sum(a * a + c * c);
+        const float rinv = 1.0f / sqrtf(ss * (1.0f / kD) + p.eps);
+        const float* wh = p.kw + (size_t)kvh * p.w_stride;
+        a *= rinv * wh[2 * lane];
+        c *= rinv * wh[2 * lane + 1];
+    }
+    reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.k_cache) + dst)[lane] = pack_bf16x2(a, c);
+    reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.v_cache) + dst)[lane] =
+        reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.v_new) + src)[lane];
+}
+
+__device__ __forceinline__ void widen8(uint4 x, float* f) {
+    f[0] = bf16_lo(x.x); f[1] = bf16_hi(x.x); f[2] = bf16_lo(x.y); f[3] = bf16_hi(x.y);
+    f[4] = bf16_lo(x.z); f[5] = bf16_hi(x.z); f[6] = bf16_lo(x.w); f[7] = bf16_hi(x.w);
+}
+
+template <int GRP>  // query heads per key/value head
+__global__ void __launch_bounds__(256) attn_decode_partial_kernel(const AttnDecodeParams p) {
+    constexpr int U = 4;          // keys in flight per 16-lane group
+    constexpr int NS = 16;        // key streams per workgroup
+    __shared__ float red[NS][GRP][kD + 2];
+    const int tid = threadIdx.x, lane = tid & 63, sl = lane & 15;
+    const int stream_id = tid >> 4;  // 0 .. 15
+    const int split = blockIdx.x % p.n_split;
+    const int row = blockIdx.x / p.n_split;  // b Hkv + kvh
+    const int b = row / p.Hkv, kvh = row - b * p.Hkv;
+    const int64_t n_keys = p.lengths[b] + 1;  // cached keys plus the new one
+    const int64_t k_begin = (int64_t)split * kAttnDecodeChunk;
+    if (k_begin >= n_keys) return;  // whole workgroup: this row has fewer splits
+    const int64_t k_end = min(n_keys, k_begin + kAttnDecodeChunk);
+
+    // this lane's 8 features of every query head of the group, normalised, scaled by
+    // s log2(e) / sqrt(d) and packed to bf16 pairs for v_dot2c_f32_bf16
+    const float pos_scale = p.log_a != 0.0
+        ? (float)(log((double)p.lengths[b] + p.a) / p.log_a) : 1.0f;
+    bf16x2_t qb[GRP][4];
+#pragma unroll
+    for (int hh = 0; hh < GRP; ++hh) {
+        const int h = kvh * GRP + hh;
+        const uint4 x = *reinterpret_cast<const uint4*>(
+            static_cast<const uint16_t*>(p.q) + ((size_t)b * p.Hq + h) * kD + 8 * sl);
+        float qf[8];
+        widen8(x, qf);
+        float scale = pos_scale * kLog2e / sqrtf((float)kD);
+        if (p.qw) {
+            float ss = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = fmaf(qf[e], qf[e], ss);
+            ss = group_sum<16>(ss);
+            scale *= 1.0f / sqrtf(ss * (1.0f / kD) + p.eps);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float w = p.qw ? p.qw[(size_t)h * p.w_stride + 8 * sl + e] : 1.0f;
+            qf[e] *= scale * w;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            qb[hh][e] = __builtin_bit_cast(bf16x2_t, pack_bf16x2(qf[2 * e], qf[2 * e + 1]));
+    }
+
+    // online softmax per head; the max is raised only past 2^8 headroom (p <= 256)
+    float m[GRP], l[GRP], o[GRP][8];
+#pragma unroll
+    for (int hh = 0; hh < GRP; ++hh) {
+        m[hh] = -INFINITY;
+        l[hh] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[hh][e] = 0.0f;
+    }
+    const uint16_t* kc = static_cast<const uint16_t*>(p.k_cache);
+    const uint16_t* vc = static_cast<const uint16_t*>(p.v_cache);
+    const size_t key_stride = (size_t)p.Hkv * kD;
+    const size_t base = ((size_t)b * p.Tmax * p.Hkv + kvh) * kD + 8 * sl;
+    for (int64_t j0 = k_begin + stream_id; j0 < k_end; j0 += NS * U) {
+        uint4 kx[U], vx[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t j = min(j0 + (int64_t)NS * u, k_end - 1);
+            kx[u] = *reinterpret_cast<const uint4*>(kc + base + (size_t)j * key_stride);
+            vx[u] = *reinterpret_cast<const uint4*>(vc + base + (size_t)j * key_stride);
+        }
+        // keys past the split end (the clamped loads) get score -inf; uniform per 16-lane group
+        float sc[U][GRP];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool valid = j0 + (int64_t)NS * u < k_end;
+            const bf16x2_t k2[4] = {__builtin_bit_cast(bf16x2_t, kx[u].x),
+                                    __builtin_bit_cast(bf16x2_t, kx[u].y),
+                                    __builtin_bit_cast(bf16x2_t, kx[u].z),
+                                    __builtin_bit_cast(bf16x2_t, kx[u].w)};
+#pragma unroll
+            for (int hh = 0; hh < GRP; ++hh) {
+                float d2 = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    d2 = __builtin_amdgcn_fdot2_f32_bf16(qb[hh][e], k2[e], d2, false);
+                d2 = group_sum<16>(d2);
+                sc[u][hh] = valid ? d2 : -INFINITY;
+            }
+        }
+        float vf[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u) widen8(vx[u], vf[u]);
+#pragma unroll
+        for (int hh = 0; hh < GRP; ++hh) {
+            float mb = sc[0][hh];
+#pragma unroll
+            for (int u = 1; u < U; ++u) mb = fmaxf(mb, sc[u][hh]);
+            if (mb > m[hh] + kRaise) {  // uniform per 16-lane group
+                const float alpha = __builtin_amdgcn_exp2f(m[hh] - mb);  // 0 at the first key
+                l[hh] *= alpha;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[hh][e] *= alpha;
+                m[hh] = mb;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float pr = __builtin_amdgcn_exp2f(sc[u][hh] - m[hh]);
+                l[hh] += pr;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[hh][e] = fmaf(pr, vf[u][e], o[hh][e]);
+            }
+        }
+    }
+    // merge the 16 streams (a stream that saw no key keeps max -inf and contributes nothing)
+#pragma unroll
+    for (int hh = 0; hh < GRP; ++hh) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[stream_id][hh][8 * sl + e] = o[hh][e];
+        if (sl == 0) {
+            red[stream_id][hh][kD] = m[hh];
+            red[stream_id][hh][kD + 1] = l[hh];
+        }
+    }
+    __syncthreads();
+    for (int hh = tid >> 6; hh < GRP; hh += 4) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) M = fmaxf(M, red[s][hh][kD]);
+        float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const float ms = red[s][hh][kD];
+            const float f = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+            L = fmaf(red[s][hh][kD + 1], f, L);
+            o0 = fmaf(red[s][hh][2 * lane], f, o0);
+            o1 = fmaf(red[s][hh][2 * lane + 1], f, o1);
+        }
+        const int h = kvh * GRP + hh;
+        float* dst = p.part + (((size_t)b * p.Hq + h) * p.n_split + split) * (kD + 2);
+        dst[2 * lane] = o0;
+        dst[2 * lane + 1] = o1;
+        if (lane == 0) {
+            dst[kD] = M;
+            dst[kD + 1] = L;
+        }
+    }
+}
+
+// One 1024-thread workgroup per (b, h): wavefront w folds splits w, w + 16, ... (four at a
+// time), then the 16 wavefronts' partials are merged through LDS.
+__global__ void __launch_bounds__(1024) attn_decode_combine_kernel(const AttnDecodeParams p) {
+    constexpr int NWV = 16;
+    __shared__ float red[NWV][kD + 2];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int row = blockIdx.x;  // b Hq + h
+    const int b = row / p.Hq, h = row - b * p.Hq;
+    const int n_split = (int)((p.lengths[b] + kAttnDecodeChunk) / kAttnDecodeChunk);
+    const float* part = p.part + (size_t)row * p.n_split * (kD + 2);
+    float M = -INFINITY, L = 0.0f, o0 = 0.0f, o1 = 0.0f;
+    for (int s0 = wv; s0 < n_split; s0 += 4 * NWV) {
+        float ms[4], ls[4], a0[4], a1[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int s = s0 + NWV * u;
+            const float* ps = part + (size_t)min(s, n_split - 1) * (kD + 2);
+            ms[u] = s < n_split ? ps[kD] : -INFINITY;
+            ls[u] = ps[kD + 1];
+            a0[u] = ps[2 * lane];
+            a1[u] = ps[2 * lane + 1];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (ms[u] == -INFINITY) continue;
+            const float m_new = fmaxf(M, ms[u]);
+            const float fo = __builtin_amdgcn_exp2f(M - m_new);
+            const float fs = __builtin_amdgcn_exp2f(ms[u] - m_new);
+            L = L * fo + ls[u] * fs;
+            o0 = o0 * fo + a0[u] * fs;
+            o1 = o1 * fo + a1[u] * fs;
+            M = m_new;
+        }
+    }
+    red[wv][2 * lane] = o0;
+    red[wv][2 * lane + 1] = o1;
+    if (lane == 0) {
+        red[wv][kD] = M;
+        red[wv][kD + 1] = L;
+    }
+    __syncthreads();
+    if (wv != 0) return;
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) Mt = fmaxf(Mt, red[w][kD]);
+    float Lt = 0.0f;
+    o0 = o1 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+        const float mw = red[w][kD];
+        const float f = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - Mt);
+        Lt = fmaf(red[w][kD + 1], f, Lt);
+        o0 = fmaf(red[w][2 * lane], f, o0);
+        o1 = fmaf(red[w][2 * lane + 1], f, o1);
+    }
+    const float inv = 1.0f / Lt;
+    o0 *= inv;
+    o1 *= inv;
+    const float ss = wave_sum(o0 * o0 + o1 * o1);
+    const float rinv = 1.0f / sqrtf(ss * (1.0f / kD) + p.eps);
+    const size_t off = (size_t)row * kD + 2 * lane;
+    const uint32_t g2 =
+        reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.g) + off)[0];
+    const float* wo = p.ow ? p.ow + (size_t)h * p.w_stride + 2 * lane : nullptr;
+    const float y0 = o0 * rinv * (wo ? wo[0] : 1.0f) * sigmoidf_(bf16_lo(g2));
+    const float y1 = o1 * rinv * (wo ? wo[1] : 1.0f) * sigmoidf_(bf16_hi(g2));
+    reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.y) + off)[0] = pack_bf16x2(y0, y1);
+    if (p.o_raw) {
+        p.o_raw[off] = o0;
+        p.o_raw[off + 1] = o1;
+    }
+}
+
+template <int GRP>
+hipError_t launch_decode_partial(const AttnDecodeParams& p, hipStream_t stream) {
+    attn_decode_partial_kernel<GRP>
+        <<<dim3((unsigned)(p.B * p.Hkv * p.n_split)), dim3(256), 0, stream>>>(p);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_attn_decode(const AttnDecodeParams& p, hipStream_t stream) {
+    attn_append_kernel<<<dim3((unsigned)((p.B * p.Hkv + 3) / 4)), dim3(256), 0, stream>>>(p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    switch (p.Hq / p.Hkv) {
+        case 1: e = launch_decode_partial<1>(p, stream); break;
+        case 2: e = launch_decode_partial<2>(p, stream); break;
+        case 4: e = launch_decode_partial<4>(p, stream); break;
+        case 8: e = launch_decode_partial<8>(p, stream); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    attn_decode_combine_kernel<<<dim3((unsigned)(p.B * p.Hq)), dim3(1024), 0, stream>>>(p);
+    return hipGetLastError();
+}
 
 int attn_heads_per_workgroup(int Hq, int Hkv) {
     const int grp = Hq / Hkv;
@@ -419,6 +697,65 @@ lt_status lightning_attn_prefill(const void* q, const void* k, const void* v, co
         ev[1] = static_cast<hipEvent_t>(main_kernel_events[1]);
     }
     if (lt::launch_attn_prefill(p, ev, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return LT_ERR_HIP;
+    return LT_OK;
+}
+
+size_t lightning_attn_decode_workspace_size(int B, int Hq, int Hkv, int d, int dtype,
+                                            int64_t max_length) {
+    if (attn_shape(B, 1, Hq, Hkv, d, dtype) != LT_OK || max_length < 0) return 0;
+    const int64_t n_split = max_length / lt::kAttnDecodeChunk + 1;
+    return round256((size_t)B * Hq * n_split * (lt::kAttnHeadDim + 2) * sizeof(float));
+}
+
+lt_status lightning_attn_decode_step(const void* q, const void* k_new, const void* v_new,
+                                     const void* gate, const float* q_norm_w,
+                                     const float* k_norm_w, const float* o_norm_w,
+                                     int norm_w_head_stride, double logit_scale_base,
+                                     double rms_eps, const int64_t* lengths, void* k_cache,
+                                     void* v_cache, int64_t cache_capacity, void* y,
+                                     float* o_raw, int B, int Hq, int Hkv, int d, int dtype,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+    if (!ok_ptr(q) || !ok_ptr(k_new) || !ok_ptr(v_new) || !ok_ptr(gate) || !ok_ptr(y) ||
+        !ok_ptr(k_cache) || !ok_ptr(v_cache) || lengths == nullptr)
+        return LT_ERR_INVALID_ARG;
+    if (!ok_opt(q_norm_w) || !ok_opt(k_norm_w) || !ok_opt(o_norm_w) || !ok_opt(o_raw))
+        return LT_ERR_INVALID_ARG;
+    if (norm_w_head_stride != 0 && norm_w_head_stride != d) return LT_ERR_INVALID_ARG;
+    if (!(logit_scale_base == 0.0 || (logit_scale_base > 1.0 && isfinite(logit_scale_base))))
+        return LT_ERR_INVALID_ARG;
+    if (!(rms_eps >= 0.0) || !isfinite(rms_eps)) return LT_ERR_INVALID_ARG;
+    if (cache_capacity <= 0) return LT_ERR_INVALID_ARG;
+    lt_status st = attn_shape(B, 1, Hq, Hkv, d, dtype);
+    if (st != LT_OK) return st;
+    if (B > lt::kAttnDecodeMaxB || Hq / Hkv > lt::kAttnMaxGroup || (Hq / Hkv & (Hq / Hkv - 1)))
+        return LT_ERR_UNSUPPORTED;
+    int64_t max_len = 0;
+    for (int b = 0; b < B; ++b) {
+        if (lengths[b] < 0 || lengths[b] >= cache_capacity) return LT_ERR_INVALID_ARG;
+        max_len = lengths[b] > max_len ? lengths[b] : max_len;
+    }
+    if ((double)B * cache_capacity * Hkv * d > 4.0e15) return LT_ERR_UNSUPPORTED;
+    const size_t need = lightning_attn_decode_workspace_size(B, Hq, Hkv, d, dtype, max_len);
+    if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+        workspace_bytes < need)
+        return LT_ERR_WORKSPACE;
+
+    lt::AttnDecodeParams p;
+    memset(&p, 0, sizeof p);
+    p.q = q; p.k_new = k_new; p.v_new = v_new; p.g = gate;
+    p.qw = q_norm_w; p.kw = k_norm_w; p.ow = o_norm_w;
+    p.k_cache = k_cache; p.v_cache = v_cache;
+    p.y = y; p.o_raw = o_raw;
+    p.part = static_cast<float*>(workspace);
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.w_stride = norm_w_head_stride;
+    p.n_split = (int)(max_len / lt::kAttnDecodeChunk + 1);
+    p.Tmax = cache_capacity;
+    p.eps = (float)rms_eps;
+    p.a = logit_scale_base;
+    p.log_a = logit_scale_base == 0.0 ? 0.0 : log(logit_scale_base);
+    for (int b = 0; b < B; ++b) p.lengths[b] = lengths[b];
+    if (lt::launch_attn_decode(p, static_cast<hipStream_t>(stream)) != hipSuccess)
         return LT_ERR_HIP;
     return LT_OK;
 }

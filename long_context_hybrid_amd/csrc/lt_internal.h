@@ -96,6 +96,30 @@ struct AttnParams {
     double a, log_a;  // logits scale base and ln(a); log_a == 0: no scale
 };
 
+// HyPE attention decode step (split over key chunks, then combined).
+constexpr int kAttnMaxGroup = 8;       // query heads per key/value head handled by one kernel
+constexpr int kAttnDecodeChunk = 2048; // keys per split of the decode step
+struct AttnDecodeParams {
+    const void* q;        // [B][Hq][d]
+    const void* k_new;    // [B][Hkv][d]
+    const void* v_new;
+    const void* g;        // [B][Hq][d]
+    const float* qw;
+    const float* kw;
+    const float* ow;
+    void* k_cache;        // [B][Tmax][Hkv][d]: row lengths[b] receives the new token's key
+    void* v_cache;
+    void* y;              // [B][Hq][d]
+    float* o_raw;
+    float* part;          // [B][Hq][n_split][d + 2]: per-split o (unnormalised), max, sum
+    int B, Hq, Hkv, w_stride, n_split;
+    int64_t Tmax;
+    float eps;
+    double a, log_a;
+    int64_t lengths[64];  // per batch row: cached tokens = position of the new token
+};
+constexpr int kAttnDecodeMaxB = 64;  // batch rows of one decode call (lengths travel by value)
+
 // events[0] / events[1] (may be null) are recorded just before / after the main chunk kernel.
 hipError_t launch_prefill(const ChunkParams& cp, const ScanParams& sp, int d, int dtype,
                           const hipEvent_t events[2], hipStream_t stream);
@@ -104,6 +128,7 @@ hipError_t launch_state_init(float* state, const float* init, size_t n, hipStrea
 // events[0] / events[1] (may be null) bracket the flash-attention kernel (after the prologue).
 hipError_t launch_attn_prefill(const AttnParams& p, const hipEvent_t events[2], hipStream_t stream);
 int attn_heads_per_workgroup(int Hq, int Hkv);
+hipError_t launch_attn_decode(const AttnDecodeParams& p, hipStream_t stream);
 
 // lightning_prefill / lightning_decode_step with q, k, v and g read at a token (prefill) or
 // sequence (decode) stride of x_stride elements, e.g. column blocks of one fused projection.

@@ -34,6 +34,8 @@ EXPORTS = (
     "lightning_layer_decode_step",
     "lightning_attn_prefill_workspace_size",
     "lightning_attn_prefill",
+    "lightning_attn_decode_workspace_size",
+    "lightning_attn_decode_step",
 )
 
 
@@ -81,6 +83,11 @@ def _load() -> ct.CDLL:
     h.lightning_attn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, f64, f64, i64, vp, vp,
                                          vp, i32, i32, i32, i32, i32, i32, vp, sz, vp, vp]
     h.lightning_attn_prefill.restype = i32
+    h.lightning_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i64]
+    h.lightning_attn_decode_workspace_size.restype = sz
+    h.lightning_attn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, f64, f64, vp, vp,
+                                             vp, i64, vp, vp, i32, i32, i32, i32, i32, vp, sz, vp]
+    h.lightning_attn_decode_step.restype = i32
     return h
 
 
@@ -380,4 +387,47 @@ def lightning_attn_prefill(q, k, v, gate, logit_scale_base, q_norm_w=None, k_nor
                                     float(rms_eps), int(pos0), yp, orp, kcp, B, T, Hq, Hkv, d, dt,
                                     wsp, wbytes, evp, _stream(stream, dev))
     _check(st, "lightning_attn_prefill")
+    return y
+
+
+def lightning_attn_decode_workspace_size(B, Hq, Hkv, d, max_length, dtype=torch.bfloat16) -> int:
+    return int(lib.lightning_attn_decode_workspace_size(B, Hq, Hkv, d, _dtype_code(dtype),
+                                                        int(max_length)))
+
+
+def lightning_attn_decode_step(q, k_new, v_new, gate, k_cache, v_cache, lengths,
+                               logit_scale_base, q_norm_w=None, k_norm_w=None, o_norm_w=None,
+                               rms_eps=1e-6, y=None, o_raw=None, workspace=None, stream=None):
+    """One decode step: q, gate [B, Hq, d], k_new, v_new [B, Hkv, d], caches
+    [B, capacity, Hkv, d] (bf16); ``lengths``: a sequence of B ints (host).  The new token's key
+    and value are written into row lengths[b] of the caches.  Returns ``y``."""
+    B, Hq, d = q.shape
+    Hkv = k_new.shape[1]
+    cap = k_cache.shape[1]
+    dev = q.device
+    dt = _dtype_code(q.dtype)
+    given = [w for w in (q_norm_w, k_norm_w, o_norm_w) if w is not None]
+    stride = 0 if all(w.dim() == 1 for w in given) else d
+    lens = [int(x) for x in lengths]
+    if len(lens) != B:
+        raise ValueError(f"need one length per batch row ({B})")
+    ptrs = [_dev(q, "q", q.dtype, (B, Hq, d), dev), _dev(k_new, "k_new", q.dtype, (B, Hkv, d), dev),
+            _dev(v_new, "v_new", q.dtype, (B, Hkv, d), dev),
+            _dev(gate, "gate", q.dtype, (B, Hq, d), dev)]
+    wq = _opt_weight(q_norm_w, Hq, d, "q_norm_w", dev, stride)
+    wk = _opt_weight(k_norm_w, Hkv, d, "k_norm_w", dev, stride)
+    wo = _opt_weight(o_norm_w, Hq, d, "o_norm_w", dev, stride)
+    kcp = _dev(k_cache, "k_cache", q.dtype, (B, cap, Hkv, d), dev)
+    vcp = _dev(v_cache, "v_cache", q.dtype, (B, cap, Hkv, d), dev)
+    if y is None:
+        y = torch.empty_like(q)
+    yp = _dev(y, "y", q.dtype, q.shape, dev)
+    orp = _dev(o_raw, "o_raw", torch.float32, q.shape, dev)
+    need = lightning_attn_decode_workspace_size(B, Hq, Hkv, d, max(lens) if lens else 0, q.dtype)
+    workspace, wsp, wbytes = _workspace(workspace, need, dev)
+    st = lib.lightning_attn_decode_step(*ptrs, wq, wk, wo, stride, float(logit_scale_base or 0.0),
+                                        float(rms_eps), (ct.c_int64 * B)(*lens), kcp, vcp, cap,
+                                        yp, orp, B, Hq, Hkv, d, dt, wsp, wbytes,
+                                        _stream(stream, dev))
+    _check(st, "lightning_attn_decode_step")
     return y

@@ -126,3 +126,111 @@ def test_attn_prefill_full_sampled_rows(spec_name, n_rows):
                 qw=inp["qw"].cpu(), kw=inp["kw"].cpu())
     ref = oracle_attn(host, rows=rows)
     compare(gpu, ref, inp, rows=rows, label=f"{spec.name} rows {len(rows)}")
+
+
+# ---- decode -----------------------------------------------------------------------------------------
+
+def _decode_inputs(B, Hq, Hkv, cap, lengths, seed, qk_norm=True):
+    gen = torch.Generator().manual_seed(seed)
+    d = 128
+
+    def rnd(*shape):
+        return torch.randn(*shape, generator=gen).to(torch.bfloat16)
+
+    inp = dict(q=rnd(B, Hq, d), k_new=rnd(B, Hkv, d), v_new=rnd(B, Hkv, d), g=rnd(B, Hq, d),
+               k_cache=rnd(B, cap, Hkv, d), v_cache=rnd(B, cap, Hkv, d), lengths=list(lengths),
+               qw=None, kw=None)
+    if qk_norm:
+        inp["qw"] = 0.5 + torch.rand(d, generator=gen)
+        inp["kw"] = 0.5 + torch.rand(d, generator=gen)
+    return inp
+
+
+def _run_decode(inp, a, device_cache=None):
+    import long_context_hybrid_amd.lightning as lt
+
+    dev = torch.device("cuda")
+    kc = inp["k_cache"].to(dev) if device_cache is None else device_cache[0]
+    vc = inp["v_cache"].to(dev) if device_cache is None else device_cache[1]
+    o_raw = torch.empty(inp["q"].shape, dtype=torch.float32, device=dev)
+    y = lt.lightning_attn_decode_step(
+        inp["q"].to(dev), inp["k_new"].to(dev), inp["v_new"].to(dev), inp["g"].to(dev), kc, vc,
+        inp["lengths"], a, q_norm_w=None if inp["qw"] is None else inp["qw"].to(dev),
+        k_norm_w=None if inp["kw"] is None else inp["kw"].to(dev), o_raw=o_raw)
+    torch.cuda.synchronize()
+    return y.float().cpu(), o_raw.cpu(), kc, vc
+
+
+def _check_decode(inp, a, label, y, o, kc, vc):
+    ref = oa.attn_decode_step(*(host_bits(inp[n]) for n in ("q", "k_new", "v_new", "g")),
+                              host_bits(inp["k_cache"]), host_bits(inp["v_cache"]),
+                              np.array(inp["lengths"]),
+                              None if inp["qw"] is None else inp["qw"].numpy(),
+                              None if inp["kw"] is None else inp["kw"].numpy(), a=a)
+    B, Hq = y.shape[:2]
+    worst = dict(y=0.0, o=0.0)
+    for b in range(B):
+        for h in range(Hq):
+            worst["y"] = max(worst["y"], rel_l2(y[b, h].numpy(), ref["y"][b, h]))
+            worst["o"] = max(worst["o"], rel_l2(o[b, h].numpy(), ref["o"][b, h]))
+    print(f"[parity] attention decode {label}: " + " ".join(f"{k}={v:.3e}" for k, v in worst.items()))
+    assert worst["y"] <= TOL and worst["o"] <= TOL, (label, worst)
+    # the new token's row: the normalised key (one bf16 rounding) and the value; nothing else
+    for b, n in enumerate(inp["lengths"]):
+        got_k = kc[b, n].float().cpu().numpy().astype(np.float64)
+        exact = ref["k_hat"][b]
+        assert np.all(np.abs(got_k - exact) <= 2.0 ** -7 * np.abs(exact) + 1e-30), label
+        assert torch.equal(vc[b, n].cpu(), inp["v_new"][b]), label
+        keep = torch.ones(kc.shape[1], dtype=torch.bool)
+        keep[n] = False
+        assert torch.equal(kc[b].cpu()[keep], inp["k_cache"][b][keep]), label
+        assert torch.equal(vc[b].cpu()[keep], inp["v_cache"][b][keep]), label
+
+
+DECODE = [
+    # (label, B, Hq, Hkv, capacity, lengths, a, qk_norm)
+    ("gqa2_mixed_lengths", 4, 4, 2, 6000, (0, 1, 777, 5000), 500.0, True),
+    ("mha", 2, 2, 2, 3000, (2047, 2048), 900.0, True),
+    ("gqa4", 3, 8, 2, 4200, (4097, 0, 31), 600.0, True),
+    ("gqa8_no_norm_no_scale", 2, 8, 1, 2500, (2499, 100), 0.0, False),
+]
+
+
+@pytest.mark.parametrize("case", DECODE, ids=[c[0] for c in DECODE])
+def test_attn_decode_small(case):
+    label, B, Hq, Hkv, cap, lengths, a, norm = case
+    inp = _decode_inputs(B, Hq, Hkv, cap, lengths, seed=len(label), qk_norm=norm)
+    _check_decode(inp, a, label, *_run_decode(inp, a))
+
+
+@pytest.mark.timeout(300)
+def test_attn_decode_full_context():
+    """One token at position 524287 of the Qwen3-1.7B-shaped attention layer (B = 1)."""
+    cap = 524288
+    inp = _decode_inputs(1, 16, 8, cap, (cap - 1,), seed=99)
+    _check_decode(inp, 500.0, "B=1 context 524287", *_run_decode(inp, 500.0))
+
+
+def test_attn_prefill_then_decode():
+    """prefill(T) writing the key cache, then a decode step at position T, equals row T of the
+    oracle's prefill of T + 1 tokens."""
+    import long_context_hybrid_amd.lightning as lt
+
+    T, Hq, Hkv = 700, 4, 2
+    inp = synth.make_custom_attn(1, T + 1, Hq, Hkv, seed=123)
+    ref = oracle_attn(inp, rows=np.array([T]))
+    dev = torch.device("cuda")
+    kc = torch.zeros((1, T + 8, Hkv, 128), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    head = {n: inp[n][:, :T].contiguous().to(dev) for n in ("q", "k", "v", "g")}
+    lt.lightning_attn_prefill(head["q"], head["k"], head["v"], head["g"], inp["a"],
+                              q_norm_w=inp["qw"].to(dev), k_norm_w=inp["kw"].to(dev),
+                              key_cache_out=kc[:, :T])
+    vc[:, :T] = head["v"]
+    y = lt.lightning_attn_decode_step(inp["q"][:, T].to(dev), inp["k"][:, T].to(dev),
+                                      inp["v"][:, T].to(dev), inp["g"][:, T].to(dev), kc, vc, [T],
+                                      inp["a"], q_norm_w=inp["qw"].to(dev),
+                                      k_norm_w=inp["kw"].to(dev))
+    torch.cuda.synchronize()
+    for h in range(Hq):
+        assert rel_l2(y[0, h].float().cpu().numpy(), ref["y"][0, 0, h]) <= TOL
