@@ -94,33 +94,131 @@ __device__ __forceinline__ int key_index(int row, int chunk) {
     return row * kD + 8 * (chunk ^ (row & 15));
 }
 
-// One block of 64 keys and values in flight: thread tid moves 16-byte chunks tid + 256 i
-// (i < 4) of the 64 x 16 chunk grid of each.
-struct KVRegs {
-    uint4 k0, k1, k2, k3, v0, v1, v2, v3;
+// Key and value blocks go from HBM straight into LDS (global_load_lds_dwordx4): one instruction
+// of a wavefront fills 1 KB of LDS, lane l's 16 bytes at offset 16 l, so each lane loads the
+// global 16-byte chunk that the tile's bank swizzle puts in its slot.  Wavefront w fills rows
+// 16 w .. 16 w + 15 of a 64-row block in four instructions of four rows.  The offsets are fixed
+// per lane (only the last block, which may run past the final key, clamps its rows), and the
+// block's first row is a uniform address, so a block costs no vector address arithmetic and no
+// registers while in flight.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glob_void_t;
+
+struct DmaOffsets {
+    uint32_t k0, k1, k2, k3, v0, v1, v2, v3;  // byte offsets of the lane's key / value chunks
 };
 
-__device__ __forceinline__ uint4 ld16(const uint16_t* base, size_t off) {
-    return *reinterpret_cast<const uint4*>(base + off);
+__device__ __forceinline__ DmaOffsets dma_offsets(int wave, int lane, uint32_t row_bytes, int last) {
+    DmaOffsets o;
+    const int slot = lane & 15;
+    uint32_t kk[4], vv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 16 * wave + 4 * i + (lane >> 4);
+        const uint32_t rb = (uint32_t)min(row, last) * row_bytes;
+        kk[i] = rb + 16u * (uint32_t)(slot ^ (row & 15));       // key_index's chunk swizzle
+        vv[i] = rb + 16u * (uint32_t)(slot ^ (4 * (row & 3)));  // nat_index's 32-column XOR
+    }
+    o.k0 = kk[0]; o.k1 = kk[1]; o.k2 = kk[2]; o.k3 = kk[3];
+    o.v0 = vv[0]; o.v1 = vv[1]; o.v2 = vv[2]; o.v3 = vv[3];
+    return o;
 }
 
-__device__ __forceinline__ KVRegs load_kv(const uint16_t* ks, const uint16_t* vs, size_t kv_base,
-                                          size_t kv_row, int key0, int T, int tid) {
-    const int ch = tid & 15, row = tid >> 4;  // chunk tid + 256 i is row + 16 i, chunk ch
-    size_t off[4];
+__device__ __forceinline__ void dma16(const char* src, __bf16* dst_wave) {
+    __builtin_amdgcn_global_load_lds((glob_void_t*)src, (lds_void_t*)dst_wave, 16, 0, 0);
+}
+
+// Rows 16 w .. 16 w + 15 of one key (or value) block into `tile`.
+__device__ __forceinline__ void dma_block(const char* blk, __bf16* tile, int wave, uint32_t o0,
+                                          uint32_t o1, uint32_t o2, uint32_t o3) {
+    __bf16* dst = tile + 16 * kD * wave;
+    dma16(blk + o0, dst);
+    dma16(blk + o1, dst + 4 * kD);
+    dma16(blk + o2, dst + 8 * kD);
+    dma16(blk + o3, dst + 12 * kD);
+}
+
+// Scores of one 64-key block for the wavefront's 32 queries, S^T[j][i] in two 32-key halves, in
+// log2 units; keys after a lane's query (and whole halves after the wavefront's last query) are
+// -inf.
+struct Scores {
+    f32x16 s[2];
+};
+
+__device__ __forceinline__ void block_scores(Scores& sc, const __bf16* kt, const bf16x8 (&qv)[kD / 16],
+                                             int key0, int q0, int qi, int ln, int lh) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        off[i] = kv_base + (size_t)min(key0 + row + 16 * i, T - 1) * kv_row + 8 * ch;
-    KVRegs r;
-    r.k0 = ld16(ks, off[0]); r.k1 = ld16(ks, off[1]); r.k2 = ld16(ks, off[2]); r.k3 = ld16(ks, off[3]);
-    r.v0 = ld16(vs, off[0]); r.v1 = ld16(vs, off[1]); r.v2 = ld16(vs, off[2]); r.v3 = ld16(vs, off[3]);
-    return r;
+    for (int sb = 0; sb < 2; ++sb) {
+        sc.s[sb] = f32x16{};
+        const int kbase = key0 + 32 * sb;
+        if (kbase > q0 + kQW - 1) {  // half entirely in the future of the wavefront
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sc.s[sb][r] = -INFINITY;
+            continue;
+        }
+        const int row = 32 * sb + ln;
+#pragma unroll
+        for (int s = 0; s < kD / 16; ++s) {
+            const bf16x8 kv = *reinterpret_cast<const bf16x8*>(&kt[key_index(row, 2 * s + lh)]);
+            sc.s[sb] = mfma_bf16(kv, qv[s], sc.s[sb]);
+        }
+        if (kbase + 31 > q0) {  // the diagonal: mask keys after the lane's query
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (kbase + acc_row(r, lh) > qi) sc.s[sb][r] = -INFINITY;
+        }
+    }
+}
+
+// Online softmax of one block (log2 units; the running max is raised only past kRaise) and
+// O^T += V^T P^T.
+__device__ __forceinline__ void block_softmax_pv(const Scores& sc, const __bf16* vt,
+                                                 f32x16 (&o)[kD / 32], float& m, float& l,
+                                                 int key0, int q0, int lane) {
+    float mx = sc.s[0][0];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc.s[0][r], sc.s[1][r]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool raise = mx > m + kRaise;
+    if (__builtin_amdgcn_ballot_w64(raise)) {  // wave-uniform: rescale when any lane raises
+        const float m_new = raise ? mx : m;
+        const float alpha = exp2f(m - m_new);  // 0 on the first visible block
+        l *= alpha;
+#pragma unroll
+        for (int c = 0; c < kD / 32; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[c][r] *= alpha;
+        m = m_new;
+    }
+    bf16x8 pb[2][2];  // [half][k-step]
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float pv = __builtin_amdgcn_exp2f(sc.s[sb][r] - m);
+            l += pv;
+            pb[sb][r >> 3][r & 7] = to_bf16(pv);
+        }
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+        if (key0 + 32 * sb > q0 + kQW - 1) continue;
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+            for (int c = 0; c < kD / 32; ++c) {
+                const bf16x8 va = tr_operand<kD>(vt, 32 * sb + 16 * ks2, 32 * c, lane);
+                o[c] = mfma_bf16(va, pb[sb][ks2], o[c]);
+            }
+    }
 }
 
 template <int GW>  // query heads per workgroup
 __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnParams p) {
     constexpr int WPH = kWaves / GW;  // wavefronts per head
     constexpr int BMQ = kQW * WPH;    // queries per workgroup
+    // Keys run one block ahead of values: in the step of block j the wavefronts read the keys
+    // of block j + 1 (the next step's scores) and the values of block j, while the keys of
+    // block j + 2 and the values of block j + 1 are written into the other halves.
     __shared__ alignas(16) __bf16 kt[2][kBN * kD];
     __shared__ alignas(16) __bf16 vt[2][kBN * kD];
 
@@ -148,112 +246,66 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnParams p) {
     const int t_end = min(p.T, t0 + BMQ);             // queries (and keys) the workgroup needs
     const int n_kb = (t_end + kBN - 1) / kBN;
 
-    const uint16_t* qs = static_cast<const uint16_t*>(p.qs);
-    const uint16_t* ks = static_cast<const uint16_t*>(p.ks);
-    const uint16_t* vs = static_cast<const uint16_t*>(p.v);
     const size_t kv_row = (size_t)p.Hkv * kD;  // elements between consecutive keys
     const size_t kv_base = (size_t)b * p.T * kv_row + (size_t)kvh * kD;
+    const char* kbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.ks) + kv_base);
+    const char* vbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.v) + kv_base);
+    const uint32_t row_bytes = (uint32_t)(kv_row * 2);
+    const size_t blk_bytes = (size_t)kBN * row_bytes;
+    const DmaOffsets full = dma_offsets(wave, lane, row_bytes, kBN - 1);
+    auto load_keys = [&](int kb, __bf16* tile) {
+        const DmaOffsets o = kb * kBN + kBN <= p.T ? full
+                                                   : dma_offsets(wave, lane, row_bytes, p.T - 1 - kb * kBN);
+        dma_block(kbase + (size_t)kb * blk_bytes, tile, wave, o.k0, o.k1, o.k2, o.k3);
+    };
+    auto load_values = [&](int kb, __bf16* tile) {
+        const DmaOffsets o = kb * kBN + kBN <= p.T ? full
+                                                   : dma_offsets(wave, lane, row_bytes, p.T - 1 - kb * kBN);
+        dma_block(vbase + (size_t)kb * blk_bytes, tile, wave, o.v0, o.v1, o.v2, o.v3);
+    };
 
     // the wavefront's queries: B operand k = 16 s + 8 lh + e of query qi
     bf16x8 qv[kD / 16];
     {
         const size_t qrow = ((size_t)b * p.T + min(qi, p.T - 1)) * p.Hq + head;
-        const uint16_t* src = qs + qrow * kD + 8 * lh;
+        const uint16_t* src = static_cast<const uint16_t*>(p.qs) + qrow * kD + 8 * lh;
 #pragma unroll
         for (int s = 0; s < kD / 16; ++s) qv[s] = *reinterpret_cast<const bf16x8*>(src + 16 * s);
     }
-
-    auto store_block = [&](const KVRegs& r, int buf) {
-        const int ch = tid & 15, row = tid >> 4;
-        __bf16* kb_ = kt[buf];
-        __bf16* vb_ = vt[buf];
-        *reinterpret_cast<uint4*>(kb_ + key_index(row, ch)) = r.k0;
-        *reinterpret_cast<uint4*>(kb_ + key_index(row + 16, ch)) = r.k1;
-        *reinterpret_cast<uint4*>(kb_ + key_index(row + 32, ch)) = r.k2;
-        *reinterpret_cast<uint4*>(kb_ + key_index(row + 48, ch)) = r.k3;
-        *reinterpret_cast<uint4*>(vb_ + nat_index<kD>(row, 8 * ch)) = r.v0;
-        *reinterpret_cast<uint4*>(vb_ + nat_index<kD>(row + 16, 8 * ch)) = r.v1;
-        *reinterpret_cast<uint4*>(vb_ + nat_index<kD>(row + 32, 8 * ch)) = r.v2;
-        *reinterpret_cast<uint4*>(vb_ + nat_index<kD>(row + 48, 8 * ch)) = r.v3;
-    };
 
     f32x16 o[kD / 32];
 #pragma unroll
     for (int c = 0; c < kD / 32; ++c) o[c] = f32x16{};
     float m = -INFINITY, l = 0.0f;
 
-    KVRegs pre = load_kv(ks, vs, kv_base, kv_row, 0, p.T, tid);
-    store_block(pre, 0);
+    // keys of blocks 0 and 1, values of block 0
+    load_keys(0, kt[0]);
+    load_values(0, vt[0]);
+    if (n_kb > 1) load_keys(1, kt[1]);
+    __builtin_amdgcn_s_waitcnt(0);  // this wavefront's LDS fills have landed
     __syncthreads();
-    for (int kb = 0; kb < n_kb; ++kb) {
-        const int buf = kb & 1;
-        // the next block's loads (clamped at the last key; unused on the final block)
-        pre = load_kv(ks, vs, kv_base, kv_row, min(kb + 1, n_kb - 1) * kBN, p.T, tid);
-        const int key0 = kb * kBN;
-        if (key0 <= q0 + kQW - 1) {  // some key of the block is visible to some query of the wave
-            f32x16 st[2];
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-                st[sb] = f32x16{};
-                const int kbase = key0 + 32 * sb;
-                if (kbase > q0 + kQW - 1) {  // sub-block entirely in the future of the wave
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) st[sb][r] = -INFINITY;
-                    continue;
-                }
-                const int row = 32 * sb + ln;
-#pragma unroll
-                for (int s = 0; s < kD / 16; ++s) {
-                    const bf16x8 kv = *reinterpret_cast<const bf16x8*>(
-                        &kt[buf][key_index(row, 2 * s + lh)]);
-                    st[sb] = mfma_bf16(kv, qv[s], st[sb]);
-                }
-                if (kbase + 31 > q0) {  // the diagonal: mask keys after the lane's query
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (kbase + acc_row(r, lh) > qi) st[sb][r] = -INFINITY;
-                }
-            }
-            // online softmax (log2 units)
-            float mx = st[0][0];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(st[0][r], st[1][r]));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const bool raise = mx > m + kRaise;
-            if (__builtin_amdgcn_ballot_w64(raise)) {  // wave-uniform: rescale when any lane raises
-                const float m_new = raise ? mx : m;
-                const float alpha = exp2f(m - m_new);  // 0 on the first visible block
-                l *= alpha;
-#pragma unroll
-                for (int c = 0; c < kD / 32; ++c)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[c][r] *= alpha;
-                m = m_new;
-            }
-            bf16x8 pb[2][2];  // [sub-block][k-step]
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float pv = __builtin_amdgcn_exp2f(st[sb][r] - m);
-                    l += pv;
-                    pb[sb][r >> 3][r & 7] = to_bf16(pv);
-                }
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-                if (key0 + 32 * sb > q0 + kQW - 1) continue;
-#pragma unroll
-                for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-                    for (int c = 0; c < kD / 32; ++c) {
-                        const bf16x8 va = tr_operand<kD>(vt[buf], 32 * sb + 16 * ks2, 32 * c, lane);
-                        o[c] = mfma_bf16(va, pb[sb][ks2], o[c]);
-                    }
-            }
-        }
-        if (kb + 1 < n_kb) store_block(pre, buf ^ 1);
+    Scores sa, sb;
+    block_scores(sa, kt[0], qv, 0, q0, qi, ln, lh);  // key 0 is visible to every query
+    __syncthreads();  // every wavefront is done with kt[0] before block 2's keys overwrite it
+
+    // one step: softmax and P V of block kb (scores in cur), scores of block kb + 1 into nxt,
+    // while the keys of block kb + 2 and the values of block kb + 1 stream into LDS
+    auto step = [&](int kb, Scores& cur, Scores& nxt) {
+        const bool more_k = kb + 2 < n_kb, more_v = kb + 1 < n_kb;
+        if (more_k) load_keys(kb + 2, kt[kb & 1]);
+        if (more_v) load_values(kb + 1, vt[(kb + 1) & 1]);
+        const int key1 = (kb + 1) * kBN;
+        if (more_v && key1 <= q0 + kQW - 1) block_scores(nxt, kt[(kb + 1) & 1], qv, key1, q0, qi, ln, lh);
+        if (kb * kBN <= q0 + kQW - 1) block_softmax_pv(cur, vt[kb & 1], o, m, l, kb * kBN, q0, lane);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    };
+    int kb = 0;
+    for (; kb + 1 < n_kb; kb += 2) {
+        step(kb, sa, sb);
+        step(kb + 1, sb, sa);
     }
+    if (kb < n_kb) step(kb, sa, sb);
 
     // epilogue: o = O / l, y = RMSNorm(o) w_o sigmoid(g)
     const float lt_ = l + __shfl_xor(l, 32);
