@@ -17,6 +17,8 @@ at the same 512K tokens with per-stage times and the QKVZ GEMM's MFMA roofline, 
 decode step, and the layer oracle timed on a bounded sample.  Under ``attention``: the hybrid's
 HyPE softmax-attention layer (NoPE, s_t = log_a(t + a) logits scale, 16 query / 8 key-value
 heads) at 512K tokens with the flash kernel's MFMA roofline, and its oracle on sampled rows.
+Under ``time_dependent_decay``: the same prefill with a per-token decay alpha_t (the
+data-dependent variant of the same kernels) and its cost relative to the fixed decay.
 """
 from __future__ import annotations
 
@@ -56,6 +58,8 @@ def parse():
     ap.add_argument("--layer-steps", type=int, default=5)
     ap.add_argument("--cpu-layer-tokens", type=int, default=65536)
     ap.add_argument("--no-attn", action="store_true", help="skip the HyPE attention leg")
+    ap.add_argument("--no-time-dep", action="store_true",
+                    help="skip the data-dependent decay variant")
     ap.add_argument("--attn-steps", type=int, default=2)
     ap.add_argument("--attn-warmup", type=int, default=1)
     ap.add_argument("--cpu-attn-rows", type=int, default=32)
@@ -237,6 +241,69 @@ def bench_decode(args, torch, lt, synth):
                          "kernel": "decode_kernel<ModeBF16,128>", "alg_bytes_per_launch": alg,
                          "bytes_per_bh": per_bh},
             "state_buffers": len(states)}
+
+
+def bench_time_dependent(args, torch, lt, synth, fixed):
+    """The same 512K prefill with a data-dependent decay alpha_t (log2 alpha ~ -U(0, 0.05) per
+    token and head) instead of the fixed lambda_h: the time-dependent variant of the kernels, whose
+    cost against the fixed decay is the contrast Fig. 7 draws between mixers.  Also its B = 64
+    decode step."""
+    spec = synth.QWEN17_512K
+    dev = torch.device("cuda:0")
+    inp = fixed["inp"]
+    B, T, H, d = inp["B"], inp["T"], inp["H"], inp["d"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(spec.seed + 7)
+    lg = (-torch.rand((B, T, H), generator=gen, device=dev) * 0.05).float()
+    y = torch.empty_like(inp["q"])
+    s_out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(lt.lightning_prefill_dd_workspace_size(B, T, H, d, spec.dtype), 1),
+                     dtype=torch.uint8, device=dev)
+    call = (inp["q"], inp["k"], inp["v"], inp["g"], inp["qw"], inp["kw"], lg, inp["rope_base"])
+    kw = dict(rms_eps=inp["eps"], state_out=s_out, y=y, workspace=ws)
+    for _ in range(args.warmup):
+        lt.lightning_prefill_dd(*call, **kw)
+    torch.cuda.synchronize()
+    hev = HipEvents()
+    ev = hev.create(2 * args.steps)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        lt.lightning_prefill_dd(*call, **kw, main_kernel_events=(ev[2 * i], ev[2 * i + 1]))
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    main_ms = sum(hev.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for i in range(args.steps)) / args.steps
+    hev.destroy(ev)
+    units = B * H * T
+    alg = units * (5 * d * 2 + 4) + fixed["P"] * B * H * 2 * d * d * 4  # + the per-token decay
+    gbs = alg / (main_ms * 1e-3) / 1e9
+    out = {"workload": spec.name + ", data-dependent decay log2(alpha) ~ -U(0, 0.05)",
+           "ms_per_step": round(ms, 4), "value": round(B * T / (ms * 1e-3), 1),
+           "unit": "tokens/s/layer",
+           "cost_vs_fixed_decay": round(ms / fixed["ms_per_step"], 3),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                        "kernel": "chunk_kernel<ModeBF16,128,false,4,true> (main pass)",
+                        "alg_bytes_per_launch": alg, "launch_ms": round(main_ms, 4)}}
+    if not args.no_decode:
+        dspec = synth.DECODE_B64
+        dinp = synth.make_decode(dspec, device=dev)
+        states = [dinp["state_in"].clone() for _ in range(args.decode_buffers)]
+        dl = (-torch.rand((dinp["B"], dinp["H"]), generator=gen, device=dev) * 0.05).float()
+        yd = torch.empty_like(dinp["q"])
+        a = (dinp["q"], dinp["k"], dinp["v"], dinp["g"], dinp["qw"], dinp["kw"], dl,
+             dinp["rope_base"], dinp["positions"])
+        for i in range(3):
+            lt.lightning_decode_step_dd(*a, states[i % len(states)], y=yd)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(args.decode_steps):
+            lt.lightning_decode_step_dd(*a, states[i % len(states)], y=yd)
+        stop.record()
+        torch.cuda.synchronize()
+        out["decode_us_per_step"] = round(start.elapsed_time(stop) * 1e3 / args.decode_steps, 3)
+    return out
 
 
 def bench_layer(args, torch, lt, synth):
@@ -518,6 +585,10 @@ def main():
     if not args.no_decode:
         print(f"[bench] decode B=64: steps {args.decode_steps}", file=sys.stderr, flush=True)
         dec = bench_decode(args, torch, lt, synth)
+    td = None
+    if not args.no_time_dep:
+        print("[bench] data-dependent decay variant, prefill 512K", file=sys.stderr, flush=True)
+        td = bench_time_dependent(args, torch, lt, synth, pre)
     layer = None
     if not args.no_layer:
         print(f"[bench] layer prefill 512K: warmup {args.warmup}, steps {args.layer_steps}",
@@ -569,6 +640,7 @@ def main():
         "mfma": pre["mfma"],
         "whole_call": pre["whole_call"],
         "decode": dec,
+        "time_dependent_decay": td,
         "layer": layer,
         "attention": attn,
         "cpu_baseline": cpu,

@@ -139,6 +139,37 @@ lt_status lightning_decode_step(const void* q, const void* k, const void* v, con
                                 int dtype, void* stream);
 
 /*
+ * ---- Data-dependent scalar decay (the time-dependent variant of the same kernels) ----
+ *
+ * Eq. 18 with the fixed decay lambda_h replaced by a per-token, per-head alpha_t in (0, 1], the
+ * scalar gate F_t = alpha_t I of Mamba2 (Appendix G, Table 11) whose kernel cost Appendix E.1
+ * (Fig. 7) contrasts with Lightning Attention's:  S_t = alpha_t S_{t-1} + k~_t^T v_t.
+ *   log2_decay : device fp32 [B][T][H] (prefill) or [B][H] (decode): log2(alpha_t), finite and
+ *                <= 0 (not checked: the values are device data).
+ * Everything else as for lightning_prefill / lightning_decode_step (no lambda).  The prefill's
+ * workspace also holds each state-only sub-segment's total log2 decay, so its size query differs.
+ */
+size_t lightning_prefill_dd_workspace_size(int B, int T, int H, int d, int dtype, int chunk,
+                                           int segments);
+
+lt_status lightning_prefill_dd(const void* q, const void* k, const void* v, const void* gate,
+                               const float* q_norm_w, const float* k_norm_w,
+                               const float* o_norm_w, int norm_w_head_stride,
+                               const float* log2_decay, double rope_base, double rms_eps,
+                               int64_t pos0, const float* state_in, float* state_out, void* y,
+                               float* o_raw, int B, int T, int H, int d, int dtype, int chunk,
+                               int segments, void* workspace, size_t workspace_bytes,
+                               void* const* main_kernel_events, void* stream);
+
+lt_status lightning_decode_step_dd(const void* q, const void* k, const void* v,
+                                   const void* gate, const float* q_norm_w,
+                                   const float* k_norm_w, const float* o_norm_w,
+                                   int norm_w_head_stride, const float* log2_decay,
+                                   double rope_base, double rms_eps, const int64_t* positions,
+                                   const float* state_in, float* state_out, void* y,
+                                   float* o_raw, int B, int H, int d, int dtype, void* stream);
+
+/*
  * ---- The whole RNN layer (Appendix A, Eq. 18, with the projections; Section 5.2, Eq. 14) ----
  *
  *   x       : device [B][T][d_model] (prefill) or [B][d_model] (decode) of `dtype`, the layer's

@@ -18,17 +18,20 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
 bool ok_opt(const void* p) { return p == nullptr || aligned16(p); }
 
+// lambda == nullptr is accepted (and nothing read) when the decay is data-dependent.
 lt_status check_common(int H, int d, int dtype, const float* qw, const float* kw,
                        const float* ow, int w_stride, const double* lambda, double rope_base,
-                       double eps) {
+                       double eps, bool time_dep = false) {
     if (dtype != LT_F32 && dtype != LT_BF16) return LT_ERR_INVALID_ARG;
     if (H <= 0 || d <= 0) return LT_ERR_INVALID_ARG;
-    if (!ok_ptr(qw) || !ok_ptr(kw) || !ok_opt(ow) || lambda == nullptr) return LT_ERR_INVALID_ARG;
+    if (!ok_ptr(qw) || !ok_ptr(kw) || !ok_opt(ow)) return LT_ERR_INVALID_ARG;
+    if (!time_dep && lambda == nullptr) return LT_ERR_INVALID_ARG;
     if (w_stride != 0 && w_stride != d) return LT_ERR_INVALID_ARG;
     if (!(rope_base > 0.0) || !isfinite(rope_base)) return LT_ERR_INVALID_ARG;
     if (!(eps >= 0.0) || !isfinite(eps)) return LT_ERR_INVALID_ARG;
-    for (int h = 0; h < H; ++h)
-        if (!(lambda[h] >= 0.0 && lambda[h] <= 1.0)) return LT_ERR_INVALID_ARG;  // also NaN
+    if (!time_dep)
+        for (int h = 0; h < H; ++h)
+            if (!(lambda[h] >= 0.0 && lambda[h] <= 1.0)) return LT_ERR_INVALID_ARG;  // also NaN
     if (d != 64 && d != 128) return LT_ERR_UNSUPPORTED;
     if (H > LT_MAX_HEADS) return LT_ERR_UNSUPPORTED;
     return LT_OK;
@@ -115,6 +118,15 @@ lt_status plan(int B, int T, int H, int d, int dtype, int chunk, int segments, P
 size_t workspace_bytes_for(int B, int H, int d, int P, int sub) {
     return P > 1 ? (size_t)B * H * ((size_t)(P - 1) * sub + 1) * d * d * sizeof(float) : 0;
 }
+// The data-dependent-decay prefill adds each state-only sub-segment's total log2 decay
+// ([B][H][(P - 1) sub] floats) after the state slots, on a 256-byte boundary.
+size_t seg_decay_offset(int B, int H, int d, int P, int sub) {
+    return (workspace_bytes_for(B, H, d, P, sub) + 255) / 256 * 256;
+}
+size_t workspace_bytes_dd(int B, int H, int d, int P, int sub) {
+    return P > 1 ? seg_decay_offset(B, H, d, P, sub) + (size_t)B * H * (P - 1) * sub * sizeof(float)
+                 : 0;
+}
 
 }  // namespace
 
@@ -163,6 +175,13 @@ size_t lightning_prefill_workspace_size(int B, int T, int H, int d, int dtype, i
     return workspace_bytes_for(B, H, d, pl.P, pl.sub);
 }
 
+size_t lightning_prefill_dd_workspace_size(int B, int T, int H, int d, int dtype, int chunk,
+                                           int segments) {
+    Plan pl;
+    if (plan(B, T, H, d, dtype, chunk, segments, &pl) != LT_OK) return 0;
+    return workspace_bytes_dd(B, H, d, pl.P, pl.sub);
+}
+
 }  // extern "C"
 
 namespace lt {
@@ -174,15 +193,17 @@ lt_status prefill_strided(const void* q, const void* k, const void* v, const voi
                           float* state_out, void* y, float* o_raw, int B, int T, int H, int d,
                           int dtype, int chunk, int segments, void* workspace,
                           size_t workspace_bytes, void* const* main_kernel_events, void* stream,
-                          bool validate_only) {
+                          bool validate_only, const float* log2_decay) {
+    const bool td = log2_decay != nullptr;
     if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(gate) || !ok_ptr(y))
         return LT_ERR_INVALID_ARG;
     if (!ok_opt(state_in) || !ok_opt(state_out) || !ok_opt(o_raw)) return LT_ERR_INVALID_ARG;
     if (B <= 0 || T <= 0) return LT_ERR_INVALID_ARG;
     if (pos0 < 0 || pos0 > ((int64_t)1 << 52) - T) return LT_ERR_INVALID_ARG;
     lt_status st = check_common(H, d, dtype, q_norm_w, k_norm_w, o_norm_w, norm_w_head_stride,
-                                lambda, rope_base, rms_eps);
+                                lambda, rope_base, rms_eps, td);
     if (st != LT_OK) return st;
+    if (td && !aligned16(log2_decay)) return LT_ERR_INVALID_ARG;
     if (x_stride < H * d || x_stride % 8 != 0) return LT_ERR_INVALID_ARG;
     if ((double)B * T * x_stride > 9.0e15) return LT_ERR_UNSUPPORTED;
     Plan pl;
@@ -192,7 +213,8 @@ lt_status prefill_strided(const void* q, const void* k, const void* v, const voi
         return LT_ERR_INVALID_ARG;
     if (validate_only) return LT_OK;
     const int P = pl.P;
-    const size_t need = workspace_bytes_for(B, H, d, P, pl.sub);
+    const size_t need =
+        td ? workspace_bytes_dd(B, H, d, P, pl.sub) : workspace_bytes_for(B, H, d, P, pl.sub);
     if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need))
         return LT_ERR_WORKSPACE;
 
@@ -209,7 +231,14 @@ lt_status prefill_strided(const void* q, const void* k, const void* v, const voi
     cp.SM = pl.sub; cp.SL = pl.sub_len; cp.SP = (P - 1) * pl.sub + 1;
     cp.w_stride = norm_w_head_stride;
     cp.eps = (float)rms_eps;
-    for (int h = 0; h < H; ++h) cp.log2_lambda[h] = log2_lambda(lambda[h]);
+    if (td) {
+        cp.log2_decay = log2_decay;
+        if (P > 1)
+            cp.seg_decay = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                    seg_decay_offset(B, H, d, P, pl.sub));
+    } else {
+        for (int h = 0; h < H; ++h) cp.log2_lambda[h] = log2_lambda(lambda[h]);
+    }
     fill_inv_freq_rev(cp.inv_freq_rev, d, rope_base);
 
     lt::ScanParams sp;
@@ -219,9 +248,13 @@ lt_status prefill_strided(const void* q, const void* k, const void* v, const voi
     sp.BH = B * H; sp.H = H; sp.P = cp.SP; sp.sub = pl.sub; sp.dd = d * d;
     // sub-segments 0 .. sub-2 of a segment have sub_len tokens, the last one the rest of L
     const int rest = pl.L - (pl.sub - 1) * pl.sub_len;
-    for (int h = 0; h < H; ++h) {
-        sp.lambda_pow_sub[h] = (float)pow(lambda[h], (double)pl.sub_len);
-        sp.lambda_pow_rest[h] = (float)pow(lambda[h], (double)rest);
+    if (td) {
+        sp.seg_decay = cp.seg_decay;
+    } else {
+        for (int h = 0; h < H; ++h) {
+            sp.lambda_pow_sub[h] = (float)pow(lambda[h], (double)pl.sub_len);
+            sp.lambda_pow_rest[h] = (float)pow(lambda[h], (double)rest);
+        }
     }
 
     hipEvent_t ev[2] = {nullptr, nullptr};
@@ -229,7 +262,8 @@ lt_status prefill_strided(const void* q, const void* k, const void* v, const voi
         ev[0] = static_cast<hipEvent_t>(main_kernel_events[0]);
         ev[1] = static_cast<hipEvent_t>(main_kernel_events[1]);
     }
-    if (lt::launch_prefill(cp, sp, d, dtype, ev, static_cast<hipStream_t>(stream)) != hipSuccess)
+    if (lt::launch_prefill(cp, sp, d, dtype, ev, static_cast<hipStream_t>(stream), td) !=
+        hipSuccess)
         return LT_ERR_HIP;
     return LT_OK;
 }
@@ -239,15 +273,18 @@ lt_status decode_strided(const void* q, const void* k, const void* v, const void
                          const float* o_norm_w, int norm_w_head_stride, const double* lambda,
                          double rope_base, double rms_eps, const int64_t* positions,
                          const float* state_in, float* state_out, void* y, float* o_raw, int B,
-                         int H, int d, int dtype, void* stream, bool validate_only) {
+                         int H, int d, int dtype, void* stream, bool validate_only,
+                         const float* log2_decay) {
+    const bool td = log2_decay != nullptr;
     if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(gate) || !ok_ptr(y))
         return LT_ERR_INVALID_ARG;
     if (!ok_ptr(positions) || !ok_ptr(state_in) || !ok_ptr(state_out) || !ok_opt(o_raw))
         return LT_ERR_INVALID_ARG;
     if (B <= 0) return LT_ERR_INVALID_ARG;
     lt_status st = check_common(H, d, dtype, q_norm_w, k_norm_w, o_norm_w, norm_w_head_stride,
-                                lambda, rope_base, rms_eps);
+                                lambda, rope_base, rms_eps, td);
     if (st != LT_OK) return st;
+    if (td && !aligned16(log2_decay)) return LT_ERR_INVALID_ARG;
     if ((long long)B * H > 0x7fffffffLL) return LT_ERR_UNSUPPORTED;
     if (x_stride < H * d || x_stride % 8 != 0) return LT_ERR_INVALID_ARG;
     if (validate_only) return LT_OK;
@@ -262,10 +299,13 @@ lt_status decode_strided(const void* q, const void* k, const void* v, const void
     dp.B = B; dp.H = H; dp.w_stride = norm_w_head_stride;
     dp.x_stride = x_stride;
     dp.eps = (float)rms_eps;
-    for (int h = 0; h < H; ++h) dp.lambda[h] = (float)lambda[h];
+    if (td)
+        dp.log2_decay = log2_decay;
+    else
+        for (int h = 0; h < H; ++h) dp.lambda[h] = (float)lambda[h];
     fill_inv_freq_rev(dp.inv_freq_rev, d, rope_base);
 
-    if (lt::launch_decode(dp, d, dtype, static_cast<hipStream_t>(stream)) != hipSuccess)
+    if (lt::launch_decode(dp, d, dtype, static_cast<hipStream_t>(stream), td) != hipSuccess)
         return LT_ERR_HIP;
     return LT_OK;
 }
@@ -285,7 +325,8 @@ lt_status lightning_prefill(const void* q, const void* k, const void* v, const v
     return lt::prefill_strided(q, k, v, gate, H * d, q_norm_w, k_norm_w, o_norm_w,
                                norm_w_head_stride, lambda, rope_base, rms_eps, pos0, state_in,
                                state_out, y, o_raw, B, T, H, d, dtype, chunk, segments,
-                               workspace, workspace_bytes, main_kernel_events, stream, false);
+                               workspace, workspace_bytes, main_kernel_events, stream, false,
+                               nullptr);
 }
 
 lt_status lightning_decode_step(const void* q, const void* k, const void* v, const void* gate,
@@ -298,7 +339,38 @@ lt_status lightning_decode_step(const void* q, const void* k, const void* v, con
     if (H <= 0 || d <= 0 || (long long)H * d > 0x7fffffffLL) return LT_ERR_INVALID_ARG;
     return lt::decode_strided(q, k, v, gate, H * d, q_norm_w, k_norm_w, o_norm_w,
                               norm_w_head_stride, lambda, rope_base, rms_eps, positions, state_in,
-                              state_out, y, o_raw, B, H, d, dtype, stream, false);
+                              state_out, y, o_raw, B, H, d, dtype, stream, false, nullptr);
+}
+
+lt_status lightning_prefill_dd(const void* q, const void* k, const void* v, const void* gate,
+                               const float* q_norm_w, const float* k_norm_w,
+                               const float* o_norm_w, int norm_w_head_stride,
+                               const float* log2_decay, double rope_base, double rms_eps,
+                               int64_t pos0, const float* state_in, float* state_out, void* y,
+                               float* o_raw, int B, int T, int H, int d, int dtype, int chunk,
+                               int segments, void* workspace, size_t workspace_bytes,
+                               void* const* main_kernel_events, void* stream) {
+    if (H <= 0 || d <= 0 || (long long)H * d > 0x7fffffffLL) return LT_ERR_INVALID_ARG;
+    if (!ok_ptr(log2_decay)) return LT_ERR_INVALID_ARG;
+    return lt::prefill_strided(q, k, v, gate, H * d, q_norm_w, k_norm_w, o_norm_w,
+                               norm_w_head_stride, nullptr, rope_base, rms_eps, pos0, state_in,
+                               state_out, y, o_raw, B, T, H, d, dtype, chunk, segments,
+                               workspace, workspace_bytes, main_kernel_events, stream, false,
+                               log2_decay);
+}
+
+lt_status lightning_decode_step_dd(const void* q, const void* k, const void* v,
+                                   const void* gate, const float* q_norm_w,
+                                   const float* k_norm_w, const float* o_norm_w,
+                                   int norm_w_head_stride, const float* log2_decay,
+                                   double rope_base, double rms_eps, const int64_t* positions,
+                                   const float* state_in, float* state_out, void* y,
+                                   float* o_raw, int B, int H, int d, int dtype, void* stream) {
+    if (H <= 0 || d <= 0 || (long long)H * d > 0x7fffffffLL) return LT_ERR_INVALID_ARG;
+    if (!ok_ptr(log2_decay)) return LT_ERR_INVALID_ARG;
+    return lt::decode_strided(q, k, v, gate, H * d, q_norm_w, k_norm_w, o_norm_w,
+                              norm_w_head_stride, nullptr, rope_base, rms_eps, positions, state_in,
+                              state_out, y, o_raw, B, H, d, dtype, stream, false, log2_decay);
 }
 
 }  // extern "C"

@@ -32,7 +32,8 @@ __device__ __forceinline__ void store_act(void* base, size_t i, float x) {
         static_cast<float*>(base)[i] = x;
 }
 
-template <class M, int D>
+// kTD: the decay of (b, h) is the data-dependent 2^log2_decay[b][h] instead of lambda_h.
+template <class M, int D, bool kTD>
 __global__ void __launch_bounds__(256) decode_kernel(const DecodeParams p) {
     constexpr int NT = 256;
     constexpr int TPR = D / 4;     // threads per state row (one float4 each)
@@ -86,7 +87,7 @@ __global__ void __launch_bounds__(256) decode_kernel(const DecodeParams p) {
     }
     __syncthreads();
 
-    const float lam = p.lambda[h];
+    const float lam = kTD ? exp2f(p.log2_decay[bh]) : p.lambda[h];
     const float4 v4 = *reinterpret_cast<const float4*>(sv + 4 * c4);
     float4 o4 = make_float4(0.f, 0.f, 0.f, 0.f);
     float* s_out = p.state_out + (size_t)bh * dd;
@@ -145,17 +146,26 @@ __global__ void __launch_bounds__(256) state_init_kernel(float* state, const flo
     }
 }
 
-}  // namespace
-
-hipError_t launch_decode(const DecodeParams& dp, int d, int dtype, hipStream_t stream) {
+template <bool kTD>
+void launch_decode_typed(const DecodeParams& dp, int d, int dtype, hipStream_t stream) {
     const dim3 grid(dp.B * dp.H), block(256);
     if (dtype == LT_BF16) {
-        if (d == 128) decode_kernel<ModeBF16, 128><<<grid, block, 0, stream>>>(dp);
-        else decode_kernel<ModeBF16, 64><<<grid, block, 0, stream>>>(dp);
+        if (d == 128) decode_kernel<ModeBF16, 128, kTD><<<grid, block, 0, stream>>>(dp);
+        else decode_kernel<ModeBF16, 64, kTD><<<grid, block, 0, stream>>>(dp);
     } else {
-        if (d == 128) decode_kernel<ModeF32, 128><<<grid, block, 0, stream>>>(dp);
-        else decode_kernel<ModeF32, 64><<<grid, block, 0, stream>>>(dp);
+        if (d == 128) decode_kernel<ModeF32, 128, kTD><<<grid, block, 0, stream>>>(dp);
+        else decode_kernel<ModeF32, 64, kTD><<<grid, block, 0, stream>>>(dp);
     }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& dp, int d, int dtype, hipStream_t stream,
+                         bool time_dep) {
+    if (time_dep)
+        launch_decode_typed<true>(dp, d, dtype, stream);
+    else
+        launch_decode_typed<false>(dp, d, dtype, stream);
     return hipGetLastError();
 }
 

@@ -42,6 +42,11 @@ struct ChunkParams {
     float eps;
     float log2_lambda[LT_MAX_HEADS];  // log2(lambda_h), -inf for lambda_h = 0
     double inv_freq_rev[64];          // base^(-2i/d) / (2 pi): rotation in revolutions per position
+    // Data-dependent decay (the time-dependent kernels only): log2(alpha_t) per token and head,
+    // [B][T][H] fp32, and the state-only pass's output of each sub-segment's total log2 decay,
+    // [B][H][SP - 1], which the segment scan reads.
+    const float* log2_decay;
+    float* seg_decay;
 };
 
 // Segment-boundary scan: ws[b][h][p] <- S_in(p) from the per-segment end states.
@@ -51,6 +56,7 @@ struct ScanParams {
     int BH, H, P, sub, dd;                // P = slots per (b, h) (sub-segments + 1)
     float lambda_pow_sub[LT_MAX_HEADS];   // lambda_h^len of sub-segments 0 .. sub-2 of a segment
     float lambda_pow_rest[LT_MAX_HEADS];  // lambda_h^len of the last sub-segment of a segment
+    const float* seg_decay;  // time-dependent kernels: [BH][P - 1] log2 decay of each sub-segment
 };
 
 struct DecodeParams {
@@ -71,6 +77,7 @@ struct DecodeParams {
     float eps;
     float lambda[LT_MAX_HEADS];
     double inv_freq_rev[64];
+    const float* log2_decay;  // time-dependent step: [B][H] log2(alpha) of this token
 };
 
 // HyPE attention prefill.  qs / ks are the prologue's outputs (ks == k when the keys are used
@@ -121,9 +128,11 @@ struct AttnDecodeParams {
 constexpr int kAttnDecodeMaxB = 64;  // batch rows of one decode call (lengths travel by value)
 
 // events[0] / events[1] (may be null) are recorded just before / after the main chunk kernel.
+// time_dep: the data-dependent-decay kernels (cp.log2_decay / dp.log2_decay set).
 hipError_t launch_prefill(const ChunkParams& cp, const ScanParams& sp, int d, int dtype,
-                          const hipEvent_t events[2], hipStream_t stream);
-hipError_t launch_decode(const DecodeParams& dp, int d, int dtype, hipStream_t stream);
+                          const hipEvent_t events[2], hipStream_t stream, bool time_dep = false);
+hipError_t launch_decode(const DecodeParams& dp, int d, int dtype, hipStream_t stream,
+                         bool time_dep = false);
 hipError_t launch_state_init(float* state, const float* init, size_t n, hipStream_t stream);
 // events[0] / events[1] (may be null) bracket the flash-attention kernel (after the prologue).
 hipError_t launch_attn_prefill(const AttnParams& p, const hipEvent_t events[2], hipStream_t stream);
@@ -133,6 +142,7 @@ hipError_t launch_attn_decode(const AttnDecodeParams& p, hipStream_t stream);
 // lightning_prefill / lightning_decode_step with q, k, v and g read at a token (prefill) or
 // sequence (decode) stride of x_stride elements, e.g. column blocks of one fused projection.
 // validate_only: run every argument check (but the prefill workspace's) and enqueue nothing.
+// log2_decay (device, [B][T][H] or [B][H]): the data-dependent decay; lambda is then unused.
 lt_status prefill_strided(const void* q, const void* k, const void* v, const void* gate,
                           int x_stride, const float* q_norm_w, const float* k_norm_w,
                           const float* o_norm_w, int norm_w_head_stride, const double* lambda,
@@ -140,13 +150,14 @@ lt_status prefill_strided(const void* q, const void* k, const void* v, const voi
                           float* state_out, void* y, float* o_raw, int B, int T, int H, int d,
                           int dtype, int chunk, int segments, void* workspace,
                           size_t workspace_bytes, void* const* main_kernel_events, void* stream,
-                          bool validate_only);
+                          bool validate_only, const float* log2_decay = nullptr);
 lt_status decode_strided(const void* q, const void* k, const void* v, const void* gate,
                          int x_stride, const float* q_norm_w, const float* k_norm_w,
                          const float* o_norm_w, int norm_w_head_stride, const double* lambda,
                          double rope_base, double rms_eps, const int64_t* positions,
                          const float* state_in, float* state_out, void* y, float* o_raw, int B,
-                         int H, int d, int dtype, void* stream, bool validate_only);
+                         int H, int d, int dtype, void* stream, bool validate_only,
+                         const float* log2_decay = nullptr);
 
 // D[M][N] = A[M][K] W[N][K]^T, row-major, fp32 accumulation, A, W and D in `dtype`.
 // ws: at least gemm_workspace_limit() bytes of device memory, 256-byte aligned.

@@ -126,7 +126,18 @@ struct alignas(16) Tiles {
     alignas(16) E vT[D * G::TS];
 };
 
-template <class M, int D, bool kStateOnly>
+// Time-dependent kernels: per chunk (two in flight), the inclusive prefix sums c_j of the
+// tokens' log2 decays, the state's log2 scale before and after the chunk, the factor a
+// renormalising chunk folds into S, and the renormalisation flag.  The io wavefronts write a
+// chunk's record with its prologue; the math wavefronts read it when they process the chunk.
+template <bool kTD>
+struct DecayRecords {};
+template <>
+struct DecayRecords<true> {
+    alignas(16) float rec[2][36];
+};
+
+template <class M, int D, bool kStateOnly, bool kTD = false>
 struct Smem {
     using G = Cfg<M, D, kStateOnly>;
     Tiles<M, D, kStateOnly> buf[G::NBUF];
@@ -137,6 +148,7 @@ struct Smem {
     // decay of the transposed score tile, [4, 8) lambda^(i+1) of the output rows
     alignas(16) float4 dec[kStateOnly ? 1 : 64 * 8];
     alignas(16) float wo[D];
+    [[no_unique_address]] DecayRecords<kTD> td;
 };
 
 // ---- activation access ------------------------------------------------------------------------
@@ -244,9 +256,10 @@ __device__ __forceinline__ void contract_acc(f32x16& acc, const f32x16& x, const
 }
 
 // One workgroup's pass over its segment.  kPrecise: the state update uses the hi + lo parts of
-// the decayed keys (bf16 mode; fp32 mode is always exact to fp32).
-template <class M, int D, bool kStateOnly, int PF, bool kPrecise>
-__device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kStateOnly>& sm) {
+// the decayed keys (bf16 mode; fp32 mode is always exact to fp32).  kTD: the decay is the
+// data-dependent alpha_t = 2^log2_decay[b][t][h] instead of the fixed lambda_h.
+template <class M, int D, bool kStateOnly, int PF, bool kPrecise, bool kTD>
+__device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kStateOnly, kTD>& sm) {
     using G = Cfg<M, D, kStateOnly>;
     using E = typename G::E;
     using In = typename M::In;
@@ -281,7 +294,7 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
     // pipeline steps: chunk s is written in step s, computed in step s+1 and stored in step s+2;
     // rounded up to a multiple of PF so the io loop can rotate PF register sets without branches
     const int n_steps = (n_chunks + 2 + PF - 1) / PF * PF;
-    const float l2l = p.log2_lambda[h];
+    const float l2l = kTD ? 0.0f : p.log2_lambda[h];
     constexpr bool precise = kPrecise;
     const size_t dd = (size_t)D * D;
     const size_t row_stride = (size_t)p.H * D;  // y / o_raw: elements between consecutive tokens
@@ -329,7 +342,7 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
     if (!kStateOnly)
         for (int i = threadIdx.x; i < D; i += G::NT) sm.wo[i] = p.ow ? p.ow[(size_t)h * p.w_stride + i] : 1.0f;
     fill_rope_table(0, 0);
-    if (!kStateOnly && wave == 0) {
+    if (!kStateOnly && !kTD && wave == 0) {
         // Per lane of a math wavefront: accumulator register r sits at row m = acc_row(r) and
         // column lm.  Score tile (transposed, P^T[j = m][i = lm]): lambda^(i-j) for j <= i, else
         // 0.  Output tile (row i = m): lambda^(i+1).
@@ -450,10 +463,35 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
         const int vsw = L::tsw(32 * w + lm);
         auto compute = [&](int chunk, const Tiles<M, D, kStateOnly>& t, float* o_stage) {
             const int n = min(C, t_end - (t_begin + chunk * C));
-            const bool renorm = chunk % period == 0;
-            // renormalising chunks fold alpha and this chunk's decay into S
-            const float carry = alpha * ((n == C) ? lam_full : pow_lambda(l2l, n));
-            const float alpha_next = pow_lambda(l2l, lazy_exponent(chunk, period, n));
+            bool renorm;
+            float carry, alpha_next;
+            // time-dependent decay factors of the score tile (P^T[j][i]: 2^(c_i - c_j), j <= i)
+            // and of the output rows (row i: 2^c_i, times the state's scale)
+            float dP[16], dO[16];
+            if constexpr (kTD) {
+                const float* rec = sm.td.rec[chunk & 1];
+                renorm = rec[35] != 0.0f;
+                carry = rec[34];
+                alpha = exp2f(rec[32]);
+                alpha_next = exp2f(rec[33]);
+                const float ci = rec[lm];
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const float4 c4 = *reinterpret_cast<const float4*>(rec + 8 * g4 + 4 * lh);
+                    const float cj[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int j = acc_row(4 * g4 + e, lh);
+                        dP[4 * g4 + e] = j <= lm ? __builtin_amdgcn_exp2f(ci - cj[e]) : 0.0f;
+                        dO[4 * g4 + e] = __builtin_amdgcn_exp2f(cj[e]) * alpha;
+                    }
+                }
+            } else {
+                renorm = chunk % period == 0;
+                // renormalising chunks fold alpha and this chunk's decay into S
+                carry = alpha * ((n == C) ? lam_full : pow_lambda(l2l, n));
+                alpha_next = pow_lambda(l2l, lazy_exponent(chunk, period, n));
+            }
             const E* vrow = t.vT + (32 * w + lm) * TS;
             if constexpr (M::kSplit) {
                 // bf16 operands.  With the kpos placement the 16-byte block at 16 s + 8 lh of a
@@ -476,8 +514,13 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
                     }
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        pt[r] *= dec[r];
-                        o[r] *= dec[16 + r] * alpha;
+                        if constexpr (kTD) {
+                            pt[r] *= dP[r];
+                            o[r] *= dO[r];
+                        } else {
+                            pt[r] *= dec[r];
+                            o[r] *= dec[16 + r] * alpha;
+                        }
                     }
                 }
                 // P V and the state update read the same V blocks
@@ -525,13 +568,13 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
                     f32x16 pt = {};
                     contract_rows<D>(pt, t.k + lm * QS, t.q + lm * QS, lh);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) pt[r] *= dec[r];
+                    for (int r = 0; r < 16; ++r) pt[r] *= kTD ? dP[r] : dec[r];
                     // inter-chunk term diag(lambda^(i+1)) Q~ S, B operand from the state registers
                     f32x16 o = {};
 #pragma unroll
                     for (int c = 0; c < NW; ++c) contract_acc(o, S[c], t.q + lm * QS + 32 * c, lh, false);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) o[r] *= dec[16 + r] * alpha;
+                    for (int r = 0; r < 16; ++r) o[r] *= kTD ? dO[r] : dec[16 + r] * alpha;
                     // intra-chunk term P V, A operand from the score registers
                     contract_acc(o, pt, vrow, lh, true, vsw);
 #pragma unroll
@@ -623,6 +666,7 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
 
         struct Regs {
             V4 q[RPT][2], k[RPT][2], v[RPT][2];  // [row s][half]
+            float g;  // time-dependent: log2 decay of row lane % 32
         };
         // (rows past the segment end re-read its last row; the prologue zeroes them)
         // full: the chunk is known to be full and not past the end (no clamping)
@@ -642,6 +686,10 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
                 r.v[s][0] = *reinterpret_cast<const V4*>(gv + cb + o);
                 r.v[s][1] = *reinterpret_cast<const V4*>(gv + cb + o + HALF);
             }
+            if constexpr (kTD) {
+                const int jr = full ? (lane & 31) : min(lane & 31, t_end - 1 - cs);
+                r.g = p.log2_decay[((size_t)b * p.T + cs + jr) * p.H + h];
+            }
         };
 
         // prologue of one chunk: registers -> normalised, rotated, decayed tiles in LDS
@@ -650,10 +698,44 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
 #pragma unroll
         for (int s = 0; s < RPT; ++s) kdec_full[s] = pow_lambda(l2l, C - 1 - (RPT * rg + s));
         const int period = renorm_period(l2l);  // the math wavefronts' lazy state scale
+        // time-dependent: the state's log2 scale (renormalised whenever it would fall below
+        // 2^-20, so S stays within 2^20 of the state) and the pass's total log2 decay
+        float td_log_alpha = 0.0f, td_total = 0.0f;
         // full: the chunk is known to hold C tokens (every row valid, no per-row test)
         auto prologue = [&](int chunk, const Regs& r, Tiles<M, D, kStateOnly>& t, bool full) {
             const int n = full ? C : min(C, t_end - (t_begin + chunk * C));
             const float inv_alpha = pow_lambda(l2l, -lazy_exponent(chunk, period, C));  // full chunks
+            float kdec_td[RPT];  // time-dependent key factors 2^(c_(n-1) - c_j) / alpha_next
+            if constexpr (kTD) {
+                // inclusive prefix sums of the chunk's log2 decays (rows past the end decay by
+                // nothing); both lane halves hold the same 32 values
+                const int jr = lane & 31;
+                float c = (full || jr < n) ? r.g : 0.0f;
+#pragma unroll
+                for (int off = 1; off < 32; off <<= 1) {
+                    const float up = __shfl_up(c, off, 32);
+                    if (jr >= off) c += up;
+                }
+                const float G = __shfl(c, 31, 32);  // the chunk's total
+                const float a_prev = td_log_alpha;
+                const bool renorm = a_prev + G < -20.0f;
+                const float a_next = renorm ? 0.0f : a_prev + G;
+                td_log_alpha = a_next;
+                td_total += G;
+#pragma unroll
+                for (int s = 0; s < RPT; ++s)
+                    kdec_td[s] = __builtin_amdgcn_exp2f(G - __shfl(c, RPT * rg + s, 32) - a_next);
+                if (wave == NW) {  // the first io wavefront publishes the chunk's record
+                    float* rec = sm.td.rec[chunk & 1];
+                    if (lane < 32) rec[lane] = c;
+                    if (lane == 0) {
+                        rec[32] = a_prev;
+                        rec[33] = a_next;
+                        rec[34] = renorm ? __builtin_amdgcn_exp2f(a_prev + G) : 1.0f;
+                        rec[35] = renorm ? 1.0f : 0.0f;
+                    }
+                }
+            }
             const float2* base = sm.rope[chunk & 1];
             float2 b4[4];
 #pragma unroll
@@ -684,8 +766,9 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
                 const float rq0 = fast_rsqrt(ssq * (1.0f / D) + p.eps);
                 const float rk0 = fast_rsqrt(ssk * (1.0f / D) + p.eps) * kscale;
                 // lambda^(n-1-j) / alpha, alpha = lambda^X the state's scale after this chunk
-                const float kdec = full ? kdec_full[s] * inv_alpha
-                                        : pow_lambda(l2l, n - 1 - j - lazy_exponent(chunk, period, n));
+                const float kdec = kTD ? kdec_td[s]
+                                   : full ? kdec_full[s] * inv_alpha
+                                          : pow_lambda(l2l, n - 1 - j - lazy_exponent(chunk, period, n));
                 const float rq = valid ? rq0 : 0.0f;
                 const float rk = valid ? rk0 : 0.0f;
                 const float kds = rk * kdec;  // decayed-key scale
@@ -802,6 +885,9 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
                 __syncthreads();  // math done with chunk s
             }
         }
+        if constexpr (kTD && kStateOnly) {
+            if (it == 0) p.seg_decay[(size_t)bh * (p.SP - 1) + seg] = td_total;
+        }
     }
 }
 
@@ -813,14 +899,18 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
 // and made once, so each pass is branch-free inside its loop.
 // The state-only pass is register-limited so that kStateOnlyBlocksPerCU of its workgroups share
 // a CU (their barriers are independent, so one hides the other's stalls).
-template <class M, int D, bool kStateOnly, int PF>
+template <class M, int D, bool kStateOnly, int PF, bool kTD>
 __global__ void __launch_bounds__((Cfg<M, D, kStateOnly>::NT))
 __attribute__((amdgpu_waves_per_eu(kStateOnly ? kStateOnlyBlocksPerCU * D / 64 : 1)))
 chunk_kernel(const ChunkParams p) {
-    __shared__ Smem<M, D, kStateOnly> sm;
+    __shared__ Smem<M, D, kStateOnly, kTD> sm;
     bool precise = true;
     if constexpr (M::kSplit) {
-        if constexpr (kStateOnly) {
+        if constexpr (kStateOnly && kTD) {
+            // the attenuation down to the final state is data-dependent: keep the low parts
+            // whenever the final state is requested
+            precise = p.state_out != nullptr;
+        } else if constexpr (kStateOnly) {
             // A sub-segment's sum reaches the final state attenuated by lambda^(T - its end).
             // Below 2^-8 the hi-only sum's rounding (about 2^-9 relative) lands under 2^-17 of the
             // final state, so the low parts are needed only for sub-segments closer to the end
@@ -836,15 +926,18 @@ chunk_kernel(const ChunkParams p) {
         }
     }
     if (precise)
-        chunk_pass<M, D, kStateOnly, PF, true>(p, sm);
+        chunk_pass<M, D, kStateOnly, PF, true, kTD>(p, sm);
     else
-        chunk_pass<M, D, kStateOnly, PF, false>(p, sm);
+        chunk_pass<M, D, kStateOnly, PF, false, kTD>(p, sm);
 }
 
 // ws[b][h][j] holds each state-only sub-segment's end state from zero (j < P-1).  The state
 // entering sub-segment j is S_in(0) = state_in, S_in(j+1) = lambda^len(j) S_in(j) + dS(j), where
 // len(j) is the sub-segment's length; it replaces slot j in place for the slots that start a
-// segment (j % sub == 0, including the last slot), the only ones the main pass reads.
+// segment (j % sub == 0, including the last slot), the only ones the main pass reads.  With a
+// time-dependent decay (kTD) lambda^len(j) is 2^seg_decay[b][h][j], the sub-segment's total
+// log2 decay as the state-only pass summed it.
+template <bool kTD>
 __global__ void __launch_bounds__(256) segment_scan_kernel(const ScanParams p) {
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (size_t)p.BH * p.dd) return;
@@ -867,40 +960,52 @@ __global__ void __launch_bounds__(256) segment_scan_kernel(const ScanParams p) {
             if (i >= p.P) break;
             const int k = i % p.sub;
             if (k == 0) w[(size_t)i * p.dd] = s;
-            s = fmaf(k == p.sub - 1 ? lam_rest : lam_sub, s, ds[u]);
+            float lam;
+            if constexpr (kTD)
+                lam = i < p.P - 1 ? exp2f(p.seg_decay[(size_t)bh * (p.P - 1) + i]) : 0.0f;
+            else
+                lam = k == p.sub - 1 ? lam_rest : lam_sub;
+            s = fmaf(lam, s, ds[u]);
         }
     }
 }
 
-template <class M, int D>
+template <class M, int D, bool kTD>
 hipError_t launch_typed(const ChunkParams& cp, const ScanParams& sp, const hipEvent_t ev[2],
                         hipStream_t stream) {
     const int BH = cp.B * cp.H;
     if (cp.P > 1) {
         constexpr int NT = Cfg<M, D, true>::NT;
-        chunk_kernel<M, D, true, kPrefetchStateOnly><<<dim3(BH * (cp.SP - 1)), dim3(NT), 0, stream>>>(cp);
+        chunk_kernel<M, D, true, kPrefetchStateOnly, kTD><<<dim3(BH * (cp.SP - 1)), dim3(NT), 0, stream>>>(cp);
         const size_t n = (size_t)BH * D * D;
-        segment_scan_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(sp);
+        segment_scan_kernel<kTD><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(sp);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (ev[0] && (err = hipEventRecord(ev[0], stream)) != hipSuccess) return err;
-    chunk_kernel<M, D, false, kPrefetchMain><<<dim3(BH * cp.P), dim3(Cfg<M, D, false>::NT), 0, stream>>>(cp);
+    chunk_kernel<M, D, false, kPrefetchMain, kTD><<<dim3(BH * cp.P), dim3(Cfg<M, D, false>::NT), 0, stream>>>(cp);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev[1] && (err = hipEventRecord(ev[1], stream)) != hipSuccess) return err;
     return hipSuccess;
 }
 
+template <bool kTD>
+hipError_t launch_mode(const ChunkParams& cp, const ScanParams& sp, int d, int dtype,
+                       const hipEvent_t ev[2], hipStream_t stream) {
+    if (dtype == LT_BF16) {
+        if (d == 128) return launch_typed<ModeBF16, 128, kTD>(cp, sp, ev, stream);
+        return launch_typed<ModeBF16, 64, kTD>(cp, sp, ev, stream);
+    }
+    if (d == 128) return launch_typed<ModeF32, 128, kTD>(cp, sp, ev, stream);
+    return launch_typed<ModeF32, 64, kTD>(cp, sp, ev, stream);
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const ChunkParams& cp, const ScanParams& sp, int d, int dtype,
-                          const hipEvent_t ev[2], hipStream_t stream) {
-    if (dtype == LT_BF16) {
-        if (d == 128) return launch_typed<ModeBF16, 128>(cp, sp, ev, stream);
-        return launch_typed<ModeBF16, 64>(cp, sp, ev, stream);
-    }
-    if (d == 128) return launch_typed<ModeF32, 128>(cp, sp, ev, stream);
-    return launch_typed<ModeF32, 64>(cp, sp, ev, stream);
+                          const hipEvent_t ev[2], hipStream_t stream, bool time_dep) {
+    return time_dep ? launch_mode<true>(cp, sp, d, dtype, ev, stream)
+                    : launch_mode<false>(cp, sp, d, dtype, ev, stream);
 }
 
 }  // namespace lt

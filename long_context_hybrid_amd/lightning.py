@@ -28,6 +28,9 @@ EXPORTS = (
     "lightning_prefill_workspace_size",
     "lightning_prefill",
     "lightning_decode_step",
+    "lightning_prefill_dd_workspace_size",
+    "lightning_prefill_dd",
+    "lightning_decode_step_dd",
     "lightning_layer_prefill_workspace_size",
     "lightning_layer_prefill",
     "lightning_layer_decode_workspace_size",
@@ -67,6 +70,14 @@ def _load() -> ct.CDLL:
     h.lightning_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, f64, f64, vp, vp,
                                         vp, vp, vp, i32, i32, i32, i32, vp]
     h.lightning_decode_step.restype = i32
+    h.lightning_prefill_dd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    h.lightning_prefill_dd_workspace_size.restype = sz
+    h.lightning_prefill_dd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, f64, f64, i64, vp, vp,
+                                       vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp, vp]
+    h.lightning_prefill_dd.restype = i32
+    h.lightning_decode_step_dd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, f64, f64, vp, vp,
+                                           vp, vp, vp, i32, i32, i32, i32, vp]
+    h.lightning_decode_step_dd.restype = i32
     h.lightning_layer_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
     h.lightning_layer_prefill_workspace_size.restype = sz
     h.lightning_layer_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, f64, f64, i64, vp, vp,
@@ -430,4 +441,74 @@ def lightning_attn_decode_step(q, k_new, v_new, gate, k_cache, v_cache, lengths,
                                         yp, orp, B, Hq, Hkv, d, dt, wsp, wbytes,
                                         _stream(stream, dev))
     _check(st, "lightning_attn_decode_step")
+    return y
+
+
+# ---- data-dependent scalar decay ------------------------------------------------------------------
+
+def lightning_prefill_dd_workspace_size(B, T, H, d, dtype=torch.bfloat16, chunk=0,
+                                        segments=0) -> int:
+    return int(lib.lightning_prefill_dd_workspace_size(B, T, H, d, _dtype_code(dtype), chunk,
+                                                       segments))
+
+
+def lightning_prefill_dd(q, k, v, gate, q_norm_w, k_norm_w, log2_decay, rope_base, rms_eps=1e-6,
+                         pos0=0, state_in=None, state_out=None, y=None, o_raw=None,
+                         o_norm_w=None, chunk=0, segments=0, workspace=None,
+                         main_kernel_events=None, stream=None):
+    """lightning_prefill with a per-token decay: ``log2_decay`` fp32 [B, T, H] (log2 alpha_t)."""
+    B, T, H, d = q.shape
+    dev = q.device
+    dt = _dtype_code(q.dtype)
+    act = dict(dtype=q.dtype, shape=q.shape, device=dev)
+    ptrs = [_dev(t, n, **act) for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"))]
+    (qwp, kwp, owp), stride = _norm_weights(q_norm_w, k_norm_w, o_norm_w, H, d, dev)
+    lgp = _dev(log2_decay, "log2_decay", torch.float32, (B, T, H), dev)
+    if y is None:
+        y = torch.empty_like(q)
+    sshape = (B, H, d, d)
+    need = lightning_prefill_dd_workspace_size(B, T, H, d, q.dtype, chunk, segments)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsp = _dev(workspace, "workspace", None, None, dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    evp = None
+    if main_kernel_events is not None:
+        evp = (ct.c_void_p * 2)(*(ct.c_void_p(int(e)) for e in main_kernel_events))
+    st = lib.lightning_prefill_dd(*ptrs, qwp, kwp, owp, stride, lgp, float(rope_base),
+                                  float(rms_eps), int(pos0),
+                                  _dev(state_in, "state_in", torch.float32, sshape, dev),
+                                  _dev(state_out, "state_out", torch.float32, sshape, dev),
+                                  _dev(y, "y", **act), _dev(o_raw, "o_raw", torch.float32, q.shape, dev),
+                                  B, T, H, d, dt, int(chunk), int(segments), wsp, wbytes, evp,
+                                  _stream(stream, dev))
+    _check(st, "lightning_prefill_dd")
+    return y
+
+
+def lightning_decode_step_dd(q, k, v, gate, q_norm_w, k_norm_w, log2_decay, rope_base, positions,
+                             state_in, state_out=None, rms_eps=1e-6, y=None, o_raw=None,
+                             o_norm_w=None, stream=None):
+    """lightning_decode_step with a per-token decay: ``log2_decay`` fp32 [B, H]."""
+    B, H, d = q.shape
+    dev = q.device
+    dt = _dtype_code(q.dtype)
+    act = dict(dtype=q.dtype, shape=q.shape, device=dev)
+    ptrs = [_dev(t, n, **act) for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"))]
+    (qwp, kwp, owp), stride = _norm_weights(q_norm_w, k_norm_w, o_norm_w, H, d, dev)
+    if y is None:
+        y = torch.empty_like(q)
+    if state_out is None:
+        state_out = state_in
+    sshape = (B, H, d, d)
+    st = lib.lightning_decode_step_dd(*ptrs, qwp, kwp, owp, stride,
+                                      _dev(log2_decay, "log2_decay", torch.float32, (B, H), dev),
+                                      float(rope_base), float(rms_eps),
+                                      _dev(positions, "positions", torch.int64, (B,), dev),
+                                      _dev(state_in, "state_in", torch.float32, sshape, dev),
+                                      _dev(state_out, "state_out", torch.float32, sshape, dev),
+                                      _dev(y, "y", **act),
+                                      _dev(o_raw, "o_raw", torch.float32, q.shape, dev), B, H, d, dt,
+                                      _stream(stream, dev))
+    _check(st, "lightning_decode_step_dd")
     return y

@@ -352,3 +352,36 @@ def test_attn_prefill_rejects(name, over, status):
                                        a["oraw"], a["cache"], a["B"], a["T"], a["Hq"], a["Hkv"],
                                        a["d"], a["dt"], a["ws"], a["wsb"], a["ev"], a["stream"])
     assert st == status
+
+
+# ---- data-dependent decay -------------------------------------------------------------------------
+
+def test_dd_workspace_adds_subsegment_decays():
+    B, T, H, d = 1, 524288, 16, 128
+    base = lt.lightning_prefill_workspace_size(B, T, H, d)
+    _, P, _ = lt.lightning_prefill_plan(B, T, H, d)
+    slots = base // (B * H * d * d * 4)  # (P - 1) sub + 1 state slots per (b, h)
+    expect = (base + 255) // 256 * 256 + B * H * (slots - 1) * 4
+    assert lt.lightning_prefill_dd_workspace_size(B, T, H, d) == expect
+    assert lt.lightning_prefill_dd_workspace_size(1, 200, 2, 128) == 0  # one segment
+
+
+@no_gpu
+@pytest.mark.parametrize("name,over,status", [
+    ("null_decay", dict(dec=None), lt.LT_ERR_INVALID_ARG),
+    ("misaligned_decay", dict(dec=FAKE + 4), lt.LT_ERR_INVALID_ARG),
+    ("null_q", dict(q=None), lt.LT_ERR_INVALID_ARG),
+    ("d_96", dict(d=96, stride=96), lt.LT_ERR_UNSUPPORTED),
+    ("workspace_missing", dict(T=524288, H=16), lt.LT_ERR_WORKSPACE),
+], ids=lambda x: x if isinstance(x, str) else "")
+def test_prefill_dd_rejects(name, over, status):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, qw=FAKE, kw=FAKE, ow=None, stride=128, dec=FAKE,
+             base=1e6, eps=1e-6, pos0=0, sin=None, sout=None, y=FAKE, oraw=None, B=1, T=256, H=2,
+             d=128, dt=lt.LT_BF16, chunk=0, seg=0, ws=None, wsb=0, ev=None, stream=None)
+    a.update(over)
+    st = lt.lib.lightning_prefill_dd(a["q"], a["k"], a["v"], a["g"], a["qw"], a["kw"], a["ow"],
+                                     a["stride"], a["dec"], a["base"], a["eps"], a["pos0"],
+                                     a["sin"], a["sout"], a["y"], a["oraw"], a["B"], a["T"], a["H"],
+                                     a["d"], a["dt"], a["chunk"], a["seg"], a["ws"], a["wsb"],
+                                     a["ev"], a["stream"])
+    assert st == status
