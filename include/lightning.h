@@ -170,6 +170,46 @@ lt_status lightning_decode_step_dd(const void* q, const void* k, const void* v,
                                    float* o_raw, int B, int H, int d, int dtype, void* stream);
 
 /*
+ * ---- Backward of the prefill (the gradients that HALO's training stages need) ----
+ *
+ * The pages train the RNN layers through the mixer (Section 4.2, Eq. 7; Sections 4.4-4.5) and
+ * print no backward pass; this is the derivative of the forward above.  For the loss
+ * L = sum(dy * y) + sum(d_state_out * state_out) of one lightning_prefill call (same inputs):
+ *   dq, dk, dv, dgate : device [B][T][H][d] of `dtype` (written): dL/dq, dL/dk, dL/dv, dL/dgate.
+ *   d_state_in   : device fp32 [B][H][d][d] (written) dL/dstate_in, or NULL (not computed).
+ *   d_q_norm_w, d_k_norm_w, d_o_norm_w : device fp32 with the weights' shape ([H][d], or [d] when
+ *                  norm_w_head_stride == 0), written with dL/dw; each may be NULL.
+ *   dy           : device [B][T][H][d] of `dtype`, dL/dy.
+ *   d_state_out  : device fp32 [B][H][d][d] dL/dstate_out, or NULL for zeros.
+ *   segments     : sequence segments per (b, h) (0 = automatic).  The gradients of a segment
+ *                  need the forward state at its start and the state gradient at its end; both
+ *                  are recomputed (a state-only pass forward, a scan of per-segment gradient sums
+ *                  backward), so nothing from the forward call is kept.
+ *   workspace    : device scratch of lightning_prefill_backward_workspace_size(...) bytes; it
+ *                  holds, among others, dL/do (bf16, the size of one activation tensor).
+ *   kernel_events: NULL, or four hipEvent_t recorded around the forward-in-time sweep (dq, dgate)
+ *                  ([0], [1]) and the backward-in-time sweep (dk, dv) ([2], [3]).
+ * Other arguments as for lightning_prefill.  Outputs may not overlap inputs or each other.
+ * Supported: dtype LT_BF16, d = 128 (LT_ERR_UNSUPPORTED otherwise).  Chaining: the backward of
+ * prefill(T1) then prefill(T2, state_in = its state_out) is the backward of the second call, whose
+ * d_state_in is the first call's d_state_out.
+ */
+size_t lightning_prefill_backward_workspace_size(int B, int T, int H, int d, int dtype,
+                                                 int segments);
+
+lt_status lightning_prefill_backward(const void* q, const void* k, const void* v, const void* gate,
+                                     const float* q_norm_w, const float* k_norm_w,
+                                     const float* o_norm_w, int norm_w_head_stride,
+                                     const double* lambda, double rope_base, double rms_eps,
+                                     int64_t pos0, const float* state_in, const void* dy,
+                                     const float* d_state_out, void* dq, void* dk, void* dv,
+                                     void* dgate, float* d_state_in, float* d_q_norm_w,
+                                     float* d_k_norm_w, float* d_o_norm_w, int B, int T, int H,
+                                     int d, int dtype, int segments, void* workspace,
+                                     size_t workspace_bytes, void* const* kernel_events,
+                                     void* stream);
+
+/*
  * ---- The whole RNN layer (Appendix A, Eq. 18, with the projections; Section 5.2, Eq. 14) ----
  *
  *   x       : device [B][T][d_model] (prefill) or [B][d_model] (decode) of `dtype`, the layer's

@@ -55,6 +55,26 @@ struct Plan {
     int sub, sub_len;  // state-only sub-segments per segment, tokens per sub-segment
 };
 
+// The state-only pass's split of segments 0 .. P-2 (of cps chunks each) into sub-segments: among
+// splits that keep kMinChunksPerSegment chunks per sub-segment and leave the last one non-empty,
+// the one with the fewest chunks per workgroup slot, counting kStateOnlyBlocksPerCU slots per CU
+// (fewer sub-segments on a tie).
+void choose_sub(long long bh, long long P, long long cps, long long* sub, long long* sub_chunks) {
+    *sub = 1;
+    *sub_chunks = cps;
+    if (P <= 1) return;
+    const long long slots = (long long)lt::kStateOnlyBlocksPerCU * lt::kNumCUs;
+    const long long most = (slots + bh * (P - 1) - 1) / (bh * (P - 1));
+    long long best_cost = -1;
+    for (long long s = 1; s <= most; ++s) {
+        const long long sc = (cps + s - 1) / s;
+        if (s > 1 && (sc < lt::kMinChunksPerSegment || cps - (s - 1) * sc < 1)) continue;
+        const long long rounds = (bh * (P - 1) * s + slots - 1) / slots;
+        const long long cost = rounds * sc;
+        if (best_cost < 0 || cost < best_cost) { best_cost = cost; *sub = s; *sub_chunks = sc; }
+    }
+}
+
 lt_status plan(int B, int T, int H, int d, int dtype, int chunk, int segments, Plan* out) {
     if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || segments < 0 || chunk < 0) return LT_ERR_INVALID_ARG;
     if (dtype != LT_F32 && dtype != LT_BF16) return LT_ERR_INVALID_ARG;
@@ -89,21 +109,7 @@ lt_status plan(int B, int T, int H, int d, int dtype, int chunk, int segments, P
     }
     P = (n_chunks + cps - 1) / cps;  // every segment non-empty
     long long sub = 1, sub_chunks = cps;
-    if (P > 1) {
-        // Among splits that keep kMinChunksPerSegment chunks per sub-segment and leave the last
-        // one non-empty, take the one with the fewest chunks per workgroup slot, counting
-        // kStateOnlyBlocksPerCU slots per CU (fewer sub-segments on a tie).
-        const long long slots = (long long)lt::kStateOnlyBlocksPerCU * lt::kNumCUs;
-        const long long most = (slots + bh * (P - 1) - 1) / (bh * (P - 1));
-        long long best_cost = -1;
-        for (long long s = 1; s <= most; ++s) {
-            const long long sc = (cps + s - 1) / s;
-            if (s > 1 && (sc < lt::kMinChunksPerSegment || cps - (s - 1) * sc < 1)) continue;
-            const long long rounds = (bh * (P - 1) * s + slots - 1) / slots;
-            const long long cost = rounds * sc;
-            if (best_cost < 0 || cost < best_cost) { best_cost = cost; sub = s; sub_chunks = sc; }
-        }
-    }
+    choose_sub(bh, P, cps, &sub, &sub_chunks);
     if (bh * ((P - 1) * sub + 1) > 0x7fffffffLL) return LT_ERR_UNSUPPORTED;
     out->C = C;
     out->P = (int)P;
@@ -126,6 +132,57 @@ size_t seg_decay_offset(int B, int H, int d, int P, int sub) {
 size_t workspace_bytes_dd(int B, int H, int d, int P, int sub) {
     return P > 1 ? seg_decay_offset(B, H, d, P, sub) + (size_t)B * H * (P - 1) * sub * sizeof(float)
                  : 0;
+}
+
+// Backward: P segments per (b, h), one workgroup each, sized so that B H P fills the CUs once
+// (each workgroup holds a whole CU's LDS); every segment keeps kMinChunksPerSegment chunks.
+Plan bwd_plan(int B, int T, int H, int segments) {
+    const int C = lt::kChunk;
+    const long long n_chunks = ((long long)T + C - 1) / C;
+    const long long bh = (long long)B * H;
+    long long P = segments;
+    if (P == 0) {
+        P = (lt::kNumCUs + bh - 1) / bh;
+        const long long cap = n_chunks / lt::kMinChunksPerSegment;
+        if (P > cap) P = cap;
+        if (P < 1) P = 1;
+    }
+    if (P > n_chunks) P = n_chunks;
+    const long long cps = (n_chunks + P - 1) / P;
+    P = (n_chunks + cps - 1) / cps;
+    long long sub, sub_chunks;
+    choose_sub(bh, P, cps, &sub, &sub_chunks);
+    Plan pl;
+    pl.C = C;
+    pl.P = (int)P;
+    pl.L = (int)(cps * C);
+    pl.sub = (int)sub;
+    pl.sub_len = (int)(sub_chunks * C);
+    return pl;
+}
+
+lt_status bwd_check_shape(int B, int T, int H, int d, int dtype, int segments) {
+    if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || segments < 0) return LT_ERR_INVALID_ARG;
+    if (dtype != LT_F32 && dtype != LT_BF16) return LT_ERR_INVALID_ARG;
+    if (dtype != LT_BF16 || d != 128 || H > LT_MAX_HEADS) return LT_ERR_UNSUPPORTED;
+    if ((long long)B * H * (T / lt::kChunk + 1) > 0x7fffffffLL) return LT_ERR_UNSUPPORTED;
+    return LT_OK;
+}
+
+// Backward workspace: forward entry states (P > 1) | per-segment state gradients | do (bf16,
+// the activations' layout) | norm-weight partial sums; each part on a 256-byte boundary.
+struct BwdLayout {
+    size_t seg_grad, d_o, wgrad, total;
+};
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+BwdLayout bwd_layout(int B, int T, int H, int d, const Plan& pl) {
+    const size_t bh = (size_t)B * H;
+    BwdLayout l;
+    l.seg_grad = align256(workspace_bytes_for(B, H, d, pl.P, pl.sub));
+    l.d_o = align256(l.seg_grad + bh * pl.P * d * d * sizeof(float));
+    l.wgrad = align256(l.d_o + (size_t)B * T * H * d * sizeof(uint16_t));
+    l.total = l.wgrad + 3 * bh * pl.P * d * sizeof(float);
+    return l;
 }
 
 }  // namespace
@@ -180,6 +237,101 @@ size_t lightning_prefill_dd_workspace_size(int B, int T, int H, int d, int dtype
     Plan pl;
     if (plan(B, T, H, d, dtype, chunk, segments, &pl) != LT_OK) return 0;
     return workspace_bytes_dd(B, H, d, pl.P, pl.sub);
+}
+
+size_t lightning_prefill_backward_workspace_size(int B, int T, int H, int d, int dtype,
+                                                 int segments) {
+    if (bwd_check_shape(B, T, H, d, dtype, segments) != LT_OK) return 0;
+    return bwd_layout(B, T, H, d, bwd_plan(B, T, H, segments)).total;
+}
+
+lt_status lightning_prefill_backward(const void* q, const void* k, const void* v, const void* gate,
+                                     const float* q_norm_w, const float* k_norm_w,
+                                     const float* o_norm_w, int norm_w_head_stride,
+                                     const double* lambda, double rope_base, double rms_eps,
+                                     int64_t pos0, const float* state_in, const void* dy,
+                                     const float* d_state_out, void* dq, void* dk, void* dv,
+                                     void* dgate, float* d_state_in, float* d_q_norm_w,
+                                     float* d_k_norm_w, float* d_o_norm_w, int B, int T, int H,
+                                     int d, int dtype, int segments, void* workspace,
+                                     size_t workspace_bytes, void* const* kernel_events,
+                                     void* stream) {
+    if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(gate) || !ok_ptr(dy))
+        return LT_ERR_INVALID_ARG;
+    if (!ok_ptr(dq) || !ok_ptr(dk) || !ok_ptr(dv) || !ok_ptr(dgate)) return LT_ERR_INVALID_ARG;
+    if (!ok_opt(state_in) || !ok_opt(d_state_out) || !ok_opt(d_state_in)) return LT_ERR_INVALID_ARG;
+    if (!ok_opt(d_q_norm_w) || !ok_opt(d_k_norm_w) || !ok_opt(d_o_norm_w)) return LT_ERR_INVALID_ARG;
+    if (pos0 < 0 || pos0 > ((int64_t)1 << 52) - T) return LT_ERR_INVALID_ARG;
+    lt_status st = check_common(H, d, dtype, q_norm_w, k_norm_w, o_norm_w, norm_w_head_stride,
+                                lambda, rope_base, rms_eps);
+    if (st != LT_OK) return st;
+    if ((st = bwd_check_shape(B, T, H, d, dtype, segments)) != LT_OK) return st;
+    if (kernel_events && (!kernel_events[0] || !kernel_events[1] || !kernel_events[2] ||
+                          !kernel_events[3]))
+        return LT_ERR_INVALID_ARG;
+    const Plan pl = bwd_plan(B, T, H, segments);
+    const BwdLayout lay = bwd_layout(B, T, H, d, pl);
+    if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < lay.total)
+        return LT_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    const int P = pl.P;
+
+    // forward entry states: the prefill's state-only pass and scan over the same segments
+    lt::ChunkParams cp;
+    memset(&cp, 0, sizeof cp);
+    cp.q = q; cp.k = k; cp.v = v; cp.g = gate;
+    cp.qw = q_norm_w; cp.kw = k_norm_w; cp.ow = o_norm_w;
+    cp.state_in = state_in;
+    cp.ws = reinterpret_cast<float*>(ws);
+    cp.pos0 = pos0;
+    cp.B = B; cp.T = T; cp.H = H; cp.P = P; cp.L = pl.L;
+    cp.x_stride = H * d;
+    cp.SM = pl.sub; cp.SL = pl.sub_len; cp.SP = (P - 1) * pl.sub + 1;
+    cp.w_stride = norm_w_head_stride;
+    cp.eps = (float)rms_eps;
+    for (int h = 0; h < H; ++h) cp.log2_lambda[h] = log2_lambda(lambda[h]);
+    fill_inv_freq_rev(cp.inv_freq_rev, d, rope_base);
+    lt::ScanParams sp;
+    memset(&sp, 0, sizeof sp);
+    sp.state_in = state_in;
+    sp.ws = cp.ws;
+    sp.BH = B * H; sp.H = H; sp.P = cp.SP; sp.sub = pl.sub; sp.dd = d * d;
+    const int rest = pl.L - (pl.sub - 1) * pl.sub_len;
+    for (int h = 0; h < H; ++h) {
+        sp.lambda_pow_sub[h] = (float)pow(lambda[h], (double)pl.sub_len);
+        sp.lambda_pow_rest[h] = (float)pow(lambda[h], (double)rest);
+    }
+
+    lt::BwdParams bp;
+    memset(&bp, 0, sizeof bp);
+    bp.q = q; bp.k = k; bp.v = v; bp.g = gate; bp.dy = dy;
+    bp.qw = q_norm_w; bp.kw = k_norm_w; bp.ow = o_norm_w;
+    bp.state_in = state_in;
+    bp.fwd_states = cp.ws;
+    bp.d_state_out = d_state_out;
+    bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dg = dgate;
+    bp.d_state_in = d_state_in;
+    bp.d_o = reinterpret_cast<uint16_t*>(ws + lay.d_o);
+    bp.seg_grad = reinterpret_cast<float*>(ws + lay.seg_grad);
+    if (d_q_norm_w || d_k_norm_w || d_o_norm_w) bp.wgrad = reinterpret_cast<float*>(ws + lay.wgrad);
+    bp.dqw = d_q_norm_w; bp.dkw = d_k_norm_w; bp.dow = d_o_norm_w;
+    bp.pos0 = pos0;
+    bp.B = B; bp.T = T; bp.H = H; bp.P = P; bp.L = pl.L; bp.SM = pl.sub; bp.SP = cp.SP;
+    bp.w_stride = norm_w_head_stride;
+    bp.eps = (float)rms_eps;
+    for (int h = 0; h < H; ++h) {
+        bp.log2_lambda[h] = cp.log2_lambda[h];
+        bp.lambda_pow_seg[h] = (float)pow(lambda[h], (double)pl.L);
+        bp.lambda_pow_last[h] = (float)pow(lambda[h], (double)(T - (int64_t)(P - 1) * pl.L));
+    }
+    memcpy(bp.inv_freq_rev, cp.inv_freq_rev, sizeof bp.inv_freq_rev);
+
+    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+    if (kernel_events)
+        for (int i = 0; i < 4; ++i) ev[i] = static_cast<hipEvent_t>(kernel_events[i]);
+    if (lt::launch_prefill_backward(bp, cp, sp, ev, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return LT_ERR_HIP;
+    return LT_OK;
 }
 
 }  // extern "C"

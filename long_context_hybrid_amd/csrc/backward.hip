@@ -1,0 +1,929 @@
+// Backward of the chunkwise Lightning Attention prefill on gfx950.
+//
+// The gradient of the forward pass of "Hybrid Linear Attention Done Right" (Appendix A, Eq. 18,
+// with the QK-norm of Eq. 12 and the gated output norm of Eq. 14), as the training of HALO
+// (Sections 4.2-4.5) needs it.  For one (b, h) and a chunk of n tokens whose forward entry state
+// is S and whose exit-state gradient is dS (dL/dS after the chunk), with D_ij = lambda^(i-j)
+// for j <= i (else 0) and do the gradient at o (before the output norm):
+//     dq~ = (do V^T (.) D) K~  +  diag(lambda^(i+1)) do S^T
+//     dk~ = (do V^T (.) D)^T Q~  +  diag(lambda^(n-1-j)) V dS^T
+//     dv  = (Q~ K~^T (.) D)^T do  +  diag(lambda^(n-1-j)) K~ dS
+//     dS  <- lambda^n dS + (diag(lambda^(i+1)) Q~)^T do          (the chunk's entry-state gradient)
+// which is the token recurrence's adjoint regrouped by chunk.  dq~ needs the forward states, so
+// it runs forward in time; dk~ and dv need the state gradients, so they run backward in time:
+//   1. forward entry states of the P segments per (b, h): the prefill's state-only pass + scan;
+//   2. bwd_dq_kernel, forward over each segment's chunks: recompute o, then the output-norm and
+//      gate gradients (dg, do; do is written for pass 4), dq~ and through RoPE^T and the QK-norm
+//      dq; it also sums the segment's own entry-state gradient W = sum_i lambda^(i+1) q~_i^T do_i
+//      (token offsets i within the segment);
+//   3. bwd_scan_kernel, backward over segments: E_(P-1) = dS_out, E_(s-1) = lambda^L_s E_s + W_s
+//      (the gradient at each segment's end), and dS_in = lambda^L_0 E_0 + W_0;
+//   4. bwd_dkv_kernel, backward over each segment's chunks from E_s: dk~ (then dk) and dv;
+//   5. bwd_wgrad_kernel: the norm weights' gradients from per-workgroup partial sums.
+//
+// Both sweeps use one workgroup of d/32 wavefronts per (b, h, segment).  Wavefront w keeps the
+// d x 32 slice of the fp32 state (or state gradient) for value columns [32w, 32w + 32) in MFMA
+// accumulators; products that contract over the value dimension read a bf16 copy of the whole
+// state that the wavefronts write to LDS once per chunk (transposed, [value][key]).  Row-wise
+// work (norms, rotation, gate) runs on all threads with d/16 threads per token row, which keep
+// their rows' raw inputs in registers between the prologue and the epilogues.  The next chunk's
+// inputs are loaded into a second register set while the current chunk is processed.
+//
+// LDS tiles are bf16 [row][d] with the 16-byte blocks of row r XOR-permuted by r mod (d/8): a
+// 16-byte row read by 16 consecutive rows and a transposing ds_read_b64_tr_b16 of 4 rows both
+// spread over the banks, so every tile serves both access patterns.
+#include "lt_device.h"
+#include "lt_internal.h"
+
+namespace lt {
+namespace {
+
+constexpr int C = kChunk;
+constexpr int kRopeAnchorB = 64;  // chunks between exact recomputations of the RoPE table
+
+template <int D>
+struct BCfg {
+    static constexpr int NW = D / 32;     // wavefronts
+    static constexpr int NT = 64 * NW;    // threads
+    static constexpr int HALF = D / 2;
+    static constexpr int TPR = D / 16;    // row-op threads per token row (8 features per half)
+    static constexpr int OS = D + 4;      // fp32 stage row stride
+    static_assert(NT / TPR == C, "the row-op threads cover one chunk");
+};
+
+template <int D>
+struct alignas(16) BwdSmem {
+    using G = BCfg<D>;
+    alignas(16) __bf16 q[C * D];   // q~
+    alignas(16) __bf16 k[C * D];   // k~
+    alignas(16) __bf16 v[C * D];
+    alignas(16) __bf16 dO[C * D];  // do
+    alignas(16) __bf16 q_lo[C * D];  // q~ - bf16(q~) and k~ - bf16(k~) (dq sweep only)
+    alignas(16) __bf16 k_lo[C * D];
+    alignas(16) __bf16 st[D * D];  // state (or state gradient) copy, [value][key]
+    alignas(16) float stage[C * G::OS];  // fp32 [token][feature] stage of o, dq~ or dk~
+    alignas(16) float2 rope[2][64];      // cos/sin(p0 f_i) of this chunk and the next
+    alignas(16) float w[3][D];           // norm weights q, k, o
+    // per lane: [0, 16) score-tile decay, [16, 32) lambda^(row + 1), [32, 48) lambda^(C-1-row)
+    alignas(16) float dec[64][48];
+    // norm-weight gradient partial sums of each row-op thread (its row, its 16 features):
+    // [0] q (or k), [1] o
+    alignas(16) float wacc[2][BCfg<D>::NT][16];
+};
+
+template <int D>
+__device__ __forceinline__ int swz(int row, int col) {
+    return row * D + (((col >> 3) ^ (row & (D / 8 - 1))) << 3) + (col & 7);
+}
+
+typedef short tr16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+template <int D>
+__device__ __forceinline__ bf16x8 tr_rows(const __bf16* tile, int r0, int r1, int col) {
+    typedef __attribute__((address_space(3))) tr16x4_t lds_t;
+    const tr16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_t*)(tile + swz<D>(r0, col)));
+    const tr16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_t*)(tile + swz<D>(r1, col)));
+    const s16x8_t ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, ab);
+}
+// Operand whose m (or n) index is the tile column colbase + lane % 32 and whose 16 k values are
+// the tile rows kbase .. kbase + 15.  ds_read_b64_tr_b16 hands lane 4a + c of a 16-lane group
+// element c of the 4-element row pieces addressed by lanes a, a + 4, a + 8, a + 12; so lane s
+// of group g addresses column colbase + 16 (g % 2) + 4 (s % 4) of row r0 + s / 4.
+// tr_acc: element e holds row kbase + 8 (e / 4) + 4 lh + e % 4 (the accumulator's row order);
+// tr_nat: element e holds row kbase + 8 lh + e (natural order).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_acc(const __bf16* tile, int kbase, int colbase, int lane) {
+    const int g = lane >> 4, sl = lane & 15;
+    const int row = kbase + 4 * (g >> 1) + (sl >> 2);
+    return tr_rows<D>(tile, row, row + 8, colbase + 16 * (g & 1) + 4 * (sl & 3));
+}
+template <int D>
+__device__ __forceinline__ bf16x8 tr_nat(const __bf16* tile, int kbase, int colbase, int lane) {
+    const int g = lane >> 4, sl = lane & 15;
+    const int row = kbase + 8 * (g >> 1) + (sl >> 2);
+    return tr_rows<D>(tile, row, row + 4, colbase + 16 * (g & 1) + 4 * (sl & 3));
+}
+// 8 consecutive elements of a row (natural k order: columns col .. col + 7)
+template <int D>
+__device__ __forceinline__ bf16x8 row8(const __bf16* tile, int row, int col) {
+    return *reinterpret_cast<const bf16x8*>(tile + swz<D>(row, col));
+}
+// a row's 16-column block s in the accumulator's k order: columns 16 s + 4 lh + (0..3) and
+// 16 s + 8 + 4 lh + (0..3)
+template <int D>
+__device__ __forceinline__ bf16x8 row_acc(const __bf16* tile, int row, int s, int lh) {
+    const uint2 a = *reinterpret_cast<const uint2*>(tile + swz<D>(row, 16 * s + 4 * lh));
+    const uint2 b = *reinterpret_cast<const uint2*>(tile + swz<D>(row, 16 * s + 8 + 4 * lh));
+    const u32x4_t ab = {a.x, a.y, b.x, b.y};
+    return __builtin_bit_cast(bf16x8, ab);
+}
+// accumulator registers [8 st, 8 st + 8) as a bf16 operand
+__device__ __forceinline__ bf16x8 acc_operand(const f32x16& x, int st) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = to_bf16(x[8 * st + e]);
+    return r;
+}
+__device__ __forceinline__ bf16x8 scale8(bf16x8 x, const float* f, float c) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = to_bf16((float)x[e] * (f[e] * c));
+    return r;
+}
+
+// the hi and lo bf16 parts of 8 fp32 values (x = hi + lo to about 2^-17 relative)
+__device__ __forceinline__ void split8(const float* x, uint4& hi, uint4& lo) {
+    float h[8], l[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        h[e] = (float)to_bf16(x[e]);
+        l[e] = x[e] - h[e];
+    }
+    hi = make_uint4(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]), pack_bf16x2(h[4], h[5]),
+                    pack_bf16x2(h[6], h[7]));
+    lo = make_uint4(pack_bf16x2(l[0], l[1]), pack_bf16x2(l[2], l[3]), pack_bf16x2(l[4], l[5]),
+                    pack_bf16x2(l[6], l[7]));
+}
+// hi and lo parts of accumulator registers [8 st, 8 st + 8) as bf16 operands
+__device__ __forceinline__ void acc_split(const f32x16& x, int st, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float v = x[8 * st + e];
+        hi[e] = to_bf16(v);
+        lo[e] = to_bf16(v - (float)hi[e]);
+    }
+}
+
+__device__ __forceinline__ uint4 keep_if(bool keep, uint4 x) {
+    return make_uint4(keep ? x.x : 0u, keep ? x.y : 0u, keep ? x.z : 0u, keep ? x.w : 0u);
+}
+
+__device__ __forceinline__ void widen8(uint4 x, float* o) {
+    o[0] = bf16_lo(x.x); o[1] = bf16_hi(x.x); o[2] = bf16_lo(x.y); o[3] = bf16_hi(x.y);
+    o[4] = bf16_lo(x.z); o[5] = bf16_hi(x.z); o[6] = bf16_lo(x.w); o[7] = bf16_hi(x.w);
+}
+__device__ __forceinline__ uint4 pack8(const float* x) {
+    return make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                      pack_bf16x2(x[6], x[7]));
+}
+
+// Shared per-workgroup set-up: norm weights, decay tables, the first RoPE table.
+template <int D>
+__device__ __forceinline__ void setup_common(const BwdParams& p, BwdSmem<D>& sm, int h,
+                                             float l2l, bool transposed_scores) {
+    constexpr int NT = BCfg<D>::NT;
+    for (int i = threadIdx.x; i < D; i += NT) {
+        const size_t o = (size_t)h * p.w_stride + i;
+        sm.w[0][i] = p.qw[o];
+        sm.w[1][i] = p.kw[o];
+        sm.w[2][i] = p.ow ? p.ow[o] : 1.0f;
+    }
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x, lm = lane & 31, lh = lane >> 5;
+        float* d = sm.dec[lane];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int m = acc_row(r, lh);
+            // score tile of the dq sweep: S^T[j = m][i = lm]; of the dk/dv sweep: S[i = m][j = lm]
+            const int i = transposed_scores ? lm : m, j = transposed_scores ? m : lm;
+            d[r] = (j <= i) ? pow_lambda(l2l, i - j) : 0.0f;
+            d[16 + r] = pow_lambda(l2l, m + 1);
+            d[32 + r] = pow_lambda(l2l, C - 1 - m);
+        }
+    }
+}
+
+// The 16 decay factors of one lane's table row, as read for a use
+__device__ __forceinline__ void load16(const float* src, float* dst) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const float4 x = reinterpret_cast<const float4*>(src)[g];
+        dst[4 * g] = x.x; dst[4 * g + 1] = x.y; dst[4 * g + 2] = x.z; dst[4 * g + 3] = x.w;
+    }
+}
+
+// ============================== forward sweep: dq, dg, do, W ==================================
+template <int D>
+__global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) {
+    using G = BCfg<D>;
+    constexpr int NW = G::NW, HALF = G::HALF, TPR = G::TPR, OS = G::OS;
+    __shared__ BwdSmem<D> sm;
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, lm = lane & 31, lh = lane >> 5;
+    const int seg = blockIdx.x % p.P, bh = blockIdx.x / p.P;
+    const int b = bh / p.H, h = bh - b * p.H;
+    const int t_begin = seg * p.L, t_end = min(p.T, t_begin + p.L);
+    const int n_chunks = (t_end - t_begin + C - 1) / C;
+    const float l2l = p.log2_lambda[h];
+    const size_t rs = (size_t)p.H * D;                      // elements between tokens
+    const size_t base = ((size_t)b * p.T * p.H + h) * D;     // token 0 of (b, h)
+    const size_t dd = (size_t)D * D;
+    // row-op role: row rr of the chunk, features 8 fg + u and HALF + 8 fg + u (u < 8)
+    const int rr = threadIdx.x / TPR, fg = threadIdx.x % TPR;
+    const uint16_t* gq = static_cast<const uint16_t*>(p.q) + base + 8 * fg;
+    const uint16_t* gk = static_cast<const uint16_t*>(p.k) + base + 8 * fg;
+    const uint16_t* gv = static_cast<const uint16_t*>(p.v) + base + 8 * fg;
+    const uint16_t* gg = static_cast<const uint16_t*>(p.g) + base + 8 * fg;
+    const uint16_t* gdy = static_cast<const uint16_t*>(p.dy) + base + 8 * fg;
+
+    setup_common<D>(p, sm, h, l2l, true);
+    // RoPE: per-chunk table cos/sin(p0 f_i) (wavefront 0, one frequency per lane) and this
+    // thread's rotation by its row, cos/sin(rr f_i)
+    const int fi = lane < HALF ? lane : HALF - 1;
+    const double frev = p.inv_freq_rev[fi];
+    float2 tstep;
+    rope_cos_sin(C, frev, tstep.x, tstep.y);
+    auto fill_table = [&](int step, int chunk) __attribute__((always_inline)) {
+        float2 e;
+        if (step % kRopeAnchorB == 0) {
+            rope_cos_sin(p.pos0 + t_begin + (int64_t)chunk * C, frev, e.x, e.y);
+        } else {
+            const float2 a = sm.rope[(step - 1) & 1][fi];
+            e.x = a.x * tstep.x - a.y * tstep.y;
+            e.y = a.y * tstep.x + a.x * tstep.y;
+        }
+        if (lane < HALF) sm.rope[step & 1][lane] = e;
+    };
+    if (wave == 0) fill_table(0, 0);
+    float2 rot[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) rope_cos_sin(rr, p.inv_freq_rev[8 * fg + u], rot[u].x, rot[u].y);
+
+    // forward entry state and the segment's entry-state gradient W
+    f32x16 S[NW], W[NW];
+    {
+        const float* src = p.P > 1 ? p.fwd_states + ((size_t)bh * p.SP + (size_t)seg * p.SM) * dd
+                                   : (p.state_in ? p.state_in + (size_t)bh * dd : nullptr);
+#pragma unroll
+        for (int c = 0; c < NW; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                S[c][r] = src ? src[(size_t)(32 * c + acc_row(r, lh)) * D + 32 * wave + lm] : 0.0f;
+                W[c][r] = 0.0f;
+            }
+    }
+    float* wacc_q = sm.wacc[0][threadIdx.x];
+    float* wacc_o = sm.wacc[1][threadIdx.x];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) wacc_q[e] = wacc_o[e] = 0.0f;
+
+    struct Regs {
+        uint4 q[2], k[2], v[2], g[2], dy[2];
+    };
+    auto load = [&](int chunk, Regs& R) __attribute__((always_inline)) {
+        const int t0 = t_begin + chunk * C;
+        const size_t o = (size_t)min(t0 + rr, t_end - 1) * rs;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const size_t oo = o + hf * HALF;
+            R.q[hf] = *reinterpret_cast<const uint4*>(gq + oo);
+            R.k[hf] = *reinterpret_cast<const uint4*>(gk + oo);
+            R.v[hf] = *reinterpret_cast<const uint4*>(gv + oo);
+            R.g[hf] = *reinterpret_cast<const uint4*>(gg + oo);
+            R.dy[hf] = *reinterpret_cast<const uint4*>(gdy + oo);
+        }
+    };
+    // cos/sin of (p0 + rr) f for this thread's 8 frequencies
+    auto angles = [&](int step, float2* cs) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float2 t = sm.rope[step & 1][8 * fg + u];
+            cs[u] = make_float2(t.x * rot[u].x - t.y * rot[u].y, t.y * rot[u].x + t.x * rot[u].y);
+        }
+    };
+    // RMSNorm (returns 1/rms), weight, rotation; x[16] = features lo 0..7, hi 0..7
+    auto norm_rotate = [&](float* x, const float* w, const float2* cs, float scale) __attribute__((always_inline)) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ss = fmaf(x[e], x[e], ss);
+        ss = group_sum<TPR>(ss);
+        const float rinv = fast_rsqrt(ss * (1.0f / D) + p.eps);
+        const float sc = rinv * scale;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float a = x[u] * sc * w[8 * fg + u], c = x[8 + u] * sc * w[HALF + 8 * fg + u];
+            x[u] = a * cs[u].x - c * cs[u].y;
+            x[8 + u] = c * cs[u].x + a * cs[u].y;
+        }
+        return rinv;
+    };
+    auto st16 = [&](__bf16* tile, const float* x, bool valid) __attribute__((always_inline)) {
+        const uint4 lo = valid ? pack8(x) : make_uint4(0, 0, 0, 0);
+        const uint4 hi = valid ? pack8(x + 8) : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(tile + swz<D>(rr, 8 * fg)) = lo;
+        *reinterpret_cast<uint4*>(tile + swz<D>(rr, HALF + 8 * fg)) = hi;
+    };
+
+    auto st16_split = [&](__bf16* hi, __bf16* lo, const float* x, bool valid) __attribute__((always_inline)) {
+        uint4 h0, l0, h1, l1;
+        split8(x, h0, l0);
+        split8(x + 8, h1, l1);
+        *reinterpret_cast<uint4*>(hi + swz<D>(rr, 8 * fg)) = keep_if(valid, h0);
+        *reinterpret_cast<uint4*>(hi + swz<D>(rr, HALF + 8 * fg)) = keep_if(valid, h1);
+        *reinterpret_cast<uint4*>(lo + swz<D>(rr, 8 * fg)) = keep_if(valid, l0);
+        *reinterpret_cast<uint4*>(lo + swz<D>(rr, HALF + 8 * fg)) = keep_if(valid, l1);
+    };
+
+    auto step = [&](int i, Regs& R, Regs& Rn) __attribute__((always_inline)) {
+        const int c = i;
+        const int t0 = t_begin + c * C;
+        const int n = min(C, t_end - t0);
+        const bool valid = rr < n;
+        // ---- P1: prologue (q~, k~, v tiles) and the state copy; prefetch the next chunk ----
+        float2 cs[8];
+        angles(i, cs);
+        float x[16];
+        widen8(R.q[0], x);
+        widen8(R.q[1], x + 8);
+        const float rq = norm_rotate(x, sm.w[0], cs, 1.0f);
+        st16_split(sm.q, sm.q_lo, x, valid);
+        widen8(R.k[0], x);
+        widen8(R.k[1], x + 8);
+        norm_rotate(x, sm.w[1], cs, 1.0f / sqrtf((float)D));
+        st16_split(sm.k, sm.k_lo, x, valid);
+        *reinterpret_cast<uint4*>(sm.v + swz<D>(rr, 8 * fg)) = keep_if(valid, R.v[0]);
+        *reinterpret_cast<uint4*>(sm.v + swz<D>(rr, HALF + 8 * fg)) = keep_if(valid, R.v[1]);
+#pragma unroll
+        for (int cc = 0; cc < NW; ++cc)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                // S[32 cc + 8 g4 + 4 lh + (0..3)][32 w + lm] -> st[32 w + lm][same keys]
+                const uint2 pk = make_uint2(pack_bf16x2(S[cc][4 * g4], S[cc][4 * g4 + 1]),
+                                            pack_bf16x2(S[cc][4 * g4 + 2], S[cc][4 * g4 + 3]));
+                *reinterpret_cast<uint2*>(sm.st + swz<D>(32 * wave + lm, 32 * cc + 8 * g4 + 4 * lh)) = pk;
+            }
+        if (c + 1 < n_chunks) load(c + 1, Rn);
+        __syncthreads();
+        // ---- P2: o = diag(lambda^(i+1)) Q~ S + (K~ Q~^T (.) D)^T V for value columns of w ----
+        if (wave == 0 && c + 1 < n_chunks) fill_table(i + 1, c + 1);
+        const float* dl = sm.dec[lane];
+        float mk[16], rf[16];
+        load16(dl, mk);
+        load16(dl + 16, rf);
+        // o is recomputed to about fp32 accuracy (hi/lo parts of q~, k~, the state and the
+        // scores): the output norm's gradient scales with 1/||o_t||, and the rows where o_t is
+        // small (often the first tokens of a sequence, where o_t = (q~_t . k~_t) v_t) would
+        // otherwise carry the bf16 rounding of the products into do_t, which then dominates the
+        // sums q~_i^T do_i of the state gradients.
+        f32x16 pt = {}, o = {};
+#pragma unroll
+        for (int s8 = 0; s8 < D / 16; ++s8) {
+            const bf16x8 kv = row8<D>(sm.k, lm, 16 * s8 + 8 * lh);
+            const bf16x8 kl = row8<D>(sm.k_lo, lm, 16 * s8 + 8 * lh);
+            const bf16x8 qv = row8<D>(sm.q, lm, 16 * s8 + 8 * lh);
+            const bf16x8 ql = row8<D>(sm.q_lo, lm, 16 * s8 + 8 * lh);
+            pt = mfma_bf16(kv, qv, pt);  // P^T[j][i] += k~_j . q~_i
+            pt = mfma_bf16(kv, ql, pt);
+            pt = mfma_bf16(kl, qv, pt);
+            const bf16x8 qa = row_acc<D>(sm.q, lm, s8, lh);
+            const bf16x8 qal = row_acc<D>(sm.q_lo, lm, s8, lh);
+            bf16x8 sh, sl;
+            acc_split(S[s8 / 2], s8 % 2, sh, sl);
+            o = mfma_bf16(qa, sh, o);
+            o = mfma_bf16(qa, sl, o);
+            o = mfma_bf16(qal, sh, o);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            pt[r] *= mk[r];
+            o[r] *= rf[r];
+        }
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            bf16x8 ph, pl;
+            acc_split(pt, st, ph, pl);
+            const bf16x8 vb = tr_acc<D>(sm.v, 16 * st, 32 * wave, lane);
+            o = mfma_bf16(ph, vb, o);
+            o = mfma_bf16(pl, vb, o);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sm.stage[acc_row(r, lh) * OS + 32 * wave + lm] = o[r];
+        __syncthreads();
+        // ---- P3: output norm and gate gradients: dg, do ----
+        {
+            float ov[16], gv[16], dyv[16];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const float* src = sm.stage + rr * OS + hf * HALF + 8 * fg;
+                const float4 a = reinterpret_cast<const float4*>(src)[0];
+                const float4 bq = reinterpret_cast<const float4*>(src)[1];
+                ov[8 * hf + 0] = a.x; ov[8 * hf + 1] = a.y; ov[8 * hf + 2] = a.z; ov[8 * hf + 3] = a.w;
+                ov[8 * hf + 4] = bq.x; ov[8 * hf + 5] = bq.y; ov[8 * hf + 6] = bq.z; ov[8 * hf + 7] = bq.w;
+                widen8(R.g[hf], gv + 8 * hf);
+                widen8(R.dy[hf], dyv + 8 * hf);
+            }
+            float ss = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) ss = fmaf(ov[e], ov[e], ss);
+            ss = group_sum<TPR>(ss);
+            const float ro = fast_rsqrt(ss * (1.0f / D) + p.eps);
+            float dn[16], dgv[16], dot = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int f = (e < 8 ? 0 : HALF) + 8 * fg + (e & 7);
+                const float nv = ov[e] * ro, s = sigmoidf_(gv[e]), wo = sm.w[2][f];
+                const float t = dyv[e] * s;
+                dn[e] = t * wo;
+                dgv[e] = dn[e] * nv * (1.0f - s);
+                dot = fmaf(dn[e], nv, dot);
+                if (valid) wacc_o[e] = fmaf(t, nv, wacc_o[e]);
+                ov[e] = nv;
+            }
+            dot = group_sum<TPR>(dot) * (1.0f / D);
+            float dov[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) dov[e] = ro * (dn[e] - ov[e] * dot);
+            st16(sm.dO, dov, valid);
+            if (valid) {
+                const size_t o2 = (size_t)(t0 + rr) * rs + 8 * fg;
+                uint16_t* pdg = static_cast<uint16_t*>(p.dg) + base + o2;
+                uint16_t* pdo = p.d_o + base + o2;
+                *reinterpret_cast<uint4*>(pdg) = pack8(dgv);
+                *reinterpret_cast<uint4*>(pdg + HALF) = pack8(dgv + 8);
+                *reinterpret_cast<uint4*>(pdo) = pack8(dov);
+                *reinterpret_cast<uint4*>(pdo + HALF) = pack8(dov + 8);
+            }
+        }
+        __syncthreads();
+        // ---- P4: dq~ for key columns of w; W and S updates for value columns of w ----
+        {
+            load16(dl, mk);
+            load16(dl + 16, rf);
+            f32x16 dpt = {}, dq = {};
+#pragma unroll
+            for (int s8 = 0; s8 < D / 16; ++s8) {
+                const bf16x8 dv8 = row8<D>(sm.dO, lm, 16 * s8 + 8 * lh);
+                dpt = mfma_bf16(row8<D>(sm.v, lm, 16 * s8 + 8 * lh), dv8, dpt);  // v_j . do_i
+                dq = mfma_bf16(dv8, tr_nat<D>(sm.st, 16 * s8, 32 * wave, lane), dq);  // do S^T
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                dpt[r] *= mk[r];
+                dq[r] *= rf[r];
+            }
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+                dq = mfma_bf16(acc_operand(dpt, st), tr_acc<D>(sm.k, 16 * st, 32 * wave, lane), dq);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sm.stage[acc_row(r, lh) * OS + 32 * wave + lm] = dq[r];
+            // W[k][v] += lambda^(cC) sum_i q~[i][k] lambda^(i+1) do[i][v]
+            const float cf = pow_lambda(l2l, c * C);
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const bf16x8 db = scale8(tr_acc<D>(sm.dO, 16 * st, 32 * wave, lane), rf + 8 * st, cf);
+#pragma unroll
+                for (int cc = 0; cc < NW; ++cc)
+                    W[cc] = mfma_bf16(tr_acc<D>(sm.q, 16 * st, 32 * cc, lane), db, W[cc]);
+            }
+            // S <- lambda^n S + sum_j k~_j^T lambda^(n-1-j) v_j
+            float rd[16];
+            if (n == C) {
+                load16(dl + 32, rd);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int j = acc_row(r, lh);
+                    rd[r] = j < n ? pow_lambda(l2l, n - 1 - j) : 0.0f;
+                }
+            }
+            const float ln = pow_lambda(l2l, n);
+#pragma unroll
+            for (int cc = 0; cc < NW; ++cc)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) S[cc][r] *= ln;
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const bf16x8 vb = scale8(tr_acc<D>(sm.v, 16 * st, 32 * wave, lane), rd + 8 * st, 1.0f);
+#pragma unroll
+                for (int cc = 0; cc < NW; ++cc)
+                    S[cc] = mfma_bf16(tr_acc<D>(sm.k, 16 * st, 32 * cc, lane), vb, S[cc]);
+            }
+        }
+        __syncthreads();
+        // ---- P5: dq = QK-norm^T(RoPE^T(dq~)) ----
+        {
+            angles(i, cs);
+            float dqt[16];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const float* src = sm.stage + rr * OS + hf * HALF + 8 * fg;
+                const float4 a = reinterpret_cast<const float4*>(src)[0];
+                const float4 bq = reinterpret_cast<const float4*>(src)[1];
+                dqt[8 * hf + 0] = a.x; dqt[8 * hf + 1] = a.y; dqt[8 * hf + 2] = a.z; dqt[8 * hf + 3] = a.w;
+                dqt[8 * hf + 4] = bq.x; dqt[8 * hf + 5] = bq.y; dqt[8 * hf + 6] = bq.z; dqt[8 * hf + 7] = bq.w;
+            }
+            widen8(R.q[0], x);
+            widen8(R.q[1], x + 8);
+            float dx[16], dot = 0.0f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float lo = cs[u].x * dqt[u] + cs[u].y * dqt[8 + u];
+                const float hi = cs[u].x * dqt[8 + u] - cs[u].y * dqt[u];
+                const float xl = x[u] * rq, xh = x[8 + u] * rq;
+                if (valid) {
+                    wacc_q[u] = fmaf(lo, xl, wacc_q[u]);
+                    wacc_q[8 + u] = fmaf(hi, xh, wacc_q[8 + u]);
+                }
+                dx[u] = lo * sm.w[0][8 * fg + u];
+                dx[8 + u] = hi * sm.w[0][HALF + 8 * fg + u];
+                x[u] = xl;
+                x[8 + u] = xh;
+                dot = fmaf(dx[u], xl, dot);
+                dot = fmaf(dx[8 + u], xh, dot);
+            }
+            dot = group_sum<TPR>(dot) * (1.0f / D);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) dx[e] = rq * (dx[e] - x[e] * dot);
+            if (valid) {
+                uint16_t* pdq = static_cast<uint16_t*>(p.dq) + base + (size_t)(t0 + rr) * rs + 8 * fg;
+                *reinterpret_cast<uint4*>(pdq) = pack8(dx);
+                *reinterpret_cast<uint4*>(pdq + HALF) = pack8(dx + 8);
+            }
+        }
+    };
+
+    // the current chunk's inputs are a plain copy of the prefetched set, so both stay in
+    // registers (references to alternating sets would put them in memory)
+    Regs cur;
+    load(0, cur);
+    __syncthreads();  // weights, decay tables and the first RoPE table
+    for (int i = 0; i < n_chunks; ++i) {
+        Regs nxt = cur;
+        step(i, cur, nxt);
+        cur = nxt;
+    }
+
+    // the segment's entry-state gradient W, and the norm-weight partial sums
+    {
+        float* dst = p.seg_grad + ((size_t)bh * p.P + seg) * dd;
+#pragma unroll
+        for (int cc = 0; cc < NW; ++cc)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                dst[(size_t)(32 * cc + acc_row(r, lh)) * D + 32 * wave + lm] = W[cc][r];
+    }
+    if (p.wgrad) {
+        const size_t nbp = (size_t)p.B * p.H * p.P;
+        __syncthreads();
+        for (int f = threadIdx.x; f < 2 * D; f += G::NT) {
+            const int which = f / D, ff = f % D;
+            const int tf = (ff % HALF) / 8, e = (ff >= HALF ? 8 : 0) + (ff & 7);
+            float s = 0.0f;
+            for (int r = 0; r < C; ++r) s += sm.wacc[which][r * TPR + tf][e];
+            p.wgrad[((which == 0 ? 0 : 2) * nbp + (size_t)bh * p.P + seg) * D + ff] = s;
+        }
+    }
+}
+
+// ============================ segment scan (backward in time) ================================
+// seg_grad[bh][s] holds W_s; it becomes E_s = dL/d(state after segment s), with
+// E_(P-1) = d_state_out and E_(s-1) = lambda^L_s E_s + W_s; d_state_in = lambda^L_0 E_0 + W_0.
+__global__ void __launch_bounds__(256) bwd_scan_kernel(const BwdParams p, int dd) {
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (size_t)p.B * p.H * dd) return;
+    const int bh = (int)(idx / dd);
+    const int e = (int)(idx - (size_t)bh * dd);
+    const int h = bh % p.H;
+    float* w = p.seg_grad + (size_t)bh * p.P * dd + e;
+    float g = p.d_state_out ? p.d_state_out[idx] : 0.0f;
+    for (int s = p.P - 1; s >= 0; --s) {
+        const float ws = w[(size_t)s * dd];
+        w[(size_t)s * dd] = g;
+        const float lam = (s == p.P - 1) ? p.lambda_pow_last[h] : p.lambda_pow_seg[h];
+        g = fmaf(lam, g, ws);
+    }
+    if (p.d_state_in) p.d_state_in[idx] = g;
+}
+
+// ============================ backward sweep: dk, dv =========================================
+template <int D>
+__global__ void __launch_bounds__(BCfg<D>::NT) bwd_dkv_kernel(const BwdParams p) {
+    using G = BCfg<D>;
+    constexpr int NW = G::NW, HALF = G::HALF, TPR = G::TPR, OS = G::OS;
+    __shared__ BwdSmem<D> sm;
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, lm = lane & 31, lh = lane >> 5;
+    const int seg = blockIdx.x % p.P, bh = blockIdx.x / p.P;
+    const int b = bh / p.H, h = bh - b * p.H;
+    const int t_begin = seg * p.L, t_end = min(p.T, t_begin + p.L);
+    const int n_chunks = (t_end - t_begin + C - 1) / C;
+    const float l2l = p.log2_lambda[h];
+    const size_t rs = (size_t)p.H * D;
+    const size_t base = ((size_t)b * p.T * p.H + h) * D;
+    const size_t dd = (size_t)D * D;
+    const int rr = threadIdx.x / TPR, fg = threadIdx.x % TPR;
+    const uint16_t* gq = static_cast<const uint16_t*>(p.q) + base + 8 * fg;
+    const uint16_t* gk = static_cast<const uint16_t*>(p.k) + base + 8 * fg;
+    const uint16_t* gv = static_cast<const uint16_t*>(p.v) + base + 8 * fg;
+    const uint16_t* gdo = p.d_o + base + 8 * fg;
+
+    setup_common<D>(p, sm, h, l2l, false);
+    const int fi = lane < HALF ? lane : HALF - 1;
+    const double frev = p.inv_freq_rev[fi];
+    float2 tstep;  // rotation back by one chunk
+    rope_cos_sin(-C, frev, tstep.x, tstep.y);
+    auto chunk_of = [&](int step) __attribute__((always_inline)) { return n_chunks - 1 - step; };
+    auto fill_table = [&](int step) __attribute__((always_inline)) {
+        float2 e;
+        if (step % kRopeAnchorB == 0) {
+            rope_cos_sin(p.pos0 + t_begin + (int64_t)chunk_of(step) * C, frev, e.x, e.y);
+        } else {
+            const float2 a = sm.rope[(step - 1) & 1][fi];
+            e.x = a.x * tstep.x - a.y * tstep.y;
+            e.y = a.y * tstep.x + a.x * tstep.y;
+        }
+        if (lane < HALF) sm.rope[step & 1][lane] = e;
+    };
+    if (wave == 0) fill_table(0);
+    float2 rot[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) rope_cos_sin(rr, p.inv_freq_rev[8 * fg + u], rot[u].x, rot[u].y);
+
+    // state gradient at the segment's end
+    f32x16 dS[NW];
+    {
+        const float* src = p.seg_grad + ((size_t)bh * p.P + seg) * dd;
+#pragma unroll
+        for (int c = 0; c < NW; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                dS[c][r] = src[(size_t)(32 * c + acc_row(r, lh)) * D + 32 * wave + lm];
+    }
+    float* wacc_k = sm.wacc[0][threadIdx.x];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) wacc_k[e] = 0.0f;
+
+    struct Regs {
+        uint4 q[2], k[2], v[2], dO[2];
+    };
+    auto load = [&](int chunk, Regs& R) __attribute__((always_inline)) {
+        const int t0 = t_begin + chunk * C;
+        const size_t o = (size_t)min(t0 + rr, t_end - 1) * rs;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const size_t oo = o + hf * HALF;
+            R.q[hf] = *reinterpret_cast<const uint4*>(gq + oo);
+            R.k[hf] = *reinterpret_cast<const uint4*>(gk + oo);
+            R.v[hf] = *reinterpret_cast<const uint4*>(gv + oo);
+            R.dO[hf] = *reinterpret_cast<const uint4*>(gdo + oo);
+        }
+    };
+    auto angles = [&](int step, float2* cs) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float2 t = sm.rope[step & 1][8 * fg + u];
+            cs[u] = make_float2(t.x * rot[u].x - t.y * rot[u].y, t.y * rot[u].x + t.x * rot[u].y);
+        }
+    };
+    auto norm_rotate = [&](float* x, const float* w, const float2* cs, float scale) __attribute__((always_inline)) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ss = fmaf(x[e], x[e], ss);
+        ss = group_sum<TPR>(ss);
+        const float rinv = fast_rsqrt(ss * (1.0f / D) + p.eps);
+        const float sc = rinv * scale;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float a = x[u] * sc * w[8 * fg + u], c = x[8 + u] * sc * w[HALF + 8 * fg + u];
+            x[u] = a * cs[u].x - c * cs[u].y;
+            x[8 + u] = c * cs[u].x + a * cs[u].y;
+        }
+        return rinv;
+    };
+    auto st16 = [&](__bf16* tile, const float* x, bool valid) __attribute__((always_inline)) {
+        const uint4 lo = valid ? pack8(x) : make_uint4(0, 0, 0, 0);
+        const uint4 hi = valid ? pack8(x + 8) : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(tile + swz<D>(rr, 8 * fg)) = lo;
+        *reinterpret_cast<uint4*>(tile + swz<D>(rr, HALF + 8 * fg)) = hi;
+    };
+    const float kscale = 1.0f / sqrtf((float)D);
+    auto st16_split = [&](__bf16* hi, __bf16* lo, const float* x, bool valid) __attribute__((always_inline)) {
+        uint4 h0, l0, h1, l1;
+        split8(x, h0, l0);
+        split8(x + 8, h1, l1);
+        *reinterpret_cast<uint4*>(hi + swz<D>(rr, 8 * fg)) = keep_if(valid, h0);
+        *reinterpret_cast<uint4*>(hi + swz<D>(rr, HALF + 8 * fg)) = keep_if(valid, h1);
+        *reinterpret_cast<uint4*>(lo + swz<D>(rr, 8 * fg)) = keep_if(valid, l0);
+        *reinterpret_cast<uint4*>(lo + swz<D>(rr, HALF + 8 * fg)) = keep_if(valid, l1);
+    };
+
+    auto step = [&](int i, Regs& R, Regs& Rn) __attribute__((always_inline)) {
+        const int c = chunk_of(i);
+        const int t0 = t_begin + c * C;
+        const int n = min(C, t_end - t0);
+        const bool valid = rr < n;
+        // ---- P1: q~, k~, v, do tiles and the state-gradient copy; prefetch ----
+        float2 cs[8];
+        angles(i, cs);
+        float x[16];
+        widen8(R.q[0], x);
+        widen8(R.q[1], x + 8);
+        norm_rotate(x, sm.w[0], cs, 1.0f);
+        st16_split(sm.q, sm.q_lo, x, valid);
+        widen8(R.k[0], x);
+        widen8(R.k[1], x + 8);
+        const float rk = norm_rotate(x, sm.w[1], cs, kscale);
+        st16_split(sm.k, sm.k_lo, x, valid);
+        // (value selects: a conditional between two lvalues would select addresses, in memory)
+        *reinterpret_cast<uint4*>(sm.v + swz<D>(rr, 8 * fg)) = keep_if(valid, R.v[0]);
+        *reinterpret_cast<uint4*>(sm.v + swz<D>(rr, HALF + 8 * fg)) = keep_if(valid, R.v[1]);
+        *reinterpret_cast<uint4*>(sm.dO + swz<D>(rr, 8 * fg)) = keep_if(valid, R.dO[0]);
+        *reinterpret_cast<uint4*>(sm.dO + swz<D>(rr, HALF + 8 * fg)) = keep_if(valid, R.dO[1]);
+#pragma unroll
+        for (int cc = 0; cc < NW; ++cc)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const uint2 pk = make_uint2(pack_bf16x2(dS[cc][4 * g4], dS[cc][4 * g4 + 1]),
+                                            pack_bf16x2(dS[cc][4 * g4 + 2], dS[cc][4 * g4 + 3]));
+                *reinterpret_cast<uint2*>(sm.st + swz<D>(32 * wave + lm, 32 * cc + 8 * g4 + 4 * lh)) = pk;
+            }
+        if (c > 0) load(c - 1, Rn);
+        __syncthreads();
+        // ---- P2: dv (value columns of w), dk~ (key columns of w), then the dS update ----
+        if (wave == 0 && c > 0) fill_table(i + 1);
+        const float* dl = sm.dec[lane];
+        float mk[16], rd[16];
+        load16(dl, mk);
+        if (n == C) {
+            load16(dl + 32, rd);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int j = acc_row(r, lh);
+                rd[r] = j < n ? pow_lambda(l2l, n - 1 - j) : 0.0f;
+            }
+        }
+        {
+            // P[i][j] = q~_i . k~_j and dP[i][j] = do_i . v_j with lane j, both masked by D.  P
+            // takes the hi/lo parts of q~ and k~ (and P V those of P): do_i is large where o_i
+            // is small, and there dv_j = sum_i P_ij do_i must not inherit bf16 score rounding.
+            f32x16 pm = {}, dpm = {}, dvv = {}, dkt = {};
+#pragma unroll
+            for (int s8 = 0; s8 < D / 16; ++s8) {
+                const bf16x8 qh = row8<D>(sm.q, lm, 16 * s8 + 8 * lh);
+                const bf16x8 kh = row8<D>(sm.k, lm, 16 * s8 + 8 * lh);
+                pm = mfma_bf16(qh, kh, pm);
+                pm = mfma_bf16(qh, row8<D>(sm.k_lo, lm, 16 * s8 + 8 * lh), pm);
+                pm = mfma_bf16(row8<D>(sm.q_lo, lm, 16 * s8 + 8 * lh), kh, pm);
+                const bf16x8 vr = row8<D>(sm.v, lm, 16 * s8 + 8 * lh);
+                dpm = mfma_bf16(row8<D>(sm.dO, lm, 16 * s8 + 8 * lh), vr, dpm);
+                // inter terms: K~ dS (value columns of w) and V dS^T (key columns of w)
+                dvv = mfma_bf16(row_acc<D>(sm.k, lm, s8, lh), acc_operand(dS[s8 / 2], s8 % 2), dvv);
+                dkt = mfma_bf16(vr, tr_nat<D>(sm.st, 16 * s8, 32 * wave, lane), dkt);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                pm[r] *= mk[r];
+                dpm[r] *= mk[r];
+                dvv[r] *= rd[r];
+                dkt[r] *= rd[r];
+            }
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                bf16x8 ph, pl;
+                acc_split(pm, st, ph, pl);
+                const bf16x8 db = tr_acc<D>(sm.dO, 16 * st, 32 * wave, lane);
+                dvv = mfma_bf16(ph, db, dvv);
+                dvv = mfma_bf16(pl, db, dvv);
+                dkt = mfma_bf16(acc_operand(dpm, st), tr_acc<D>(sm.q, 16 * st, 32 * wave, lane), dkt);
+            }
+            uint16_t* pdv = static_cast<uint16_t*>(p.dv) + base + (size_t)t0 * rs + 32 * wave + lm;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int j = acc_row(r, lh);
+                if (j < n) pdv[(size_t)j * rs] = to_bf16_bits(dvv[r]);
+                sm.stage[j * OS + 32 * wave + lm] = dkt[r];
+            }
+        }
+        {
+            // dS <- lambda^n dS + sum_i q~_i^T lambda^(i+1) do_i
+            float rf[16];
+            load16(dl + 16, rf);
+            const float ln = pow_lambda(l2l, n);
+#pragma unroll
+            for (int cc = 0; cc < NW; ++cc)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dS[cc][r] *= ln;
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const bf16x8 db = scale8(tr_acc<D>(sm.dO, 16 * st, 32 * wave, lane), rf + 8 * st, 1.0f);
+#pragma unroll
+                for (int cc = 0; cc < NW; ++cc)
+                    dS[cc] = mfma_bf16(tr_acc<D>(sm.q, 16 * st, 32 * cc, lane), db, dS[cc]);
+            }
+        }
+        __syncthreads();
+        // ---- P3: dk = QK-norm^T(RoPE^T(dk~) / sqrt(d)) ----
+        {
+            angles(i, cs);
+            float dkt[16];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const float* src = sm.stage + rr * OS + hf * HALF + 8 * fg;
+                const float4 a = reinterpret_cast<const float4*>(src)[0];
+                const float4 bq = reinterpret_cast<const float4*>(src)[1];
+                dkt[8 * hf + 0] = a.x; dkt[8 * hf + 1] = a.y; dkt[8 * hf + 2] = a.z; dkt[8 * hf + 3] = a.w;
+                dkt[8 * hf + 4] = bq.x; dkt[8 * hf + 5] = bq.y; dkt[8 * hf + 6] = bq.z; dkt[8 * hf + 7] = bq.w;
+            }
+            widen8(R.k[0], x);
+            widen8(R.k[1], x + 8);
+            float dx[16], dot = 0.0f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float lo = (cs[u].x * dkt[u] + cs[u].y * dkt[8 + u]) * kscale;
+                const float hi = (cs[u].x * dkt[8 + u] - cs[u].y * dkt[u]) * kscale;
+                const float xl = x[u] * rk, xh = x[8 + u] * rk;
+                if (valid) {
+                    wacc_k[u] = fmaf(lo, xl, wacc_k[u]);
+                    wacc_k[8 + u] = fmaf(hi, xh, wacc_k[8 + u]);
+                }
+                dx[u] = lo * sm.w[1][8 * fg + u];
+                dx[8 + u] = hi * sm.w[1][HALF + 8 * fg + u];
+                x[u] = xl;
+                x[8 + u] = xh;
+                dot = fmaf(dx[u], xl, dot);
+                dot = fmaf(dx[8 + u], xh, dot);
+            }
+            dot = group_sum<TPR>(dot) * (1.0f / D);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) dx[e] = rk * (dx[e] - x[e] * dot);
+            if (valid) {
+                uint16_t* pdk = static_cast<uint16_t*>(p.dk) + base + (size_t)(t0 + rr) * rs + 8 * fg;
+                *reinterpret_cast<uint4*>(pdk) = pack8(dx);
+                *reinterpret_cast<uint4*>(pdk + HALF) = pack8(dx + 8);
+            }
+        }
+    };
+
+    Regs cur;
+    load(n_chunks - 1, cur);
+    __syncthreads();
+    for (int i = 0; i < n_chunks; ++i) {
+        Regs nxt = cur;
+        step(i, cur, nxt);
+        cur = nxt;
+    }
+    if (p.wgrad) {
+        const size_t nbp = (size_t)p.B * p.H * p.P;
+        __syncthreads();
+        for (int f = threadIdx.x; f < D; f += G::NT) {
+            const int tf = (f % HALF) / 8, e = (f >= HALF ? 8 : 0) + (f & 7);
+            float s = 0.0f;
+            for (int r = 0; r < C; ++r) s += sm.wacc[0][r * TPR + tf][e];
+            p.wgrad[(nbp + (size_t)bh * p.P + seg) * D + f] = s;
+        }
+    }
+}
+
+// Norm-weight gradients: the sum of the partials over batch rows and segments (and heads when
+// the weights are shared, w_stride == 0).  One thread per (weight, head row, feature).
+__global__ void __launch_bounds__(256) bwd_wgrad_kernel(const BwdParams p, int d) {
+    const int rows = p.w_stride ? p.H : 1;
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= 3 * rows * d) return;
+    const int which = idx / (rows * d);
+    const int hr = (idx / d) % rows, f = idx % d;
+    if (!(which == 0 ? p.dqw : which == 1 ? p.dkw : p.dow)) return;
+    const size_t nbp = (size_t)p.B * p.H * p.P;
+    float s = 0.0f;
+    for (int b = 0; b < p.B; ++b)
+        for (int h = (p.w_stride ? hr : 0); h < (p.w_stride ? hr + 1 : p.H); ++h)
+            for (int sg = 0; sg < p.P; ++sg)
+                s += p.wgrad[((size_t)which * nbp + ((size_t)b * p.H + h) * p.P + sg) * d + f];
+    float* out = which == 0 ? p.dqw : which == 1 ? p.dkw : p.dow;
+    if (out) out[(size_t)hr * d + f] = s;
+}
+
+}  // namespace
+
+hipError_t launch_prefill_backward(const BwdParams& p, const ChunkParams& fwd_cp,
+                                   const ScanParams& fwd_sp, const hipEvent_t ev[4],
+                                   hipStream_t stream) {
+    constexpr int D = 128;
+    const int BH = p.B * p.H;
+    hipError_t err;
+    if (p.P > 1 && (err = launch_prefill_states(fwd_cp, fwd_sp, D, LT_BF16, stream)) != hipSuccess)
+        return err;
+    if (ev[0] && (err = hipEventRecord(ev[0], stream)) != hipSuccess) return err;
+    bwd_dq_kernel<D><<<dim3(BH * p.P), dim3(BCfg<D>::NT), 0, stream>>>(p);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (ev[1] && (err = hipEventRecord(ev[1], stream)) != hipSuccess) return err;
+    const size_t n = (size_t)BH * D * D;
+    bwd_scan_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(p, D * D);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (ev[2] && (err = hipEventRecord(ev[2], stream)) != hipSuccess) return err;
+    bwd_dkv_kernel<D><<<dim3(BH * p.P), dim3(BCfg<D>::NT), 0, stream>>>(p);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (ev[3] && (err = hipEventRecord(ev[3], stream)) != hipSuccess) return err;
+    if (p.wgrad) {
+        const int m = 3 * (p.w_stride ? p.H : 1) * D;
+        bwd_wgrad_kernel<<<dim3((m + 255) / 256), dim3(256), 0, stream>>>(p, D);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    return hipSuccess;
+}
+
+}  // namespace lt

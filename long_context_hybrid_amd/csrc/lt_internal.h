@@ -80,6 +80,44 @@ struct DecodeParams {
     const float* log2_decay;  // time-dependent step: [B][H] log2(alpha) of this token
 };
 
+// Backward of the fixed-decay prefill (bf16, d = 128).  The sequence of each (b, h) is cut into
+// P segments of L tokens (the last one shorter); the forward pass's entry state of segment s is
+// slot s * SM of fwd_states (the state-only pass and scan of launch_prefill_states) when P > 1,
+// else state_in.
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const void* dy;
+    const float* qw;
+    const float* kw;
+    const float* ow;           // may be null (ones)
+    const float* state_in;     // may be null (zeros)
+    const float* fwd_states;   // [B][H][SP][d][d] when P > 1
+    const float* d_state_out;  // may be null (zeros)
+    void* dq;
+    void* dk;
+    void* dv;
+    void* dg;
+    float* d_state_in;         // may be null
+    uint16_t* d_o;             // [B][T][H][d] bf16: dL/do, written by the first sweep
+    float* seg_grad;           // [B][H][P][d][d]: each segment's own dL/d(entry state), then
+                               // (after the scan) dL/d(state after the segment)
+    float* wgrad;              // [3][B][H][P][d] norm-weight partials (q, k, o), or null
+    float* dqw;                // norm-weight gradients (null when wgrad is null)
+    float* dkw;
+    float* dow;
+    int64_t pos0;
+    int B, T, H, P, L, SM, SP;
+    int w_stride;
+    float eps;
+    float log2_lambda[LT_MAX_HEADS];
+    float lambda_pow_seg[LT_MAX_HEADS];   // lambda_h^L
+    float lambda_pow_last[LT_MAX_HEADS];  // lambda_h^(T - (P - 1) L)
+    double inv_freq_rev[64];
+};
+
 // HyPE attention prefill.  qs / ks are the prologue's outputs (ks == k when the keys are used
 // as given); everything else is as passed to lightning_attn_prefill.
 constexpr int kAttnHeadDim = 128;
@@ -131,6 +169,14 @@ constexpr int kAttnDecodeMaxB = 64;  // batch rows of one decode call (lengths t
 // time_dep: the data-dependent-decay kernels (cp.log2_decay / dp.log2_decay set).
 hipError_t launch_prefill(const ChunkParams& cp, const ScanParams& sp, int d, int dtype,
                           const hipEvent_t events[2], hipStream_t stream, bool time_dep = false);
+// The state-only pass and segment scan of launch_prefill alone: ws slot p * SM receives the
+// entry state of segment p (cp.P > 1).
+hipError_t launch_prefill_states(const ChunkParams& cp, const ScanParams& sp, int d, int dtype,
+                                 hipStream_t stream);
+// events (may be null): [0]/[1] bracket the first (dq) sweep, [2]/[3] the second (dk, dv).
+hipError_t launch_prefill_backward(const BwdParams& p, const ChunkParams& fwd_cp,
+                                   const ScanParams& fwd_sp, const hipEvent_t events[4],
+                                   hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& dp, int d, int dtype, hipStream_t stream,
                          bool time_dep = false);
 hipError_t launch_state_init(float* state, const float* init, size_t n, hipStream_t stream);

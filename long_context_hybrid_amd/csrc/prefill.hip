@@ -971,15 +971,19 @@ __global__ void __launch_bounds__(256) segment_scan_kernel(const ScanParams p) {
 }
 
 template <class M, int D, bool kTD>
+void launch_states_typed(const ChunkParams& cp, const ScanParams& sp, hipStream_t stream) {
+    const int BH = cp.B * cp.H;
+    constexpr int NT = Cfg<M, D, true>::NT;
+    chunk_kernel<M, D, true, kPrefetchStateOnly, kTD><<<dim3(BH * (cp.SP - 1)), dim3(NT), 0, stream>>>(cp);
+    const size_t n = (size_t)BH * D * D;
+    segment_scan_kernel<kTD><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(sp);
+}
+
+template <class M, int D, bool kTD>
 hipError_t launch_typed(const ChunkParams& cp, const ScanParams& sp, const hipEvent_t ev[2],
                         hipStream_t stream) {
     const int BH = cp.B * cp.H;
-    if (cp.P > 1) {
-        constexpr int NT = Cfg<M, D, true>::NT;
-        chunk_kernel<M, D, true, kPrefetchStateOnly, kTD><<<dim3(BH * (cp.SP - 1)), dim3(NT), 0, stream>>>(cp);
-        const size_t n = (size_t)BH * D * D;
-        segment_scan_kernel<kTD><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(sp);
-    }
+    if (cp.P > 1) launch_states_typed<M, D, kTD>(cp, sp, stream);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (ev[0] && (err = hipEventRecord(ev[0], stream)) != hipSuccess) return err;
@@ -1001,6 +1005,20 @@ hipError_t launch_mode(const ChunkParams& cp, const ScanParams& sp, int d, int d
 }
 
 }  // namespace
+
+hipError_t launch_prefill_states(const ChunkParams& cp, const ScanParams& sp, int d, int dtype,
+                                 hipStream_t stream) {
+    if (cp.P > 1) {
+        if (dtype == LT_BF16) {
+            if (d == 128) launch_states_typed<ModeBF16, 128, false>(cp, sp, stream);
+            else launch_states_typed<ModeBF16, 64, false>(cp, sp, stream);
+        } else {
+            if (d == 128) launch_states_typed<ModeF32, 128, false>(cp, sp, stream);
+            else launch_states_typed<ModeF32, 64, false>(cp, sp, stream);
+        }
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_prefill(const ChunkParams& cp, const ScanParams& sp, int d, int dtype,
                           const hipEvent_t ev[2], hipStream_t stream, bool time_dep) {

@@ -31,6 +31,8 @@ EXPORTS = (
     "lightning_prefill_dd_workspace_size",
     "lightning_prefill_dd",
     "lightning_decode_step_dd",
+    "lightning_prefill_backward_workspace_size",
+    "lightning_prefill_backward",
     "lightning_layer_prefill_workspace_size",
     "lightning_layer_prefill",
     "lightning_layer_decode_workspace_size",
@@ -75,6 +77,14 @@ def _load() -> ct.CDLL:
     h.lightning_prefill_dd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, f64, f64, i64, vp, vp,
                                        vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp, vp]
     h.lightning_prefill_dd.restype = i32
+    h.lightning_prefill_backward_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    h.lightning_prefill_backward_workspace_size.restype = sz
+    # q k v gate qw kw ow stride lambda base eps pos0 state_in dy d_state_out dq dk dv dgate
+    # d_state_in dqw dkw dow B T H d dtype segments workspace bytes events stream
+    h.lightning_prefill_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, f64, f64, i64,
+                                             vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
+                                             i32, i32, i32, i32, vp, sz, vp, vp]
+    h.lightning_prefill_backward.restype = i32
     h.lightning_decode_step_dd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, f64, f64, vp, vp,
                                            vp, vp, vp, i32, i32, i32, i32, vp]
     h.lightning_decode_step_dd.restype = i32
@@ -512,3 +522,48 @@ def lightning_decode_step_dd(q, k, v, gate, q_norm_w, k_norm_w, log2_decay, rope
                                       _stream(stream, dev))
     _check(st, "lightning_decode_step_dd")
     return y
+
+
+def lightning_prefill_backward_workspace_size(B, T, H, d, dtype=torch.bfloat16, segments=0) -> int:
+    return int(lib.lightning_prefill_backward_workspace_size(B, T, H, d, _dtype_code(dtype),
+                                                             segments))
+
+
+def lightning_prefill_backward(q, k, v, gate, q_norm_w, k_norm_w, lambdas, rope_base, dy,
+                               rms_eps=1e-6, pos0=0, state_in=None, d_state_out=None,
+                               o_norm_w=None, want_state_grad=True, want_weight_grads=True,
+                               segments=0, workspace=None, kernel_events=None, stream=None):
+    """Gradients of sum(dy * y) + sum(d_state_out * state_out) for lightning_prefill on the same
+    inputs.  Returns a dict: dq, dk, dv, dgate (like q), d_state_in [B, H, d, d] fp32 (with
+    ``want_state_grad``) and d_q_norm_w, d_k_norm_w, d_o_norm_w (with ``want_weight_grads``;
+    shaped like the weights, d_o_norm_w also when o_norm_w is None)."""
+    B, T, H, d = q.shape
+    dev = q.device
+    dt = _dtype_code(q.dtype)
+    act = dict(dtype=q.dtype, shape=q.shape, device=dev)
+    ptrs = [_dev(t, n, **act) for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"))]
+    (qwp, kwp, owp), stride = _norm_weights(q_norm_w, k_norm_w, o_norm_w, H, d, dev)
+    out = {n: torch.empty_like(q) for n in ("dq", "dk", "dv", "dgate")}
+    sshape = (B, H, d, d)
+    if want_state_grad:
+        out["d_state_in"] = torch.empty(sshape, dtype=torch.float32, device=dev)
+    wshape = (H, d) if stride else (d,)
+    if want_weight_grads:
+        for n in ("d_q_norm_w", "d_k_norm_w", "d_o_norm_w"):
+            out[n] = torch.empty(wshape, dtype=torch.float32, device=dev)
+    need = lightning_prefill_backward_workspace_size(B, T, H, d, q.dtype, segments)
+    workspace, wsp, wbytes = _workspace(workspace, need, dev)
+    evp = None
+    if kernel_events is not None:
+        evp = (ct.c_void_p * 4)(*(ct.c_void_p(int(e)) for e in kernel_events))
+    st = lib.lightning_prefill_backward(
+        *ptrs, qwp, kwp, owp, stride, _lambda_array(lambdas, H), float(rope_base),
+        float(rms_eps), int(pos0), _dev(state_in, "state_in", torch.float32, sshape, dev),
+        _dev(dy, "dy", **act), _dev(d_state_out, "d_state_out", torch.float32, sshape, dev),
+        *(_dev(out[n], n, **act) for n in ("dq", "dk", "dv", "dgate")),
+        _dev(out.get("d_state_in"), "d_state_in", torch.float32, sshape, dev),
+        *(_dev(out.get(n), n, torch.float32, wshape, dev)
+          for n in ("d_q_norm_w", "d_k_norm_w", "d_o_norm_w")),
+        B, T, H, d, dt, int(segments), wsp, wbytes, evp, _stream(stream, dev))
+    _check(st, "lightning_prefill_backward")
+    return out

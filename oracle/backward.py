@@ -119,8 +119,8 @@ def prefill_backward(q, k, v, g, dy, qw, kw, lambdas, rope_base, eps=1e-6, pos0=
     d_state_in [n, d, d], and each pair's contribution to the norm-weight gradients dqw, dkw,
     dow [n, d] (sum them over the pairs that share a weight row).  All fp64.
     """
-    qf, kf, vf, gf, dyf = (widen(x) for x in (q, k, v, g, dy))
-    B, T, H, d = qf.shape
+    q, k, v, g, dy = (np.asarray(x) for x in (q, k, v, g, dy))
+    B, T, H, d = q.shape
     lam = np.asarray(lambdas, dtype=np.float64)
     if slices is None:
         slices = [(b, h) for b in range(B) for h in range(H)]
@@ -133,18 +133,19 @@ def prefill_backward(q, k, v, g, dy, qw, kw, lambdas, rope_base, eps=1e-6, pos0=
     ks = 1.0 / math.sqrt(d)
     for i, (b, h) in enumerate(slices):
         wq, wk, wo = _wrow(qw, h, d), _wrow(kw, h, d), _wrow(ow, h, d)
-        xq, rq = _norm_rows(qf[b, :, h], eps)
-        xk, rk = _norm_rows(kf[b, :, h], eps)
+        # inputs are widened one (b, h) slice at a time
+        xq, rq = _norm_rows(widen(q[b, :, h]), eps)
+        xk, rk = _norm_rows(widen(k[b, :, h]), eps)
         qt = _rotate_rows(xq * wq, pos, rope_base)
         kt = _rotate_rows(xk * wk, pos, rope_base) * ks
-        vv = vf[b, :, h]
+        vv = widen(v[b, :, h])
         S0 = None if state_in is None else state_in[b, h]
         o, _ = core_forward(qt, kt, vv, lam[h], S0)
         # output gate and norm
         ro = 1.0 / np.sqrt(np.mean(o * o, axis=1) + eps)
         nrm = o * ro[:, None]
-        s = _sigmoid(gf[b, :, h])
-        dyb = dyf[b, :, h]
+        s = _sigmoid(widen(g[b, :, h]))
+        dyb = widen(dy[b, :, h])
         out["dg"][i] = dyb * nrm * wo * s * (1.0 - s)
         out["dow"][i] = np.sum(dyb * nrm * s, axis=0)
         do = _norm_backward(dyb * wo * s, nrm, ro)

@@ -133,6 +133,12 @@ ATTN_QWEN17_512K = dataclasses.replace(
     name="HyPE attention layer (Qwen3-1.7B shape) B=1 T=524288 Hq=16 Hkv=8 d=128 bf16, a=500",
     T=524288, seed=1008)
 
+# Training shape of the mixer's backward: HALO's long-context stage trains at 16K tokens
+# (Section 4.5, Appendix B); the per-device micro-batch is not given, 8 sequences are taken here.
+BWD_QWEN17_16K = PrefillSpec(
+    "Qwen3-1.7B-shaped RNN layer backward B=8 H=16 T=16384 d=128 bf16 (16K training context)",
+    8, 16384, 16, 128, torch.bfloat16, tuple(qwen_lambdas(16)), 1e6, "uniform", "zeros", 0, 1009)
+
 WORKLOADS = {
     "tiny": TINY,
     "qwen17_32k": QWEN17_32K,
@@ -143,6 +149,7 @@ WORKLOADS = {
     "layer_decode_b64": LAYER_DECODE_B64,
     "attn_qwen17_32k": ATTN_QWEN17_32K,
     "attn_qwen17_512k": ATTN_QWEN17_512K,
+    "bwd_qwen17_16k": BWD_QWEN17_16K,
 }
 
 
@@ -181,6 +188,27 @@ def make_prefill(spec: PrefillSpec, device="cpu", T: int | None = None) -> dict:
     return dict(q=q, k=k, v=v, g=g, qw=qw, kw=kw, ow=None, lambdas=list(spec.lambdas),
                 rope_base=spec.rope_base, eps=spec.eps, pos0=spec.pos0, state_in=state,
                 B=B, T=T, H=H, d=d, dtype=spec.dtype, chunk=spec.chunk)
+
+
+def make_backward(spec: PrefillSpec, device="cpu", T: int | None = None, B: int | None = None,
+                  d_state_out: bool = False) -> dict:
+    """A prefill batch (as make_prefill) plus the upstream gradients of the backward: dy ~ N(0, 1)
+    in the activations' dtype and, with ``d_state_out``, a 0.01 N(0, 1) fp32 gradient of the final
+    state (else None).  ``B`` keeps the first B rows of the spec's batch."""
+    out = make_prefill(spec, device, T)
+    if B is not None and B != out["B"]:
+        for n in ("q", "k", "v", "g"):
+            out[n] = out[n][:B].contiguous()
+        if out["state_in"] is not None:
+            out["state_in"] = out["state_in"][:B].contiguous()
+        out["B"] = B
+    gen = _gen(spec.seed + 500, device)
+    out["dy"] = _randn(out["q"].shape, gen, device, spec.dtype)
+    out["d_state_out"] = None
+    if d_state_out:
+        out["d_state_out"] = _randn((out["B"], out["H"], out["d"], out["d"]), gen, device,
+                                    torch.float32, 0.01)
+    return out
 
 
 def make_decode(spec: DecodeSpec, device="cpu", B: int | None = None) -> dict:

@@ -385,3 +385,66 @@ def test_prefill_dd_rejects(name, over, status):
                                      a["d"], a["dt"], a["chunk"], a["seg"], a["ws"], a["wsb"],
                                      a["ev"], a["stream"])
     assert st == status
+
+
+# ---- prefill backward ----------------------------------------------------------------------------
+
+def test_backward_workspace_layout():
+    B, T, H, d = 8, 16384, 16, 128
+    ws = lt.lightning_prefill_backward_workspace_size(B, T, H, d)
+    # at least: do (bf16, one activation tensor) + one d x d state gradient per (b, h, segment)
+    assert ws >= B * T * H * d * 2 + B * H * d * d * 4
+    assert ws % 4 == 0
+    # unsupported shapes report 0
+    assert lt.lightning_prefill_backward_workspace_size(B, T, H, 64) == 0
+    assert lt.lightning_prefill_backward_workspace_size(B, T, H, d, torch.float32) == 0
+    # one segment (B H fills the CUs): no forward state slots, one gradient per (b, h)
+    one = lt.lightning_prefill_backward_workspace_size(16, 256, 16, d)
+    do_bytes = 16 * 256 * 16 * d * 2
+    assert one >= do_bytes + 16 * 16 * d * d * 4
+    assert one < do_bytes + 16 * 16 * d * d * 4 + 3 * 16 * 16 * d * 4 + 1024
+
+
+def _bwd_args(**over):
+    H = over.pop("H", 2)
+    lam = over.pop("lam", [0.9] * H)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, qw=FAKE, kw=FAKE, ow=None, stride=128,
+             lam=(ct.c_double * len(lam))(*lam), base=1e6, eps=1e-6, pos0=0, sin=None, dy=FAKE,
+             dso=None, dq=FAKE, dk=FAKE, dv=FAKE, dg=FAKE, dsi=None, dqw=None, dkw=None, dow=None,
+             B=1, T=256, H=H, d=128, dt=lt.LT_BF16, seg=0, ws=FAKE, wsb=1 << 40, ev=None,
+             stream=None)
+    a.update(over)
+    return a
+
+
+BWD_BAD = [
+    ("null_dy", dict(dy=None), lt.LT_ERR_INVALID_ARG),
+    ("null_dq", dict(dq=None), lt.LT_ERR_INVALID_ARG),
+    ("null_dgate", dict(dg=None), lt.LT_ERR_INVALID_ARG),
+    ("misaligned_dk", dict(dk=FAKE + 2), lt.LT_ERR_INVALID_ARG),
+    ("misaligned_d_state_out", dict(dso=FAKE + 4), lt.LT_ERR_INVALID_ARG),
+    ("misaligned_weight_grad", dict(dkw=FAKE + 4), lt.LT_ERR_INVALID_ARG),
+    ("null_qnorm", dict(qw=None), lt.LT_ERR_INVALID_ARG),
+    ("lambda_above_one", dict(lam=[0.9, 1.5]), lt.LT_ERR_INVALID_ARG),
+    ("zero_T", dict(T=0), lt.LT_ERR_INVALID_ARG),
+    ("negative_segments", dict(seg=-1), lt.LT_ERR_INVALID_ARG),
+    ("pos0_negative", dict(pos0=-3), lt.LT_ERR_INVALID_ARG),
+    ("fp32", dict(dt=lt.LT_F32), lt.LT_ERR_UNSUPPORTED),
+    ("d_64", dict(d=64, stride=64), lt.LT_ERR_UNSUPPORTED),
+    ("workspace_missing", dict(ws=None), lt.LT_ERR_WORKSPACE),
+    ("workspace_small", dict(wsb=1024), lt.LT_ERR_WORKSPACE),
+    ("events_null_entries", dict(ev=(ct.c_void_p * 4)(None, None, None, None)),
+     lt.LT_ERR_INVALID_ARG),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,over,status", BWD_BAD, ids=[c[0] for c in BWD_BAD])
+def test_prefill_backward_rejects(name, over, status):
+    a = _bwd_args(**over)
+    st = lt.lib.lightning_prefill_backward(
+        a["q"], a["k"], a["v"], a["g"], a["qw"], a["kw"], a["ow"], a["stride"], a["lam"],
+        a["base"], a["eps"], a["pos0"], a["sin"], a["dy"], a["dso"], a["dq"], a["dk"], a["dv"],
+        a["dg"], a["dsi"], a["dqw"], a["dkw"], a["dow"], a["B"], a["T"], a["H"], a["d"], a["dt"],
+        a["seg"], a["ws"], a["wsb"], a["ev"], a["stream"])
+    assert st == status
