@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--attn-warmup", type=int, default=1)
     ap.add_argument("--cpu-attn-rows", type=int, default=32)
     ap.add_argument("--attn-decode-steps", type=int, default=50)
+    ap.add_argument("--no-backward", action="store_true", help="skip the prefill-backward leg")
+    ap.add_argument("--bwd-steps", type=int, default=5)
+    ap.add_argument("--cpu-bwd-slices", type=int, default=2)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed runs, copy this many MiB device to device three times "
                          "(a plain copy of known size that calibrates HBM byte counters)")
@@ -490,6 +493,105 @@ def bench_attn_decode(args, torch, lt, synth):
                          "alg_bytes_per_step": alg}}
 
 
+def backward_segments(B, T, H, C=32, cus=256, min_chunks=8):
+    """The segment count lightning_prefill_backward chooses (segments = 0): B H P workgroups
+    fill the CUs once, every segment keeps at least 8 chunks."""
+    n_chunks = -(-T // C)
+    P = max(1, min(-(-cus // (B * H)), n_chunks // min_chunks))
+    cps = -(-n_chunks // P)
+    return -(-n_chunks // cps)
+
+
+def bench_backward(args, torch, lt, synth):
+    """The backward of the mixer prefill at the 16K training shape (B = 8, H = 16): dq, dk, dv,
+    dgate, d_state_in and the three norm-weight gradients from dL/dy.  The two chunk sweeps are
+    timed by HIP events on the call's stream."""
+    spec = synth.BWD_QWEN17_16K
+    dev = torch.device("cuda:0")
+    inp = synth.make_backward(spec, device=dev)
+    B, T, H, d = inp["B"], inp["T"], inp["H"], inp["d"]
+    ws = torch.empty(lt.lightning_prefill_backward_workspace_size(B, T, H, d), dtype=torch.uint8,
+                     device=dev)
+    call = (inp["q"], inp["k"], inp["v"], inp["g"], inp["qw"], inp["kw"], inp["lambdas"],
+            inp["rope_base"], inp["dy"])
+    kw = dict(rms_eps=inp["eps"], workspace=ws)
+    for _ in range(args.warmup):
+        lt.lightning_prefill_backward(*call, **kw)
+    torch.cuda.synchronize()
+    hev = HipEvents()
+    ev = hev.create(4 * args.bwd_steps)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.bwd_steps):
+        lt.lightning_prefill_backward(*call, **kw, kernel_events=ev[4 * i:4 * i + 4])
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.bwd_steps
+    n = args.bwd_steps
+    dq_ms = sum(hev.elapsed_ms(ev[4 * i], ev[4 * i + 1]) for i in range(n)) / n
+    dkv_ms = sum(hev.elapsed_ms(ev[4 * i + 2], ev[4 * i + 3]) for i in range(n)) / n
+    hev.destroy(ev)
+    P = backward_segments(B, T, H)
+    units = B * T * H
+    wgs = B * H * P
+    st = d * d * 4
+    # dq sweep: reads q, k, v, gate, dy; writes dq, dgate, do (bf16); entry state in, W out
+    alg_dq = units * 8 * d * 2 + wgs * 2 * st
+    # dk/dv sweep: reads q, k, v, do; writes dk, dv; the segment's end-state gradient in
+    alg_dkv = units * 6 * d * 2 + wgs * st
+    C = 32
+    # useful MFMA flops per token-head: dq sweep 4 C d + 4 d^2 multiply-adds (scores, P V, do V^T,
+    # dP K~; q~ S, do S^T, W, S update), dk/dv sweep 4 C d + 3 d^2
+    fl_dq = units * 2 * (4 * C * d + 4 * d * d)
+    fl_dkv = units * 2 * (4 * C * d + 3 * d * d)
+    legs = {"dq_sweep": (dq_ms, alg_dq, fl_dq, "bwd_dq_kernel<128> (forward-in-time sweep)"),
+            "dkv_sweep": (dkv_ms, alg_dkv, fl_dkv, "bwd_dkv_kernel<128> (backward-in-time sweep)")}
+    dom = max(legs, key=lambda k: legs[k][0])
+    kms, alg, fl, kname = legs[dom]
+    gbs = alg / (kms * 1e-3) / 1e9
+    out = {"workload": spec.name, "ms_per_step": round(ms, 4),
+           "value": round(B * T / (ms * 1e-3), 1), "unit": "tokens/s/layer",
+           "steps": args.bwd_steps, "segments": P,
+           "stages_ms": {"dq_sweep": round(dq_ms, 4), "dkv_sweep": round(dkv_ms, 4),
+                         "rest": round(ms - dq_ms - dkv_ms, 4)},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                        "kernel": kname, "alg_bytes_per_launch": alg, "launch_ms": round(kms, 4)},
+           "sweeps": {k: {"ms": round(v[0], 4), "alg_bytes": v[1],
+                          "achieved_gbs": round(v[1] / (v[0] * 1e-3) / 1e9, 1),
+                          "useful_tflops": round(v[2] / (v[0] * 1e-3) / 1e12, 1)}
+                      for k, v in legs.items()},
+           "whole_call": {"alg_bytes": alg_dq + alg_dkv,
+                          "hbm_frac": round((alg_dq + alg_dkv) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+    return out
+
+
+def cpu_baseline_backward(args, torch, synth):
+    """The gradient oracle (fp64 numpy, token by token) on whole (b, h) slices of the 16K
+    training-shape backward workload."""
+    import numpy as np
+
+    from oracle import backward as ob
+
+    spec = synth.BWD_QWEN17_16K
+    inp = synth.make_backward(spec, device="cuda:0")
+    n = args.cpu_bwd_slices
+    slices = [(b, 0) for b in range(n)]
+    host = {k: synth.host_bits(inp[k][:n, :, :1].cpu()) for k in ("q", "k", "v", "g", "dy")}
+    t0 = time.perf_counter()
+    r = ob.prefill_backward(host["q"], host["k"], host["v"], host["g"], host["dy"],
+                            inp["qw"][:1].cpu().numpy(), inp["kw"][:1].cpu().numpy(),
+                            inp["lambdas"][:1], inp["rope_base"], eps=inp["eps"], slices=slices)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(r["dq"]).all()
+    T, H = inp["T"], inp["H"]
+    return {"value": round(n * T / dt / H, 1), "unit": "tokens/s/layer", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n} whole (b, h) slices ({T} tokens, head 0) of the {spec.name} workload, "
+                      f"fp64 numpy on one thread of control, {dt:.1f} s; token-heads/s divided "
+                      f"by the {H} heads of a layer"}
+
+
 def cpu_baseline_attn(args, torch, synth):
     """The attention oracle on evenly spaced query rows of the 512K workload (all heads): their
     mean cost is the mean over all rows, so rows / time estimates the whole prefill's rate."""
@@ -607,6 +709,11 @@ def main():
             print(f"[bench] attention decode at 512K context: steps {args.attn_decode_steps}",
                   file=sys.stderr, flush=True)
             attn["decode"] = bench_attn_decode(args, torch, lt, synth)
+    bwd = None
+    if not args.no_backward:
+        print(f"[bench] prefill backward at the 16K training shape: steps {args.bwd_steps}",
+              file=sys.stderr, flush=True)
+        bwd = bench_backward(args, torch, lt, synth)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -617,6 +724,9 @@ def main():
         if attn is not None:
             print("[bench] cpu baseline of the attention (oracle)", file=sys.stderr, flush=True)
             attn["cpu_baseline"] = cpu_baseline_attn(args, torch, synth)
+        if bwd is not None:
+            print("[bench] cpu baseline of the backward (oracle)", file=sys.stderr, flush=True)
+            bwd["cpu_baseline"] = cpu_baseline_backward(args, torch, synth)
     if args.copy_mib > 0:
         print(f"[bench] calibration copy of {args.copy_mib} MiB", file=sys.stderr, flush=True)
         copy_calibration(torch, args.copy_mib)
@@ -643,6 +753,7 @@ def main():
         "time_dependent_decay": td,
         "layer": layer,
         "attention": attn,
+        "backward": bwd,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
