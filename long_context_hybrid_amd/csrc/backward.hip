@@ -29,9 +29,12 @@
 // their rows' raw inputs in registers between the prologue and the epilogues.  The next chunk's
 // inputs are loaded into a second register set while the current chunk is processed.
 //
-// LDS tiles are bf16 [row][d] with the 16-byte blocks of row r XOR-permuted by r mod (d/8): a
-// 16-byte row read by 16 consecutive rows and a transposing ds_read_b64_tr_b16 of 4 rows both
-// spread over the banks, so every tile serves both access patterns.
+// LDS tiles are bf16 [row][d] with the 16-byte blocks of row r XOR-permuted by
+// f(r) = 4 (r mod 4) + (r / 4 mod 4): 16 consecutive rows take 16 distinct blocks (16-byte row
+// reads), and the four rows a transposing ds_read_b64_tr_b16 gathers move a 4-block group each
+// to a different place (measured on gfx950: no bank conflicts for those reads, against about 6
+// extra cycles per read with the plain r mod 16 permutation), so every tile serves both access
+// patterns.
 #include "lt_device.h"
 #include "lt_internal.h"
 
@@ -58,22 +61,28 @@ struct alignas(16) BwdSmem {
     alignas(16) __bf16 k[C * D];   // k~
     alignas(16) __bf16 v[C * D];
     alignas(16) __bf16 dO[C * D];  // do
-    alignas(16) __bf16 q_lo[C * D];  // q~ - bf16(q~) and k~ - bf16(k~) (dq sweep only)
+    alignas(16) __bf16 dOs[C * D];   // lambda^(cC + i + 1) do (dq sweep: the W update's operand)
+    alignas(16) __bf16 q_lo[C * D];  // q~ - bf16(q~) and k~ - bf16(k~)
     alignas(16) __bf16 k_lo[C * D];
     alignas(16) __bf16 st[D * D];  // state (or state gradient) copy, [value][key]
     alignas(16) float stage[C * G::OS];  // fp32 [token][feature] stage of o, dq~ or dk~
     alignas(16) float2 rope[2][64];      // cos/sin(p0 f_i) of this chunk and the next
     alignas(16) float w[3][D];           // norm weights q, k, o
-    // per lane: [0, 16) score-tile decay, [16, 32) lambda^(row + 1), [32, 48) lambda^(C-1-row)
-    alignas(16) float dec[64][48];
-    // norm-weight gradient partial sums of each row-op thread (its row, its 16 features):
-    // [0] q (or k), [1] o
-    alignas(16) float wacc[2][BCfg<D>::NT][16];
+    // decay factors per lane, as float4 groups g < 12 stored [g][lane] (consecutive lanes read
+    // consecutive 16-byte words): groups [0, 4) the score-tile decay, [4, 8) lambda^(row + 1),
+    // [8, 12) lambda^(C-1-row) of the lane's accumulator rows
+    alignas(16) float4 dec[12][64];
+    // norm-weight gradient partial sums of each row-op thread (its row, its 16 features), stored
+    // [which][feature slot][thread] so that a wavefront's accesses hit consecutive banks:
+    // which 0 = q (or k), 1 = o
+    alignas(16) float wacc[2][16][BCfg<D>::NT];
 };
 
 template <int D>
 __device__ __forceinline__ int swz(int row, int col) {
-    return row * D + (((col >> 3) ^ (row & (D / 8 - 1))) << 3) + (col & 7);
+    static_assert(D == 128, "the block permutation assumes 16 blocks per row");
+    const int f = 4 * (row & 3) + ((row >> 2) & 3);
+    return row * D + (((col >> 3) ^ f) << 3) + (col & 7);
 }
 
 typedef short tr16x4_t __attribute__((ext_vector_type(4)));
@@ -181,7 +190,7 @@ __device__ __forceinline__ void setup_common(const BwdParams& p, BwdSmem<D>& sm,
     }
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x, lm = lane & 31, lh = lane >> 5;
-        float* d = sm.dec[lane];
+        float d[48];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int m = acc_row(r, lh);
@@ -191,14 +200,19 @@ __device__ __forceinline__ void setup_common(const BwdParams& p, BwdSmem<D>& sm,
             d[16 + r] = pow_lambda(l2l, m + 1);
             d[32 + r] = pow_lambda(l2l, C - 1 - m);
         }
+#pragma unroll
+        for (int g = 0; g < 12; ++g)
+            sm.dec[g][lane] = make_float4(d[4 * g], d[4 * g + 1], d[4 * g + 2], d[4 * g + 3]);
     }
 }
 
-// The 16 decay factors of one lane's table row, as read for a use
-__device__ __forceinline__ void load16(const float* src, float* dst) {
+// 16 decay factors of this lane: table part `part` (0 score decay, 1 lambda^(row+1),
+// 2 lambda^(C-1-row))
+template <int D>
+__device__ __forceinline__ void load16(const BwdSmem<D>& sm, int part, int lane, float* dst) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        const float4 x = reinterpret_cast<const float4*>(src)[g];
+        const float4 x = sm.dec[4 * part + g][lane];
         dst[4 * g] = x.x; dst[4 * g + 1] = x.y; dst[4 * g + 2] = x.z; dst[4 * g + 3] = x.w;
     }
 }
@@ -264,10 +278,11 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
                 W[c][r] = 0.0f;
             }
     }
-    float* wacc_q = sm.wacc[0][threadIdx.x];
-    float* wacc_o = sm.wacc[1][threadIdx.x];
+    // wacc_x[NT * e]: this thread's partial sum for feature slot e
+    float* wacc_q = &sm.wacc[0][0][threadIdx.x];
+    float* wacc_o = &sm.wacc[1][0][threadIdx.x];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) wacc_q[e] = wacc_o[e] = 0.0f;
+    for (int e = 0; e < 16; ++e) wacc_q[G::NT * e] = wacc_o[G::NT * e] = 0.0f;
 
     struct Regs {
         uint4 q[2], k[2], v[2], g[2], dy[2];
@@ -358,15 +373,15 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
         __syncthreads();
         // ---- P2: o = diag(lambda^(i+1)) Q~ S + (K~ Q~^T (.) D)^T V for value columns of w ----
         if (wave == 0 && c + 1 < n_chunks) fill_table(i + 1, c + 1);
-        const float* dl = sm.dec[lane];
         float mk[16], rf[16];
-        load16(dl, mk);
-        load16(dl + 16, rf);
-        // o is recomputed to about fp32 accuracy (hi/lo parts of q~, k~, the state and the
-        // scores): the output norm's gradient scales with 1/||o_t||, and the rows where o_t is
-        // small (often the first tokens of a sequence, where o_t = (q~_t . k~_t) v_t) would
-        // otherwise carry the bf16 rounding of the products into do_t, which then dominates the
-        // sums q~_i^T do_i of the state gradients.
+        load16<D>(sm, 0, lane, mk);
+        load16<D>(sm, 1, lane, rf);
+        // The intra-chunk part of o is recomputed to about fp32 accuracy (hi/lo parts of q~, k~
+        // and the scores): the output norm's gradient scales with 1/||o_t||, and the rows where
+        // o_t is small (mostly the first tokens of a sequence, where o_t = (q~_t . k~_t) v_t)
+        // would otherwise carry the bf16 rounding of the scores into do_t, which then dominates
+        // the sums q~_i^T do_i of the state gradients.  The inter-chunk term q~ S keeps bf16
+        // operands: splitting them changed none of the measured gradients.
         f32x16 pt = {}, o = {};
 #pragma unroll
         for (int s8 = 0; s8 < D / 16; ++s8) {
@@ -377,13 +392,7 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
             pt = mfma_bf16(kv, qv, pt);  // P^T[j][i] += k~_j . q~_i
             pt = mfma_bf16(kv, ql, pt);
             pt = mfma_bf16(kl, qv, pt);
-            const bf16x8 qa = row_acc<D>(sm.q, lm, s8, lh);
-            const bf16x8 qal = row_acc<D>(sm.q_lo, lm, s8, lh);
-            bf16x8 sh, sl;
-            acc_split(S[s8 / 2], s8 % 2, sh, sl);
-            o = mfma_bf16(qa, sh, o);
-            o = mfma_bf16(qa, sl, o);
-            o = mfma_bf16(qal, sh, o);
+            o = mfma_bf16(row_acc<D>(sm.q, lm, s8, lh), acc_operand(S[s8 / 2], s8 % 2), o);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -428,7 +437,7 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
                 dn[e] = t * wo;
                 dgv[e] = dn[e] * nv * (1.0f - s);
                 dot = fmaf(dn[e], nv, dot);
-                if (valid) wacc_o[e] = fmaf(t, nv, wacc_o[e]);
+                if (valid) wacc_o[G::NT * e] = fmaf(t, nv, wacc_o[G::NT * e]);
                 ov[e] = nv;
             }
             dot = group_sum<TPR>(dot) * (1.0f / D);
@@ -436,6 +445,11 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
 #pragma unroll
             for (int e = 0; e < 16; ++e) dov[e] = ro * (dn[e] - ov[e] * dot);
             st16(sm.dO, dov, valid);
+            // the W update's operand: do scaled by lambda^(offset in the segment + 1)
+            const float wsc = pow_lambda(l2l, c * C + rr + 1);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) dn[e] = dov[e] * wsc;
+            st16(sm.dOs, dn, valid);
             if (valid) {
                 const size_t o2 = (size_t)(t0 + rr) * rs + 8 * fg;
                 uint16_t* pdg = static_cast<uint16_t*>(p.dg) + base + o2;
@@ -449,8 +463,8 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
         __syncthreads();
         // ---- P4: dq~ for key columns of w; W and S updates for value columns of w ----
         {
-            load16(dl, mk);
-            load16(dl + 16, rf);
+            load16<D>(sm, 0, lane, mk);
+            load16<D>(sm, 1, lane, rf);
             f32x16 dpt = {}, dq = {};
 #pragma unroll
             for (int s8 = 0; s8 < D / 16; ++s8) {
@@ -468,11 +482,10 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
                 dq = mfma_bf16(acc_operand(dpt, st), tr_acc<D>(sm.k, 16 * st, 32 * wave, lane), dq);
 #pragma unroll
             for (int r = 0; r < 16; ++r) sm.stage[acc_row(r, lh) * OS + 32 * wave + lm] = dq[r];
-            // W[k][v] += lambda^(cC) sum_i q~[i][k] lambda^(i+1) do[i][v]
-            const float cf = pow_lambda(l2l, c * C);
+            // W[k][v] += sum_i q~[i][k] lambda^(cC + i + 1) do[i][v]
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
-                const bf16x8 db = scale8(tr_acc<D>(sm.dO, 16 * st, 32 * wave, lane), rf + 8 * st, cf);
+                const bf16x8 db = tr_acc<D>(sm.dOs, 16 * st, 32 * wave, lane);
 #pragma unroll
                 for (int cc = 0; cc < NW; ++cc)
                     W[cc] = mfma_bf16(tr_acc<D>(sm.q, 16 * st, 32 * cc, lane), db, W[cc]);
@@ -480,7 +493,7 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
             // S <- lambda^n S + sum_j k~_j^T lambda^(n-1-j) v_j
             float rd[16];
             if (n == C) {
-                load16(dl + 32, rd);
+                load16<D>(sm, 2, lane, rd);
             } else {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -523,8 +536,8 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
                 const float hi = cs[u].x * dqt[8 + u] - cs[u].y * dqt[u];
                 const float xl = x[u] * rq, xh = x[8 + u] * rq;
                 if (valid) {
-                    wacc_q[u] = fmaf(lo, xl, wacc_q[u]);
-                    wacc_q[8 + u] = fmaf(hi, xh, wacc_q[8 + u]);
+                    wacc_q[G::NT * u] = fmaf(lo, xl, wacc_q[G::NT * u]);
+                    wacc_q[G::NT * (8 + u)] = fmaf(hi, xh, wacc_q[G::NT * (8 + u)]);
                 }
                 dx[u] = lo * sm.w[0][8 * fg + u];
                 dx[8 + u] = hi * sm.w[0][HALF + 8 * fg + u];
@@ -571,7 +584,7 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
             const int which = f / D, ff = f % D;
             const int tf = (ff % HALF) / 8, e = (ff >= HALF ? 8 : 0) + (ff & 7);
             float s = 0.0f;
-            for (int r = 0; r < C; ++r) s += sm.wacc[which][r * TPR + tf][e];
+            for (int r = 0; r < C; ++r) s += sm.wacc[which][e][r * TPR + tf];
             p.wgrad[((which == 0 ? 0 : 2) * nbp + (size_t)bh * p.P + seg) * D + ff] = s;
         }
     }
@@ -652,9 +665,9 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dkv_kernel(const BwdParams p)
             for (int r = 0; r < 16; ++r)
                 dS[c][r] = src[(size_t)(32 * c + acc_row(r, lh)) * D + 32 * wave + lm];
     }
-    float* wacc_k = sm.wacc[0][threadIdx.x];
+    float* wacc_k = &sm.wacc[0][0][threadIdx.x];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) wacc_k[e] = 0.0f;
+    for (int e = 0; e < 16; ++e) wacc_k[G::NT * e] = 0.0f;
 
     struct Regs {
         uint4 q[2], k[2], v[2], dO[2];
@@ -744,11 +757,10 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dkv_kernel(const BwdParams p)
         __syncthreads();
         // ---- P2: dv (value columns of w), dk~ (key columns of w), then the dS update ----
         if (wave == 0 && c > 0) fill_table(i + 1);
-        const float* dl = sm.dec[lane];
         float mk[16], rd[16];
-        load16(dl, mk);
+        load16<D>(sm, 0, lane, mk);
         if (n == C) {
-            load16(dl + 32, rd);
+            load16<D>(sm, 2, lane, rd);
         } else {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -801,7 +813,7 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dkv_kernel(const BwdParams p)
         {
             // dS <- lambda^n dS + sum_i q~_i^T lambda^(i+1) do_i
             float rf[16];
-            load16(dl + 16, rf);
+            load16<D>(sm, 1, lane, rf);
             const float ln = pow_lambda(l2l, n);
 #pragma unroll
             for (int cc = 0; cc < NW; ++cc)
@@ -837,8 +849,8 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dkv_kernel(const BwdParams p)
                 const float hi = (cs[u].x * dkt[8 + u] - cs[u].y * dkt[u]) * kscale;
                 const float xl = x[u] * rk, xh = x[8 + u] * rk;
                 if (valid) {
-                    wacc_k[u] = fmaf(lo, xl, wacc_k[u]);
-                    wacc_k[8 + u] = fmaf(hi, xh, wacc_k[8 + u]);
+                    wacc_k[G::NT * u] = fmaf(lo, xl, wacc_k[G::NT * u]);
+                    wacc_k[G::NT * (8 + u)] = fmaf(hi, xh, wacc_k[G::NT * (8 + u)]);
                 }
                 dx[u] = lo * sm.w[1][8 * fg + u];
                 dx[8 + u] = hi * sm.w[1][HALF + 8 * fg + u];
@@ -872,7 +884,7 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dkv_kernel(const BwdParams p)
         for (int f = threadIdx.x; f < D; f += G::NT) {
             const int tf = (f % HALF) / 8, e = (f >= HALF ? 8 : 0) + (f & 7);
             float s = 0.0f;
-            for (int r = 0; r < C; ++r) s += sm.wacc[0][r * TPR + tf][e];
+            for (int r = 0; r < C; ++r) s += sm.wacc[0][e][r * TPR + tf];
             p.wgrad[(nbp + (size_t)bh * p.P + seg) * D + f] = s;
         }
     }
