@@ -87,6 +87,8 @@ def copy_calibration(torch, mib):
 MIXER_SOURCES = ("abi.hip", "decode.hip", "lt_device.h", "lt_internal.h", "prefill.hip")
 LAYER_SOURCES = ("gemm.hip", "layer.hip")
 LAYER_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic_layer_qwen17_512k.md")
+BWD_SOURCES = ("backward.hip", "lt_device.h", "lt_internal.h")
+BWD_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic_backward_qwen17_16k.md")
 
 
 def source_fingerprint(sources=MIXER_SOURCES):
@@ -549,13 +551,14 @@ def bench_backward(args, torch, lt, synth):
     dom = max(legs, key=lambda k: legs[k][0])
     kms, alg, fl, kname = legs[dom]
     gbs = alg / (kms * 1e-3) / 1e9
+    traffic = measured_traffic(dom, spec.name, BWD_TRAFFIC_RECORD, BWD_SOURCES)
     out = {"workload": spec.name, "ms_per_step": round(ms, 4),
            "value": round(B * T / (ms * 1e-3), 1), "unit": "tokens/s/layer",
            "steps": args.bwd_steps, "segments": P,
            "stages_ms": {"dq_sweep": round(dq_ms, 4), "dkv_sweep": round(dkv_ms, 4),
                          "rest": round(ms - dq_ms - dkv_ms, 4)},
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                         "kernel": kname, "alg_bytes_per_launch": alg, "launch_ms": round(kms, 4)},
            "sweeps": {k: {"ms": round(v[0], 4), "alg_bytes": v[1],
                           "achieved_gbs": round(v[1] / (v[0] * 1e-3) / 1e9, 1),
