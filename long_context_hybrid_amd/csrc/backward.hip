@@ -164,10 +164,6 @@ __device__ __forceinline__ void acc_split(const f32x16& x, int st, bf16x8& hi, b
     }
 }
 
-__device__ __forceinline__ uint4 keep_if(bool keep, uint4 x) {
-    return make_uint4(keep ? x.x : 0u, keep ? x.y : 0u, keep ? x.z : 0u, keep ? x.w : 0u);
-}
-
 __device__ __forceinline__ void widen8(uint4 x, float* o) {
     o[0] = bf16_lo(x.x); o[1] = bf16_hi(x.x); o[2] = bf16_lo(x.y); o[3] = bf16_hi(x.y);
     o[4] = bf16_lo(x.z); o[5] = bf16_hi(x.z); o[6] = bf16_lo(x.w); o[7] = bf16_hi(x.w);
@@ -279,6 +275,10 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
             }
     }
     // wacc_x[NT * e]: this thread's partial sum for feature slot e
+    // The state is kept lazily scaled, state = alpha * S: a chunk multiplies alpha by lambda^n
+    // and divides the values it adds by the new alpha instead of rescaling the 64 accumulator
+    // registers; S absorbs alpha when it would fall below 2^-20 (every chunk for lambda = 0).
+    float alpha = 1.0f;
     float* wacc_q = &sm.wacc[0][0][threadIdx.x];
     float* wacc_o = &sm.wacc[1][0][threadIdx.x];
 #pragma unroll
@@ -324,21 +324,21 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
         }
         return rinv;
     };
-    auto st16 = [&](__bf16* tile, const float* x, bool valid) __attribute__((always_inline)) {
-        const uint4 lo = valid ? pack8(x) : make_uint4(0, 0, 0, 0);
-        const uint4 hi = valid ? pack8(x + 8) : make_uint4(0, 0, 0, 0);
+    auto st16 = [&](__bf16* tile, const float* x) __attribute__((always_inline)) {
+        const uint4 lo = pack8(x);
+        const uint4 hi = pack8(x + 8);
         *reinterpret_cast<uint4*>(tile + swz<D>(rr, 8 * fg)) = lo;
         *reinterpret_cast<uint4*>(tile + swz<D>(rr, HALF + 8 * fg)) = hi;
     };
 
-    auto st16_split = [&](__bf16* hi, __bf16* lo, const float* x, bool valid) __attribute__((always_inline)) {
+    auto st16_split = [&](__bf16* hi, __bf16* lo, const float* x) __attribute__((always_inline)) {
         uint4 h0, l0, h1, l1;
         split8(x, h0, l0);
         split8(x + 8, h1, l1);
-        *reinterpret_cast<uint4*>(hi + swz<D>(rr, 8 * fg)) = keep_if(valid, h0);
-        *reinterpret_cast<uint4*>(hi + swz<D>(rr, HALF + 8 * fg)) = keep_if(valid, h1);
-        *reinterpret_cast<uint4*>(lo + swz<D>(rr, 8 * fg)) = keep_if(valid, l0);
-        *reinterpret_cast<uint4*>(lo + swz<D>(rr, HALF + 8 * fg)) = keep_if(valid, l1);
+        *reinterpret_cast<uint4*>(hi + swz<D>(rr, 8 * fg)) = h0;
+        *reinterpret_cast<uint4*>(hi + swz<D>(rr, HALF + 8 * fg)) = h1;
+        *reinterpret_cast<uint4*>(lo + swz<D>(rr, 8 * fg)) = l0;
+        *reinterpret_cast<uint4*>(lo + swz<D>(rr, HALF + 8 * fg)) = l1;
     };
 
     auto step = [&](int i, Regs& R, Regs& Rn) __attribute__((always_inline)) {
@@ -346,6 +346,9 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
         const int t0 = t_begin + c * C;
         const int n = min(C, t_end - t0);
         const bool valid = rr < n;
+        // rows past the end of a partial chunk get zero inputs: their tile rows, do and every
+        // partial sum they enter are then zero (their loads re-read the last row)
+        if (n < C && !valid) R = Regs{};
         // ---- P1: prologue (q~, k~, v tiles) and the state copy; prefetch the next chunk ----
         float2 cs[8];
         angles(i, cs);
@@ -353,13 +356,13 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
         widen8(R.q[0], x);
         widen8(R.q[1], x + 8);
         const float rq = norm_rotate(x, sm.w[0], cs, 1.0f);
-        st16_split(sm.q, sm.q_lo, x, valid);
+        st16_split(sm.q, sm.q_lo, x);
         widen8(R.k[0], x);
         widen8(R.k[1], x + 8);
         norm_rotate(x, sm.w[1], cs, 1.0f / sqrtf((float)D));
-        st16_split(sm.k, sm.k_lo, x, valid);
-        *reinterpret_cast<uint4*>(sm.v + swz<D>(rr, 8 * fg)) = keep_if(valid, R.v[0]);
-        *reinterpret_cast<uint4*>(sm.v + swz<D>(rr, HALF + 8 * fg)) = keep_if(valid, R.v[1]);
+        st16_split(sm.k, sm.k_lo, x);
+        *reinterpret_cast<uint4*>(sm.v + swz<D>(rr, 8 * fg)) = R.v[0];
+        *reinterpret_cast<uint4*>(sm.v + swz<D>(rr, HALF + 8 * fg)) = R.v[1];
 #pragma unroll
         for (int cc = 0; cc < NW; ++cc)
 #pragma unroll
@@ -397,7 +400,7 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             pt[r] *= mk[r];
-            o[r] *= rf[r];
+            o[r] *= rf[r] * alpha;
         }
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
@@ -437,19 +440,19 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
                 dn[e] = t * wo;
                 dgv[e] = dn[e] * nv * (1.0f - s);
                 dot = fmaf(dn[e], nv, dot);
-                if (valid) wacc_o[G::NT * e] = fmaf(t, nv, wacc_o[G::NT * e]);
+                wacc_o[G::NT * e] = fmaf(t, nv, wacc_o[G::NT * e]);
                 ov[e] = nv;
             }
             dot = group_sum<TPR>(dot) * (1.0f / D);
             float dov[16];
 #pragma unroll
             for (int e = 0; e < 16; ++e) dov[e] = ro * (dn[e] - ov[e] * dot);
-            st16(sm.dO, dov, valid);
+            st16(sm.dO, dov);
             // the W update's operand: do scaled by lambda^(offset in the segment + 1)
             const float wsc = pow_lambda(l2l, c * C + rr + 1);
 #pragma unroll
             for (int e = 0; e < 16; ++e) dn[e] = dov[e] * wsc;
-            st16(sm.dOs, dn, valid);
+            st16(sm.dOs, dn);
             if (valid) {
                 const size_t o2 = (size_t)(t0 + rr) * rs + 8 * fg;
                 uint16_t* pdg = static_cast<uint16_t*>(p.dg) + base + o2;
@@ -475,7 +478,7 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 dpt[r] *= mk[r];
-                dq[r] *= rf[r];
+                dq[r] *= rf[r] * alpha;
             }
 #pragma unroll
             for (int st = 0; st < 2; ++st)
@@ -501,14 +504,21 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
                     rd[r] = j < n ? pow_lambda(l2l, n - 1 - j) : 0.0f;
                 }
             }
-            const float ln = pow_lambda(l2l, n);
+            const float a_next = alpha * pow_lambda(l2l, n);
+            float inv = 1.0f;
+            if (a_next < 0x1p-20f) {
 #pragma unroll
-            for (int cc = 0; cc < NW; ++cc)
+                for (int cc = 0; cc < NW; ++cc)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) S[cc][r] *= ln;
+                    for (int r = 0; r < 16; ++r) S[cc][r] *= a_next;
+                alpha = 1.0f;
+            } else {
+                alpha = a_next;
+                inv = 1.0f / a_next;
+            }
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
-                const bf16x8 vb = scale8(tr_acc<D>(sm.v, 16 * st, 32 * wave, lane), rd + 8 * st, 1.0f);
+                const bf16x8 vb = scale8(tr_acc<D>(sm.v, 16 * st, 32 * wave, lane), rd + 8 * st, inv);
 #pragma unroll
                 for (int cc = 0; cc < NW; ++cc)
                     S[cc] = mfma_bf16(tr_acc<D>(sm.k, 16 * st, 32 * cc, lane), vb, S[cc]);
@@ -535,10 +545,8 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
                 const float lo = cs[u].x * dqt[u] + cs[u].y * dqt[8 + u];
                 const float hi = cs[u].x * dqt[8 + u] - cs[u].y * dqt[u];
                 const float xl = x[u] * rq, xh = x[8 + u] * rq;
-                if (valid) {
-                    wacc_q[G::NT * u] = fmaf(lo, xl, wacc_q[G::NT * u]);
-                    wacc_q[G::NT * (8 + u)] = fmaf(hi, xh, wacc_q[G::NT * (8 + u)]);
-                }
+                wacc_q[G::NT * u] = fmaf(lo, xl, wacc_q[G::NT * u]);
+                wacc_q[G::NT * (8 + u)] = fmaf(hi, xh, wacc_q[G::NT * (8 + u)]);
                 dx[u] = lo * sm.w[0][8 * fg + u];
                 dx[8 + u] = hi * sm.w[0][HALF + 8 * fg + u];
                 x[u] = xl;
@@ -665,6 +673,8 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dkv_kernel(const BwdParams p)
             for (int r = 0; r < 16; ++r)
                 dS[c][r] = src[(size_t)(32 * c + acc_row(r, lh)) * D + 32 * wave + lm];
     }
+    // the state gradient is kept lazily scaled like the dq sweep's state: dS = beta * dS_stored
+    float beta = 1.0f;
     float* wacc_k = &sm.wacc[0][0][threadIdx.x];
 #pragma unroll
     for (int e = 0; e < 16; ++e) wacc_k[G::NT * e] = 0.0f;
@@ -706,21 +716,21 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dkv_kernel(const BwdParams p)
         }
         return rinv;
     };
-    auto st16 = [&](__bf16* tile, const float* x, bool valid) __attribute__((always_inline)) {
-        const uint4 lo = valid ? pack8(x) : make_uint4(0, 0, 0, 0);
-        const uint4 hi = valid ? pack8(x + 8) : make_uint4(0, 0, 0, 0);
+    auto st16 = [&](__bf16* tile, const float* x) __attribute__((always_inline)) {
+        const uint4 lo = pack8(x);
+        const uint4 hi = pack8(x + 8);
         *reinterpret_cast<uint4*>(tile + swz<D>(rr, 8 * fg)) = lo;
         *reinterpret_cast<uint4*>(tile + swz<D>(rr, HALF + 8 * fg)) = hi;
     };
     const float kscale = 1.0f / sqrtf((float)D);
-    auto st16_split = [&](__bf16* hi, __bf16* lo, const float* x, bool valid) __attribute__((always_inline)) {
+    auto st16_split = [&](__bf16* hi, __bf16* lo, const float* x) __attribute__((always_inline)) {
         uint4 h0, l0, h1, l1;
         split8(x, h0, l0);
         split8(x + 8, h1, l1);
-        *reinterpret_cast<uint4*>(hi + swz<D>(rr, 8 * fg)) = keep_if(valid, h0);
-        *reinterpret_cast<uint4*>(hi + swz<D>(rr, HALF + 8 * fg)) = keep_if(valid, h1);
-        *reinterpret_cast<uint4*>(lo + swz<D>(rr, 8 * fg)) = keep_if(valid, l0);
-        *reinterpret_cast<uint4*>(lo + swz<D>(rr, HALF + 8 * fg)) = keep_if(valid, l1);
+        *reinterpret_cast<uint4*>(hi + swz<D>(rr, 8 * fg)) = h0;
+        *reinterpret_cast<uint4*>(hi + swz<D>(rr, HALF + 8 * fg)) = h1;
+        *reinterpret_cast<uint4*>(lo + swz<D>(rr, 8 * fg)) = l0;
+        *reinterpret_cast<uint4*>(lo + swz<D>(rr, HALF + 8 * fg)) = l1;
     };
 
     auto step = [&](int i, Regs& R, Regs& Rn) __attribute__((always_inline)) {
@@ -728,6 +738,7 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dkv_kernel(const BwdParams p)
         const int t0 = t_begin + c * C;
         const int n = min(C, t_end - t0);
         const bool valid = rr < n;
+        if (n < C && !valid) R = Regs{};  // rows past the end: zero inputs
         // ---- P1: q~, k~, v, do tiles and the state-gradient copy; prefetch ----
         float2 cs[8];
         angles(i, cs);
@@ -735,16 +746,16 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dkv_kernel(const BwdParams p)
         widen8(R.q[0], x);
         widen8(R.q[1], x + 8);
         norm_rotate(x, sm.w[0], cs, 1.0f);
-        st16_split(sm.q, sm.q_lo, x, valid);
+        st16_split(sm.q, sm.q_lo, x);
         widen8(R.k[0], x);
         widen8(R.k[1], x + 8);
         const float rk = norm_rotate(x, sm.w[1], cs, kscale);
-        st16_split(sm.k, sm.k_lo, x, valid);
+        st16_split(sm.k, sm.k_lo, x);
         // (value selects: a conditional between two lvalues would select addresses, in memory)
-        *reinterpret_cast<uint4*>(sm.v + swz<D>(rr, 8 * fg)) = keep_if(valid, R.v[0]);
-        *reinterpret_cast<uint4*>(sm.v + swz<D>(rr, HALF + 8 * fg)) = keep_if(valid, R.v[1]);
-        *reinterpret_cast<uint4*>(sm.dO + swz<D>(rr, 8 * fg)) = keep_if(valid, R.dO[0]);
-        *reinterpret_cast<uint4*>(sm.dO + swz<D>(rr, HALF + 8 * fg)) = keep_if(valid, R.dO[1]);
+        *reinterpret_cast<uint4*>(sm.v + swz<D>(rr, 8 * fg)) = R.v[0];
+        *reinterpret_cast<uint4*>(sm.v + swz<D>(rr, HALF + 8 * fg)) = R.v[1];
+        *reinterpret_cast<uint4*>(sm.dO + swz<D>(rr, 8 * fg)) = R.dO[0];
+        *reinterpret_cast<uint4*>(sm.dO + swz<D>(rr, HALF + 8 * fg)) = R.dO[1];
 #pragma unroll
         for (int cc = 0; cc < NW; ++cc)
 #pragma unroll
@@ -790,8 +801,8 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dkv_kernel(const BwdParams p)
             for (int r = 0; r < 16; ++r) {
                 pm[r] *= mk[r];
                 dpm[r] *= mk[r];
-                dvv[r] *= rd[r];
-                dkt[r] *= rd[r];
+                dvv[r] *= rd[r] * beta;
+                dkt[r] *= rd[r] * beta;
             }
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
@@ -814,14 +825,21 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dkv_kernel(const BwdParams p)
             // dS <- lambda^n dS + sum_i q~_i^T lambda^(i+1) do_i
             float rf[16];
             load16<D>(sm, 1, lane, rf);
-            const float ln = pow_lambda(l2l, n);
+            const float b_next = beta * pow_lambda(l2l, n);
+            float inv = 1.0f;
+            if (b_next < 0x1p-20f) {
 #pragma unroll
-            for (int cc = 0; cc < NW; ++cc)
+                for (int cc = 0; cc < NW; ++cc)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) dS[cc][r] *= ln;
+                    for (int r = 0; r < 16; ++r) dS[cc][r] *= b_next;
+                beta = 1.0f;
+            } else {
+                beta = b_next;
+                inv = 1.0f / b_next;
+            }
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
-                const bf16x8 db = scale8(tr_acc<D>(sm.dO, 16 * st, 32 * wave, lane), rf + 8 * st, 1.0f);
+                const bf16x8 db = scale8(tr_acc<D>(sm.dO, 16 * st, 32 * wave, lane), rf + 8 * st, inv);
 #pragma unroll
                 for (int cc = 0; cc < NW; ++cc)
                     dS[cc] = mfma_bf16(tr_acc<D>(sm.q, 16 * st, 32 * cc, lane), db, dS[cc]);
@@ -848,10 +866,8 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dkv_kernel(const BwdParams p)
                 const float lo = (cs[u].x * dkt[u] + cs[u].y * dkt[8 + u]) * kscale;
                 const float hi = (cs[u].x * dkt[8 + u] - cs[u].y * dkt[u]) * kscale;
                 const float xl = x[u] * rk, xh = x[8 + u] * rk;
-                if (valid) {
-                    wacc_k[G::NT * u] = fmaf(lo, xl, wacc_k[G::NT * u]);
-                    wacc_k[G::NT * (8 + u)] = fmaf(hi, xh, wacc_k[G::NT * (8 + u)]);
-                }
+                wacc_k[G::NT * u] = fmaf(lo, xl, wacc_k[G::NT * u]);
+                wacc_k[G::NT * (8 + u)] = fmaf(hi, xh, wacc_k[G::NT * (8 + u)]);
                 dx[u] = lo * sm.w[1][8 * fg + u];
                 dx[8 + u] = hi * sm.w[1][HALF + 8 * fg + u];
                 x[u] = xl;
