@@ -188,12 +188,20 @@ def gpu_layer_decode(inp):
 
 
 @pytest.mark.parametrize("spec_name,values", [("full", "gauss"), ("small_ternary", "ternary"),
+                                              ("one_row_ternary", "ternary"),
+                                              ("rows_40_ternary", "ternary"),
                                               ("small_fp32", "gauss")])
 def test_layer_decode(spec_name, values):
+    """1, 5, 40 and 64 batch rows (bf16) and 3 (fp32); the ternary inputs' projections are
+    exact integers, so there the projections must match the oracle bit for bit."""
     if spec_name == "full":
         inp = synth.make_layer(synth.LAYER_DECODE_B64)
     elif spec_name == "small_ternary":
         inp = synth.make_custom_layer(5, 1, 2, 128, 256, seed=8, state="randn", values=values)
+    elif spec_name == "one_row_ternary":
+        inp = synth.make_custom_layer(1, 1, 2, 128, 256, seed=10, state="randn", values=values)
+    elif spec_name == "rows_40_ternary":
+        inp = synth.make_custom_layer(40, 1, 2, 128, 256, seed=11, state="randn", values=values)
     else:
         inp = synth.make_custom_layer(3, 1, 2, 64, 64, dtype=torch.float32, seed=9,
                                       state="randn", lambdas=(0.0, 0.95))
