@@ -227,3 +227,55 @@ def test_backward_full_size_sampled_heads():
            for n in ("dq", "dk", "dv", "dgate")}
     gpu["d_state_in"] = {(b, h): out["d_state_in"][b, h].cpu() for b, h in slices}
     compare(gpu, ref, sub, "16K training shape")
+
+
+def test_backward_composes_over_split_calls_on_gpu():
+    """The backward of two chained prefill calls, the second's d_state_in fed to the first as its
+    d_state_out (and the first call's final state as the second's state_in, from the forward
+    kernel), equals the backward of the whole call."""
+    import long_context_hybrid_amd.lightning as lt
+
+    T, T1 = 1000, 613
+    inp = synth.make_custom_prefill(1, T, 2, 128, dtype=torch.bfloat16, seed=47, state="randn")
+    gen = torch.Generator().manual_seed(48)
+    inp["dy"] = torch.randn(inp["q"].shape, generator=gen).to(torch.bfloat16)
+    inp["d_state_out"] = 0.01 * torch.randn((1, 2, 128, 128), generator=gen)
+    dev = torch.device("cuda")
+    whole = gpu_backward(inp, segments=3)
+    first = dict(inp, **{n: inp[n][:, :T1].contiguous() for n in ("q", "k", "v", "g", "dy")})
+    second = dict(inp, **{n: inp[n][:, T1:].contiguous() for n in ("q", "k", "v", "g", "dy")},
+                  pos0=T1)
+    s_mid = torch.empty((1, 2, 128, 128), dtype=torch.float32, device=dev)
+    lt.lightning_prefill(*(first[n].to(dev) for n in ("q", "k", "v", "g")), inp["qw"].to(dev),
+                         inp["kw"].to(dev), inp["lambdas"], inp["rope_base"],
+                         state_in=inp["state_in"].to(dev), state_out=s_mid)
+    torch.cuda.synchronize()
+    second["state_in"] = s_mid.cpu()
+    g2 = gpu_backward(second, segments=2)
+    first["d_state_out"] = g2["d_state_in"]
+    g1 = gpu_backward(first, segments=2)
+    for name in ("dq", "dk", "dv", "dgate"):
+        joined = torch.cat([g1[name], g2[name]], 1)
+        for h in range(2):
+            e = rel_l2(joined[0, :, h].numpy(), whole[name][0, :, h].numpy())
+            assert e <= TOL, (name, h, e)
+    for h in range(2):
+        e = rel_l2(g1["d_state_in"][0, h].numpy(), whole["d_state_in"][0, h].numpy())
+        print(f"[parity] backward split calls: d_state_in head {h} {e:.2e}")
+        assert e <= TOL
+    for name in ("d_q_norm_w", "d_k_norm_w", "d_o_norm_w"):
+        e = rel_l2((g1[name] + g2[name]).numpy(), whole[name].numpy())
+        assert e <= TOL, (name, e)
+
+
+def test_backward_state_gradient_only():
+    """dy = 0 with a final-state gradient: do vanishes, so dq and dgate are exactly zero, and dk,
+    dv and d_state_in come from d_state_out alone (against the oracle)."""
+    inp = synth.make_custom_prefill(1, 500, 2, 128, dtype=torch.bfloat16, seed=49, state="randn")
+    gen = torch.Generator().manual_seed(50)
+    inp["dy"] = torch.zeros(inp["q"].shape, dtype=torch.bfloat16)
+    inp["d_state_out"] = torch.randn((1, 2, 128, 128), generator=gen)
+    ref = oracle_backward(inp)
+    gpu = gpu_backward(inp, segments=3)
+    assert float(gpu["dq"].abs().max()) == 0.0 and float(gpu["dgate"].abs().max()) == 0.0
+    compare(gpu, ref, inp, "state gradient only", grads=GRADS[1:3])
