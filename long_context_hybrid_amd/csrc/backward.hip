@@ -213,6 +213,89 @@ __device__ __forceinline__ void load16(const BwdSmem<D>& sm, int part, int lane,
     }
 }
 
+// The row work of a sweep: thread `rr * TPR + fg` handles token row rr of the chunk and the
+// features 8 fg + u and HALF + 8 fg + u (u < 8), the half-split RoPE pairs.  The RoPE table
+// cos/sin(p0 f_i) of each processing step is filled by wavefront 0, one frequency per lane, by
+// advancing the previous step's entry by one chunk (forward or back) and recomputing it exactly
+// (fp64 angle reduction) every kRopeAnchorB steps; each thread rotates it by cos/sin(rr f_i).
+template <int D>
+struct RowWork {
+    static constexpr int HALF = D / 2, TPR = D / 16;
+    BwdSmem<D>& sm;
+    const BwdParams& p;
+    int rr, fg;
+    float2 tstep;   // rotation by one processing step (one chunk forward or back)
+    float2 rot[8];  // cos/sin(rr f) of this thread's frequencies
+
+    __device__ __forceinline__ RowWork(BwdSmem<D>& s, const BwdParams& params, int dir)
+        : sm(s), p(params) {
+        rr = threadIdx.x / TPR;
+        fg = threadIdx.x % TPR;
+        const int lane = threadIdx.x & 63;
+        rope_cos_sin(dir * C, p.inv_freq_rev[lane < HALF ? lane : HALF - 1], tstep.x, tstep.y);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) rope_cos_sin(rr, p.inv_freq_rev[8 * fg + u], rot[u].x, rot[u].y);
+    }
+    // table of processing step `step`, whose chunk starts at absolute position pos (wavefront 0)
+    __device__ __forceinline__ void fill_table(int step, int64_t pos) {
+        const int lane = threadIdx.x & 63, fi = lane < HALF ? lane : HALF - 1;
+        const double frev = p.inv_freq_rev[fi];
+        float2 e;
+        if (step % kRopeAnchorB == 0) {
+            rope_cos_sin(pos, frev, e.x, e.y);
+        } else {
+            const float2 a = sm.rope[(step - 1) & 1][fi];
+            e.x = a.x * tstep.x - a.y * tstep.y;
+            e.y = a.y * tstep.x + a.x * tstep.y;
+        }
+        if (lane < HALF) sm.rope[step & 1][lane] = e;
+    }
+    // cos/sin of (p0 + rr) f for this thread's 8 frequencies
+    __device__ __forceinline__ void angles(int step, float2* cs) const {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float2 t = sm.rope[step & 1][8 * fg + u];
+            cs[u] = make_float2(t.x * rot[u].x - t.y * rot[u].y, t.y * rot[u].x + t.x * rot[u].y);
+        }
+    }
+    // RMSNorm of the row (returns 1/rms), weight, rotation, scale; x[16] = features lo 0..7,
+    // hi 0..7 of this thread
+    __device__ __forceinline__ float norm_rotate(float* x, const float* w, const float2* cs,
+                                                 float scale) const {
+        float ss = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ss = fmaf(x[e], x[e], ss);
+        ss = group_sum<TPR>(ss);
+        const float rinv = fast_rsqrt(ss * (1.0f / D) + p.eps);
+        const float sc = rinv * scale;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float a = x[u] * sc * w[8 * fg + u], c = x[8 + u] * sc * w[HALF + 8 * fg + u];
+            x[u] = a * cs[u].x - c * cs[u].y;
+            x[8 + u] = c * cs[u].x + a * cs[u].y;
+        }
+        return rinv;
+    }
+    // the 16 values of this thread's row as bf16 (hi parts, and the lo parts when given)
+    __device__ __forceinline__ void store(__bf16* tile, const float* x) const {
+        *reinterpret_cast<uint4*>(tile + swz<D>(rr, 8 * fg)) = pack8(x);
+        *reinterpret_cast<uint4*>(tile + swz<D>(rr, HALF + 8 * fg)) = pack8(x + 8);
+    }
+    __device__ __forceinline__ void store_split(__bf16* hi, __bf16* lo, const float* x) const {
+        uint4 h0, l0, h1, l1;
+        split8(x, h0, l0);
+        split8(x + 8, h1, l1);
+        *reinterpret_cast<uint4*>(hi + swz<D>(rr, 8 * fg)) = h0;
+        *reinterpret_cast<uint4*>(hi + swz<D>(rr, HALF + 8 * fg)) = h1;
+        *reinterpret_cast<uint4*>(lo + swz<D>(rr, 8 * fg)) = l0;
+        *reinterpret_cast<uint4*>(lo + swz<D>(rr, HALF + 8 * fg)) = l1;
+    }
+    __device__ __forceinline__ void store_raw(__bf16* tile, const uint4* x) const {
+        *reinterpret_cast<uint4*>(tile + swz<D>(rr, 8 * fg)) = x[0];
+        *reinterpret_cast<uint4*>(tile + swz<D>(rr, HALF + 8 * fg)) = x[1];
+    }
+};
+
 // ============================== forward sweep: dq, dg, do, W ==================================
 template <int D>
 __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) {
@@ -239,27 +322,9 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
     const uint16_t* gdy = static_cast<const uint16_t*>(p.dy) + base + 8 * fg;
 
     setup_common<D>(p, sm, h, l2l, true);
-    // RoPE: per-chunk table cos/sin(p0 f_i) (wavefront 0, one frequency per lane) and this
-    // thread's rotation by its row, cos/sin(rr f_i)
-    const int fi = lane < HALF ? lane : HALF - 1;
-    const double frev = p.inv_freq_rev[fi];
-    float2 tstep;
-    rope_cos_sin(C, frev, tstep.x, tstep.y);
-    auto fill_table = [&](int step, int chunk) __attribute__((always_inline)) {
-        float2 e;
-        if (step % kRopeAnchorB == 0) {
-            rope_cos_sin(p.pos0 + t_begin + (int64_t)chunk * C, frev, e.x, e.y);
-        } else {
-            const float2 a = sm.rope[(step - 1) & 1][fi];
-            e.x = a.x * tstep.x - a.y * tstep.y;
-            e.y = a.y * tstep.x + a.x * tstep.y;
-        }
-        if (lane < HALF) sm.rope[step & 1][lane] = e;
-    };
-    if (wave == 0) fill_table(0, 0);
-    float2 rot[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) rope_cos_sin(rr, p.inv_freq_rev[8 * fg + u], rot[u].x, rot[u].y);
+    RowWork<D> rw(sm, p, 1);
+    auto chunk_pos = [&](int chunk) { return p.pos0 + t_begin + (int64_t)chunk * C; };
+    if (wave == 0) rw.fill_table(0, chunk_pos(0));
 
     // forward entry state and the segment's entry-state gradient W
     f32x16 S[NW], W[NW];
@@ -300,47 +365,6 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
             R.dy[hf] = *reinterpret_cast<const uint4*>(gdy + oo);
         }
     };
-    // cos/sin of (p0 + rr) f for this thread's 8 frequencies
-    auto angles = [&](int step, float2* cs) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const float2 t = sm.rope[step & 1][8 * fg + u];
-            cs[u] = make_float2(t.x * rot[u].x - t.y * rot[u].y, t.y * rot[u].x + t.x * rot[u].y);
-        }
-    };
-    // RMSNorm (returns 1/rms), weight, rotation; x[16] = features lo 0..7, hi 0..7
-    auto norm_rotate = [&](float* x, const float* w, const float2* cs, float scale) __attribute__((always_inline)) {
-        float ss = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) ss = fmaf(x[e], x[e], ss);
-        ss = group_sum<TPR>(ss);
-        const float rinv = fast_rsqrt(ss * (1.0f / D) + p.eps);
-        const float sc = rinv * scale;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const float a = x[u] * sc * w[8 * fg + u], c = x[8 + u] * sc * w[HALF + 8 * fg + u];
-            x[u] = a * cs[u].x - c * cs[u].y;
-            x[8 + u] = c * cs[u].x + a * cs[u].y;
-        }
-        return rinv;
-    };
-    auto st16 = [&](__bf16* tile, const float* x) __attribute__((always_inline)) {
-        const uint4 lo = pack8(x);
-        const uint4 hi = pack8(x + 8);
-        *reinterpret_cast<uint4*>(tile + swz<D>(rr, 8 * fg)) = lo;
-        *reinterpret_cast<uint4*>(tile + swz<D>(rr, HALF + 8 * fg)) = hi;
-    };
-
-    auto st16_split = [&](__bf16* hi, __bf16* lo, const float* x) __attribute__((always_inline)) {
-        uint4 h0, l0, h1, l1;
-        split8(x, h0, l0);
-        split8(x + 8, h1, l1);
-        *reinterpret_cast<uint4*>(hi + swz<D>(rr, 8 * fg)) = h0;
-        *reinterpret_cast<uint4*>(hi + swz<D>(rr, HALF + 8 * fg)) = h1;
-        *reinterpret_cast<uint4*>(lo + swz<D>(rr, 8 * fg)) = l0;
-        *reinterpret_cast<uint4*>(lo + swz<D>(rr, HALF + 8 * fg)) = l1;
-    };
-
     auto step = [&](int i, Regs& R, Regs& Rn) __attribute__((always_inline)) {
         const int c = i;
         const int t0 = t_begin + c * C;
@@ -351,18 +375,17 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
         if (n < C && !valid) R = Regs{};
         // ---- P1: prologue (q~, k~, v tiles) and the state copy; prefetch the next chunk ----
         float2 cs[8];
-        angles(i, cs);
+        rw.angles(i, cs);
         float x[16];
         widen8(R.q[0], x);
         widen8(R.q[1], x + 8);
-        const float rq = norm_rotate(x, sm.w[0], cs, 1.0f);
-        st16_split(sm.q, sm.q_lo, x);
+        const float rq = rw.norm_rotate(x, sm.w[0], cs, 1.0f);
+        rw.store_split(sm.q, sm.q_lo, x);
         widen8(R.k[0], x);
         widen8(R.k[1], x + 8);
-        norm_rotate(x, sm.w[1], cs, 1.0f / sqrtf((float)D));
-        st16_split(sm.k, sm.k_lo, x);
-        *reinterpret_cast<uint4*>(sm.v + swz<D>(rr, 8 * fg)) = R.v[0];
-        *reinterpret_cast<uint4*>(sm.v + swz<D>(rr, HALF + 8 * fg)) = R.v[1];
+        rw.norm_rotate(x, sm.w[1], cs, 1.0f / sqrtf((float)D));
+        rw.store_split(sm.k, sm.k_lo, x);
+        rw.store_raw(sm.v, R.v);
 #pragma unroll
         for (int cc = 0; cc < NW; ++cc)
 #pragma unroll
@@ -375,7 +398,7 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
         if (c + 1 < n_chunks) load(c + 1, Rn);
         __syncthreads();
         // ---- P2: o = diag(lambda^(i+1)) Q~ S + (K~ Q~^T (.) D)^T V for value columns of w ----
-        if (wave == 0 && c + 1 < n_chunks) fill_table(i + 1, c + 1);
+        if (wave == 0 && c + 1 < n_chunks) rw.fill_table(i + 1, chunk_pos(c + 1));
         float mk[16], rf[16];
         load16<D>(sm, 0, lane, mk);
         load16<D>(sm, 1, lane, rf);
@@ -447,12 +470,12 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
             float dov[16];
 #pragma unroll
             for (int e = 0; e < 16; ++e) dov[e] = ro * (dn[e] - ov[e] * dot);
-            st16(sm.dO, dov);
+            rw.store(sm.dO, dov);
             // the W update's operand: do scaled by lambda^(offset in the segment + 1)
             const float wsc = pow_lambda(l2l, c * C + rr + 1);
 #pragma unroll
             for (int e = 0; e < 16; ++e) dn[e] = dov[e] * wsc;
-            st16(sm.dOs, dn);
+            rw.store(sm.dOs, dn);
             if (valid) {
                 const size_t o2 = (size_t)(t0 + rr) * rs + 8 * fg;
                 uint16_t* pdg = static_cast<uint16_t*>(p.dg) + base + o2;
@@ -527,7 +550,7 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
         __syncthreads();
         // ---- P5: dq = QK-norm^T(RoPE^T(dq~)) ----
         {
-            angles(i, cs);
+            rw.angles(i, cs);
             float dqt[16];
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
@@ -642,26 +665,10 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dkv_kernel(const BwdParams p)
     const uint16_t* gdo = p.d_o + base + 8 * fg;
 
     setup_common<D>(p, sm, h, l2l, false);
-    const int fi = lane < HALF ? lane : HALF - 1;
-    const double frev = p.inv_freq_rev[fi];
-    float2 tstep;  // rotation back by one chunk
-    rope_cos_sin(-C, frev, tstep.x, tstep.y);
-    auto chunk_of = [&](int step) __attribute__((always_inline)) { return n_chunks - 1 - step; };
-    auto fill_table = [&](int step) __attribute__((always_inline)) {
-        float2 e;
-        if (step % kRopeAnchorB == 0) {
-            rope_cos_sin(p.pos0 + t_begin + (int64_t)chunk_of(step) * C, frev, e.x, e.y);
-        } else {
-            const float2 a = sm.rope[(step - 1) & 1][fi];
-            e.x = a.x * tstep.x - a.y * tstep.y;
-            e.y = a.y * tstep.x + a.x * tstep.y;
-        }
-        if (lane < HALF) sm.rope[step & 1][lane] = e;
-    };
-    if (wave == 0) fill_table(0);
-    float2 rot[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) rope_cos_sin(rr, p.inv_freq_rev[8 * fg + u], rot[u].x, rot[u].y);
+    RowWork<D> rw(sm, p, -1);  // processing steps run backward over the chunks
+    auto chunk_of = [&](int step) { return n_chunks - 1 - step; };
+    auto chunk_pos = [&](int step) { return p.pos0 + t_begin + (int64_t)chunk_of(step) * C; };
+    if (wave == 0) rw.fill_table(0, chunk_pos(0));
 
     // state gradient at the segment's end
     f32x16 dS[NW];
@@ -694,44 +701,7 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dkv_kernel(const BwdParams p)
             R.dO[hf] = *reinterpret_cast<const uint4*>(gdo + oo);
         }
     };
-    auto angles = [&](int step, float2* cs) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const float2 t = sm.rope[step & 1][8 * fg + u];
-            cs[u] = make_float2(t.x * rot[u].x - t.y * rot[u].y, t.y * rot[u].x + t.x * rot[u].y);
-        }
-    };
-    auto norm_rotate = [&](float* x, const float* w, const float2* cs, float scale) __attribute__((always_inline)) {
-        float ss = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) ss = fmaf(x[e], x[e], ss);
-        ss = group_sum<TPR>(ss);
-        const float rinv = fast_rsqrt(ss * (1.0f / D) + p.eps);
-        const float sc = rinv * scale;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const float a = x[u] * sc * w[8 * fg + u], c = x[8 + u] * sc * w[HALF + 8 * fg + u];
-            x[u] = a * cs[u].x - c * cs[u].y;
-            x[8 + u] = c * cs[u].x + a * cs[u].y;
-        }
-        return rinv;
-    };
-    auto st16 = [&](__bf16* tile, const float* x) __attribute__((always_inline)) {
-        const uint4 lo = pack8(x);
-        const uint4 hi = pack8(x + 8);
-        *reinterpret_cast<uint4*>(tile + swz<D>(rr, 8 * fg)) = lo;
-        *reinterpret_cast<uint4*>(tile + swz<D>(rr, HALF + 8 * fg)) = hi;
-    };
     const float kscale = 1.0f / sqrtf((float)D);
-    auto st16_split = [&](__bf16* hi, __bf16* lo, const float* x) __attribute__((always_inline)) {
-        uint4 h0, l0, h1, l1;
-        split8(x, h0, l0);
-        split8(x + 8, h1, l1);
-        *reinterpret_cast<uint4*>(hi + swz<D>(rr, 8 * fg)) = h0;
-        *reinterpret_cast<uint4*>(hi + swz<D>(rr, HALF + 8 * fg)) = h1;
-        *reinterpret_cast<uint4*>(lo + swz<D>(rr, 8 * fg)) = l0;
-        *reinterpret_cast<uint4*>(lo + swz<D>(rr, HALF + 8 * fg)) = l1;
-    };
 
     auto step = [&](int i, Regs& R, Regs& Rn) __attribute__((always_inline)) {
         const int c = chunk_of(i);
@@ -741,21 +711,19 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dkv_kernel(const BwdParams p)
         if (n < C && !valid) R = Regs{};  // rows past the end: zero inputs
         // ---- P1: q~, k~, v, do tiles and the state-gradient copy; prefetch ----
         float2 cs[8];
-        angles(i, cs);
+        rw.angles(i, cs);
         float x[16];
         widen8(R.q[0], x);
         widen8(R.q[1], x + 8);
-        norm_rotate(x, sm.w[0], cs, 1.0f);
-        st16_split(sm.q, sm.q_lo, x);
+        rw.norm_rotate(x, sm.w[0], cs, 1.0f);
+        rw.store_split(sm.q, sm.q_lo, x);
         widen8(R.k[0], x);
         widen8(R.k[1], x + 8);
-        const float rk = norm_rotate(x, sm.w[1], cs, kscale);
-        st16_split(sm.k, sm.k_lo, x);
+        const float rk = rw.norm_rotate(x, sm.w[1], cs, kscale);
+        rw.store_split(sm.k, sm.k_lo, x);
         // (value selects: a conditional between two lvalues would select addresses, in memory)
-        *reinterpret_cast<uint4*>(sm.v + swz<D>(rr, 8 * fg)) = R.v[0];
-        *reinterpret_cast<uint4*>(sm.v + swz<D>(rr, HALF + 8 * fg)) = R.v[1];
-        *reinterpret_cast<uint4*>(sm.dO + swz<D>(rr, 8 * fg)) = R.dO[0];
-        *reinterpret_cast<uint4*>(sm.dO + swz<D>(rr, HALF + 8 * fg)) = R.dO[1];
+        rw.store_raw(sm.v, R.v);
+        rw.store_raw(sm.dO, R.dO);
 #pragma unroll
         for (int cc = 0; cc < NW; ++cc)
 #pragma unroll
@@ -767,7 +735,7 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dkv_kernel(const BwdParams p)
         if (c > 0) load(c - 1, Rn);
         __syncthreads();
         // ---- P2: dv (value columns of w), dk~ (key columns of w), then the dS update ----
-        if (wave == 0 && c > 0) fill_table(i + 1);
+        if (wave == 0 && c > 0) rw.fill_table(i + 1, chunk_pos(i + 1));
         float mk[16], rd[16];
         load16<D>(sm, 0, lane, mk);
         if (n == C) {
@@ -848,7 +816,7 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dkv_kernel(const BwdParams p)
         __syncthreads();
         // ---- P3: dk = QK-norm^T(RoPE^T(dk~) / sqrt(d)) ----
         {
-            angles(i, cs);
+            rw.angles(i, cs);
             float dkt[16];
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
