@@ -55,7 +55,7 @@ typedef enum {
     LT_OK = 0,
     LT_ERR_INVALID_ARG = 1, /* null/misaligned pointer, non-positive size, lambda outside [0,1],
                                rope_base <= 0, eps < 0 or not finite */
-    LT_ERR_UNSUPPORTED = 2, /* a valid request this build does not implement (d, dtype, H, chunk) */
+    LT_ERR_UNSUPPORTED = 2, /* a valid request the library does not implement (d, dtype, H, chunk) */
     LT_ERR_WORKSPACE = 3,   /* workspace pointer missing or smaller than the size query says */
     LT_ERR_HIP = 4          /* the HIP runtime reported an error while enqueuing */
 } lt_status;
@@ -81,7 +81,7 @@ lt_status lightning_state_init(float* state, int B, int H, int d, const float* i
 /* Chunk length and number of sequence segments lightning_prefill will use for this shape when
  * called with the same `chunk` and `segments` requests (0 = automatic), and the number of tokens
  * in each segment but the last (which holds the rest of the sequence, never more).  Any output
- * pointer may be NULL.  Returns LT_ERR_UNSUPPORTED for a request the build does not implement. */
+ * pointer may be NULL.  Returns LT_ERR_UNSUPPORTED for a request the library does not implement. */
 lt_status lightning_prefill_plan(int B, int T, int H, int d, int dtype, int chunk, int segments,
                                  int* chunk_out, int* segments_out, int* segment_len_out);
 
