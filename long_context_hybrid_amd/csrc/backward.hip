@@ -173,16 +173,18 @@ __device__ __forceinline__ uint4 pack8(const float* x) {
                       pack_bf16x2(x[6], x[7]));
 }
 
-// Shared per-workgroup set-up: norm weights, decay tables, the first RoPE table.
-template <int D>
-__device__ __forceinline__ void setup_common(const BwdParams& p, BwdSmem<D>& sm, int h,
-                                             float l2l, bool transposed_scores) {
+// Shared per-workgroup set-up: norm weights (the q, k and, where the layout has it, o rows of
+// sm.w) and the decay tables.
+template <int D, class SM>
+__device__ __forceinline__ void setup_common(const BwdParams& p, SM& sm, int h, float l2l,
+                                             bool transposed_scores) {
     constexpr int NT = BCfg<D>::NT;
+    constexpr int NWT = sizeof(sm.w) / sizeof(sm.w[0]);
     for (int i = threadIdx.x; i < D; i += NT) {
         const size_t o = (size_t)h * p.w_stride + i;
         sm.w[0][i] = p.qw[o];
         sm.w[1][i] = p.kw[o];
-        sm.w[2][i] = p.ow ? p.ow[o] : 1.0f;
+        if constexpr (NWT > 2) sm.w[NWT - 1][i] = p.ow ? p.ow[o] : 1.0f;
     }
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x, lm = lane & 31, lh = lane >> 5;
@@ -204,8 +206,8 @@ __device__ __forceinline__ void setup_common(const BwdParams& p, BwdSmem<D>& sm,
 
 // 16 decay factors of this lane: table part `part` (0 score decay, 1 lambda^(row+1),
 // 2 lambda^(C-1-row))
-template <int D>
-__device__ __forceinline__ void load16(const BwdSmem<D>& sm, int part, int lane, float* dst) {
+template <class SM>
+__device__ __forceinline__ void load16(const SM& sm, int part, int lane, float* dst) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         const float4 x = sm.dec[4 * part + g][lane];
@@ -218,19 +220,21 @@ __device__ __forceinline__ void load16(const BwdSmem<D>& sm, int part, int lane,
 // cos/sin(p0 f_i) of each processing step is filled by wavefront 0, one frequency per lane, by
 // advancing the previous step's entry by one chunk (forward or back) and recomputing it exactly
 // (fp64 angle reduction) every kRopeAnchorB steps; each thread rotates it by cos/sin(rr f_i).
-template <int D>
+// `t` is the thread's index among the row-work threads; the table has NSLOT slots, one per
+// processing step modulo NSLOT.
+template <int D, class SM, int NSLOT = 2>
 struct RowWork {
     static constexpr int HALF = D / 2, TPR = D / 16;
-    BwdSmem<D>& sm;
+    SM& sm;
     const BwdParams& p;
     int rr, fg;
     float2 tstep;   // rotation by one processing step (one chunk forward or back)
     float2 rot[8];  // cos/sin(rr f) of this thread's frequencies
 
-    __device__ __forceinline__ RowWork(BwdSmem<D>& s, const BwdParams& params, int dir)
+    __device__ __forceinline__ RowWork(SM& s, const BwdParams& params, int dir, int t)
         : sm(s), p(params) {
-        rr = threadIdx.x / TPR;
-        fg = threadIdx.x % TPR;
+        rr = t / TPR;
+        fg = t % TPR;
         const int lane = threadIdx.x & 63;
         rope_cos_sin(dir * C, p.inv_freq_rev[lane < HALF ? lane : HALF - 1], tstep.x, tstep.y);
 #pragma unroll
@@ -244,17 +248,17 @@ struct RowWork {
         if (step % kRopeAnchorB == 0) {
             rope_cos_sin(pos, frev, e.x, e.y);
         } else {
-            const float2 a = sm.rope[(step - 1) & 1][fi];
+            const float2 a = sm.rope[(step - 1) & (NSLOT - 1)][fi];
             e.x = a.x * tstep.x - a.y * tstep.y;
             e.y = a.y * tstep.x + a.x * tstep.y;
         }
-        if (lane < HALF) sm.rope[step & 1][lane] = e;
+        if (lane < HALF) sm.rope[step & (NSLOT - 1)][lane] = e;
     }
     // cos/sin of (p0 + rr) f for this thread's 8 frequencies
     __device__ __forceinline__ void angles(int step, float2* cs) const {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const float2 t = sm.rope[step & 1][8 * fg + u];
+            const float2 t = sm.rope[step & (NSLOT - 1)][8 * fg + u];
             cs[u] = make_float2(t.x * rot[u].x - t.y * rot[u].y, t.y * rot[u].x + t.x * rot[u].y);
         }
     }
@@ -322,7 +326,7 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
     const uint16_t* gdy = static_cast<const uint16_t*>(p.dy) + base + 8 * fg;
 
     setup_common<D>(p, sm, h, l2l, true);
-    RowWork<D> rw(sm, p, 1);
+    RowWork<D, BwdSmem<D>> rw(sm, p, 1, threadIdx.x);
     auto chunk_pos = [&](int chunk) { return p.pos0 + t_begin + (int64_t)chunk * C; };
     if (wave == 0) rw.fill_table(0, chunk_pos(0));
 
@@ -400,8 +404,8 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
         // ---- P2: o = diag(lambda^(i+1)) Q~ S + (K~ Q~^T (.) D)^T V for value columns of w ----
         if (wave == 0 && c + 1 < n_chunks) rw.fill_table(i + 1, chunk_pos(c + 1));
         float mk[16], rf[16];
-        load16<D>(sm, 0, lane, mk);
-        load16<D>(sm, 1, lane, rf);
+        load16(sm, 0, lane, mk);
+        load16(sm, 1, lane, rf);
         // The intra-chunk part of o is recomputed to about fp32 accuracy (hi/lo parts of q~, k~
         // and the scores): the output norm's gradient scales with 1/||o_t||, and the rows where
         // o_t is small (mostly the first tokens of a sequence, where o_t = (q~_t . k~_t) v_t)
@@ -489,8 +493,8 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
         __syncthreads();
         // ---- P4: dq~ for key columns of w; W and S updates for value columns of w ----
         {
-            load16<D>(sm, 0, lane, mk);
-            load16<D>(sm, 1, lane, rf);
+            load16(sm, 0, lane, mk);
+            load16(sm, 1, lane, rf);
             f32x16 dpt = {}, dq = {};
 #pragma unroll
             for (int s8 = 0; s8 < D / 16; ++s8) {
@@ -519,7 +523,7 @@ __global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) 
             // S <- lambda^n S + sum_j k~_j^T lambda^(n-1-j) v_j
             float rd[16];
             if (n == C) {
-                load16<D>(sm, 2, lane, rd);
+                load16(sm, 2, lane, rd);
             } else {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -642,234 +646,307 @@ __global__ void __launch_bounds__(256) bwd_scan_kernel(const BwdParams p, int dd
 }
 
 // ============================ backward sweep: dk, dv =========================================
+// Warp-specialised: wavefronts 0 .. NW-1 own the state gradient (value columns 32 w ..) and do
+// the MFMA work of a chunk; wavefronts NW .. 2 NW-1 do the row work (loads, the q~/k~ prologue,
+// the dk epilogue), so on every SIMD one wavefront's VALU work overlaps the other's MFMA work.
+// The chunk tiles are double-buffered: in step s the row wavefronts stage chunk s (processing
+// order, backward in time) and finish the dk of chunk s - 2 while the MFMA wavefronts process
+// chunk s - 1.  Each step has two phases: (A) the MFMA wavefronts copy the state gradient to
+// LDS and the row wavefronts read the staged dk~ of chunk s - 2; (B) everything else.
 template <int D>
-__global__ void __launch_bounds__(BCfg<D>::NT) bwd_dkv_kernel(const BwdParams p) {
+struct alignas(16) DkvSmem {
+    using G = BCfg<D>;
+    struct alignas(16) Tiles {
+        __bf16 q[C * D], k[C * D], q_lo[C * D], k_lo[C * D], v[C * D], dO[C * D];
+    };
+    Tiles t[2];
+    alignas(16) __bf16 st[D * D];        // state-gradient copy, [value][key]
+    alignas(16) float stage[C * G::OS];  // dk~ of a chunk (and the weight-gradient sums at the end)
+    alignas(16) float2 rope[4][64];      // cos/sin(p0 f_i) of four consecutive steps
+    alignas(16) float w[2][D];           // norm weights q, k
+    alignas(16) float4 dec[12][64];      // as in BwdSmem
+};
+
+template <int D>
+__global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dkv_kernel(const BwdParams p) {
     using G = BCfg<D>;
     constexpr int NW = G::NW, HALF = G::HALF, TPR = G::TPR, OS = G::OS;
-    __shared__ BwdSmem<D> sm;
+    __shared__ DkvSmem<D> sm;
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, lm = lane & 31, lh = lane >> 5;
+    const bool is_math = wave < NW;
     const int seg = blockIdx.x % p.P, bh = blockIdx.x / p.P;
     const int b = bh / p.H, h = bh - b * p.H;
     const int t_begin = seg * p.L, t_end = min(p.T, t_begin + p.L);
     const int n_chunks = (t_end - t_begin + C - 1) / C;
+    const int n_steps = n_chunks + 2;
     const float l2l = p.log2_lambda[h];
     const size_t rs = (size_t)p.H * D;
     const size_t base = ((size_t)b * p.T * p.H + h) * D;
     const size_t dd = (size_t)D * D;
-    const int rr = threadIdx.x / TPR, fg = threadIdx.x % TPR;
-    const uint16_t* gq = static_cast<const uint16_t*>(p.q) + base + 8 * fg;
-    const uint16_t* gk = static_cast<const uint16_t*>(p.k) + base + 8 * fg;
-    const uint16_t* gv = static_cast<const uint16_t*>(p.v) + base + 8 * fg;
-    const uint16_t* gdo = p.d_o + base + 8 * fg;
-
-    setup_common<D>(p, sm, h, l2l, false);
-    RowWork<D> rw(sm, p, -1);  // processing steps run backward over the chunks
     auto chunk_of = [&](int step) { return n_chunks - 1 - step; };
-    auto chunk_pos = [&](int step) { return p.pos0 + t_begin + (int64_t)chunk_of(step) * C; };
-    if (wave == 0) rw.fill_table(0, chunk_pos(0));
-
-    // state gradient at the segment's end
-    f32x16 dS[NW];
-    {
-        const float* src = p.seg_grad + ((size_t)bh * p.P + seg) * dd;
-#pragma unroll
-        for (int c = 0; c < NW; ++c)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                dS[c][r] = src[(size_t)(32 * c + acc_row(r, lh)) * D + 32 * wave + lm];
-    }
-    // the state gradient is kept lazily scaled like the dq sweep's state: dS = beta * dS_stored
-    float beta = 1.0f;
-    float* wacc_k = &sm.wacc[0][0][threadIdx.x];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) wacc_k[G::NT * e] = 0.0f;
-
-    struct Regs {
-        uint4 q[2], k[2], v[2], dO[2];
-    };
-    auto load = [&](int chunk, Regs& R) __attribute__((always_inline)) {
-        const int t0 = t_begin + chunk * C;
-        const size_t o = (size_t)min(t0 + rr, t_end - 1) * rs;
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const size_t oo = o + hf * HALF;
-            R.q[hf] = *reinterpret_cast<const uint4*>(gq + oo);
-            R.k[hf] = *reinterpret_cast<const uint4*>(gk + oo);
-            R.v[hf] = *reinterpret_cast<const uint4*>(gv + oo);
-            R.dO[hf] = *reinterpret_cast<const uint4*>(gdo + oo);
-        }
-    };
+    auto chunk_len = [&](int step) { return min(C, t_end - (t_begin + chunk_of(step) * C)); };
     const float kscale = 1.0f / sqrtf((float)D);
 
-    auto step = [&](int i, Regs& R, Regs& Rn) __attribute__((always_inline)) {
-        const int c = chunk_of(i);
-        const int t0 = t_begin + c * C;
-        const int n = min(C, t_end - t0);
-        const bool valid = rr < n;
-        if (n < C && !valid) R = Regs{};  // rows past the end: zero inputs
-        // ---- P1: q~, k~, v, do tiles and the state-gradient copy; prefetch ----
-        float2 cs[8];
-        rw.angles(i, cs);
-        float x[16];
-        widen8(R.q[0], x);
-        widen8(R.q[1], x + 8);
-        rw.norm_rotate(x, sm.w[0], cs, 1.0f);
-        rw.store_split(sm.q, sm.q_lo, x);
-        widen8(R.k[0], x);
-        widen8(R.k[1], x + 8);
-        const float rk = rw.norm_rotate(x, sm.w[1], cs, kscale);
-        rw.store_split(sm.k, sm.k_lo, x);
-        // (value selects: a conditional between two lvalues would select addresses, in memory)
-        rw.store_raw(sm.v, R.v);
-        rw.store_raw(sm.dO, R.dO);
-#pragma unroll
-        for (int cc = 0; cc < NW; ++cc)
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const uint2 pk = make_uint2(pack_bf16x2(dS[cc][4 * g4], dS[cc][4 * g4 + 1]),
-                                            pack_bf16x2(dS[cc][4 * g4 + 2], dS[cc][4 * g4 + 3]));
-                *reinterpret_cast<uint2*>(sm.st + swz<D>(32 * wave + lm, 32 * cc + 8 * g4 + 4 * lh)) = pk;
-            }
-        if (c > 0) load(c - 1, Rn);
-        __syncthreads();
-        // ---- P2: dv (value columns of w), dk~ (key columns of w), then the dS update ----
-        if (wave == 0 && c > 0) rw.fill_table(i + 1, chunk_pos(i + 1));
-        float mk[16], rd[16];
-        load16<D>(sm, 0, lane, mk);
-        if (n == C) {
-            load16<D>(sm, 2, lane, rd);
-        } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int j = acc_row(r, lh);
-                rd[r] = j < n ? pow_lambda(l2l, n - 1 - j) : 0.0f;
-            }
-        }
+    setup_common<D>(p, sm, h, l2l, false);
+
+    if (is_math) {
+        // ================== MFMA wavefronts: the state gradient and the chunk products ==========
+        f32x16 dS[NW];
         {
-            // P[i][j] = q~_i . k~_j and dP[i][j] = do_i . v_j with lane j, both masked by D.  P
-            // takes the hi/lo parts of q~ and k~ (and P V those of P): do_i is large where o_i
-            // is small, and there dv_j = sum_i P_ij do_i must not inherit bf16 score rounding.
-            f32x16 pm = {}, dpm = {}, dvv = {}, dkt = {};
+            const float* src = p.seg_grad + ((size_t)bh * p.P + seg) * dd;
 #pragma unroll
-            for (int s8 = 0; s8 < D / 16; ++s8) {
-                const bf16x8 qh = row8<D>(sm.q, lm, 16 * s8 + 8 * lh);
-                const bf16x8 kh = row8<D>(sm.k, lm, 16 * s8 + 8 * lh);
-                pm = mfma_bf16(qh, kh, pm);
-                pm = mfma_bf16(qh, row8<D>(sm.k_lo, lm, 16 * s8 + 8 * lh), pm);
-                pm = mfma_bf16(row8<D>(sm.q_lo, lm, 16 * s8 + 8 * lh), kh, pm);
-                const bf16x8 vr = row8<D>(sm.v, lm, 16 * s8 + 8 * lh);
-                dpm = mfma_bf16(row8<D>(sm.dO, lm, 16 * s8 + 8 * lh), vr, dpm);
-                // inter terms: K~ dS (value columns of w) and V dS^T (key columns of w)
-                dvv = mfma_bf16(row_acc<D>(sm.k, lm, s8, lh), acc_operand(dS[s8 / 2], s8 % 2), dvv);
-                dkt = mfma_bf16(vr, tr_nat<D>(sm.st, 16 * s8, 32 * wave, lane), dkt);
-            }
+            for (int c = 0; c < NW; ++c)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                pm[r] *= mk[r];
-                dpm[r] *= mk[r];
-                dvv[r] *= rd[r] * beta;
-                dkt[r] *= rd[r] * beta;
-            }
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                bf16x8 ph, pl;
-                acc_split(pm, st, ph, pl);
-                const bf16x8 db = tr_acc<D>(sm.dO, 16 * st, 32 * wave, lane);
-                dvv = mfma_bf16(ph, db, dvv);
-                dvv = mfma_bf16(pl, db, dvv);
-                dkt = mfma_bf16(acc_operand(dpm, st), tr_acc<D>(sm.q, 16 * st, 32 * wave, lane), dkt);
-            }
-            uint16_t* pdv = static_cast<uint16_t*>(p.dv) + base + (size_t)t0 * rs + 32 * wave + lm;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int j = acc_row(r, lh);
-                if (j < n) pdv[(size_t)j * rs] = to_bf16_bits(dvv[r]);
-                sm.stage[j * OS + 32 * wave + lm] = dkt[r];
-            }
+                for (int r = 0; r < 16; ++r)
+                    dS[c][r] = src[(size_t)(32 * c + acc_row(r, lh)) * D + 32 * wave + lm];
         }
-        {
-            // dS <- lambda^n dS + sum_i q~_i^T lambda^(i+1) do_i
-            float rf[16];
-            load16<D>(sm, 1, lane, rf);
-            const float b_next = beta * pow_lambda(l2l, n);
-            float inv = 1.0f;
-            if (b_next < 0x1p-20f) {
+        float beta = 1.0f;  // dS = beta * dS_stored (lazily scaled, as in the dq sweep)
+        __syncthreads();  // weights, tables, the first staged chunk's table
+        for (int s = 0; s < n_steps; ++s) {
+            const int i = s - 1;
+            const bool act = i >= 0 && i < n_chunks;
+            if (act) {
 #pragma unroll
                 for (int cc = 0; cc < NW; ++cc)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) dS[cc][r] *= b_next;
-                beta = 1.0f;
-            } else {
-                beta = b_next;
-                inv = 1.0f / b_next;
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const uint2 pk = make_uint2(pack_bf16x2(dS[cc][4 * g4], dS[cc][4 * g4 + 1]),
+                                                    pack_bf16x2(dS[cc][4 * g4 + 2], dS[cc][4 * g4 + 3]));
+                        *reinterpret_cast<uint2*>(sm.st + swz<D>(32 * wave + lm, 32 * cc + 8 * g4 + 4 * lh)) = pk;
+                    }
             }
+            __syncthreads();  // phase B
+            if (act) {
+                const auto& T = sm.t[i & 1];
+                const int c = chunk_of(i);
+                const int t0 = t_begin + c * C;
+                const int n = chunk_len(i);
+                // causal mask (.) D and the decay lambda^(n-1-j) of row j (zero past the end),
+                // read after each product's loop so they are not live across it
+                auto masks = [&](float* mk, float* rd) __attribute__((always_inline)) {
+                    load16(sm, 0, lane, mk);
+                    if (n == C) {
+                        load16(sm, 2, lane, rd);
+                    } else {
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                const bf16x8 db = scale8(tr_acc<D>(sm.dO, 16 * st, 32 * wave, lane), rf + 8 * st, inv);
+                        for (int r = 0; r < 16; ++r) {
+                            const int j = acc_row(r, lh);
+                            rd[r] = j < n ? pow_lambda(l2l, n - 1 - j) : 0.0f;
+                        }
+                    }
+                };
+                {
+                    // P[i][j] = q~_i . k~_j (lane j) from hi/lo parts (do_i is large where o_i is
+                    // small, and there dv_j = sum_i P_ij do_i must not inherit score rounding);
+                    // dv = (P (.) D)^T do + diag(lambda^(n-1-j)) K~ dS for value columns of w
+                    f32x16 pm = {}, dvv = {};
 #pragma unroll
-                for (int cc = 0; cc < NW; ++cc)
-                    dS[cc] = mfma_bf16(tr_acc<D>(sm.q, 16 * st, 32 * cc, lane), db, dS[cc]);
+                    for (int s8 = 0; s8 < D / 16; ++s8) {
+                        const bf16x8 qh = row8<D>(T.q, lm, 16 * s8 + 8 * lh);
+                        const bf16x8 kh = row8<D>(T.k, lm, 16 * s8 + 8 * lh);
+                        pm = mfma_bf16(qh, kh, pm);
+                        pm = mfma_bf16(qh, row8<D>(T.k_lo, lm, 16 * s8 + 8 * lh), pm);
+                        pm = mfma_bf16(row8<D>(T.q_lo, lm, 16 * s8 + 8 * lh), kh, pm);
+                        dvv = mfma_bf16(row_acc<D>(T.k, lm, s8, lh), acc_operand(dS[s8 / 2], s8 % 2), dvv);
+                    }
+                    float mk[16], rd[16];
+                    masks(mk, rd);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        pm[r] *= mk[r];
+                        dvv[r] *= rd[r] * beta;
+                    }
+#pragma unroll
+                    for (int st = 0; st < 2; ++st) {
+                        bf16x8 ph, pl;
+                        acc_split(pm, st, ph, pl);
+                        const bf16x8 db = tr_acc<D>(T.dO, 16 * st, 32 * wave, lane);
+                        dvv = mfma_bf16(ph, db, dvv);
+                        dvv = mfma_bf16(pl, db, dvv);
+                    }
+                    // row acc_row(r, lh) = 4 lh + (8 (r / 4) + r % 4): the lane part goes into
+                    // the pointer, the rest is a wave-uniform offset
+                    uint16_t* pdv = static_cast<uint16_t*>(p.dv) + base + (size_t)(t0 + 4 * lh) * rs +
+                                    32 * wave + lm;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int jr = 8 * (r / 4) + r % 4;
+                        if (jr + 4 * lh < n) pdv[(size_t)jr * rs] = to_bf16_bits(dvv[r]);
+                    }
+                }
+                {
+                    // dP[i][j] = do_i . v_j (lane j); dk~ = (dP (.) D)^T Q~ + diag(lambda^(n-1-j))
+                    // V dS^T for key columns of w, staged for the row wavefronts
+                    f32x16 dpm = {}, dkt = {};
+#pragma unroll
+                    for (int s8 = 0; s8 < D / 16; ++s8) {
+                        const bf16x8 vr = row8<D>(T.v, lm, 16 * s8 + 8 * lh);
+                        dpm = mfma_bf16(row8<D>(T.dO, lm, 16 * s8 + 8 * lh), vr, dpm);
+                        dkt = mfma_bf16(vr, tr_nat<D>(sm.st, 16 * s8, 32 * wave, lane), dkt);
+                    }
+                    float mk[16], rd[16];
+                    masks(mk, rd);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        dpm[r] *= mk[r];
+                        dkt[r] *= rd[r] * beta;
+                    }
+#pragma unroll
+                    for (int st = 0; st < 2; ++st)
+                        dkt = mfma_bf16(acc_operand(dpm, st), tr_acc<D>(T.q, 16 * st, 32 * wave, lane), dkt);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sm.stage[acc_row(r, lh) * OS + 32 * wave + lm] = dkt[r];
+                }
+                {
+                    // dS <- lambda^n dS + sum_i q~_i^T lambda^(i+1) do_i
+                    float rf[16];
+                    load16(sm, 1, lane, rf);
+                    const float b_next = beta * pow_lambda(l2l, n);
+                    float inv = 1.0f;
+                    if (b_next < 0x1p-20f) {
+#pragma unroll
+                        for (int cc = 0; cc < NW; ++cc)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) dS[cc][r] *= b_next;
+                        beta = 1.0f;
+                    } else {
+                        beta = b_next;
+                        inv = 1.0f / b_next;
+                    }
+#pragma unroll
+                    for (int st = 0; st < 2; ++st) {
+                        const bf16x8 db = scale8(tr_acc<D>(T.dO, 16 * st, 32 * wave, lane), rf + 8 * st, inv);
+#pragma unroll
+                        for (int cc = 0; cc < NW; ++cc)
+                            dS[cc] = mfma_bf16(tr_acc<D>(T.q, 16 * st, 32 * cc, lane), db, dS[cc]);
+                    }
+                }
             }
+            __syncthreads();  // next phase A
         }
-        __syncthreads();
-        // ---- P3: dk = QK-norm^T(RoPE^T(dk~) / sqrt(d)) ----
-        {
-            rw.angles(i, cs);
-            float dkt[16];
+        __syncthreads();  // the row wavefronts' weight-gradient sums are in the stage
+    } else {
+        // ===================== row wavefronts: loads, prologue, dk epilogue =====================
+        const int rt = threadIdx.x - G::NT;  // index among the row-work threads
+        RowWork<D, DkvSmem<D>, 4> rw(sm, p, -1, rt);
+        const int rr = rw.rr, fg = rw.fg;
+        const uint16_t* gq = static_cast<const uint16_t*>(p.q) + base + 8 * fg;
+        const uint16_t* gk = static_cast<const uint16_t*>(p.k) + base + 8 * fg;
+        const uint16_t* gv = static_cast<const uint16_t*>(p.v) + base + 8 * fg;
+        const uint16_t* gdo = p.d_o + base + 8 * fg;
+        auto chunk_pos = [&](int step) { return p.pos0 + t_begin + (int64_t)chunk_of(step) * C; };
+        struct Regs {
+            uint4 q[2], k[2], v[2], dO[2];
+        };
+        auto load = [&](int step, Regs& R) __attribute__((always_inline)) {
+            const int t0 = t_begin + chunk_of(step) * C;
+            const size_t o = (size_t)min(t0 + rr, t_end - 1) * rs;
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
-                const float* src = sm.stage + rr * OS + hf * HALF + 8 * fg;
-                const float4 a = reinterpret_cast<const float4*>(src)[0];
-                const float4 bq = reinterpret_cast<const float4*>(src)[1];
-                dkt[8 * hf + 0] = a.x; dkt[8 * hf + 1] = a.y; dkt[8 * hf + 2] = a.z; dkt[8 * hf + 3] = a.w;
-                dkt[8 * hf + 4] = bq.x; dkt[8 * hf + 5] = bq.y; dkt[8 * hf + 6] = bq.z; dkt[8 * hf + 7] = bq.w;
+                const size_t oo = o + hf * HALF;
+                R.q[hf] = *reinterpret_cast<const uint4*>(gq + oo);
+                R.k[hf] = *reinterpret_cast<const uint4*>(gk + oo);
+                R.v[hf] = *reinterpret_cast<const uint4*>(gv + oo);
+                R.dO[hf] = *reinterpret_cast<const uint4*>(gdo + oo);
             }
-            widen8(R.k[0], x);
-            widen8(R.k[1], x + 8);
-            float dx[16], dot = 0.0f;
+        };
+        float wk_acc[16];  // this thread's dL/dw_k partial sums
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float lo = (cs[u].x * dkt[u] + cs[u].y * dkt[8 + u]) * kscale;
-                const float hi = (cs[u].x * dkt[8 + u] - cs[u].y * dkt[u]) * kscale;
-                const float xl = x[u] * rk, xh = x[8 + u] * rk;
-                wacc_k[G::NT * u] = fmaf(lo, xl, wacc_k[G::NT * u]);
-                wacc_k[G::NT * (8 + u)] = fmaf(hi, xh, wacc_k[G::NT * (8 + u)]);
-                dx[u] = lo * sm.w[1][8 * fg + u];
-                dx[8 + u] = hi * sm.w[1][HALF + 8 * fg + u];
-                x[u] = xl;
-                x[8 + u] = xh;
-                dot = fmaf(dx[u], xl, dot);
-                dot = fmaf(dx[8 + u], xh, dot);
-            }
-            dot = group_sum<TPR>(dot) * (1.0f / D);
+        for (int e = 0; e < 16; ++e) wk_acc[e] = 0.0f;
+        if (wave == NW) rw.fill_table(0, chunk_pos(0));
+        Regs cur;
+        load(0, cur);
+        uint4 k1[2] = {}, k2[2] = {};  // raw keys of the two previously staged chunks
+        float rk1 = 0.0f, rk2 = 0.0f;  // their 1/rms
+        __syncthreads();
+        for (int s = 0; s < n_steps; ++s) {
+            const int e = s - 2;  // the chunk whose dk is finished in this step
+            const bool ep = e >= 0 && e < n_chunks;
+            float dkt[16];
+            if (ep) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) dx[e] = rk * (dx[e] - x[e] * dot);
-            if (valid) {
-                uint16_t* pdk = static_cast<uint16_t*>(p.dk) + base + (size_t)(t0 + rr) * rs + 8 * fg;
-                *reinterpret_cast<uint4*>(pdk) = pack8(dx);
-                *reinterpret_cast<uint4*>(pdk + HALF) = pack8(dx + 8);
+                for (int hf = 0; hf < 2; ++hf) {
+                    const float* src = sm.stage + rr * OS + hf * HALF + 8 * fg;
+                    const float4 a = reinterpret_cast<const float4*>(src)[0];
+                    const float4 bq = reinterpret_cast<const float4*>(src)[1];
+                    dkt[8 * hf + 0] = a.x; dkt[8 * hf + 1] = a.y; dkt[8 * hf + 2] = a.z; dkt[8 * hf + 3] = a.w;
+                    dkt[8 * hf + 4] = bq.x; dkt[8 * hf + 5] = bq.y; dkt[8 * hf + 6] = bq.z; dkt[8 * hf + 7] = bq.w;
+                }
             }
+            __syncthreads();  // phase B
+            if (ep) {
+                // dk = QK-norm^T(RoPE^T(dk~) / sqrt(d)) for chunk e
+                float2 cs[8];
+                rw.angles(e, cs);
+                float x[16], dx[16], dot = 0.0f;
+                widen8(k2[0], x);
+                widen8(k2[1], x + 8);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float lo = (cs[u].x * dkt[u] + cs[u].y * dkt[8 + u]) * kscale;
+                    const float hi = (cs[u].x * dkt[8 + u] - cs[u].y * dkt[u]) * kscale;
+                    const float xl = x[u] * rk2, xh = x[8 + u] * rk2;
+                    wk_acc[u] = fmaf(lo, xl, wk_acc[u]);
+                    wk_acc[8 + u] = fmaf(hi, xh, wk_acc[8 + u]);
+                    dx[u] = lo * sm.w[1][8 * fg + u];
+                    dx[8 + u] = hi * sm.w[1][HALF + 8 * fg + u];
+                    x[u] = xl;
+                    x[8 + u] = xh;
+                    dot = fmaf(dx[u], xl, dot);
+                    dot = fmaf(dx[8 + u], xh, dot);
+                }
+                dot = group_sum<TPR>(dot) * (1.0f / D);
+#pragma unroll
+                for (int q = 0; q < 16; ++q) dx[q] = rk2 * (dx[q] - x[q] * dot);
+                if (rr < chunk_len(e)) {
+                    uint16_t* pdk = static_cast<uint16_t*>(p.dk) + base +
+                                    (size_t)(t_begin + chunk_of(e) * C + rr) * rs + 8 * fg;
+                    *reinterpret_cast<uint4*>(pdk) = pack8(dx);
+                    *reinterpret_cast<uint4*>(pdk + HALF) = pack8(dx + 8);
+                }
+            }
+            float rk = 0.0f;
+            Regs nxt = cur;
+            if (s < n_chunks) {
+                // stage chunk s: q~, k~ (hi and lo parts), v, do; rows past a partial chunk's end
+                // get zero inputs (their loads re-read the last row)
+                auto& T = sm.t[s & 1];
+                if (rr >= chunk_len(s)) cur = Regs{};
+                float2 cs[8];
+                rw.angles(s, cs);
+                float x[16];
+                widen8(cur.q[0], x);
+                widen8(cur.q[1], x + 8);
+                rw.norm_rotate(x, sm.w[0], cs, 1.0f);
+                rw.store_split(T.q, T.q_lo, x);
+                widen8(cur.k[0], x);
+                widen8(cur.k[1], x + 8);
+                rk = rw.norm_rotate(x, sm.w[1], cs, kscale);
+                rw.store_split(T.k, T.k_lo, x);
+                rw.store_raw(T.v, cur.v);
+                rw.store_raw(T.dO, cur.dO);
+                if (s + 1 < n_chunks) load(s + 1, nxt);
+                if (wave == NW && s + 1 < n_chunks) rw.fill_table(s + 1, chunk_pos(s + 1));
+            }
+            k2[0] = k1[0]; k2[1] = k1[1]; rk2 = rk1;
+            k1[0] = cur.k[0]; k1[1] = cur.k[1]; rk1 = rk;
+            cur = nxt;
+            __syncthreads();  // next phase A
         }
-    };
-
-    Regs cur;
-    load(n_chunks - 1, cur);
-    __syncthreads();
-    for (int i = 0; i < n_chunks; ++i) {
-        Regs nxt = cur;
-        step(i, cur, nxt);
-        cur = nxt;
+        // the weight-gradient partial sums of the 32 rows, via the stage
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            sm.stage[rr * OS + (q < 8 ? 0 : HALF) + 8 * fg + (q & 7)] = wk_acc[q];
+        __syncthreads();
     }
     if (p.wgrad) {
         const size_t nbp = (size_t)p.B * p.H * p.P;
-        __syncthreads();
-        for (int f = threadIdx.x; f < D; f += G::NT) {
-            const int tf = (f % HALF) / 8, e = (f >= HALF ? 8 : 0) + (f & 7);
-            float s = 0.0f;
-            for (int r = 0; r < C; ++r) s += sm.wacc[0][e][r * TPR + tf];
-            p.wgrad[(nbp + (size_t)bh * p.P + seg) * D + f] = s;
+        for (int f = threadIdx.x; f < D; f += 2 * G::NT) {
+            float sum = 0.0f;
+            for (int r = 0; r < C; ++r) sum += sm.stage[r * OS + f];
+            p.wgrad[(nbp + (size_t)bh * p.P + seg) * D + f] = sum;
         }
     }
 }
@@ -911,7 +988,7 @@ hipError_t launch_prefill_backward(const BwdParams& p, const ChunkParams& fwd_cp
     bwd_scan_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(p, D * D);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev[2] && (err = hipEventRecord(ev[2], stream)) != hipSuccess) return err;
-    bwd_dkv_kernel<D><<<dim3(BH * p.P), dim3(BCfg<D>::NT), 0, stream>>>(p);
+    bwd_dkv_kernel<D><<<dim3(BH * p.P), dim3(2 * BCfg<D>::NT), 0, stream>>>(p);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev[3] && (err = hipEventRecord(ev[3], stream)) != hipSuccess) return err;
     if (p.wgrad) {
