@@ -54,28 +54,27 @@ struct BCfg {
     static_assert(NT / TPR == C, "the row-op threads cover one chunk");
 };
 
+// LDS of the forward (dq) sweep.  The chunk tiles q~, k~, v are double-buffered: the row
+// wavefronts stage chunk c + 1 while the MFMA wavefronts still read chunk c.
 template <int D>
-struct alignas(16) BwdSmem {
+struct alignas(16) DqSmem {
     using G = BCfg<D>;
-    alignas(16) __bf16 q[C * D];   // q~
-    alignas(16) __bf16 k[C * D];   // k~
-    alignas(16) __bf16 v[C * D];
-    alignas(16) __bf16 dO[C * D];  // do
-    alignas(16) __bf16 dOs[C * D];   // lambda^(cC + i + 1) do (dq sweep: the W update's operand)
-    alignas(16) __bf16 q_lo[C * D];  // q~ - bf16(q~) and k~ - bf16(k~)
+    struct alignas(16) Tiles {
+        __bf16 q[C * D], k[C * D], v[C * D];  // q~, k~ (bf16 parts), v
+    };
+    Tiles t[2];
+    alignas(16) __bf16 q_lo[C * D];      // q~ - bf16(q~) and k~ - bf16(k~) of the staged chunk
     alignas(16) __bf16 k_lo[C * D];
-    alignas(16) __bf16 st[D * D];  // state (or state gradient) copy, [value][key]
-    alignas(16) float stage[C * G::OS];  // fp32 [token][feature] stage of o, dq~ or dk~
-    alignas(16) float2 rope[2][64];      // cos/sin(p0 f_i) of this chunk and the next
+    alignas(16) __bf16 dO[C * D];        // do
+    alignas(16) __bf16 st[D * D];        // state copy, [value][key]
+    alignas(16) float so[C * G::OS];     // fp32 [token][feature] stage of o
+    alignas(16) float sq[C * G::OS];     // ... and of dq~
+    alignas(16) float2 rope[4][64];      // cos/sin(p0 f_i) of four consecutive chunks
     alignas(16) float w[3][D];           // norm weights q, k, o
     // decay factors per lane, as float4 groups g < 12 stored [g][lane] (consecutive lanes read
     // consecutive 16-byte words): groups [0, 4) the score-tile decay, [4, 8) lambda^(row + 1),
     // [8, 12) lambda^(C-1-row) of the lane's accumulator rows
     alignas(16) float4 dec[12][64];
-    // norm-weight gradient partial sums of each row-op thread (its row, its 16 features), stored
-    // [which][feature slot][thread] so that a wavefront's accesses hit consecutive banks:
-    // which 0 = q (or k), 1 = o
-    alignas(16) float wacc[2][16][BCfg<D>::NT];
 };
 
 template <int D>
@@ -171,6 +170,25 @@ __device__ __forceinline__ void widen8(uint4 x, float* o) {
 __device__ __forceinline__ uint4 pack8(const float* x) {
     return make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
                       pack_bf16x2(x[6], x[7]));
+}
+
+// bf16 copy of a state-shaped accumulator set A[cc] (key rows 32 cc + acc_row(r, lh), value
+// column 32 w + lm) into st[value][key].  With kRecompute the lane index passes through an
+// empty asm statement, so that the 16 swizzled addresses are recomputed at each call instead of
+// being held in registers across a sweep's loop (for a kernel short of registers).
+template <int D, int NW, bool kRecompute>
+__device__ __forceinline__ void store_st(__bf16* st, const f32x16* A, int wave, int lane_in) {
+    int lane = lane_in;
+    if constexpr (kRecompute) asm volatile("" : "+v"(lane));
+    const int lm = lane & 31, lh = lane >> 5;
+#pragma unroll
+    for (int cc = 0; cc < NW; ++cc)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const uint2 pk = make_uint2(pack_bf16x2(A[cc][4 * g4], A[cc][4 * g4 + 1]),
+                                        pack_bf16x2(A[cc][4 * g4 + 2], A[cc][4 * g4 + 3]));
+            *reinterpret_cast<uint2*>(st + swz<D>(32 * wave + lm, 32 * cc + 8 * g4 + 4 * lh)) = pk;
+        }
 }
 
 // Shared per-workgroup set-up: norm weights (the q, k and, where the layout has it, o rows of
@@ -301,326 +319,362 @@ struct RowWork {
 };
 
 // ============================== forward sweep: dq, dg, do, W ==================================
+// Warp-specialised like the dk/dv sweep: wavefronts 0 .. NW-1 hold the state S and the entry-
+// state gradient W (value columns 32 w ..) and do the MFMA work; wavefronts NW .. 2 NW-1 do the
+// row work.  A chunk needs its do (row work) between its o and its dq~ (MFMA work), so a step
+// has three phases.  In step s, for chunk c = s - 1:
+//   P1  MFMA: S_c copy to LDS, o_c                      rows: dq of chunk c - 1 (epilogue)
+//   P2  MFMA: S_(c+1) = lambda^n S_c + K~^T V           rows: the output-norm gradients, do_c
+//   P3  MFMA: dq~_c, W += Q~^T Lambda do_c              rows: q~, k~, v of chunk c + 1 (prologue)
 template <int D>
-__global__ void __launch_bounds__(BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) {
+__global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) {
     using G = BCfg<D>;
     constexpr int NW = G::NW, HALF = G::HALF, TPR = G::TPR, OS = G::OS;
-    __shared__ BwdSmem<D> sm;
+    __shared__ DqSmem<D> sm;
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, lm = lane & 31, lh = lane >> 5;
+    const bool is_math = wave < NW;
     const int seg = blockIdx.x % p.P, bh = blockIdx.x / p.P;
     const int b = bh / p.H, h = bh - b * p.H;
     const int t_begin = seg * p.L, t_end = min(p.T, t_begin + p.L);
     const int n_chunks = (t_end - t_begin + C - 1) / C;
+    const int n_steps = n_chunks + 2;
     const float l2l = p.log2_lambda[h];
     const size_t rs = (size_t)p.H * D;                      // elements between tokens
     const size_t base = ((size_t)b * p.T * p.H + h) * D;     // token 0 of (b, h)
     const size_t dd = (size_t)D * D;
-    // row-op role: row rr of the chunk, features 8 fg + u and HALF + 8 fg + u (u < 8)
-    const int rr = threadIdx.x / TPR, fg = threadIdx.x % TPR;
-    const uint16_t* gq = static_cast<const uint16_t*>(p.q) + base + 8 * fg;
-    const uint16_t* gk = static_cast<const uint16_t*>(p.k) + base + 8 * fg;
-    const uint16_t* gv = static_cast<const uint16_t*>(p.v) + base + 8 * fg;
-    const uint16_t* gg = static_cast<const uint16_t*>(p.g) + base + 8 * fg;
-    const uint16_t* gdy = static_cast<const uint16_t*>(p.dy) + base + 8 * fg;
+    auto chunk_len = [&](int c) { return min(C, t_end - (t_begin + c * C)); };
 
     setup_common<D>(p, sm, h, l2l, true);
-    RowWork<D, BwdSmem<D>> rw(sm, p, 1, threadIdx.x);
-    auto chunk_pos = [&](int chunk) { return p.pos0 + t_begin + (int64_t)chunk * C; };
-    if (wave == 0) rw.fill_table(0, chunk_pos(0));
 
-    // forward entry state and the segment's entry-state gradient W
-    f32x16 S[NW], W[NW];
-    {
-        const float* src = p.P > 1 ? p.fwd_states + ((size_t)bh * p.SP + (size_t)seg * p.SM) * dd
-                                   : (p.state_in ? p.state_in + (size_t)bh * dd : nullptr);
-#pragma unroll
-        for (int c = 0; c < NW; ++c)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                S[c][r] = src ? src[(size_t)(32 * c + acc_row(r, lh)) * D + 32 * wave + lm] : 0.0f;
-                W[c][r] = 0.0f;
-            }
-    }
-    // wacc_x[NT * e]: this thread's partial sum for feature slot e
-    // The state is kept lazily scaled, state = alpha * S: a chunk multiplies alpha by lambda^n
-    // and divides the values it adds by the new alpha instead of rescaling the 64 accumulator
-    // registers; S absorbs alpha when it would fall below 2^-20 (every chunk for lambda = 0).
-    float alpha = 1.0f;
-    float* wacc_q = &sm.wacc[0][0][threadIdx.x];
-    float* wacc_o = &sm.wacc[1][0][threadIdx.x];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) wacc_q[G::NT * e] = wacc_o[G::NT * e] = 0.0f;
-
-    struct Regs {
-        uint4 q[2], k[2], v[2], g[2], dy[2];
-    };
-    auto load = [&](int chunk, Regs& R) __attribute__((always_inline)) {
-        const int t0 = t_begin + chunk * C;
-        const size_t o = (size_t)min(t0 + rr, t_end - 1) * rs;
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const size_t oo = o + hf * HALF;
-            R.q[hf] = *reinterpret_cast<const uint4*>(gq + oo);
-            R.k[hf] = *reinterpret_cast<const uint4*>(gk + oo);
-            R.v[hf] = *reinterpret_cast<const uint4*>(gv + oo);
-            R.g[hf] = *reinterpret_cast<const uint4*>(gg + oo);
-            R.dy[hf] = *reinterpret_cast<const uint4*>(gdy + oo);
-        }
-    };
-    auto step = [&](int i, Regs& R, Regs& Rn) __attribute__((always_inline)) {
-        const int c = i;
-        const int t0 = t_begin + c * C;
-        const int n = min(C, t_end - t0);
-        const bool valid = rr < n;
-        // rows past the end of a partial chunk get zero inputs: their tile rows, do and every
-        // partial sum they enter are then zero (their loads re-read the last row)
-        if (n < C && !valid) R = Regs{};
-        // ---- P1: prologue (q~, k~, v tiles) and the state copy; prefetch the next chunk ----
-        float2 cs[8];
-        rw.angles(i, cs);
-        float x[16];
-        widen8(R.q[0], x);
-        widen8(R.q[1], x + 8);
-        const float rq = rw.norm_rotate(x, sm.w[0], cs, 1.0f);
-        rw.store_split(sm.q, sm.q_lo, x);
-        widen8(R.k[0], x);
-        widen8(R.k[1], x + 8);
-        rw.norm_rotate(x, sm.w[1], cs, 1.0f / sqrtf((float)D));
-        rw.store_split(sm.k, sm.k_lo, x);
-        rw.store_raw(sm.v, R.v);
-#pragma unroll
-        for (int cc = 0; cc < NW; ++cc)
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                // S[32 cc + 8 g4 + 4 lh + (0..3)][32 w + lm] -> st[32 w + lm][same keys]
-                const uint2 pk = make_uint2(pack_bf16x2(S[cc][4 * g4], S[cc][4 * g4 + 1]),
-                                            pack_bf16x2(S[cc][4 * g4 + 2], S[cc][4 * g4 + 3]));
-                *reinterpret_cast<uint2*>(sm.st + swz<D>(32 * wave + lm, 32 * cc + 8 * g4 + 4 * lh)) = pk;
-            }
-        if (c + 1 < n_chunks) load(c + 1, Rn);
-        __syncthreads();
-        // ---- P2: o = diag(lambda^(i+1)) Q~ S + (K~ Q~^T (.) D)^T V for value columns of w ----
-        if (wave == 0 && c + 1 < n_chunks) rw.fill_table(i + 1, chunk_pos(c + 1));
-        float mk[16], rf[16];
-        load16(sm, 0, lane, mk);
-        load16(sm, 1, lane, rf);
-        // The intra-chunk part of o is recomputed to about fp32 accuracy (hi/lo parts of q~, k~
-        // and the scores): the output norm's gradient scales with 1/||o_t||, and the rows where
-        // o_t is small (mostly the first tokens of a sequence, where o_t = (q~_t . k~_t) v_t)
-        // would otherwise carry the bf16 rounding of the scores into do_t, which then dominates
-        // the sums q~_i^T do_i of the state gradients.  The inter-chunk term q~ S keeps bf16
-        // operands: splitting them changed none of the measured gradients.
-        f32x16 pt = {}, o = {};
-#pragma unroll
-        for (int s8 = 0; s8 < D / 16; ++s8) {
-            const bf16x8 kv = row8<D>(sm.k, lm, 16 * s8 + 8 * lh);
-            const bf16x8 kl = row8<D>(sm.k_lo, lm, 16 * s8 + 8 * lh);
-            const bf16x8 qv = row8<D>(sm.q, lm, 16 * s8 + 8 * lh);
-            const bf16x8 ql = row8<D>(sm.q_lo, lm, 16 * s8 + 8 * lh);
-            pt = mfma_bf16(kv, qv, pt);  // P^T[j][i] += k~_j . q~_i
-            pt = mfma_bf16(kv, ql, pt);
-            pt = mfma_bf16(kl, qv, pt);
-            o = mfma_bf16(row_acc<D>(sm.q, lm, s8, lh), acc_operand(S[s8 / 2], s8 % 2), o);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            pt[r] *= mk[r];
-            o[r] *= rf[r] * alpha;
-        }
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            bf16x8 ph, pl;
-            acc_split(pt, st, ph, pl);
-            const bf16x8 vb = tr_acc<D>(sm.v, 16 * st, 32 * wave, lane);
-            o = mfma_bf16(ph, vb, o);
-            o = mfma_bf16(pl, vb, o);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sm.stage[acc_row(r, lh) * OS + 32 * wave + lm] = o[r];
-        __syncthreads();
-        // ---- P3: output norm and gate gradients: dg, do ----
+    if (is_math) {
+        // ========== MFMA wavefronts: state, entry-state gradient and the chunk products ==========
+        f32x16 S[NW], W[NW];
         {
-            float ov[16], gv[16], dyv[16];
+            const float* src = p.P > 1 ? p.fwd_states + ((size_t)bh * p.SP + (size_t)seg * p.SM) * dd
+                                       : (p.state_in ? p.state_in + (size_t)bh * dd : nullptr);
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const float* src = sm.stage + rr * OS + hf * HALF + 8 * fg;
-                const float4 a = reinterpret_cast<const float4*>(src)[0];
-                const float4 bq = reinterpret_cast<const float4*>(src)[1];
-                ov[8 * hf + 0] = a.x; ov[8 * hf + 1] = a.y; ov[8 * hf + 2] = a.z; ov[8 * hf + 3] = a.w;
-                ov[8 * hf + 4] = bq.x; ov[8 * hf + 5] = bq.y; ov[8 * hf + 6] = bq.z; ov[8 * hf + 7] = bq.w;
-                widen8(R.g[hf], gv + 8 * hf);
-                widen8(R.dy[hf], dyv + 8 * hf);
-            }
-            float ss = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) ss = fmaf(ov[e], ov[e], ss);
-            ss = group_sum<TPR>(ss);
-            const float ro = fast_rsqrt(ss * (1.0f / D) + p.eps);
-            float dn[16], dgv[16], dot = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int f = (e < 8 ? 0 : HALF) + 8 * fg + (e & 7);
-                const float nv = ov[e] * ro, s = sigmoidf_(gv[e]), wo = sm.w[2][f];
-                const float t = dyv[e] * s;
-                dn[e] = t * wo;
-                dgv[e] = dn[e] * nv * (1.0f - s);
-                dot = fmaf(dn[e], nv, dot);
-                wacc_o[G::NT * e] = fmaf(t, nv, wacc_o[G::NT * e]);
-                ov[e] = nv;
-            }
-            dot = group_sum<TPR>(dot) * (1.0f / D);
-            float dov[16];
-#pragma unroll
-            for (int e = 0; e < 16; ++e) dov[e] = ro * (dn[e] - ov[e] * dot);
-            rw.store(sm.dO, dov);
-            // the W update's operand: do scaled by lambda^(offset in the segment + 1)
-            const float wsc = pow_lambda(l2l, c * C + rr + 1);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) dn[e] = dov[e] * wsc;
-            rw.store(sm.dOs, dn);
-            if (valid) {
-                const size_t o2 = (size_t)(t0 + rr) * rs + 8 * fg;
-                uint16_t* pdg = static_cast<uint16_t*>(p.dg) + base + o2;
-                uint16_t* pdo = p.d_o + base + o2;
-                *reinterpret_cast<uint4*>(pdg) = pack8(dgv);
-                *reinterpret_cast<uint4*>(pdg + HALF) = pack8(dgv + 8);
-                *reinterpret_cast<uint4*>(pdo) = pack8(dov);
-                *reinterpret_cast<uint4*>(pdo + HALF) = pack8(dov + 8);
-            }
-        }
-        __syncthreads();
-        // ---- P4: dq~ for key columns of w; W and S updates for value columns of w ----
-        {
-            load16(sm, 0, lane, mk);
-            load16(sm, 1, lane, rf);
-            f32x16 dpt = {}, dq = {};
-#pragma unroll
-            for (int s8 = 0; s8 < D / 16; ++s8) {
-                const bf16x8 dv8 = row8<D>(sm.dO, lm, 16 * s8 + 8 * lh);
-                dpt = mfma_bf16(row8<D>(sm.v, lm, 16 * s8 + 8 * lh), dv8, dpt);  // v_j . do_i
-                dq = mfma_bf16(dv8, tr_nat<D>(sm.st, 16 * s8, 32 * wave, lane), dq);  // do S^T
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                dpt[r] *= mk[r];
-                dq[r] *= rf[r] * alpha;
-            }
-#pragma unroll
-            for (int st = 0; st < 2; ++st)
-                dq = mfma_bf16(acc_operand(dpt, st), tr_acc<D>(sm.k, 16 * st, 32 * wave, lane), dq);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sm.stage[acc_row(r, lh) * OS + 32 * wave + lm] = dq[r];
-            // W[k][v] += sum_i q~[i][k] lambda^(cC + i + 1) do[i][v]
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                const bf16x8 db = tr_acc<D>(sm.dOs, 16 * st, 32 * wave, lane);
-#pragma unroll
-                for (int cc = 0; cc < NW; ++cc)
-                    W[cc] = mfma_bf16(tr_acc<D>(sm.q, 16 * st, 32 * cc, lane), db, W[cc]);
-            }
-            // S <- lambda^n S + sum_j k~_j^T lambda^(n-1-j) v_j
-            float rd[16];
-            if (n == C) {
-                load16(sm, 2, lane, rd);
-            } else {
+            for (int cc = 0; cc < NW; ++cc)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int j = acc_row(r, lh);
-                    rd[r] = j < n ? pow_lambda(l2l, n - 1 - j) : 0.0f;
+                    S[cc][r] = src ? src[(size_t)(32 * cc + acc_row(r, lh)) * D + 32 * wave + lm] : 0.0f;
+                    W[cc][r] = 0.0f;
+                }
+        }
+        // The state is kept lazily scaled, state = alpha * S: a chunk multiplies alpha by
+        // lambda^n and divides the values it adds by the new alpha instead of rescaling the 64
+        // accumulator registers; S absorbs alpha when it would fall below 2^-20 (every chunk
+        // for lambda = 0).
+        float alpha = 1.0f;
+        __syncthreads();  // weights, decay tables and the first RoPE table
+        for (int s = 0; s < n_steps; ++s) {
+            const int c = s - 1;
+            const bool act = c >= 0 && c < n_chunks;
+            const auto& T = sm.t[c & 1];
+            const int n = act ? chunk_len(c) : 0;
+            const float alpha_c = alpha;  // the scale of S_c, for dq~
+            // ---- P1: st = S_c; o = diag(lambda^(i+1)) Q~ S + (K~ Q~^T (.) D)^T V ----
+            if (act) {
+                store_st<D, NW, true>(sm.st, S, wave, lane);
+                // The intra-chunk part of o is recomputed to about fp32 accuracy (hi/lo parts of
+                // q~, k~ and the scores): the output norm's gradient scales with 1/||o_t||, and
+                // the rows where o_t is small (mostly the first tokens of a sequence, where
+                // o_t = (q~_t . k~_t) v_t) would otherwise carry the bf16 rounding of the scores
+                // into do_t, which then dominates the sums q~_i^T do_i of the state gradients.
+                // The inter-chunk term q~ S keeps bf16 operands: splitting them changed none of
+                // the measured gradients.
+                f32x16 pt = {}, o = {};
+#pragma unroll
+                for (int s8 = 0; s8 < D / 16; ++s8) {
+                    const bf16x8 kv = row8<D>(T.k, lm, 16 * s8 + 8 * lh);
+                    const bf16x8 qv = row8<D>(T.q, lm, 16 * s8 + 8 * lh);
+                    pt = mfma_bf16(kv, qv, pt);  // P^T[j][i] += k~_j . q~_i
+                    pt = mfma_bf16(kv, row8<D>(sm.q_lo, lm, 16 * s8 + 8 * lh), pt);
+                    pt = mfma_bf16(row8<D>(sm.k_lo, lm, 16 * s8 + 8 * lh), qv, pt);
+                    o = mfma_bf16(row_acc<D>(T.q, lm, s8, lh), acc_operand(S[s8 / 2], s8 % 2), o);
+                }
+                float mk[16], rf[16];
+                load16(sm, 0, lane, mk);
+                load16(sm, 1, lane, rf);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    pt[r] *= mk[r];
+                    o[r] *= rf[r] * alpha;
+                }
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    bf16x8 ph, pl;
+                    acc_split(pt, st, ph, pl);
+                    const bf16x8 vb = tr_acc<D>(T.v, 16 * st, 32 * wave, lane);
+                    o = mfma_bf16(ph, vb, o);
+                    o = mfma_bf16(pl, vb, o);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sm.so[acc_row(r, lh) * OS + 32 * wave + lm] = o[r];
+            }
+            __syncthreads();
+            // ---- P2: S <- lambda^n S + sum_j k~_j^T lambda^(n-1-j) v_j ----
+            if (act) {
+                float rd[16];
+                if (n == C) {
+                    load16(sm, 2, lane, rd);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int j = acc_row(r, lh);
+                        rd[r] = j < n ? pow_lambda(l2l, n - 1 - j) : 0.0f;
+                    }
+                }
+                const float a_next = alpha * pow_lambda(l2l, n);
+                float inv = 1.0f;
+                if (a_next < 0x1p-20f) {
+#pragma unroll
+                    for (int cc = 0; cc < NW; ++cc)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) S[cc][r] *= a_next;
+                    alpha = 1.0f;
+                } else {
+                    alpha = a_next;
+                    inv = 1.0f / a_next;
+                }
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    const bf16x8 vb = scale8(tr_acc<D>(T.v, 16 * st, 32 * wave, lane), rd + 8 * st, inv);
+#pragma unroll
+                    for (int cc = 0; cc < NW; ++cc)
+                        S[cc] = mfma_bf16(tr_acc<D>(T.k, 16 * st, 32 * cc, lane), vb, S[cc]);
                 }
             }
-            const float a_next = alpha * pow_lambda(l2l, n);
-            float inv = 1.0f;
-            if (a_next < 0x1p-20f) {
+            __syncthreads();
+            // ---- P3: dq~ for key columns of w; W for value columns of w ----
+            if (act) {
+                f32x16 dpt = {}, dq = {};
 #pragma unroll
-                for (int cc = 0; cc < NW; ++cc)
+                for (int s8 = 0; s8 < D / 16; ++s8) {
+                    const bf16x8 dv8 = row8<D>(sm.dO, lm, 16 * s8 + 8 * lh);
+                    dpt = mfma_bf16(row8<D>(T.v, lm, 16 * s8 + 8 * lh), dv8, dpt);   // v_j . do_i
+                    dq = mfma_bf16(dv8, tr_nat<D>(sm.st, 16 * s8, 32 * wave, lane), dq);  // do S^T
+                }
+                float mk[16], rf[16];
+                load16(sm, 0, lane, mk);
+                load16(sm, 1, lane, rf);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) S[cc][r] *= a_next;
-                alpha = 1.0f;
-            } else {
-                alpha = a_next;
-                inv = 1.0f / a_next;
+                for (int r = 0; r < 16; ++r) {
+                    dpt[r] *= mk[r];
+                    dq[r] *= rf[r] * alpha_c;
+                }
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+                    dq = mfma_bf16(acc_operand(dpt, st), tr_acc<D>(T.k, 16 * st, 32 * wave, lane), dq);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sm.sq[acc_row(r, lh) * OS + 32 * wave + lm] = dq[r];
+                // W[k][v] += sum_i q~[i][k] lambda^(cC + i + 1) do[i][v]
+                const float wsc = pow_lambda(l2l, c * C);
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    const bf16x8 db = scale8(tr_acc<D>(sm.dO, 16 * st, 32 * wave, lane), rf + 8 * st, wsc);
+#pragma unroll
+                    for (int cc = 0; cc < NW; ++cc)
+                        W[cc] = mfma_bf16(tr_acc<D>(T.q, 16 * st, 32 * cc, lane), db, W[cc]);
+                }
             }
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                const bf16x8 vb = scale8(tr_acc<D>(sm.v, 16 * st, 32 * wave, lane), rd + 8 * st, inv);
-#pragma unroll
-                for (int cc = 0; cc < NW; ++cc)
-                    S[cc] = mfma_bf16(tr_acc<D>(sm.k, 16 * st, 32 * cc, lane), vb, S[cc]);
-            }
+            __syncthreads();
         }
-        __syncthreads();
-        // ---- P5: dq = QK-norm^T(RoPE^T(dq~)) ----
-        {
-            rw.angles(i, cs);
-            float dqt[16];
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const float* src = sm.stage + rr * OS + hf * HALF + 8 * fg;
-                const float4 a = reinterpret_cast<const float4*>(src)[0];
-                const float4 bq = reinterpret_cast<const float4*>(src)[1];
-                dqt[8 * hf + 0] = a.x; dqt[8 * hf + 1] = a.y; dqt[8 * hf + 2] = a.z; dqt[8 * hf + 3] = a.w;
-                dqt[8 * hf + 4] = bq.x; dqt[8 * hf + 5] = bq.y; dqt[8 * hf + 6] = bq.z; dqt[8 * hf + 7] = bq.w;
-            }
-            widen8(R.q[0], x);
-            widen8(R.q[1], x + 8);
-            float dx[16], dot = 0.0f;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float lo = cs[u].x * dqt[u] + cs[u].y * dqt[8 + u];
-                const float hi = cs[u].x * dqt[8 + u] - cs[u].y * dqt[u];
-                const float xl = x[u] * rq, xh = x[8 + u] * rq;
-                wacc_q[G::NT * u] = fmaf(lo, xl, wacc_q[G::NT * u]);
-                wacc_q[G::NT * (8 + u)] = fmaf(hi, xh, wacc_q[G::NT * (8 + u)]);
-                dx[u] = lo * sm.w[0][8 * fg + u];
-                dx[8 + u] = hi * sm.w[0][HALF + 8 * fg + u];
-                x[u] = xl;
-                x[8 + u] = xh;
-                dot = fmaf(dx[u], xl, dot);
-                dot = fmaf(dx[8 + u], xh, dot);
-            }
-            dot = group_sum<TPR>(dot) * (1.0f / D);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) dx[e] = rq * (dx[e] - x[e] * dot);
-            if (valid) {
-                uint16_t* pdq = static_cast<uint16_t*>(p.dq) + base + (size_t)(t0 + rr) * rs + 8 * fg;
-                *reinterpret_cast<uint4*>(pdq) = pack8(dx);
-                *reinterpret_cast<uint4*>(pdq + HALF) = pack8(dx + 8);
-            }
-        }
-    };
-
-    // the current chunk's inputs are a plain copy of the prefetched set, so both stay in
-    // registers (references to alternating sets would put them in memory)
-    Regs cur;
-    load(0, cur);
-    __syncthreads();  // weights, decay tables and the first RoPE table
-    for (int i = 0; i < n_chunks; ++i) {
-        Regs nxt = cur;
-        step(i, cur, nxt);
-        cur = nxt;
-    }
-
-    // the segment's entry-state gradient W, and the norm-weight partial sums
-    {
+        // the segment's entry-state gradient W
         float* dst = p.seg_grad + ((size_t)bh * p.P + seg) * dd;
 #pragma unroll
         for (int cc = 0; cc < NW; ++cc)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 dst[(size_t)(32 * cc + acc_row(r, lh)) * D + 32 * wave + lm] = W[cc][r];
+        __syncthreads();  // the row wavefronts' weight-gradient sums are in the stages
+    } else {
+        // ============= row wavefronts: loads, prologue, output-norm gradients, dq =============
+        const int rt = threadIdx.x - G::NT;
+        RowWork<D, DqSmem<D>, 4> rw(sm, p, 1, rt);
+        const int rr = rw.rr, fg = rw.fg;
+        const uint16_t* gq = static_cast<const uint16_t*>(p.q) + base + 8 * fg;
+        const uint16_t* gk = static_cast<const uint16_t*>(p.k) + base + 8 * fg;
+        const uint16_t* gv = static_cast<const uint16_t*>(p.v) + base + 8 * fg;
+        const uint16_t* gg = static_cast<const uint16_t*>(p.g) + base + 8 * fg;
+        const uint16_t* gdy = static_cast<const uint16_t*>(p.dy) + base + 8 * fg;
+        auto chunk_pos = [&](int c) { return p.pos0 + t_begin + (int64_t)c * C; };
+        // row rr of chunk c (the last row for rows past the end; their values are zeroed)
+        auto row_off = [&](int c) { return (size_t)min(t_begin + c * C + rr, t_end - 1) * rs; };
+        struct Regs {
+            uint4 q[2], k[2], v[2];
+        };
+        auto load = [&](int c, Regs& R) __attribute__((always_inline)) {
+            const size_t o = row_off(c);
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                R.q[hf] = *reinterpret_cast<const uint4*>(gq + o + hf * HALF);
+                R.k[hf] = *reinterpret_cast<const uint4*>(gk + o + hf * HALF);
+                R.v[hf] = *reinterpret_cast<const uint4*>(gv + o + hf * HALF);
+            }
+        };
+        float wq_acc[16], wo_acc[16];  // this thread's dL/dw_q and dL/dw_o partial sums
+#pragma unroll
+        for (int e = 0; e < 16; ++e) wq_acc[e] = wo_acc[e] = 0.0f;
+        if (wave == NW) rw.fill_table(0, chunk_pos(0));
+        Regs cur;
+        load(0, cur);
+        uint4 q1[2] = {}, q2[2] = {};  // raw queries of the two previously staged chunks
+        float rq1 = 0.0f, rq2 = 0.0f;  // their 1/rms
+        // gate and output gradient rows of a chunk, loaded one step before their use
+        uint4 gr[2], dyr[2];
+        auto load_gdy = [&](int c) __attribute__((always_inline)) {
+            const size_t o = row_off(c);
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                gr[hf] = *reinterpret_cast<const uint4*>(gg + o + hf * HALF);
+                dyr[hf] = *reinterpret_cast<const uint4*>(gdy + o + hf * HALF);
+            }
+        };
+        load_gdy(0);
+        __syncthreads();
+        for (int s = 0; s < n_steps; ++s) {
+            const int c = s - 1, e = s - 2;
+            const bool act = c >= 0 && c < n_chunks;
+            // ---- P1: dq of chunk e ----
+            if (e >= 0 && e < n_chunks) {
+                // dq = QK-norm^T(RoPE^T(dq~))
+                float2 cs[8];
+                rw.angles(e, cs);
+                float dqt[16], x[16];
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const float* src = sm.sq + rr * OS + hf * HALF + 8 * fg;
+                    const float4 a = reinterpret_cast<const float4*>(src)[0];
+                    const float4 bq = reinterpret_cast<const float4*>(src)[1];
+                    dqt[8 * hf + 0] = a.x; dqt[8 * hf + 1] = a.y; dqt[8 * hf + 2] = a.z; dqt[8 * hf + 3] = a.w;
+                    dqt[8 * hf + 4] = bq.x; dqt[8 * hf + 5] = bq.y; dqt[8 * hf + 6] = bq.z; dqt[8 * hf + 7] = bq.w;
+                }
+                widen8(q2[0], x);
+                widen8(q2[1], x + 8);
+                float dx[16], dot = 0.0f;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float lo = cs[u].x * dqt[u] + cs[u].y * dqt[8 + u];
+                    const float hi = cs[u].x * dqt[8 + u] - cs[u].y * dqt[u];
+                    const float xl = x[u] * rq2, xh = x[8 + u] * rq2;
+                    wq_acc[u] = fmaf(lo, xl, wq_acc[u]);
+                    wq_acc[8 + u] = fmaf(hi, xh, wq_acc[8 + u]);
+                    dx[u] = lo * sm.w[0][8 * fg + u];
+                    dx[8 + u] = hi * sm.w[0][HALF + 8 * fg + u];
+                    x[u] = xl;
+                    x[8 + u] = xh;
+                    dot = fmaf(dx[u], xl, dot);
+                    dot = fmaf(dx[8 + u], xh, dot);
+                }
+                dot = group_sum<TPR>(dot) * (1.0f / D);
+#pragma unroll
+                for (int q = 0; q < 16; ++q) dx[q] = rq2 * (dx[q] - x[q] * dot);
+                if (rr < chunk_len(e)) {
+                    uint16_t* pdq = static_cast<uint16_t*>(p.dq) + base +
+                                    (size_t)(t_begin + e * C + rr) * rs + 8 * fg;
+                    *reinterpret_cast<uint4*>(pdq) = pack8(dx);
+                    *reinterpret_cast<uint4*>(pdq + HALF) = pack8(dx + 8);
+                }
+            }
+            __syncthreads();
+            // ---- P2: output norm and gate gradients of chunk c: dg, do ----
+            if (act) {
+                float ov[16], gv8[16], dyv[16];
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const float* src = sm.so + rr * OS + hf * HALF + 8 * fg;
+                    const float4 a = reinterpret_cast<const float4*>(src)[0];
+                    const float4 bq = reinterpret_cast<const float4*>(src)[1];
+                    ov[8 * hf + 0] = a.x; ov[8 * hf + 1] = a.y; ov[8 * hf + 2] = a.z; ov[8 * hf + 3] = a.w;
+                    ov[8 * hf + 4] = bq.x; ov[8 * hf + 5] = bq.y; ov[8 * hf + 6] = bq.z; ov[8 * hf + 7] = bq.w;
+                    widen8(gr[hf], gv8 + 8 * hf);
+                    widen8(dyr[hf], dyv + 8 * hf);
+                }
+                // rows past the end (their loads re-read the last row) get dy = 0, hence do = 0
+                if (rr >= chunk_len(c)) {
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) dyv[q] = 0.0f;
+                }
+                float ss = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) ss = fmaf(ov[q], ov[q], ss);
+                ss = group_sum<TPR>(ss);
+                const float ro = fast_rsqrt(ss * (1.0f / D) + p.eps);
+                float dn[16], dgv[16], dot = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int f = (q < 8 ? 0 : HALF) + 8 * fg + (q & 7);
+                    const float nv = ov[q] * ro, sg = sigmoidf_(gv8[q]), wo = sm.w[2][f];
+                    const float t = dyv[q] * sg;
+                    dn[q] = t * wo;
+                    dgv[q] = dn[q] * nv * (1.0f - sg);
+                    dot = fmaf(dn[q], nv, dot);
+                    wo_acc[q] = fmaf(t, nv, wo_acc[q]);
+                    ov[q] = nv;
+                }
+                dot = group_sum<TPR>(dot) * (1.0f / D);
+#pragma unroll
+                for (int q = 0; q < 16; ++q) dn[q] = ro * (dn[q] - ov[q] * dot);
+                if (c + 1 < n_chunks) load_gdy(c + 1);
+                rw.store(sm.dO, dn);
+                if (rr < chunk_len(c)) {
+                    const size_t o2 = (size_t)(t_begin + c * C + rr) * rs + 8 * fg;
+                    uint16_t* pdg = static_cast<uint16_t*>(p.dg) + base + o2;
+                    uint16_t* pdo = p.d_o + base + o2;
+                    *reinterpret_cast<uint4*>(pdg) = pack8(dgv);
+                    *reinterpret_cast<uint4*>(pdg + HALF) = pack8(dgv + 8);
+                    *reinterpret_cast<uint4*>(pdo) = pack8(dn);
+                    *reinterpret_cast<uint4*>(pdo + HALF) = pack8(dn + 8);
+                }
+            }
+            __syncthreads();
+            // ---- P3: stage chunk s (q~, k~ with their lo parts, v); prefetch chunk s + 1 ----
+            float rq = 0.0f;
+            Regs nxt = cur;
+            if (s < n_chunks) {
+                // rows past the end of a partial chunk get zero inputs: their tile rows, do and
+                // every partial sum they enter are then zero
+                auto& T = sm.t[s & 1];
+                if (rr >= chunk_len(s)) cur = Regs{};
+                float2 cs[8];
+                rw.angles(s, cs);
+                float x[16];
+                widen8(cur.q[0], x);
+                widen8(cur.q[1], x + 8);
+                rq = rw.norm_rotate(x, sm.w[0], cs, 1.0f);
+                rw.store_split(T.q, sm.q_lo, x);
+                widen8(cur.k[0], x);
+                widen8(cur.k[1], x + 8);
+                rw.norm_rotate(x, sm.w[1], cs, 1.0f / sqrtf((float)D));
+                rw.store_split(T.k, sm.k_lo, x);
+                rw.store_raw(T.v, cur.v);
+                if (s + 1 < n_chunks) load(s + 1, nxt);
+                if (wave == NW && s + 1 < n_chunks) rw.fill_table(s + 1, chunk_pos(s + 1));
+            }
+            q2[0] = q1[0]; q2[1] = q1[1]; rq2 = rq1;
+            q1[0] = cur.q[0]; q1[1] = cur.q[1]; rq1 = rq;
+            cur = nxt;
+            __syncthreads();
+        }
+        // the norm-weight partial sums of the 32 rows, via the stages
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int f = (q < 8 ? 0 : HALF) + 8 * fg + (q & 7);
+            sm.so[rr * OS + f] = wq_acc[q];
+            sm.sq[rr * OS + f] = wo_acc[q];
+        }
+        __syncthreads();
     }
     if (p.wgrad) {
         const size_t nbp = (size_t)p.B * p.H * p.P;
-        __syncthreads();
-        for (int f = threadIdx.x; f < 2 * D; f += G::NT) {
+        for (int f = threadIdx.x; f < 2 * D; f += 2 * G::NT) {
             const int which = f / D, ff = f % D;
-            const int tf = (ff % HALF) / 8, e = (ff >= HALF ? 8 : 0) + (ff & 7);
-            float s = 0.0f;
-            for (int r = 0; r < C; ++r) s += sm.wacc[which][e][r * TPR + tf];
-            p.wgrad[((which == 0 ? 0 : 2) * nbp + (size_t)bh * p.P + seg) * D + ff] = s;
+            const float* src = which == 0 ? sm.so : sm.sq;
+            float sum = 0.0f;
+            for (int r = 0; r < C; ++r) sum += src[r * OS + ff];
+            p.wgrad[((which == 0 ? 0 : 2) * nbp + (size_t)bh * p.P + seg) * D + ff] = sum;
         }
     }
 }
@@ -664,7 +718,7 @@ struct alignas(16) DkvSmem {
     alignas(16) float stage[C * G::OS];  // dk~ of a chunk (and the weight-gradient sums at the end)
     alignas(16) float2 rope[4][64];      // cos/sin(p0 f_i) of four consecutive steps
     alignas(16) float w[2][D];           // norm weights q, k
-    alignas(16) float4 dec[12][64];      // as in BwdSmem
+    alignas(16) float4 dec[12][64];      // as in DqSmem
 };
 
 template <int D>
@@ -708,14 +762,7 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dkv_kernel(const BwdParam
             const int i = s - 1;
             const bool act = i >= 0 && i < n_chunks;
             if (act) {
-#pragma unroll
-                for (int cc = 0; cc < NW; ++cc)
-#pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4) {
-                        const uint2 pk = make_uint2(pack_bf16x2(dS[cc][4 * g4], dS[cc][4 * g4 + 1]),
-                                                    pack_bf16x2(dS[cc][4 * g4 + 2], dS[cc][4 * g4 + 3]));
-                        *reinterpret_cast<uint2*>(sm.st + swz<D>(32 * wave + lm, 32 * cc + 8 * g4 + 4 * lh)) = pk;
-                    }
+                store_st<D, NW, false>(sm.st, dS, wave, lane);
             }
             __syncthreads();  // phase B
             if (act) {
@@ -981,7 +1028,7 @@ hipError_t launch_prefill_backward(const BwdParams& p, const ChunkParams& fwd_cp
     if (p.P > 1 && (err = launch_prefill_states(fwd_cp, fwd_sp, D, LT_BF16, stream)) != hipSuccess)
         return err;
     if (ev[0] && (err = hipEventRecord(ev[0], stream)) != hipSuccess) return err;
-    bwd_dq_kernel<D><<<dim3(BH * p.P), dim3(BCfg<D>::NT), 0, stream>>>(p);
+    bwd_dq_kernel<D><<<dim3(BH * p.P), dim3(2 * BCfg<D>::NT), 0, stream>>>(p);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev[1] && (err = hipEventRecord(ev[1], stream)) != hipSuccess) return err;
     const size_t n = (size_t)BH * D * D;
