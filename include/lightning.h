@@ -186,7 +186,9 @@ lt_status lightning_decode_step_dd(const void* q, const void* k, const void* v,
  *                  are recomputed (a state-only pass forward, a scan of per-segment gradient sums
  *                  backward), so nothing from the forward call is kept.
  *   workspace    : device scratch of lightning_prefill_backward_workspace_size(...) bytes; it
- *                  holds, among others, dL/do (bf16, the size of one activation tensor).
+ *                  holds, among others, dL/do (bf16, the size of one activation tensor) and the
+ *                  masked score tiles of both products of every 32-token chunk (2 x 32 x 32 fp32
+ *                  per chunk, as large as one bf16 activation tensor at d = 128).
  *   kernel_events: NULL, or four hipEvent_t recorded around the forward-in-time sweep (dq, dgate)
  *                  ([0], [1]) and the backward-in-time sweep (dk, dv) ([2], [3]).
  * Other arguments as for lightning_prefill.  Outputs may not overlap inputs or each other.

@@ -172,7 +172,7 @@ lt_status bwd_check_shape(int B, int T, int H, int d, int dtype, int segments) {
 // Backward workspace: forward entry states (P > 1) | per-segment state gradients | do (bf16,
 // the activations' layout) | norm-weight partial sums; each part on a 256-byte boundary.
 struct BwdLayout {
-    size_t seg_grad, d_o, wgrad, total;
+    size_t seg_grad, d_o, scores, wgrad, total;
 };
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 BwdLayout bwd_layout(int B, int T, int H, int d, const Plan& pl) {
@@ -180,7 +180,10 @@ BwdLayout bwd_layout(int B, int T, int H, int d, const Plan& pl) {
     BwdLayout l;
     l.seg_grad = align256(workspace_bytes_for(B, H, d, pl.P, pl.sub));
     l.d_o = align256(l.seg_grad + bh * pl.P * d * d * sizeof(float));
-    l.wgrad = align256(l.d_o + (size_t)B * T * H * d * sizeof(uint16_t));
+    // the dq sweep's masked score tiles P (.) D and dP (.) D, 2 C x C fp32 per chunk
+    const size_t n_chunks = ((size_t)T + pl.C - 1) / pl.C;
+    l.scores = align256(l.d_o + (size_t)B * T * H * d * sizeof(uint16_t));
+    l.wgrad = align256(l.scores + bh * n_chunks * 2 * pl.C * pl.C * sizeof(float));
     l.total = l.wgrad + 3 * bh * pl.P * d * sizeof(float);
     return l;
 }
@@ -313,6 +316,7 @@ lt_status lightning_prefill_backward(const void* q, const void* k, const void* v
     bp.d_state_in = d_state_in;
     bp.d_o = reinterpret_cast<uint16_t*>(ws + lay.d_o);
     bp.seg_grad = reinterpret_cast<float*>(ws + lay.seg_grad);
+    bp.scores = reinterpret_cast<float*>(ws + lay.scores);
     if (d_q_norm_w || d_k_norm_w || d_o_norm_w) bp.wgrad = reinterpret_cast<float*>(ws + lay.wgrad);
     bp.dqw = d_q_norm_w; bp.dkw = d_k_norm_w; bp.dow = d_o_norm_w;
     bp.pos0 = pos0;

@@ -191,6 +191,23 @@ __device__ __forceinline__ void store_st(__bf16* st, const f32x16* A, int wave, 
         }
 }
 
+// The masked score tiles of a chunk are computed once, in the dq sweep, and read back by the
+// dk/dv sweep: which = 0 is P (.) D with P[i][j] = q~_i . k~_j, which = 1 is dP (.) D with
+// dP[i][j] = do_i . v_j.  Global layout per chunk: fp32 [i][j], row-major.  The dq sweep holds
+// them transposed in its accumulators (lane column i = lm, register r: row j = acc_row(r, lh)),
+// whose four consecutive j per register group make one 16-byte store.
+__device__ __forceinline__ float* score_tile(const BwdParams& p, int bh, int chunk, int which) {
+    const size_t nc = ((size_t)p.T + C - 1) / C;
+    return p.scores + (((size_t)bh * nc + chunk) * 2 + which) * (C * C);
+}
+__device__ __forceinline__ void store_score_tile(const BwdParams& p, int bh, int chunk, int which,
+                                                 int lm, int lh, const f32x16& x) {
+    float* dst = score_tile(p, bh, chunk, which) + lm * C + 4 * lh;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+        *reinterpret_cast<float4*>(dst + 8 * a) = make_float4(x[4 * a], x[4 * a + 1], x[4 * a + 2], x[4 * a + 3]);
+}
+
 // Shared per-workgroup set-up: norm weights (the q, k and, where the layout has it, o rows of
 // sm.w) and the decay tables.
 template <int D, class SM>
@@ -402,6 +419,7 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dq_kernel(const BwdParams
                     pt[r] *= mk[r];
                     o[r] *= rf[r] * alpha;
                 }
+                if (wave == 0) store_score_tile(p, bh, t_begin / C + c, 0, lm, lh, pt);
 #pragma unroll
                 for (int st = 0; st < 2; ++st) {
                     bf16x8 ph, pl;
@@ -464,6 +482,7 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dq_kernel(const BwdParams
                     dpt[r] *= mk[r];
                     dq[r] *= rf[r] * alpha_c;
                 }
+                if (wave == 1) store_score_tile(p, bh, t_begin / C + c, 1, lm, lh, dpt);
 #pragma unroll
                 for (int st = 0; st < 2; ++st)
                     dq = mfma_bf16(acc_operand(dpt, st), tr_acc<D>(T.k, 16 * st, 32 * wave, lane), dq);
@@ -710,8 +729,11 @@ __global__ void __launch_bounds__(256) bwd_scan_kernel(const BwdParams p, int dd
 template <int D>
 struct alignas(16) DkvSmem {
     using G = BCfg<D>;
+    static constexpr int PS = C + 8;  // row stride of the score tiles (the two halves of a
+                                      // wavefront's column reads fall on disjoint banks)
     struct alignas(16) Tiles {
-        __bf16 q[C * D], k[C * D], q_lo[C * D], k_lo[C * D], v[C * D], dO[C * D];
+        __bf16 q[C * D], k[C * D], v[C * D], dO[C * D];  // q~, k~ (bf16), v, do
+        float P[C * PS], dP[C * PS];                     // P (.) D and dP (.) D, [i][j]
     };
     Tiles t[2];
     alignas(16) __bf16 st[D * D];        // state-gradient copy, [value][key]
@@ -770,10 +792,9 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dkv_kernel(const BwdParam
                 const int c = chunk_of(i);
                 const int t0 = t_begin + c * C;
                 const int n = chunk_len(i);
-                // causal mask (.) D and the decay lambda^(n-1-j) of row j (zero past the end),
-                // read after each product's loop so they are not live across it
-                auto masks = [&](float* mk, float* rd) __attribute__((always_inline)) {
-                    load16(sm, 0, lane, mk);
+                // the decay lambda^(n-1-j) of row j (zero past the end), read after each
+                // product's loop so that it is not live across it
+                auto decays = [&](float* rd) __attribute__((always_inline)) {
                     if (n == C) {
                         load16(sm, 2, lane, rd);
                     } else {
@@ -785,24 +806,19 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dkv_kernel(const BwdParam
                     }
                 };
                 {
-                    // P[i][j] = q~_i . k~_j (lane j) from hi/lo parts (do_i is large where o_i is
-                    // small, and there dv_j = sum_i P_ij do_i must not inherit score rounding);
-                    // dv = (P (.) D)^T do + diag(lambda^(n-1-j)) K~ dS for value columns of w
-                    f32x16 pm = {}, dvv = {};
+                    // dv = (P (.) D)^T do + diag(lambda^(n-1-j)) K~ dS for value columns of w,
+                    // with the dq sweep's P (.) D (lane j, rows i = acc_row(r, lh)); its hi and
+                    // lo parts enter the product (do_i is large where o_i is small, and there
+                    // dv_j = sum_i P_ij do_i must not inherit the scores' bf16 rounding)
+                    f32x16 pm, dvv = {};
 #pragma unroll
-                    for (int s8 = 0; s8 < D / 16; ++s8) {
-                        const bf16x8 qh = row8<D>(T.q, lm, 16 * s8 + 8 * lh);
-                        const bf16x8 kh = row8<D>(T.k, lm, 16 * s8 + 8 * lh);
-                        pm = mfma_bf16(qh, kh, pm);
-                        pm = mfma_bf16(qh, row8<D>(T.k_lo, lm, 16 * s8 + 8 * lh), pm);
-                        pm = mfma_bf16(row8<D>(T.q_lo, lm, 16 * s8 + 8 * lh), kh, pm);
+                    for (int s8 = 0; s8 < D / 16; ++s8)
                         dvv = mfma_bf16(row_acc<D>(T.k, lm, s8, lh), acc_operand(dS[s8 / 2], s8 % 2), dvv);
-                    }
-                    float mk[16], rd[16];
-                    masks(mk, rd);
+                    float rd[16];
+                    decays(rd);
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        pm[r] *= mk[r];
+                        pm[r] = T.P[acc_row(r, lh) * DkvSmem<D>::PS + lm];
                         dvv[r] *= rd[r] * beta;
                     }
 #pragma unroll
@@ -824,20 +840,18 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dkv_kernel(const BwdParam
                     }
                 }
                 {
-                    // dP[i][j] = do_i . v_j (lane j); dk~ = (dP (.) D)^T Q~ + diag(lambda^(n-1-j))
-                    // V dS^T for key columns of w, staged for the row wavefronts
-                    f32x16 dpm = {}, dkt = {};
+                    // dk~ = (dP (.) D)^T Q~ + diag(lambda^(n-1-j)) V dS^T for key columns of w,
+                    // with the dq sweep's dP (.) D (lane j), staged for the row wavefronts
+                    f32x16 dpm, dkt = {};
 #pragma unroll
-                    for (int s8 = 0; s8 < D / 16; ++s8) {
-                        const bf16x8 vr = row8<D>(T.v, lm, 16 * s8 + 8 * lh);
-                        dpm = mfma_bf16(row8<D>(T.dO, lm, 16 * s8 + 8 * lh), vr, dpm);
-                        dkt = mfma_bf16(vr, tr_nat<D>(sm.st, 16 * s8, 32 * wave, lane), dkt);
-                    }
-                    float mk[16], rd[16];
-                    masks(mk, rd);
+                    for (int s8 = 0; s8 < D / 16; ++s8)
+                        dkt = mfma_bf16(row8<D>(T.v, lm, 16 * s8 + 8 * lh),
+                                        tr_nat<D>(sm.st, 16 * s8, 32 * wave, lane), dkt);
+                    float rd[16];
+                    decays(rd);
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        dpm[r] *= mk[r];
+                        dpm[r] = T.dP[acc_row(r, lh) * DkvSmem<D>::PS + lm];
                         dkt[r] *= rd[r] * beta;
                     }
 #pragma unroll
@@ -886,6 +900,7 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dkv_kernel(const BwdParam
         auto chunk_pos = [&](int step) { return p.pos0 + t_begin + (int64_t)chunk_of(step) * C; };
         struct Regs {
             uint4 q[2], k[2], v[2], dO[2];
+            float4 P, dP;  // score-tile elements [rr][4 fg, 4 fg + 4)
         };
         auto load = [&](int step, Regs& R) __attribute__((always_inline)) {
             const int t0 = t_begin + chunk_of(step) * C;
@@ -898,6 +913,9 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dkv_kernel(const BwdParam
                 R.v[hf] = *reinterpret_cast<const uint4*>(gv + oo);
                 R.dO[hf] = *reinterpret_cast<const uint4*>(gdo + oo);
             }
+            const int g = t_begin / C + chunk_of(step);
+            R.P = *reinterpret_cast<const float4*>(score_tile(p, bh, g, 0) + rr * C + 4 * fg);
+            R.dP = *reinterpret_cast<const float4*>(score_tile(p, bh, g, 1) + rr * C + 4 * fg);
         };
         float wk_acc[16];  // this thread's dL/dw_k partial sums
 #pragma unroll
@@ -957,8 +975,9 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dkv_kernel(const BwdParam
             float rk = 0.0f;
             Regs nxt = cur;
             if (s < n_chunks) {
-                // stage chunk s: q~, k~ (hi and lo parts), v, do; rows past a partial chunk's end
-                // get zero inputs (their loads re-read the last row)
+                // stage chunk s: q~, k~, v, do and the score tiles; rows past a partial chunk's
+                // end get zero inputs (their loads re-read the last row; their score rows are
+                // zero anyway)
                 auto& T = sm.t[s & 1];
                 if (rr >= chunk_len(s)) cur = Regs{};
                 float2 cs[8];
@@ -967,13 +986,15 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dkv_kernel(const BwdParam
                 widen8(cur.q[0], x);
                 widen8(cur.q[1], x + 8);
                 rw.norm_rotate(x, sm.w[0], cs, 1.0f);
-                rw.store_split(T.q, T.q_lo, x);
+                rw.store(T.q, x);
                 widen8(cur.k[0], x);
                 widen8(cur.k[1], x + 8);
                 rk = rw.norm_rotate(x, sm.w[1], cs, kscale);
-                rw.store_split(T.k, T.k_lo, x);
+                rw.store(T.k, x);
                 rw.store_raw(T.v, cur.v);
                 rw.store_raw(T.dO, cur.dO);
+                *reinterpret_cast<float4*>(T.P + rr * DkvSmem<D>::PS + 4 * fg) = cur.P;
+                *reinterpret_cast<float4*>(T.dP + rr * DkvSmem<D>::PS + 4 * fg) = cur.dP;
                 if (s + 1 < n_chunks) load(s + 1, nxt);
                 if (wave == NW && s + 1 < n_chunks) rw.fill_table(s + 1, chunk_pos(s + 1));
             }

@@ -104,6 +104,8 @@ struct BwdParams {
     uint16_t* d_o;             // [B][T][H][d] bf16: dL/do, written by the first sweep
     float* seg_grad;           // [B][H][P][d][d]: each segment's own dL/d(entry state), then
                                // (after the scan) dL/d(state after the segment)
+    float* scores;             // [B][H][ceil(T/C)][2][C][C] fp32: per chunk P (.) D and dP (.) D
+                               // (row i, column j), written by the first sweep
     float* wgrad;              // [3][B][H][P][d] norm-weight partials (q, k, o), or null
     float* dqw;                // norm-weight gradients (null when wgrad is null)
     float* dkw;

@@ -392,8 +392,9 @@ def test_prefill_dd_rejects(name, over, status):
 def test_backward_workspace_layout():
     B, T, H, d = 8, 16384, 16, 128
     ws = lt.lightning_prefill_backward_workspace_size(B, T, H, d)
-    # at least: do (bf16, one activation tensor) + one d x d state gradient per (b, h, segment)
-    assert ws >= B * T * H * d * 2 + B * H * d * d * 4
+    # at least: do (bf16, one activation tensor), the two masked 32 x 32 fp32 score tiles of
+    # every chunk, one d x d state gradient per (b, h, segment)
+    assert ws >= B * T * H * d * 2 + B * H * (T // 32) * 2 * 32 * 32 * 4 + B * H * d * d * 4
     assert ws % 4 == 0
     # unsupported shapes report 0
     assert lt.lightning_prefill_backward_workspace_size(B, T, H, 64) == 0
@@ -401,8 +402,9 @@ def test_backward_workspace_layout():
     # one segment (B H fills the CUs): no forward state slots, one gradient per (b, h)
     one = lt.lightning_prefill_backward_workspace_size(16, 256, 16, d)
     do_bytes = 16 * 256 * 16 * d * 2
-    assert one >= do_bytes + 16 * 16 * d * d * 4
-    assert one < do_bytes + 16 * 16 * d * d * 4 + 3 * 16 * 16 * d * 4 + 1024
+    score_bytes = 16 * 16 * (256 // 32) * 2 * 32 * 32 * 4
+    assert one >= do_bytes + score_bytes + 16 * 16 * d * d * 4
+    assert one < do_bytes + score_bytes + 16 * 16 * d * d * 4 + 3 * 16 * 16 * d * 4 + 1024
 
 
 def _bwd_args(**over):
