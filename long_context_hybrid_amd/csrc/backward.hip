@@ -60,21 +60,20 @@ template <int D>
 struct alignas(16) DqSmem {
     using G = BCfg<D>;
     struct alignas(16) Tiles {
-        __bf16 q[C * D], k[C * D], v[C * D];  // q~, k~ (bf16 parts), v
+        __bf16 q[C * D], k[C * D], k_lo[C * D], v[C * D];  // q~, k~ (bf16 parts), k~ - bf16(k~), v
     };
     Tiles t[2];
-    alignas(16) __bf16 q_lo[C * D];      // q~ - bf16(q~) and k~ - bf16(k~) of the staged chunk
-    alignas(16) __bf16 k_lo[C * D];
+    alignas(16) __bf16 q_lo[C * D];      // q~ - bf16(q~) of the chunk in the MFMA wavefronts' hands
     alignas(16) __bf16 dO[C * D];        // do
     alignas(16) __bf16 st[D * D];        // state copy, [value][key]
     alignas(16) float so[C * G::OS];     // fp32 [token][feature] stage of o
     alignas(16) float sq[C * G::OS];     // ... and of dq~
     alignas(16) float2 rope[4][64];      // cos/sin(p0 f_i) of four consecutive chunks
     alignas(16) float w[3][D];           // norm weights q, k, o
-    // decay factors per lane, as float4 groups g < 12 stored [g][lane] (consecutive lanes read
-    // consecutive 16-byte words): groups [0, 4) the score-tile decay, [4, 8) lambda^(row + 1),
-    // [8, 12) lambda^(C-1-row) of the lane's accumulator rows
-    alignas(16) float4 dec[12][64];
+    // decay factors per lane, as float4 groups stored [g][lane] (consecutive lanes read
+    // consecutive 16-byte words): groups [0, 4) the score-tile decay, [4, 8) lambda^(row + 1) of
+    // the lane's accumulator rows (the dk/dv sweep's table adds [8, 12), lambda^(C-1-row))
+    alignas(16) float4 dec[8][64];
 };
 
 template <int D>
@@ -233,8 +232,9 @@ __device__ __forceinline__ void setup_common(const BwdParams& p, SM& sm, int h, 
             d[16 + r] = pow_lambda(l2l, m + 1);
             d[32 + r] = pow_lambda(l2l, C - 1 - m);
         }
+        constexpr int NG = sizeof(sm.dec) / sizeof(sm.dec[0]);  // 8 or 12 groups
 #pragma unroll
-        for (int g = 0; g < 12; ++g)
+        for (int g = 0; g < NG; ++g)
             sm.dec[g][lane] = make_float4(d[4 * g], d[4 * g + 1], d[4 * g + 2], d[4 * g + 3]);
     }
 }
@@ -340,9 +340,11 @@ struct RowWork {
 // state gradient W (value columns 32 w ..) and do the MFMA work; wavefronts NW .. 2 NW-1 do the
 // row work.  A chunk needs its do (row work) between its o and its dq~ (MFMA work), so a step
 // has three phases.  In step s, for chunk c = s - 1:
-//   P1  MFMA: S_c copy to LDS, o_c                      rows: dq of chunk c - 1 (epilogue)
-//   P2  MFMA: S_(c+1) = lambda^n S_c + K~^T V           rows: the output-norm gradients, do_c
-//   P3  MFMA: dq~_c, W += Q~^T Lambda do_c              rows: q~, k~, v of chunk c + 1 (prologue)
+//   P1  MFMA: o_c                                  rows: dq of chunk c - 1, k~ of chunk c + 1
+//   P2  MFMA: S_c copy to LDS, S_(c+1) = lambda^n S_c + K~^T V
+//                                                  rows: the output-norm gradients, do_c
+//   P3  MFMA: dq~_c, W += Q~^T Lambda do_c         rows: q~, v of chunk c + 1
+// (the split of the row work follows measured phase times: o and dq~ are the long MFMA parts).
 template <int D>
 __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) {
     using G = BCfg<D>;
@@ -350,7 +352,7 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dq_kernel(const BwdParams
     __shared__ DqSmem<D> sm;
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63, lm = lane & 31, lh = lane >> 5;
+    const int lane0 = threadIdx.x & 63;
     const bool is_math = wave < NW;
     const int seg = blockIdx.x % p.P, bh = blockIdx.x / p.P;
     const int b = bh / p.H, h = bh - b * p.H;
@@ -375,7 +377,7 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dq_kernel(const BwdParams
             for (int cc = 0; cc < NW; ++cc)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    S[cc][r] = src ? src[(size_t)(32 * cc + acc_row(r, lh)) * D + 32 * wave + lm] : 0.0f;
+                    S[cc][r] = src ? src[(size_t)(32 * cc + acc_row(r, lane0 >> 5)) * D + 32 * wave + (lane0 & 31)] : 0.0f;
                     W[cc][r] = 0.0f;
                 }
         }
@@ -391,9 +393,13 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dq_kernel(const BwdParams
             const auto& T = sm.t[c & 1];
             const int n = act ? chunk_len(c) : 0;
             const float alpha_c = alpha;  // the scale of S_c, for dq~
-            // ---- P1: st = S_c; o = diag(lambda^(i+1)) Q~ S + (K~ Q~^T (.) D)^T V ----
+            // the lane index, opaque to the compiler: LDS addresses are recomputed in each step
+            // instead of being held in registers (or spilled) across the loop
+            int lane = lane0;
+            asm volatile("" : "+v"(lane));
+            const int lm = lane & 31, lh = lane >> 5;
+            // ---- P1: o = diag(lambda^(i+1)) Q~ S + (K~ Q~^T (.) D)^T V ----
             if (act) {
-                store_st<D, NW, true>(sm.st, S, wave, lane);
                 // The intra-chunk part of o is recomputed to about fp32 accuracy (hi/lo parts of
                 // q~, k~ and the scores): the output norm's gradient scales with 1/||o_t||, and
                 // the rows where o_t is small (mostly the first tokens of a sequence, where
@@ -408,7 +414,7 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dq_kernel(const BwdParams
                     const bf16x8 qv = row8<D>(T.q, lm, 16 * s8 + 8 * lh);
                     pt = mfma_bf16(kv, qv, pt);  // P^T[j][i] += k~_j . q~_i
                     pt = mfma_bf16(kv, row8<D>(sm.q_lo, lm, 16 * s8 + 8 * lh), pt);
-                    pt = mfma_bf16(row8<D>(sm.k_lo, lm, 16 * s8 + 8 * lh), qv, pt);
+                    pt = mfma_bf16(row8<D>(T.k_lo, lm, 16 * s8 + 8 * lh), qv, pt);
                     o = mfma_bf16(row_acc<D>(T.q, lm, s8, lh), acc_operand(S[s8 / 2], s8 % 2), o);
                 }
                 float mk[16], rf[16];
@@ -432,17 +438,14 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dq_kernel(const BwdParams
                 for (int r = 0; r < 16; ++r) sm.so[acc_row(r, lh) * OS + 32 * wave + lm] = o[r];
             }
             __syncthreads();
-            // ---- P2: S <- lambda^n S + sum_j k~_j^T lambda^(n-1-j) v_j ----
+            // ---- P2: st = S_c; S <- lambda^n S + sum_j k~_j^T lambda^(n-1-j) v_j ----
             if (act) {
+                store_st<D, NW, true>(sm.st, S, wave, lane);
                 float rd[16];
-                if (n == C) {
-                    load16(sm, 2, lane, rd);
-                } else {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int j = acc_row(r, lh);
-                        rd[r] = j < n ? pow_lambda(l2l, n - 1 - j) : 0.0f;
-                    }
+                for (int r = 0; r < 16; ++r) {
+                    const int j = acc_row(r, lh);
+                    rd[r] = j < n ? pow_lambda(l2l, n - 1 - j) : 0.0f;
                 }
                 const float a_next = alpha * pow_lambda(l2l, n);
                 float inv = 1.0f;
@@ -506,7 +509,7 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dq_kernel(const BwdParams
         for (int cc = 0; cc < NW; ++cc)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                dst[(size_t)(32 * cc + acc_row(r, lh)) * D + 32 * wave + lm] = W[cc][r];
+                dst[(size_t)(32 * cc + acc_row(r, lane0 >> 5)) * D + 32 * wave + (lane0 & 31)] = W[cc][r];
         __syncthreads();  // the row wavefronts' weight-gradient sums are in the stages
     } else {
         // ============= row wavefronts: loads, prologue, output-norm gradients, dq =============
@@ -556,7 +559,7 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dq_kernel(const BwdParams
         for (int s = 0; s < n_steps; ++s) {
             const int c = s - 1, e = s - 2;
             const bool act = c >= 0 && c < n_chunks;
-            // ---- P1: dq of chunk e ----
+            // ---- P1: dq of chunk e; k~ of chunk s ----
             if (e >= 0 && e < n_chunks) {
                 // dq = QK-norm^T(RoPE^T(dq~))
                 float2 cs[8];
@@ -596,6 +599,18 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dq_kernel(const BwdParams
                     *reinterpret_cast<uint4*>(pdq) = pack8(dx);
                     *reinterpret_cast<uint4*>(pdq + HALF) = pack8(dx + 8);
                 }
+            }
+            if (s < n_chunks) {
+                // k~ of chunk s (bf16 and lo parts).  Rows past the end of a partial chunk get
+                // zero inputs: their tile rows, do and every partial sum they enter are then zero
+                if (rr >= chunk_len(s)) cur = Regs{};
+                float2 cs[8];
+                rw.angles(s, cs);
+                float x[16];
+                widen8(cur.k[0], x);
+                widen8(cur.k[1], x + 8);
+                rw.norm_rotate(x, sm.w[1], cs, 1.0f / sqrtf((float)D));
+                rw.store_split(sm.t[s & 1].k, sm.t[s & 1].k_lo, x);
             }
             __syncthreads();
             // ---- P2: output norm and gate gradients of chunk c: dg, do ----
@@ -649,14 +664,11 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dq_kernel(const BwdParams
                 }
             }
             __syncthreads();
-            // ---- P3: stage chunk s (q~, k~ with their lo parts, v); prefetch chunk s + 1 ----
+            // ---- P3: stage q~ (with its lo part) and v of chunk s; prefetch chunk s + 1 ----
             float rq = 0.0f;
             Regs nxt = cur;
             if (s < n_chunks) {
-                // rows past the end of a partial chunk get zero inputs: their tile rows, do and
-                // every partial sum they enter are then zero
                 auto& T = sm.t[s & 1];
-                if (rr >= chunk_len(s)) cur = Regs{};
                 float2 cs[8];
                 rw.angles(s, cs);
                 float x[16];
@@ -664,10 +676,6 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dq_kernel(const BwdParams
                 widen8(cur.q[1], x + 8);
                 rq = rw.norm_rotate(x, sm.w[0], cs, 1.0f);
                 rw.store_split(T.q, sm.q_lo, x);
-                widen8(cur.k[0], x);
-                widen8(cur.k[1], x + 8);
-                rw.norm_rotate(x, sm.w[1], cs, 1.0f / sqrtf((float)D));
-                rw.store_split(T.k, sm.k_lo, x);
                 rw.store_raw(T.v, cur.v);
                 if (s + 1 < n_chunks) load(s + 1, nxt);
                 if (wave == NW && s + 1 < n_chunks) rw.fill_table(s + 1, chunk_pos(s + 1));
@@ -740,7 +748,7 @@ struct alignas(16) DkvSmem {
     alignas(16) float stage[C * G::OS];  // dk~ of a chunk (and the weight-gradient sums at the end)
     alignas(16) float2 rope[4][64];      // cos/sin(p0 f_i) of four consecutive steps
     alignas(16) float w[2][D];           // norm weights q, k
-    alignas(16) float4 dec[12][64];      // as in DqSmem
+    alignas(16) float4 dec[12][64];      // as in DqSmem, plus lambda^(C-1-row)
 };
 
 template <int D>
