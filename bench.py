@@ -537,15 +537,20 @@ def bench_backward(args, torch, lt, synth):
     units = B * T * H
     wgs = B * H * P
     st = d * d * 4
-    # dq sweep: reads q, k, v, gate, dy; writes dq, dgate, do (bf16); entry state in, W out
-    alg_dq = units * 8 * d * 2 + wgs * 2 * st
-    # dk/dv sweep: reads q, k, v, do; writes dk, dv; the segment's end-state gradient in
-    alg_dkv = units * 6 * d * 2 + wgs * st
     C = 32
+    # the two masked C x C fp32 score tiles of each chunk: C * 4 * 2 bytes per token-head
+    score = units * 2 * C * 4
+    # dq sweep: reads q, k, v, gate, dy; writes dq, dgate, do (bf16) and the score tiles;
+    # entry state in, W out
+    alg_dq = units * 8 * d * 2 + score + wgs * 2 * st
+    # dk/dv sweep: reads q, k, v, do and the score tiles; writes dk, dv; the segment's end-state
+    # gradient in
+    alg_dkv = units * 6 * d * 2 + score + wgs * st
     # useful MFMA flops per token-head: dq sweep 4 C d + 4 d^2 multiply-adds (scores, P V, do V^T,
-    # dP K~; q~ S, do S^T, W, S update), dk/dv sweep 4 C d + 3 d^2
+    # dP K~; q~ S, do S^T, W, S update), dk/dv sweep 2 C d + 3 d^2 (P^T do, dP^T Q~; K~ dS,
+    # V dS^T, dS update)
     fl_dq = units * 2 * (4 * C * d + 4 * d * d)
-    fl_dkv = units * 2 * (4 * C * d + 3 * d * d)
+    fl_dkv = units * 2 * (2 * C * d + 3 * d * d)
     legs = {"dq_sweep": (dq_ms, alg_dq, fl_dq, "bwd_dq_kernel<128> (forward-in-time sweep)"),
             "dkv_sweep": (dkv_ms, alg_dkv, fl_dkv, "bwd_dkv_kernel<128> (backward-in-time sweep)")}
     dom = max(legs, key=lambda k: legs[k][0])
