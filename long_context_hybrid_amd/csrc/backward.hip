@@ -15,19 +15,21 @@
 //   2. bwd_dq_kernel, forward over each segment's chunks: recompute o, then the output-norm and
 //      gate gradients (dg, do; do is written for pass 4), dq~ and through RoPE^T and the QK-norm
 //      dq; it also sums the segment's own entry-state gradient W = sum_i lambda^(i+1) q~_i^T do_i
-//      (token offsets i within the segment);
+//      (token offsets i within the segment), and stores each chunk's masked score tiles
+//      P (.) D and dP (.) D (P = Q~ K~^T, dP = do V^T) for pass 4;
 //   3. bwd_scan_kernel, backward over segments: E_(P-1) = dS_out, E_(s-1) = lambda^L_s E_s + W_s
 //      (the gradient at each segment's end), and dS_in = lambda^L_0 E_0 + W_0;
 //   4. bwd_dkv_kernel, backward over each segment's chunks from E_s: dk~ (then dk) and dv;
 //   5. bwd_wgrad_kernel: the norm weights' gradients from per-workgroup partial sums.
 //
-// Both sweeps use one workgroup of d/32 wavefronts per (b, h, segment).  Wavefront w keeps the
-// d x 32 slice of the fp32 state (or state gradient) for value columns [32w, 32w + 32) in MFMA
-// accumulators; products that contract over the value dimension read a bf16 copy of the whole
-// state that the wavefronts write to LDS once per chunk (transposed, [value][key]).  Row-wise
-// work (norms, rotation, gate) runs on all threads with d/16 threads per token row, which keep
-// their rows' raw inputs in registers between the prologue and the epilogues.  The next chunk's
-// inputs are loaded into a second register set while the current chunk is processed.
+// Both sweeps use one workgroup of 2 d/32 wavefronts per (b, h, segment), in two roles.  MFMA
+// wavefront w < d/32 keeps the d x 32 slice of the fp32 state (or state gradient) for value
+// columns [32w, 32w + 32) in registers and does the chunk's products; products that contract
+// over the value dimension read a bf16 copy of the whole state that these wavefronts write to LDS
+// once per chunk (transposed, [value][key]).  The other d/32 wavefronts do the row-wise work
+// (loads, norms, rotation, gate) with d/16 threads per token row, staging the next chunk's
+// tiles (double-buffered in LDS) and finishing the previous chunk's dq or dk while the MFMA
+// wavefronts work, so that VALU and MFMA work overlap on every SIMD.
 //
 // LDS tiles are bf16 [row][d] with the 16-byte blocks of row r XOR-permuted by
 // f(r) = 4 (r mod 4) + (r / 4 mod 4): 16 consecutive rows take 16 distinct blocks (16-byte row
