@@ -76,6 +76,7 @@ struct alignas(16) DqSmem {
     // consecutive 16-byte words): groups [0, 4) the score-tile decay, [4, 8) lambda^(row + 1) of
     // the lane's accumulator rows (the dk/dv sweep's table adds [8, 12), lambda^(C-1-row))
     alignas(16) float4 dec[8][64];
+    alignas(16) float rdec[C];           // lambda^(C-1-m), m < C (a full chunk's update decay)
 };
 
 template <int D>
@@ -368,6 +369,7 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dq_kernel(const BwdParams
     auto chunk_len = [&](int c) { return min(C, t_end - (t_begin + c * C)); };
 
     setup_common<D>(p, sm, h, l2l, true);
+    if (threadIdx.x < C) sm.rdec[threadIdx.x] = pow_lambda(l2l, C - 1 - threadIdx.x);
 
     if (is_math) {
         // ========== MFMA wavefronts: state, entry-state gradient and the chunk products ==========
@@ -444,10 +446,19 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dq_kernel(const BwdParams
             if (act) {
                 store_st<D, NW, true>(sm.st, S, wave, lane);
                 float rd[16];
+                if (n == C) {
+                    // rows acc_row(4a + b, lh) = 8a + 4lh + b: four consecutive table entries
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int j = acc_row(r, lh);
-                    rd[r] = j < n ? pow_lambda(l2l, n - 1 - j) : 0.0f;
+                    for (int a = 0; a < 4; ++a) {
+                        const float4 x = *reinterpret_cast<const float4*>(&sm.rdec[8 * a + 4 * lh]);
+                        rd[4 * a] = x.x; rd[4 * a + 1] = x.y; rd[4 * a + 2] = x.z; rd[4 * a + 3] = x.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int j = acc_row(r, lh);
+                        rd[r] = j < n ? pow_lambda(l2l, n - 1 - j) : 0.0f;
+                    }
                 }
                 const float a_next = alpha * pow_lambda(l2l, n);
                 float inv = 1.0f;
