@@ -139,17 +139,22 @@ __device__ __forceinline__ void dma_block(const char* blk, __bf16* tile, int wav
 }
 
 // Scores of one 64-key block for the wavefront's 32 queries, S^T[j][i] in two 32-key halves, in
-// log2 units; keys after a lane's query (and whole halves after the wavefront's last query) are
-// -inf.
+// log2 units and shifted by the lane's running max at the time (`sub`, 0 before the first
+// block): the accumulators start at -sub, so the softmax needs no per-element subtraction while
+// the max stays put.  Keys after a lane's query (and whole halves after the wavefront's last
+// query) are -inf.
 struct Scores {
     f32x16 s[2];
+    float sub;
 };
 
 __device__ __forceinline__ void block_scores(Scores& sc, const __bf16* kt, const bf16x8 (&qv)[kD / 16],
-                                             int key0, int q0, int qi, int ln, int lh) {
+                                             int key0, int q0, int qi, int ln, int lh, float m) {
+    sc.sub = m == -INFINITY ? 0.0f : m;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
-        sc.s[sb] = f32x16{};
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc.s[sb][r] = -sc.sub;
         const int kbase = key0 + 32 * sb;
         if (kbase > q0 + kQW - 1) {  // half entirely in the future of the wavefront
 #pragma unroll
@@ -170,15 +175,33 @@ __device__ __forceinline__ void block_scores(Scores& sc, const __bf16* kt, const
     }
 }
 
+// max(a, b, c) as one v_max3_f32.  fmaxf would first quiet each input (a second instruction per
+// value); the scores hold no NaN, and -inf orders as usual.
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // Online softmax of one block (log2 units; the running max is raised only past kRaise) and
-// O^T += V^T P^T.
+// O^T += V^T P^T.  The row sum l adds the bf16 probabilities the product uses (packed dot
+// products with ones), so O and l are normalised consistently.
 __device__ __forceinline__ void block_softmax_pv(const Scores& sc, const __bf16* vt,
                                                  f32x16 (&o)[kD / 32], float& m, float& l,
                                                  int key0, int q0, int lane) {
-    float mx = sc.s[0][0];
+    // the block max by three-input maxima: 32 values in 16 instructions
+    float a[11];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc.s[0][r], sc.s[1][r]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    for (int i = 0; i < 5; ++i) {
+        a[i] = max3_raw(sc.s[0][3 * i], sc.s[0][3 * i + 1], sc.s[0][3 * i + 2]);
+        a[5 + i] = max3_raw(sc.s[1][3 * i], sc.s[1][3 * i + 1], sc.s[1][3 * i + 2]);
+    }
+    a[10] = max3_raw(sc.s[0][15], sc.s[1][15], a[0]);
+    const float b0 = max3_raw(a[1], a[2], a[3]), b1 = max3_raw(a[4], a[5], a[6]);
+    const float b2 = max3_raw(a[7], a[8], a[9]);
+    float mx = max3_raw(b0, b1, max3_raw(b2, a[10], a[10]));
+    const float other = __shfl_xor(mx, 32);
+    mx = max3_raw(mx, other, other) + sc.sub;
     const bool raise = mx > m + kRaise;
     if (__builtin_amdgcn_ballot_w64(raise)) {  // wave-uniform: rescale when any lane raises
         const float m_new = raise ? mx : m;
@@ -190,15 +213,33 @@ __device__ __forceinline__ void block_softmax_pv(const Scores& sc, const __bf16*
             for (int r = 0; r < 16; ++r) o[c][r] *= alpha;
         m = m_new;
     }
+    // p = 2^(s - m) = 2^(s' - delta) with the stored s' = s - sub; delta is 0 unless the max
+    // moved after this block's scores were formed (the first block, and rare raises)
+    const float delta = m - sc.sub;
     bf16x8 pb[2][2];  // [half][k-step]
+    if (__builtin_amdgcn_ballot_w64(delta != 0.0f)) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                pb[sb][r >> 3][r & 7] = to_bf16(__builtin_amdgcn_exp2f(sc.s[sb][r] - delta));
+    } else {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                pb[sb][r >> 3][r & 7] = to_bf16(__builtin_amdgcn_exp2f(sc.s[sb][r]));
+    }
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float pv = __builtin_amdgcn_exp2f(sc.s[sb][r] - m);
-            l += pv;
-            pb[sb][r >> 3][r & 7] = to_bf16(pv);
-        }
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bf16x2_t pr = {pb[sb][ks][2 * e], pb[sb][ks][2 * e + 1]};
+                l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
+            }
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
         if (key0 + 32 * sb > q0 + kQW - 1) continue;
@@ -285,7 +326,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnParams p) {
     __builtin_amdgcn_s_waitcnt(0);  // this wavefront's LDS fills have landed
     __syncthreads();
     Scores sa, sb;
-    block_scores(sa, kt[0], qv, 0, q0, qi, ln, lh);  // key 0 is visible to every query
+    block_scores(sa, kt[0], qv, 0, q0, qi, ln, lh, m);  // key 0 is visible to every query
     __syncthreads();  // every wavefront is done with kt[0] before block 2's keys overwrite it
 
     // one step: softmax and P V of block kb (scores in cur), scores of block kb + 1 into nxt,
@@ -295,7 +336,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnParams p) {
         if (more_k) load_keys(kb + 2, kt[kb & 1]);
         if (more_v) load_values(kb + 1, vt[(kb + 1) & 1]);
         const int key1 = (kb + 1) * kBN;
-        if (more_v && key1 <= q0 + kQW - 1) block_scores(nxt, kt[(kb + 1) & 1], qv, key1, q0, qi, ln, lh);
+        if (more_v && key1 <= q0 + kQW - 1) block_scores(nxt, kt[(kb + 1) & 1], qv, key1, q0, qi, ln, lh, m);
         if (kb * kBN <= q0 + kQW - 1) block_softmax_pv(cur, vt[kb & 1], o, m, l, kb * kBN, q0, lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
