@@ -441,6 +441,20 @@ BWD_BAD = [
 
 
 @no_gpu
+def test_prefill_backward_workspace_boundary():
+    """One byte below the reported size is rejected before anything is enqueued (the layout the
+    size query reports is the one the call checks, score tiles included)."""
+    need = lt.lightning_prefill_backward_workspace_size(1, 256, 2, 128)
+    a = _bwd_args(wsb=need - 1)
+    st = lt.lib.lightning_prefill_backward(
+        a["q"], a["k"], a["v"], a["g"], a["qw"], a["kw"], a["ow"], a["stride"], a["lam"],
+        a["base"], a["eps"], a["pos0"], a["sin"], a["dy"], a["dso"], a["dq"], a["dk"], a["dv"],
+        a["dg"], a["dsi"], a["dqw"], a["dkw"], a["dow"], a["B"], a["T"], a["H"], a["d"], a["dt"],
+        a["seg"], a["ws"], a["wsb"], a["ev"], a["stream"])
+    assert st == lt.LT_ERR_WORKSPACE
+
+
+@no_gpu
 @pytest.mark.parametrize("name,over,status", BWD_BAD, ids=[c[0] for c in BWD_BAD])
 def test_prefill_backward_rejects(name, over, status):
     a = _bwd_args(**over)
