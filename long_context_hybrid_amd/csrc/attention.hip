@@ -141,39 +141,11 @@ __device__ __forceinline__ void dma_block(const char* blk, __bf16* tile, int wav
 // Scores of one 64-key block for the wavefront's 32 queries, S^T[j][i] in two 32-key halves, in
 // log2 units and shifted by the lane's running max at the time (`sub`, 0 before the first
 // block): the accumulators start at -sub, so the softmax needs no per-element subtraction while
-// the max stays put.  Keys after a lane's query (and whole halves after the wavefront's last
-// query) are -inf.
+// the max stays put.
 struct Scores {
     f32x16 s[2];
     float sub;
 };
-
-__device__ __forceinline__ void block_scores(Scores& sc, const __bf16* kt, const bf16x8 (&qv)[kD / 16],
-                                             int key0, int q0, int qi, int ln, int lh, float m) {
-    sc.sub = m == -INFINITY ? 0.0f : m;
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sc.s[sb][r] = -sc.sub;
-        const int kbase = key0 + 32 * sb;
-        if (kbase > q0 + kQW - 1) {  // half entirely in the future of the wavefront
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sc.s[sb][r] = -INFINITY;
-            continue;
-        }
-        const int row = 32 * sb + ln;
-#pragma unroll
-        for (int s = 0; s < kD / 16; ++s) {
-            const bf16x8 kv = *reinterpret_cast<const bf16x8*>(&kt[key_index(row, 2 * s + lh)]);
-            sc.s[sb] = mfma_bf16(kv, qv[s], sc.s[sb]);
-        }
-        if (kbase + 31 > q0) {  // the diagonal: mask keys after the lane's query
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (kbase + acc_row(r, lh) > qi) sc.s[sb][r] = -INFINITY;
-        }
-    }
-}
 
 // max(a, b, c) as one v_max3_f32.  fmaxf would first quiet each input (a second instruction per
 // value); the scores hold no NaN, and -inf orders as usual.
@@ -183,13 +155,37 @@ __device__ __forceinline__ float max3_raw(float a, float b, float c) {
     return r;
 }
 
-// Online softmax of one block (log2 units; the running max is raised only past kRaise) and
-// O^T += V^T P^T.  The row sum l adds the bf16 probabilities the product uses (packed dot
-// products with ones), so O and l are normalised consistently.
-__device__ __forceinline__ void block_softmax_pv(const Scores& sc, const __bf16* vt,
-                                                 f32x16 (&o)[kD / 32], float& m, float& l,
-                                                 int key0, int q0, int lane) {
-    // the block max by three-input maxima: 32 values in 16 instructions
+// Every key of the block against every query of the wavefront; the causal mask is applied
+// later, by mask_scores, to the blocks that reach the diagonal.
+__device__ __forceinline__ void block_scores(Scores& sc, const __bf16* kt, const bf16x8 (&qv)[kD / 16],
+                                             int ln, int lh, float m) {
+    sc.sub = m == -INFINITY ? 0.0f : m;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc.s[sb][r] = -sc.sub;
+#pragma unroll
+        for (int s = 0; s < kD / 16; ++s) {
+            const bf16x8 kv = *reinterpret_cast<const bf16x8*>(&kt[key_index(32 * sb + ln, 2 * s + lh)]);
+            sc.s[sb] = mfma_bf16(kv, qv[s], sc.s[sb]);
+        }
+    }
+}
+
+// Keys after the lane's query (row key0 + 32 sb + acc_row(r, lh) of the block) become -inf.
+__device__ __forceinline__ void mask_scores(Scores& sc, int key0, int qi, int lh) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (key0 + 32 * sb + acc_row(r, lh) > qi) sc.s[sb][r] = -INFINITY;
+}
+
+// Online-softmax bookkeeping of one block before its probabilities: the block max (three-input
+// maxima, 16 instructions for 32 values); the running max m is raised only past kRaise (then O
+// and l are rescaled), and the stored scores are re-based on m when it moved after they were
+// formed.  Both branches are wave-uniform and rare after the first block.
+__device__ __forceinline__ void settle(Scores& sc, f32x16 (&o)[kD / 32], float& m, float& l) {
     float a[11];
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
@@ -203,7 +199,7 @@ __device__ __forceinline__ void block_softmax_pv(const Scores& sc, const __bf16*
     const float other = __shfl_xor(mx, 32);
     mx = max3_raw(mx, other, other) + sc.sub;
     const bool raise = mx > m + kRaise;
-    if (__builtin_amdgcn_ballot_w64(raise)) {  // wave-uniform: rescale when any lane raises
+    if (__builtin_amdgcn_ballot_w64(raise)) {
         const float m_new = raise ? mx : m;
         const float alpha = exp2f(m - m_new);  // 0 on the first visible block
         l *= alpha;
@@ -213,23 +209,26 @@ __device__ __forceinline__ void block_softmax_pv(const Scores& sc, const __bf16*
             for (int r = 0; r < 16; ++r) o[c][r] *= alpha;
         m = m_new;
     }
-    // p = 2^(s - m) = 2^(s' - delta) with the stored s' = s - sub; delta is 0 unless the max
-    // moved after this block's scores were formed (the first block, and rare raises)
     const float delta = m - sc.sub;
-    bf16x8 pb[2][2];  // [half][k-step]
     if (__builtin_amdgcn_ballot_w64(delta != 0.0f)) {
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                pb[sb][r >> 3][r & 7] = to_bf16(__builtin_amdgcn_exp2f(sc.s[sb][r] - delta));
-    } else {
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                pb[sb][r >> 3][r & 7] = to_bf16(__builtin_amdgcn_exp2f(sc.s[sb][r]));
+            for (int r = 0; r < 16; ++r) sc.s[sb][r] -= delta;
+        sc.sub = m;
     }
+}
+
+// p = 2^(s - m) of one settled block, the row sum l (the bf16 probabilities the product uses,
+// added by packed dot products with ones, so O and l are normalised consistently) and
+// O^T += V^T P^T.
+__device__ __forceinline__ void block_probs_pv(const Scores& sc, const __bf16* vt,
+                                               f32x16 (&o)[kD / 32], float& l, int lane) {
+    bf16x8 pb[2][2];  // [half][k-step]
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pb[sb][r >> 3][r & 7] = to_bf16(__builtin_amdgcn_exp2f(sc.s[sb][r]));
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
@@ -241,8 +240,7 @@ __device__ __forceinline__ void block_softmax_pv(const Scores& sc, const __bf16*
                 l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
             }
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-        if (key0 + 32 * sb > q0 + kQW - 1) continue;
+    for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
@@ -250,7 +248,6 @@ __device__ __forceinline__ void block_softmax_pv(const Scores& sc, const __bf16*
                 const bf16x8 va = tr_operand<kD>(vt, 32 * sb + 16 * ks2, 32 * c, lane);
                 o[c] = mfma_bf16(va, pb[sb][ks2], o[c]);
             }
-    }
 }
 
 template <int GW>  // query heads per workgroup
@@ -326,18 +323,24 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnParams p) {
     __builtin_amdgcn_s_waitcnt(0);  // this wavefront's LDS fills have landed
     __syncthreads();
     Scores sa, sb;
-    block_scores(sa, kt[0], qv, 0, q0, qi, ln, lh, m);  // key 0 is visible to every query
+    block_scores(sa, kt[0], qv, ln, lh, m);  // key 0 is visible to every query
     __syncthreads();  // every wavefront is done with kt[0] before block 2's keys overwrite it
 
     // one step: softmax and P V of block kb (scores in cur), scores of block kb + 1 into nxt,
-    // while the keys of block kb + 2 and the values of block kb + 1 stream into LDS
+    // while the keys of block kb + 2 and the values of block kb + 1 stream into LDS.  The rare
+    // cases (the diagonal's mask, a moved max) are settled first, so the scores of the next
+    // block and the probabilities and P V of this one form one branch-free stretch in which
+    // MFMA and VALU work interleave.  A wavefront whose queries end before a block still runs
+    // it (every key masked: p = 0), one block at most per query tile; the last step's scores
+    // read keys nothing uses.
     auto step = [&](int kb, Scores& cur, Scores& nxt) {
-        const bool more_k = kb + 2 < n_kb, more_v = kb + 1 < n_kb;
-        if (more_k) load_keys(kb + 2, kt[kb & 1]);
-        if (more_v) load_values(kb + 1, vt[(kb + 1) & 1]);
-        const int key1 = (kb + 1) * kBN;
-        if (more_v && key1 <= q0 + kQW - 1) block_scores(nxt, kt[(kb + 1) & 1], qv, key1, q0, qi, ln, lh, m);
-        if (kb * kBN <= q0 + kQW - 1) block_softmax_pv(cur, vt[kb & 1], o, m, l, kb * kBN, q0, lane);
+        const int key0 = kb * kBN;
+        if (key0 + kBN - 1 > q0) mask_scores(cur, key0, qi, lh);
+        settle(cur, o, m, l);
+        if (kb + 2 < n_kb) load_keys(kb + 2, kt[kb & 1]);
+        if (kb + 1 < n_kb) load_values(kb + 1, vt[(kb + 1) & 1]);
+        block_scores(nxt, kt[(kb + 1) & 1], qv, ln, lh, m);
+        block_probs_pv(cur, vt[kb & 1], o, l, lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
