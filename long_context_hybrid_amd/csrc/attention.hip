@@ -148,7 +148,9 @@ struct Scores {
 };
 
 // max(a, b, c) as one v_max3_f32.  fmaxf would first quiet each input (a second instruction per
-// value); the scores hold no NaN, and -inf orders as usual.
+// value); the scores hold no NaN, and -inf orders as usual.  The compiler's hazard checks do not
+// look inside inline assembly, so its inputs must not come straight from an MFMA: settle passes
+// the scores through a wait first.
 __device__ __forceinline__ float max3_raw(float a, float b, float c) {
     float r;
     asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
@@ -186,6 +188,10 @@ __device__ __forceinline__ void mask_scores(Scores& sc, int key0, int qi, int lh
 // and l are rescaled), and the stored scores are re-based on m when it moved after they were
 // formed.  Both branches are wave-uniform and rare after the first block.
 __device__ __forceinline__ void settle(Scores& sc, f32x16 (&o)[kD / 32], float& m, float& l) {
+    // the scores may be MFMA results a few instructions old: 20 wait states (more than a 32x32
+    // MFMA's result needs before a VALU read) first, with the scores passed through the same
+    // statement so that no v_max3_f32 can be scheduled ahead of it
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(sc.s[0]), "+v"(sc.s[1]));
     float a[11];
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
