@@ -8,10 +8,11 @@
 //        q~ = bf16( s_t log2(e) / sqrt(d) * Norm(q) w_q )      (Norm only with QK-norm weights)
 //        k^ = bf16( Norm(k) w_k )            (with key norm weights, or to fill a key cache)
 //      so the score of the main loop is already in log2 units and softmax uses bare exp2.
-//   2. attn_fwd_kernel: flash-style causal attention.  A workgroup of 4 wavefronts holds the
-//      query heads that share one key/value head (up to 4 of them) for a tile of queries, and
-//      streams that head's keys and values in blocks of 64 through double-buffered LDS.  Each
-//      wavefront owns 32 queries of one head:
+//   2. attn_fwd_kernel: flash-style causal attention.  A workgroup of 8 wavefronts (one per CU,
+//      two per SIMD) holds the query heads that share one key/value head (up to 4 of them) for a
+//      tile of queries, and streams that head's keys and values in blocks of 64 through
+//      double-buffered LDS, so each block serves 256 query rows.  Each wavefront owns 32
+//      queries of one head:
 //        * scores are computed transposed, S^T[j][i] = K[j] . q~[i] (A = key rows from LDS,
 //          B = the wavefront's queries, held in registers for the whole loop), so every lane
 //          owns one query: the row max needs one exchange between the two lane halves;
@@ -39,7 +40,7 @@ namespace {
 constexpr int kD = 128;      // head width
 constexpr int kBN = 64;      // keys per block
 constexpr int kQW = 32;      // queries per wavefront
-constexpr int kWaves = 4;    // wavefronts per workgroup
+constexpr int kWaves = 8;    // wavefronts per workgroup (two per SIMD, one workgroup per CU)
 constexpr int kXcds = 8;     // XCDs of an MI355X
 constexpr float kRaise = 8.0f;  // log2 headroom before the running max is raised
 constexpr float kLog2e = 1.4426950408889634f;
@@ -97,30 +98,31 @@ __device__ __forceinline__ int key_index(int row, int chunk) {
 // Key and value blocks go from HBM straight into LDS (global_load_lds_dwordx4): one instruction
 // of a wavefront fills 1 KB of LDS, lane l's 16 bytes at offset 16 l, so each lane loads the
 // global 16-byte chunk that the tile's bank swizzle puts in its slot.  Wavefront w fills rows
-// 16 w .. 16 w + 15 of a 64-row block in four instructions of four rows.  The offsets are fixed
+// kRowsPerWave w .. of a 64-row block in instructions of four rows.  The offsets are fixed
 // per lane (only the last block, which may run past the final key, clamps its rows), and the
 // block's first row is a uniform address, so a block costs no vector address arithmetic and no
 // registers while in flight.
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glob_void_t;
 
+constexpr int kRowsPerWave = kBN / kWaves;     // rows of a block each wavefront loads
+constexpr int kDmaPerBlock = kRowsPerWave / 4;  // its DMA instructions (four rows each)
+static_assert(kRowsPerWave % 4 == 0, "four 256-byte rows per DMA instruction");
+
 struct DmaOffsets {
-    uint32_t k0, k1, k2, k3, v0, v1, v2, v3;  // byte offsets of the lane's key / value chunks
+    uint32_t k[kDmaPerBlock], v[kDmaPerBlock];  // byte offsets of the lane's key / value chunks
 };
 
 __device__ __forceinline__ DmaOffsets dma_offsets(int wave, int lane, uint32_t row_bytes, int last) {
     DmaOffsets o;
     const int slot = lane & 15;
-    uint32_t kk[4], vv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 16 * wave + 4 * i + (lane >> 4);
+    for (int i = 0; i < kDmaPerBlock; ++i) {
+        const int row = kRowsPerWave * wave + 4 * i + (lane >> 4);
         const uint32_t rb = (uint32_t)min(row, last) * row_bytes;
-        kk[i] = rb + 16u * (uint32_t)(slot ^ (row & 15));       // key_index's chunk swizzle
-        vv[i] = rb + 16u * (uint32_t)(slot ^ (4 * (row & 3)));  // nat_index's 32-column XOR
+        o.k[i] = rb + 16u * (uint32_t)(slot ^ (row & 15));       // key_index's chunk swizzle
+        o.v[i] = rb + 16u * (uint32_t)(slot ^ (4 * (row & 3)));  // nat_index's 32-column XOR
     }
-    o.k0 = kk[0]; o.k1 = kk[1]; o.k2 = kk[2]; o.k3 = kk[3];
-    o.v0 = vv[0]; o.v1 = vv[1]; o.v2 = vv[2]; o.v3 = vv[3];
     return o;
 }
 
@@ -128,14 +130,11 @@ __device__ __forceinline__ void dma16(const char* src, __bf16* dst_wave) {
     __builtin_amdgcn_global_load_lds((glob_void_t*)src, (lds_void_t*)dst_wave, 16, 0, 0);
 }
 
-// Rows 16 w .. 16 w + 15 of one key (or value) block into `tile`.
-__device__ __forceinline__ void dma_block(const char* blk, __bf16* tile, int wave, uint32_t o0,
-                                          uint32_t o1, uint32_t o2, uint32_t o3) {
-    __bf16* dst = tile + 16 * kD * wave;
-    dma16(blk + o0, dst);
-    dma16(blk + o1, dst + 4 * kD);
-    dma16(blk + o2, dst + 8 * kD);
-    dma16(blk + o3, dst + 12 * kD);
+// Rows kRowsPerWave w .. of one key (or value) block into `tile`.
+__device__ __forceinline__ void dma_block(const char* blk, __bf16* tile, int wave, const uint32_t* off) {
+    __bf16* dst = tile + kRowsPerWave * kD * wave;
+#pragma unroll
+    for (int i = 0; i < kDmaPerBlock; ++i) dma16(blk + off[i], dst + 4 * i * kD);
 }
 
 // Scores of one 64-key block for the wavefront's 32 queries, S^T[j][i] in two 32-key halves, in
@@ -257,12 +256,15 @@ __device__ __forceinline__ void block_probs_pv(const Scores& sc, const __bf16* v
 }
 
 template <int GW>  // query heads per workgroup
-__global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnParams p) {
+__global__ void __launch_bounds__(64 * kWaves, 1) attn_fwd_kernel(const AttnParams p) {
     constexpr int WPH = kWaves / GW;  // wavefronts per head
     constexpr int BMQ = kQW * WPH;    // queries per workgroup
     // Keys run one block ahead of values: in the step of block j the wavefronts read the keys
     // of block j + 1 (the next step's scores) and the values of block j, while the keys of
-    // block j + 2 and the values of block j + 1 are written into the other halves.
+    // block j + 2 and the values of block j + 1 are written into the other halves.  Eight
+    // wavefronts share each block (256 query rows at two query heads per workgroup).  A third
+    // buffer of each (96 KiB) would let loads run two steps ahead, but LDS offsets past 64 KiB
+    // leave the 16-bit immediate of ds_read, and the extra address registers spilled.
     __shared__ alignas(16) __bf16 kt[2][kBN * kD];
     __shared__ alignas(16) __bf16 vt[2][kBN * kD];
 
@@ -300,12 +302,12 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnParams p) {
     auto load_keys = [&](int kb, __bf16* tile) {
         const DmaOffsets o = kb * kBN + kBN <= p.T ? full
                                                    : dma_offsets(wave, lane, row_bytes, p.T - 1 - kb * kBN);
-        dma_block(kbase + (size_t)kb * blk_bytes, tile, wave, o.k0, o.k1, o.k2, o.k3);
+        dma_block(kbase + (size_t)kb * blk_bytes, tile, wave, o.k);
     };
     auto load_values = [&](int kb, __bf16* tile) {
         const DmaOffsets o = kb * kBN + kBN <= p.T ? full
                                                    : dma_offsets(wave, lane, row_bytes, p.T - 1 - kb * kBN);
-        dma_block(vbase + (size_t)kb * blk_bytes, tile, wave, o.v0, o.v1, o.v2, o.v3);
+        dma_block(vbase + (size_t)kb * blk_bytes, tile, wave, o.v);
     };
 
     // the wavefront's queries: B operand k = 16 s + 8 lh + e of query qi
@@ -322,7 +324,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnParams p) {
     for (int c = 0; c < kD / 32; ++c) o[c] = f32x16{};
     float m = -INFINITY, l = 0.0f;
 
-    // keys of blocks 0 and 1, values of block 0
+    // keys of blocks 0, 1 and 2, values of blocks 0 and 1
     load_keys(0, kt[0]);
     load_values(0, vt[0]);
     if (n_kb > 1) load_keys(1, kt[1]);
@@ -402,7 +404,7 @@ hipError_t launch_fwd(const AttnParams& p, hipStream_t stream) {
     const long long n_qt = (p.T + BMQ - 1) / BMQ;
     const long long n_work = (long long)p.B * p.Hkv * (p.Hq / p.Hkv / GW) * n_qt;
     const long long per_xcd = (n_work + kXcds - 1) / kXcds;
-    attn_fwd_kernel<GW><<<dim3((unsigned)(per_xcd * kXcds)), dim3(256), 0, stream>>>(p);
+    attn_fwd_kernel<GW><<<dim3((unsigned)(per_xcd * kXcds)), dim3(64 * kWaves), 0, stream>>>(p);
     return hipGetLastError();
 }
 
