@@ -495,15 +495,6 @@ def bench_attn_decode(args, torch, lt, synth):
                          "alg_bytes_per_step": alg}}
 
 
-def backward_segments(B, T, H, C=32, cus=256, min_chunks=8):
-    """The segment count lightning_prefill_backward chooses (segments = 0): B H P workgroups
-    fill the CUs once, every segment keeps at least 8 chunks."""
-    n_chunks = -(-T // C)
-    P = max(1, min(-(-cus // (B * H)), n_chunks // min_chunks))
-    cps = -(-n_chunks // P)
-    return -(-n_chunks // cps)
-
-
 def bench_backward(args, torch, lt, synth):
     """The backward of the mixer prefill at the 16K training shape (B = 8, H = 16): dq, dk, dv,
     dgate, d_state_in and the three norm-weight gradients from dL/dy.  The two chunk sweeps are
@@ -533,44 +524,58 @@ def bench_backward(args, torch, lt, synth):
     dq_ms = sum(hev.elapsed_ms(ev[4 * i], ev[4 * i + 1]) for i in range(n)) / n
     dkv_ms = sum(hev.elapsed_ms(ev[4 * i + 2], ev[4 * i + 3]) for i in range(n)) / n
     hev.destroy(ev)
-    P = backward_segments(B, T, H)
+    pl = lt.lightning_prefill_plan_cus(torch.cuda.get_device_properties(0).multi_processor_count,
+                                       B, T, H, d)
+    P, seg_len = pl["backward_segments"], pl["backward_segment_len"]
     units = B * T * H
     wgs = B * H * P
     st = d * d * 4
     C = 32
-    # the two masked C x C fp32 score tiles of each chunk: C * 4 * 2 bytes per token-head
+    act = d * 2  # one bf16 activation row of one token-head
+    # The method's minimum per call: read q, k, v, gate, dy once and write dq, dk, dv, dgate once
+    # (9 rows per token-head), plus recomputing the forward entry states of segments 1 .. P-1
+    # (k and v of segments 0 .. P-2 read once more) and the d x d states (entry state and state
+    # gradient per segment; d_state_in).
+    recompute = B * H * (P - 1) * seg_len * 2 * act if P > 1 else 0
+    method_min = units * 9 * act + recompute + wgs * 2 * st + B * H * st
+    # What the current kernels move besides: dL/do written by the first sweep and read by the
+    # second, and the two masked C x C fp32 score tiles of every chunk likewise.
     score = units * 2 * C * 4
-    # dq sweep: reads q, k, v, gate, dy; writes dq, dgate, do (bf16) and the score tiles;
-    # entry state in, W out
-    alg_dq = units * 8 * d * 2 + score + wgs * 2 * st
-    # dk/dv sweep: reads q, k, v, do and the score tiles; writes dk, dv; the segment's end-state
-    # gradient in
-    alg_dkv = units * 6 * d * 2 + score + wgs * st
+    intermediates = 2 * units * act + 2 * score
+    # Bytes each sweep moves as built (inputs, outputs and intermediates):
+    # dq sweep reads q, k, v, gate, dy; writes dq, dgate, do and the score tiles; entry state in,
+    # W out.  dk/dv sweep reads q, k, v, do and the score tiles; writes dk, dv; the segment's
+    # end-state gradient in.
+    moved_dq = units * 8 * act + score + wgs * 2 * st
+    moved_dkv = units * 6 * act + score + wgs * st
     # useful MFMA flops per token-head: dq sweep 4 C d + 4 d^2 multiply-adds (scores, P V, do V^T,
     # dP K~; q~ S, do S^T, W, S update), dk/dv sweep 2 C d + 3 d^2 (P^T do, dP^T Q~; K~ dS,
     # V dS^T, dS update)
     fl_dq = units * 2 * (4 * C * d + 4 * d * d)
     fl_dkv = units * 2 * (2 * C * d + 3 * d * d)
-    legs = {"dq_sweep": (dq_ms, alg_dq, fl_dq, "bwd_dq_kernel<128> (forward-in-time sweep)"),
-            "dkv_sweep": (dkv_ms, alg_dkv, fl_dkv, "bwd_dkv_kernel<128> (backward-in-time sweep)")}
+    legs = {"dq_sweep": (dq_ms, moved_dq, fl_dq, "bwd_dq_kernel<128> (forward-in-time sweep)"),
+            "dkv_sweep": (dkv_ms, moved_dkv, fl_dkv, "bwd_dkv_kernel<128> (backward-in-time sweep)")}
     dom = max(legs, key=lambda k: legs[k][0])
-    kms, alg, fl, kname = legs[dom]
-    gbs = alg / (kms * 1e-3) / 1e9
     traffic = measured_traffic(dom, spec.name, BWD_TRAFFIC_RECORD, BWD_SOURCES)
+    # The roofline is the whole call's against the method's minimum bytes: intermediates the
+    # implementation chooses to round-trip through HBM earn nothing.
+    gbs = method_min / (ms * 1e-3) / 1e9
     out = {"workload": spec.name, "ms_per_step": round(ms, 4),
            "value": round(B * T / (ms * 1e-3), 1), "unit": "tokens/s/layer",
            "steps": args.bwd_steps, "segments": P,
            "stages_ms": {"dq_sweep": round(dq_ms, 4), "dkv_sweep": round(dkv_ms, 4),
                          "rest": round(ms - dq_ms - dkv_ms, 4)},
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                        "kernel": kname, "alg_bytes_per_launch": alg, "launch_ms": round(kms, 4)},
-           "sweeps": {k: {"ms": round(v[0], 4), "alg_bytes": v[1],
-                          "achieved_gbs": round(v[1] / (v[0] * 1e-3) / 1e9, 1),
+                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "traffic": traffic, "traffic_kernel": legs[dom][3],
+                        "kernel": "whole backward call (state pass, scan, both sweeps, weight sums)",
+                        "alg_bytes_per_launch": method_min,
+                        "bytes_per_token_head": 9 * act, "launch_ms": round(ms, 4)},
+           "intermediate_bytes": intermediates,
+           "sweeps": {k: {"ms": round(v[0], 4), "moved_bytes": v[1],
+                          "moved_gbs": round(v[1] / (v[0] * 1e-3) / 1e9, 1),
                           "useful_tflops": round(v[2] / (v[0] * 1e-3) / 1e12, 1)}
-                      for k, v in legs.items()},
-           "whole_call": {"alg_bytes": alg_dq + alg_dkv,
-                          "hbm_frac": round((alg_dq + alg_dkv) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+                      for k, v in legs.items()}}
     return out
 
 

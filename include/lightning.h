@@ -31,10 +31,16 @@
  *     hipBLASLt handle per device is created on the first layer call and kept (with whatever
  *     memory hipBLASLt gives it) until the process ends.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only enqueues work and
- *     never synchronises the device.  The mixer calls keep no state between calls; the layer
+ *     never synchronises the device.  The work decomposition of the prefill calls depends on the
+ *     number of compute units of the current device, which is queried once per device and
+ *     cached; besides that cache the mixer calls keep no state between calls, and the layer
  *     calls cache, per device and GEMM shape, the hipBLASLt descriptors and algorithm (guarded
  *     by a lock).  All calls are re-entrant; calls that share a workspace or output buffers must
  *     be ordered by the caller.
+ *   - LT_ERR_HIP: the HIP runtime failed (no device visible, a launch rejected).  For tests of
+ *     this path, setting the environment variable LT_FORCE_FAIL to a value other than "" or
+ *     "0" makes every call that would launch work return LT_ERR_HIP instead, after its argument
+ *     checks and before anything is enqueued (no output is written).
  *   - Layouts are dense and row-major: activations [B][T][H][d] (prefill) or [B][H][d] (decode),
  *     state [B][H][d][d], norm weights [H][d] (or one shared [d] when norm_w_head_stride == 0).
  *   - Argument errors are detected on the host before anything is launched; the call then
@@ -81,11 +87,35 @@ lt_status lightning_state_init(float* state, int B, int H, int d, const float* i
 /* Chunk length and number of sequence segments lightning_prefill will use for this shape when
  * called with the same `chunk` and `segments` requests (0 = automatic), and the number of tokens
  * in each segment but the last (which holds the rest of the sequence, never more).  Any output
- * pointer may be NULL.  Returns LT_ERR_UNSUPPORTED for a request the library does not implement. */
+ * pointer may be NULL.  The split depends on the current device's compute units.  Returns
+ * LT_ERR_UNSUPPORTED for a request the library does not implement, LT_ERR_HIP when no device is
+ * visible. */
 lt_status lightning_prefill_plan(int B, int T, int H, int d, int dtype, int chunk, int segments,
                                  int* chunk_out, int* segments_out, int* segment_len_out);
 
-/* Device workspace (bytes) lightning_prefill needs for this shape and request. */
+/* The plan of a prefill request for a device with `num_cus` compute units (lightning_prefill_plan
+ * and the size queries use the current device's), with every workspace size that follows from
+ * it.  Fields that do not apply (sub-segments with one segment; the backward's fields for a shape
+ * it does not support) are 0.  Host-only: usable without a device. */
+typedef struct {
+    int chunk;                      /* tokens per chunk */
+    int segments;                   /* sequence segments per (b, h) */
+    int segment_len;                /* tokens of each segment but the last (T with one segment) */
+    int state_subsegments;          /* state-only sub-segments of each of segments 0 .. P-2 */
+    int subsegment_len;             /* tokens of each of those sub-segments but the last */
+    int backward_segments;          /* lightning_prefill_backward's segments per (b, h) */
+    int backward_segment_len;
+    int reserved;
+    size_t workspace_bytes;         /* lightning_prefill_workspace_size */
+    size_t dd_workspace_bytes;      /* lightning_prefill_dd_workspace_size */
+    size_t backward_workspace_bytes;/* lightning_prefill_backward_workspace_size */
+} lt_prefill_plan;
+
+lt_status lightning_prefill_plan_cus(int num_cus, int B, int T, int H, int d, int dtype,
+                                     int chunk, int segments, lt_prefill_plan* out);
+
+/* Device workspace (bytes) lightning_prefill needs for this shape and request on the current
+ * device (0 when the request is unsupported or no device is visible). */
 size_t lightning_prefill_workspace_size(int B, int T, int H, int d, int dtype, int chunk,
                                         int segments);
 

@@ -59,11 +59,12 @@ struct Plan {
 // splits that keep kMinChunksPerSegment chunks per sub-segment and leave the last one non-empty,
 // the one with the fewest chunks per workgroup slot, counting kStateOnlyBlocksPerCU slots per CU
 // (fewer sub-segments on a tie).
-void choose_sub(long long bh, long long P, long long cps, long long* sub, long long* sub_chunks) {
+void choose_sub(long long cus, long long bh, long long P, long long cps, long long* sub,
+                long long* sub_chunks) {
     *sub = 1;
     *sub_chunks = cps;
     if (P <= 1) return;
-    const long long slots = (long long)lt::kStateOnlyBlocksPerCU * lt::kNumCUs;
+    const long long slots = (long long)lt::kStateOnlyBlocksPerCU * cus;
     const long long most = (slots + bh * (P - 1) - 1) / (bh * (P - 1));
     long long best_cost = -1;
     for (long long s = 1; s <= most; ++s) {
@@ -75,17 +76,27 @@ void choose_sub(long long bh, long long P, long long cps, long long* sub, long l
     }
 }
 
-lt_status plan(int B, int T, int H, int d, int dtype, int chunk, int segments, Plan* out) {
+// The checks of a plan request that need no device: shape, dtype, chunk.
+lt_status check_plan_args(int B, int T, int H, int d, int dtype, int chunk, int segments) {
     if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || segments < 0 || chunk < 0) return LT_ERR_INVALID_ARG;
     if (dtype != LT_F32 && dtype != LT_BF16) return LT_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return LT_ERR_UNSUPPORTED;
     if (chunk != 0 && chunk != lt::kChunk) return LT_ERR_UNSUPPORTED;
+    return LT_OK;
+}
+
+// The split for a device with `cus` compute units (cus >= 1).
+lt_status plan(int cus, int B, int T, int H, int d, int dtype, int chunk, int segments,
+               Plan* out) {
+    const lt_status st = check_plan_args(B, T, H, d, dtype, chunk, segments);
+    if (st != LT_OK) return st;
+    if (cus <= 0) return LT_ERR_INVALID_ARG;
     const int C = lt::kChunk;
     const long long n_chunks = ((long long)T + C - 1) / C;
     const long long bh = (long long)B * H;
     long long P = segments;
     if (P == 0) {
-        P = (lt::kNumCUs + bh - 1) / bh;
+        P = (cus + bh - 1) / bh;
         const long long cap = n_chunks / lt::kMinChunksPerSegment;
         if (P > cap) P = cap;
         if (P < 1) P = 1;
@@ -109,7 +120,7 @@ lt_status plan(int B, int T, int H, int d, int dtype, int chunk, int segments, P
     }
     P = (n_chunks + cps - 1) / cps;  // every segment non-empty
     long long sub = 1, sub_chunks = cps;
-    choose_sub(bh, P, cps, &sub, &sub_chunks);
+    choose_sub(cus, bh, P, cps, &sub, &sub_chunks);
     if (bh * ((P - 1) * sub + 1) > 0x7fffffffLL) return LT_ERR_UNSUPPORTED;
     out->C = C;
     out->P = (int)P;
@@ -117,6 +128,15 @@ lt_status plan(int B, int T, int H, int d, int dtype, int chunk, int segments, P
     out->sub = (int)sub;
     out->sub_len = (int)(sub_chunks * C);
     return LT_OK;
+}
+
+// The plan on the current device (LT_ERR_HIP when its compute units cannot be queried).
+lt_status device_plan(int B, int T, int H, int d, int dtype, int chunk, int segments, Plan* out) {
+    const lt_status st = check_plan_args(B, T, H, d, dtype, chunk, segments);
+    if (st != LT_OK) return st;
+    const int cus = lt::device_cu_count();
+    if (cus <= 0) return LT_ERR_HIP;
+    return plan(cus, B, T, H, d, dtype, chunk, segments, out);
 }
 
 // State slots per (b, h) in the workspace: one per state-only sub-segment, plus the entry state
@@ -136,13 +156,13 @@ size_t workspace_bytes_dd(int B, int H, int d, int P, int sub) {
 
 // Backward: P segments per (b, h), one workgroup each, sized so that B H P fills the CUs once
 // (each workgroup holds a whole CU's LDS); every segment keeps kMinChunksPerSegment chunks.
-Plan bwd_plan(int B, int T, int H, int segments) {
+Plan bwd_plan(int cus, int B, int T, int H, int segments) {
     const int C = lt::kChunk;
     const long long n_chunks = ((long long)T + C - 1) / C;
     const long long bh = (long long)B * H;
     long long P = segments;
     if (P == 0) {
-        P = (lt::kNumCUs + bh - 1) / bh;
+        P = (cus + bh - 1) / bh;
         const long long cap = n_chunks / lt::kMinChunksPerSegment;
         if (P > cap) P = cap;
         if (P < 1) P = 1;
@@ -151,7 +171,7 @@ Plan bwd_plan(int B, int T, int H, int segments) {
     const long long cps = (n_chunks + P - 1) / P;
     P = (n_chunks + cps - 1) / cps;
     long long sub, sub_chunks;
-    choose_sub(bh, P, cps, &sub, &sub_chunks);
+    choose_sub(cus, bh, P, cps, &sub, &sub_chunks);
     Plan pl;
     pl.C = C;
     pl.P = (int)P;
@@ -220,7 +240,7 @@ lt_status lightning_state_init(float* state, int B, int H, int d, const float* i
 lt_status lightning_prefill_plan(int B, int T, int H, int d, int dtype, int chunk, int segments,
                                  int* chunk_out, int* segments_out, int* segment_len_out) {
     Plan pl;
-    const lt_status st = plan(B, T, H, d, dtype, chunk, segments, &pl);
+    const lt_status st = device_plan(B, T, H, d, dtype, chunk, segments, &pl);
     if (st != LT_OK) return st;
     if (chunk_out) *chunk_out = pl.C;
     if (segments_out) *segments_out = pl.P;
@@ -228,24 +248,49 @@ lt_status lightning_prefill_plan(int B, int T, int H, int d, int dtype, int chun
     return LT_OK;
 }
 
+lt_status lightning_prefill_plan_cus(int num_cus, int B, int T, int H, int d, int dtype,
+                                     int chunk, int segments, lt_prefill_plan* out) {
+    if (num_cus <= 0 || out == nullptr) return LT_ERR_INVALID_ARG;
+    Plan pl;
+    const lt_status st = plan(num_cus, B, T, H, d, dtype, chunk, segments, &pl);
+    if (st != LT_OK) return st;
+    memset(out, 0, sizeof *out);
+    out->chunk = pl.C;
+    out->segments = pl.P;
+    out->segment_len = pl.P > 1 ? pl.L : T;
+    out->state_subsegments = pl.P > 1 ? pl.sub : 0;
+    out->subsegment_len = pl.P > 1 ? pl.sub_len : 0;
+    out->workspace_bytes = workspace_bytes_for(B, H, d, pl.P, pl.sub);
+    out->dd_workspace_bytes = workspace_bytes_dd(B, H, d, pl.P, pl.sub);
+    if (bwd_check_shape(B, T, H, d, dtype, segments) == LT_OK) {
+        const Plan bp = bwd_plan(num_cus, B, T, H, segments);
+        out->backward_segments = bp.P;
+        out->backward_segment_len = bp.P > 1 ? bp.L : T;
+        out->backward_workspace_bytes = bwd_layout(B, T, H, d, bp).total;
+    }
+    return LT_OK;
+}
+
 size_t lightning_prefill_workspace_size(int B, int T, int H, int d, int dtype, int chunk,
                                         int segments) {
     Plan pl;
-    if (plan(B, T, H, d, dtype, chunk, segments, &pl) != LT_OK) return 0;
+    if (device_plan(B, T, H, d, dtype, chunk, segments, &pl) != LT_OK) return 0;
     return workspace_bytes_for(B, H, d, pl.P, pl.sub);
 }
 
 size_t lightning_prefill_dd_workspace_size(int B, int T, int H, int d, int dtype, int chunk,
                                            int segments) {
     Plan pl;
-    if (plan(B, T, H, d, dtype, chunk, segments, &pl) != LT_OK) return 0;
+    if (device_plan(B, T, H, d, dtype, chunk, segments, &pl) != LT_OK) return 0;
     return workspace_bytes_dd(B, H, d, pl.P, pl.sub);
 }
 
 size_t lightning_prefill_backward_workspace_size(int B, int T, int H, int d, int dtype,
                                                  int segments) {
     if (bwd_check_shape(B, T, H, d, dtype, segments) != LT_OK) return 0;
-    return bwd_layout(B, T, H, d, bwd_plan(B, T, H, segments)).total;
+    const int cus = lt::device_cu_count();
+    if (cus <= 0) return 0;
+    return bwd_layout(B, T, H, d, bwd_plan(cus, B, T, H, segments)).total;
 }
 
 lt_status lightning_prefill_backward(const void* q, const void* k, const void* v, const void* gate,
@@ -272,7 +317,9 @@ lt_status lightning_prefill_backward(const void* q, const void* k, const void* v
     if (kernel_events && (!kernel_events[0] || !kernel_events[1] || !kernel_events[2] ||
                           !kernel_events[3]))
         return LT_ERR_INVALID_ARG;
-    const Plan pl = bwd_plan(B, T, H, segments);
+    const int cus = lt::device_cu_count();
+    if (cus <= 0) return LT_ERR_HIP;
+    const Plan pl = bwd_plan(cus, B, T, H, segments);
     const BwdLayout lay = bwd_layout(B, T, H, d, pl);
     if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < lay.total)
         return LT_ERR_WORKSPACE;
@@ -362,12 +409,14 @@ lt_status prefill_strided(const void* q, const void* k, const void* v, const voi
     if (td && !aligned16(log2_decay)) return LT_ERR_INVALID_ARG;
     if (x_stride < H * d || x_stride % 8 != 0) return LT_ERR_INVALID_ARG;
     if ((double)B * T * x_stride > 9.0e15) return LT_ERR_UNSUPPORTED;
-    Plan pl;
-    st = plan(B, T, H, d, dtype, chunk, segments, &pl);
+    st = check_plan_args(B, T, H, d, dtype, chunk, segments);
     if (st != LT_OK) return st;
     if (main_kernel_events && (!main_kernel_events[0] || !main_kernel_events[1]))
         return LT_ERR_INVALID_ARG;
     if (validate_only) return LT_OK;
+    Plan pl;
+    st = device_plan(B, T, H, d, dtype, chunk, segments, &pl);
+    if (st != LT_OK) return st;
     const int P = pl.P;
     const size_t need =
         td ? workspace_bytes_dd(B, H, d, P, pl.sub) : workspace_bytes_for(B, H, d, P, pl.sub);

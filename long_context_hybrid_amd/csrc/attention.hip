@@ -324,7 +324,7 @@ __global__ void __launch_bounds__(64 * kWaves, 1) attn_fwd_kernel(const AttnPara
     for (int c = 0; c < kD / 32; ++c) o[c] = f32x16{};
     float m = -INFINITY, l = 0.0f;
 
-    // keys of blocks 0, 1 and 2, values of blocks 0 and 1
+    // keys of blocks 0 and 1, values of block 0
     load_keys(0, kt[0]);
     load_values(0, vt[0]);
     if (n_kb > 1) load_keys(1, kt[1]);
@@ -339,8 +339,10 @@ __global__ void __launch_bounds__(64 * kWaves, 1) attn_fwd_kernel(const AttnPara
     // cases (the diagonal's mask, a moved max) are settled first, so the scores of the next
     // block and the probabilities and P V of this one form one branch-free stretch in which
     // MFMA and VALU work interleave.  A wavefront whose queries end before a block still runs
-    // it (every key masked: p = 0), one block at most per query tile; the last step's scores
-    // read keys nothing uses.
+    // it (every key masked: p = 0): with two query heads per workgroup (128-query tiles) the
+    // first two wavefronts of a head run one such block per tile, with one head (256-query
+    // tiles) wavefronts 0-1 run three, 2-3 two and 4-5 one.  The last step's scores read keys
+    // nothing uses.
     auto step = [&](int kb, Scores& cur, Scores& nxt) {
         const int key0 = kb * kBN;
         if (key0 + kBN - 1 > q0) mask_scores(cur, key0, qi, lh);
@@ -673,6 +675,7 @@ hipError_t launch_decode_partial(const AttnDecodeParams& p, hipStream_t stream) 
 }  // namespace
 
 hipError_t launch_attn_decode(const AttnDecodeParams& p, hipStream_t stream) {
+    if (const hipError_t g = launch_gate(); g != hipSuccess) return g;
     attn_append_kernel<<<dim3((unsigned)((p.B * p.Hkv + 3) / 4)), dim3(256), 0, stream>>>(p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -695,6 +698,7 @@ int attn_heads_per_workgroup(int Hq, int Hkv) {
 
 hipError_t launch_attn_prefill(const AttnParams& p, const hipEvent_t events[2],
                                hipStream_t stream) {
+    if (const hipError_t g = launch_gate(); g != hipSuccess) return g;
     const long long rows =
         (long long)p.B * p.T * p.Hq + (p.write_keys ? (long long)p.B * p.T * p.Hkv : 0);
     attn_prologue_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream>>>(p);

@@ -1064,6 +1064,7 @@ __global__ void __launch_bounds__(256) bwd_wgrad_kernel(const BwdParams p, int d
 hipError_t launch_prefill_backward(const BwdParams& p, const ChunkParams& fwd_cp,
                                    const ScanParams& fwd_sp, const hipEvent_t ev[4],
                                    hipStream_t stream) {
+    if (const hipError_t g = launch_gate(); g != hipSuccess) return g;
     constexpr int D = 128;
     const int BH = p.B * p.H;
     hipError_t err;

@@ -162,6 +162,7 @@ void launch_decode_typed(const DecodeParams& dp, int d, int dtype, hipStream_t s
 
 hipError_t launch_decode(const DecodeParams& dp, int d, int dtype, hipStream_t stream,
                          bool time_dep) {
+    if (const hipError_t g = launch_gate(); g != hipSuccess) return g;
     if (time_dep)
         launch_decode_typed<true>(dp, d, dtype, stream);
     else
@@ -170,6 +171,7 @@ hipError_t launch_decode(const DecodeParams& dp, int d, int dtype, hipStream_t s
 }
 
 hipError_t launch_state_init(float* state, const float* init, size_t n, hipStream_t stream) {
+    if (const hipError_t g = launch_gate(); g != hipSuccess) return g;
     if (state == init) return hipSuccess;
     const size_t threads = (n + 3) / 4;
     state_init_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream>>>(state, init, n);

@@ -91,6 +91,7 @@ size_t gemm_workspace_limit() { return size_t(32) << 20; }
 
 lt_status gemm_xwt(const void* A, const void* W, void* D, int64_t M, int64_t N, int64_t K,
                    int dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (launch_gate() != hipSuccess) return LT_ERR_HIP;
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return LT_ERR_HIP;
     hipblasLtHandle_t h;

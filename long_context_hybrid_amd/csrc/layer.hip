@@ -76,6 +76,19 @@ lt_status lightning_layer_prefill(const void* x, const void* w_qkvz, const void*
     if (stage_events)
         for (int i = 0; i < 4; ++i)
             if (!stage_events[i]) return LT_ERR_INVALID_ARG;
+    const size_t es = dtype == LT_BF16 ? 2 : 4;
+    const int hd = H * d;
+    // The mixer's own argument checks run first (on stand-in pointers with the alignment of the
+    // real ones), so that a bad norm weight, lambda, rope base or eps launches nothing at all.
+    {
+        char* const fake = reinterpret_cast<char*>(static_cast<uintptr_t>(kAlign));
+        lt_status st = lt::prefill_strided(
+            fake, fake + (size_t)hd * es, fake + (size_t)2 * hd * es, fake + (size_t)3 * hd * es,
+            4 * hd, q_norm_w, k_norm_w, o_norm_w, norm_w_head_stride, lambda, rope_base, rms_eps,
+            pos0, state_in, state_out, fake, nullptr, B, T, H, d, dtype, chunk, segments, nullptr,
+            0, nullptr, nullptr, /*validate_only=*/true);
+        if (st != LT_OK) return st;
+    }
     int c = 0;
     lt_status st = lightning_prefill_plan(B, T, H, d, dtype, chunk, segments, &c, nullptr, nullptr);
     if (st != LT_OK) return st;
@@ -86,23 +99,12 @@ lt_status lightning_layer_prefill(const void* x, const void* w_qkvz, const void*
         workspace_bytes < w.total)
         return LT_ERR_WORKSPACE;
     char* ws = static_cast<char*>(workspace);
-    const size_t es = dtype == LT_BF16 ? 2 : 4;
-    const int hd = H * d;
     char* proj = ws + w.proj;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     auto mark = [&](int i) {
         return stage_events == nullptr ||
                hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s) == hipSuccess;
     };
-
-    // The mixer's own argument checks run first, on the pointers it will be given, so that a
-    // bad norm weight, lambda, rope base or eps launches nothing at all.
-    st = lt::prefill_strided(proj, proj + (size_t)hd * es, proj + (size_t)2 * hd * es,
-                             proj + (size_t)3 * hd * es, 4 * hd, q_norm_w, k_norm_w, o_norm_w,
-                             norm_w_head_stride, lambda, rope_base, rms_eps, pos0, state_in,
-                             state_out, ws + w.y, nullptr, B, T, H, d, dtype, chunk, segments,
-                             nullptr, 0, nullptr, nullptr, /*validate_only=*/true);
-    if (st != LT_OK) return st;
 
     const int64_t rows = (int64_t)B * T;
     if (!mark(0)) return LT_ERR_HIP;

@@ -9,8 +9,18 @@
 
 namespace lt {
 
+// Compute units of the calling thread's current device.  Queried through the HIP runtime on the
+// first call for a device and cached for the life of the process (the only state the library
+// keeps between calls besides the GEMM plan cache).  Returns 0 when the query fails, e.g. when no
+// device is visible; the callers then report LT_ERR_HIP.
+int device_cu_count();
+
+// Launch-failure hook for tests of the error path: while the environment variable LT_FORCE_FAIL
+// is set to a value other than "" or "0", every launch wrapper returns hipErrorLaunchFailure
+// before enqueuing anything, so the entry points report LT_ERR_HIP with no output written.
+hipError_t launch_gate();
+
 constexpr int kChunk = 32;        // tokens per chunk of the prefill chunk loop
-constexpr int kNumCUs = 256;      // compute units of an MI355X; sizes the automatic segment split
 constexpr int kMinChunksPerSegment = 8;
 constexpr int kStateOnlyBlocksPerCU = 2;  // workgroups per CU that the state-only pass is sized for
 constexpr int kLastSegmentPercent = 92;   // bf16: last segment length relative to the others

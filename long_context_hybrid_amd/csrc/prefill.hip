@@ -1008,6 +1008,7 @@ hipError_t launch_mode(const ChunkParams& cp, const ScanParams& sp, int d, int d
 
 hipError_t launch_prefill_states(const ChunkParams& cp, const ScanParams& sp, int d, int dtype,
                                  hipStream_t stream) {
+    if (const hipError_t g = launch_gate(); g != hipSuccess) return g;
     if (cp.P > 1) {
         if (dtype == LT_BF16) {
             if (d == 128) launch_states_typed<ModeBF16, 128, false>(cp, sp, stream);
@@ -1022,6 +1023,7 @@ hipError_t launch_prefill_states(const ChunkParams& cp, const ScanParams& sp, in
 
 hipError_t launch_prefill(const ChunkParams& cp, const ScanParams& sp, int d, int dtype,
                           const hipEvent_t ev[2], hipStream_t stream, bool time_dep) {
+    if (const hipError_t g = launch_gate(); g != hipSuccess) return g;
     return time_dep ? launch_mode<true>(cp, sp, d, dtype, ev, stream)
                     : launch_mode<false>(cp, sp, d, dtype, ev, stream);
 }

@@ -14,7 +14,8 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liblightning.so")
+# LIGHTNING_LIBRARY selects another build of the same sources (e.g. the host-sanitizer build).
+LIB_PATH = os.environ.get("LIGHTNING_LIBRARY") or os.path.join(HERE, "liblightning.so")
 
 LT_OK, LT_ERR_INVALID_ARG, LT_ERR_UNSUPPORTED, LT_ERR_WORKSPACE, LT_ERR_HIP = range(5)
 LT_F32, LT_BF16 = 0, 1
@@ -25,6 +26,7 @@ EXPORTS = (
     "lightning_hypenet_gamma",
     "lightning_state_init",
     "lightning_prefill_plan",
+    "lightning_prefill_plan_cus",
     "lightning_prefill_workspace_size",
     "lightning_prefill",
     "lightning_decode_step",
@@ -42,6 +44,15 @@ EXPORTS = (
     "lightning_attn_decode_workspace_size",
     "lightning_attn_decode_step",
 )
+
+
+class PrefillPlan(ct.Structure):
+    """lt_prefill_plan of include/lightning.h."""
+    _fields_ = [("chunk", ct.c_int), ("segments", ct.c_int), ("segment_len", ct.c_int),
+                ("state_subsegments", ct.c_int), ("subsegment_len", ct.c_int),
+                ("backward_segments", ct.c_int), ("backward_segment_len", ct.c_int),
+                ("reserved", ct.c_int), ("workspace_bytes", ct.c_size_t),
+                ("dd_workspace_bytes", ct.c_size_t), ("backward_workspace_bytes", ct.c_size_t)]
 
 
 class LightningError(RuntimeError):
@@ -64,6 +75,9 @@ def _load() -> ct.CDLL:
     h.lightning_state_init.restype = i32
     h.lightning_prefill_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp]
     h.lightning_prefill_plan.restype = i32
+    h.lightning_prefill_plan_cus.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32,
+                                             ct.POINTER(PrefillPlan)]
+    h.lightning_prefill_plan_cus.restype = i32
     h.lightning_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     h.lightning_prefill_workspace_size.restype = sz
     h.lightning_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, f64, f64, i64, vp, vp,
@@ -201,6 +215,17 @@ def lightning_prefill_plan(B, T, H, d, dtype=torch.bfloat16, chunk=0, segments=0
                                       ct.byref(c), ct.byref(p), ct.byref(n)),
            "lightning_prefill_plan")
     return c.value, p.value, n.value
+
+
+def lightning_prefill_plan_cus(num_cus, B, T, H, d, dtype=torch.bfloat16, chunk=0,
+                               segments=0) -> dict:
+    """The plan (and workspace sizes) of a prefill request on a device with num_cus compute
+    units, as a dict of the lt_prefill_plan fields.  Host-only."""
+    out = PrefillPlan()
+    _check(lib.lightning_prefill_plan_cus(num_cus, B, T, H, d, _dtype_code(dtype), chunk,
+                                          segments, ct.byref(out)),
+           "lightning_prefill_plan_cus")
+    return {name: getattr(out, name) for name, _ in PrefillPlan._fields_ if name != "reserved"}
 
 
 def lightning_prefill_workspace_size(B, T, H, d, dtype=torch.bfloat16, chunk=0, segments=0) -> int:

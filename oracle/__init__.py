@@ -56,6 +56,10 @@ def load(path: str | None = None):
     if path is not None:
         return _bind(ct.CDLL(path))
     if _lib is None:
+        alt = os.environ.get("ORACLE_LIBRARY")  # another build of oracle.c (sanitizer runs)
+        if alt:
+            _lib = _bind(ct.CDLL(alt))
+            return _lib
         if not os.path.exists(LIB_PATH):
             from . import build as _build
 

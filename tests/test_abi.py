@@ -84,32 +84,84 @@ def test_hypenet_gamma_time_scales():
     (2, 100000, 2, 64, 64, 2),      # 3125 chunks over 64 segments of 49 (sub-segments 25 + 24)
 ])
 def test_plan_and_workspace(B, T, H, d, expect_p, expect_sub):
-    c, p, seg_len = lt.lightning_prefill_plan(B, T, H, d)
-    assert c == 32 and p == expect_p
+    pl = lt.lightning_prefill_plan_cus(256, B, T, H, d)
+    p, seg_len = pl["segments"], pl["segment_len"]
+    assert pl["chunk"] == 32 and p == expect_p
     # every segment but the last has seg_len tokens (a whole number of chunks); the last is
     # non-empty and no longer; one segment is the whole sequence
     if p > 1:
         assert seg_len % 32 == 0 and 0 < T - (p - 1) * seg_len <= seg_len
+        assert pl["state_subsegments"] == expect_sub
     else:
-        assert seg_len == T
-    ws = lt.lightning_prefill_workspace_size(B, T, H, d)
+        assert seg_len == T and pl["state_subsegments"] == 0
     # one fp32 d x d state per state-only sub-segment of segments 0 .. P-2, plus the entry state
     # of the last segment
     slots = (p - 1) * expect_sub + 1
-    assert ws == (B * H * slots * d * d * 4 if p > 1 else 0)
+    assert pl["workspace_bytes"] == (B * H * slots * d * d * 4 if p > 1 else 0)
+
+
+@pytest.mark.parametrize("cus,B,T,H,expect_p,expect_sub,expect_len", [
+    # 512K tokens, 16 heads on 32 CUs: two segments; the bf16 last segment is made shorter
+    # (8533 + 7851 chunks), and each state-only segment is cut in four (4 x 16 = 64 = 2 x 32 slots)
+    (32, 1, 524288, 16, 2, 4, 8533 * 32),
+    # on 80 CUs: five segments of 3330 chunks (the last 3064), state-only pass in halves
+    (80, 1, 524288, 16, 5, 2, 3330 * 32),
+    # B*H = 128 already fills 32 or 80 CUs: no segments at all
+    (32, 4, 131072, 32, 1, 0, 131072),
+    (80, 4, 131072, 32, 1, 0, 131072),
+    # 128 chunks of one head: the eight-chunk minimum caps the split at 16 segments on any device
+    (32, 1, 4096, 1, 16, 1, 256),
+    (80, 1, 4096, 1, 16, 1, 256),
+])
+def test_plan_on_other_devices(cus, B, T, H, expect_p, expect_sub, expect_len):
+    pl = lt.lightning_prefill_plan_cus(cus, B, T, H, 128)
+    assert (pl["segments"], pl["state_subsegments"], pl["segment_len"]) == \
+        (expect_p, expect_sub, expect_len)
+    if expect_p > 1:
+        # the main pass gives every CU a workgroup (unless the eight-chunk minimum per segment
+        # runs out first); the state-only pass stays within its two slots per CU
+        assert B * H * expect_p >= min(cus, B * H * (((T + 31) // 32) // 8))
+        assert B * H * (expect_p - 1) * expect_sub <= 2 * cus
+    slots = (expect_p - 1) * expect_sub + 1 if expect_p > 1 else 0
+    assert pl["workspace_bytes"] == B * H * slots * 128 * 128 * 4
+
+
+def test_plan_needs_positive_cus():
+    for cus in (0, -1):
+        with pytest.raises(lt.LightningError) as e:
+            lt.lightning_prefill_plan_cus(cus, 1, 1000, 2, 128)
+        assert e.value.status == lt.LT_ERR_INVALID_ARG
 
 
 def test_plan_explicit_segments_and_chunk():
-    assert lt.lightning_prefill_plan(1, 1000, 2, 128, segments=3)[:2] == (32, 3)
+    assert lt.lightning_prefill_plan_cus(256, 1, 1000, 2, 128, segments=3)["segments"] == 3
     # more segments than chunks collapses to one chunk per segment
-    assert lt.lightning_prefill_plan(1, 100, 2, 128, segments=50)[:2] == (32, 4)
-    with pytest.raises(lt.LightningError) as e:
-        lt.lightning_prefill_plan(1, 1000, 2, 128, chunk=48)
-    assert e.value.status == lt.LT_ERR_UNSUPPORTED
-    with pytest.raises(lt.LightningError) as e:
-        lt.lightning_prefill_plan(1, 1000, 2, 96)
-    assert e.value.status == lt.LT_ERR_UNSUPPORTED
+    pl = lt.lightning_prefill_plan_cus(256, 1, 100, 2, 128, segments=50)
+    assert (pl["chunk"], pl["segments"]) == (32, 4)
+    for kw in (dict(chunk=48), dict(d=96)):
+        a = dict(B=1, T=1000, H=2, d=128)
+        a.update(kw)
+        with pytest.raises(lt.LightningError) as e:
+            lt.lightning_prefill_plan(a["B"], a["T"], a["H"], a["d"], chunk=a.get("chunk", 0))
+        assert e.value.status == lt.LT_ERR_UNSUPPORTED
+        with pytest.raises(lt.LightningError) as e:
+            lt.lightning_prefill_plan_cus(256, a["B"], a["T"], a["H"], a["d"],
+                                          chunk=a.get("chunk", 0))
+        assert e.value.status == lt.LT_ERR_UNSUPPORTED
     assert lt.lightning_prefill_workspace_size(1, 1000, 2, 96) == 0
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="checks the behaviour without a device")
+def test_plan_without_a_device_is_a_hip_error():
+    """The automatic split depends on the device's compute units: with no device visible the
+    device-dependent queries report LT_ERR_HIP (or a size of 0), never a guessed plan."""
+    with pytest.raises(lt.LightningError) as e:
+        lt.lightning_prefill_plan(1, 524288, 16, 128)
+    assert e.value.status == lt.LT_ERR_HIP
+    assert lt.lightning_prefill_workspace_size(1, 524288, 16, 128) == 0
+    assert lt.lightning_prefill_dd_workspace_size(1, 524288, 16, 128) == 0
+    assert lt.lightning_prefill_backward_workspace_size(8, 16384, 16, 128) == 0
+    assert lt.lightning_layer_prefill_workspace_size(1, 4096, 16, 128, 2048) == 0
 
 
 # ---- argument validation with fake device addresses (only where no GPU is visible) ---------
@@ -161,10 +213,11 @@ PREFILL_BAD = [
     ("eps_negative", dict(eps=-1e-6), lt.LT_ERR_INVALID_ARG),
     ("pos0_negative", dict(pos0=-1), lt.LT_ERR_INVALID_ARG),
     ("chunk_unsupported", dict(chunk=48), lt.LT_ERR_UNSUPPORTED),
-    ("workspace_missing", dict(T=524288, H=16, lam=[0.9] * 16), lt.LT_ERR_WORKSPACE),
-    ("workspace_small", dict(T=524288, H=16, lam=[0.9] * 16, ws=FAKE, wsb=1024), lt.LT_ERR_WORKSPACE),
-    ("workspace_misaligned", dict(T=524288, H=16, lam=[0.9] * 16, ws=FAKE + 8, wsb=1 << 30),
-     lt.LT_ERR_WORKSPACE),
+    # Every argument valid: the call then needs the device (its compute units size the plan and
+    # the workspace), and without one it reports LT_ERR_HIP before anything else.  The workspace
+    # checks themselves run with a device in tests/test_gpu_errors.py.
+    ("no_device", dict(T=524288, H=16, lam=[0.9] * 16, ws=FAKE, wsb=1 << 40), lt.LT_ERR_HIP),
+    ("no_device_workspace_missing", dict(T=524288, H=16, lam=[0.9] * 16), lt.LT_ERR_HIP),
     ("events_null_entries", dict(ev=(ct.c_void_p * 2)(None, None)), lt.LT_ERR_INVALID_ARG),
 ]
 
@@ -184,6 +237,8 @@ DECODE_BAD = [
     ("d_32", dict(d=32, stride=32), lt.LT_ERR_UNSUPPORTED),
     ("lambda_above_one", dict(lam=[2.0, 0.5]), lt.LT_ERR_INVALID_ARG),
     ("eps_nan", dict(eps=float("nan")), lt.LT_ERR_INVALID_ARG),
+    # every argument valid: the launch itself fails without a device
+    ("no_device", dict(), lt.LT_ERR_HIP),
 ]
 
 
@@ -212,18 +267,15 @@ def test_state_init_rejects():
 # ---- the whole layer -------------------------------------------------------------------------------
 
 def test_layer_workspace_sizes():
-    # 512K-token Qwen3-1.7B-shaped layer: projections and y in bf16, then the mixer's state slots,
-    # then 32 MiB of GEMM scratch, each part 256-byte aligned
-    B, T, H, d, dm = 1, 524288, 16, 128, 2048
-    mix = lt.lightning_prefill_workspace_size(B, T, H, d)
-    expect = T * 4 * H * d * 2 + T * H * d * 2 + (mix + 255) // 256 * 256 + (32 << 20)
-    assert lt.lightning_layer_prefill_workspace_size(B, T, H, d, dm) == expect
-    assert lt.lightning_layer_decode_workspace_size(64, H, d, dm) == \
-        64 * 4 * H * d * 2 + 64 * H * d * 2 + (32 << 20)
+    # decode step: projections and y in bf16, then 32 MiB of GEMM scratch, each part 256-byte
+    # aligned (no mixer workspace, so no device is needed to size it)
+    B, H, d, dm = 64, 16, 128, 2048
+    assert lt.lightning_layer_decode_workspace_size(B, H, d, dm) == \
+        B * 4 * H * d * 2 + B * H * d * 2 + (32 << 20)
     f32 = lt.lightning_layer_decode_workspace_size(3, 2, 64, 64, torch.float32)
     assert f32 == (3 * 512 * 4 + 255) // 256 * 256 + (3 * 128 * 4 + 255) // 256 * 256 + (32 << 20)
-    assert lt.lightning_layer_prefill_workspace_size(B, T, H, d, 100) == 0  # d_model % 8
-    assert lt.lightning_layer_prefill_workspace_size(B, T, H, 96, dm) == 0
+    assert lt.lightning_layer_prefill_workspace_size(1, 4096, H, d, 100) == 0  # d_model % 8
+    assert lt.lightning_layer_prefill_workspace_size(1, 4096, H, 96, dm) == 0
     assert lt.lightning_layer_decode_workspace_size(0, H, d, dm) == 0
 
 
@@ -247,9 +299,10 @@ LAYER_BAD = [
     ("zero_T", dict(T=0), lt.LT_ERR_INVALID_ARG),
     ("bad_dtype", dict(dt=3), lt.LT_ERR_INVALID_ARG),
     ("d_96", dict(d=96, stride=96), lt.LT_ERR_UNSUPPORTED),
-    ("workspace_missing", dict(ws=None), lt.LT_ERR_WORKSPACE),
-    ("workspace_small", dict(wsb=1 << 20), lt.LT_ERR_WORKSPACE),
-    ("workspace_not_256_aligned", dict(ws=FAKE * 16 + 16), lt.LT_ERR_WORKSPACE),
+    # valid arguments: sizing the mixer's workspace needs the device, so without one the call
+    # reports LT_ERR_HIP (the workspace checks run on the GPU in tests/test_layer_gpu.py)
+    ("no_device", dict(), lt.LT_ERR_HIP),
+    ("no_device_workspace_missing", dict(ws=None), lt.LT_ERR_HIP),
     # mixer arguments are checked before the first GEMM is enqueued
     ("lambda_nan", dict(lam=[float("nan"), 0.5]), lt.LT_ERR_INVALID_ARG),
     ("null_qnorm", dict(qw=None), lt.LT_ERR_INVALID_ARG),
@@ -358,12 +411,13 @@ def test_attn_prefill_rejects(name, over, status):
 
 def test_dd_workspace_adds_subsegment_decays():
     B, T, H, d = 1, 524288, 16, 128
-    base = lt.lightning_prefill_workspace_size(B, T, H, d)
-    _, P, _ = lt.lightning_prefill_plan(B, T, H, d)
+    pl = lt.lightning_prefill_plan_cus(256, B, T, H, d)
+    base = pl["workspace_bytes"]
     slots = base // (B * H * d * d * 4)  # (P - 1) sub + 1 state slots per (b, h)
+    assert slots == (pl["segments"] - 1) * pl["state_subsegments"] + 1
     expect = (base + 255) // 256 * 256 + B * H * (slots - 1) * 4
-    assert lt.lightning_prefill_dd_workspace_size(B, T, H, d) == expect
-    assert lt.lightning_prefill_dd_workspace_size(1, 200, 2, 128) == 0  # one segment
+    assert pl["dd_workspace_bytes"] == expect
+    assert lt.lightning_prefill_plan_cus(256, 1, 200, 2, 128)["dd_workspace_bytes"] == 0
 
 
 @no_gpu
@@ -372,7 +426,7 @@ def test_dd_workspace_adds_subsegment_decays():
     ("misaligned_decay", dict(dec=FAKE + 4), lt.LT_ERR_INVALID_ARG),
     ("null_q", dict(q=None), lt.LT_ERR_INVALID_ARG),
     ("d_96", dict(d=96, stride=96), lt.LT_ERR_UNSUPPORTED),
-    ("workspace_missing", dict(T=524288, H=16), lt.LT_ERR_WORKSPACE),
+    ("no_device_workspace_missing", dict(T=524288, H=16), lt.LT_ERR_HIP),
 ], ids=lambda x: x if isinstance(x, str) else "")
 def test_prefill_dd_rejects(name, over, status):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, qw=FAKE, kw=FAKE, ow=None, stride=128, dec=FAKE,
@@ -391,16 +445,18 @@ def test_prefill_dd_rejects(name, over, status):
 
 def test_backward_workspace_layout():
     B, T, H, d = 8, 16384, 16, 128
-    ws = lt.lightning_prefill_backward_workspace_size(B, T, H, d)
+    pl = lt.lightning_prefill_plan_cus(256, B, T, H, d)
+    ws = pl["backward_workspace_bytes"]
     # at least: do (bf16, one activation tensor), the two masked 32 x 32 fp32 score tiles of
     # every chunk, one d x d state gradient per (b, h, segment)
     assert ws >= B * T * H * d * 2 + B * H * (T // 32) * 2 * 32 * 32 * 4 + B * H * d * d * 4
-    assert ws % 4 == 0
+    assert ws % 4 == 0 and pl["backward_segments"] == 2
     # unsupported shapes report 0
-    assert lt.lightning_prefill_backward_workspace_size(B, T, H, 64) == 0
-    assert lt.lightning_prefill_backward_workspace_size(B, T, H, d, torch.float32) == 0
+    assert lt.lightning_prefill_plan_cus(256, B, T, H, 64)["backward_workspace_bytes"] == 0
+    assert lt.lightning_prefill_plan_cus(256, B, T, H, d, torch.float32)[
+        "backward_workspace_bytes"] == 0
     # one segment (B H fills the CUs): no forward state slots, one gradient per (b, h)
-    one = lt.lightning_prefill_backward_workspace_size(16, 256, 16, d)
+    one = lt.lightning_prefill_plan_cus(256, 16, 256, 16, d)["backward_workspace_bytes"]
     do_bytes = 16 * 256 * 16 * d * 2
     score_bytes = 16 * 16 * (256 // 32) * 2 * 32 * 32 * 4
     assert one >= do_bytes + score_bytes + 16 * 16 * d * d * 4
@@ -433,25 +489,13 @@ BWD_BAD = [
     ("pos0_negative", dict(pos0=-3), lt.LT_ERR_INVALID_ARG),
     ("fp32", dict(dt=lt.LT_F32), lt.LT_ERR_UNSUPPORTED),
     ("d_64", dict(d=64, stride=64), lt.LT_ERR_UNSUPPORTED),
-    ("workspace_missing", dict(ws=None), lt.LT_ERR_WORKSPACE),
-    ("workspace_small", dict(wsb=1024), lt.LT_ERR_WORKSPACE),
     ("events_null_entries", dict(ev=(ct.c_void_p * 4)(None, None, None, None)),
      lt.LT_ERR_INVALID_ARG),
+    # valid arguments: the plan needs the device, so without one the call reports LT_ERR_HIP
+    # (the workspace checks run on the GPU in tests/test_gpu_errors.py)
+    ("no_device", dict(), lt.LT_ERR_HIP),
+    ("no_device_workspace_missing", dict(ws=None), lt.LT_ERR_HIP),
 ]
-
-
-@no_gpu
-def test_prefill_backward_workspace_boundary():
-    """One byte below the reported size is rejected before anything is enqueued (the layout the
-    size query reports is the one the call checks, score tiles included)."""
-    need = lt.lightning_prefill_backward_workspace_size(1, 256, 2, 128)
-    a = _bwd_args(wsb=need - 1)
-    st = lt.lib.lightning_prefill_backward(
-        a["q"], a["k"], a["v"], a["g"], a["qw"], a["kw"], a["ow"], a["stride"], a["lam"],
-        a["base"], a["eps"], a["pos0"], a["sin"], a["dy"], a["dso"], a["dq"], a["dk"], a["dv"],
-        a["dg"], a["dsi"], a["dqw"], a["dkw"], a["dow"], a["B"], a["T"], a["H"], a["d"], a["dt"],
-        a["seg"], a["ws"], a["wsb"], a["ev"], a["stream"])
-    assert st == lt.LT_ERR_WORKSPACE
 
 
 @no_gpu

@@ -84,6 +84,9 @@ SMALL = [
     ("gqa2_ragged", 1, 300, 4, 2, 500.0, True, 0),
     ("gqa4_two_batches", 2, 1000, 8, 2, 600.0, True, 0),
     ("mha_short_ragged", 1, 65, 2, 2, 900.0, True, 0),
+    # one query head per workgroup: three 256-query tiles, so wavefronts run fully masked
+    # blocks (up to three per tile) and tiles end mid-block
+    ("mha_three_tiles", 1, 700, 2, 2, 500.0, True, 0),
     ("gqa2_no_norm_no_scale", 1, 513, 4, 2, 0.0, False, 0),
     ("gqa8_far_position", 1, 777, 8, 1, 500.0, True, 100000),
     ("single_token", 3, 1, 4, 2, 500.0, True, 5),
