@@ -152,6 +152,28 @@ lt_status lightning_prefill(const void* q, const void* k, const void* v, const v
                             void* const* main_kernel_events, void* stream);
 
 /*
+ * lightning_prefill without a workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Arguments and
+ * results are those of lightning_prefill without `workspace`, `workspace_bytes` and the timing
+ * events.  The segment-boundary states live in a static device array of LT_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every device it runs on until the process ends; the call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).  A request whose workspace
+ * (lightning_prefill_workspace_size) exceeds the array returns LT_ERR_UNSUPPORTED: use
+ * lightning_prefill with a workspace instead.  Every call on one device shares that device's
+ * array, so calls that overlap on one device (other streams, other threads) race: the caller
+ * must order them.
+ */
+#define LT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+lt_status lightning_prefill_noalloc(const void* q, const void* k, const void* v, const void* gate,
+                                    const float* q_norm_w, const float* k_norm_w,
+                                    const float* o_norm_w, int norm_w_head_stride,
+                                    const double* lambda, double rope_base, double rms_eps,
+                                    int64_t pos0, const float* state_in, float* state_out,
+                                    void* y, float* o_raw, int B, int T, int H, int d, int dtype,
+                                    int chunk, int segments, void* stream);
+
+/*
  * One recurrent decode step: one new token per batch row, every head.
  *   q, k, v, gate : device [B][H][d] of `dtype`.
  *   positions    : device int64 [B], the absolute (0-based) position of each row's token.

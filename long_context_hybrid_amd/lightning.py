@@ -29,6 +29,7 @@ EXPORTS = (
     "lightning_prefill_plan_cus",
     "lightning_prefill_workspace_size",
     "lightning_prefill",
+    "lightning_prefill_noalloc",
     "lightning_decode_step",
     "lightning_prefill_dd_workspace_size",
     "lightning_prefill_dd",
@@ -83,6 +84,9 @@ def _load() -> ct.CDLL:
     h.lightning_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, f64, f64, i64, vp, vp,
                                     vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp, vp]
     h.lightning_prefill.restype = i32
+    h.lightning_prefill_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, f64, f64, i64,
+                                            vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+    h.lightning_prefill_noalloc.restype = i32
     h.lightning_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, f64, f64, vp, vp,
                                         vp, vp, vp, i32, i32, i32, i32, vp]
     h.lightning_decode_step.restype = i32
@@ -266,6 +270,31 @@ def lightning_prefill(q, k, v, gate, q_norm_w, k_norm_w, lambdas, rope_base, rms
                                B, T, H, d, dt, int(chunk), int(segments), wsp, wbytes, evp,
                                _stream(stream, dev))
     _check(st, "lightning_prefill")
+    return y
+
+
+def lightning_prefill_noalloc(q, k, v, gate, q_norm_w, k_norm_w, lambdas, rope_base,
+                              rms_eps=1e-6, pos0=0, state_in=None, state_out=None, y=None,
+                              o_raw=None, o_norm_w=None, chunk=0, segments=0, stream=None):
+    """lightning_prefill through the entry point that allocates nothing (its segment states live
+    in the library's static device scratch).  ``y`` must be given or is allocated here, before
+    the call."""
+    B, T, H, d = q.shape
+    dev = q.device
+    dt = _dtype_code(q.dtype)
+    act = dict(dtype=q.dtype, shape=q.shape, device=dev)
+    ptrs = [_dev(t, n, **act) for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"))]
+    (qwp, kwp, owp), stride = _norm_weights(q_norm_w, k_norm_w, o_norm_w, H, d, dev)
+    if y is None:
+        y = torch.empty_like(q)
+    sshape = (B, H, d, d)
+    st = lib.lightning_prefill_noalloc(
+        *ptrs, qwp, kwp, owp, stride, _lambda_array(lambdas, H), float(rope_base),
+        float(rms_eps), int(pos0), _dev(state_in, "state_in", torch.float32, sshape, dev),
+        _dev(state_out, "state_out", torch.float32, sshape, dev), _dev(y, "y", **act),
+        _dev(o_raw, "o_raw", torch.float32, q.shape, dev), B, T, H, d, dt, int(chunk),
+        int(segments), _stream(stream, dev))
+    _check(st, "lightning_prefill_noalloc")
     return y
 
 
