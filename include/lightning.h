@@ -27,9 +27,10 @@
  *     borrowed for the duration of the work enqueued on `stream` and never freed or retained.
  *     `lambda` (and `out` of lightning_hypenet_gamma) are HOST pointers read before the call
  *     returns.  The library's own code allocates no device memory: prefill and the layer calls
- *     take a caller-owned workspace.  The layer calls run their two GEMMs through hipBLASLt; one
- *     hipBLASLt handle per device is created on the first layer call and kept (with whatever
- *     memory hipBLASLt gives it) until the process ends.
+ *     take a caller-owned workspace.  The layer calls run their projections with the library's
+ *     own MFMA kernels for up to 128 rows (decode steps, short prefills) and through hipBLASLt
+ *     beyond; one hipBLASLt handle per device is created on the first such call and kept (with
+ *     whatever memory hipBLASLt gives it) until the process ends.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only enqueues work and
  *     never synchronises the device.  The work decomposition of the prefill calls depends on the
  *     number of compute units of the current device, which is queried once per device and

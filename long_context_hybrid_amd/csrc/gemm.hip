@@ -1,4 +1,5 @@
-// Dense projections of the RNN layer through hipBLASLt.
+// Dense projections of the RNN layer: the skinny MFMA kernel of gemv.hip for few rows (decode
+// steps), hipBLASLt for the prefill's long products.
 //
 // The layer around the mixer ("Hybrid Linear Attention Done Right", Appendix A, Eq. 18) has two
 // plain GEMMs: x [W_q | W_k | W_v | W_z] in front of the mixer and the output projection W_o^T
@@ -92,6 +93,13 @@ size_t gemm_workspace_limit() { return size_t(32) << 20; }
 lt_status gemm_xwt(const void* A, const void* W, void* D, int64_t M, int64_t N, int64_t K,
                    int dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
     if (launch_gate() != hipSuccess) return LT_ERR_HIP;
+    if (M <= kSkinnyMaxRows) {
+        if (N > 0x7fffffffLL || K > 0x7fffffffLL) return LT_ERR_UNSUPPORTED;
+        return launch_skinny_gemm(A, W, D, (int)M, (int)N, (int)K, (int)K, (int)K, (int)N, dtype,
+                                  stream) == hipSuccess
+                   ? LT_OK
+                   : LT_ERR_HIP;
+    }
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return LT_ERR_HIP;
     hipblasLtHandle_t h;

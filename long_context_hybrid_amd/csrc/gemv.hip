@@ -1,0 +1,219 @@
+// Skinny GEMM of the layer's decode step on gfx950 MFMA: D[M][N] = A[M][K] W[N][K]^T with few
+// rows (one per sequence of a decode batch), fp32 accumulation, D rounded once to the storage
+// type.  For the RNN layer ("Hybrid Linear Attention Done Right", Appendix A, Eq. 18) these are
+// the projections x [W_q | W_k | W_v | W_z] of the new tokens and the output projection y W_o^T.
+//
+// With M <= 64 the product is bound by streaming W from HBM once (32 MiB and 8 MiB for the
+// Qwen3-1.7B-shaped layer), so the kernel is laid out for that stream:
+//   * a workgroup owns 32 output columns (one 32 x 32 MFMA tile in n), all M rows (one or two
+//     32-row tiles) and all of K.  (Splitting K over workgroups measured slower: summing the
+//     partial tiles inside the kernel needs a device-scope release, which writes back the whole
+//     L2, and a second summing kernel costs more than the split saves at these sizes.);
+//   * K is streamed in stages of 512 bytes per row.  The workgroup's 256 threads load a stage's
+//     W rows and A rows as contiguous 512-byte runs (two rows per wavefront instruction), three
+//     or four stages ahead in registers, and write them to a double-buffered LDS tile whose 16-byte
+//     chunks are XOR-swizzled by row, so both the row-run writes and the column reads of the MFMA
+//     operands are free of bank conflicts;
+//   * within a stage the four wavefronts split the k steps; lane (n, half) takes four
+//     consecutive chunks per step group, and both operands use that same k order, which leaves
+//     the sum unchanged;
+//   * the wavefronts' partial tiles are summed through LDS and each output rounded once.
+// fp32 storage uses v_mfma_f32_32x32x2_f32 on the same tiles (128 k per stage).
+#include "lt_device.h"
+#include "lt_internal.h"
+
+namespace lt {
+namespace {
+
+struct SkinnyParams {
+    const void* A;
+    const void* W;
+    void* D;
+    int M, N, K;
+    int lda, ldw, ldd;  // elements between consecutive rows
+};
+
+constexpr int kThreads = 256;              // four wavefronts
+constexpr int kStageBytes = 512;           // bytes of one row per stage
+constexpr int kChunks = kStageBytes / 16;  // 16-byte chunks per row per stage
+
+template <class T>
+struct SkinnyOps;
+template <>
+struct SkinnyOps<uint16_t> {  // bf16
+    static constexpr int PE = 8;  // elements per chunk
+    static __device__ __forceinline__ f32x16 mac(uint4 a, uint4 w, f32x16 c) {
+        return mfma_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, w), c);
+    }
+    static __device__ __forceinline__ void store(void* D, size_t i, float x) {
+        static_cast<uint16_t*>(D)[i] = to_bf16_bits(x);
+    }
+};
+template <>
+struct SkinnyOps<float> {
+    static constexpr int PE = 4;
+    static __device__ __forceinline__ f32x16 mac(uint4 a, uint4 w, f32x16 c) {
+        c = mfma_f32(__uint_as_float(a.x), __uint_as_float(w.x), c);
+        c = mfma_f32(__uint_as_float(a.y), __uint_as_float(w.y), c);
+        c = mfma_f32(__uint_as_float(a.z), __uint_as_float(w.z), c);
+        return mfma_f32(__uint_as_float(a.w), __uint_as_float(w.w), c);
+    }
+    static __device__ __forceinline__ void store(void* D, size_t i, float x) {
+        static_cast<float*>(D)[i] = x;
+    }
+};
+
+// LDS position (16-byte units) of chunk c of tile row r
+__device__ __forceinline__ int swz(int r, int c) { return r * kChunks + (c ^ (r & (kChunks - 1))); }
+
+// MT: 32-row tiles of A (1 or 2); NS: k stages in flight in registers (the registers of four
+// stages of two A tiles would exceed the 256 a wavefront can address).
+// Grid: (ceil(N / 32), ceil(M / (32 MT))).
+template <class T, int MT, int NS>
+__global__ void __launch_bounds__(kThreads) skinny_gemm_kernel(const SkinnyParams p) {
+    using Ops = SkinnyOps<T>;
+    constexpr int PE = Ops::PE;
+    constexpr int KS = kChunks * PE;                // k per stage
+    constexpr int ROWS = 32 + 32 * MT;              // W rows, then A rows
+    constexpr int LPT = ROWS * kChunks / kThreads;  // 16-byte loads per thread per stage
+    static_assert(ROWS * kChunks % kThreads == 0, "whole loads per thread");
+    __shared__ uint4 tile[2][ROWS * kChunks];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, lm = lane & 31, lh = lane >> 5;
+    const int n0 = blockIdx.x * 32, m0 = blockIdx.y * 32 * MT;
+    // stages of K, padded to whole rounds of NS: the padding stages lie past K, so their loads
+    // read a valid chunk and are masked to zero like any chunk past K
+    const int nk = (p.K + KS - 1) / KS;
+    const int ns = (nk + NS - 1) / NS * NS;
+    const int k_end = p.K;
+    auto stage_k = [&](int s) { return s * KS; };  // first k of step s
+
+    // Loads: thread t, load i covers chunk c = 256 i + t of the stage: tile row c / 32, chunk
+    // c % 32 (one wavefront instruction reads two rows' 512 contiguous bytes).  Rows past N or M
+    // read a valid (clamped) row and are never stored.  Chunks at or past K (a multiple of PE,
+    // so a chunk is wholly in or out) read the row's last chunk and are masked to zero when
+    // written to LDS; the loads themselves are unconditional, so the loop below has no branch
+    // around them.
+    const int col = tid % kChunks;
+    const T* src[LPT];
+    int dst[LPT];
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+        const int r = (i * kThreads + tid) / kChunks;
+        dst[i] = swz(r, col);
+        src[i] = r < 32 ? static_cast<const T*>(p.W) + (size_t)min(n0 + r, p.N - 1) * p.ldw
+                        : static_cast<const T*>(p.A) + (size_t)min(m0 + r - 32, p.M - 1) * p.lda;
+    }
+    auto load = [&](int s, uint4* v) {
+        const int kc = min(stage_k(s) + col * PE, k_end - PE);
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) v[i] = *reinterpret_cast<const uint4*>(src[i] + kc);
+    };
+    // (the mask is applied here, where the data is needed anyway, so the loads stay in flight)
+    auto store_tile = [&](int s, const uint4* v) {
+        uint4* t = tile[s & 1];
+        const int k0 = stage_k(s);
+        if (k0 + KS <= k_end) {  // the stage lies within the range (workgroup-uniform)
+#pragma unroll
+            for (int i = 0; i < LPT; ++i) t[dst[i]] = v[i];
+        } else {
+            const uint32_t mk = k0 + col * PE < k_end ? 0xffffffffu : 0u;
+#pragma unroll
+            for (int i = 0; i < LPT; ++i)
+                t[dst[i]] = make_uint4(v[i].x & mk, v[i].y & mk, v[i].z & mk, v[i].w & mk);
+        }
+    };
+
+    f32x16 acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = f32x16{};
+    // wavefront w takes chunks 8 w .. 8 w + 7 of every row of a stage; lane half h its four
+    // chunks 8 w + 4 h + j, j = 0..3 (the MFMA's k slot of half h in step j)
+    auto compute = [&](int buf) {
+        const uint4* tb = tile[buf];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = 8 * wave + 4 * lh + j;
+            const uint4 w = tb[swz(lm, c)];
+#pragma unroll
+            for (int t = 0; t < MT; ++t) acc[t] = Ops::mac(tb[swz(32 + 32 * t + lm, c)], w, acc[t]);
+        }
+    };
+
+    // Pipeline: stage s is loaded NS stages ahead into register set s % NS, written to LDS
+    // buffer s % 2 at the start of step s and consumed after the step's barrier.  The buffer
+    // written in step s was last read in step s - 2, which every wavefront finished before step
+    // s - 1's barrier.  Every round but the last loads the next round's stages.
+    uint4 rg[NS][LPT];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) load(i, rg[i]);
+    int s0 = 0;
+    for (; s0 + NS < ns; s0 += NS) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const int s = s0 + i;
+            store_tile(s, rg[i]);
+            load(s + NS, rg[i]);
+            __syncthreads();
+            compute(s & 1);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        const int s = s0 + i;
+        store_tile(s, rg[i]);
+        __syncthreads();
+        compute(s & 1);
+    }
+    __syncthreads();  // every wavefront is done with the tiles before they hold the partial sums
+
+    // sum the four wavefronts' partial tiles, element e = (t, r, lane)
+    float* red = reinterpret_cast<float*>(&tile[0][0]);
+    static_assert(4 * MT * 16 * 64 * 4 <= (int)sizeof(tile), "partial tiles fit the LDS tiles");
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[((wave * MT + t) * 16 + r) * 64 + lane] = acc[t][r];
+    __syncthreads();
+    constexpr int NE = MT * 16 * 64;
+#pragma unroll
+    for (int q = 0; q < NE / kThreads; ++q) {
+        const int e = q * kThreads + tid, t = e / 1024, r = (e / 64) % 16, l = e % 64;
+        float sum = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) sum += red[((w2 * MT + t) * 16 + r) * 64 + l];
+        const int m = m0 + 32 * t + acc_row(r, l >> 5), n = n0 + (l & 31);
+        if (m < p.M && n < p.N) Ops::store(p.D, (size_t)m * p.ldd + n, sum);
+    }
+}
+
+template <class T, int MT, int NS>
+void launch_ns(const SkinnyParams& sp, hipStream_t stream) {
+    skinny_gemm_kernel<T, MT, NS><<<dim3((sp.N + 31) / 32, (sp.M + 32 * MT - 1) / (32 * MT)),
+                                    dim3(kThreads), 0, stream>>>(sp);
+}
+
+template <class T>
+void launch_typed(const SkinnyParams& sp, hipStream_t stream) {
+    if (sp.M <= 32)
+        launch_ns<T, 1, 4>(sp, stream);
+    else
+        launch_ns<T, 2, 3>(sp, stream);
+}
+
+}  // namespace
+
+hipError_t launch_skinny_gemm(const void* A, const void* W, void* D, int M, int N, int K,
+                              int lda, int ldw, int ldd, int dtype, hipStream_t stream) {
+    if (const hipError_t g = launch_gate(); g != hipSuccess) return g;
+    SkinnyParams sp{A, W, D, M, N, K, lda, ldw, ldd};
+    if (dtype == LT_BF16)
+        launch_typed<uint16_t>(sp, stream);
+    else
+        launch_typed<float>(sp, stream);
+    return hipGetLastError();
+}
+
+}  // namespace lt

@@ -217,7 +217,15 @@ lt_status decode_strided(const void* q, const void* k, const void* v, const void
                          int H, int d, int dtype, void* stream, bool validate_only,
                          const float* log2_decay = nullptr);
 
-// D[M][N] = A[M][K] W[N][K]^T, row-major, fp32 accumulation, A, W and D in `dtype`.
+// Skinny GEMM for few rows (decode steps): D[M][N] = A[M][K] W[N][K]^T with row strides lda,
+// ldw, ldd (elements), fp32 accumulation, D rounded once to `dtype`.  K a multiple of 8, every
+// row 16-byte aligned.  One launch on `stream`.
+constexpr int64_t kSkinnyMaxRows = 128;
+hipError_t launch_skinny_gemm(const void* A, const void* W, void* D, int M, int N, int K,
+                              int lda, int ldw, int ldd, int dtype, hipStream_t stream);
+
+// D[M][N] = A[M][K] W[N][K]^T, row-major, fp32 accumulation, A, W and D in `dtype`: the skinny
+// kernel for M <= kSkinnyMaxRows, else hipBLASLt.
 // ws: at least gemm_workspace_limit() bytes of device memory, 256-byte aligned.
 size_t gemm_workspace_limit();
 lt_status gemm_xwt(const void* A, const void* W, void* D, int64_t M, int64_t N, int64_t K,

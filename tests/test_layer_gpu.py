@@ -187,15 +187,19 @@ def gpu_layer_decode(inp):
     return dict(out=out.float().cpu(), state=s.cpu(), proj=proj.float().cpu(), y=y.float().cpu())
 
 
-@pytest.mark.parametrize("spec_name,values", [("full", "gauss"), ("small_ternary", "ternary"),
+@pytest.mark.parametrize("spec_name,values", [("full", "gauss"), ("full_one_row", "gauss"),
+                                              ("small_ternary", "ternary"),
                                               ("one_row_ternary", "ternary"),
                                               ("rows_40_ternary", "ternary"),
                                               ("small_fp32", "gauss")])
 def test_layer_decode(spec_name, values):
-    """1, 5, 40 and 64 batch rows (bf16) and 3 (fp32); the ternary inputs' projections are
+    """1, 5, 40 and 64 batch rows (bf16; 64 and 1 with the full-size d_model 2048 weights, whose
+    output product splits K over workgroups) and 3 (fp32); the ternary inputs' projections are
     exact integers, so there the projections must match the oracle bit for bit."""
     if spec_name == "full":
         inp = synth.make_layer(synth.LAYER_DECODE_B64)
+    elif spec_name == "full_one_row":  # the full-size weights with one sequence (batch 1)
+        inp = synth.make_layer(synth.LAYER_DECODE_B64, B=1)
     elif spec_name == "small_ternary":
         inp = synth.make_custom_layer(5, 1, 2, 128, 256, seed=8, state="randn", values=values)
     elif spec_name == "one_row_ternary":
