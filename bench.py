@@ -85,7 +85,7 @@ def copy_calibration(torch, mib):
 
 
 MIXER_SOURCES = ("abi.hip", "decode.hip", "lt_device.h", "lt_internal.h", "prefill.hip")
-LAYER_SOURCES = ("gemm.hip", "layer.hip")
+LAYER_SOURCES = ("gemm.hip", "gemm_tile.hip", "gemv.hip", "layer.hip")
 LAYER_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic_layer_qwen17_512k.md")
 BWD_SOURCES = ("backward.hip", "lt_device.h", "lt_internal.h")
 BWD_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic_backward_qwen17_16k.md")
@@ -356,7 +356,7 @@ def bench_layer(args, torch, lt, synth):
                          "unit": "TFLOP/s", "frac": round(t1 / BF16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic("qkvz_gemm", spec.name,
                                                      LAYER_TRAFFIC_RECORD, LAYER_SOURCES),
-                         "kernel": "hipBLASLt bf16 GEMM x [W_q|W_k|W_v|W_z] (M=%d N=%d K=%d)"
+                         "kernel": "gemm_tile_kernel: x [W_q|W_k|W_v|W_z] (M=%d N=%d K=%d)"
                                    % (rows, 4 * H * d, dm),
                          "flops_per_launch": f1, "launch_ms": round(stage[0], 4),
                          "alg_bytes_per_launch": rows * dm * 2 + 4 * H * d * dm * 2

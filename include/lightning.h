@@ -26,18 +26,15 @@
  *   - Device pointers are plain device addresses (hipMalloc or a PyTorch CUDA tensor); they are
  *     borrowed for the duration of the work enqueued on `stream` and never freed or retained.
  *     `lambda` (and `out` of lightning_hypenet_gamma) are HOST pointers read before the call
- *     returns.  The library's own code allocates no device memory: prefill and the layer calls
- *     take a caller-owned workspace.  The layer calls run their projections with the library's
- *     own MFMA kernels for up to 128 rows (decode steps, short prefills) and through hipBLASLt
- *     beyond; one hipBLASLt handle per device is created on the first such call and kept (with
- *     whatever memory hipBLASLt gives it) until the process ends.
+ *     returns.  The library allocates no device memory: prefill and the layer calls take a
+ *     caller-owned workspace, and every kernel, the layer's projection GEMMs included, is the
+ *     library's own.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only enqueues work and
  *     never synchronises the device.  The work decomposition of the prefill calls depends on the
  *     number of compute units of the current device, which is queried once per device and
- *     cached; besides that cache the mixer calls keep no state between calls, and the layer
- *     calls cache, per device and GEMM shape, the hipBLASLt descriptors and algorithm (guarded
- *     by a lock).  All calls are re-entrant; calls that share a workspace or output buffers must
- *     be ordered by the caller.
+ *     cached; besides that cache the calls keep no state between calls (lightning_prefill_noalloc
+ *     aside, see there).  All calls are re-entrant; calls that share a workspace or output
+ *     buffers must be ordered by the caller.
  *   - LT_ERR_HIP: the HIP runtime failed (no device visible, a launch rejected).  For tests of
  *     this path, setting the environment variable LT_FORCE_FAIL to a value other than "" or
  *     "0" makes every call that would launch work return LT_ERR_HIP instead, after its argument
@@ -284,13 +281,11 @@ lt_status lightning_prefill_backward(const void* q, const void* k, const void* v
  * workspace : device memory of at least the size query's bytes, 256-byte aligned, holding
  *   at offset 0                     the projections [B][T][4 H d] (column blocks q | k | v | g),
  *   at round_up(B T 4 H d es, 256)  the mixer output y [B][T][H][d],
- * (es = 2 for bf16, 4 for fp32), then the mixer's and the GEMMs' scratch.  After the call's work
- * has run, the first two parts hold the layer's intermediate tensors (a test hook).
+ * (es = 2 for bf16, 4 for fp32), then (prefill) the mixer's workspace.  After the call's work has
+ * run, the first two parts hold the layer's intermediate tensors (a test hook).
  * stage_events : NULL, or four hipEvent_t handles recorded on `stream` before the QKVZ GEMM,
  *   after it, after the mixer and after the output GEMM.
- * Errors: as for the mixer calls; LT_ERR_UNSUPPORTED also when hipBLASLt has no algorithm for a
- * GEMM shape, LT_ERR_HIP when hipBLASLt fails to enqueue.  d_model not a multiple of 8 is
- * LT_ERR_INVALID_ARG.
+ * Errors: as for the mixer calls.  d_model not a multiple of 8 is LT_ERR_INVALID_ARG.
  */
 size_t lightning_layer_prefill_workspace_size(int B, int T, int H, int d, int d_model, int dtype,
                                               int chunk, int segments);

@@ -1,5 +1,4 @@
-"""Build step of the gfx950 library: compiles csrc/*.hip into liblightning.so in this directory
-(linked against hipBLASLt, which runs the layer's prefill projection GEMMs).
+"""Build step of the gfx950 library: compiles csrc/*.hip into liblightning.so in this directory.
 
 Run ``python -m long_context_hybrid_amd.build`` (or call ``build()``).  Each source is compiled
 to an object in its own hipcc process (in parallel), then the objects are linked.  The library is
@@ -19,7 +18,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMPILE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
                  "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-LINK_FLAGS = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
+LINK_FLAGS = ["-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib"]
 
 
 def sources():

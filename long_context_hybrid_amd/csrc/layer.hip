@@ -22,10 +22,10 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
 
-// Workspace of one layer call: [projections | y | mixer workspace | GEMM workspace], each part
-// starting on a 256-byte boundary.
+// Workspace of one layer call: [projections | y | mixer workspace], each part starting on a
+// 256-byte boundary.
 struct LayerWs {
-    size_t proj, y, mixer, gemm, total;
+    size_t proj, y, mixer, total;
 };
 
 bool layer_ws(int64_t rows, int H, int d, int dtype, size_t mixer_bytes, LayerWs* w) {
@@ -35,8 +35,7 @@ bool layer_ws(int64_t rows, int H, int d, int dtype, size_t mixer_bytes, LayerWs
     w->proj = 0;
     w->y = round_up((size_t)rows * 4 * H * d * es);
     w->mixer = w->y + round_up((size_t)rows * H * d * es);
-    w->gemm = w->mixer + round_up(mixer_bytes);
-    w->total = w->gemm + lt::gemm_workspace_limit();
+    w->total = w->mixer + round_up(mixer_bytes);
     return true;
 }
 
@@ -108,19 +107,17 @@ lt_status lightning_layer_prefill(const void* x, const void* w_qkvz, const void*
 
     const int64_t rows = (int64_t)B * T;
     if (!mark(0)) return LT_ERR_HIP;
-    st = lt::gemm_xwt(x, w_qkvz, proj, rows, 4 * (int64_t)hd, d_model, dtype, ws + w.gemm,
-                      lt::gemm_workspace_limit(), s);
+    st = lt::gemm_xwt(x, w_qkvz, proj, rows, 4 * (int64_t)hd, d_model, dtype, s);
     if (st != LT_OK) return st;
     if (!mark(1)) return LT_ERR_HIP;
     st = lt::prefill_strided(proj, proj + (size_t)hd * es, proj + (size_t)2 * hd * es,
                              proj + (size_t)3 * hd * es, 4 * hd, q_norm_w, k_norm_w, o_norm_w,
                              norm_w_head_stride, lambda, rope_base, rms_eps, pos0, state_in,
                              state_out, ws + w.y, nullptr, B, T, H, d, dtype, chunk, segments,
-                             ws + w.mixer, w.gemm - w.mixer, nullptr, stream, false);
+                             ws + w.mixer, w.total - w.mixer, nullptr, stream, false);
     if (st != LT_OK) return st;
     if (!mark(2)) return LT_ERR_HIP;
-    st = lt::gemm_xwt(ws + w.y, w_o, out, rows, d_model, hd, dtype, ws + w.gemm,
-                      lt::gemm_workspace_limit(), s);
+    st = lt::gemm_xwt(ws + w.y, w_o, out, rows, d_model, hd, dtype, s);
     if (st != LT_OK) return st;
     if (!mark(3)) return LT_ERR_HIP;
     return LT_OK;
@@ -162,13 +159,11 @@ lt_status lightning_layer_decode_step(const void* x, const void* w_qkvz, const v
     };
     lt_status st = mixer(true);
     if (st != LT_OK) return st;
-    st = lt::gemm_xwt(x, w_qkvz, proj, B, 4 * (int64_t)hd, d_model, dtype, ws + w.gemm,
-                      lt::gemm_workspace_limit(), s);
+    st = lt::gemm_xwt(x, w_qkvz, proj, B, 4 * (int64_t)hd, d_model, dtype, s);
     if (st != LT_OK) return st;
     st = mixer(false);
     if (st != LT_OK) return st;
-    return lt::gemm_xwt(ws + w.y, w_o, out, B, d_model, hd, dtype, ws + w.gemm,
-                        lt::gemm_workspace_limit(), s);
+    return lt::gemm_xwt(ws + w.y, w_o, out, B, d_model, hd, dtype, s);
 }
 
 }  // extern "C"

@@ -224,11 +224,14 @@ constexpr int64_t kSkinnyMaxRows = 128;
 hipError_t launch_skinny_gemm(const void* A, const void* W, void* D, int M, int N, int K,
                               int lda, int ldw, int ldd, int dtype, hipStream_t stream);
 
-// D[M][N] = A[M][K] W[N][K]^T, row-major, fp32 accumulation, A, W and D in `dtype`: the skinny
-// kernel for M <= kSkinnyMaxRows, else hipBLASLt.
-// ws: at least gemm_workspace_limit() bytes of device memory, 256-byte aligned.
-size_t gemm_workspace_limit();
+// Large bf16 GEMM (prefill projections): D[M][N] = A[M][K] W[N][K]^T, K a multiple of 128,
+// rows 16-byte aligned, M and N any.  One launch on `stream`.
+hipError_t launch_tile_gemm(const void* A, const void* W, void* D, int64_t M, int N, int K,
+                            hipStream_t stream);
+
+// D[M][N] = A[M][K] W[N][K]^T, row-major, fp32 accumulation, A, W and D in `dtype`, on the
+// library's own kernels (the tile kernel for long bf16 products, the skinny kernel otherwise).
 lt_status gemm_xwt(const void* A, const void* W, void* D, int64_t M, int64_t N, int64_t K,
-                   int dtype, void* ws, size_t ws_bytes, hipStream_t stream);
+                   int dtype, hipStream_t stream);
 
 }  // namespace lt

@@ -147,7 +147,7 @@ def test_prefill_workspace_missing_on_gpu(bufs):
 
 def test_size_queries_on_the_device(bufs):
     """The device-dependent size queries agree with the explicit-CU planner for this device's
-    compute-unit count, and the layer's workspace is projections | y | mixer slots | GEMM scratch."""
+    compute-unit count, and the layer's workspace is projections | y | mixer slots."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     B, T, H, d, dm = 1, 524288, 16, 128, 2048
     pl = lt.lightning_prefill_plan_cus(cus, B, T, H, d)
@@ -159,7 +159,7 @@ def test_size_queries_on_the_device(bufs):
     bp = lt.lightning_prefill_plan_cus(cus, 8, 16384, 16, d)
     assert lt.lightning_prefill_backward_workspace_size(8, 16384, 16, d) == \
         bp["backward_workspace_bytes"]
-    expect = T * 4 * H * d * 2 + T * H * d * 2 + (mix + 255) // 256 * 256 + (32 << 20)
+    expect = T * 4 * H * d * 2 + T * H * d * 2 + (mix + 255) // 256 * 256
     assert lt.lightning_layer_prefill_workspace_size(B, T, H, d, dm) == expect
 
 
