@@ -19,6 +19,11 @@
 //     the sum unchanged;
 //   * the wavefronts' partial tiles are summed through LDS and each output rounded once.
 // fp32 storage uses v_mfma_f32_32x32x2_f32 on the same tiles (128 k per stage).
+//
+// With at most four rows of A (a decode step of one to four sequences) a 32-row MFMA tile would
+// be almost empty, so gemv_small_kernel does the product with VALU FMAs instead: a wavefront owns
+// two rows of W and streams them along K, 16 bytes per lane per step, with the few rows of A
+// read alongside (they stay in the caches); the partial sums are reduced across the wavefront.
 #include "lt_device.h"
 #include "lt_internal.h"
 
@@ -189,15 +194,98 @@ __global__ void __launch_bounds__(kThreads) skinny_gemm_kernel(const SkinnyParam
     }
 }
 
+
+// D[m][n] for m < MM (MM <= 4): wavefront w of workgroup b owns W rows n = 2 (4 b + w) + {0, 1}.
+// Lane l takes the 16-byte chunks c = l + 64 i of K.  Chunks at or past K re-read the last chunk
+// and are masked to zero (unconditional loads, no branch in the loop).  Grid: ceil(N / 8).
+template <class T, int MM>
+__global__ void __launch_bounds__(kThreads) gemv_small_kernel(const SkinnyParams p) {
+    using Ops = SkinnyOps<T>;
+    constexpr int PE = Ops::PE;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n0 = (blockIdx.x * 4 + wave) * 2;
+    if (n0 >= p.N) return;
+    const int n1 = min(n0 + 1, p.N - 1);
+    const T* w0 = static_cast<const T*>(p.W) + (size_t)n0 * p.ldw;
+    const T* w1 = static_cast<const T*>(p.W) + (size_t)n1 * p.ldw;
+    const T* a = static_cast<const T*>(p.A);
+    const int nch = p.K / PE;
+    float acc[MM][2];
+#pragma unroll
+    for (int m = 0; m < MM; ++m) acc[m][0] = acc[m][1] = 0.0f;
+#pragma unroll 4
+    for (int c0 = 0; c0 < nch; c0 += 64) {
+        const int c = c0 + lane;
+        const size_t e = (size_t)min(c, nch - 1) * PE;
+        const uint32_t mk = c < nch ? 0xffffffffu : 0u;
+        uint4 x0 = *reinterpret_cast<const uint4*>(w0 + e);
+        uint4 x1 = *reinterpret_cast<const uint4*>(w1 + e);
+        x0 = make_uint4(x0.x & mk, x0.y & mk, x0.z & mk, x0.w & mk);
+        x1 = make_uint4(x1.x & mk, x1.y & mk, x1.z & mk, x1.w & mk);
+#pragma unroll
+        for (int m = 0; m < MM; ++m) {
+            uint4 y = *reinterpret_cast<const uint4*>(a + (size_t)m * p.lda + e);
+            y = make_uint4(y.x & mk, y.y & mk, y.z & mk, y.w & mk);
+            const uint32_t wa[4] = {x0.x, x0.y, x0.z, x0.w}, wb[4] = {x1.x, x1.y, x1.z, x1.w};
+            const uint32_t ya[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if constexpr (PE == 8) {
+                    const float al = bf16_lo(ya[q]), ah = bf16_hi(ya[q]);
+                    acc[m][0] = fmaf(al, bf16_lo(wa[q]), acc[m][0]);
+                    acc[m][0] = fmaf(ah, bf16_hi(wa[q]), acc[m][0]);
+                    acc[m][1] = fmaf(al, bf16_lo(wb[q]), acc[m][1]);
+                    acc[m][1] = fmaf(ah, bf16_hi(wb[q]), acc[m][1]);
+                } else {
+                    const float av = __uint_as_float(ya[q]);
+                    acc[m][0] = fmaf(av, __uint_as_float(wa[q]), acc[m][0]);
+                    acc[m][1] = fmaf(av, __uint_as_float(wb[q]), acc[m][1]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MM; ++m)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            float x = group_sum<16>(acc[m][j]);
+            x += __shfl_xor(x, 16);
+            x += __shfl_xor(x, 32);
+            acc[m][j] = x;
+        }
+    if (lane == 0) {
+#pragma unroll
+        for (int m = 0; m < MM; ++m) {
+            Ops::store(p.D, (size_t)m * p.ldd + n0, acc[m][0]);
+            if (n0 + 1 < p.N) Ops::store(p.D, (size_t)m * p.ldd + n0 + 1, acc[m][1]);
+        }
+    }
+}
+
 template <class T, int MT, int NS>
 void launch_ns(const SkinnyParams& sp, hipStream_t stream) {
     skinny_gemm_kernel<T, MT, NS><<<dim3((sp.N + 31) / 32, (sp.M + 32 * MT - 1) / (32 * MT)),
                                     dim3(kThreads), 0, stream>>>(sp);
 }
 
+template <class T, int MM>
+void launch_small(const SkinnyParams& sp, hipStream_t stream) {
+    gemv_small_kernel<T, MM><<<dim3((sp.N + 7) / 8), dim3(kThreads), 0, stream>>>(sp);
+}
+
+// One or two 32-row tiles per workgroup: two read each W column block once for 64 rows, but
+// leave most compute units idle when N has fewer 32-column blocks than there are of them.
 template <class T>
-void launch_typed(const SkinnyParams& sp, hipStream_t stream) {
-    if (sp.M <= 32)
+void launch_typed(const SkinnyParams& sp, int cus, hipStream_t stream) {
+    switch (sp.M) {
+    case 1: return launch_small<T, 1>(sp, stream);
+    case 2: return launch_small<T, 2>(sp, stream);
+    case 3: return launch_small<T, 3>(sp, stream);
+    case 4: return launch_small<T, 4>(sp, stream);
+    default: break;
+    }
+    if (sp.M <= 32 || (sp.N + 31) / 32 < cus)
         launch_ns<T, 1, 4>(sp, stream);
     else
         launch_ns<T, 2, 3>(sp, stream);
@@ -209,10 +297,12 @@ hipError_t launch_skinny_gemm(const void* A, const void* W, void* D, int M, int 
                               int lda, int ldw, int ldd, int dtype, hipStream_t stream) {
     if (const hipError_t g = launch_gate(); g != hipSuccess) return g;
     SkinnyParams sp{A, W, D, M, N, K, lda, ldw, ldd};
+    const int cus = device_cu_count();
+    if (cus <= 0) return hipErrorInvalidDevice;
     if (dtype == LT_BF16)
-        launch_typed<uint16_t>(sp, stream);
+        launch_typed<uint16_t>(sp, cus, stream);
     else
-        launch_typed<float>(sp, stream);
+        launch_typed<float>(sp, cus, stream);
     return hipGetLastError();
 }
 

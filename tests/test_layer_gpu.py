@@ -190,12 +190,14 @@ def gpu_layer_decode(inp):
 @pytest.mark.parametrize("spec_name,values", [("full", "gauss"), ("full_one_row", "gauss"),
                                               ("small_ternary", "ternary"),
                                               ("one_row_ternary", "ternary"),
+                                              ("rows_4_ternary", "ternary"),
                                               ("rows_40_ternary", "ternary"),
                                               ("small_fp32", "gauss")])
 def test_layer_decode(spec_name, values):
-    """1, 5, 40 and 64 batch rows (bf16; 64 and 1 with the full-size d_model 2048 weights, whose
-    output product splits K over workgroups) and 3 (fp32); the ternary inputs' projections are
-    exact integers, so there the projections must match the oracle bit for bit."""
+    """1, 4, 5, 40 and 64 batch rows (bf16; 64 and 1 with the full-size d_model 2048 weights) and
+    3 (fp32): up to four rows take the VALU product, more the MFMA tiles.  The ternary inputs'
+    projections are exact integers, so there the projections must match the oracle bit for
+    bit."""
     if spec_name == "full":
         inp = synth.make_layer(synth.LAYER_DECODE_B64)
     elif spec_name == "full_one_row":  # the full-size weights with one sequence (batch 1)
@@ -204,6 +206,8 @@ def test_layer_decode(spec_name, values):
         inp = synth.make_custom_layer(5, 1, 2, 128, 256, seed=8, state="randn", values=values)
     elif spec_name == "one_row_ternary":
         inp = synth.make_custom_layer(1, 1, 2, 128, 256, seed=10, state="randn", values=values)
+    elif spec_name == "rows_4_ternary":
+        inp = synth.make_custom_layer(4, 1, 2, 128, 256, seed=12, state="randn", values=values)
     elif spec_name == "rows_40_ternary":
         inp = synth.make_custom_layer(40, 1, 2, 128, 256, seed=11, state="randn", values=values)
     else:
