@@ -11,10 +11,14 @@ Printed (one JSON line): prefill tokens/s/layer (``value``), the main kernel's r
 (algorithmic HBM bytes per launch / its average duration, timed with HIP events recorded by the
 library around that kernel on the launch stream), its MFMA rate, the batched decode step
 (B = 64, H = 16, d = 128) in microseconds with its HBM roofline, and the fp64 CPU oracle timed on
-a bounded sample of the same prefill workload on this host's cores.  Under ``layer``: the whole
-RNN layer around the mixer (QKVZ projection GEMM, mixer, output projection GEMM; d_model = 2048)
-at the same 512K tokens with per-stage times and the QKVZ GEMM's MFMA roofline, its B = 64
-decode step, and the layer oracle timed on a bounded sample.  Under ``attention``: the hybrid's
+a bounded sample of the same prefill workload on this host's cores.  ``decode.batch_1``: the
+same step with one sequence (16 workgroups), timed as a captured HIP graph's replay because a
+step takes less time than its launch.  Under ``other_configs``: the prefill of the 32K-token
+layer and of the Qwen3-8B-shaped one (B = 4, H = 32, T = 128K, nonzero initial state), each with
+its roofline.  Under ``layer``: the whole RNN layer around the mixer (QKVZ projection GEMM,
+mixer, output projection GEMM; d_model = 2048) at the same 512K tokens with per-stage times and
+the QKVZ GEMM's MFMA roofline, its B = 64 and B = 1 decode steps, and the layer oracle timed on
+a bounded sample.  Under ``attention``: the hybrid's
 HyPE softmax-attention layer (NoPE, s_t = log_a(t + a) logits scale, 16 query / 8 key-value
 heads) at 512K tokens with the flash kernel's MFMA roofline, and its oracle on sampled rows.
 Under ``time_dependent_decay``: the same prefill with a per-token decay alpha_t (the
@@ -53,6 +57,8 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=524288)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the 32K and Qwen3-8B-shaped prefill legs")
     ap.add_argument("--no-layer", action="store_true",
                     help="skip the whole-layer legs (projections + mixer + output projection)")
     ap.add_argument("--layer-steps", type=int, default=5)
@@ -155,8 +161,9 @@ class HipEvents:
             self.hip.hipEventDestroy(ct.c_void_p(e))
 
 
-def bench_prefill(args, torch, lt, synth):
-    spec = synth.WORKLOADS[args.workload]
+def bench_prefill(args, torch, lt, synth, workload=None, steps=None):
+    spec = synth.WORKLOADS[workload or args.workload]
+    steps = steps or args.steps
     dev = torch.device("cuda:0")
     inp = synth.make_prefill(spec, device=dev)
     B, T, H, d = inp["B"], inp["T"], inp["H"], inp["d"]
@@ -174,19 +181,19 @@ def bench_prefill(args, torch, lt, synth):
     torch.cuda.synchronize()
 
     hev = HipEvents()
-    ev = hev.create(2 * args.steps)
+    ev = hev.create(2 * steps)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    for i in range(args.steps):
+    for i in range(steps):
         lt.lightning_prefill(*call_args, **kw, main_kernel_events=(ev[2 * i], ev[2 * i + 1]))
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    main_ms = sum(hev.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for i in range(args.steps)) / args.steps
+    main_ms = sum(hev.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for i in range(steps)) / steps
     hev.destroy(ev)
 
-    ms_per_step = total_ms / args.steps
+    ms_per_step = total_ms / steps
     tokens = B * T
     act_bytes = 2 if spec.dtype == torch.bfloat16 else 4
     units = B * H * T  # token-heads per launch
@@ -198,7 +205,7 @@ def bench_prefill(args, torch, lt, synth):
     tflops = useful_flops / (main_ms * 1e-3) / 1e12
     pre_bytes = B * H * (P - 1) * seg_len * 2 * d * act_bytes if P > 1 else 0  # k, v of segments 0 .. P-2
     return dict(
-        spec=spec, inp=inp, chunk=chunk, P=P, ms_per_step=ms_per_step, main_ms=main_ms,
+        spec=spec, inp=inp, chunk=chunk, P=P, ms_per_step=ms_per_step, main_ms=main_ms, steps=steps,
         value=tokens / (ms_per_step * 1e-3),
         roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                   "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -216,36 +223,83 @@ def bench_prefill(args, torch, lt, synth):
     )
 
 
-def bench_decode(args, torch, lt, synth):
+def bench_decode(args, torch, lt, synth, B=None):
+    """The mixer's decode step over rotating state buffers (so the state cannot be served from
+    MALL).  At B = 64 the steps are launched one by one; with fewer rows a step's kernel takes
+    less time than the host needs to launch it, so the steps are captured once into a HIP graph
+    (torch.cuda.graph) and the graph's replay is timed."""
     spec = synth.DECODE_B64
     dev = torch.device("cuda:0")
-    inp = synth.make_decode(spec, device=dev)
+    inp = synth.make_decode(spec, device=dev, B=B)
     B, H, d = inp["B"], inp["H"], inp["d"]
-    states = [inp["state_in"].clone() for _ in range(args.decode_buffers)]
+    # enough buffers that the states of one pass over them exceed the 256 MB MALL
+    nbuf = max(args.decode_buffers, -(-300 * 2**20 // (B * H * d * d * 4)))
+    states = [inp["state_in"].clone() for _ in range(nbuf)]
     y = torch.empty_like(inp["q"])
     a = (inp["q"], inp["k"], inp["v"], inp["g"], inp["qw"], inp["kw"], inp["lambdas"],
          inp["rope_base"], inp["positions"])
-    for i in range(3):
+
+    def step(i):
         lt.lightning_decode_step(*a, states[i % len(states)], y=y, rms_eps=inp["eps"])
+
+    for i in range(3):
+        step(i)
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(args.decode_steps):
-        lt.lightning_decode_step(*a, states[i % len(states)], y=y, rms_eps=inp["eps"])
-    stop.record()
+    graph = B < 64
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            with torch.cuda.graph(g, stream=cs):
+                for i in range(args.decode_steps):
+                    step(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        start.record()
+        g.replay()
+        stop.record()
+    else:
+        start.record()
+        for i in range(args.decode_steps):
+            step(i)
+        stop.record()
     torch.cuda.synchronize()
     us = start.elapsed_time(stop) * 1e3 / args.decode_steps
     act_bytes = 2
     per_bh = 2 * d * d * 4 + 5 * d * act_bytes
     alg = B * H * per_bh + B * 8
     gbs = alg / (us * 1e-6) / 1e9
-    return {"workload": spec.name, "us_per_step": round(us, 3),
+    name = spec.name if B == spec.B else spec.name.replace("B=%d" % spec.B, "B=%d" % B)
+    return {"workload": name, "us_per_step": round(us, 3),
+            "timing": "HIP graph of %d steps" % args.decode_steps if graph else "eager launches",
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "traffic": measured_traffic("decode", spec.name),
+                         "traffic": measured_traffic("decode", name),
                          "kernel": "decode_kernel<ModeBF16,128>", "alg_bytes_per_launch": alg,
-                         "bytes_per_bh": per_bh},
+                         "bytes_per_bh": per_bh, "workgroups": B * H},
             "state_buffers": len(states)}
+
+
+def bench_configs(args, torch, lt, synth):
+    """The other prefill configurations at their own sizes: the 32K-token Qwen3-1.7B-shaped layer
+    and the Qwen3-8B-shaped one (B = 4, H = 32, T = 128K, nonzero initial state)."""
+    out = {}
+    for name, steps in (("qwen17_32k", max(args.steps, 20)), ("qwen8_128k", args.steps)):
+        print(f"[bench] prefill {name}: warmup {args.warmup}, steps {steps}", file=sys.stderr,
+              flush=True)
+        r = bench_prefill(args, torch, lt, synth, workload=name, steps=steps)
+        sp = r["spec"]
+        out[name] = {"workload": sp.name, "B": sp.B, "T": sp.T, "H": sp.H, "d": sp.d,
+                     "chunk": r["chunk"], "segments": r["P"], "steps": steps,
+                     "ms_per_step": round(r["ms_per_step"], 4),
+                     "value": round(r["value"], 1), "unit": "tokens/s/layer",
+                     "roofline": r["roofline"], "mfma": r["mfma"], "whole_call": r["whole_call"]}
+        del r
+        torch.cuda.empty_cache()
+    return out
 
 
 def bench_time_dependent(args, torch, lt, synth, fixed):
@@ -366,12 +420,13 @@ def bench_layer(args, torch, lt, synth):
             "mfma_floor_ms": round((f1 + f2) / (BF16_PEAK_TFLOPS * 1e12) * 1e3, 3)}
 
 
-def bench_layer_decode(args, torch, lt, synth):
-    """One layer decode step at B = 64 over rotating sets of (state, weights), so that neither
-    the 64 MiB state nor the 40 MiB of projection weights can be served from MALL."""
+def bench_layer_decode(args, torch, lt, synth, B=None):
+    """One layer decode step at B = 64 (or B) over rotating sets of (state, weights), so that
+    neither the state nor the 40 MiB of projection weights can be served from MALL.  With fewer
+    than 64 rows the steps are timed as the replay of a captured HIP graph (see bench_decode)."""
     spec = synth.LAYER_DECODE_B64
     dev = torch.device("cuda:0")
-    inp = synth.make_layer(spec, device=dev)
+    inp = synth.make_layer(spec, device=dev, B=B)
     B, H, d, dm = inp["B"], inp["H"], inp["d"], inp["d_model"]
     nset = args.decode_buffers
     sets = [(inp["state_in"].clone(), inp["w_qkvz"].clone(), inp["w_o"].clone())
@@ -390,17 +445,35 @@ def bench_layer_decode(args, torch, lt, synth):
         step(i)
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(args.decode_steps):
-        step(i)
-    stop.record()
+    graph = B < 64
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            with torch.cuda.graph(g, stream=cs):
+                for i in range(args.decode_steps):
+                    step(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        start.record()
+        g.replay()
+        stop.record()
+    else:
+        start.record()
+        for i in range(args.decode_steps):
+            step(i)
+        stop.record()
     torch.cuda.synchronize()
     us = start.elapsed_time(stop) * 1e3 / args.decode_steps
     wbytes = (4 * H * d * dm + dm * H * d) * 2
     io = B * dm * 2 * 2 + B * (4 * H * d + H * d) * 2 * 2  # x, out; projections and y written + read
     alg = wbytes + B * H * 2 * d * d * 4 + io + B * 8
     gbs = alg / (us * 1e-6) / 1e9
-    return {"workload": spec.name, "us_per_step": round(us, 3),
+    name = spec.name if B == spec.B else spec.name.replace("B=%d" % spec.B, "B=%d" % B)
+    return {"workload": name, "us_per_step": round(us, 3),
+            "timing": "HIP graph of %d steps" % args.decode_steps if graph else "eager launches",
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                          "alg_bytes_per_step": alg, "weight_bytes": wbytes},
@@ -700,6 +773,11 @@ def main():
     if not args.no_decode:
         print(f"[bench] decode B=64: steps {args.decode_steps}", file=sys.stderr, flush=True)
         dec = bench_decode(args, torch, lt, synth)
+        print(f"[bench] decode B=1: steps {args.decode_steps}", file=sys.stderr, flush=True)
+        dec["batch_1"] = bench_decode(args, torch, lt, synth, B=1)
+    configs = None
+    if not args.no_configs:
+        configs = bench_configs(args, torch, lt, synth)
     td = None
     if not args.no_time_dep:
         print("[bench] data-dependent decay variant, prefill 512K", file=sys.stderr, flush=True)
@@ -713,6 +791,9 @@ def main():
             print(f"[bench] layer decode B=64: steps {args.decode_steps}", file=sys.stderr,
                   flush=True)
             layer["decode"] = bench_layer_decode(args, torch, lt, synth)
+            print(f"[bench] layer decode B=1: steps {args.decode_steps}", file=sys.stderr,
+                  flush=True)
+            layer["decode"]["batch_1"] = bench_layer_decode(args, torch, lt, synth, B=1)
     attn = None
     if not args.no_attn:
         print(f"[bench] attention prefill 512K: warmup {args.attn_warmup}, steps {args.attn_steps}",
@@ -763,6 +844,7 @@ def main():
         "mfma": pre["mfma"],
         "whole_call": pre["whole_call"],
         "decode": dec,
+        "other_configs": configs,
         "time_dependent_decay": td,
         "layer": layer,
         "attention": attn,
