@@ -51,6 +51,7 @@ def parse():
     ap.add_argument("--workload", default="qwen17_512k",
                     choices=["qwen17_512k", "qwen17_32k", "qwen8_128k"])
     ap.add_argument("--segments", type=int, default=0, help="0 = library default")
+    ap.add_argument("--chunk", type=int, default=0, help="tokens per chunk: 0 (= 32) or 64")
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--decode-buffers", type=int, default=8,
                     help="rotating state buffers (64 MiB each) so the step cannot run from MALL")
@@ -167,15 +168,15 @@ def bench_prefill(args, torch, lt, synth, workload=None, steps=None):
     dev = torch.device("cuda:0")
     inp = synth.make_prefill(spec, device=dev)
     B, T, H, d = inp["B"], inp["T"], inp["H"], inp["d"]
-    chunk, P, seg_len = lt.lightning_prefill_plan(B, T, H, d, spec.dtype, 0, args.segments)
+    chunk, P, seg_len = lt.lightning_prefill_plan(B, T, H, d, spec.dtype, args.chunk, args.segments)
     y = torch.empty_like(inp["q"])
     s_out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
-    ws_bytes = lt.lightning_prefill_workspace_size(B, T, H, d, spec.dtype, 0, args.segments)
+    ws_bytes = lt.lightning_prefill_workspace_size(B, T, H, d, spec.dtype, args.chunk, args.segments)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     call_args = (inp["q"], inp["k"], inp["v"], inp["g"], inp["qw"], inp["kw"], inp["lambdas"],
                  inp["rope_base"])
     kw = dict(rms_eps=inp["eps"], pos0=inp["pos0"], state_in=inp["state_in"], state_out=s_out,
-              y=y, segments=args.segments, workspace=ws)
+              y=y, chunk=args.chunk, segments=args.segments, workspace=ws)
     for _ in range(args.warmup):
         lt.lightning_prefill(*call_args, **kw)
     torch.cuda.synchronize()

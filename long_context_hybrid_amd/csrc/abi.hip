@@ -81,7 +81,9 @@ lt_status check_plan_args(int B, int T, int H, int d, int dtype, int chunk, int 
     if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || segments < 0 || chunk < 0) return LT_ERR_INVALID_ARG;
     if (dtype != LT_F32 && dtype != LT_BF16) return LT_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return LT_ERR_UNSUPPORTED;
-    if (chunk != 0 && chunk != lt::kChunk) return LT_ERR_UNSUPPORTED;
+    // 32 (the default) or 64 tokens per chunk; 64-token fp32 tiles at d = 128 do not fit in LDS
+    if (chunk != 0 && chunk != lt::kChunk && chunk != 64) return LT_ERR_UNSUPPORTED;
+    if (chunk == 64 && dtype == LT_F32 && d == 128) return LT_ERR_UNSUPPORTED;
     return LT_OK;
 }
 
@@ -91,7 +93,7 @@ lt_status plan(int cus, int B, int T, int H, int d, int dtype, int chunk, int se
     const lt_status st = check_plan_args(B, T, H, d, dtype, chunk, segments);
     if (st != LT_OK) return st;
     if (cus <= 0) return LT_ERR_INVALID_ARG;
-    const int C = lt::kChunk;
+    const int C = chunk == 64 ? 64 : lt::kChunk;
     const long long n_chunks = ((long long)T + C - 1) / C;
     const long long bh = (long long)B * H;
     long long P = segments;
@@ -281,6 +283,7 @@ size_t lightning_prefill_workspace_size(int B, int T, int H, int d, int dtype, i
 size_t lightning_prefill_dd_workspace_size(int B, int T, int H, int d, int dtype, int chunk,
                                            int segments) {
     Plan pl;
+    if (chunk == 64) return 0;  // the data-dependent decay runs 32-token chunks only
     if (device_plan(B, T, H, d, dtype, chunk, segments, &pl) != LT_OK) return 0;
     return workspace_bytes_dd(B, H, d, pl.P, pl.sub);
 }
@@ -334,7 +337,7 @@ lt_status lightning_prefill_backward(const void* q, const void* k, const void* v
     cp.state_in = state_in;
     cp.ws = reinterpret_cast<float*>(ws);
     cp.pos0 = pos0;
-    cp.B = B; cp.T = T; cp.H = H; cp.P = P; cp.L = pl.L;
+    cp.B = B; cp.T = T; cp.H = H; cp.P = P; cp.C = pl.C; cp.L = pl.L;
     cp.x_stride = H * d;
     cp.SM = pl.sub; cp.SL = pl.sub_len; cp.SP = (P - 1) * pl.sub + 1;
     cp.w_stride = norm_w_head_stride;
@@ -409,6 +412,7 @@ lt_status prefill_strided(const void* q, const void* k, const void* v, const voi
     if (td && !aligned16(log2_decay)) return LT_ERR_INVALID_ARG;
     if (x_stride < H * d || x_stride % 8 != 0) return LT_ERR_INVALID_ARG;
     if ((double)B * T * x_stride > 9.0e15) return LT_ERR_UNSUPPORTED;
+    if (td && chunk == 64) return LT_ERR_UNSUPPORTED;  // the data-dependent decay: 32-token chunks
     st = check_plan_args(B, T, H, d, dtype, chunk, segments);
     if (st != LT_OK) return st;
     if (main_kernel_events && (!main_kernel_events[0] || !main_kernel_events[1]))
@@ -431,7 +435,7 @@ lt_status prefill_strided(const void* q, const void* k, const void* v, const voi
     cp.y = y; cp.o_raw = o_raw;
     cp.ws = static_cast<float*>(workspace);
     cp.pos0 = pos0;
-    cp.B = B; cp.T = T; cp.H = H; cp.P = P; cp.L = pl.L;
+    cp.B = B; cp.T = T; cp.H = H; cp.P = P; cp.C = pl.C; cp.L = pl.L;
     cp.x_stride = x_stride;
     cp.SM = pl.sub; cp.SL = pl.sub_len; cp.SP = (P - 1) * pl.sub + 1;
     cp.w_stride = norm_w_head_stride;

@@ -43,6 +43,7 @@ struct ChunkParams {
     int B, T, H;
     int x_stride;  // elements between consecutive tokens of q, k, v and g (y is [B][T][H][d])
     int P;      // segments per (b, h) of the main pass
+    int C;      // tokens per chunk of the main pass: 32, or 64 (fixed decay; not fp32 with d = 128)
     int L;      // tokens per segment (multiple of the chunk), the last segment may be shorter
     // The state-only pass splits segments 0 .. P-2 into SM sub-segments: SM - 1 of SL tokens and
     // a last one with the rest of the segment.  The workspace holds SP = (P - 1) SM + 1 states

@@ -40,11 +40,16 @@
 #include "lt_device.h"
 #include "lt_internal.h"
 
+#include <type_traits>
+
 namespace lt {
 namespace {
 
-constexpr int C = kChunk;  // 32 tokens per chunk
-static_assert(C == 32, "the tiling below assumes one 32-row block per chunk");
+constexpr int C = kChunk;  // 32 tokens per chunk (the state-only pass, the time-dependent kernels)
+// The main pass also runs with 64-token chunks (CC = 64): the chunk is two 32-row blocks, its
+// scores three 32 x 32 blocks (the two diagonal ones causal, the off-diagonal one full) and the
+// state is updated once per 64 tokens.  Its tiles are single-buffered (two buffers of 64-row
+// tiles do not fit in LDS), so the io and math wavefronts take turns instead of overlapping.
 // Chunks of q/k/v in flight per workgroup (register sets of the io wavefronts).  The main pass
 // is limited by its 256-VGPR budget at two wavefronts per SIMD.
 #ifndef LT_PREFETCH_MAIN
@@ -64,14 +69,16 @@ constexpr int kRopeAnchor = 64;  // chunks between exact recomputations of the R
 // segment start) S absorbs alpha and alpha returns to 1; the period keeps alpha >= 2^-20, so S
 // stays within 2^20 of the state's own magnitude.  lambda = 0 renormalises every chunk and
 // lambda = 1 never needs to.
+template <int CC = C>
 __device__ __forceinline__ int renorm_period(float log2_lambda) {
-    const float r = 20.0f / ((float)C * -log2_lambda);
+    const float r = 20.0f / ((float)CC * -log2_lambda);
     return r >= 1048576.0f ? 1048576 : max(1, (int)r);
 }
 // X after chunk `chunk` (0-based within the segment) holding n tokens
+template <int CC = C>
 __device__ __forceinline__ int lazy_exponent(int chunk, int period, int n) {
     const int cr = chunk % period;
-    return cr == 0 ? 0 : C * (cr - 1) + n;
+    return cr == 0 ? 0 : CC * (cr - 1) + n;
 }
 
 // Placement of the contraction index inside an LDS tile row.
@@ -95,31 +102,32 @@ struct Layout<ModeF32> {  // fp32 tiles keep the natural placement
     static __device__ __forceinline__ int tsw(int) { return 0; }
 };
 
-template <class M, int D, bool kStateOnly>
+template <class M, int D, bool kStateOnly, int CC = C>
 struct Cfg {
     using E = typename M::E;
     static constexpr int NW = D / 32;                 // math wavefronts
     // The bf16 main pass has two io wavefronts per SIMD (a lone wavefront issues VALU work at
-    // about half the rate two do) and they also run the output stage; elsewhere one.
-    static constexpr bool kWideIo = M::kSplit && !kStateOnly;
+    // about half the rate two do) and they also run the output stage; elsewhere one (with
+    // 64-token chunks the register budget of three wavefronts per SIMD is too small).
+    static constexpr bool kWideIo = M::kSplit && !kStateOnly && CC == 32;
     static constexpr int NIO = kWideIo ? 2 * NW : NW;  // io wavefronts
     static constexpr int NT = 64 * (NW + NIO);        // threads per workgroup
     static constexpr int HALF = D / 2;
     static constexpr int kPad = (sizeof(E) == 2) ? 8 : 4;  // 16 bytes of padding per row
     static constexpr int QS = D + kPad;               // row stride of q~/k~ tiles [token][dim]
-    static constexpr int TS = C + kPad;               // row stride of transposed tiles [dim][token]
+    static constexpr int TS = CC + kPad;              // row stride of transposed tiles [dim][token]
     static constexpr int OS = D + 8;                  // row stride of the fp32 output stage
     // Double buffering needs ~2x the tile space; fp32 tiles at d = 128 only fit single-buffered.
-    static constexpr bool kOverlap = (sizeof(E) == 2) || (D == 64);
+    static constexpr bool kOverlap = CC == 32 && ((sizeof(E) == 2) || (D == 64));
     static constexpr int NBUF = kOverlap ? 2 : 1;
 };
 
-template <class M, int D, bool kStateOnly>
+template <class M, int D, bool kStateOnly, int CC = C>
 struct alignas(16) Tiles {
-    using G = Cfg<M, D, kStateOnly>;
+    using G = Cfg<M, D, kStateOnly, CC>;
     using E = typename G::E;
-    alignas(16) E q[kStateOnly ? 1 : C * G::QS];   // q~ [token][key dim]
-    alignas(16) E k[kStateOnly ? 1 : C * G::QS];   // k~ [token][key dim]
+    alignas(16) E q[kStateOnly ? 1 : CC * G::QS];   // q~ [token][key dim]
+    alignas(16) E k[kStateOnly ? 1 : CC * G::QS];   // k~ [token][key dim]
     // decayed keys (hi part) and v: bf16 mode [token][dim] (nat_index), fp32 mode [dim][token]
     alignas(16) E khT[D * G::TS];
     alignas(16) E klT[M::kSplit ? D * G::TS : 1];  // decayed keys, lo part (bf16 mode)
@@ -137,16 +145,18 @@ struct DecayRecords<true> {
     alignas(16) float rec[2][36];
 };
 
-template <class M, int D, bool kStateOnly, bool kTD = false>
+template <class M, int D, bool kStateOnly, bool kTD = false, int CC = C>
 struct Smem {
-    using G = Cfg<M, D, kStateOnly>;
-    Tiles<M, D, kStateOnly> buf[G::NBUF];
-    alignas(16) float o[kStateOnly ? 1 : G::NBUF * C * G::OS];  // o before the output norm [token][value dim]
+    using G = Cfg<M, D, kStateOnly, CC>;
+    Tiles<M, D, kStateOnly, CC> buf[G::NBUF];
+    alignas(16) float o[kStateOnly ? 1 : G::NBUF * CC * G::OS];  // o before the output norm [token][value dim]
     alignas(16) float2 rope[2][65];  // cos/sin(p0 f_i) of the next two chunks
                                      // (entry 64: write sink of idle lanes)
     // decay factors of the math wavefronts' accumulator elements, per lane: [0, 4) the causal
-    // decay of the transposed score tile, [4, 8) lambda^(i+1) of the output rows
-    alignas(16) float4 dec[kStateOnly ? 1 : 64 * 8];
+    // decay of the transposed (diagonal) score tile, [4, 8) lambda^(i+1) of the output rows;
+    // with 64-token chunks also [8, 12) the off-diagonal score block's lambda^(32+i-j) and
+    // [12, 16) lambda^(33+i) of the second block's output rows
+    alignas(16) float4 dec[kStateOnly ? 1 : 64 * (CC / 4)];
     alignas(16) float wo[D];
     [[no_unique_address]] DecayRecords<kTD> td;
 };
@@ -258,9 +268,10 @@ __device__ __forceinline__ void contract_acc(f32x16& acc, const f32x16& x, const
 // One workgroup's pass over its segment.  kPrecise: the state update uses the hi + lo parts of
 // the decayed keys (bf16 mode; fp32 mode is always exact to fp32).  kTD: the decay is the
 // data-dependent alpha_t = 2^log2_decay[b][t][h] instead of the fixed lambda_h.
-template <class M, int D, bool kStateOnly, int PF, bool kPrecise, bool kTD>
-__device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kStateOnly, kTD>& sm) {
-    using G = Cfg<M, D, kStateOnly>;
+template <class M, int D, bool kStateOnly, int PF, bool kPrecise, bool kTD, int CC>
+__device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kStateOnly, kTD, CC>& sm) {
+    static_assert(CC == 32 || (CC == 64 && !kStateOnly && !kTD), "64-token chunks: fixed-decay main pass");
+    using G = Cfg<M, D, kStateOnly, CC>;
     using E = typename G::E;
     using In = typename M::In;
     using A = Act<M>;
@@ -290,7 +301,7 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
         t_begin = seg * p.L;
         t_end = min(p.T, t_begin + p.L);
     }
-    const int n_chunks = (t_end - t_begin + C - 1) / C;
+    const int n_chunks = (t_end - t_begin + CC - 1) / CC;
     // pipeline steps: chunk s is written in step s, computed in step s+1 and stored in step s+2;
     // rounded up to a multiple of PF so the io loop can rotate PF register sets without branches
     const int n_steps = (n_chunks + 2 + PF - 1) / PF * PF;
@@ -303,17 +314,17 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
     const size_t x_base = (size_t)b * p.T * x_stride + (size_t)h * D;
 
     // ---- io-role constants ----
-    constexpr int RPT = 2 * NW / NIO;         // rows per io thread (2, or 1 with two io per SIMD)
     constexpr int FG = D / 8;                 // prologue: threads per row group
+    constexpr int RPT = CC * FG / (64 * NIO);  // rows per io thread
     const int it = threadIdx.x - 64 * NW;     // io thread index (negative in math waves)
     const int fg = it % FG, rg = it / FG;     // rows RPT rg + s, features 4 fg + u and HALF + 4 fg + u
-    static_assert(64 * NIO / FG * RPT == C, "the io wavefronts cover the chunk's rows");
+    static_assert(64 * NIO / FG * RPT == CC, "the io wavefronts cover the chunk's rows");
     // ---- output stage (io or math wavefronts) ----
     constexpr int ETH = 64 * (kEpiIo ? NIO : NW);  // its threads
-    constexpr int EPT = C * D / ETH, TPR = D / EPT;  // outputs per thread, threads per row
+    constexpr int EPT = CC * D / ETH, TPR = D / EPT;  // outputs per thread, threads per row
     const int et = kEpiIo ? it : (int)threadIdx.x;
     const int er = et / TPR, ec = et % TPR;
-    static_assert(ETH / TPR == C && EPT % 8 == 0, "the output stage covers the chunk's rows");
+    static_assert(ETH / TPR == CC && EPT % 8 == 0, "the output stage covers the chunk's rows");
 
     // Per-chunk RoPE base table cos/sin(p0 f_i), one frequency per lane, filled by a single io
     // wavefront (the io wavefronts take turns chunk by chunk).  Most chunks advance the previous
@@ -325,12 +336,12 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
     const int table_i = lane < HALF ? lane : 64;
     const double table_frev = p.inv_freq_rev[min(lane, HALF - 1)];
     float2 table_step;  // cos/sin(C f_i)
-    rope_cos_sin(C, table_frev, table_step.x, table_step.y);
+    rope_cos_sin(CC, table_frev, table_step.x, table_step.y);
     auto fill_rope_table = [&](int chunk, int slot) {
         if (wave - NW != chunk % NIO) return;  // wave-uniform
         float2 e;
         if (chunk % kRopeAnchor == 0) {
-            rope_cos_sin(p.pos0 + t_begin + (int64_t)chunk * C, table_frev, e.x, e.y);
+            rope_cos_sin(p.pos0 + t_begin + (int64_t)chunk * CC, table_frev, e.x, e.y);
         } else {
             const float2 a = sm.rope[slot ^ 1][table_i];  // the previous chunk's entry
             e.x = a.x * table_step.x - a.y * table_step.y;
@@ -346,18 +357,26 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
         // Per lane of a math wavefront: accumulator register r sits at row m = acc_row(r) and
         // column lm.  Score tile (transposed, P^T[j = m][i = lm]): lambda^(i-j) for j <= i, else
         // 0.  Output tile (row i = m): lambda^(i+1).
-        float4* dl = sm.dec + 8 * lane;
+        // With 64-token chunks also the off-diagonal block (query i in the second block, key j
+        // in the first): lambda^(32+i-j), and the second block's rows: lambda^(33+i).
+        float4* dl = sm.dec + (CC / 4) * lane;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            float mk[4], rs[4];
+            float mk[4], rs[4], mo[4], rb[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int m = acc_row(4 * g + e, lh);
                 mk[e] = (lm >= m) ? pow_lambda(l2l, lm - m) : 0.0f;
                 rs[e] = pow_lambda(l2l, m + 1);
+                mo[e] = pow_lambda(l2l, 32 + lm - m);
+                rb[e] = pow_lambda(l2l, 33 + m);
             }
             dl[g] = make_float4(mk[0], mk[1], mk[2], mk[3]);
             dl[4 + g] = make_float4(rs[0], rs[1], rs[2], rs[3]);
+            if constexpr (CC == 64) {
+                dl[8 + g] = make_float4(mo[0], mo[1], mo[2], mo[3]);
+                dl[12 + g] = make_float4(rb[0], rb[1], rb[2], rb[3]);
+            }
         }
     }
     __syncthreads();
@@ -366,20 +385,20 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
     // unconditional (rows past the segment end re-read its last row), which keeps the
     // memory-wait bookkeeping exact across iterations.
     const uint32_t rs32 = (uint32_t)row_stride, xs32 = (uint32_t)x_stride;
-    auto chunk_start = [&](int chunk) { return t_begin + min(chunk, n_chunks - 1) * C; };
+    auto chunk_start = [&](int chunk) { return t_begin + min(chunk, n_chunks - 1) * CC; };
     const In* gg = static_cast<const In*>(p.g) + x_base;
     In* gy = static_cast<In*>(p.y) + head_base;
     // epilogue of one chunk: y = RMSNorm(o) * w_o * sigmoid(g)
     constexpr int GV = EPT * sizeof(In) / 16;  // 16-byte vectors of gate logits per thread
     auto load_gate = [&](int chunk, uint4* gr, bool full = false) {
-        const int cs = full ? t_begin + chunk * C : chunk_start(chunk);
+        const int cs = full ? t_begin + chunk * CC : chunk_start(chunk);
         const uint32_t o = (uint32_t)(full ? er : min(er, t_end - 1 - cs)) * xs32 + EPT * ec;
         const uint4* src = reinterpret_cast<const uint4*>(gg + (size_t)cs * x_stride + o);
 #pragma unroll
         for (int i = 0; i < GV; ++i) gr[i] = src[i];
     };
     auto epilogue = [&](int chunk, const float* o_stage, const uint4* gr, bool full) {
-        const int t = t_begin + chunk * C + er;
+        const int t = t_begin + chunk * CC + er;
         float o[EPT];
         const float* orow = o_stage + er * OS + EPT * ec;
 #pragma unroll
@@ -454,15 +473,15 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
                     S[c][r] = src ? src[(size_t)(32 * c + acc_row(r, lh)) * D + 32 * w + lm] : 0.0f;
         }
         // this lane's decay factors, kept in LDS rather than in 32 registers for the whole loop
-        const float* dec = reinterpret_cast<const float*>(sm.dec + 8 * lane);
-        const float lam_full = pow_lambda(l2l, C);
-        const int period = renorm_period(l2l);
+        const float* dec = reinterpret_cast<const float*>(sm.dec + (CC / 4) * lane);
+        const float lam_full = pow_lambda(l2l, CC);
+        const int period = renorm_period<CC>(l2l);
         float alpha = 1.0f;  // state = alpha * S
 
         using L = Layout<M>;
         const int vsw = L::tsw(32 * w + lm);
-        auto compute = [&](int chunk, const Tiles<M, D, kStateOnly>& t, float* o_stage) {
-            const int n = min(C, t_end - (t_begin + chunk * C));
+        auto compute = [&](int chunk, const Tiles<M, D, kStateOnly, CC>& t, float* o_stage) {
+            const int n = min(CC, t_end - (t_begin + chunk * CC));
             bool renorm;
             float carry, alpha_next;
             // time-dependent decay factors of the score tile (P^T[j][i]: 2^(c_i - c_j), j <= i)
@@ -489,11 +508,134 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
             } else {
                 renorm = chunk % period == 0;
                 // renormalising chunks fold alpha and this chunk's decay into S
-                carry = alpha * ((n == C) ? lam_full : pow_lambda(l2l, n));
-                alpha_next = pow_lambda(l2l, lazy_exponent(chunk, period, n));
+                carry = alpha * ((n == CC) ? lam_full : pow_lambda(l2l, n));
+                alpha_next = pow_lambda(l2l, lazy_exponent<CC>(chunk, period, n));
             }
             const E* vrow = t.vT + (32 * w + lm) * TS;
-            if constexpr (M::kSplit) {
+            if constexpr (CC == 64) {
+                // 64 tokens as two 32-row blocks a (rows 0-31) and b (rows 32-63): scores P_aa,
+                // P_ba (query in b, key in a: not masked, decay lambda^(32+i-j)) and P_bb; each
+                // block's output from the state entering the chunk; one state update over all 64
+                // tokens.  The bf16 operand placement is that of the 32-token path.
+                const E* qa_row = t.q + lm * QS;
+                const E* qb_row = t.q + (32 + lm) * QS;
+                const E* ka_row = t.k + lm * QS;
+                const E* kb_row = t.k + (32 + lm) * QS;
+                {  // block a
+                    f32x16 pt = {}, o = {};
+                    if constexpr (M::kSplit) {
+#pragma unroll
+                        for (int s8 = 0; s8 < D / 16; ++s8) {
+                            const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qa_row + 16 * s8 + 8 * lh);
+                            const bf16x8 kv = *reinterpret_cast<const bf16x8*>(ka_row + 16 * s8 + 8 * lh);
+                            bf16x8 sv;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) sv[e] = to_bf16(S[s8 / 2][8 * (s8 % 2) + e]);
+                            pt = mfma_bf16(kv, qv, pt);
+                            o = mfma_bf16(qv, sv, o);
+                        }
+                    } else {
+                        contract_rows<D>(pt, ka_row, qa_row, lh);
+#pragma unroll
+                        for (int c = 0; c < NW; ++c) contract_acc(o, S[c], qa_row + 32 * c, lh, false);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        pt[r] *= dec[r];
+                        o[r] *= dec[16 + r] * alpha;
+                    }
+                    if constexpr (M::kSplit) {
+#pragma unroll
+                        for (int st = 0; st < 2; ++st) {
+                            const bf16x8 vb = tr_operand<D>(t.vT, 16 * st, 32 * w, lane);
+                            bf16x8 pv;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) pv[e] = to_bf16(pt[8 * st + e]);
+                            o = mfma_bf16(pv, vb, o);
+                        }
+                    } else {
+                        contract_acc(o, pt, vrow, lh, true, vsw);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o_stage[acc_row(r, lh) * OS + 32 * w + lm] = o[r];
+                }
+                {  // block b
+                    f32x16 pa = {}, pb = {}, o = {};
+                    if constexpr (M::kSplit) {
+#pragma unroll
+                        for (int s8 = 0; s8 < D / 16; ++s8) {
+                            const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qb_row + 16 * s8 + 8 * lh);
+                            const bf16x8 kav = *reinterpret_cast<const bf16x8*>(ka_row + 16 * s8 + 8 * lh);
+                            const bf16x8 kbv = *reinterpret_cast<const bf16x8*>(kb_row + 16 * s8 + 8 * lh);
+                            bf16x8 sv;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) sv[e] = to_bf16(S[s8 / 2][8 * (s8 % 2) + e]);
+                            pa = mfma_bf16(kav, qv, pa);
+                            pb = mfma_bf16(kbv, qv, pb);
+                            o = mfma_bf16(qv, sv, o);
+                        }
+                    } else {
+                        contract_rows<D>(pa, ka_row, qb_row, lh);
+                        contract_rows<D>(pb, kb_row, qb_row, lh);
+#pragma unroll
+                        for (int c = 0; c < NW; ++c) contract_acc(o, S[c], qb_row + 32 * c, lh, false);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        pa[r] *= dec[32 + r];
+                        pb[r] *= dec[r];
+                        o[r] *= dec[48 + r] * alpha;
+                    }
+                    if constexpr (M::kSplit) {
+#pragma unroll
+                        for (int st = 0; st < 2; ++st) {
+                            const bf16x8 va = tr_operand<D>(t.vT, 16 * st, 32 * w, lane);
+                            const bf16x8 vb = tr_operand<D>(t.vT, 32 + 16 * st, 32 * w, lane);
+                            bf16x8 pva, pvb;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                pva[e] = to_bf16(pa[8 * st + e]);
+                                pvb[e] = to_bf16(pb[8 * st + e]);
+                            }
+                            o = mfma_bf16(pva, va, o);
+                            o = mfma_bf16(pvb, vb, o);
+                        }
+                    } else {
+                        contract_acc(o, pa, vrow, lh, true, vsw);
+                        contract_acc(o, pb, vrow + 32, lh, true, vsw);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o_stage[(32 + acc_row(r, lh)) * OS + 32 * w + lm] = o[r];
+                }
+                if (renorm) {
+#pragma unroll
+                    for (int c = 0; c < NW; ++c)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) S[c][r] *= carry;
+                }
+                if constexpr (M::kSplit) {
+#pragma unroll
+                    for (int st = 0; st < 4; ++st) {
+                        const bf16x8 vb = tr_operand<D>(t.vT, 16 * st, 32 * w, lane);
+                        bf16x8 ah[NW], al[NW];
+#pragma unroll
+                        for (int c = 0; c < NW; ++c) {
+                            ah[c] = tr_operand<D>(t.khT, 16 * st, 32 * c, lane);
+                            if (precise) al[c] = tr_operand<D>(t.klT, 16 * st, 32 * c, lane);
+                        }
+#pragma unroll
+                        for (int c = 0; c < NW; ++c) S[c] = mfma_bf16(ah[c], vb, S[c]);
+                        if (precise) {
+#pragma unroll
+                            for (int c = 0; c < NW; ++c) S[c] = mfma_bf16(al[c], vb, S[c]);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < NW; ++c)
+                        contract_rows<CC>(S[c], t.khT + (32 * c + lm) * TS, vrow, lh, L::tsw(32 * c + lm), vsw);
+                }
+            } else if constexpr (M::kSplit) {
                 // bf16 operands.  With the kpos placement the 16-byte block at 16 s + 8 lh of a
                 // q~ row is both the B operand of the scores (natural k) and the A operand of the
                 // query-state product (k in accumulator order), so one read feeds both and the
@@ -588,7 +730,7 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
                 }
 #pragma unroll
                 for (int c = 0; c < NW; ++c)
-                    contract_rows<C>(S[c], t.khT + (32 * c + lm) * TS, vrow, lh, L::tsw(32 * c + lm), vsw);
+                    contract_rows<CC>(S[c], t.khT + (32 * c + lm) * TS, vrow, lh, L::tsw(32 * c + lm), vsw);
             }
             alpha = alpha_next;
         };
@@ -601,21 +743,23 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
             if (!kStateOnly && !kEpiIo) load_gate(0, gcur);
             for (int s = 0; s < n_steps; ++s) {
                 if (!kStateOnly && !kEpiIo && s >= 2 && s - 2 < n_chunks) {
-                    epilogue(s - 2, sm.o + (s & 1) * C * OS, gcur, s - 1 < n_chunks);
+                    epilogue(s - 2, sm.o + (s & 1) * CC * OS, gcur, s - 1 < n_chunks);
                     load_gate(s - 1, gcur);
                 }
                 if (s >= 1 && s <= n_chunks)
-                    compute(s - 1, sm.buf[(s - 1) & 1], kStateOnly ? nullptr : sm.o + ((s - 1) & 1) * C * OS);
+                    compute(s - 1, sm.buf[(s - 1) & 1], kStateOnly ? nullptr : sm.o + ((s - 1) & 1) * CC * OS);
                 __syncthreads();
             }
         } else {
+            // single buffer: per chunk, the io wavefronts stage it, the math wavefronts process
+            // it, then the output stage (here unless the io wavefronts run it) stores it
             uint4 gcur[GV];
-            if (!kStateOnly) load_gate(0, gcur);
+            if (!kStateOnly && !kEpiIo) load_gate(0, gcur);
             for (int s = 0; s < n_chunks; ++s) {
                 __syncthreads();  // chunk s in LDS
                 compute(s, sm.buf[0], kStateOnly ? nullptr : sm.o);
                 __syncthreads();  // tiles consumed, output staged
-                if (!kStateOnly) {
+                if (!kStateOnly && !kEpiIo) {
                     epilogue(s, sm.o, gcur, s + 1 < n_chunks);
                     load_gate(s + 1, gcur);
                 }
@@ -671,7 +815,7 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
         // (rows past the segment end re-read its last row; the prologue zeroes them)
         // full: the chunk is known to be full and not past the end (no clamping)
         auto load = [&](int chunk, Regs& r, bool full) {
-            const int cs = full ? t_begin + chunk * C : chunk_start(chunk);
+            const int cs = full ? t_begin + chunk * CC : chunk_start(chunk);
             const size_t cb = (size_t)cs * x_stride;
 #pragma unroll
             for (int s = 0; s < RPT; ++s) {
@@ -696,15 +840,15 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
         // decay of this thread's two rows in a full chunk, lambda^(C-1-j)
         float kdec_full[RPT];
 #pragma unroll
-        for (int s = 0; s < RPT; ++s) kdec_full[s] = pow_lambda(l2l, C - 1 - (RPT * rg + s));
-        const int period = renorm_period(l2l);  // the math wavefronts' lazy state scale
+        for (int s = 0; s < RPT; ++s) kdec_full[s] = pow_lambda(l2l, CC - 1 - (RPT * rg + s));
+        const int period = renorm_period<CC>(l2l);  // the math wavefronts' lazy state scale
         // time-dependent: the state's log2 scale (renormalised whenever it would fall below
         // 2^-20, so S stays within 2^20 of the state) and the pass's total log2 decay
         float td_log_alpha = 0.0f, td_total = 0.0f;
         // full: the chunk is known to hold C tokens (every row valid, no per-row test)
-        auto prologue = [&](int chunk, const Regs& r, Tiles<M, D, kStateOnly>& t, bool full) {
-            const int n = full ? C : min(C, t_end - (t_begin + chunk * C));
-            const float inv_alpha = pow_lambda(l2l, -lazy_exponent(chunk, period, C));  // full chunks
+        auto prologue = [&](int chunk, const Regs& r, Tiles<M, D, kStateOnly, CC>& t, bool full) {
+            const int n = full ? CC : min(CC, t_end - (t_begin + chunk * CC));
+            const float inv_alpha = pow_lambda(l2l, -lazy_exponent<CC>(chunk, period, CC));  // full chunks
             float kdec_td[RPT];  // time-dependent key factors 2^(c_(n-1) - c_j) / alpha_next
             if constexpr (kTD) {
                 // inclusive prefix sums of the chunk's log2 decays (rows past the end decay by
@@ -768,7 +912,7 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
                 // lambda^(n-1-j) / alpha, alpha = lambda^X the state's scale after this chunk
                 const float kdec = kTD ? kdec_td[s]
                                    : full ? kdec_full[s] * inv_alpha
-                                          : pow_lambda(l2l, n - 1 - j - lazy_exponent(chunk, period, n));
+                                          : pow_lambda(l2l, n - 1 - j - lazy_exponent<CC>(chunk, period, n));
                 const float rq = valid ? rq0 : 0.0f;
                 const float rk = valid ? rk0 : 0.0f;
                 const float kds = rk * kdec;  // decayed-key scale
@@ -824,14 +968,17 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
                     }
                 }
             } else {
-                static_assert(RPT == 2 || kStateOnly || M::kSplit, "fp32 tiles pair two rows");
-                const int jp = Layout<M>::kpos(2 * rg);  // the two tokens stay adjacent
+                static_assert(RPT % 2 == 0 || kStateOnly || M::kSplit, "fp32 tiles pair two rows");
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int f = (i < 4) ? 4 * fg + i : HALF + 4 * fg + (i - 4);
-                    const int col = f * TS + (jp ^ Layout<M>::tsw(f));
-                    st2(t.khT + col, kd[0][i], kd[1][i]);
-                    st_pair(t.vT + col, r.v[0][i / 4], r.v[1][i / 4], i % 4);
+                for (int pr = 0; pr < RPT / 2; ++pr) {
+                    const int jp = Layout<M>::kpos(RPT * rg + 2 * pr);  // the two tokens stay adjacent
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int f = (i < 4) ? 4 * fg + i : HALF + 4 * fg + (i - 4);
+                        const int col = f * TS + (jp ^ Layout<M>::tsw(f));
+                        st2(t.khT + col, kd[2 * pr][i], kd[2 * pr + 1][i]);
+                        st_pair(t.vT + col, r.v[2 * pr][i / 4], r.v[2 * pr + 1][i / 4], i % 4);
+                    }
                 }
             }
         };
@@ -856,7 +1003,7 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
                 load(s + PF, cur, steady);
                 if (steady || s + 1 < n_chunks) fill_rope_table(s + 1, (s + 1) & 1);
                 if (kEpiIo && (steady || (s >= 2 && s - 2 < n_chunks))) {
-                    epilogue(s - 2, sm.o + (s & 1) * C * OS, gep, steady || s - 1 < n_chunks);
+                    epilogue(s - 2, sm.o + (s & 1) * CC * OS, gep, steady || s - 1 < n_chunks);
                     load_gate(s - 2 + PF, gep, steady);
                 }
                 __syncthreads();
@@ -876,13 +1023,24 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
                 for (int i = 0; i < PF; ++i) step(s0 + i, rs[i], gs[(i + PF - 2) % PF], false);
             }
         } else {
-            Regs ra;
-            for (int s = 0; s < n_chunks; ++s) {
-                load(s, ra, false);
-                prologue(s, ra, sm.buf[0], false);
+            // single buffer: the next chunk's q/k/v are loaded while this one is processed; the
+            // output stage (when it runs here) stores a chunk before the next one is staged
+            Regs ra, rb;
+            uint4 gcur[kEpiIo ? GV : 1];
+            load(0, ra, false);
+            auto one = [&](int s, Regs& cur, Regs& nxt) {
+                if (s >= n_chunks) return;  // (uniform)
+                load(s + 1, nxt, false);
+                if (kEpiIo) load_gate(s, gcur);
+                prologue(s, cur, sm.buf[0], false);
                 if (s + 1 < n_chunks) fill_rope_table(s + 1, (s + 1) & 1);
                 __syncthreads();  // chunk s in LDS
-                __syncthreads();  // math done with chunk s
+                __syncthreads();  // math done with chunk s, outputs staged
+                if (kEpiIo) epilogue(s, sm.o, gcur, s + 1 < n_chunks);
+            };
+            for (int s = 0; s < n_chunks; s += 2) {
+                one(s, ra, rb);
+                one(s + 1, rb, ra);
             }
         }
         if constexpr (kTD && kStateOnly) {
@@ -899,11 +1057,11 @@ __device__ __forceinline__ void chunk_pass(const ChunkParams& p, Smem<M, D, kSta
 // and made once, so each pass is branch-free inside its loop.
 // The state-only pass is register-limited so that kStateOnlyBlocksPerCU of its workgroups share
 // a CU (their barriers are independent, so one hides the other's stalls).
-template <class M, int D, bool kStateOnly, int PF, bool kTD>
-__global__ void __launch_bounds__((Cfg<M, D, kStateOnly>::NT))
+template <class M, int D, bool kStateOnly, int PF, bool kTD, int CC = C>
+__global__ void __launch_bounds__((Cfg<M, D, kStateOnly, CC>::NT))
 __attribute__((amdgpu_waves_per_eu(kStateOnly ? kStateOnlyBlocksPerCU * D / 64 : 1)))
 chunk_kernel(const ChunkParams p) {
-    __shared__ Smem<M, D, kStateOnly, kTD> sm;
+    __shared__ Smem<M, D, kStateOnly, kTD, CC> sm;
     bool precise = true;
     if constexpr (M::kSplit) {
         if constexpr (kStateOnly && kTD) {
@@ -926,9 +1084,9 @@ chunk_kernel(const ChunkParams p) {
         }
     }
     if (precise)
-        chunk_pass<M, D, kStateOnly, PF, true, kTD>(p, sm);
+        chunk_pass<M, D, kStateOnly, PF, true, kTD, CC>(p, sm);
     else
-        chunk_pass<M, D, kStateOnly, PF, false, kTD>(p, sm);
+        chunk_pass<M, D, kStateOnly, PF, false, kTD, CC>(p, sm);
 }
 
 // ws[b][h][j] holds each state-only sub-segment's end state from zero (j < P-1).  The state
@@ -987,7 +1145,15 @@ hipError_t launch_typed(const ChunkParams& cp, const ScanParams& sp, const hipEv
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (ev[0] && (err = hipEventRecord(ev[0], stream)) != hipSuccess) return err;
-    chunk_kernel<M, D, false, kPrefetchMain, kTD><<<dim3(BH * cp.P), dim3(Cfg<M, D, false>::NT), 0, stream>>>(cp);
+    if constexpr (!kTD && !(std::is_same_v<M, ModeF32> && D == 128)) {
+        if (cp.C == 64)  // (64-token chunks: fixed decay; fp32 d = 128 tiles do not fit in LDS)
+            chunk_kernel<M, D, false, kPrefetchMain, false, 64><<<dim3(BH * cp.P), dim3(Cfg<M, D, false, 64>::NT), 0, stream>>>(cp);
+        else
+            chunk_kernel<M, D, false, kPrefetchMain, kTD><<<dim3(BH * cp.P), dim3(Cfg<M, D, false>::NT), 0, stream>>>(cp);
+    } else {
+        if (cp.C != C) return hipErrorInvalidValue;
+        chunk_kernel<M, D, false, kPrefetchMain, kTD><<<dim3(BH * cp.P), dim3(Cfg<M, D, false>::NT), 0, stream>>>(cp);
+    }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev[1] && (err = hipEventRecord(ev[1], stream)) != hipSuccess) return err;
     return hipSuccess;

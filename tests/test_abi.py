@@ -151,6 +151,20 @@ def test_plan_explicit_segments_and_chunk():
     assert lt.lightning_prefill_workspace_size(1, 1000, 2, 96) == 0
 
 
+def test_plan_chunk64():
+    """64-token chunks: segments are whole 64-token chunks (and state-only sub-segments too);
+    fp32 with d = 128 (tiles too large for LDS) is unsupported, bf16 and fp32 d = 64 are not."""
+    pl = lt.lightning_prefill_plan_cus(256, 1, 524288, 16, 128, chunk=64)
+    assert pl["chunk"] == 64 and pl["segments"] > 1
+    assert pl["segment_len"] % 64 == 0 and pl["subsegment_len"] % 64 == 0
+    assert (pl["segments"] - 1) * pl["segment_len"] < 524288 <= pl["segments"] * pl["segment_len"]
+    for dt, d in ((torch.bfloat16, 64), (torch.float32, 64), (torch.bfloat16, 128)):
+        assert lt.lightning_prefill_plan_cus(256, 1, 256, 2, d, dtype=dt, chunk=64)["chunk"] == 64
+    with pytest.raises(lt.LightningError) as e:
+        lt.lightning_prefill_plan_cus(256, 1, 1000, 2, 128, dtype=torch.float32, chunk=64)
+    assert e.value.status == lt.LT_ERR_UNSUPPORTED
+
+
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="checks the behaviour without a device")
 def test_plan_without_a_device_is_a_hip_error():
     """The automatic split depends on the device's compute units: with no device visible the

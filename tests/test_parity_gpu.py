@@ -58,6 +58,31 @@ def test_prefill_small(case):
         compare_prefill(gpu, ref, dtype, label=f"{label} segments={seg}")
 
 
+# 64-token chunks (the main pass's second instantiation): every small case but fp32 with d = 128,
+# whose 64-row tiles do not fit in LDS (the library rejects that combination)
+SMALL64 = [c for c in SMALL if not (c[5] == torch.float32 and c[4] == 128)]
+
+
+@pytest.mark.parametrize("case", SMALL64, ids=[c[0] for c in SMALL64])
+def test_prefill_small_chunk64(case):
+    label, B, T, H, d, dtype, lams, state, seg_list = case
+    inp = synth.make_custom_prefill(B, T, H, d, dtype=dtype, seed=zlib.crc32(label.encode()) % 10000,
+                                    lambdas=lams, rope_base=1e4 if d == 64 else 1e6, state=state)
+    ref = oracle_prefill(inp)
+    for seg in seg_list:
+        gpu = gpu_prefill(inp, chunk=64, segments=seg)
+        compare_prefill(gpu, ref, dtype, label=f"{label} chunk=64 segments={seg}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 127, 129, 191])
+def test_prefill_chunk64_boundary_lengths(T):
+    inp = synth.make_custom_prefill(2, T, 2, 128, dtype=torch.bfloat16, seed=T + 100, state="randn")
+    ref = oracle_prefill(inp)
+    compare_prefill(gpu_prefill(inp, chunk=64), ref, torch.bfloat16, label=f"T={T} chunk=64")
+    compare_prefill(gpu_prefill(inp, chunk=64, segments=2), ref, torch.bfloat16,
+                    label=f"T={T} chunk=64 seg=2")
+
+
 @pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 127, 129])
 def test_prefill_short_and_boundary_lengths(T):
     inp = synth.make_custom_prefill(2, T, 2, 128, dtype=torch.bfloat16, seed=T, state="randn")
@@ -67,16 +92,18 @@ def test_prefill_short_and_boundary_lengths(T):
 
 
 def test_tiny_workload_as_specified():
-    """The tiny workload as drawn (fp32, d = 64).  Its chunk length of 64 is the oracle's chunked
-    form (equal to the recurrence, see the oracle pins); the library computes with its own
-    32-token chunks and must match the same oracle."""
+    """The tiny workload as drawn (fp32, d = 64) at its stated chunk length of 64, and at the
+    library's default of 32.  The oracle's chunked form at C = 64 equals its recurrence (see the
+    oracle pins)."""
     inp = synth.make_prefill(synth.TINY)
     ref = oracle_prefill(inp)
     ref64 = oracle.prefill(*(host_bits(inp[n]) for n in ("q", "k", "v", "g")), inp["qw"].numpy(),
                            inp["kw"].numpy(), inp["lambdas"], inp["rope_base"], chunk=64)
     assert np.max(np.abs(ref64["y"] - ref["y"])) <= 1e-12
-    worst = compare_prefill(gpu_prefill(inp), ref, torch.float32, label="tiny workload")
-    assert worst["state"] <= 1e-4
+    for chunk in (64, 0):
+        worst = compare_prefill(gpu_prefill(inp, chunk=chunk), ref, torch.float32,
+                                label=f"tiny workload chunk={chunk}")
+        assert worst["state"] <= 1e-4
 
 
 def test_output_norm_weight_shared_norm_weights_and_position_origin():
@@ -234,7 +261,7 @@ def _gather_slices(inp, slices):
                 lambdas=[inp["lambdas"][h] for _, h in slices], state_in=s_in)
 
 
-def _full_size(spec, slices, device_inputs):
+def _full_size(spec, slices, device_inputs, chunk=0):
     import long_context_hybrid_amd.lightning as lt
 
     inp = synth.make_prefill(spec, device="cuda" if device_inputs else "cpu")
@@ -242,11 +269,11 @@ def _full_size(spec, slices, device_inputs):
     B, T, H, d = inp["q"].shape
     s_in = None if inp["state_in"] is None else inp["state_in"].to(dev)
     s_out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
-    # the launch configuration the benchmark times (automatic chunk and segments)
+    # the launch configuration the benchmark times (automatic segments; chunk 0 = 32)
     y = lt.lightning_prefill(*(inp[n].to(dev) for n in ("q", "k", "v", "g")), inp["qw"].to(dev),
                              inp["kw"].to(dev), inp["lambdas"], inp["rope_base"],
                              rms_eps=inp["eps"], pos0=inp["pos0"], state_in=s_in,
-                             state_out=s_out)
+                             state_out=s_out, chunk=chunk)
     torch.cuda.synchronize()
     gpu = dict(y=torch.stack([y[b, :, h].float().cpu() for b, h in slices], dim=1)[None],
                state=torch.stack([s_out[b, h].cpu() for b, h in slices])[None])
@@ -255,12 +282,16 @@ def _full_size(spec, slices, device_inputs):
     del inp
     ref = oracle_prefill(sub)
     return compare_prefill(gpu, ref, torch.bfloat16, what=("y", "state"),
-                           label=f"{spec.name} slices {slices}")
+                           label=f"{spec.name} chunk={chunk} slices {slices}")
 
 
 def test_full_qwen17_32k_all_heads():
     slices = [(0, h) for h in range(16)]
     _full_size(synth.QWEN17_32K, slices, device_inputs=False)
+
+
+def test_full_qwen17_32k_all_heads_chunk64():
+    _full_size(synth.QWEN17_32K, [(0, h) for h in range(16)], device_inputs=False, chunk=64)
 
 
 def test_full_qwen17_512k_sampled_heads():
