@@ -127,10 +127,11 @@ def measured_traffic(kernel, workload, record=TRAFFIC_RECORD, sources=MIXER_SOUR
     rec = json.loads(lines[-1][len("traffic-record: "):])
     if rec.get("source_sha256") != source_fingerprint(sources):
         return None
-    k = rec["kernels"].get(kernel)
-    if k is None or k.get("workload") != workload:
-        return None
-    return int(round((k["fetch_kib"] * rec["fetch_scale"] + k["write_kib"] * rec["write_scale"]) * 1024))
+    for k in rec.get("entries", []):
+        if k["kernel"] == kernel and k["workload"] == workload:
+            return int(round((k["fetch_kib"] * rec["fetch_scale"] + k["write_kib"] * rec["write_scale"])
+                             * 1024))
+    return None
 
 
 class HipEvents:
@@ -343,7 +344,8 @@ def bench_time_dependent(args, torch, lt, synth, fixed):
            "unit": "tokens/s/layer",
            "cost_vs_fixed_decay": round(ms / fixed["ms_per_step"], 3),
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "traffic": measured_traffic("main", spec.name + ", data-dependent decay"),
                         "kernel": "chunk_kernel<ModeBF16,128,false,4,true> (main pass)",
                         "alg_bytes_per_launch": alg, "launch_ms": round(main_ms, 4)}}
     if not args.no_decode:
