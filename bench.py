@@ -142,6 +142,12 @@ class HipEvents:
         self.hip.hipEventCreate.argtypes = [ct.POINTER(ct.c_void_p)]
         self.hip.hipEventElapsedTime.argtypes = [ct.POINTER(ct.c_float), ct.c_void_p, ct.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ct.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ct.c_void_p, ct.c_void_p]
+
+    def record(self, e, stream):
+        """Record event `e` on a torch stream (the library's calls run on torch's current one)."""
+        if self.hip.hipEventRecord(ct.c_void_p(e), ct.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def create(self, n):
         evs = []
@@ -485,8 +491,9 @@ def bench_layer_decode(args, torch, lt, synth, B=None):
 
 def bench_attn(args, torch, lt, synth):
     """HyPE softmax attention (the hybrid's attention layers) at 512K tokens: the prologue
-    (QK-norm and the s_t log2(e)/sqrt(d) query scale) and the flash-attention kernel, the latter
-    timed with the HIP events the library records around it."""
+    (QK-norm and the s_t log2(e)/sqrt(d) query scale; the normalised keys into the key cache)
+    and the flash-attention kernel, timed with the HIP events the library records around the
+    latter and one recorded just before each call."""
     spec = synth.ATTN_QWEN17_512K
     dev = torch.device("cuda:0")
     inp = synth.make_attn(spec, device=dev)
@@ -504,16 +511,22 @@ def bench_attn(args, torch, lt, synth):
     torch.cuda.synchronize()
     hev = HipEvents()
     n = args.attn_steps
-    ev = hev.create(2 * n)
+    ev = hev.create(3 * n)
+    cur = torch.cuda.current_stream(dev)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(n):
-        lt.lightning_attn_prefill(*call, **kw, main_kernel_events=(ev[2 * i], ev[2 * i + 1]))
+        hev.record(ev[3 * i], cur)
+        lt.lightning_attn_prefill(*call, **kw, main_kernel_events=(ev[3 * i + 1], ev[3 * i + 2]))
     stop.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / n
-    main_ms = sum(hev.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for i in range(n)) / n
+    main_ms = sum(hev.elapsed_ms(ev[3 * i + 1], ev[3 * i + 2]) for i in range(n)) / n
+    pro_ms = sum(hev.elapsed_ms(ev[3 * i], ev[3 * i + 1]) for i in range(n)) / n
     hev.destroy(ev)
+    # prologue bytes: q read and q~ written (Hq rows), k read and k^ written to the key cache
+    pro_bytes = 2 * B * T * (Hq + Hkv) * d * 2
+    pro_gbs = pro_bytes / (pro_ms * 1e-3) / 1e9
     flops = 4 * d * Hq * B * T * (T + 1) // 2  # q.k and p.v over the causal triangle
     tf = flops / (main_ms * 1e-3) / 1e12
     del inp, y, cache, ws
@@ -523,7 +536,9 @@ def bench_attn(args, torch, lt, synth):
                          "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
                          "traffic": None, "kernel": "attn_fwd_kernel<2> (flash attention)",
                          "flops_per_launch": flops, "launch_ms": round(main_ms, 3)},
-            "prologue_ms": round(ms - main_ms, 3)}
+            "prologue": {"ms": round(pro_ms, 4), "bound": "hbm", "achieved": round(pro_gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(pro_gbs / HBM_PEAK_GBS, 4), "alg_bytes": pro_bytes}}
 
 
 def bench_attn_decode(args, torch, lt, synth):

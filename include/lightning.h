@@ -363,8 +363,8 @@ lt_status lightning_attn_prefill(const void* q, const void* k, const void* v, co
  *   y             : device [B][Hq][d] bf16;  o_raw : device fp32 [B][Hq][d] or NULL.
  *   workspace     : at least lightning_attn_decode_workspace_size(B, Hq, Hkv, d, dtype,
  *                   max_b lengths[b]) bytes, 256-byte aligned (per-split partial results).
- * Other arguments as for lightning_attn_prefill.  Supported: d = 128, bf16, B <= 64,
- * Hq / Hkv in {1, 2, 4, 8}.  A step after lightning_attn_prefill(T) (cache filled through
+ * Other arguments as for lightning_attn_prefill.  Supported: d = 128, bf16, B <= 64 (the lengths
+ * travel by value; lightning_attn_decode_step_dev below takes any B), Hq / Hkv in {1, 2, 4, 8}.  A step after lightning_attn_prefill(T) (cache filled through
  * key_cache_out and the caller's values) with lengths = T equals row T of the prefill of T + 1
  * tokens.
  */
@@ -379,6 +379,32 @@ lt_status lightning_attn_decode_step(const void* q, const void* k_new, const voi
                                      void* v_cache, int64_t cache_capacity, void* y,
                                      float* o_raw, int B, int Hq, int Hkv, int d, int dtype,
                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * lightning_attn_decode_step with the lengths in device memory, so that a serving loop can keep
+ * them on the GPU (advance them with its own kernel, capture the step in a graph) with no host
+ * round trip per step.  The same step as above (Appendix A, Eq. 17; Section 5.1, Eq. 11); the
+ * arguments are the same except:
+ *   lengths    : DEVICE int64 [B] (8-byte aligned), read by the step's kernels (stream-ordered):
+ *                row b's cached tokens, the new token's position.
+ *   max_length : host bound, 0 <= max_length < cache_capacity, on every lengths[b]; it sizes the
+ *                grid and the workspace (lightning_attn_decode_workspace_size(..., max_length)),
+ *                so a tight bound saves launch work, not bandwidth.
+ *   B          : any positive count (no 64-row limit).
+ * A row whose lengths[b] lies outside [0, max_length] (which the host cannot check) is not
+ * computed: its caches are left unwritten and its y (and o_raw) rows are filled with NaN.
+ * Errors: LT_ERR_INVALID_ARG for a null or misaligned lengths pointer or a max_length out of
+ * range; otherwise as lightning_attn_decode_step.
+ */
+lt_status lightning_attn_decode_step_dev(const void* q, const void* k_new, const void* v_new,
+                                         const void* gate, const float* q_norm_w,
+                                         const float* k_norm_w, const float* o_norm_w,
+                                         int norm_w_head_stride, double logit_scale_base,
+                                         double rms_eps, const int64_t* lengths,
+                                         int64_t max_length, void* k_cache, void* v_cache,
+                                         int64_t cache_capacity, void* y, float* o_raw, int B,
+                                         int Hq, int Hkv, int d, int dtype, void* workspace,
+                                         size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

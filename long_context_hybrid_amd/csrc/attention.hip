@@ -4,7 +4,7 @@
 // RMSNorm of Eq. 14.
 //
 // Prefill runs two kernels:
-//   1. attn_prologue_kernel: one wavefront per (token, head) row writes
+//   1. attn_prologue_kernel: 16 lanes per (token, head) row (16-byte accesses) write
 //        q~ = bf16( s_t log2(e) / sqrt(d) * Norm(q) w_q )      (Norm only with QK-norm weights)
 //        k^ = bf16( Norm(k) w_k )            (with key norm weights, or to fill a key cache)
 //      so the score of the main loop is already in log2 units and softmax uses bare exp2.
@@ -28,6 +28,7 @@
 // dispatched to the 8 XCDs round-robin), heaviest causal tiles first, so the workgroups that
 // stream the same keys and values share that XCD's L2.
 #include <math.h>
+#include <algorithm>
 #include <stdint.h>
 #include <string.h>
 
@@ -51,40 +52,75 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+__device__ __forceinline__ void widen8(uint4 x, float* f) {
+    f[0] = bf16_lo(x.x); f[1] = bf16_hi(x.x); f[2] = bf16_lo(x.y); f[3] = bf16_hi(x.y);
+    f[4] = bf16_lo(x.z); f[5] = bf16_hi(x.z); f[6] = bf16_lo(x.w); f[7] = bf16_hi(x.w);
+}
+
 // ---- 1. prologue ------------------------------------------------------------------------------
-// Rows 0 .. B T Hq - 1 are queries, the rest (when keys are written) keys.  Lane i holds
-// features 2i and 2i + 1.
+// Rows 0 .. B T Hq - 1 are queries, the rest (when keys are written) keys.  A 16-lane group
+// handles one row, lane s the features 8 s .. 8 s + 7 (one 16-byte load and store); a
+// workgroup takes kPrologueRows consecutive rows per pass, each thread four of them with their
+// loads issued together, and strides over the rows by the grid.  The logits scale of the
+// pass's 64 rows (fp64 logarithm) is computed once, lane l of every wavefront for row l, and
+// handed to the row's group by a lane shuffle.
+constexpr int kPrologueRows = 64;
+
 __global__ void __launch_bounds__(256) attn_prologue_kernel(const AttnParams p) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, sl = threadIdx.x & 15, grp = threadIdx.x >> 4;
     const int64_t nq = (int64_t)p.B * p.T * p.Hq;
-    const int64_t nk = p.write_keys ? (int64_t)p.B * p.T * p.Hkv : 0;
-    if (row >= nq + nk) return;
-    const bool is_q = row < nq;
-    const int64_t r = is_q ? row : row - nq;
-    const int H = is_q ? p.Hq : p.Hkv;
-    const int h = (int)(r % H);
-    const int64_t t = (r / H) % p.T;
-    const uint16_t* src = static_cast<const uint16_t*>(is_q ? p.q : p.k) + r * kD;
-    const uint32_t x2 = reinterpret_cast<const uint32_t*>(src)[lane];
-    float a = bf16_lo(x2), b = bf16_hi(x2);
-    const float* w = is_q ? p.qw : p.kw;
-    if (w) {
-        const float ss = wave_sum(a * a + b * b);
-        const float rinv = 1.0f / sqrtf(ss * (1.0f / kD) + p.eps);
-        const float* wh = w + (size_t)h * p.w_stride;
-        a *= rinv * wh[2 * lane];
-        b *= rinv * wh[2 * lane + 1];
+    const int64_t total = nq + (p.write_keys ? (int64_t)p.B * p.T * p.Hkv : 0);
+    const float base_scale = kLog2e / sqrtf((float)kD);
+    for (int64_t base = (int64_t)blockIdx.x * kPrologueRows; base < total;
+         base += (int64_t)gridDim.x * kPrologueRows) {
+        uint4 x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t row = min(base + grp + 16 * u, total - 1);
+            const bool is_q = row < nq;
+            const uint16_t* src = static_cast<const uint16_t*>(is_q ? p.q : p.k) +
+                                  (is_q ? row : row - nq) * kD + 8 * sl;
+            x[u] = *reinterpret_cast<const uint4*>(src);
+        }
+        // s_t log2(e) / sqrt(d) of row base + lane (queries), s_t = ln(p + a) / ln(a)
+        float lane_scale = base_scale;
+        if (p.log_a != 0.0 && base + lane < nq) {
+            const int64_t t = ((base + lane) / p.Hq) % p.T;
+            lane_scale *= (float)(log((double)(p.pos0 + t) + p.a) / p.log_a);
+        }
+        float row_scale[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) row_scale[u] = __shfl(lane_scale, grp + 16 * u);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t row = base + grp + 16 * u;
+            if (row >= total) break;  // uniform per 16-lane group
+            const bool is_q = row < nq;
+            const int64_t r = is_q ? row : row - nq;
+            float f[8];
+            widen8(x[u], f);
+            float scale = is_q ? row_scale[u] : 1.0f;
+            const float* w = is_q ? p.qw : p.kw;
+            if (w) {
+                float ss = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+                ss = group_sum<16>(ss);
+                scale *= 1.0f / sqrtf(ss * (1.0f / kD) + p.eps);
+                const int h = p.w_stride ? (int)(r % (is_q ? p.Hq : p.Hkv)) : 0;
+                const float4* wh = reinterpret_cast<const float4*>(w + (size_t)h * p.w_stride + 8 * sl);
+                const float4 w0 = wh[0], w1 = wh[1];
+                f[0] *= scale * w0.x; f[1] *= scale * w0.y; f[2] *= scale * w0.z; f[3] *= scale * w0.w;
+                f[4] *= scale * w1.x; f[5] *= scale * w1.y; f[6] *= scale * w1.z; f[7] *= scale * w1.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f[e] *= scale;
+            }
+            uint16_t* dst = static_cast<uint16_t*>(is_q ? p.qs : p.ks) + r * kD + 8 * sl;
+            *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                                                        pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+        }
     }
-    if (is_q) {
-        // s_t log2(e) / sqrt(d), with s_t = ln(p + a) / ln(a) evaluated in fp64 once per row
-        float scale = kLog2e / sqrtf((float)kD);
-        if (p.log_a != 0.0) scale *= (float)(log((double)(p.pos0 + t) + p.a) / p.log_a);
-        a *= scale;
-        b *= scale;
-    }
-    uint16_t* dst = static_cast<uint16_t*>(is_q ? p.qs : p.ks) + r * kD;
-    reinterpret_cast<uint32_t*>(dst)[lane] = pack_bf16x2(a, b);
 }
 
 // ---- 2. flash attention -------------------------------------------------------------------------
@@ -421,14 +457,25 @@ hipError_t launch_fwd(const AttnParams& p, hipStream_t stream) {
 //     into one partial (unnormalised o, max, sum in log2 units) per head and split;
 // (c) attn_decode_combine_kernel: one workgroup per (b, h) merges the splits and applies the
 //     output norm and gate.
+// A row's length comes from the host (by value) or from device memory; a device length outside
+// [0, min(max_length, capacity - 1)] marks the row invalid: its caches are not written and its
+// y (and o_raw) are filled with NaN.
+
+// the row's length, or -1 when it is out of range
+__device__ __forceinline__ int64_t row_length(const AttnDecodeParams& p, int b) {
+    const int64_t n = p.lengths_dev ? p.lengths_dev[b] : p.lengths[b];
+    return (n >= 0 && n <= p.max_length && n < p.Tmax) ? n : -1;
+}
 
 __global__ void __launch_bounds__(256) attn_append_kernel(const AttnDecodeParams p) {
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // b Hkv + kvh
     if (row >= p.B * p.Hkv) return;
     const int b = row / p.Hkv, kvh = row - b * p.Hkv;
+    const int64_t len = row_length(p, b);
+    if (len < 0) return;
     const size_t src = (size_t)row * kD;
-    const size_t dst = (((size_t)b * p.Tmax + p.lengths[b]) * p.Hkv + kvh) * kD;
+    const size_t dst = (((size_t)b * p.Tmax + len) * p.Hkv + kvh) * kD;
     const uint32_t k2 = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.k_new) + src)[lane];
     float a = bf16_lo(k2), c = bf16_hi(k2);
     if (p.kw) {
@@ -443,11 +490,6 @@ __global__ void __launch_bounds__(256) attn_append_kernel(const AttnDecodeParams
         reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.v_new) + src)[lane];
 }
 
-__device__ __forceinline__ void widen8(uint4 x, float* f) {
-    f[0] = bf16_lo(x.x); f[1] = bf16_hi(x.x); f[2] = bf16_lo(x.y); f[3] = bf16_hi(x.y);
-    f[4] = bf16_lo(x.z); f[5] = bf16_hi(x.z); f[6] = bf16_lo(x.w); f[7] = bf16_hi(x.w);
-}
-
 template <int GRP>  // query heads per key/value head
 __global__ void __launch_bounds__(256) attn_decode_partial_kernel(const AttnDecodeParams p) {
     constexpr int U = 4;          // keys in flight per 16-lane group
@@ -458,7 +500,9 @@ __global__ void __launch_bounds__(256) attn_decode_partial_kernel(const AttnDeco
     const int split = blockIdx.x % p.n_split;
     const int row = blockIdx.x / p.n_split;  // b Hkv + kvh
     const int b = row / p.Hkv, kvh = row - b * p.Hkv;
-    const int64_t n_keys = p.lengths[b] + 1;  // cached keys plus the new one
+    const int64_t len = row_length(p, b);
+    if (len < 0) return;  // whole workgroup: an invalid row
+    const int64_t n_keys = len + 1;  // cached keys plus the new one
     const int64_t k_begin = (int64_t)split * kAttnDecodeChunk;
     if (k_begin >= n_keys) return;  // whole workgroup: this row has fewer splits
     const int64_t k_end = min(n_keys, k_begin + kAttnDecodeChunk);
@@ -466,7 +510,7 @@ __global__ void __launch_bounds__(256) attn_decode_partial_kernel(const AttnDeco
     // this lane's 8 features of every query head of the group, normalised, scaled by
     // s log2(e) / sqrt(d) and packed to bf16 pairs for v_dot2c_f32_bf16
     const float pos_scale = p.log_a != 0.0
-        ? (float)(log((double)p.lengths[b] + p.a) / p.log_a) : 1.0f;
+        ? (float)(log((double)len + p.a) / p.log_a) : 1.0f;
     bf16x2_t qb[GRP][4];
 #pragma unroll
     for (int hh = 0; hh < GRP; ++hh) {
@@ -600,7 +644,16 @@ __global__ void __launch_bounds__(1024) attn_decode_combine_kernel(const AttnDec
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int row = blockIdx.x;  // b Hq + h
     const int b = row / p.Hq, h = row - b * p.Hq;
-    const int n_split = (int)((p.lengths[b] + kAttnDecodeChunk) / kAttnDecodeChunk);
+    const int64_t len = row_length(p, b);
+    if (len < 0) {  // whole workgroup: NaN output for an invalid row
+        if (wv == 0) {
+            const size_t off = (size_t)row * kD + 2 * lane;
+            reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.y) + off)[0] = 0x7fc07fc0u;
+            if (p.o_raw) p.o_raw[off] = p.o_raw[off + 1] = __builtin_nanf("");
+        }
+        return;
+    }
+    const int n_split = (int)((len + kAttnDecodeChunk) / kAttnDecodeChunk);
     const float* part = p.part + (size_t)row * p.n_split * (kD + 2);
     float M = -INFINITY, L = 0.0f, o0 = 0.0f, o1 = 0.0f;
     for (int s0 = wv; s0 < n_split; s0 += 4 * NWV) {
@@ -701,7 +754,8 @@ hipError_t launch_attn_prefill(const AttnParams& p, const hipEvent_t events[2],
     if (const hipError_t g = launch_gate(); g != hipSuccess) return g;
     const long long rows =
         (long long)p.B * p.T * p.Hq + (p.write_keys ? (long long)p.B * p.T * p.Hkv : 0);
-    attn_prologue_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream>>>(p);
+    const long long blocks = std::min((rows + kPrologueRows - 1) / kPrologueRows, 1LL << 20);
+    attn_prologue_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (events[0] && (e = hipEventRecord(events[0], stream)) != hipSuccess) return e;
@@ -816,16 +870,24 @@ size_t lightning_attn_decode_workspace_size(int B, int Hq, int Hkv, int d, int d
     return round256((size_t)B * Hq * n_split * (lt::kAttnHeadDim + 2) * sizeof(float));
 }
 
-lt_status lightning_attn_decode_step(const void* q, const void* k_new, const void* v_new,
-                                     const void* gate, const float* q_norm_w,
-                                     const float* k_norm_w, const float* o_norm_w,
-                                     int norm_w_head_stride, double logit_scale_base,
-                                     double rms_eps, const int64_t* lengths, void* k_cache,
-                                     void* v_cache, int64_t cache_capacity, void* y,
-                                     float* o_raw, int B, int Hq, int Hkv, int d, int dtype,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The decode step's checks and launch, for lengths given on the host (lengths_host, validated
+// here) or in device memory (lengths_dev, bounded by max_len and checked by the kernels).
+lt_status attn_decode(const void* q, const void* k_new, const void* v_new, const void* gate,
+                      const float* q_norm_w, const float* k_norm_w, const float* o_norm_w,
+                      int norm_w_head_stride, double logit_scale_base, double rms_eps,
+                      const int64_t* lengths_host, const int64_t* lengths_dev, int64_t max_len,
+                      void* k_cache, void* v_cache, int64_t cache_capacity, void* y,
+                      float* o_raw, int B, int Hq, int Hkv, int d, int dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
     if (!ok_ptr(q) || !ok_ptr(k_new) || !ok_ptr(v_new) || !ok_ptr(gate) || !ok_ptr(y) ||
-        !ok_ptr(k_cache) || !ok_ptr(v_cache) || lengths == nullptr)
+        !ok_ptr(k_cache) || !ok_ptr(v_cache))
+        return LT_ERR_INVALID_ARG;
+    if (lengths_host == nullptr &&
+        (lengths_dev == nullptr || (reinterpret_cast<uintptr_t>(lengths_dev) & 7u) != 0))
         return LT_ERR_INVALID_ARG;
     if (!ok_opt(q_norm_w) || !ok_opt(k_norm_w) || !ok_opt(o_norm_w) || !ok_opt(o_raw))
         return LT_ERR_INVALID_ARG;
@@ -836,14 +898,20 @@ lt_status lightning_attn_decode_step(const void* q, const void* k_new, const voi
     if (cache_capacity <= 0) return LT_ERR_INVALID_ARG;
     lt_status st = attn_shape(B, 1, Hq, Hkv, d, dtype);
     if (st != LT_OK) return st;
-    if (B > lt::kAttnDecodeMaxB || Hq / Hkv > lt::kAttnMaxGroup || (Hq / Hkv & (Hq / Hkv - 1)))
-        return LT_ERR_UNSUPPORTED;
-    int64_t max_len = 0;
-    for (int b = 0; b < B; ++b) {
-        if (lengths[b] < 0 || lengths[b] >= cache_capacity) return LT_ERR_INVALID_ARG;
-        max_len = lengths[b] > max_len ? lengths[b] : max_len;
+    if (Hq / Hkv > lt::kAttnMaxGroup || (Hq / Hkv & (Hq / Hkv - 1))) return LT_ERR_UNSUPPORTED;
+    if (lengths_host) {
+        if (B > lt::kAttnDecodeMaxB) return LT_ERR_UNSUPPORTED;
+        max_len = 0;
+        for (int b = 0; b < B; ++b) {
+            if (lengths_host[b] < 0 || lengths_host[b] >= cache_capacity) return LT_ERR_INVALID_ARG;
+            max_len = lengths_host[b] > max_len ? lengths_host[b] : max_len;
+        }
+    } else if (max_len < 0 || max_len >= cache_capacity) {
+        return LT_ERR_INVALID_ARG;
     }
     if ((double)B * cache_capacity * Hkv * d > 4.0e15) return LT_ERR_UNSUPPORTED;
+    const int64_t n_split = max_len / lt::kAttnDecodeChunk + 1;
+    if ((double)B * Hkv * n_split > 2.0e9 || (double)B * Hq > 2.0e9) return LT_ERR_UNSUPPORTED;
     const size_t need = lightning_attn_decode_workspace_size(B, Hq, Hkv, d, dtype, max_len);
     if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
         workspace_bytes < need)
@@ -857,15 +925,54 @@ lt_status lightning_attn_decode_step(const void* q, const void* k_new, const voi
     p.y = y; p.o_raw = o_raw;
     p.part = static_cast<float*>(workspace);
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.w_stride = norm_w_head_stride;
-    p.n_split = (int)(max_len / lt::kAttnDecodeChunk + 1);
+    p.n_split = (int)n_split;
     p.Tmax = cache_capacity;
+    p.max_length = max_len;
     p.eps = (float)rms_eps;
     p.a = logit_scale_base;
     p.log_a = logit_scale_base == 0.0 ? 0.0 : log(logit_scale_base);
-    for (int b = 0; b < B; ++b) p.lengths[b] = lengths[b];
+    if (lengths_host) {
+        for (int b = 0; b < B; ++b) p.lengths[b] = lengths_host[b];
+    } else {
+        p.lengths_dev = lengths_dev;
+    }
     if (lt::launch_attn_decode(p, static_cast<hipStream_t>(stream)) != hipSuccess)
         return LT_ERR_HIP;
     return LT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lt_status lightning_attn_decode_step(const void* q, const void* k_new, const void* v_new,
+                                     const void* gate, const float* q_norm_w,
+                                     const float* k_norm_w, const float* o_norm_w,
+                                     int norm_w_head_stride, double logit_scale_base,
+                                     double rms_eps, const int64_t* lengths, void* k_cache,
+                                     void* v_cache, int64_t cache_capacity, void* y,
+                                     float* o_raw, int B, int Hq, int Hkv, int d, int dtype,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+    if (lengths == nullptr) return LT_ERR_INVALID_ARG;
+    return attn_decode(q, k_new, v_new, gate, q_norm_w, k_norm_w, o_norm_w, norm_w_head_stride,
+                       logit_scale_base, rms_eps, lengths, nullptr, 0, k_cache, v_cache,
+                       cache_capacity, y, o_raw, B, Hq, Hkv, d, dtype, workspace,
+                       workspace_bytes, stream);
+}
+
+lt_status lightning_attn_decode_step_dev(const void* q, const void* k_new, const void* v_new,
+                                         const void* gate, const float* q_norm_w,
+                                         const float* k_norm_w, const float* o_norm_w,
+                                         int norm_w_head_stride, double logit_scale_base,
+                                         double rms_eps, const int64_t* lengths,
+                                         int64_t max_length, void* k_cache, void* v_cache,
+                                         int64_t cache_capacity, void* y, float* o_raw, int B,
+                                         int Hq, int Hkv, int d, int dtype, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+    return attn_decode(q, k_new, v_new, gate, q_norm_w, k_norm_w, o_norm_w, norm_w_head_stride,
+                       logit_scale_base, rms_eps, nullptr, lengths, max_length, k_cache, v_cache,
+                       cache_capacity, y, o_raw, B, Hq, Hkv, d, dtype, workspace,
+                       workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -172,11 +172,15 @@ struct AttnDecodeParams {
     float* part;          // [B][Hq][n_split][d + 2]: per-split o (unnormalised), max, sum
     int B, Hq, Hkv, w_stride, n_split;
     int64_t Tmax;
+    int64_t max_length;   // bound on every row's length; the grid has n_split splits for it
     float eps;
     double a, log_a;
-    int64_t lengths[64];  // per batch row: cached tokens = position of the new token
+    // per batch row: cached tokens = position of the new token.  From device memory when
+    // lengths_dev is set (any B), else by value (B <= kAttnDecodeMaxB).
+    const int64_t* lengths_dev;
+    int64_t lengths[64];
 };
-constexpr int kAttnDecodeMaxB = 64;  // batch rows of one decode call (lengths travel by value)
+constexpr int kAttnDecodeMaxB = 64;  // batch rows of a call whose lengths travel by value
 
 // events[0] / events[1] (may be null) are recorded just before / after the main chunk kernel.
 // time_dep: the data-dependent-decay kernels (cp.log2_decay / dp.log2_decay set).

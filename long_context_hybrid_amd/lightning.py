@@ -44,6 +44,7 @@ EXPORTS = (
     "lightning_attn_prefill",
     "lightning_attn_decode_workspace_size",
     "lightning_attn_decode_step",
+    "lightning_attn_decode_step_dev",
 )
 
 
@@ -127,6 +128,10 @@ def _load() -> ct.CDLL:
     h.lightning_attn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, f64, f64, vp, vp,
                                              vp, i64, vp, vp, i32, i32, i32, i32, i32, vp, sz, vp]
     h.lightning_attn_decode_step.restype = i32
+    h.lightning_attn_decode_step_dev.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, f64, f64, vp,
+                                                 i64, vp, vp, i64, vp, vp, i32, i32, i32, i32,
+                                                 i32, vp, sz, vp]
+    h.lightning_attn_decode_step_dev.restype = i32
     return h
 
 
@@ -472,10 +477,14 @@ def lightning_attn_decode_workspace_size(B, Hq, Hkv, d, max_length, dtype=torch.
 
 def lightning_attn_decode_step(q, k_new, v_new, gate, k_cache, v_cache, lengths,
                                logit_scale_base, q_norm_w=None, k_norm_w=None, o_norm_w=None,
-                               rms_eps=1e-6, y=None, o_raw=None, workspace=None, stream=None):
+                               rms_eps=1e-6, y=None, o_raw=None, workspace=None, stream=None,
+                               max_length=None):
     """One decode step: q, gate [B, Hq, d], k_new, v_new [B, Hkv, d], caches
-    [B, capacity, Hkv, d] (bf16); ``lengths``: a sequence of B ints (host).  The new token's key
-    and value are written into row lengths[b] of the caches.  Returns ``y``."""
+    [B, capacity, Hkv, d] (bf16).  ``lengths``: a sequence of B ints (host;
+    lightning_attn_decode_step), or an int64 CUDA tensor [B] read by the kernels
+    (lightning_attn_decode_step_dev), whose values must not exceed ``max_length`` (default
+    capacity - 1).  The new token's key and value are written into row lengths[b] of the
+    caches.  Returns ``y``."""
     B, Hq, d = q.shape
     Hkv = k_new.shape[1]
     cap = k_cache.shape[1]
@@ -483,9 +492,15 @@ def lightning_attn_decode_step(q, k_new, v_new, gate, k_cache, v_cache, lengths,
     dt = _dtype_code(q.dtype)
     given = [w for w in (q_norm_w, k_norm_w, o_norm_w) if w is not None]
     stride = 0 if all(w.dim() == 1 for w in given) else d
-    lens = [int(x) for x in lengths]
-    if len(lens) != B:
-        raise ValueError(f"need one length per batch row ({B})")
+    on_device = isinstance(lengths, torch.Tensor) and lengths.is_cuda
+    if on_device:
+        lp = _dev(lengths, "lengths", torch.int64, (B,), dev)
+        bound = cap - 1 if max_length is None else int(max_length)
+    else:
+        lens = [int(x) for x in lengths]
+        if len(lens) != B:
+            raise ValueError(f"need one length per batch row ({B})")
+        bound = max(lens) if lens else 0
     ptrs = [_dev(q, "q", q.dtype, (B, Hq, d), dev), _dev(k_new, "k_new", q.dtype, (B, Hkv, d), dev),
             _dev(v_new, "v_new", q.dtype, (B, Hkv, d), dev),
             _dev(gate, "gate", q.dtype, (B, Hq, d), dev)]
@@ -498,8 +513,14 @@ def lightning_attn_decode_step(q, k_new, v_new, gate, k_cache, v_cache, lengths,
         y = torch.empty_like(q)
     yp = _dev(y, "y", q.dtype, q.shape, dev)
     orp = _dev(o_raw, "o_raw", torch.float32, q.shape, dev)
-    need = lightning_attn_decode_workspace_size(B, Hq, Hkv, d, max(lens) if lens else 0, q.dtype)
+    need = lightning_attn_decode_workspace_size(B, Hq, Hkv, d, max(bound, 0), q.dtype)
     workspace, wsp, wbytes = _workspace(workspace, need, dev)
+    if on_device:
+        st = lib.lightning_attn_decode_step_dev(
+            *ptrs, wq, wk, wo, stride, float(logit_scale_base or 0.0), float(rms_eps), lp, bound,
+            kcp, vcp, cap, yp, orp, B, Hq, Hkv, d, dt, wsp, wbytes, _stream(stream, dev))
+        _check(st, "lightning_attn_decode_step_dev")
+        return y
     st = lib.lightning_attn_decode_step(*ptrs, wq, wk, wo, stride, float(logit_scale_base or 0.0),
                                         float(rms_eps), (ct.c_int64 * B)(*lens), kcp, vcp, cap,
                                         yp, orp, B, Hq, Hkv, d, dt, wsp, wbytes,

@@ -421,6 +421,60 @@ def test_attn_prefill_rejects(name, over, status):
     assert st == status
 
 
+def _attn_decode_call(dev_lengths, **over):
+    B = over.get("B", 2)
+    lens = (ct.c_int64 * B)(*([3] * B))
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, g=FAKE, qw=FAKE, kw=FAKE, ow=None, stride=0, a=500.0,
+             eps=1e-6, lengths=FAKE if dev_lengths else lens, maxlen=100, kc=FAKE, vc=FAKE,
+             cap=4096, y=FAKE, oraw=None, B=B, Hq=4, Hkv=2, d=128, dt=lt.LT_BF16, ws=FAKE * 16,
+             wsb=1 << 40, stream=None)
+    a.update(over)
+    head = (a["q"], a["kn"], a["vn"], a["g"], a["qw"], a["kw"], a["ow"], a["stride"], a["a"],
+            a["eps"], a["lengths"])
+    tail = (a["kc"], a["vc"], a["cap"], a["y"], a["oraw"], a["B"], a["Hq"], a["Hkv"], a["d"],
+            a["dt"], a["ws"], a["wsb"], a["stream"])
+    if dev_lengths:
+        return lt.lib.lightning_attn_decode_step_dev(*head, a["maxlen"], *tail)
+    return lt.lib.lightning_attn_decode_step(*head, *tail)
+
+
+ATTN_DECODE_BAD = [
+    # (label, device lengths?, overrides, status)
+    ("null_lengths", False, dict(lengths=None), lt.LT_ERR_INVALID_ARG),
+    ("length_negative", False, dict(lengths=(ct.c_int64 * 2)(3, -1)), lt.LT_ERR_INVALID_ARG),
+    ("length_at_capacity", False, dict(lengths=(ct.c_int64 * 2)(4096, 0)), lt.LT_ERR_INVALID_ARG),
+    ("host_lengths_b65", False, dict(B=65), lt.LT_ERR_UNSUPPORTED),
+    ("group_3", False, dict(Hq=6, Hkv=2), lt.LT_ERR_UNSUPPORTED),
+    ("group_16", False, dict(Hq=16, Hkv=1), lt.LT_ERR_UNSUPPORTED),
+    ("zero_capacity", False, dict(cap=0), lt.LT_ERR_INVALID_ARG),
+    ("null_v_cache", False, dict(vc=None), lt.LT_ERR_INVALID_ARG),
+    ("workspace_small", False, dict(wsb=256), lt.LT_ERR_WORKSPACE),
+    ("dev_null_lengths", True, dict(lengths=None), lt.LT_ERR_INVALID_ARG),
+    ("dev_lengths_misaligned", True, dict(lengths=FAKE + 4), lt.LT_ERR_INVALID_ARG),
+    ("dev_max_length_negative", True, dict(maxlen=-1), lt.LT_ERR_INVALID_ARG),
+    ("dev_max_length_at_capacity", True, dict(maxlen=4096), lt.LT_ERR_INVALID_ARG),
+    ("dev_group_3", True, dict(Hq=6, Hkv=2), lt.LT_ERR_UNSUPPORTED),
+    ("dev_workspace_small", True, dict(wsb=256), lt.LT_ERR_WORKSPACE),
+    # valid arguments (B beyond the host path's 64 rows, 8-byte aligned lengths): validation
+    # passes and the launch fails for want of a device
+    ("dev_b100_passes_validation", True, dict(B=100, lengths=FAKE + 8), lt.LT_ERR_HIP),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,dev_lengths,over,status", ATTN_DECODE_BAD,
+                         ids=[c[0] for c in ATTN_DECODE_BAD])
+def test_attn_decode_rejects(name, dev_lengths, over, status):
+    assert _attn_decode_call(dev_lengths, **over) == status
+
+
+def test_attn_decode_workspace_follows_the_bound():
+    one = lt.lightning_attn_decode_workspace_size(3, 8, 2, 128, 2047)
+    two = lt.lightning_attn_decode_workspace_size(3, 8, 2, 128, 2048)
+    assert one == 3 * 8 * 1 * 130 * 4 // 256 * 256 + 256 and two > one
+    assert lt.lightning_attn_decode_workspace_size(3, 8, 2, 128, -1) == 0
+
+
 # ---- data-dependent decay -------------------------------------------------------------------------
 
 def test_dd_workspace_adds_subsegment_decays():

@@ -237,3 +237,119 @@ def test_attn_prefill_then_decode():
     torch.cuda.synchronize()
     for h in range(Hq):
         assert rel_l2(y[0, h].float().cpu().numpy(), ref["y"][0, 0, h]) <= TOL
+
+
+# ---- decode with the lengths in device memory ------------------------------------------------------
+
+def _run_decode_dev(inp, a, max_length=None, lengths=None):
+    import long_context_hybrid_amd.lightning as lt
+
+    dev = torch.device("cuda")
+    kc, vc = inp["k_cache"].to(dev), inp["v_cache"].to(dev)
+    o_raw = torch.empty(inp["q"].shape, dtype=torch.float32, device=dev)
+    lens = torch.tensor(inp["lengths"] if lengths is None else lengths, dtype=torch.int64,
+                        device=dev)
+    y = lt.lightning_attn_decode_step(
+        inp["q"].to(dev), inp["k_new"].to(dev), inp["v_new"].to(dev), inp["g"].to(dev), kc, vc,
+        lens, a, q_norm_w=None if inp["qw"] is None else inp["qw"].to(dev),
+        k_norm_w=None if inp["kw"] is None else inp["kw"].to(dev), o_raw=o_raw,
+        max_length=max_length)
+    torch.cuda.synchronize()
+    return y.float().cpu(), o_raw.cpu(), kc, vc
+
+
+@pytest.mark.parametrize("case", DECODE, ids=[c[0] for c in DECODE])
+def test_attn_decode_device_lengths_match_host(case):
+    """The device-lengths entry point runs the same kernels: with the bound at capacity - 1
+    (most splits of the short rows exit at once) y, o and both caches equal the host-lengths
+    call bit for bit, and the oracle."""
+    label, B, Hq, Hkv, cap, lengths, a, norm = case
+    inp = _decode_inputs(B, Hq, Hkv, cap, lengths, seed=len(label), qk_norm=norm)
+    host = _run_decode(inp, a)
+    devr = _run_decode_dev(inp, a)
+    for x, y in zip(host, devr):
+        assert torch.equal(x, y), label
+    _check_decode(inp, a, label + " (device lengths)", *devr)
+
+
+def test_attn_decode_device_lengths_large_batch():
+    """B = 80, more rows than host lengths allow, lengths from 0 across a split boundary."""
+    B, Hq, Hkv, cap = 80, 4, 2, 2100
+    lengths = [(i * 523) % 2100 for i in range(B)]
+    assert 0 in lengths and max(lengths) >= 2048
+    inp = _decode_inputs(B, Hq, Hkv, cap, lengths, seed=80)
+    _check_decode(inp, 500.0, "B=80 device lengths",
+                  *_run_decode_dev(inp, 500.0, max_length=max(lengths)))
+
+
+def test_attn_decode_device_lengths_invalid_rows():
+    """Rows whose device length is negative or above max_length get NaN outputs and no cache
+    write; the other rows are computed as usual."""
+    B, Hq, Hkv, cap = 4, 4, 2, 3000
+    good = [17, 2500, 0, 900]
+    bad = [17, 2999, -5, 900]  # row 1 above the bound 2600, row 2 negative
+    inp = _decode_inputs(B, Hq, Hkv, cap, good, seed=5)
+    y, o, kc, vc = _run_decode_dev(inp, 500.0, max_length=2600, lengths=bad)
+    for b in (1, 2):
+        assert torch.isnan(y[b]).all() and torch.isnan(o[b]).all()
+        assert torch.equal(kc[b].cpu(), inp["k_cache"][b])
+        assert torch.equal(vc[b].cpu(), inp["v_cache"][b])
+    ref_y, ref_o, ref_kc, ref_vc = _run_decode(inp, 500.0)
+    for b in (0, 3):
+        assert torch.equal(y[b], ref_y[b]) and torch.equal(o[b], ref_o[b])
+        assert torch.equal(kc[b], ref_kc[b]) and torch.equal(vc[b], ref_vc[b])
+
+
+def test_attn_decode_device_lengths_graph_loop():
+    """A decode loop captured once in a HIP graph: each replay appends one token at the lengths
+    held on the GPU, which the loop advances on the device between replays.  Every replay's y and
+    the final caches equal eager host-lengths steps with the same inputs."""
+    import long_context_hybrid_amd.lightning as lt
+
+    dev = torch.device("cuda")
+    B, Hq, Hkv, cap, steps = 3, 8, 2, 4200, 4
+    start = [2046, 5, 300]  # row 0 crosses the split boundary at 2048
+    inp = _decode_inputs(B, Hq, Hkv, cap, start, seed=31)
+    gen = torch.Generator().manual_seed(32)
+    news = [{n: torch.randn(B, h, 128, generator=gen).to(torch.bfloat16)
+             for n, h in (("q", Hq), ("k_new", Hkv), ("v_new", Hkv), ("g", Hq))}
+            for _ in range(steps)]
+    qw, kw = inp["qw"].to(dev), inp["kw"].to(dev)
+    # eager reference: host lengths, one step after another on its own caches
+    kc_ref, vc_ref = inp["k_cache"].to(dev), inp["v_cache"].to(dev)
+    ys_ref = []
+    for s in range(steps):
+        x = {n: news[s][n].to(dev) for n in news[s]}
+        y = lt.lightning_attn_decode_step(x["q"], x["k_new"], x["v_new"], x["g"], kc_ref, vc_ref,
+                                          [L + s for L in start], 500.0, q_norm_w=qw, k_norm_w=kw)
+        ys_ref.append(y.clone())
+    # the graph: static inputs, device lengths, a workspace sized for the bound
+    kc, vc = inp["k_cache"].to(dev), inp["v_cache"].to(dev)
+    sq = {n: torch.empty_like(news[0][n], device=dev) for n in news[0]}
+    lens = torch.tensor(start, dtype=torch.int64, device=dev)
+    y = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device=dev)
+    bound = cap - 1
+    ws = torch.empty(lt.lightning_attn_decode_workspace_size(B, Hq, Hkv, 128, bound),
+                     dtype=torch.uint8, device=dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        # capture only (no step runs): the caches are written by the replays alone
+        with torch.cuda.graph(graph, stream=side):
+            lt.lightning_attn_decode_step(sq["q"], sq["k_new"], sq["v_new"], sq["g"], kc, vc,
+                                          lens, 500.0, q_norm_w=qw, k_norm_w=kw, y=y,
+                                          workspace=ws, max_length=bound,
+                                          stream=torch.cuda.current_stream())
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for s in range(steps):
+        for n in sq:
+            sq[n].copy_(news[s][n].to(dev))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ys_ref[s]), f"replay {s}"
+        lens += 1
+        torch.cuda.synchronize()
+    assert torch.equal(kc, kc_ref) and torch.equal(vc, vc_ref)
+    assert lens.tolist() == [L + steps for L in start]

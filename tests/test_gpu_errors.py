@@ -278,12 +278,17 @@ def _force_fail_cases():
     y = full(q1.shape, torch.bfloat16)
     cases["attn_decode_step"] = ([y, kc, vc], lambda y=y, kc=kc, vc=vc: lt.lightning_attn_decode_step(
         q1, k1, v1, g1, kc, vc, [3], ain["a"], q_norm_w=ain["qw"], k_norm_w=ain["kw"], y=y))
+    kc, vc = full((1, 16, 2, 128), torch.bfloat16), full((1, 16, 2, 128), torch.bfloat16)
+    y = full(q1.shape, torch.bfloat16)
+    lens = torch.full((1,), 3, dtype=torch.int64, device=dev)
+    cases["attn_decode_step_dev"] = ([y, kc, vc], lambda y=y, kc=kc, vc=vc: lt.lightning_attn_decode_step(
+        q1, k1, v1, g1, kc, vc, lens, ain["a"], q_norm_w=ain["qw"], k_norm_w=ain["kw"], y=y))
     return cases
 
 
 FORCE_FAIL_NAMES = ["state_init", "prefill", "decode_step", "prefill_dd", "decode_step_dd",
                     "prefill_backward", "layer_prefill", "layer_decode_step", "attn_prefill",
-                    "attn_decode_step"]
+                    "attn_decode_step", "attn_decode_step_dev"]
 
 
 @pytest.mark.parametrize("name", FORCE_FAIL_NAMES)
