@@ -30,6 +30,7 @@ import argparse
 import ctypes as ct
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -169,6 +170,26 @@ class HipEvents:
             self.hip.hipEventDestroy(ct.c_void_p(e))
 
 
+def eager_step_stats(torch, step, n, group=10):
+    """Median and minimum step time over n eagerly launched steps, in groups of `group` steps
+    bracketed by HIP events (a step is shorter than its host-side launch plus one event record,
+    so an event per step would time launch gaps).  A separate pass after the timed loop."""
+    hev = HipEvents()
+    ng = max(1, n // group)
+    ev = hev.create(ng + 1)
+    cur = torch.cuda.current_stream()
+    for gi in range(ng):
+        hev.record(ev[gi], cur)
+        for i in range(group):
+            step(gi * group + i)
+    hev.record(ev[ng], cur)
+    torch.cuda.synchronize()
+    per = [hev.elapsed_ms(ev[i], ev[i + 1]) * 1e3 / group for i in range(ng)]
+    hev.destroy(ev)
+    return {"us_median": round(statistics.median(per), 3), "us_min": round(min(per), 3),
+            "groups": ng, "steps_per_group": group}
+
+
 def bench_prefill(args, torch, lt, synth, workload=None, steps=None):
     spec = synth.WORKLOADS[workload or args.workload]
     steps = steps or args.steps
@@ -190,16 +211,23 @@ def bench_prefill(args, torch, lt, synth, workload=None, steps=None):
 
     hev = HipEvents()
     ev = hev.create(2 * steps)
+    call_ev = hev.create(steps + 1)  # before each call, and after the last
+    cur = torch.cuda.current_stream(dev)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(steps):
+        hev.record(call_ev[i], cur)
         lt.lightning_prefill(*call_args, **kw, main_kernel_events=(ev[2 * i], ev[2 * i + 1]))
+    hev.record(call_ev[steps], cur)
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    main_ms = sum(hev.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for i in range(steps)) / steps
+    main_list = [hev.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for i in range(steps)]
+    call_list = [hev.elapsed_ms(call_ev[i], call_ev[i + 1]) for i in range(steps)]
+    main_ms = sum(main_list) / steps
     hev.destroy(ev)
+    hev.destroy(call_ev)
 
     ms_per_step = total_ms / steps
     tokens = B * T
@@ -215,6 +243,10 @@ def bench_prefill(args, torch, lt, synth, workload=None, steps=None):
     return dict(
         spec=spec, inp=inp, chunk=chunk, P=P, ms_per_step=ms_per_step, main_ms=main_ms, steps=steps,
         value=tokens / (ms_per_step * 1e-3),
+        step_stats={"call_ms_median": round(statistics.median(call_list), 4),
+                    "call_ms_min": round(min(call_list), 4),
+                    "main_ms_median": round(statistics.median(main_list), 4),
+                    "main_ms_min": round(min(main_list), 4)},
         roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                   "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                   "traffic": measured_traffic("main", spec.name),
@@ -276,6 +308,7 @@ def bench_decode(args, torch, lt, synth, B=None):
         stop.record()
     torch.cuda.synchronize()
     us = start.elapsed_time(stop) * 1e3 / args.decode_steps
+    stats = None if graph else eager_step_stats(torch, step, args.decode_steps)
     act_bytes = 2
     per_bh = 2 * d * d * 4 + 5 * d * act_bytes
     alg = B * H * per_bh + B * 8
@@ -288,7 +321,7 @@ def bench_decode(args, torch, lt, synth, B=None):
                          "traffic": measured_traffic("decode", name),
                          "kernel": "decode_kernel<ModeBF16,128>", "alg_bytes_per_launch": alg,
                          "bytes_per_bh": per_bh, "workgroups": B * H},
-            "state_buffers": len(states)}
+            "step_stats": stats, "state_buffers": len(states)}
 
 
 def bench_configs(args, torch, lt, synth):
@@ -304,7 +337,8 @@ def bench_configs(args, torch, lt, synth):
                      "chunk": r["chunk"], "segments": r["P"], "steps": steps,
                      "ms_per_step": round(r["ms_per_step"], 4),
                      "value": round(r["value"], 1), "unit": "tokens/s/layer",
-                     "roofline": r["roofline"], "mfma": r["mfma"], "whole_call": r["whole_call"]}
+                     "roofline": r["roofline"], "mfma": r["mfma"], "whole_call": r["whole_call"],
+                     "step_stats": r["step_stats"]}
         del r
         torch.cuda.empty_cache()
     return out
@@ -476,6 +510,7 @@ def bench_layer_decode(args, torch, lt, synth, B=None):
         stop.record()
     torch.cuda.synchronize()
     us = start.elapsed_time(stop) * 1e3 / args.decode_steps
+    stats = None if graph else eager_step_stats(torch, step, args.decode_steps)
     wbytes = (4 * H * d * dm + dm * H * d) * 2
     io = B * dm * 2 * 2 + B * (4 * H * d + H * d) * 2 * 2  # x, out; projections and y written + read
     alg = wbytes + B * H * 2 * d * d * 4 + io + B * 8
@@ -486,7 +521,7 @@ def bench_layer_decode(args, torch, lt, synth, B=None):
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                          "alg_bytes_per_step": alg, "weight_bytes": wbytes},
-            "rotating_sets": nset}
+            "step_stats": stats, "rotating_sets": nset}
 
 
 def bench_attn(args, torch, lt, synth):
@@ -860,6 +895,7 @@ def main():
                    "chunk": pre["chunk"], "segments": pre["P"], "state": "fp32"},
         "roofline": pre["roofline"],
         "mfma": pre["mfma"],
+        "step_stats": pre["step_stats"],
         "whole_call": pre["whole_call"],
         "decode": dec,
         "other_configs": configs,
