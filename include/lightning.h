@@ -242,7 +242,11 @@ lt_status lightning_decode_step_dd(const void* q, const void* k, const void* v,
  *   kernel_events: NULL, or four hipEvent_t recorded around the forward-in-time sweep (dq, dgate)
  *                  ([0], [1]) and the backward-in-time sweep (dk, dv) ([2], [3]).
  * Other arguments as for lightning_prefill.  Outputs may not overlap inputs or each other.
- * Supported: dtype LT_BF16, d = 128 (LT_ERR_UNSUPPORTED otherwise).  Chaining: the backward of
+ * Supported: dtype LT_BF16 or LT_F32, d = 64 or 128 (LT_ERR_UNSUPPORTED otherwise).  The products
+ * take bf16 operands in both cases: fp32 inputs are rounded once to bf16 copies in the workspace
+ * (the size query counts them), and fp32 gradients are written from the fp32 values the kernels
+ * hold, so their precision is the bf16 path's (relative error of a few 1e-3), not fp32's.
+ * Chaining: the backward of
  * prefill(T1) then prefill(T2, state_in = its state_out) is the backward of the second call, whose
  * d_state_in is the first call's d_state_out.
  */

@@ -186,18 +186,19 @@ Plan bwd_plan(int cus, int B, int T, int H, int segments) {
 lt_status bwd_check_shape(int B, int T, int H, int d, int dtype, int segments) {
     if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || segments < 0) return LT_ERR_INVALID_ARG;
     if (dtype != LT_F32 && dtype != LT_BF16) return LT_ERR_INVALID_ARG;
-    if (dtype != LT_BF16 || d != 128 || H > LT_MAX_HEADS) return LT_ERR_UNSUPPORTED;
+    if ((d != 64 && d != 128) || H > LT_MAX_HEADS) return LT_ERR_UNSUPPORTED;
     if ((long long)B * H * (T / lt::kChunk + 1) > 0x7fffffffLL) return LT_ERR_UNSUPPORTED;
     return LT_OK;
 }
 
 // Backward workspace: forward entry states (P > 1) | per-segment state gradients | do (bf16,
-// the activations' layout) | norm-weight partial sums; each part on a 256-byte boundary.
+// the activations' layout) | score tiles | norm-weight partial sums | (fp32 inputs) bf16 copies
+// of q, k, v, g, dy; each part on a 256-byte boundary.
 struct BwdLayout {
-    size_t seg_grad, d_o, scores, wgrad, total;
+    size_t seg_grad, d_o, scores, wgrad, conv, conv_part, total;
 };
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-BwdLayout bwd_layout(int B, int T, int H, int d, const Plan& pl) {
+BwdLayout bwd_layout(int B, int T, int H, int d, int dtype, const Plan& pl) {
     const size_t bh = (size_t)B * H;
     BwdLayout l;
     l.seg_grad = align256(workspace_bytes_for(B, H, d, pl.P, pl.sub));
@@ -206,7 +207,9 @@ BwdLayout bwd_layout(int B, int T, int H, int d, const Plan& pl) {
     const size_t n_chunks = ((size_t)T + pl.C - 1) / pl.C;
     l.scores = align256(l.d_o + (size_t)B * T * H * d * sizeof(uint16_t));
     l.wgrad = align256(l.scores + bh * n_chunks * 2 * pl.C * pl.C * sizeof(float));
-    l.total = l.wgrad + 3 * bh * pl.P * d * sizeof(float);
+    l.conv = align256(l.wgrad + 3 * bh * pl.P * d * sizeof(float));
+    l.conv_part = dtype == LT_F32 ? align256((size_t)B * T * H * d * sizeof(uint16_t)) : 0;
+    l.total = l.conv + 5 * l.conv_part;
     return l;
 }
 
@@ -268,7 +271,7 @@ lt_status lightning_prefill_plan_cus(int num_cus, int B, int T, int H, int d, in
         const Plan bp = bwd_plan(num_cus, B, T, H, segments);
         out->backward_segments = bp.P;
         out->backward_segment_len = bp.P > 1 ? bp.L : T;
-        out->backward_workspace_bytes = bwd_layout(B, T, H, d, bp).total;
+        out->backward_workspace_bytes = bwd_layout(B, T, H, d, dtype, bp).total;
     }
     return LT_OK;
 }
@@ -293,7 +296,7 @@ size_t lightning_prefill_backward_workspace_size(int B, int T, int H, int d, int
     if (bwd_check_shape(B, T, H, d, dtype, segments) != LT_OK) return 0;
     const int cus = lt::device_cu_count();
     if (cus <= 0) return 0;
-    return bwd_layout(B, T, H, d, bwd_plan(cus, B, T, H, segments)).total;
+    return bwd_layout(B, T, H, d, dtype, bwd_plan(cus, B, T, H, segments)).total;
 }
 
 lt_status lightning_prefill_backward(const void* q, const void* k, const void* v, const void* gate,
@@ -323,16 +326,25 @@ lt_status lightning_prefill_backward(const void* q, const void* k, const void* v
     const int cus = lt::device_cu_count();
     if (cus <= 0) return LT_ERR_HIP;
     const Plan pl = bwd_plan(cus, B, T, H, segments);
-    const BwdLayout lay = bwd_layout(B, T, H, d, pl);
+    const BwdLayout lay = bwd_layout(B, T, H, d, dtype, pl);
     if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < lay.total)
         return LT_ERR_WORKSPACE;
     char* ws = static_cast<char*>(workspace);
     const int P = pl.P;
+    // fp32 inputs: the sweeps (and the forward state pass) read bf16 copies
+    const void* in[5] = {q, k, v, gate, dy};
+    uint16_t* copy[5] = {};
+    if (dtype == LT_F32) {
+        for (int i = 0; i < 5; ++i) {
+            copy[i] = reinterpret_cast<uint16_t*>(ws + lay.conv + i * lay.conv_part);
+            in[i] = copy[i];
+        }
+    }
 
     // forward entry states: the prefill's state-only pass and scan over the same segments
     lt::ChunkParams cp;
     memset(&cp, 0, sizeof cp);
-    cp.q = q; cp.k = k; cp.v = v; cp.g = gate;
+    cp.q = in[0]; cp.k = in[1]; cp.v = in[2]; cp.g = in[3];
     cp.qw = q_norm_w; cp.kw = k_norm_w; cp.ow = o_norm_w;
     cp.state_in = state_in;
     cp.ws = reinterpret_cast<float*>(ws);
@@ -357,7 +369,17 @@ lt_status lightning_prefill_backward(const void* q, const void* k, const void* v
 
     lt::BwdParams bp;
     memset(&bp, 0, sizeof bp);
-    bp.q = q; bp.k = k; bp.v = v; bp.g = gate; bp.dy = dy;
+    bp.q = in[0]; bp.k = in[1]; bp.v = in[2]; bp.g = in[3]; bp.dy = in[4];
+    if (dtype == LT_F32) {
+        const void* src[5] = {q, k, v, gate, dy};
+        for (int i = 0; i < 5; ++i) {
+            bp.conv_src[i] = static_cast<const float*>(src[i]);
+            bp.conv_dst[i] = copy[i];
+        }
+        bp.conv_n = (size_t)B * T * H * d;
+    }
+    bp.d = d;
+    bp.out_f32 = dtype == LT_F32;
     bp.qw = q_norm_w; bp.kw = k_norm_w; bp.ow = o_norm_w;
     bp.state_in = state_in;
     bp.fwd_states = cp.ws;

@@ -31,12 +31,21 @@
 // tiles (double-buffered in LDS) and finishing the previous chunk's dq or dk while the MFMA
 // wavefronts work, so that VALU and MFMA work overlap on every SIMD.
 //
-// LDS tiles are bf16 [row][d] with the 16-byte blocks of row r XOR-permuted by
-// f(r) = 4 (r mod 4) + (r / 4 mod 4): 16 consecutive rows take 16 distinct blocks (16-byte row
-// reads), and the four rows a transposing ds_read_b64_tr_b16 gathers move a 4-block group each
-// to a different place (measured on gfx950: no bank conflicts for those reads, against about 6
-// extra cycles per read with the plain r mod 16 permutation), so every tile serves both access
-// patterns.
+// LDS tiles are bf16 [row][d] with the 16-byte blocks of row r XOR-permuted.  At d = 128 (a row
+// fills the 256 bytes of the 64 banks) by f(r) = 4 (r mod 4) + (r / 4 mod 4): 16 consecutive
+// rows take 16 distinct blocks (16-byte row reads), and the four rows a transposing
+// ds_read_b64_tr_b16 gathers move a 4-block group each to a different place (measured on gfx950:
+// no bank conflicts for those reads, against about 6 extra cycles per read with the plain
+// r mod 16 permutation), so every tile serves both access patterns.  At d = 64 two rows share
+// the 256 bytes (even rows the lower half, odd rows the upper), and f(r) is the 3-bit reversal of
+// r / 2 mod 8: the 8 even (and the 8 odd) rows of 16 consecutive ones take 8 distinct blocks, and
+// rows r and r + 2 (r mod 4 < 2) fall into different 4-block groups, the same two properties.
+//
+// Inputs are bf16.  fp32 activations are first rounded to bf16 copies in the workspace (the
+// products take bf16 operands either way); the gradients dq, dk, dv and dg are then written in
+// fp32 from the fp32 values the sweeps hold.
+#include <algorithm>
+
 #include "lt_device.h"
 #include "lt_internal.h"
 
@@ -81,8 +90,14 @@ struct alignas(16) DqSmem {
 
 template <int D>
 __device__ __forceinline__ int swz(int row, int col) {
-    static_assert(D == 128, "the block permutation assumes 16 blocks per row");
-    const int f = 4 * (row & 3) + ((row >> 2) & 3);
+    static_assert(D == 128 || D == 64, "block permutations for 16 or 8 blocks per row");
+    int f;
+    if constexpr (D == 128) {
+        f = 4 * (row & 3) + ((row >> 2) & 3);
+    } else {
+        const int a = (row >> 1) & 7;
+        f = ((a & 1) << 2) | (a & 2) | (a >> 2);
+    }
     return row * D + (((col >> 3) ^ f) << 3) + (col & 7);
 }
 
@@ -173,6 +188,23 @@ __device__ __forceinline__ uint4 pack8(const float* x) {
     return make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
                       pack_bf16x2(x[6], x[7]));
 }
+
+// the 16 values of a row-work thread (features c .. c + 7 and half + c .. half + c + 7, from
+// `dst`) to a bf16 or fp32 output
+__device__ __forceinline__ void store_row16(uint16_t* dst, int half, const float* x) {
+    *reinterpret_cast<uint4*>(dst) = pack8(x);
+    *reinterpret_cast<uint4*>(dst + half) = pack8(x + 8);
+}
+__device__ __forceinline__ void store_row16(float* dst, int half, const float* x) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        float4* o = reinterpret_cast<float4*>(dst + hf * half);
+        o[0] = make_float4(x[8 * hf], x[8 * hf + 1], x[8 * hf + 2], x[8 * hf + 3]);
+        o[1] = make_float4(x[8 * hf + 4], x[8 * hf + 5], x[8 * hf + 6], x[8 * hf + 7]);
+    }
+}
+__device__ __forceinline__ void store_one(uint16_t* dst, float x) { *dst = to_bf16_bits(x); }
+__device__ __forceinline__ void store_one(float* dst, float x) { *dst = x; }
 
 // bf16 copy of a state-shaped accumulator set A[cc] (key rows 32 cc + acc_row(r, lh), value
 // column 32 w + lm) into st[value][key].  With kRecompute the lane index passes through an
@@ -348,7 +380,8 @@ struct RowWork {
 //                                                  rows: the output-norm gradients, do_c
 //   P3  MFMA: dq~_c, W += Q~^T Lambda do_c         rows: q~, v of chunk c + 1
 // (the split of the row work follows measured phase times: o and dq~ are the long MFMA parts).
-template <int D>
+// OT: the gradients' storage (uint16_t bf16 bits or float).
+template <int D, class OT>
 __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dq_kernel(const BwdParams p) {
     using G = BCfg<D>;
     constexpr int NW = G::NW, HALF = G::HALF, TPR = G::TPR, OS = G::OS;
@@ -606,12 +639,10 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dq_kernel(const BwdParams
                 dot = group_sum<TPR>(dot) * (1.0f / D);
 #pragma unroll
                 for (int q = 0; q < 16; ++q) dx[q] = rq2 * (dx[q] - x[q] * dot);
-                if (rr < chunk_len(e)) {
-                    uint16_t* pdq = static_cast<uint16_t*>(p.dq) + base +
-                                    (size_t)(t_begin + e * C + rr) * rs + 8 * fg;
-                    *reinterpret_cast<uint4*>(pdq) = pack8(dx);
-                    *reinterpret_cast<uint4*>(pdq + HALF) = pack8(dx + 8);
-                }
+                if (rr < chunk_len(e))
+                    store_row16(static_cast<OT*>(p.dq) + base +
+                                    (size_t)(t_begin + e * C + rr) * rs + 8 * fg,
+                                HALF, dx);
             }
             if (s < n_chunks) {
                 // k~ of chunk s (bf16 and lo parts).  Rows past the end of a partial chunk get
@@ -668,12 +699,8 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dq_kernel(const BwdParams
                 rw.store(sm.dO, dn);
                 if (rr < chunk_len(c)) {
                     const size_t o2 = (size_t)(t_begin + c * C + rr) * rs + 8 * fg;
-                    uint16_t* pdg = static_cast<uint16_t*>(p.dg) + base + o2;
-                    uint16_t* pdo = p.d_o + base + o2;
-                    *reinterpret_cast<uint4*>(pdg) = pack8(dgv);
-                    *reinterpret_cast<uint4*>(pdg + HALF) = pack8(dgv + 8);
-                    *reinterpret_cast<uint4*>(pdo) = pack8(dn);
-                    *reinterpret_cast<uint4*>(pdo + HALF) = pack8(dn + 8);
+                    store_row16(static_cast<OT*>(p.dg) + base + o2, HALF, dgv);
+                    store_row16(p.d_o + base + o2, HALF, dn);
                 }
             }
             __syncthreads();
@@ -764,7 +791,7 @@ struct alignas(16) DkvSmem {
     alignas(16) float4 dec[12][64];      // as in DqSmem, plus lambda^(C-1-row)
 };
 
-template <int D>
+template <int D, class OT>
 __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dkv_kernel(const BwdParams p) {
     using G = BCfg<D>;
     constexpr int NW = G::NW, HALF = G::HALF, TPR = G::TPR, OS = G::OS;
@@ -852,12 +879,11 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dkv_kernel(const BwdParam
                     }
                     // row acc_row(r, lh) = 4 lh + (8 (r / 4) + r % 4): the lane part goes into
                     // the pointer, the rest is a wave-uniform offset
-                    uint16_t* pdv = static_cast<uint16_t*>(p.dv) + base + (size_t)(t0 + 4 * lh) * rs +
-                                    32 * wave + lm;
+                    OT* pdv = static_cast<OT*>(p.dv) + base + (size_t)(t0 + 4 * lh) * rs + 32 * wave + lm;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int jr = 8 * (r / 4) + r % 4;
-                        if (jr + 4 * lh < n) pdv[(size_t)jr * rs] = to_bf16_bits(dvv[r]);
+                        if (jr + 4 * lh < n) store_one(pdv + (size_t)jr * rs, dvv[r]);
                     }
                 }
                 {
@@ -919,9 +945,13 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dkv_kernel(const BwdParam
         const uint16_t* gv = static_cast<const uint16_t*>(p.v) + base + 8 * fg;
         const uint16_t* gdo = p.d_o + base + 8 * fg;
         auto chunk_pos = [&](int step) { return p.pos0 + t_begin + (int64_t)chunk_of(step) * C; };
+        // score-tile elements of this thread: row rr, columns SPT fg .. SPT fg + SPT - 1 (the
+        // TPR threads of a row cover its C columns)
+        constexpr int SPT = C / TPR;
+        static_assert(SPT % 4 == 0, "whole float4 pieces of a score row per thread");
         struct Regs {
             uint4 q[2], k[2], v[2], dO[2];
-            float4 P, dP;  // score-tile elements [rr][4 fg, 4 fg + 4)
+            float4 P[SPT / 4], dP[SPT / 4];
         };
         auto load = [&](int step, Regs& R) __attribute__((always_inline)) {
             const int t0 = t_begin + chunk_of(step) * C;
@@ -935,8 +965,11 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dkv_kernel(const BwdParam
                 R.dO[hf] = *reinterpret_cast<const uint4*>(gdo + oo);
             }
             const int g = t_begin / C + chunk_of(step);
-            R.P = *reinterpret_cast<const float4*>(score_tile(p, bh, g, 0) + rr * C + 4 * fg);
-            R.dP = *reinterpret_cast<const float4*>(score_tile(p, bh, g, 1) + rr * C + 4 * fg);
+#pragma unroll
+            for (int u = 0; u < SPT / 4; ++u) {
+                R.P[u] = *reinterpret_cast<const float4*>(score_tile(p, bh, g, 0) + rr * C + SPT * fg + 4 * u);
+                R.dP[u] = *reinterpret_cast<const float4*>(score_tile(p, bh, g, 1) + rr * C + SPT * fg + 4 * u);
+            }
         };
         float wk_acc[16];  // this thread's dL/dw_k partial sums
 #pragma unroll
@@ -986,12 +1019,10 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dkv_kernel(const BwdParam
                 dot = group_sum<TPR>(dot) * (1.0f / D);
 #pragma unroll
                 for (int q = 0; q < 16; ++q) dx[q] = rk2 * (dx[q] - x[q] * dot);
-                if (rr < chunk_len(e)) {
-                    uint16_t* pdk = static_cast<uint16_t*>(p.dk) + base +
-                                    (size_t)(t_begin + chunk_of(e) * C + rr) * rs + 8 * fg;
-                    *reinterpret_cast<uint4*>(pdk) = pack8(dx);
-                    *reinterpret_cast<uint4*>(pdk + HALF) = pack8(dx + 8);
-                }
+                if (rr < chunk_len(e))
+                    store_row16(static_cast<OT*>(p.dk) + base +
+                                    (size_t)(t_begin + chunk_of(e) * C + rr) * rs + 8 * fg,
+                                HALF, dx);
             }
             float rk = 0.0f;
             Regs nxt = cur;
@@ -1014,8 +1045,11 @@ __global__ void __launch_bounds__(2 * BCfg<D>::NT) bwd_dkv_kernel(const BwdParam
                 rw.store(T.k, x);
                 rw.store_raw(T.v, cur.v);
                 rw.store_raw(T.dO, cur.dO);
-                *reinterpret_cast<float4*>(T.P + rr * DkvSmem<D>::PS + 4 * fg) = cur.P;
-                *reinterpret_cast<float4*>(T.dP + rr * DkvSmem<D>::PS + 4 * fg) = cur.dP;
+#pragma unroll
+                for (int u = 0; u < SPT / 4; ++u) {
+                    *reinterpret_cast<float4*>(T.P + rr * DkvSmem<D>::PS + SPT * fg + 4 * u) = cur.P[u];
+                    *reinterpret_cast<float4*>(T.dP + rr * DkvSmem<D>::PS + SPT * fg + 4 * u) = cur.dP[u];
+                }
                 if (s + 1 < n_chunks) load(s + 1, nxt);
                 if (wave == NW && s + 1 < n_chunks) rw.fill_table(s + 1, chunk_pos(s + 1));
             }
@@ -1059,26 +1093,33 @@ __global__ void __launch_bounds__(256) bwd_wgrad_kernel(const BwdParams p, int d
     if (out) out[(size_t)hr * d + f] = s;
 }
 
-}  // namespace
+// Rounds the fp32 inputs to bf16 copies: blockIdx.y picks the tensor, each thread 8 values.
+__global__ void __launch_bounds__(256) bwd_convert_kernel(const BwdParams p) {
+    const float* src = p.conv_src[blockIdx.y];
+    uint16_t* dst = p.conv_dst[blockIdx.y];
+    const size_t n8 = p.conv_n / 8;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
+         i += (size_t)gridDim.x * blockDim.x) {
+        const float4 a = reinterpret_cast<const float4*>(src)[2 * i];
+        const float4 b = reinterpret_cast<const float4*>(src)[2 * i + 1];
+        const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        reinterpret_cast<uint4*>(dst)[i] = pack8(x);
+    }
+}
 
-hipError_t launch_prefill_backward(const BwdParams& p, const ChunkParams& fwd_cp,
-                                   const ScanParams& fwd_sp, const hipEvent_t ev[4],
-                                   hipStream_t stream) {
-    if (const hipError_t g = launch_gate(); g != hipSuccess) return g;
-    constexpr int D = 128;
+template <int D, class OT>
+hipError_t launch_sweeps(const BwdParams& p, const hipEvent_t ev[4], hipStream_t stream) {
     const int BH = p.B * p.H;
     hipError_t err;
-    if (p.P > 1 && (err = launch_prefill_states(fwd_cp, fwd_sp, D, LT_BF16, stream)) != hipSuccess)
-        return err;
     if (ev[0] && (err = hipEventRecord(ev[0], stream)) != hipSuccess) return err;
-    bwd_dq_kernel<D><<<dim3(BH * p.P), dim3(2 * BCfg<D>::NT), 0, stream>>>(p);
+    bwd_dq_kernel<D, OT><<<dim3(BH * p.P), dim3(2 * BCfg<D>::NT), 0, stream>>>(p);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev[1] && (err = hipEventRecord(ev[1], stream)) != hipSuccess) return err;
     const size_t n = (size_t)BH * D * D;
     bwd_scan_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(p, D * D);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev[2] && (err = hipEventRecord(ev[2], stream)) != hipSuccess) return err;
-    bwd_dkv_kernel<D><<<dim3(BH * p.P), dim3(2 * BCfg<D>::NT), 0, stream>>>(p);
+    bwd_dkv_kernel<D, OT><<<dim3(BH * p.P), dim3(2 * BCfg<D>::NT), 0, stream>>>(p);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev[3] && (err = hipEventRecord(ev[3], stream)) != hipSuccess) return err;
     if (p.wgrad) {
@@ -1087,6 +1128,29 @@ hipError_t launch_prefill_backward(const BwdParams& p, const ChunkParams& fwd_cp
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_prefill_backward(const BwdParams& p, const ChunkParams& fwd_cp,
+                                   const ScanParams& fwd_sp, const hipEvent_t ev[4],
+                                   hipStream_t stream) {
+    if (const hipError_t g = launch_gate(); g != hipSuccess) return g;
+    if (p.d != 64 && p.d != 128) return hipErrorInvalidValue;
+    hipError_t err;
+    if (p.conv_n) {
+        const size_t n8 = p.conv_n / 8;
+        const unsigned gx = (unsigned)std::min<size_t>((n8 + 255) / 256, 65536);
+        bwd_convert_kernel<<<dim3(gx, 5), dim3(256), 0, stream>>>(p);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    if (p.P > 1 && (err = launch_prefill_states(fwd_cp, fwd_sp, p.d, LT_BF16, stream)) != hipSuccess)
+        return err;
+    if (p.d == 128)
+        return p.out_f32 ? launch_sweeps<128, float>(p, ev, stream)
+                         : launch_sweeps<128, uint16_t>(p, ev, stream);
+    return p.out_f32 ? launch_sweeps<64, float>(p, ev, stream)
+                     : launch_sweeps<64, uint16_t>(p, ev, stream);
 }
 
 }  // namespace lt

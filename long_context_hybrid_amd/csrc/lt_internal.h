@@ -96,11 +96,16 @@ struct DecodeParams {
 // slot s * SM of fwd_states (the state-only pass and scan of launch_prefill_states) when P > 1,
 // else state_in.
 struct BwdParams {
-    const void* q;
-    const void* k;
+    const void* q;             // bf16 [B][T][H][d] (the sweeps read bf16; fp32 inputs are first
+    const void* k;             // rounded into workspace copies, see conv_*)
     const void* v;
     const void* g;
     const void* dy;
+    const float* conv_src[5];  // fp32 q, k, v, g, dy to round to bf16 into conv_dst before the
+    uint16_t* conv_dst[5];     // sweeps (conv_n elements each); conv_n = 0: none
+    size_t conv_n;
+    int d;                     // head width, 64 or 128
+    int out_f32;               // dq, dk, dv, dg are fp32 (else bf16)
     const float* qw;
     const float* kw;
     const float* ow;           // may be null (ones)

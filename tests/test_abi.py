@@ -519,10 +519,14 @@ def test_backward_workspace_layout():
     # every chunk, one d x d state gradient per (b, h, segment)
     assert ws >= B * T * H * d * 2 + B * H * (T // 32) * 2 * 32 * 32 * 4 + B * H * d * d * 4
     assert ws % 4 == 0 and pl["backward_segments"] == 2
-    # unsupported shapes report 0
-    assert lt.lightning_prefill_plan_cus(256, B, T, H, 64)["backward_workspace_bytes"] == 0
-    assert lt.lightning_prefill_plan_cus(256, B, T, H, d, torch.float32)[
-        "backward_workspace_bytes"] == 0
+    # fp32 inputs add five bf16 copies (q, k, v, g, dy) of one activation tensor each
+    ws32 = lt.lightning_prefill_plan_cus(256, B, T, H, d, torch.float32)["backward_workspace_bytes"]
+    assert ws32 == ws + 5 * B * T * H * d * 2
+    # d = 64: smaller by the state and activation parts
+    ws64 = lt.lightning_prefill_plan_cus(256, B, T, H, 64)["backward_workspace_bytes"]
+    assert B * T * H * 64 * 2 + B * H * 64 * 64 * 4 <= ws64 < ws
+    assert lt.lightning_prefill_plan_cus(256, B, T, H, 64, torch.float32)[
+        "backward_workspace_bytes"] == ws64 + 5 * B * T * H * 64 * 2
     # one segment (B H fills the CUs): no forward state slots, one gradient per (b, h)
     one = lt.lightning_prefill_plan_cus(256, 16, 256, 16, d)["backward_workspace_bytes"]
     do_bytes = 16 * 256 * 16 * d * 2
@@ -555,13 +559,15 @@ BWD_BAD = [
     ("zero_T", dict(T=0), lt.LT_ERR_INVALID_ARG),
     ("negative_segments", dict(seg=-1), lt.LT_ERR_INVALID_ARG),
     ("pos0_negative", dict(pos0=-3), lt.LT_ERR_INVALID_ARG),
-    ("fp32", dict(dt=lt.LT_F32), lt.LT_ERR_UNSUPPORTED),
-    ("d_64", dict(d=64, stride=64), lt.LT_ERR_UNSUPPORTED),
+    ("d_96", dict(d=96, stride=96), lt.LT_ERR_UNSUPPORTED),
+    ("d_32", dict(d=32, stride=32), lt.LT_ERR_UNSUPPORTED),
     ("events_null_entries", dict(ev=(ct.c_void_p * 4)(None, None, None, None)),
      lt.LT_ERR_INVALID_ARG),
     # valid arguments: the plan needs the device, so without one the call reports LT_ERR_HIP
     # (the workspace checks run on the GPU in tests/test_gpu_errors.py)
     ("no_device", dict(), lt.LT_ERR_HIP),
+    ("no_device_fp32", dict(dt=lt.LT_F32), lt.LT_ERR_HIP),
+    ("no_device_d64", dict(d=64, stride=64), lt.LT_ERR_HIP),
     ("no_device_workspace_missing", dict(ws=None), lt.LT_ERR_HIP),
 ]
 

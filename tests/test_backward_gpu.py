@@ -1,6 +1,9 @@
 """Parity of the prefill backward (lightning_prefill_backward) with the fp64 gradient oracle of
 oracle/backward.py, on the same seeded inputs, compared per (b, h) slice.
 
+Cases span d = 128 and d = 64, bf16 and fp32 activations (fp32 inputs are rounded once to bf16
+copies for the products; the gradients come back in fp32).
+
 Tolerances (relative L2 error per slice): every gradient <= 2e-2.  The backward's products run
 on bf16 MFMA operands with fp32 accumulation (q~, k~, v, do and the bf16 copy of the state that
 the products contracting over the value dimension read), like the forward's score and output
@@ -157,6 +160,47 @@ def test_backward_small(case):
         gpu = gpu_backward(inp, segments=seg)
         compare(gpu, ref, inp, f"{label} segments={seg}")
         compare_weights(gpu, ref, inp, f"{label} segments={seg}", want_o=True)
+
+
+# d = 64 and fp32 activations: the same sweeps at half the head width, and fp32 inputs rounded
+# once to bf16 copies (the products take bf16 operands either way) with fp32 gradients written
+# out, so the bound stays the bf16 one.
+WIDE_CASES = [
+    # (label, B, T, H, d, dtype, state, d_state_out, segments)
+    ("d64_ragged", 1, 300, 2, 64, torch.bfloat16, "randn", True, (0, 3)),
+    ("d64_two_rows", 2, 333, 3, 64, torch.bfloat16, "zeros", False, (0, 2)),
+    ("d64_sub_segments", 1, 4096 + 33, 2, 64, torch.bfloat16, "randn", True, (0, 4)),
+    ("fp32_d128_ragged", 1, 300, 2, 128, torch.float32, "randn", True, (0, 3)),
+    ("fp32_d64_two_rows", 2, 200, 2, 64, torch.float32, "randn", False, (0, 2)),
+]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=[c[0] for c in WIDE_CASES])
+def test_backward_d64_and_fp32(case):
+    label, B, T, H, d, dtype, state, dso, segs = case
+    seed = zlib.crc32(label.encode()) % 9973
+    inp = synth.make_custom_prefill(B, T, H, d, dtype=dtype, seed=seed, state=state)
+    gen = torch.Generator().manual_seed(seed + 1)
+    inp["dy"] = torch.randn(inp["q"].shape, generator=gen).to(dtype)
+    inp["d_state_out"] = (0.01 * torch.randn((B, H, d, d), generator=gen)) if dso else None
+    ref = oracle_backward(inp)
+    for seg in segs:
+        gpu = gpu_backward(inp, segments=seg)
+        compare(gpu, ref, inp, f"{label} segments={seg}")
+        compare_weights(gpu, ref, inp, f"{label} segments={seg}")
+
+
+def test_backward_tiny_workload():
+    """The tiny workload as specified (B = 1, H = 2, T = 256, d = 64, fp32, lambda = (0.9, 0.99),
+    rope base 1e4, unit norm weights)."""
+    inp = synth.make_prefill(synth.TINY)
+    gen = torch.Generator().manual_seed(51)
+    inp["dy"] = torch.randn(inp["q"].shape, generator=gen).to(torch.float32)
+    inp["d_state_out"] = None
+    ref = oracle_backward(inp)
+    gpu = gpu_backward(inp)
+    compare(gpu, ref, inp, "tiny workload")
+    compare_weights(gpu, ref, inp, "tiny workload")
 
 
 def test_backward_output_weight_and_shared_norm_weights():
