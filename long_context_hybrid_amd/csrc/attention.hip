@@ -236,9 +236,14 @@ __device__ __forceinline__ void settle(Scores& sc, f32x16 (&o)[kD / 32], float& 
     a[10] = max3_raw(sc.s[0][15], sc.s[1][15], a[0]);
     const float b0 = max3_raw(a[1], a[2], a[3]), b1 = max3_raw(a[4], a[5], a[6]);
     const float b2 = max3_raw(a[7], a[8], a[9]);
-    float mx = max3_raw(b0, b1, max3_raw(b2, a[10], a[10]));
-    const float other = __shfl_xor(mx, 32);
-    mx = max3_raw(mx, other, other) + sc.sub;
+    const float mh = max3_raw(b0, b1, max3_raw(b2, a[10], a[10]));
+    // the two lane halves hold the two 16-key halves of each query's column: swapping the
+    // value with itself across the halves (v_permlane32_swap, no LDS round trip) leaves lanes
+    // 0-31's maxima in one result and lanes 32-63's in the other
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mh), __float_as_uint(mh),
+                                                     false, false);
+    const float mx = max3_raw(__uint_as_float(sw[0]), __uint_as_float(sw[1]),
+                              __uint_as_float(sw[1])) + sc.sub;
     const bool raise = mx > m + kRaise;
     if (__builtin_amdgcn_ballot_w64(raise)) {
         const float m_new = raise ? mx : m;
@@ -379,13 +384,20 @@ __global__ void __launch_bounds__(64 * kWaves, 1) attn_fwd_kernel(const AttnPara
     // first two wavefronts of a head run one such block per tile, with one head (256-query
     // tiles) wavefronts 0-1 run three, 2-3 two and 4-5 one.  The last step's scores read keys
     // nothing uses.
+    // Waves w and w + 4 share a SIMD: the first four form the next block's scores before the
+    // softmax of this one, the other four after it, so that on each SIMD one wavefront's score
+    // MFMAs meet the other's softmax instead of both running the same phase at once (the
+    // step's barrier realigns them every block).  A score formed before the running max moves
+    // is re-based by the next settle.
+    const bool scores_first = wave < kWaves / 2;
     auto step = [&](int kb, Scores& cur, Scores& nxt) {
         const int key0 = kb * kBN;
-        if (key0 + kBN - 1 > q0) mask_scores(cur, key0, qi, lh);
-        settle(cur, o, m, l);
         if (kb + 2 < n_kb) load_keys(kb + 2, kt[kb & 1]);
         if (kb + 1 < n_kb) load_values(kb + 1, vt[(kb + 1) & 1]);
-        block_scores(nxt, kt[(kb + 1) & 1], qv, ln, lh, m);
+        if (scores_first) block_scores(nxt, kt[(kb + 1) & 1], qv, ln, lh, m);
+        if (key0 + kBN - 1 > q0) mask_scores(cur, key0, qi, lh);
+        settle(cur, o, m, l);
+        if (!scores_first) block_scores(nxt, kt[(kb + 1) & 1], qv, ln, lh, m);
         block_probs_pv(cur, vt[kb & 1], o, l, lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
