@@ -64,10 +64,13 @@ typedef enum {
     LT_ERR_HIP = 4          /* the HIP runtime reported an error while enqueuing */
 } lt_status;
 
-typedef enum {
+/* Storage type of activations and outputs.  An int, so that a caller may pass any value (an
+ * unknown one is rejected with LT_ERR_INVALID_ARG) without an out-of-range enum. */
+typedef int lt_dtype;
+enum {
     LT_F32 = 0, /* activations and outputs stored as IEEE fp32 */
     LT_BF16 = 1 /* activations and outputs stored as bfloat16 */
-} lt_dtype;
+};
 
 #define LT_MAX_HEADS 256
 
@@ -78,9 +81,12 @@ const char* lightning_status_string(int status);
  * written to out[h-1] (host memory, H doubles).  LT_ERR_INVALID_ARG if H < 1 or out is NULL. */
 lt_status lightning_hypenet_gamma(int H, double* out);
 
-/* Fill the fp32 recurrent state [B][H][d][d] with zeros (init == NULL) or with a copy of `init`
- * (same shape, device memory; may not overlap `state` unless equal to it). */
-lt_status lightning_state_init(float* state, int B, int H, int d, const float* init, void* stream);
+/* Fill the fp32 recurrent state [B][H][dk][dv] with zeros (init == NULL) or with a copy of `init`
+ * (same shape, device memory; may not overlap `state` unless equal to it).  The mixer's calls use
+ * dk = dv = d; the fill itself takes any positive sizes.  LT_ERR_INVALID_ARG for a null or
+ * misaligned pointer or a size <= 0. */
+lt_status lightning_state_init(float* state, int B, int H, int dk, int dv, const float* init,
+                               void* stream);
 
 /* Chunk length and number of sequence segments lightning_prefill will use for this shape when
  * called with the same `chunk` and `segments` requests (0 = automatic), and the number of tokens
@@ -88,7 +94,7 @@ lt_status lightning_state_init(float* state, int B, int H, int d, const float* i
  * pointer may be NULL.  The split depends on the current device's compute units.  Returns
  * LT_ERR_UNSUPPORTED for a request the library does not implement, LT_ERR_HIP when no device is
  * visible. */
-lt_status lightning_prefill_plan(int B, int T, int H, int d, int dtype, int chunk, int segments,
+lt_status lightning_prefill_plan(int B, int T, int H, int d, lt_dtype dtype, int chunk, int segments,
                                  int* chunk_out, int* segments_out, int* segment_len_out);
 
 /* The plan of a prefill request for a device with `num_cus` compute units (lightning_prefill_plan
@@ -109,12 +115,12 @@ typedef struct {
     size_t backward_workspace_bytes;/* lightning_prefill_backward_workspace_size */
 } lt_prefill_plan;
 
-lt_status lightning_prefill_plan_cus(int num_cus, int B, int T, int H, int d, int dtype,
+lt_status lightning_prefill_plan_cus(int num_cus, int B, int T, int H, int d, lt_dtype dtype,
                                      int chunk, int segments, lt_prefill_plan* out);
 
 /* Device workspace (bytes) lightning_prefill needs for this shape and request on the current
  * device (0 when the request is unsupported or no device is visible). */
-size_t lightning_prefill_workspace_size(int B, int T, int H, int d, int dtype, int chunk,
+size_t lightning_prefill_workspace_size(int B, int T, int H, int d, lt_dtype dtype, int chunk,
                                         int segments);
 
 /*
@@ -145,7 +151,7 @@ lt_status lightning_prefill(const void* q, const void* k, const void* v, const v
                             const float* q_norm_w, const float* k_norm_w, const float* o_norm_w,
                             int norm_w_head_stride, const double* lambda, double rope_base,
                             double rms_eps, int64_t pos0, const float* state_in, float* state_out,
-                            void* y, float* o_raw, int B, int T, int H, int d, int dtype,
+                            void* y, float* o_raw, int B, int T, int H, int d, lt_dtype dtype,
                             int chunk, int segments, void* workspace, size_t workspace_bytes,
                             void* const* main_kernel_events, void* stream);
 
@@ -168,7 +174,7 @@ lt_status lightning_prefill_noalloc(const void* q, const void* k, const void* v,
                                     const float* o_norm_w, int norm_w_head_stride,
                                     const double* lambda, double rope_base, double rms_eps,
                                     int64_t pos0, const float* state_in, float* state_out,
-                                    void* y, float* o_raw, int B, int T, int H, int d, int dtype,
+                                    void* y, float* o_raw, int B, int T, int H, int d, lt_dtype dtype,
                                     int chunk, int segments, void* stream);
 
 /*
@@ -186,7 +192,7 @@ lt_status lightning_decode_step(const void* q, const void* k, const void* v, con
                                 const double* lambda, double rope_base, double rms_eps,
                                 const int64_t* positions, const float* state_in,
                                 float* state_out, void* y, float* o_raw, int B, int H, int d,
-                                int dtype, void* stream);
+                                lt_dtype dtype, void* stream);
 
 /*
  * ---- Data-dependent scalar decay (the time-dependent variant of the same kernels) ----
@@ -199,7 +205,7 @@ lt_status lightning_decode_step(const void* q, const void* k, const void* v, con
  * Everything else as for lightning_prefill / lightning_decode_step (no lambda).  The prefill's
  * workspace also holds each state-only sub-segment's total log2 decay, so its size query differs.
  */
-size_t lightning_prefill_dd_workspace_size(int B, int T, int H, int d, int dtype, int chunk,
+size_t lightning_prefill_dd_workspace_size(int B, int T, int H, int d, lt_dtype dtype, int chunk,
                                            int segments);
 
 lt_status lightning_prefill_dd(const void* q, const void* k, const void* v, const void* gate,
@@ -207,7 +213,7 @@ lt_status lightning_prefill_dd(const void* q, const void* k, const void* v, cons
                                const float* o_norm_w, int norm_w_head_stride,
                                const float* log2_decay, double rope_base, double rms_eps,
                                int64_t pos0, const float* state_in, float* state_out, void* y,
-                               float* o_raw, int B, int T, int H, int d, int dtype, int chunk,
+                               float* o_raw, int B, int T, int H, int d, lt_dtype dtype, int chunk,
                                int segments, void* workspace, size_t workspace_bytes,
                                void* const* main_kernel_events, void* stream);
 
@@ -217,7 +223,7 @@ lt_status lightning_decode_step_dd(const void* q, const void* k, const void* v,
                                    int norm_w_head_stride, const float* log2_decay,
                                    double rope_base, double rms_eps, const int64_t* positions,
                                    const float* state_in, float* state_out, void* y,
-                                   float* o_raw, int B, int H, int d, int dtype, void* stream);
+                                   float* o_raw, int B, int H, int d, lt_dtype dtype, void* stream);
 
 /*
  * ---- Backward of the prefill (the gradients that HALO's training stages need) ----
@@ -250,7 +256,7 @@ lt_status lightning_decode_step_dd(const void* q, const void* k, const void* v,
  * prefill(T1) then prefill(T2, state_in = its state_out) is the backward of the second call, whose
  * d_state_in is the first call's d_state_out.
  */
-size_t lightning_prefill_backward_workspace_size(int B, int T, int H, int d, int dtype,
+size_t lightning_prefill_backward_workspace_size(int B, int T, int H, int d, lt_dtype dtype,
                                                  int segments);
 
 lt_status lightning_prefill_backward(const void* q, const void* k, const void* v, const void* gate,
@@ -261,7 +267,7 @@ lt_status lightning_prefill_backward(const void* q, const void* k, const void* v
                                      const float* d_state_out, void* dq, void* dk, void* dv,
                                      void* dgate, float* d_state_in, float* d_q_norm_w,
                                      float* d_k_norm_w, float* d_o_norm_w, int B, int T, int H,
-                                     int d, int dtype, int segments, void* workspace,
+                                     int d, lt_dtype dtype, int segments, void* workspace,
                                      size_t workspace_bytes, void* const* kernel_events,
                                      void* stream);
 
@@ -291,7 +297,7 @@ lt_status lightning_prefill_backward(const void* q, const void* k, const void* v
  *   after it, after the mixer and after the output GEMM.
  * Errors: as for the mixer calls.  d_model not a multiple of 8 is LT_ERR_INVALID_ARG.
  */
-size_t lightning_layer_prefill_workspace_size(int B, int T, int H, int d, int d_model, int dtype,
+size_t lightning_layer_prefill_workspace_size(int B, int T, int H, int d, int d_model, lt_dtype dtype,
                                               int chunk, int segments);
 
 lt_status lightning_layer_prefill(const void* x, const void* w_qkvz, const void* w_o,
@@ -299,14 +305,14 @@ lt_status lightning_layer_prefill(const void* x, const void* w_qkvz, const void*
                                   const float* o_norm_w, int norm_w_head_stride,
                                   const double* lambda, double rope_base, double rms_eps,
                                   int64_t pos0, const float* state_in, float* state_out,
-                                  void* out, int B, int T, int H, int d, int d_model, int dtype,
+                                  void* out, int B, int T, int H, int d, int d_model, lt_dtype dtype,
                                   int chunk, int segments, void* workspace,
                                   size_t workspace_bytes, void* const* stage_events,
                                   void* stream);
 
 /* One decode step of the layer: x [B][d_model] -> out [B][d_model], the state updated as by
  * lightning_decode_step.  Workspace layout as above with T = 1. */
-size_t lightning_layer_decode_workspace_size(int B, int H, int d, int d_model, int dtype);
+size_t lightning_layer_decode_workspace_size(int B, int H, int d, int d_model, lt_dtype dtype);
 
 lt_status lightning_layer_decode_step(const void* x, const void* w_qkvz, const void* w_o,
                                       const float* q_norm_w, const float* k_norm_w,
@@ -314,7 +320,7 @@ lt_status lightning_layer_decode_step(const void* x, const void* w_qkvz, const v
                                       const double* lambda, double rope_base, double rms_eps,
                                       const int64_t* positions, const float* state_in,
                                       float* state_out, void* out, int B, int H, int d,
-                                      int d_model, int dtype, void* workspace,
+                                      int d_model, lt_dtype dtype, void* workspace,
                                       size_t workspace_bytes, void* stream);
 
 /*
@@ -342,7 +348,7 @@ lt_status lightning_layer_decode_step(const void* x, const void* w_qkvz, const v
  *                   prologue that normalises and scales q and k).
  * Supported: d = 128, bf16 (others return LT_ERR_UNSUPPORTED).
  */
-size_t lightning_attn_prefill_workspace_size(int B, int T, int Hq, int Hkv, int d, int dtype,
+size_t lightning_attn_prefill_workspace_size(int B, int T, int Hq, int Hkv, int d, lt_dtype dtype,
                                              int has_key_norm, int has_key_cache);
 
 lt_status lightning_attn_prefill(const void* q, const void* k, const void* v, const void* gate,
@@ -350,7 +356,7 @@ lt_status lightning_attn_prefill(const void* q, const void* k, const void* v, co
                                  const float* o_norm_w, int norm_w_head_stride,
                                  double logit_scale_base, double rms_eps, int64_t pos0, void* y,
                                  float* o_raw, void* key_cache_out, int B, int T, int Hq, int Hkv,
-                                 int d, int dtype, void* workspace, size_t workspace_bytes,
+                                 int d, lt_dtype dtype, void* workspace, size_t workspace_bytes,
                                  void* const* main_kernel_events, void* stream);
 
 /*
@@ -372,7 +378,7 @@ lt_status lightning_attn_prefill(const void* q, const void* k, const void* v, co
  * key_cache_out and the caller's values) with lengths = T equals row T of the prefill of T + 1
  * tokens.
  */
-size_t lightning_attn_decode_workspace_size(int B, int Hq, int Hkv, int d, int dtype,
+size_t lightning_attn_decode_workspace_size(int B, int Hq, int Hkv, int d, lt_dtype dtype,
                                             int64_t max_length);
 
 lt_status lightning_attn_decode_step(const void* q, const void* k_new, const void* v_new,
@@ -381,7 +387,7 @@ lt_status lightning_attn_decode_step(const void* q, const void* k_new, const voi
                                      int norm_w_head_stride, double logit_scale_base,
                                      double rms_eps, const int64_t* lengths, void* k_cache,
                                      void* v_cache, int64_t cache_capacity, void* y,
-                                     float* o_raw, int B, int Hq, int Hkv, int d, int dtype,
+                                     float* o_raw, int B, int Hq, int Hkv, int d, lt_dtype dtype,
                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -407,7 +413,7 @@ lt_status lightning_attn_decode_step_dev(const void* q, const void* k_new, const
                                          double rms_eps, const int64_t* lengths,
                                          int64_t max_length, void* k_cache, void* v_cache,
                                          int64_t cache_capacity, void* y, float* o_raw, int B,
-                                         int Hq, int Hkv, int d, int dtype, void* workspace,
+                                         int Hq, int Hkv, int d, lt_dtype dtype, void* workspace,
                                          size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus

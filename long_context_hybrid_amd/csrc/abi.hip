@@ -234,15 +234,17 @@ lt_status lightning_hypenet_gamma(int H, double* out) {
     return LT_OK;
 }
 
-lt_status lightning_state_init(float* state, int B, int H, int d, const float* init, void* stream) {
-    if (!ok_ptr(state) || !ok_opt(init) || B <= 0 || H <= 0 || d <= 0) return LT_ERR_INVALID_ARG;
-    const size_t n = (size_t)B * H * d * d;
+lt_status lightning_state_init(float* state, int B, int H, int dk, int dv, const float* init,
+                               void* stream) {
+    if (!ok_ptr(state) || !ok_opt(init) || B <= 0 || H <= 0 || dk <= 0 || dv <= 0)
+        return LT_ERR_INVALID_ARG;
+    const size_t n = (size_t)B * H * dk * dv;
     if (lt::launch_state_init(state, init, n, static_cast<hipStream_t>(stream)) != hipSuccess)
         return LT_ERR_HIP;
     return LT_OK;
 }
 
-lt_status lightning_prefill_plan(int B, int T, int H, int d, int dtype, int chunk, int segments,
+lt_status lightning_prefill_plan(int B, int T, int H, int d, lt_dtype dtype, int chunk, int segments,
                                  int* chunk_out, int* segments_out, int* segment_len_out) {
     Plan pl;
     const lt_status st = device_plan(B, T, H, d, dtype, chunk, segments, &pl);
@@ -253,7 +255,7 @@ lt_status lightning_prefill_plan(int B, int T, int H, int d, int dtype, int chun
     return LT_OK;
 }
 
-lt_status lightning_prefill_plan_cus(int num_cus, int B, int T, int H, int d, int dtype,
+lt_status lightning_prefill_plan_cus(int num_cus, int B, int T, int H, int d, lt_dtype dtype,
                                      int chunk, int segments, lt_prefill_plan* out) {
     if (num_cus <= 0 || out == nullptr) return LT_ERR_INVALID_ARG;
     Plan pl;
@@ -276,14 +278,14 @@ lt_status lightning_prefill_plan_cus(int num_cus, int B, int T, int H, int d, in
     return LT_OK;
 }
 
-size_t lightning_prefill_workspace_size(int B, int T, int H, int d, int dtype, int chunk,
+size_t lightning_prefill_workspace_size(int B, int T, int H, int d, lt_dtype dtype, int chunk,
                                         int segments) {
     Plan pl;
     if (device_plan(B, T, H, d, dtype, chunk, segments, &pl) != LT_OK) return 0;
     return workspace_bytes_for(B, H, d, pl.P, pl.sub);
 }
 
-size_t lightning_prefill_dd_workspace_size(int B, int T, int H, int d, int dtype, int chunk,
+size_t lightning_prefill_dd_workspace_size(int B, int T, int H, int d, lt_dtype dtype, int chunk,
                                            int segments) {
     Plan pl;
     if (chunk == 64) return 0;  // the data-dependent decay runs 32-token chunks only
@@ -291,7 +293,7 @@ size_t lightning_prefill_dd_workspace_size(int B, int T, int H, int d, int dtype
     return workspace_bytes_dd(B, H, d, pl.P, pl.sub);
 }
 
-size_t lightning_prefill_backward_workspace_size(int B, int T, int H, int d, int dtype,
+size_t lightning_prefill_backward_workspace_size(int B, int T, int H, int d, lt_dtype dtype,
                                                  int segments) {
     if (bwd_check_shape(B, T, H, d, dtype, segments) != LT_OK) return 0;
     const int cus = lt::device_cu_count();
@@ -307,7 +309,7 @@ lt_status lightning_prefill_backward(const void* q, const void* k, const void* v
                                      const float* d_state_out, void* dq, void* dk, void* dv,
                                      void* dgate, float* d_state_in, float* d_q_norm_w,
                                      float* d_k_norm_w, float* d_o_norm_w, int B, int T, int H,
-                                     int d, int dtype, int segments, void* workspace,
+                                     int d, lt_dtype dtype, int segments, void* workspace,
                                      size_t workspace_bytes, void* const* kernel_events,
                                      void* stream) {
     if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(gate) || !ok_ptr(dy))
@@ -549,7 +551,7 @@ lt_status lightning_prefill(const void* q, const void* k, const void* v, const v
                             const float* q_norm_w, const float* k_norm_w, const float* o_norm_w,
                             int norm_w_head_stride, const double* lambda, double rope_base,
                             double rms_eps, int64_t pos0, const float* state_in, float* state_out,
-                            void* y, float* o_raw, int B, int T, int H, int d, int dtype,
+                            void* y, float* o_raw, int B, int T, int H, int d, lt_dtype dtype,
                             int chunk, int segments, void* workspace, size_t workspace_bytes,
                             void* const* main_kernel_events, void* stream) {
     if (H <= 0 || d <= 0 || (long long)H * d > 0x7fffffffLL) return LT_ERR_INVALID_ARG;
@@ -566,7 +568,7 @@ lt_status lightning_decode_step(const void* q, const void* k, const void* v, con
                                 const double* lambda, double rope_base, double rms_eps,
                                 const int64_t* positions, const float* state_in,
                                 float* state_out, void* y, float* o_raw, int B, int H, int d,
-                                int dtype, void* stream) {
+                                lt_dtype dtype, void* stream) {
     if (H <= 0 || d <= 0 || (long long)H * d > 0x7fffffffLL) return LT_ERR_INVALID_ARG;
     return lt::decode_strided(q, k, v, gate, H * d, q_norm_w, k_norm_w, o_norm_w,
                               norm_w_head_stride, lambda, rope_base, rms_eps, positions, state_in,
@@ -578,7 +580,7 @@ lt_status lightning_prefill_dd(const void* q, const void* k, const void* v, cons
                                const float* o_norm_w, int norm_w_head_stride,
                                const float* log2_decay, double rope_base, double rms_eps,
                                int64_t pos0, const float* state_in, float* state_out, void* y,
-                               float* o_raw, int B, int T, int H, int d, int dtype, int chunk,
+                               float* o_raw, int B, int T, int H, int d, lt_dtype dtype, int chunk,
                                int segments, void* workspace, size_t workspace_bytes,
                                void* const* main_kernel_events, void* stream) {
     if (H <= 0 || d <= 0 || (long long)H * d > 0x7fffffffLL) return LT_ERR_INVALID_ARG;
@@ -596,7 +598,7 @@ lt_status lightning_decode_step_dd(const void* q, const void* k, const void* v,
                                    int norm_w_head_stride, const float* log2_decay,
                                    double rope_base, double rms_eps, const int64_t* positions,
                                    const float* state_in, float* state_out, void* y,
-                                   float* o_raw, int B, int H, int d, int dtype, void* stream) {
+                                   float* o_raw, int B, int H, int d, lt_dtype dtype, void* stream) {
     if (H <= 0 || d <= 0 || (long long)H * d > 0x7fffffffLL) return LT_ERR_INVALID_ARG;
     if (!ok_ptr(log2_decay)) return LT_ERR_INVALID_ARG;
     return lt::decode_strided(q, k, v, gate, H * d, q_norm_w, k_norm_w, o_norm_w,

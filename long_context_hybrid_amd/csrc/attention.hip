@@ -813,7 +813,7 @@ lt_status attn_shape(int B, int T, int Hq, int Hkv, int d, int dtype) {
 
 extern "C" {
 
-size_t lightning_attn_prefill_workspace_size(int B, int T, int Hq, int Hkv, int d, int dtype,
+size_t lightning_attn_prefill_workspace_size(int B, int T, int Hq, int Hkv, int d, lt_dtype dtype,
                                              int has_key_norm, int has_key_cache) {
     if (attn_shape(B, T, Hq, Hkv, d, dtype) != LT_OK) return 0;
     return attn_ws_bytes(B, T, Hq, Hkv, has_key_norm && !has_key_cache);
@@ -824,7 +824,7 @@ lt_status lightning_attn_prefill(const void* q, const void* k, const void* v, co
                                  const float* o_norm_w, int norm_w_head_stride,
                                  double logit_scale_base, double rms_eps, int64_t pos0, void* y,
                                  float* o_raw, void* key_cache_out, int B, int T, int Hq, int Hkv,
-                                 int d, int dtype, void* workspace, size_t workspace_bytes,
+                                 int d, lt_dtype dtype, void* workspace, size_t workspace_bytes,
                                  void* const* main_kernel_events, void* stream) {
     if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(gate) || !ok_ptr(y))
         return LT_ERR_INVALID_ARG;
@@ -875,7 +875,7 @@ lt_status lightning_attn_prefill(const void* q, const void* k, const void* v, co
     return LT_OK;
 }
 
-size_t lightning_attn_decode_workspace_size(int B, int Hq, int Hkv, int d, int dtype,
+size_t lightning_attn_decode_workspace_size(int B, int Hq, int Hkv, int d, lt_dtype dtype,
                                             int64_t max_length) {
     if (attn_shape(B, 1, Hq, Hkv, d, dtype) != LT_OK || max_length < 0) return 0;
     const int64_t n_split = max_length / lt::kAttnDecodeChunk + 1;
@@ -963,7 +963,7 @@ lt_status lightning_attn_decode_step(const void* q, const void* k_new, const voi
                                      int norm_w_head_stride, double logit_scale_base,
                                      double rms_eps, const int64_t* lengths, void* k_cache,
                                      void* v_cache, int64_t cache_capacity, void* y,
-                                     float* o_raw, int B, int Hq, int Hkv, int d, int dtype,
+                                     float* o_raw, int B, int Hq, int Hkv, int d, lt_dtype dtype,
                                      void* workspace, size_t workspace_bytes, void* stream) {
     if (lengths == nullptr) return LT_ERR_INVALID_ARG;
     return attn_decode(q, k_new, v_new, gate, q_norm_w, k_norm_w, o_norm_w, norm_w_head_stride,
@@ -979,7 +979,7 @@ lt_status lightning_attn_decode_step_dev(const void* q, const void* k_new, const
                                          double rms_eps, const int64_t* lengths,
                                          int64_t max_length, void* k_cache, void* v_cache,
                                          int64_t cache_capacity, void* y, float* o_raw, int B,
-                                         int Hq, int Hkv, int d, int dtype, void* workspace,
+                                         int Hq, int Hkv, int d, lt_dtype dtype, void* workspace,
                                          size_t workspace_bytes, void* stream) {
     return attn_decode(q, k_new, v_new, gate, q_norm_w, k_norm_w, o_norm_w, norm_w_head_stride,
                        logit_scale_base, rms_eps, nullptr, lengths, max_length, k_cache, v_cache,

@@ -49,7 +49,7 @@ bool layer_shape_ok(int B, int H, int d, int d_model, int dtype) {
 
 extern "C" {
 
-size_t lightning_layer_prefill_workspace_size(int B, int T, int H, int d, int d_model, int dtype,
+size_t lightning_layer_prefill_workspace_size(int B, int T, int H, int d, int d_model, lt_dtype dtype,
                                               int chunk, int segments) {
     if (!layer_shape_ok(B, H, d, d_model, dtype) || T <= 0) return 0;
     int c = 0;
@@ -66,7 +66,7 @@ lt_status lightning_layer_prefill(const void* x, const void* w_qkvz, const void*
                                   const float* o_norm_w, int norm_w_head_stride,
                                   const double* lambda, double rope_base, double rms_eps,
                                   int64_t pos0, const float* state_in, float* state_out,
-                                  void* out, int B, int T, int H, int d, int d_model, int dtype,
+                                  void* out, int B, int T, int H, int d, int d_model, lt_dtype dtype,
                                   int chunk, int segments, void* workspace,
                                   size_t workspace_bytes, void* const* stage_events,
                                   void* stream) {
@@ -123,7 +123,7 @@ lt_status lightning_layer_prefill(const void* x, const void* w_qkvz, const void*
     return LT_OK;
 }
 
-size_t lightning_layer_decode_workspace_size(int B, int H, int d, int d_model, int dtype) {
+size_t lightning_layer_decode_workspace_size(int B, int H, int d, int d_model, lt_dtype dtype) {
     if (!layer_shape_ok(B, H, d, d_model, dtype)) return 0;
     LayerWs w;
     if (!layer_ws(B, H, d, dtype, 0, &w)) return 0;
@@ -136,7 +136,7 @@ lt_status lightning_layer_decode_step(const void* x, const void* w_qkvz, const v
                                       const double* lambda, double rope_base, double rms_eps,
                                       const int64_t* positions, const float* state_in,
                                       float* state_out, void* out, int B, int H, int d,
-                                      int d_model, int dtype, void* workspace,
+                                      int d_model, lt_dtype dtype, void* workspace,
                                       size_t workspace_bytes, void* stream) {
     if (!ok_ptr(x) || !ok_ptr(w_qkvz) || !ok_ptr(w_o) || !ok_ptr(out)) return LT_ERR_INVALID_ARG;
     if (!layer_shape_ok(B, H, d, d_model, dtype)) return LT_ERR_INVALID_ARG;

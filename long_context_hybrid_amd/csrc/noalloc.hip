@@ -55,7 +55,7 @@ lt_status lightning_prefill_noalloc(const void* q, const void* k, const void* v,
                                     const float* o_norm_w, int norm_w_head_stride,
                                     const double* lambda, double rope_base, double rms_eps,
                                     int64_t pos0, const float* state_in, float* state_out,
-                                    void* y, float* o_raw, int B, int T, int H, int d, int dtype,
+                                    void* y, float* o_raw, int B, int T, int H, int d, lt_dtype dtype,
                                     int chunk, int segments, void* stream) {
     if (H <= 0 || d <= 0 || (long long)H * d > 0x7fffffffLL) return LT_ERR_INVALID_ARG;
     // every argument check of the prefill first, so bad arguments launch and query nothing

@@ -73,7 +73,7 @@ def _load() -> ct.CDLL:
     h.lightning_status_string.restype = ct.c_char_p
     h.lightning_hypenet_gamma.argtypes = [i32, vp]
     h.lightning_hypenet_gamma.restype = i32
-    h.lightning_state_init.argtypes = [vp, i32, i32, i32, vp, vp]
+    h.lightning_state_init.argtypes = [vp, i32, i32, i32, i32, vp, vp]
     h.lightning_state_init.restype = i32
     h.lightning_prefill_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp]
     h.lightning_prefill_plan.restype = i32
@@ -207,13 +207,13 @@ def lightning_hypenet_gamma(H: int) -> list:
 
 
 def lightning_state_init(state: torch.Tensor, init: torch.Tensor | None = None, stream=None):
-    B, H, d, d2 = state.shape
-    if d != d2:
-        raise ValueError("state must be [B, H, d, d]")
+    """Zero `state` [B, H, dk, dv] (fp32), or copy `init` (same shape) into it."""
+    B, H, dk, dv = state.shape
     dev = state.device
     sp = _dev(state, "state", torch.float32, None, dev)
     ip = _dev(init, "init", torch.float32, state.shape, dev)
-    _check(lib.lightning_state_init(sp, B, H, d, ip, _stream(stream, dev)), "lightning_state_init")
+    _check(lib.lightning_state_init(sp, B, H, dk, dv, ip, _stream(stream, dev)),
+           "lightning_state_init")
     return state
 
 

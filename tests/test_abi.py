@@ -273,9 +273,11 @@ def test_decode_rejects(name, over, status):
 
 @no_gpu
 def test_state_init_rejects():
-    assert lt.lib.lightning_state_init(None, 1, 1, 64, None, None) == lt.LT_ERR_INVALID_ARG
-    assert lt.lib.lightning_state_init(FAKE + 4, 1, 1, 64, None, None) == lt.LT_ERR_INVALID_ARG
-    assert lt.lib.lightning_state_init(FAKE, 0, 1, 64, None, None) == lt.LT_ERR_INVALID_ARG
+    assert lt.lib.lightning_state_init(None, 1, 1, 64, 64, None, None) == lt.LT_ERR_INVALID_ARG
+    assert lt.lib.lightning_state_init(FAKE + 4, 1, 1, 64, 64, None, None) == lt.LT_ERR_INVALID_ARG
+    assert lt.lib.lightning_state_init(FAKE, 0, 1, 64, 64, None, None) == lt.LT_ERR_INVALID_ARG
+    assert lt.lib.lightning_state_init(FAKE, 1, 1, 64, 0, None, None) == lt.LT_ERR_INVALID_ARG
+    assert lt.lib.lightning_state_init(FAKE, 1, 1, -2, 64, None, None) == lt.LT_ERR_INVALID_ARG
 
 
 # ---- the whole layer -------------------------------------------------------------------------------

@@ -131,11 +131,26 @@ def test_decode_rejects_on_gpu(bufs, name, over, status):
     assert _decode(bufs) == lt.LT_OK
 
 
+def test_state_init_rectangular_copy_and_zero():
+    """dk != dv: the fill covers B H dk dv values exactly."""
+    dev = torch.device("cuda")
+    init = torch.randn(2, 3, 64, 128, device=dev)
+    st = torch.full((2 * 3 * 64 * 128 + 64,), 7.0, device=dev)
+    view = st[: init.numel()].view(init.shape)
+    lt.lightning_state_init(view, init)
+    torch.cuda.synchronize()
+    assert torch.equal(view, init)
+    assert bool((st[init.numel():] == 7.0).all())  # nothing past the end is written
+    lt.lightning_state_init(view)
+    torch.cuda.synchronize()
+    assert int(view.count_nonzero()) == 0 and bool((st[init.numel():] == 7.0).all())
+
+
 def test_state_init_on_gpu(bufs):
     st = bufs["state"]
-    assert lt.lib.lightning_state_init(_ptr(st, 4), 1, 2, 128, None, None) == lt.LT_ERR_INVALID_ARG
-    assert lt.lib.lightning_state_init(_ptr(st), 0, 2, 128, None, None) == lt.LT_ERR_INVALID_ARG
-    assert lt.lib.lightning_state_init(_ptr(st), 1, 2, 128, None, None) == lt.LT_OK
+    assert lt.lib.lightning_state_init(_ptr(st, 4), 1, 2, 128, 128, None, None) == lt.LT_ERR_INVALID_ARG
+    assert lt.lib.lightning_state_init(_ptr(st), 0, 2, 128, 128, None, None) == lt.LT_ERR_INVALID_ARG
+    assert lt.lib.lightning_state_init(_ptr(st), 1, 2, 128, 128, None, None) == lt.LT_OK
     torch.cuda.synchronize()
     assert int(st[: 2 * 128 * 128 * 4].count_nonzero()) == 0
 
