@@ -272,6 +272,15 @@ def test_attn_decode_device_lengths_match_host(case):
     _check_decode(inp, a, label + " (device lengths)", *devr)
 
 
+@pytest.mark.timeout(300)
+def test_attn_decode_device_lengths_full_context():
+    """One token at position 524287 of the Qwen3-1.7B-shaped attention layer with the length in
+    device memory (the bound sizes 256 splits of 2048 keys)."""
+    cap = 524288
+    inp = _decode_inputs(1, 16, 8, cap, (cap - 1,), seed=98)
+    _check_decode(inp, 500.0, "B=1 context 524287 (device lengths)", *_run_decode_dev(inp, 500.0))
+
+
 def test_attn_decode_device_lengths_large_batch():
     """B = 80, more rows than host lengths allow, lengths from 0 across a split boundary."""
     B, Hq, Hkv, cap = 80, 4, 2, 2100
