@@ -271,13 +271,15 @@ gemm_tile_kernel(const TileParams p) {
         wait_lgkm0();
         barrier();
         issue_a(SB, ring1);
-        // Rows past M fall outside a slice's resource; chunks past N get an offset outside it.
+        // A slice's resource starts at its first element, so rows past M fall outside it; chunks
+        // past N get an offset outside it.  (The stores take no scalar offset: with a register
+        // there the compiler does not keep a VALU write of a 16-byte store's data registers one
+        // wait state away from the store, and the store can then write the new values.)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            // (readfirstlane: the slice's rows are uniform, so its resource lives in SGPRs)
+            // (readfirstlane: the slice's rows are uniform, so its resources live in SGPRs)
             const int row0 = __builtin_amdgcn_readfirstlane(cm0 + 128 * wm + 32 * i);
-            const __amdgpu_buffer_rsrc_t d_rsrc =
-                make_rsrc_uniform(p.D + (size_t)row0 * p.N, (uint32_t)max(0, min(32, p.M - row0)) * d_row);
+            const int rows = max(0, min(32, p.M - row0));
 #pragma unroll
             for (int jp = 0; jp < 2; ++jp) {
                 // (one slice at a time: pinning the slice's accumulators to AGPRs here keeps the
@@ -294,12 +296,15 @@ gemm_tile_kernel(const TileParams p) {
                     }
                 const int col0 = __builtin_amdgcn_readfirstlane(cn0 + 128 * wn + 64 * jp);
                 const bool in_n = 8 * (lane & 7) < p.N - col0;
+                const bool live = rows > 0 && col0 < p.N;
+                const __amdgpu_buffer_rsrc_t d_rsrc =
+                    make_rsrc_uniform(p.D + (size_t)row0 * p.N + (live ? col0 : 0),
+                                      live ? (uint32_t)rows * d_row - 2u * (uint32_t)col0 : 0u);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const uint4 v = *reinterpret_cast<const uint4*>(out_r + 8 * kOutPitch * u);
                     const u32x4_t x = {v.x, v.y, v.z, v.w};
-                    __builtin_amdgcn_raw_buffer_store_b128(x, d_rsrc, in_n ? st_off[u] : 0x80000000u,
-                                                           2u * (uint32_t)col0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(x, d_rsrc, in_n ? st_off[u] : 0x80000000u, 0, 0);
                 }
             }
         }
