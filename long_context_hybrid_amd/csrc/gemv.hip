@@ -4,7 +4,10 @@
 // the projections x [W_q | W_k | W_v | W_z] of the new tokens and the output projection y W_o^T.
 //
 // With M <= 64 the product is bound by streaming W from HBM once (32 MiB and 8 MiB for the
-// Qwen3-1.7B-shaped layer), so the kernel is laid out for that stream:
+// Qwen3-1.7B-shaped layer).  bf16 with five or more rows runs skinny_ring_kernel (described at
+// the kernel): each wavefront of a workgroup streams its own contiguous range of K through a
+// private LDS ring, with no barrier in the loop.  Other shapes and fp32 storage run
+// skinny_gemm_kernel, laid out for the same stream:
 //   * a workgroup owns 32 output columns (one 32 x 32 MFMA tile in n), all M rows (one or two
 //     32-row tiles) and all of K.  (Splitting K over workgroups measured slower: summing the
 //     partial tiles inside the kernel needs a device-scope release, which writes back the whole
@@ -24,6 +27,9 @@
 // be almost empty, so gemv_small_kernel does the product with VALU FMAs instead: a wavefront owns
 // two rows of W and streams them along K, 16 bytes per lane per step, with the few rows of A
 // read alongside (they stay in the caches); the partial sums are reduced across the wavefront.
+#include <algorithm>
+#include <type_traits>
+
 #include "lt_device.h"
 #include "lt_internal.h"
 
@@ -195,6 +201,127 @@ __global__ void __launch_bounds__(kThreads) skinny_gemm_kernel(const SkinnyParam
 }
 
 
+// bf16 skinny GEMM with private stage rings.  A workgroup owns 32 output columns and MT 32-row
+// tiles of A; its NWV wavefronts split K into NWV contiguous ranges, and each one streams the 32
+// W rows and 32 MT A rows of its own range through its own two-stage LDS ring, 64 k (128 bytes
+// per row) per stage, filled by buffer_load_dwordx4 ... lds.  No wavefront reads another's
+// ring, so the main loop has no barriers: a wavefront waits only for its own loads.  The
+// partial tiles are summed through LDS once at the end and each output rounded once.
+//   * a DMA instruction fills 8 rows (1 KiB): lane l loads row r = 8 i + l / 8 at chunk
+//     (l % 8) ^ ((r / 2) % 8), so chunk c of row r sits at position c ^ ((r / 2) % 8) and the
+//     16 lanes of an operand read phase (16 consecutive rows, one chunk) hit 16 distinct
+//     16-byte bank groups;
+//   * rows past N or M fall outside the operand's buffer resource and read zero;
+//   * requirements (checked by the caller): K a multiple of 64 NWV, row strides a multiple of
+//     8 elements, A and W 16-byte aligned.
+// Grid: (ceil(N / 32), ceil(M / (32 MT))).
+struct RingParams {
+    const uint16_t* A;
+    const uint16_t* W;
+    uint16_t* D;
+    int M, N, K;
+    int lda, ldw, ldd;
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ring_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+// (a function of its own: inside a lambda of a kernel template, this builtin keeps the host
+// pass from emitting the kernel's launch stub)
+__device__ __forceinline__ void ring_dma(__amdgpu_buffer_rsrc_t r, unsigned char* lds, uint32_t voff,
+                                         uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, 0);
+}
+// s_waitcnt with only the vector-memory count (six bits)
+template <int N>
+__device__ __forceinline__ void ring_wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ int ring_off(int r, int c) { return r * 128 + 16 * (c ^ ((r >> 1) & 7)); }
+
+template <int MT, int NWV>
+__global__ void __launch_bounds__(64 * NWV) skinny_ring_kernel(const RingParams p) {
+    constexpr int NST = 2;                  // stages per ring
+    constexpr int ROWS = 32 + 32 * MT;      // W rows, then A rows
+    constexpr int SB = ROWS * 128;          // bytes of one stage
+    constexpr int NI = ROWS / 8;            // DMA instructions per stage
+    constexpr int RED = MT * 16 * 64 * 4 * NWV;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[NWV * NST * SB > RED ? NWV * NST * SB : RED];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, lm = lane & 31, lh = lane >> 5;
+    const int n0 = blockIdx.x * 32, m0 = blockIdx.y * 32 * MT;
+    const uint32_t wrow = 2u * (uint32_t)p.ldw, arow = 2u * (uint32_t)p.lda;
+    const __amdgpu_buffer_rsrc_t wr =
+        ring_rsrc(p.W + (size_t)n0 * p.ldw, (uint32_t)min(32, p.N - n0) * wrow);
+    const __amdgpu_buffer_rsrc_t ar =
+        ring_rsrc(p.A + (size_t)m0 * p.lda, (uint32_t)min(32 * MT, p.M - m0) * arow);
+    uint32_t off[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int r = 8 * i + (lane >> 3);
+        off[i] = (uint32_t)(i < 4 ? r : r - 32) * (i < 4 ? wrow : arow) +
+                 16u * (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
+    }
+    unsigned char* ring = lds + wave * NST * SB;
+    const int kq = p.K / NWV;                           // this wavefront's k range
+    const uint32_t kb0 = 2u * (uint32_t)(wave * kq);    // its first byte within a row
+    const int ns = kq / 64;
+    auto issue = [&](int s) {
+        unsigned char* st = ring + (s & 1) * SB;
+        const uint32_t so = __builtin_amdgcn_readfirstlane(kb0 + 128u * (uint32_t)s);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) ring_dma(i < 4 ? wr : ar, st + i * 1024, off[i], so);
+    };
+    f32x16 acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = f32x16{};
+    // W is the MFMA's first operand, so the accumulators hold D^T: lane (lm, lh) register r is
+    // D[m0 + 32 t + lm][n0 + acc_row(r, lh)]
+    auto compute = [&](int s) {
+        const unsigned char* st = ring + (s & 1) * SB;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bf16x8 w = *reinterpret_cast<const bf16x8*>(st + ring_off(lm, 2 * j + lh));
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + ring_off(32 + 32 * t + lm, 2 * j + lh));
+                acc[t] = mfma_bf16(w, a, acc[t]);
+            }
+        }
+    };
+    issue(0);
+    if (ns > 1) issue(1);
+    for (int s = 0; s < ns; ++s) {
+        if (s + 1 < ns) ring_wait_vm<NI>();  // stage s landed; stage s + 1 may be in flight
+        else ring_wait_vm<0>();
+        compute(s);
+        if (s + 2 < ns) {
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // this stage's operand reads are done
+            issue(s + 2);
+        }
+    }
+    __syncthreads();  // every wavefront is done with its ring before it holds the partial tiles
+    float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[((wave * MT + t) * 16 + r) * 64 + lane] = acc[t][r];
+    __syncthreads();
+    constexpr int NE = MT * 16 * 64;
+    for (int e = tid; e < NE; e += 64 * NWV) {
+        const int t = e / 1024, r = (e / 64) % 16, l = e % 64;
+        float sum = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < NWV; ++w2) sum += red[((w2 * MT + t) * 16 + r) * 64 + l];
+        const int m = m0 + 32 * t + (l & 31), n = n0 + acc_row(r, l >> 5);
+        if (m < p.M && n < p.N) p.D[(size_t)m * p.ldd + n] = to_bf16_bits(sum);
+    }
+}
+
 // D[m][n] for m < MM (MM <= 4): wavefront w of workgroup b owns W rows n = 2 (4 b + w) + {0, 1}.
 // Lane l takes the 16-byte chunks c = l + 64 i of K.  Chunks at or past K re-read the last chunk
 // and are masked to zero (unconditional loads, no branch in the loop).  Grid: ceil(N / 8).
@@ -276,6 +403,35 @@ void launch_small(const SkinnyParams& sp, hipStream_t stream) {
 
 // One or two 32-row tiles per workgroup: two read each W column block once for 64 rows, but
 // leave most compute units idle when N has fewer 32-column blocks than there are of them.
+template <int MT, int NWV>
+void launch_ring(const SkinnyParams& sp, hipStream_t stream) {
+    const RingParams rp{static_cast<const uint16_t*>(sp.A), static_cast<const uint16_t*>(sp.W),
+                        static_cast<uint16_t*>(sp.D), sp.M, sp.N, sp.K, sp.lda, sp.ldw, sp.ldd};
+    skinny_ring_kernel<MT, NWV><<<dim3((sp.N + 31) / 32, (sp.M + 32 * MT - 1) / (32 * MT)),
+                                  dim3(64 * NWV), 0, stream>>>(rp);
+}
+
+// bf16 with 5 or more rows: the ring kernel where its layout applies.  With at least as many
+// 32-column blocks as compute units, 64-row tiles and four wavefronts (W read once per 64 rows);
+// with fewer (the output projection), 32-row tiles and eight wavefronts, which keep more loads in
+// flight on the few compute units that have columns.  Returns false where neither applies.
+bool launch_ring_bf16(const SkinnyParams& sp, int cus, hipStream_t stream) {
+    const bool aligned = (reinterpret_cast<uintptr_t>(sp.A) & 15) == 0 &&
+                         (reinterpret_cast<uintptr_t>(sp.W) & 15) == 0 && sp.lda % 8 == 0 &&
+                         sp.ldw % 8 == 0;
+    if (!aligned || sp.M < 5) return false;
+    // (32 rows of the longest stride in one resource: fits the 32-bit record count)
+    if ((int64_t)64 * 2 * std::max(sp.lda, sp.ldw) > 0x7fffffffLL) return false;
+    if ((sp.N + 31) / 32 >= cus) {
+        if (sp.K % 256 != 0) return false;
+        launch_ring<2, 4>(sp, stream);
+        return true;
+    }
+    if (sp.K % 512 != 0) return false;
+    launch_ring<1, 8>(sp, stream);
+    return true;
+}
+
 template <class T>
 void launch_typed(const SkinnyParams& sp, int cus, hipStream_t stream) {
     switch (sp.M) {
@@ -284,6 +440,9 @@ void launch_typed(const SkinnyParams& sp, int cus, hipStream_t stream) {
     case 3: return launch_small<T, 3>(sp, stream);
     case 4: return launch_small<T, 4>(sp, stream);
     default: break;
+    }
+    if constexpr (std::is_same_v<T, uint16_t>) {
+        if (launch_ring_bf16(sp, cus, stream)) return;
     }
     if (sp.M <= 32 || (sp.N + 31) / 32 < cus)
         launch_ns<T, 1, 4>(sp, stream);

@@ -192,12 +192,18 @@ def gpu_layer_decode(inp):
                                               ("one_row_ternary", "ternary"),
                                               ("rows_4_ternary", "ternary"),
                                               ("rows_40_ternary", "ternary"),
+                                              ("rows_33_wide", "gauss"),
+                                              ("rows_100_wide", "gauss"),
+                                              ("rows_70_ragged_out", "gauss"),
                                               ("small_fp32", "gauss")])
 def test_layer_decode(spec_name, values):
-    """1, 4, 5, 40 and 64 batch rows (bf16; 64 and 1 with the full-size d_model 2048 weights) and
-    3 (fp32): up to four rows take the VALU product, more the MFMA tiles.  The ternary inputs'
-    projections are exact integers, so there the projections must match the oracle bit for
-    bit."""
+    """1, 4, 5, 33, 40, 64, 70 and 100 batch rows (bf16; 64 and 1 with the full-size d_model 2048
+    weights) and 3 (fp32): up to four rows take the VALU product, more the MFMA tiles.  33 and
+    100 rows (8192 projection columns) take the 64-row ring tiles, one ragged tile and a full one
+    plus a ragged one; their output projection (256 and 512 columns, K = 2048) and the 70-row
+    case's (200 columns, ragged, K = 512, three 32-row tiles) take the 32-row ring tiles.  The
+    ternary inputs' projections are exact integers, so there the projections must match the
+    oracle bit for bit."""
     if spec_name == "full":
         inp = synth.make_layer(synth.LAYER_DECODE_B64)
     elif spec_name == "full_one_row":  # the full-size weights with one sequence (batch 1)
@@ -210,6 +216,12 @@ def test_layer_decode(spec_name, values):
         inp = synth.make_custom_layer(4, 1, 2, 128, 256, seed=12, state="randn", values=values)
     elif spec_name == "rows_40_ternary":
         inp = synth.make_custom_layer(40, 1, 2, 128, 256, seed=11, state="randn", values=values)
+    elif spec_name == "rows_33_wide":
+        inp = synth.make_custom_layer(33, 1, 16, 128, 512, seed=13, state="randn", values=values)
+    elif spec_name == "rows_100_wide":
+        inp = synth.make_custom_layer(100, 1, 16, 128, 256, seed=14, state="randn", values=values)
+    elif spec_name == "rows_70_ragged_out":
+        inp = synth.make_custom_layer(70, 1, 4, 128, 200, seed=15, state="randn", values=values)
     else:
         inp = synth.make_custom_layer(3, 1, 2, 64, 64, dtype=torch.float32, seed=9,
                                       state="randn", lambdas=(0.0, 0.95))
