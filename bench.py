@@ -263,6 +263,27 @@ def bench_prefill(args, torch, lt, synth, workload=None, steps=None):
     )
 
 
+def graph_replay_us(torch, step, n):
+    """Mean step time of one replay of n steps captured into a HIP graph (torch.cuda.graph),
+    after one untimed replay."""
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(g, stream=cs):
+            for i in range(n):
+                step(i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) * 1e3 / n
+
+
 def bench_decode(args, torch, lt, synth, B=None):
     """The mixer's decode step over rotating state buffers (so the state cannot be served from
     MALL).  At B = 64 the steps are launched one by one; with fewer rows a step's kernel takes
@@ -285,30 +306,20 @@ def bench_decode(args, torch, lt, synth, B=None):
     for i in range(3):
         step(i)
     torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     graph = B < 64
     if graph:
-        g = torch.cuda.CUDAGraph()
-        cs = torch.cuda.Stream()
-        cs.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(cs):
-            with torch.cuda.graph(g, stream=cs):
-                for i in range(args.decode_steps):
-                    step(i)
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        start.record()
-        g.replay()
-        stop.record()
+        us = graph_replay_us(torch, step, args.decode_steps)
     else:
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record()
         for i in range(args.decode_steps):
             step(i)
         stop.record()
-    torch.cuda.synchronize()
-    us = start.elapsed_time(stop) * 1e3 / args.decode_steps
+        torch.cuda.synchronize()
+        us = start.elapsed_time(stop) * 1e3 / args.decode_steps
     stats = None if graph else eager_step_stats(torch, step, args.decode_steps)
+    # the same steps replayed from a captured graph (no host launch gaps), beside the eager time
+    us_graph = us if graph else graph_replay_us(torch, step, args.decode_steps)
     act_bytes = 2
     per_bh = 2 * d * d * 4 + 5 * d * act_bytes
     alg = B * H * per_bh + B * 8
@@ -321,7 +332,8 @@ def bench_decode(args, torch, lt, synth, B=None):
                          "traffic": measured_traffic("decode", name),
                          "kernel": "decode_kernel<ModeBF16,128>", "alg_bytes_per_launch": alg,
                          "bytes_per_bh": per_bh, "workgroups": B * H},
-            "step_stats": stats, "state_buffers": len(states)}
+            "step_stats": stats, "us_per_step_graph": round(us_graph, 3),
+            "state_buffers": len(states)}
 
 
 def bench_configs(args, torch, lt, synth):
@@ -487,30 +499,20 @@ def bench_layer_decode(args, torch, lt, synth, B=None):
     for i in range(3):
         step(i)
     torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     graph = B < 64
     if graph:
-        g = torch.cuda.CUDAGraph()
-        cs = torch.cuda.Stream()
-        cs.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(cs):
-            with torch.cuda.graph(g, stream=cs):
-                for i in range(args.decode_steps):
-                    step(i)
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        start.record()
-        g.replay()
-        stop.record()
+        us = graph_replay_us(torch, step, args.decode_steps)
     else:
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record()
         for i in range(args.decode_steps):
             step(i)
         stop.record()
-    torch.cuda.synchronize()
-    us = start.elapsed_time(stop) * 1e3 / args.decode_steps
+        torch.cuda.synchronize()
+        us = start.elapsed_time(stop) * 1e3 / args.decode_steps
     stats = None if graph else eager_step_stats(torch, step, args.decode_steps)
+    # the same steps replayed from a captured graph (no host launch gaps), beside the eager time
+    us_graph = us if graph else graph_replay_us(torch, step, args.decode_steps)
     wbytes = (4 * H * d * dm + dm * H * d) * 2
     io = B * dm * 2 * 2 + B * (4 * H * d + H * d) * 2 * 2  # x, out; projections and y written + read
     alg = wbytes + B * H * 2 * d * d * 4 + io + B * 8
@@ -521,7 +523,7 @@ def bench_layer_decode(args, torch, lt, synth, B=None):
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                          "alg_bytes_per_step": alg, "weight_bytes": wbytes},
-            "step_stats": stats, "rotating_sets": nset}
+            "step_stats": stats, "us_per_step_graph": round(us_graph, 3), "rotating_sets": nset}
 
 
 def bench_attn(args, torch, lt, synth):
