@@ -245,6 +245,28 @@ def test_layer_decode(spec_name, values):
     assert worst["y"] <= tol["y"] and worst["out"] <= tol["out"] and worst["state"] <= stol, worst
 
 
+@pytest.mark.timeout(300)
+def test_layer_projections_many_tiles_per_workgroup():
+    """Every projection of a 10277-token prefill with 8192 projection columns: 41 row blocks (the
+    last one 37 rows) by 32 column blocks of the 256 x 256-tile GEMM, about five tiles per
+    workgroup of its persistent grid, so each workgroup's later tiles start while its previous
+    tile's epilogue stores are in flight.  All of them are compared with the oracle's products,
+    and the layer output with the fp64 product of the GPU's own y and W_o."""
+    inp = synth.make_custom_layer(1, 10277, 16, 128, 256, seed=21, state="zeros", values="gauss")
+    gpu = gpu_layer(inp)
+    x = host_bits(inp["x"])
+    pq = ol.projections(x, host_bits(inp["w_qkvz"]), inp["H"], inp["d"])
+    T, hd = inp["T"], inp["H"] * inp["d"]
+    ref = np.concatenate([ol.widen(a).reshape(1, T, hd) for a in pq], -1)
+    check_proj(gpu["proj"], ref, torch.bfloat16, False, "10277-token projections",
+               acc_bound(inp["x"], inp["w_qkvz"]))
+    yw = gpu["y"].double().reshape(T, hd).numpy() @ ol.widen(host_bits(inp["w_o"])).T
+    ref_out = ol.widen(ol.store(yw, ol.BF16))
+    bound = acc_bound(gpu["y"].reshape(T, hd).to(torch.bfloat16), inp["w_o"])
+    check_proj(gpu["out"].reshape(T, -1), ref_out, torch.bfloat16, False,
+               "10277-token output projection", bound)
+
+
 # ---- the benchmarked layer at full size -----------------------------------------------------------
 
 @pytest.mark.timeout(400)  # the oracle's share (two heads over 512K tokens) takes about a minute
