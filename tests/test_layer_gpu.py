@@ -192,15 +192,16 @@ def gpu_layer_decode(inp):
                                               ("one_row_ternary", "ternary"),
                                               ("rows_4_ternary", "ternary"),
                                               ("rows_40_ternary", "ternary"),
+                                              ("rows_5_wide", "gauss"),
                                               ("rows_33_wide", "gauss"),
                                               ("rows_100_wide", "gauss"),
                                               ("rows_70_ragged_out", "gauss"),
                                               ("small_fp32", "gauss")])
 def test_layer_decode(spec_name, values):
     """1, 4, 5, 33, 40, 64, 70 and 100 batch rows (bf16; 64 and 1 with the full-size d_model 2048
-    weights) and 3 (fp32): up to four rows take the VALU product, more the MFMA tiles.  33 and
-    100 rows (8192 projection columns) take the 64-row ring tiles, one ragged tile and a full one
-    plus a ragged one; their output projection (256 and 512 columns, K = 2048) and the 70-row
+    weights) and 3 (fp32): up to four rows take the VALU product, more the MFMA tiles.  5, 33
+    and 100 rows (8192 projection columns) take the 64-row ring tiles, one ragged tile and a full
+    one plus a ragged one; their output projection (256 and 512 columns, K = 2048) and the 70-row
     case's (200 columns, ragged, K = 512, three 32-row tiles) take the 32-row ring tiles.  The
     ternary inputs' projections are exact integers, so there the projections must match the
     oracle bit for bit."""
@@ -216,6 +217,8 @@ def test_layer_decode(spec_name, values):
         inp = synth.make_custom_layer(4, 1, 2, 128, 256, seed=12, state="randn", values=values)
     elif spec_name == "rows_40_ternary":
         inp = synth.make_custom_layer(40, 1, 2, 128, 256, seed=11, state="randn", values=values)
+    elif spec_name == "rows_5_wide":
+        inp = synth.make_custom_layer(5, 1, 16, 128, 512, seed=16, state="randn", values=values)
     elif spec_name == "rows_33_wide":
         inp = synth.make_custom_layer(33, 1, 16, 128, 512, seed=13, state="randn", values=values)
     elif spec_name == "rows_100_wide":
