@@ -93,7 +93,8 @@ def copy_calibration(torch, mib):
 
 
 MIXER_SOURCES = ("abi.hip", "decode.hip", "lt_device.h", "lt_internal.h", "prefill.hip")
-LAYER_SOURCES = ("gemm.hip", "gemm_tile.hip", "gemv.hip", "layer.hip")
+LAYER_SOURCES = ("decode.hip", "gemm.hip", "gemm_tile.hip", "gemv.hip", "layer.hip", "lt_device.h",
+                 "lt_internal.h")
 LAYER_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic_layer_qwen17_512k.md")
 BWD_SOURCES = ("backward.hip", "lt_device.h", "lt_internal.h")
 BWD_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic_backward_qwen17_16k.md")
@@ -101,7 +102,7 @@ BWD_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic_backward_qwen17
 
 def source_fingerprint(sources=MIXER_SOURCES):
     """sha256 over the sources of the measured kernels and their launch configuration (the code
-    the byte counters measured): the mixer's by default, the layer's GEMM calls with
+    the byte counters measured): the mixer's by default, the layer's GEMMs and decode step with
     LAYER_SOURCES."""
     import hashlib
 
@@ -521,7 +522,9 @@ def bench_layer_decode(args, torch, lt, synth, B=None):
     return {"workload": name, "us_per_step": round(us, 3),
             "timing": "HIP graph of %d steps" % args.decode_steps if graph else "eager launches",
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("layer_decode_step", name, LAYER_TRAFFIC_RECORD,
+                                                     LAYER_SOURCES),
                          "alg_bytes_per_step": alg, "weight_bytes": wbytes},
             "step_stats": stats, "us_per_step_graph": round(us_graph, 3), "rotating_sets": nset}
 
