@@ -97,6 +97,8 @@ LAYER_SOURCES = ("decode.hip", "gemm.hip", "gemm_tile.hip", "gemv.hip", "layer.h
                  "lt_internal.h")
 LAYER_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic_layer_qwen17_512k.md")
 BWD_SOURCES = ("backward.hip", "lt_device.h", "lt_internal.h")
+ATTN_SOURCES = ("attention.hip", "lt_device.h", "lt_internal.h")
+ATTN_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic_attention_qwen17_512k.md")
 BWD_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic_backward_qwen17_16k.md")
 
 
@@ -574,11 +576,15 @@ def bench_attn(args, torch, lt, synth):
             "value": round(B * T / (ms * 1e-3), 1), "unit": "tokens/s/layer", "steps": n,
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                         "traffic": None, "kernel": "attn_fwd_kernel<2> (flash attention)",
+                         "traffic": measured_traffic("attn_fwd", spec.name, ATTN_TRAFFIC_RECORD,
+                                                     ATTN_SOURCES),
+                         "kernel": "attn_fwd_kernel<2> (flash attention)",
                          "flops_per_launch": flops, "launch_ms": round(main_ms, 3)},
             "prologue": {"ms": round(pro_ms, 4), "bound": "hbm", "achieved": round(pro_gbs, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(pro_gbs / HBM_PEAK_GBS, 4), "alg_bytes": pro_bytes}}
+                         "frac": round(pro_gbs / HBM_PEAK_GBS, 4), "alg_bytes": pro_bytes,
+                         "traffic": measured_traffic("attn_prologue", spec.name, ATTN_TRAFFIC_RECORD,
+                                                     ATTN_SOURCES)}}
 
 
 def bench_attn_decode(args, torch, lt, synth):
@@ -619,10 +625,12 @@ def bench_attn_decode(args, torch, lt, synth):
     alg = 2 * (n + 1) * Hkv * d * 2 + (2 * Hq + 2 * Hkv + Hq) * d * 2
     gbs = alg / (us * 1e-6) / 1e9
     del kc, vc
-    return {"workload": "HyPE attention decode step B=1, 524287 cached tokens, Hq=16 Hkv=8 "
-                        "d=128 bf16", "us_per_step": round(us, 2),
+    name = "HyPE attention decode step B=1, 524287 cached tokens, Hq=16 Hkv=8 d=128 bf16"
+    return {"workload": name, "us_per_step": round(us, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("attn_decode_step", name, ATTN_TRAFFIC_RECORD,
+                                                     ATTN_SOURCES),
                          "alg_bytes_per_step": alg}}
 
 
