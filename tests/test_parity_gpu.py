@@ -6,6 +6,7 @@ degenerate cases (lambda = 0, lambda = 1, T = 1, a partial last chunk).  The ful
 run in the launch configuration the benchmark times and are compared on every (b, h) slice
 (y, o and the final state), the oracle running them in groups of parallel slices.
 """
+import math
 import zlib
 
 import numpy as np
@@ -44,6 +45,10 @@ SMALL = [
     ("bf16_d128_slow_heads", 1, 8192 + 33, 3, 128, torch.bfloat16, (0.99999, 0.999, 0.5), "randn", (3, 5)),
     # 3 and 2 sub-segments per segment, fp32 activations
     ("fp32_d64_subsegments", 2, 2048 + 40, 1, 64, torch.float32, (0.9999,), "randn", (2, 3)),
+    # the paper's own decay schedule (Appendix A, Eq. 19): gamma_h = exp(-2^(-8h/H)), h = 1..16,
+    # from 0.49 (memory of about one token) to 0.996 (about 256 tokens)
+    ("bf16_d128_eq19_gamma", 1, 2048 + 9, 16, 128, torch.bfloat16,
+     tuple(math.exp(-2.0 ** (-8.0 * h / 16)) for h in range(1, 17)), "randn", (0, 4)),
 ]
 
 
