@@ -21,6 +21,7 @@ lambda = 0), the others must be finite: dv and dg to the bound above, dq and dk 
 error of at most 2e-2 of the norm of the same rows' gradients for the same inputs with
 lambda = 0.5 (where they are of ordinary size).
 """
+import math
 import zlib
 
 import numpy as np
@@ -143,6 +144,10 @@ CASES = [
     ("lambda_one", 1, 200, 1, (1.0,), "randn", True, 0, (0, 2)),
     ("long_position", 1, 257, 2, None, "zeros", True, 500000, (0, 2)),
     ("sub_segments", 1, 4096 + 33, 2, None, "randn", True, 0, (0, 4)),
+    # the paper's decay schedule (Appendix A, Eq. 19): gamma_h = exp(-2^(-8h/H)), h = 1..16;
+    # the fast heads' lazily scaled state and state gradient renormalise in every chunk
+    ("eq19_gamma", 1, 1024 + 5, 16, tuple(math.exp(-2.0 ** (-8.0 * h / 16)) for h in range(1, 17)),
+     "randn", True, 0, (0, 3)),
 ]
 
 
